@@ -1,0 +1,217 @@
+"""fp64 reference of one MoE decode/verify round — TEST INFRASTRUCTURE ONLY.
+
+Written from the pages, row by row, with no blocking, fusion or reordering:
+
+  * infero README, "Beyond plain text decode" (MoE bullet): a router scores
+    experts, a top-k kernel picks them at decode, and a counting sort groups
+    (row, expert) pairs by expert for a per-expert GEMM.
+  * infero README, "Layout" (decoder-block figure): the expert is the SwiGLU
+    feed-forward silu(W_g x) * (W_u x) followed by W_d.
+  * infero README, "Design notes": block-encoded weights are read in place;
+    activations are fp32 so intermediates compare against a CPU reference.
+  * infero README, "AWQ, FP8, and NVFP4 checkpoints": a 4-bit block format
+    keeps a scale and a minimum every 32 weights.
+  * AlphaInfer page, section 2 ("One captured graph per decode round"): a
+    round is one forward pass over 1-8 token rows; section 3.1: each extra
+    verified row routes to experts the others did not need, so the set of
+    experts a round touches is the union over its rows.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * dequantisation is w = s*q + m (fp16 scale s, fp16 minimum m, q in 0..15);
+  * byte j of a 32-block holds element 2j (low nibble) and 2j+1 (high nibble);
+  * selection is the k largest logits in descending order, ties to the lower
+    expert id;
+  * routing weights are the softmax of the k selected logits, nothing else;
+  * SiLU is applied to the gate projection; no shared expert, no norm;
+  * a multi-layer round adds each layer's MoE output to its input
+    (residual), and a single-layer round returns the MoE output alone.
+
+Parity pins (tests/test_oracle_pins.py): every function below is pinned by a
+check independent of its own formula (hand-written golden blocks, closed
+forms, brute force, textbook routines, invariants).  No function is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 32
+
+
+# ---------------------------------------------------------------------------
+# Weight format
+# ---------------------------------------------------------------------------
+
+def unpack_codes(codes: np.ndarray) -> np.ndarray:
+    """uint8 [..., K/2] -> int64 [..., K]: element 2j is byte j's low nibble, 2j+1 its high nibble."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    lo = (codes & 0x0F).astype(np.int64)
+    hi = (codes >> 4).astype(np.int64)
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.int64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def unpack_scale_min(sm: np.ndarray):
+    """uint32 [..., K/32] -> (scale f64, minimum f64): low half fp16 scale, high half fp16 minimum."""
+    sm = np.asarray(sm).view(np.uint32)
+    s16 = (sm & 0xFFFF).astype(np.uint16).view(np.float16)
+    m16 = (sm >> 16).astype(np.uint16).view(np.float16)
+    return s16.astype(np.float64), m16.astype(np.float64)
+
+
+def dequantize(codes: np.ndarray, sm: np.ndarray) -> np.ndarray:
+    """W[r, c] = s[r, c//32] * q[r, c] + m[r, c//32], exact in fp64 (an 11-bit x 4-bit product plus an fp16)."""
+    q = unpack_codes(codes).astype(np.float64)
+    s, m = unpack_scale_min(sm)
+    K = q.shape[-1]
+    blk = np.arange(K) // BLOCK
+    return s[..., blk] * q + m[..., blk]
+
+
+# ---------------------------------------------------------------------------
+# Router, selection, routing weights
+# ---------------------------------------------------------------------------
+
+def router_logits(router_w: np.ndarray, router_b, x: np.ndarray) -> np.ndarray:
+    """z[e] = sum_h Wr[e, h] * x[h] (+ b[e]) in fp64; each fp32 x fp32 product is exact in fp64."""
+    z = np.asarray(router_w, dtype=np.float64) @ np.asarray(x, dtype=np.float64)
+    if router_b is not None:
+        z = z + np.asarray(router_b, dtype=np.float64)
+    return z
+
+
+def select_topk(z: np.ndarray, k: int) -> np.ndarray:
+    """The k largest logits' expert ids, descending; equal logits go to the lower id (stable sort)."""
+    order = np.argsort(-np.asarray(z, dtype=np.float64), kind="stable")
+    return order[:k].astype(np.int64)
+
+
+def selection_gap(z: np.ndarray, k: int) -> float:
+    """Smallest logit gap that decides the selection or its order (ranks 0..k, i.e. k+1 values)."""
+    zs = np.sort(np.asarray(z, dtype=np.float64))[::-1]
+    n = min(k + 1, zs.size)
+    if n < 2:
+        return float("inf")
+    return float(np.min(zs[: n - 1] - zs[1:n]))
+
+
+def routing_weights(z: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Softmax over the selected logits only: p_j = exp(z_j - max) / sum_j' exp(z_j' - max)."""
+    zs = np.asarray(z, dtype=np.float64)[ids]
+    e = np.exp(zs - zs.max())
+    return e / e.sum()
+
+
+# ---------------------------------------------------------------------------
+# Expert feed-forward
+# ---------------------------------------------------------------------------
+
+def silu(a: np.ndarray) -> np.ndarray:
+    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a))."""
+    a = np.asarray(a, dtype=np.float64)
+    return a / (1.0 + np.exp(-a))
+
+
+def expert_forward(gate_q, gate_sm, up_q, up_sm, down_q, down_sm, x: np.ndarray) -> np.ndarray:
+    """One expert on one row: y = W_d (silu(W_g x) * (W_u x)), weights dequantised in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    Wg = dequantize(gate_q, gate_sm)      # [I, H]
+    Wu = dequantize(up_q, up_sm)          # [I, H]
+    Wd = dequantize(down_q, down_sm)      # [H, I]
+    g = Wg @ x
+    v = Wu @ x
+    h = silu(g) * v
+    return Wd @ h
+
+
+def _expert_arrays(layer: dict, e: int):
+    return (layer["gate_q"][e], layer["gate_sm"][e], layer["up_q"][e], layer["up_sm"][e],
+            layer["down_q"][e], layer["down_sm"][e])
+
+
+# ---------------------------------------------------------------------------
+# One layer, one round
+# ---------------------------------------------------------------------------
+
+def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False):
+    """One MoE layer over rows X [T, H]; each row is evaluated on its own.
+
+    `layer` maps the weight names (router_w, router_b, gate_q, gate_sm, up_q, up_sm, down_q, down_sm)
+    to arrays indexable by expert.  Returns (out [T,H] f64, ids [T,k] int64, p [T,k] f64, gaps [T]).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    T, H = X.shape
+    out = np.zeros((T, H), dtype=np.float64)
+    ids = np.zeros((T, k), dtype=np.int64)
+    p = np.zeros((T, k), dtype=np.float64)
+    gaps = np.zeros(T, dtype=np.float64)
+    cache = {}
+    for t in range(T):
+        z = router_logits(layer["router_w"], layer.get("router_b"), X[t])
+        sel = select_topk(z, k)
+        w = routing_weights(z, sel)
+        gaps[t] = selection_gap(z, k)
+        acc = np.zeros(H, dtype=np.float64)
+        for j in range(k):
+            e = int(sel[j])
+            if e not in cache:
+                cache[e] = _expert_arrays(layer, e)
+            acc = acc + w[j] * expert_forward(*cache[e], X[t])
+        out[t] = X[t] + acc if residual else acc
+        ids[t] = sel
+        p[t] = w
+    return out, ids, p, gaps
+
+
+def moe_round(layers, X: np.ndarray, k: int, residual: bool):
+    """A round over L layers: X^{l+1} = X^l + MoE_l(X^l) with residual, else a single MoE layer.
+
+    Returns (out [T,H] f64, ids [L,T,k], p [L,T,k], gaps [L,T]).
+    """
+    layers = list(layers)
+    if not residual and len(layers) != 1:
+        raise ValueError("a round without residual has exactly one layer")
+    x = np.asarray(X, dtype=np.float64)
+    all_ids, all_p, all_gaps = [], [], []
+    for layer in layers:
+        x, ids, p, gaps = moe_layer(layer, x, k, residual)
+        all_ids.append(ids)
+        all_p.append(p)
+        all_gaps.append(gaps)
+    return x, np.stack(all_ids), np.stack(all_p), np.stack(all_gaps)
+
+
+# ---------------------------------------------------------------------------
+# Worklist: counting sort of (row, rank) pairs by expert
+# ---------------------------------------------------------------------------
+
+def build_worklist(ids: np.ndarray):
+    """Group the T*k (row t, rank j) pairs by expert.
+
+    Returns (uniq, offs, pairs):
+      uniq  : the union of the rows' selected experts, ascending;
+      offs  : exclusive prefix sum of how many rows chose each unique expert (len n_unique + 1);
+      pairs : [T*k, 2] (t, j), grouped by expert in uniq order, t ascending within an expert.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    E = int(ids.max()) + 1 if ids.size else 0
+    count = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            count[ids[t, j]] += 1
+    uniq = np.array([e for e in range(E) if count[e] > 0], dtype=np.int64)
+    offs = np.zeros(len(uniq) + 1, dtype=np.int64)
+    for u, e in enumerate(uniq):
+        offs[u + 1] = offs[u] + count[e]
+    pairs = np.zeros((T * k, 2), dtype=np.int64)
+    fill = offs[:-1].copy()
+    pos = {int(e): u for u, e in enumerate(uniq)}
+    for t in range(T):
+        for j in range(k):
+            u = pos[int(ids[t, j])]
+            pairs[fill[u]] = (t, j)
+            fill[u] += 1
+    return uniq, offs, pairs

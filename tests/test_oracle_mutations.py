@@ -1,0 +1,171 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that some pin catches each one."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe_oracle as om
+import test_oracle_pins as pins
+
+BLOCK = 32
+
+
+def _swap_nibbles(codes):
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.int64)
+    out[..., 0::2] = codes >> 4
+    out[..., 1::2] = codes & 0x0F
+    return out
+
+
+def _dequant_no_min(codes, sm):
+    q = om.unpack_codes(codes).astype(np.float64)
+    s, m = om.unpack_scale_min(sm)
+    blk = np.arange(q.shape[-1]) // BLOCK
+    return s[..., blk] * q
+
+
+def _dequant_wrong_block(codes, sm):
+    q = om.unpack_codes(codes).astype(np.float64)
+    s, m = om.unpack_scale_min(sm)
+    blk = (np.arange(q.shape[-1]) % s.shape[-1])
+    return s[..., blk] * q + m[..., blk]
+
+
+def _swap_scale_min(sm):
+    s, m = ORIG["unpack_scale_min"](sm)
+    return m, s
+
+
+def _router_no_bias(router_w, router_b, x):
+    return np.asarray(router_w, dtype=np.float64) @ np.asarray(x, dtype=np.float64)
+
+
+def _router_fp32(router_w, router_b, x):
+    z = (np.asarray(router_w, dtype=np.float32) @ np.asarray(x, dtype=np.float32)).astype(np.float64)
+    if router_b is not None:
+        z = z + np.asarray(router_b, dtype=np.float64)
+    return z
+
+
+def _topk_ties_high(z, k):
+    return np.argsort(np.asarray(z, dtype=np.float64), kind="stable")[::-1][:k].astype(np.int64)
+
+
+def _topk_ascending(z, k):
+    return ORIG["select_topk"](z, k)[::-1].copy()
+
+
+def _softmax_all(z, ids):
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - z.max())
+    return e[ids] / e.sum()
+
+
+def _silu_sign(a):
+    a = np.asarray(a, dtype=np.float64)
+    return a / (1.0 + np.exp(a))
+
+
+def _expert_silu_on_up(gq, gs, uq, us, dq, ds, x):
+    x = np.asarray(x, dtype=np.float64)
+    g = om.dequantize(gq, gs) @ x
+    v = om.dequantize(uq, us) @ x
+    return om.dequantize(dq, ds) @ (g * om.silu(v))
+
+
+def _expert_add(gq, gs, uq, us, dq, ds, x):
+    x = np.asarray(x, dtype=np.float64)
+    g = om.dequantize(gq, gs) @ x
+    v = om.dequantize(uq, us) @ x
+    return om.dequantize(dq, ds) @ (om.silu(g) + v)
+
+
+def _worklist_rows_descending(ids):
+    uniq, offs, pairs = ORIG["build_worklist"](ids)
+    for u in range(len(uniq)):
+        pairs[offs[u]:offs[u + 1]] = pairs[offs[u]:offs[u + 1]][::-1]
+    return uniq, offs, pairs
+
+
+def _layer_unweighted(layer, X, k, residual=False):
+    out, ids, p, gaps = ORIG["moe_layer"](layer, X, k, residual)
+    ones = np.ones_like(p)
+    out2 = np.zeros_like(out)
+    X = np.asarray(X, dtype=np.float64)
+    for t in range(X.shape[0]):
+        for j in range(k):
+            e = int(ids[t, j])
+            out2[t] += ones[t, j] * om.expert_forward(layer["gate_q"][e], layer["gate_sm"][e], layer["up_q"][e],
+                                                      layer["up_sm"][e], layer["down_q"][e], layer["down_sm"][e],
+                                                      X[t])
+        if residual:
+            out2[t] += X[t]
+    return out2, ids, p, gaps
+
+
+def _round_no_residual(layers, X, k, residual):
+    x = np.asarray(X, dtype=np.float64)
+    outs = []
+    for layer in layers:
+        x, ids, p, gaps = ORIG["moe_layer"](layer, x, k, False)
+        outs.append((ids, p, gaps))
+    return (x, np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]),
+            np.stack([o[2] for o in outs]))
+
+
+ORIG = {name: getattr(om, name) for name in
+        ("unpack_codes", "unpack_scale_min", "dequantize", "router_logits", "select_topk",
+         "routing_weights", "silu", "expert_forward", "moe_layer", "moe_round", "build_worklist")}
+
+MUTATIONS = {
+    "swapped nibbles": ("unpack_codes", _swap_nibbles),
+    "dropped minimum": ("dequantize", _dequant_no_min),
+    "wrong block index": ("dequantize", _dequant_wrong_block),
+    "scale/min swapped": ("unpack_scale_min", _swap_scale_min),
+    "router bias dropped": ("router_logits", _router_no_bias),
+    "router accumulates in fp32": ("router_logits", _router_fp32),
+    "ties to higher id": ("select_topk", _topk_ties_high),
+    "ascending order": ("select_topk", _topk_ascending),
+    "softmax over all experts": ("routing_weights", _softmax_all),
+    "silu sign": ("silu", _silu_sign),
+    "silu on up": ("expert_forward", _expert_silu_on_up),
+    "add instead of multiply": ("expert_forward", _expert_add),
+    "unweighted combine": ("moe_layer", _layer_unweighted),
+    "rows descending in worklist": ("build_worklist", _worklist_rows_descending),
+    "residual dropped": ("moe_round", _round_no_residual),
+}
+
+
+def _all_pins():
+    calls = []
+    for name in dir(pins):
+        fn = getattr(pins, name)
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        if params:
+            argnames, values = params[0].args[0], params[0].args[1]
+            for v in list(values)[:3]:
+                if isinstance(argnames, str) and "," in argnames:
+                    kw = dict(zip([a.strip() for a in argnames.split(",")], v))
+                else:
+                    kw = {argnames: v}
+                calls.append((name, fn, kw))
+        else:
+            calls.append((name, fn, {}))
+    return calls
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_some_pin_catches(mutation, monkeypatch):
+    target, fake = MUTATIONS[mutation]
+    monkeypatch.setattr(om, target, fake)
+    monkeypatch.setattr(oracle, target, fake)
+    caught = []
+    for name, fn, kw in _all_pins():
+        try:
+            fn(**kw)
+        except (AssertionError, ValueError, IndexError, KeyError, TypeError):
+            caught.append(name)
+    assert caught, f"no pin caught the planted mistake: {mutation}"

@@ -1,0 +1,326 @@
+"""Pins for the fp64 oracle, each independent of the formula it checks.
+
+Hand-written golden blocks pin the weight format; exact sums, brute force and
+textbook routines pin the router and the selection; closed forms and
+explicit loops pin the expert; the dense all-experts formulation pins the
+combine; invariants pin the round and the worklist.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synth
+from conftest import read_golden
+
+
+# ---------------------------------------------------------------------------
+# helpers that build weights by hand (no oracle code)
+# ---------------------------------------------------------------------------
+
+def fp16_bits(v):
+    return int(np.array(v, dtype=np.float16).view(np.uint16))
+
+
+def const_matrix(rows, K, q, scale, minimum):
+    """A [rows][K] matrix whose every weight is scale*q + minimum, in the packed layout."""
+    byte = (q & 0xF) | ((q & 0xF) << 4)
+    codes = np.full((rows, K // 2), byte, dtype=np.uint8)
+    sm = np.full((rows, K // 32), fp16_bits(scale) | (fp16_bits(minimum) << 16), dtype=np.uint32)
+    return codes, sm
+
+
+def small_layer(E=6, H=64, I=32, seed=3, zipf=None):
+    cfg = synth.ShapeConfig("t", H=H, E=E, k=2, I=I, zipf_s=zipf)
+    return synth.make_layer(cfg, seed=seed, layer=0, device="cpu").numpy()
+
+
+# ---------------------------------------------------------------------------
+# weight format
+# ---------------------------------------------------------------------------
+
+def golden_blocks():
+    blocks, cur = [], None
+    for key, toks in read_golden("q4b32_blocks.txt"):
+        if key == "block":
+            cur = {"name": toks[0]}
+            blocks.append(cur)
+        elif key == "codes":
+            cur["codes"] = np.array([int(t, 16) for t in toks], dtype=np.uint8)
+        elif key == "scale_bits":
+            cur["s"] = int(toks[0], 16)
+        elif key == "min_bits":
+            cur["m"] = int(toks[0], 16)
+        elif key == "w":
+            cur["w"] = np.array([float(t) for t in toks])
+    return blocks
+
+
+def test_golden_blocks_dequantise_exactly():
+    blocks = golden_blocks()
+    assert len(blocks) == 3
+    for b in blocks:
+        sm = np.array([b["s"] | (b["m"] << 16)], dtype=np.uint32)
+        w = oracle.dequantize(b["codes"][None, :], sm[None, :])[0]
+        assert w.shape == (32,)
+        np.testing.assert_array_equal(w, b["w"], err_msg=b["name"])
+
+
+def test_golden_block_codes_and_multi_block_rows():
+    A, B, C = golden_blocks()
+    np.testing.assert_array_equal(oracle.unpack_codes(A["codes"]), np.arange(32) % 16)
+    # a row of three blocks: each block must use its own scale/min
+    codes = np.concatenate([A["codes"], B["codes"], C["codes"]])[None, :]
+    sm = np.array([[b["s"] | (b["m"] << 16) for b in (A, B, C)]], dtype=np.uint32)
+    w = oracle.dequantize(codes, sm)[0]
+    np.testing.assert_array_equal(w, np.concatenate([A["w"], B["w"], C["w"]]))
+
+
+def test_quantise_then_dequantise_is_within_half_a_step():
+    g = torch.Generator().manual_seed(11)
+    W = torch.randn((6, 256), generator=g) * 0.02
+    codes, sm = synth.quantize_q4b32(W)
+    deq = oracle.dequantize(codes.numpy(), sm.numpy().view(np.uint32))
+    Wd = W.double().numpy()
+    blocks = Wd.reshape(6, 8, 32)
+    mn = blocks.min(-1)
+    s16 = ((blocks.max(-1) - mn) / 15).astype(np.float32).astype(np.float16).astype(np.float64)
+    m16 = mn.astype(np.float32).astype(np.float16).astype(np.float64)
+    bound = 0.5 * s16 + np.abs(m16 - mn) + 1e-9
+    err = np.abs(deq - Wd).reshape(6, 8, 32)
+    assert np.all(err <= bound[..., None])
+    # rounding error of a uniform grid has rms ~ s/sqrt(12); a swapped or shifted nibble would not
+    assert np.sqrt(np.mean(err ** 2)) < 0.4 * s16.mean()
+
+
+# ---------------------------------------------------------------------------
+# router and selection
+# ---------------------------------------------------------------------------
+
+def test_router_logits_equal_exactly_rounded_sums():
+    rng = np.random.default_rng(5)
+    Wr = rng.standard_normal((5, 96)).astype(np.float32) * 0.02
+    x = rng.standard_normal(96).astype(np.float32)
+    b = rng.standard_normal(5).astype(np.float32)
+    z = oracle.router_logits(Wr, b, x)
+    for e in range(5):
+        terms = [float(Wr[e, h]) * float(x[h]) for h in range(96)]   # exact in fp64
+        ref = math.fsum(terms + [float(b[e])])
+        assert abs(z[e] - ref) <= 1e-14 * (sum(abs(t) for t in terms) + abs(float(b[e])))
+    z0 = oracle.router_logits(Wr, None, x)
+    for e in range(5):
+        ref = math.fsum(float(Wr[e, h]) * float(x[h]) for h in range(96))
+        assert abs(z0[e] - ref) <= 1e-14 * np.abs(Wr[e].astype(np.float64) * x).sum()
+
+
+@pytest.mark.parametrize("k", range(1, 8))
+def test_topk_matches_brute_force(k):
+    rng = np.random.default_rng(k)
+    for _ in range(20):
+        z = rng.standard_normal(7)
+        ids = oracle.select_topk(z, k)
+        best = max(itertools.combinations(range(7), k), key=lambda c: sum(z[list(c)]))
+        assert set(ids.tolist()) == set(best)
+        assert all(z[ids[i]] > z[ids[i + 1]] for i in range(k - 1))
+
+
+def test_topk_ties_go_to_lower_id():
+    z = np.array([1.0, 2.0, 2.0, 0.0, 2.0])
+    assert oracle.select_topk(z, 1).tolist() == [1]
+    assert oracle.select_topk(z, 2).tolist() == [1, 2]
+    assert oracle.select_topk(z, 3).tolist() == [1, 2, 4]
+    assert oracle.select_topk(z, 4).tolist() == [1, 2, 4, 0]
+    assert oracle.selection_gap(z, 2) == 0.0
+    assert oracle.selection_gap(np.array([3.0, 1.0, 0.5, -2.0]), 2) == 0.5
+
+
+def test_routing_weights_reduce_to_textbook_softmax():
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal(6) * 3
+    ids = oracle.select_topk(z, 6)
+    p = oracle.routing_weights(z, ids)
+    np.testing.assert_allclose(p, scipy.special.softmax(z)[ids], rtol=1e-14, atol=0)
+    assert oracle.routing_weights(z, oracle.select_topk(z, 1)).tolist() == [1.0]
+    i2 = oracle.select_topk(z, 2)
+    p2 = oracle.routing_weights(z, i2)
+    assert abs(p2[0] - scipy.special.expit(z[i2[0]] - z[i2[1]])) < 1e-15
+    assert abs(p2.sum() - 1.0) < 1e-15
+
+
+def test_silu_is_x_times_sigmoid():
+    a = np.linspace(-30, 30, 241)
+    np.testing.assert_allclose(oracle.silu(a), a * scipy.special.expit(a), rtol=1e-14, atol=1e-300)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# expert feed-forward
+# ---------------------------------------------------------------------------
+
+def test_closed_form_expert():
+    H, I = 64, 32
+    gq, gs = const_matrix(I, H, 1, 1.0, 0.0)     # gate: all ones
+    uq, us = const_matrix(I, H, 0, 0.0, 1.0)     # up: all ones, through the minimum
+    dq, ds = const_matrix(H, I, 1, 1.0, 0.0)     # down: all ones
+    for x0, x1 in ((1.0, 0.0), (0.5, 0.25), (-2.0, 0.5)):
+        x = np.zeros(H)
+        x[0], x[1] = x0, x1
+        S = x0 + x1
+        y = oracle.expert_forward(gq, gs, uq, us, dq, ds, x)
+        expect = I * (S / (1.0 + math.exp(-S))) * S
+        np.testing.assert_allclose(y, np.full(H, expect), rtol=1e-15)
+    dq2, ds2 = const_matrix(H, I, 1, 2.0, 0.0)   # down: all twos
+    x = np.zeros(H)
+    x[3] = 1.0
+    np.testing.assert_array_equal(oracle.expert_forward(gq, gs, uq, us, dq2, ds2, x),
+                                  2 * oracle.expert_forward(gq, gs, uq, us, dq, ds, x))
+
+
+def test_single_expert_layer_equals_explicit_loops():
+    L = small_layer(E=1, H=64, I=32, seed=21)
+    x = np.random.default_rng(2).standard_normal(64).astype(np.float32)
+    out, ids, p, _ = oracle.moe_layer(L, x[None, :], k=1)
+    assert ids.tolist() == [[0]] and p.tolist() == [[1.0]]
+    Wg = oracle.dequantize(L["gate_q"][0], L["gate_sm"][0])
+    Wu = oracle.dequantize(L["up_q"][0], L["up_sm"][0])
+    Wd = oracle.dequantize(L["down_q"][0], L["down_sm"][0])
+    h = []
+    for i in range(32):
+        g = sum(Wg[i, c] * float(x[c]) for c in range(64))
+        v = sum(Wu[i, c] * float(x[c]) for c in range(64))
+        h.append(g / (1.0 + math.exp(-g)) * v)
+    y = [sum(Wd[r, i] * h[i] for i in range(32)) for r in range(64)]
+    np.testing.assert_allclose(out[0], y, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# combine, round structure
+# ---------------------------------------------------------------------------
+
+def test_sparse_combine_equals_dense_all_experts():
+    E, H, I, T, k = 6, 64, 32, 3, 3
+    L = small_layer(E=E, H=H, I=I, seed=4, zipf=1.0)
+    X = np.random.default_rng(1).standard_normal((T, H)).astype(np.float32)
+    out, ids, p, _ = oracle.moe_layer(L, X, k)
+    # dense: evaluate every expert on every row, weight by a softmax restricted to the top-k mask
+    Y = np.stack([[oracle.expert_forward(L["gate_q"][e], L["gate_sm"][e], L["up_q"][e], L["up_sm"][e],
+                                         L["down_q"][e], L["down_sm"][e], X[t]) for e in range(E)]
+                  for t in range(T)])                                   # [T, E, H]
+    Z = X.astype(np.float64) @ L["router_w"].astype(np.float64).T + L["router_b"].astype(np.float64)
+    for t in range(T):
+        kth = np.sort(Z[t])[::-1][k - 1]
+        mask = Z[t] >= kth
+        assert mask.sum() == k
+        gate = np.where(mask, scipy.special.softmax(np.where(mask, Z[t], -np.inf)), 0.0)
+        np.testing.assert_allclose(out[t], gate @ Y[t], rtol=1e-12, atol=1e-14)
+        assert set(ids[t].tolist()) == set(np.nonzero(mask)[0].tolist())
+
+
+def test_round_equals_per_row_evaluations():
+    L = small_layer(E=8, H=64, I=32, seed=6)
+    X = np.random.default_rng(3).standard_normal((5, 64)).astype(np.float32)
+    out, ids, p, _ = oracle.moe_layer(L, X, k=2)
+    for t in range(5):
+        o1, i1, p1, _ = oracle.moe_layer(L, X[t:t + 1], k=2)
+        np.testing.assert_array_equal(o1[0], out[t])
+        np.testing.assert_array_equal(i1[0], ids[t])
+        np.testing.assert_array_equal(p1[0], p[t])
+
+
+def test_doubling_down_scale_and_min_doubles_output():
+    L = small_layer(E=5, H=64, I=32, seed=8)
+    X = np.random.default_rng(4).standard_normal((2, 64)).astype(np.float32)
+    out, *_ = oracle.moe_layer(L, X, k=2)
+    L2 = dict(L)
+    s, m = L["down_sm"] & 0xFFFF, L["down_sm"] >> 16
+    s2 = (s.astype(np.uint16).view(np.float16) * np.float16(2)).view(np.uint16).astype(np.uint32)
+    m2 = (m.astype(np.uint16).view(np.float16) * np.float16(2)).view(np.uint16).astype(np.uint32)
+    L2["down_sm"] = (s2 | (m2 << 16)).astype(np.uint32)
+    out2, *_ = oracle.moe_layer(L2, X, k=2)
+    np.testing.assert_array_equal(out2, 2 * out)
+
+
+def test_permuting_experts_permutes_ids_only():
+    E = 7
+    L = small_layer(E=E, H=64, I=32, seed=10, zipf=1.1)
+    X = np.random.default_rng(5).standard_normal((3, 64)).astype(np.float32)
+    out, ids, p, _ = oracle.moe_layer(L, X, k=3)
+    perm = np.random.default_rng(0).permutation(E)          # new expert i is old expert perm[i]
+    LP = {key: (None if v is None else v[perm]) for key, v in L.items()}
+    outP, idsP, pP, _ = oracle.moe_layer(LP, X, k=3)
+    np.testing.assert_array_equal(perm[idsP], ids)
+    np.testing.assert_array_equal(pP, p)
+    np.testing.assert_array_equal(outP, out)
+
+
+def test_residual_stack_is_layer_composition():
+    layers = [small_layer(E=6, H=64, I=32, seed=s) for s in (12, 13, 14)]
+    X = np.random.default_rng(6).standard_normal((2, 64)).astype(np.float32)
+    out, ids, p, gaps = oracle.moe_round(layers, X, k=2, residual=True)
+    x = X.astype(np.float64)
+    for li, L in enumerate(layers):
+        y, i, _, _ = oracle.moe_layer(L, x, k=2)
+        np.testing.assert_array_equal(i, ids[li])
+        x = x + y
+    np.testing.assert_array_equal(out, x)
+    assert ids.shape == (3, 2, 2) and gaps.shape == (3, 2)
+    with pytest.raises(ValueError):
+        oracle.moe_round(layers, X, k=2, residual=False)
+
+
+def test_router_bias_forces_selection():
+    L = small_layer(E=6, H=64, I=32, seed=15)
+    L["router_b"] = np.zeros(6, dtype=np.float32)
+    L["router_b"][4] = 100.0
+    X = np.random.default_rng(7).standard_normal((3, 64)).astype(np.float32)
+    _, ids, p, _ = oracle.moe_layer(L, X, k=2)
+    assert (ids[:, 0] == 4).all()
+    assert (p[:, 0] > 0.999).all()
+
+
+# ---------------------------------------------------------------------------
+# worklist
+# ---------------------------------------------------------------------------
+
+def golden_worklists():
+    cases, cur = [], None
+    parse = lambda toks: [[int(v) for v in grp.split()] for grp in " ".join(toks).split("/")]
+    for key, toks in read_golden("worklist_small.txt"):
+        if key == "ids":
+            cur = {"ids": np.array(parse(toks))}
+            cases.append(cur)
+        elif key in ("uniq", "offs"):
+            cur[key] = [int(v) for v in toks]
+        elif key == "pairs":
+            cur["pairs"] = parse(toks)
+    return cases
+
+
+def test_worklist_golden():
+    cases = golden_worklists()
+    assert len(cases) == 2
+    for c in cases:
+        uniq, offs, pairs = oracle.build_worklist(c["ids"])
+        assert uniq.tolist() == c["uniq"]
+        assert offs.tolist() == c["offs"]
+        assert pairs.tolist() == c["pairs"]
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 128), (3, 10, 512), (8, 8, 256), (64, 8, 256), (5, 2, 8)])
+def test_worklist_invariants(T, k, E):
+    rng = np.random.default_rng(T * 1000 + k)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    uniq, offs, pairs = oracle.build_worklist(ids)
+    union = sorted(set(ids.ravel().tolist()))
+    assert uniq.tolist() == union                     # n_unique == |union of per-row sets|
+    assert offs[0] == 0 and offs[-1] == T * k and np.all(np.diff(offs) >= 1)
+    seen = sorted(map(tuple, pairs.tolist()))
+    assert seen == [(t, j) for t in range(T) for j in range(k)]   # every pair exactly once
+    for u, e in enumerate(uniq):
+        seg = pairs[offs[u]:offs[u + 1]]
+        assert all(ids[t, j] == e for t, j in seg)
+        assert np.all(np.diff(seg[:, 0]) > 0)           # rows ascending within an expert
