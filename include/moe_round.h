@@ -1,0 +1,170 @@
+/*
+ * moe_round.h — C ABI of the MI355X (gfx950) MoE decode/verify round.
+ *
+ * One call evaluates the mixture-of-experts feed-forward of one decode or
+ * speculative-verify round over T token rows (1 <= T <= 64) and L stacked
+ * MoE layers.  Per layer, on the GPU:
+ *   router GEMV (fp32 weights and activations, fp64 accumulation) -> top-k
+ *   per row -> softmax over the k selected logits -> union of the rows'
+ *   experts as a deterministic worklist -> fused dequant-GEMV of the unique
+ *   experts' 4-bit gate/up weights with SwiGLU -> dequant-GEMV of their
+ *   down weights with the routing-weighted scatter-add back into each row.
+ *
+ * The pages this follows:
+ *   - "How AlphaInfer makes local decoding fast", section 2 (One captured
+ *     graph per decode round): a round is one forward pass over 1-8 rows,
+ *     recorded once as a graph and replayed; per-request data, including
+ *     which expert lives where, is ingress written into fixed buffers, and
+ *     the graph is never rebuilt.  Section 3.1: each extra verified row
+ *     routes to experts the other rows did not need, so it adds weight bytes.
+ *   - infero README, "Beyond plain text decode" (MoE bullet): top-k routing
+ *     at decode, counting sort of (row, expert) pairs into per-expert work.
+ *   - infero README, "Layout" figure: expert = silu(W_g x) * (W_u x) -> W_d.
+ *   - infero README, "Design notes": block-encoded weights are consumed in
+ *     place, never dequantised into memory; activations stay fp32.
+ *   - infero README, "Status" (tensor parallelism): unsupported requests are
+ *     refused outright rather than mishandled.
+ *
+ * Weight format (one matrix W[rows][K], K = reduction length, K % 32 == 0):
+ *   codes    uint8  [rows][K/2]  byte j holds element 2j in bits 0-3 and
+ *                                element 2j+1 in bits 4-7; 16-byte aligned
+ *   scalemin uint32 [rows][K/32] bits 0-15: fp16 scale s, bits 16-31: fp16
+ *                                minimum m; weight = s*q + m, q in 0..15
+ *   gate, up: [E][I][H] (K = H); down: [E][H][I] (K = I).
+ *   router: fp32 [E][H], optional fp32 bias [E].
+ *
+ * Memory: every pointer argument except `cfg`, `layers` and the host
+ * outputs of the introspection calls is DEVICE memory on the current HIP
+ * device.  Weights are caller-owned and borrowed: they must stay valid until
+ * the handle is destroyed or a later run names other weights.  The handle
+ * owns only its scratch.
+ *
+ * Errors: every call returns a moe_status; nothing aborts, prints or
+ * throws.  A rejected call leaves the handle unchanged.  After MOE_ERR_HIP
+ * the failing hipError_t is kept and returned by moe_round_last_hip_error.
+ *
+ * Threading: a handle is not re-entrant; use one handle per stream.
+ */
+#ifndef MOE_ROUND_H
+#define MOE_ROUND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ROUND_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_ROUND_API __attribute__((visibility("default")))
+#else
+#define MOE_ROUND_API
+#endif
+
+/* Supported set (outside it, init refuses with MOE_ERR_UNSUPPORTED).
+ * Block set: a reduction length K (H for gate/up, I for down) is supported when K/32 = G * NB
+ * with G the largest power of two <= 64 dividing K/32, G >= 4 and NB <= 4 (e.g. K = 128, 256,
+ * 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192).  G lanes share one weight row. */
+#define MOE_ROUND_MAX_ROWS 64      /* T_max */
+#define MOE_ROUND_MAX_EXPERTS 512  /* E     */
+#define MOE_ROUND_MAX_TOPK 16      /* k     */
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG -1  /* null/misaligned pointer, bad size, aliasing  */
+#define MOE_ERR_UNSUPPORTED -2  /* a shape outside the supported set            */
+#define MOE_ERR_HIP -3          /* a HIP runtime call failed                    */
+#define MOE_ERR_OOM -4          /* scratch allocation failed                    */
+#define MOE_ERR_STATE -5        /* call out of order (e.g. worklist before run) */
+
+typedef struct moe_round_config {
+  int32_t abi_version; /* must equal MOE_ROUND_ABI_VERSION                        */
+  int32_t hidden;      /* H: multiple of 256, at most 8192, H/32 in the block set */
+  int32_t inter;       /* I: multiple of 32, I/32 in the block set                */
+  int32_t n_experts;   /* E: 1..512                                               */
+  int32_t top_k_max;   /* largest k a run may ask for: 1..min(E, 16)              */
+  int32_t n_layers;    /* L >= 1                                                  */
+  int32_t max_rows;    /* T_max: 1..64                                            */
+  int32_t residual;    /* 0: out = MoE(x), needs L == 1; 1: x_{l+1} = x_l + MoE_l */
+  int32_t use_graph;   /* 1: replay one captured hipGraph per (T, k); 0: eager    */
+} moe_round_config;
+
+/* One layer's weights (device pointers, caller-owned). router_bias may be NULL. */
+typedef struct moe_layer_weights {
+  const float* router_w;     /* [E][H]                 */
+  const float* router_bias;  /* [E] or NULL            */
+  const uint8_t* gate_q;     /* [E][I][H/2]            */
+  const uint32_t* gate_sm;   /* [E][I][H/32]           */
+  const uint8_t* up_q;       /* [E][I][H/2]            */
+  const uint32_t* up_sm;     /* [E][I][H/32]           */
+  const uint8_t* down_q;     /* [E][H][I/2]            */
+  const uint32_t* down_sm;   /* [E][H][I/32]           */
+} moe_layer_weights;
+
+typedef struct moe_round moe_round; /* opaque handle */
+
+/* Pure host check of a configuration; touches no GPU. MOE_OK if init would accept its shape. */
+MOE_ROUND_API moe_status moe_round_validate_config(const moe_round_config* cfg);
+
+/*
+ * Create a handle: validates cfg and layers[0..L-1] (host array of structs holding device
+ * pointers), allocates scratch on the current device and binds the handle to `stream`
+ * (a hipStream_t; NULL = the null stream).  Graphs are captured lazily, once per (T, k).
+ */
+MOE_ROUND_API moe_status moe_round_init(const moe_round_config* cfg, const moe_layer_weights* layers,
+                          void* stream, moe_round** out);
+
+/*
+ * Run one round, asynchronously on the handle's stream.
+ *   hidden      device fp32 [T][H] input rows (read only; must not overlap `out`)
+ *   T, k        1 <= T <= max_rows, 1 <= k <= top_k_max
+ *   layers      host array [L] of new weight pointers, or NULL to keep the current ones
+ *               (new pointers are ingress: written into the handle's fixed table, no recapture)
+ *   out         device fp32 [T][H] result: MoE(x) (residual = 0) or x_L (residual = 1)
+ *   expert_ids  device int32 [L][T][k] selected experts per row, descending logit, or NULL
+ *   route_w     device fp32 [L][T][k] routing weights (softmax of the selected logits), or NULL
+ * Pointers must be 16-byte aligned.  Returns after enqueueing; no host synchronisation.
+ */
+MOE_ROUND_API moe_status moe_round_run(moe_round* h, const float* hidden, int32_t T, int32_t k,
+                         const moe_layer_weights* layers, float* out, int32_t* expert_ids,
+                         float* route_w);
+
+/*
+ * Introspection of the last run (synchronises the stream; host outputs).
+ *   n_unique     number of distinct experts layer `layer` touched
+ *   uniq         [n_unique] those experts, ascending                   (may be NULL)
+ *   offs         [n_unique + 1] exclusive prefix sum of rows per expert (may be NULL)
+ *   pairs        [T*k][2] (row t, rank j) grouped by expert, t ascending (may be NULL)
+ * Buffers must hold at least min(T*k, E) (uniq), that + 1 (offs) and 2*T*k (pairs) entries.
+ */
+MOE_ROUND_API moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t* n_unique, int32_t* uniq,
+                              int32_t* offs, int32_t* pairs);
+
+/* n_unique of every layer of the last run into host int32 [L] (synchronises the stream). */
+MOE_ROUND_API moe_status moe_round_last_unique(moe_round* h, int32_t* n_unique_per_layer);
+
+/*
+ * Eager run with a HIP event pair around every kernel, for measurement: same arguments as
+ * moe_round_run; synchronises; writes the per-kernel elapsed milliseconds into host float
+ * [L][4] (router logits, selection + worklist, gate/up, down).  May be called on a graph handle.
+ */
+MOE_ROUND_API moe_status moe_round_run_timed(moe_round* h, const float* hidden, int32_t T, int32_t k,
+                               const moe_layer_weights* layers, float* out, int32_t* expert_ids,
+                               float* route_w, float* kernel_ms);
+
+/* The hipError_t (as int) of the last MOE_ERR_HIP on this handle, 0 if none. */
+MOE_ROUND_API int32_t moe_round_last_hip_error(const moe_round* h);
+
+/* A static, human-readable description of a status code. */
+MOE_ROUND_API const char* moe_round_strerror(moe_status s);
+
+/* Free the handle's scratch and graphs. NULL is a no-op. Synchronises the handle's stream. */
+MOE_ROUND_API void moe_round_destroy(moe_round* h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUND_H */

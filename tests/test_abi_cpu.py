@@ -1,0 +1,130 @@
+"""The C ABI library loads and exports every declared symbol; host-side validation (no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moe_round.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from verify_router_gemv_amd import binding, build
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return binding.load()
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_ROUND_API\s+[\w\s\*]+?\b(moe_round_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    assert "moe_round_init" in names and "moe_round_run" in names and "moe_round_destroy" in names
+    assert len(names) == 9
+
+
+def test_library_exports_exactly_the_declared_symbols(lib):
+    from verify_router_gemv_amd import binding
+    for name in declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T moe_round_" in l)
+    assert exported == declared()
+
+
+def cfg(**kw):
+    from verify_router_gemv_amd import binding
+    base = dict(H=2048, I=512, E=256, top_k_max=8, n_layers=1, max_rows=8, residual=False, use_graph=True)
+    base.update(kw)
+    c = binding.make_config(base["H"], base["I"], base["E"], base["top_k_max"], base["n_layers"],
+                            base["max_rows"], base["residual"], base["use_graph"])
+    for k, v in kw.items():
+        if k.startswith("raw_"):
+            setattr(c, k[4:], v)
+    return c
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H=256, I=128, E=8, top_k_max=2, max_rows=1),
+    dict(H=2048, I=768, E=128, top_k_max=8, max_rows=1),
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=8),
+    dict(H=2048, I=512, E=512, top_k_max=10, n_layers=48, max_rows=3, residual=True),
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=64),
+    dict(H=768, I=384, E=40, top_k_max=5, max_rows=16),
+    dict(H=8192, I=2048, E=512, top_k_max=16, max_rows=64),
+])
+def test_supported_configs_validate(lib, kw):
+    from verify_router_gemv_amd import binding
+    assert binding.validate_config(cfg(**kw)) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(raw_abi_version=2), -1),
+    (dict(H=0), -1),
+    (dict(I=-32), -1),
+    (dict(E=0), -1),
+    (dict(top_k_max=0), -1),
+    (dict(max_rows=0), -1),
+    (dict(n_layers=2, residual=False), -1),
+    (dict(E=4, top_k_max=8), -1),
+    (dict(raw_use_graph=2), -1),
+    (dict(raw_residual=3), -1),
+    (dict(max_rows=65), -2),
+    (dict(E=513, top_k_max=8), -2),
+    (dict(top_k_max=17, E=256), -2),
+    (dict(H=2080), -2),          # not a multiple of 256
+    (dict(H=1280), -2),          # H/32 = 40 = 8 * 5: five blocks per lane
+    (dict(I=640), -2),           # I/32 = 20 = 4 * 5
+    (dict(I=96), -2),            # I/32 = 3: fewer than 4 lanes per row
+    (dict(H=16384), -2),
+])
+def test_unsupported_or_invalid_configs_are_refused(lib, kw, expect):
+    from verify_router_gemv_amd import binding
+    assert binding.validate_config(cfg(**kw)) == expect
+
+
+def test_null_and_bad_arguments_are_refused_before_any_gpu_call(lib):
+    from verify_router_gemv_amd import binding
+    h = ctypes.c_void_p()
+    c = cfg()
+    assert lib.moe_round_init(ctypes.byref(c), None, None, ctypes.byref(h)) == -1
+    assert lib.moe_round_init(None, None, None, ctypes.byref(h)) == -1
+    w = (binding.LayerWeights * 1)()
+    assert lib.moe_round_init(ctypes.byref(c), w, None, ctypes.byref(h)) == -1     # null weight pointers
+    w[0] = binding.LayerWeights(*([0x1000] * 8))
+    w[0].gate_q = 0x1008                                                            # misaligned codes
+    assert lib.moe_round_init(ctypes.byref(c), w, None, ctypes.byref(h)) == -1
+    bad = cfg(max_rows=65)
+    assert lib.moe_round_init(ctypes.byref(bad), w, None, ctypes.byref(h)) == -2
+    assert lib.moe_round_run(None, None, 1, 1, None, None, None, None) == -1
+    assert lib.moe_round_worklist(None, 0, None, None, None, None) == -1
+    assert lib.moe_round_last_unique(None, None) == -1
+    assert lib.moe_round_last_hip_error(None) == 0
+    lib.moe_round_destroy(None)
+
+
+def test_status_strings(lib):
+    from verify_router_gemv_amd import binding
+    assert binding.strerror(0) == "ok"
+    assert "unsupported" in binding.strerror(-2) or "supported" in binding.strerror(-2)
+    assert binding.strerror(-3) == "HIP runtime error"
+    assert binding.strerror(99) == "unknown status"
+
+
+def test_binding_refuses_host_tensors(lib):
+    from verify_router_gemv_amd import binding
+    E, H, I = 4, 256, 128
+    layer = dict(router_w=torch.zeros(E, H), router_b=None,
+                 gate_q=torch.zeros(E, I, H // 2, dtype=torch.uint8), gate_sm=torch.zeros(E, I, H // 32, dtype=torch.int32),
+                 up_q=torch.zeros(E, I, H // 2, dtype=torch.uint8), up_sm=torch.zeros(E, I, H // 32, dtype=torch.int32),
+                 down_q=torch.zeros(E, H, I // 2, dtype=torch.uint8), down_sm=torch.zeros(E, H, I // 32, dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        binding.layer_struct(layer, H, I, E)

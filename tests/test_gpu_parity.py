@@ -1,0 +1,180 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on every workload shape (needs an MI355X).
+
+Expert ids and the worklist must match bit-exactly; routing weights to fp32 rounding; the round's
+output within relative L2 1e-4 and max-abs 1e-3 * max|y|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from moe_helpers import GpuRound, assert_close, check_layer_round, errors, oracle_view, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = synth.config("tiny")
+    layer = synth.make_layer(cfg, seed=0, layer=0, device=DEV)
+    return cfg, layer, oracle_view(layer)
+
+
+def test_tiny_many_seeded_rounds(tiny):
+    cfg, layer, view = tiny
+    say("case tiny: 200 seeded rounds, T=1, k=2")
+    g = GpuRound([layer], cfg, max_rows=1)
+    worst = 0.0
+    for r in range(200):
+        X = synth.make_activations(cfg, 1, seed=0, round_idx=r, device=DEV)
+        rel, _, _ = check_layer_round(g, [view], X, cfg.k, f"tiny round {r}")
+        worst = max(worst, rel)
+    say(f"  worst rel-L2 {worst:.2e}")
+    g.close()
+
+
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_tiny_k_edges(tiny, k):
+    cfg, layer, view = tiny
+    say(f"case tiny k={k}")
+    g = GpuRound([layer], cfg, max_rows=4, k_max=8)
+    for T in (1, 4):
+        X = synth.make_activations(cfg, T, seed=1, round_idx=k, device=DEV)
+        check_layer_round(g, [view], X, k, f"tiny k={k} T={T}")
+        if k == 1:
+            _, _, rw, _ = g.run(X, k)
+            assert np.all(rw == 1.0)
+    g.close()
+
+
+@pytest.fixture(scope="module")
+def verify():
+    cfg = synth.config("verify")
+    layer = synth.make_layer(cfg, seed=0, layer=0, device=DEV)
+    return cfg, layer, oracle_view(layer)
+
+
+@pytest.mark.parametrize("use_graph", [True, False])
+def test_verify_sweep(verify, use_graph):
+    cfg, layer, view = verify
+    g = GpuRound([layer], cfg, max_rows=8, use_graph=use_graph)
+    for T in cfg.T:
+        for r in range(3):
+            say(f"case verify T={T} round {r} graph={use_graph}")
+            X = synth.make_activations(cfg, T, seed=0, round_idx=r, device=DEV)
+            rel, mabs, nu = check_layer_round(g, [view], X, cfg.k, f"verify T={T} r={r}")
+            say(f"  n_unique={nu[0]} rel-L2={rel:.2e} max-abs-frac={mabs:.2e}")
+    g.close()
+
+
+def test_decode(verify):
+    cfg = synth.config("decode")
+    layer = synth.make_layer(cfg, seed=0, layer=0, device=DEV)
+    view = oracle_view(layer)
+    g = GpuRound([layer], cfg, max_rows=1)
+    for r in range(4):
+        say(f"case decode round {r}")
+        X = synth.make_activations(cfg, 1, seed=0, round_idx=r, device=DEV)
+        rel, mabs, nu = check_layer_round(g, [view], X, cfg.k, f"decode r={r}")
+        say(f"  n_unique={nu[0]} rel-L2={rel:.2e}")
+    g.close()
+
+
+def test_wide(verify):
+    cfg = synth.config("wide")
+    # the wide workload has the verify shape (H, E, k, I) with independent rows
+    _, layer, view = verify
+    g = GpuRound([layer], cfg, max_rows=64)
+    for T in cfg.T:
+        say(f"case wide T={T}")
+        X = synth.make_activations(cfg, T, seed=0, round_idx=T, device=DEV)
+        rel, mabs, nu = check_layer_round(g, [view], X, cfg.k, f"wide T={T}")
+        say(f"  n_unique={nu[0]} rel-L2={rel:.2e}")
+    g.close()
+
+
+def test_rows_are_independent(verify):
+    """A row's output does not depend on the other rows of the round (within fp32 rounding)."""
+    cfg, layer, _ = verify
+    g = GpuRound([layer], cfg, max_rows=8)
+    X = synth.make_activations(cfg, 5, seed=3, round_idx=0, device=DEV)
+    say("case row independence T=5")
+    out, ids, _, _ = g.run(X)
+    for t in range(5):
+        o1, i1, _, _ = g.run(X[t:t + 1].contiguous())
+        assert np.array_equal(i1[0, 0], ids[0, t])
+        rel, mabs = errors(o1[0], out[t])
+        assert rel < 1e-6, rel
+    g.close()
+
+
+def test_weight_and_pointer_ingress(verify):
+    """New weight pointers and new hidden/out buffers are picked up without a recapture."""
+    cfg, layer, view = verify
+    other = synth.make_layer(cfg, seed=7, layer=0, device=DEV)
+    oview = oracle_view(other)
+    g = GpuRound([layer], cfg, max_rows=8)
+    X = synth.make_activations(cfg, 3, seed=0, round_idx=11, device=DEV)
+    say("case ingress: weights A")
+    check_layer_round(g, [view], X, cfg.k, "weights A")
+    say("case ingress: weights B via run(layers=...)")
+    out, ids, _, _ = g.run(X, layers=[other])
+    ref, rids, _, _ = oracle.moe_round([oview], X.cpu().numpy(), cfg.k, residual=False)
+    assert np.array_equal(ids[0], rids[0])
+    assert_close(out, ref, "weights B")
+    say("case ingress: weights B kept when layers=None, new buffers")
+    X2 = X.clone()
+    out2, ids2, _, _ = g.run(X2)
+    assert np.array_equal(ids2, ids)
+    assert_close(out2, ref, "weights B again")
+    g.close()
+
+
+def test_ragged_shape_paths():
+    """Other lane splits (H=768: 8 lanes x 3 blocks; I=384: 4 lanes x 3 blocks), ragged T, bias."""
+    cfg = synth.ShapeConfig("ragged", H=768, E=40, k=5, I=384, T=(1, 7, 13), zipf_s=0.7)
+    layer = synth.make_layer(cfg, seed=5, layer=0, device=DEV)
+    view = oracle_view(layer)
+    g = GpuRound([layer], cfg, max_rows=16)
+    for T in cfg.T:
+        say(f"case ragged H=768 I=384 E=40 k=5 T={T}")
+        X = synth.make_activations(cfg, T, seed=5, round_idx=T, device=DEV)
+        check_layer_round(g, [view], X, cfg.k, f"ragged T={T}")
+    g.close()
+
+
+def test_deep_stack_free_running():
+    """48 layers, residual, T=3: ids per layer bit-exact and the summed MoE output within tolerance."""
+    cfg = synth.config("deep")
+    say("case deep: generating 48 layers on the GPU")
+    layers = []
+    for l in range(cfg.L):
+        layers.append(synth.make_layer(cfg, seed=0, layer=l, device=DEV))
+        if l % 8 == 7:
+            say(f"  generated {l + 1} layers")
+    views = [oracle_view(l) for l in layers]
+    g = GpuRound(layers, cfg, max_rows=3)
+    checked = 0
+    for r in range(3):
+        X = synth.make_activations(cfg, 3, seed=0, round_idx=r, device=DEV)
+        say(f"case deep round {r}: oracle")
+        ref, rids, rp, gaps = oracle.moe_round(views, X.cpu().numpy(), cfg.k, residual=True)
+        if gaps.min() < 1e-5:
+            say(f"  round {r}: oracle selection gap {gaps.min():.2e} < 1e-5, ill-conditioned; skipped")
+            continue
+        say(f"case deep round {r}: GPU")
+        out, ids, rw, _ = g.run(X)
+        for l in range(cfg.L):
+            assert np.array_equal(ids[l], rids[l]), f"layer {l}"
+        Xh = X.cpu().numpy()
+        rel, mabs = assert_close(out - Xh, ref - Xh, f"deep round {r}")
+        say(f"  rel-L2 {rel:.2e}, n_unique per layer mean {np.mean(g.h.last_unique()):.1f}")
+        checked += 1
+        break
+    assert checked >= 1
+    g.close()
+    del layers
+    torch.cuda.empty_cache()

@@ -11,21 +11,21 @@ BLOCK = 32
 
 def _swap_nibbles(codes):
     codes = np.asarray(codes, dtype=np.uint8)
-    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.int64)
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.float64)
     out[..., 0::2] = codes >> 4
     out[..., 1::2] = codes & 0x0F
     return out
 
 
 def _dequant_no_min(codes, sm):
-    q = om.unpack_codes(codes).astype(np.float64)
+    q = om.unpack_codes(codes)
     s, m = om.unpack_scale_min(sm)
     blk = np.arange(q.shape[-1]) // BLOCK
     return s[..., blk] * q
 
 
 def _dequant_wrong_block(codes, sm):
-    q = om.unpack_codes(codes).astype(np.float64)
+    q = om.unpack_codes(codes)
     s, m = om.unpack_scale_min(sm)
     blk = (np.arange(q.shape[-1]) % s.shape[-1])
     return s[..., blk] * q + m[..., blk]
@@ -66,18 +66,20 @@ def _silu_sign(a):
     return a / (1.0 + np.exp(a))
 
 
-def _expert_silu_on_up(gq, gs, uq, us, dq, ds, x):
+def _ffn_silu_on_up(Wg, Wu, Wd, x):
     x = np.asarray(x, dtype=np.float64)
-    g = om.dequantize(gq, gs) @ x
-    v = om.dequantize(uq, us) @ x
-    return om.dequantize(dq, ds) @ (g * om.silu(v))
+    return Wd @ ((Wg @ x) * om.silu(Wu @ x))
 
 
-def _expert_add(gq, gs, uq, us, dq, ds, x):
+def _ffn_add(Wg, Wu, Wd, x):
     x = np.asarray(x, dtype=np.float64)
-    g = om.dequantize(gq, gs) @ x
-    v = om.dequantize(uq, us) @ x
-    return om.dequantize(dq, ds) @ (om.silu(g) + v)
+    return Wd @ (om.silu(Wg @ x) + Wu @ x)
+
+
+def _ffn_transposed_down(Wg, Wu, Wd, x):
+    x = np.asarray(x, dtype=np.float64)
+    h = om.silu(Wg @ x) * (Wu @ x)
+    return (Wd.reshape(Wd.shape[1], Wd.shape[0]) @ h) if Wd.shape[0] != Wd.shape[1] else Wd.T @ h
 
 
 def _worklist_rows_descending(ids):
@@ -89,15 +91,13 @@ def _worklist_rows_descending(ids):
 
 def _layer_unweighted(layer, X, k, residual=False):
     out, ids, p, gaps = ORIG["moe_layer"](layer, X, k, residual)
-    ones = np.ones_like(p)
-    out2 = np.zeros_like(out)
     X = np.asarray(X, dtype=np.float64)
+    out2 = np.zeros_like(out)
     for t in range(X.shape[0]):
         for j in range(k):
             e = int(ids[t, j])
-            out2[t] += ones[t, j] * om.expert_forward(layer["gate_q"][e], layer["gate_sm"][e], layer["up_q"][e],
-                                                      layer["up_sm"][e], layer["down_q"][e], layer["down_sm"][e],
-                                                      X[t])
+            out2[t] += om.expert_forward(layer["gate_q"][e], layer["gate_sm"][e], layer["up_q"][e],
+                                         layer["up_sm"][e], layer["down_q"][e], layer["down_sm"][e], X[t])
         if residual:
             out2[t] += X[t]
     return out2, ids, p, gaps
@@ -115,7 +115,8 @@ def _round_no_residual(layers, X, k, residual):
 
 ORIG = {name: getattr(om, name) for name in
         ("unpack_codes", "unpack_scale_min", "dequantize", "router_logits", "select_topk",
-         "routing_weights", "silu", "expert_forward", "moe_layer", "moe_round", "build_worklist")}
+         "routing_weights", "silu", "swiglu_ffn", "expert_forward", "moe_layer", "moe_round",
+         "build_worklist")}
 
 MUTATIONS = {
     "swapped nibbles": ("unpack_codes", _swap_nibbles),
@@ -128,8 +129,9 @@ MUTATIONS = {
     "ascending order": ("select_topk", _topk_ascending),
     "softmax over all experts": ("routing_weights", _softmax_all),
     "silu sign": ("silu", _silu_sign),
-    "silu on up": ("expert_forward", _expert_silu_on_up),
-    "add instead of multiply": ("expert_forward", _expert_add),
+    "silu on up": ("swiglu_ffn", _ffn_silu_on_up),
+    "add instead of multiply": ("swiglu_ffn", _ffn_add),
+    "down projection transposed": ("swiglu_ffn", _ffn_transposed_down),
     "unweighted combine": ("moe_layer", _layer_unweighted),
     "rows descending in worklist": ("build_worklist", _worklist_rows_descending),
     "residual dropped": ("moe_round", _round_no_residual),

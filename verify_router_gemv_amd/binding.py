@@ -1,0 +1,226 @@
+"""Thin ctypes binding over libmoe_round.so (argument marshalling only).
+
+Every step of the round runs in the HIP library; this module only checks tensor
+dtypes/shapes/devices, passes raw device pointers and maps status codes to
+exceptions.  PyTorch provides device memory and the stream.  If the library is
+not built, importing the binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_round.so")
+
+ABI_VERSION = 1
+MAX_ROWS = 64
+MAX_EXPERTS = 512
+MAX_TOPK = 16
+KERNELS_PER_LAYER = 4
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_OOM, ERR_STATE = 0, -1, -2, -3, -4, -5
+
+
+class MoeRoundError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{what}: {strerror(status)} (status {status}"
+        msg += f", hipError {hip_error})" if hip_error else ")"
+        super().__init__(msg)
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "abi_version", "hidden", "inter", "n_experts", "top_k_max", "n_layers", "max_rows",
+        "residual", "use_graph")]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "router_w", "router_bias", "gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it is missing: there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m verify_router_gemv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, vp = ctypes.c_int32, ctypes.c_void_p
+    P = ctypes.POINTER
+    sig = {
+        "moe_round_validate_config": (i32, [P(Config)]),
+        "moe_round_init": (i32, [P(Config), P(LayerWeights), vp, P(vp)]),
+        "moe_round_run": (i32, [vp, vp, i32, i32, P(LayerWeights), vp, vp, vp]),
+        "moe_round_run_timed": (i32, [vp, vp, i32, i32, P(LayerWeights), vp, vp, vp, P(ctypes.c_float)]),
+        "moe_round_worklist": (i32, [vp, i32, P(i32), P(i32), P(i32), P(i32)]),
+        "moe_round_last_unique": (i32, [vp, P(i32)]),
+        "moe_round_last_hip_error": (i32, [vp]),
+        "moe_round_strerror": (ctypes.c_char_p, [i32]),
+        "moe_round_destroy": (None, [vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    try:
+        return load().moe_round_strerror(status).decode()
+    except ImportError:
+        return f"status {status}"
+
+
+def make_config(H, I, E, top_k_max, n_layers=1, max_rows=8, residual=False, use_graph=True) -> Config:
+    return Config(ABI_VERSION, H, I, E, top_k_max, n_layers, max_rows, int(bool(residual)), int(bool(use_graph)))
+
+
+def validate_config(cfg: Config) -> int:
+    return load().moe_round_validate_config(ctypes.byref(cfg))
+
+
+_FIELDS = ("router_w", "router_bias", "gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")
+
+
+def _get(layer, name):
+    if isinstance(layer, dict):
+        return layer.get(name if name != "router_bias" else "router_b", layer.get(name))
+    return getattr(layer, "router_b" if name == "router_bias" else name)
+
+
+def _check(t: torch.Tensor, name: str, dtypes, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def layer_struct(layer, H: int, I: int, E: int) -> LayerWeights:
+    """Marshal one layer's weights (object or dict with the eight tensors) into the C struct."""
+    spec = {
+        "router_w": ((torch.float32,), (E, H)),
+        "router_bias": ((torch.float32,), (E,)),
+        "gate_q": ((torch.uint8,), (E, I, H // 2)),
+        "gate_sm": ((torch.int32, torch.uint32), (E, I, H // 32)),
+        "up_q": ((torch.uint8,), (E, I, H // 2)),
+        "up_sm": ((torch.int32, torch.uint32), (E, I, H // 32)),
+        "down_q": ((torch.uint8,), (E, H, I // 2)),
+        "down_sm": ((torch.int32, torch.uint32), (E, H, I // 32)),
+    }
+    ptrs = {}
+    for f in _FIELDS:
+        t = _get(layer, f)
+        if t is None and f == "router_bias":
+            ptrs[f] = None
+            continue
+        _check(t, f, *spec[f])
+        ptrs[f] = t.data_ptr()
+    return LayerWeights(*[ptrs[f] for f in _FIELDS])
+
+
+class MoeRound:
+    """A handle over the C ABI: one MoE round evaluator bound to a stream."""
+
+    def __init__(self, layers: Sequence, H: int, I: int, E: int, top_k_max: int, max_rows: int = 8,
+                 residual: bool = False, use_graph: bool = True, stream: Optional[torch.cuda.Stream] = None):
+        self.lib = load()
+        self.H, self.I, self.E, self.L = H, I, E, len(layers)
+        self.top_k_max, self.max_rows = top_k_max, max_rows
+        self.cfg = make_config(H, I, E, top_k_max, self.L, max_rows, residual, use_graph)
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self._layers = list(layers)          # keep the weight tensors alive
+        self._wt = (LayerWeights * self.L)(*[layer_struct(l, H, I, E) for l in layers])
+        h = ctypes.c_void_p()
+        st = self.lib.moe_round_init(ctypes.byref(self.cfg), self._wt, ctypes.c_void_p(self.stream.cuda_stream),
+                                     ctypes.byref(h))
+        if st != OK:
+            raise MoeRoundError(st, "moe_round_init")
+        self.h = h
+
+    def _raise(self, st, what):
+        raise MoeRoundError(st, what, self.lib.moe_round_last_hip_error(self.h))
+
+    def set_layers(self, layers: Sequence):
+        if len(layers) != self.L:
+            raise ValueError("layer count must not change")
+        self._layers = list(layers)
+        self._wt = (LayerWeights * self.L)(*[layer_struct(l, self.H, self.I, self.E) for l in layers])
+        return self._wt
+
+    def _run_args(self, hidden, k, out, ids, route_w, layers):
+        T = hidden.shape[0]
+        _check(hidden, "hidden", (torch.float32,), (T, self.H))
+        _check(out, "out", (torch.float32,), (T, self.H))
+        if ids is not None:
+            _check(ids, "expert_ids", (torch.int32,), (self.L, T, k))
+        if route_w is not None:
+            _check(route_w, "route_w", (torch.float32,), (self.L, T, k))
+        wt = self.set_layers(layers) if layers is not None else None
+        return (self.h, ctypes.c_void_p(hidden.data_ptr()), T, k, wt, ctypes.c_void_p(out.data_ptr()),
+                ctypes.c_void_p(ids.data_ptr() if ids is not None else 0),
+                ctypes.c_void_p(route_w.data_ptr() if route_w is not None else 0))
+
+    def run(self, hidden: torch.Tensor, k: int, out: torch.Tensor, ids: Optional[torch.Tensor] = None,
+            route_w: Optional[torch.Tensor] = None, layers: Optional[Sequence] = None):
+        st = self.lib.moe_round_run(*self._run_args(hidden, k, out, ids, route_w, layers))
+        if st != OK:
+            self._raise(st, "moe_round_run")
+
+    def run_timed(self, hidden, k, out, ids=None, route_w=None, layers=None):
+        """Eager run with HIP events around each kernel; returns [L][4] milliseconds
+        (router logits, selection + worklist, gate/up, down)."""
+        ms = (ctypes.c_float * (KERNELS_PER_LAYER * self.L))()
+        st = self.lib.moe_round_run_timed(*self._run_args(hidden, k, out, ids, route_w, layers), ms)
+        if st != OK:
+            self._raise(st, "moe_round_run_timed")
+        return [[ms[KERNELS_PER_LAYER * l + i] for i in range(KERNELS_PER_LAYER)] for l in range(self.L)]
+
+    def worklist(self, layer: int = 0):
+        T_k = self.max_rows * self.top_k_max
+        ucap = min(T_k, self.E)
+        n = ctypes.c_int32()
+        uniq = (ctypes.c_int32 * ucap)()
+        offs = (ctypes.c_int32 * (ucap + 1))()
+        pairs = (ctypes.c_int32 * (2 * T_k))()
+        st = self.lib.moe_round_worklist(self.h, layer, ctypes.byref(n), uniq, offs, pairs)
+        if st != OK:
+            self._raise(st, "moe_round_worklist")
+        nu = n.value
+        return list(uniq[:nu]), list(offs[:nu + 1]), [tuple(pairs[2 * i:2 * i + 2]) for i in range(offs[nu])]
+
+    def last_unique(self):
+        arr = (ctypes.c_int32 * self.L)()
+        st = self.lib.moe_round_last_unique(self.h, arr)
+        if st != OK:
+            self._raise(st, "moe_round_last_unique")
+        return list(arr)
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.moe_round_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

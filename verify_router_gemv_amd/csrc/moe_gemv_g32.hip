@@ -1,0 +1,6 @@
+// GEMV kernels (gate/up and down) for rows split over 32 lanes; see moe_kernels.h.
+#include "moe_kernels.h"
+
+namespace moe {
+bool pick_gemv_g32(int NB, int RC, bool up, KernelFn* fn, int* rows) { return pick_nb<32>(NB, RC, up, fn, rows); }
+}  // namespace moe

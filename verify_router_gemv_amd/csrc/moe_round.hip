@@ -1,0 +1,413 @@
+// MoE decode/verify round for MI355X (gfx950): the handle, launch plans and the C ABI.
+// The kernels are in moe_kernels.h; this file only validates, allocates, launches and captures.
+//
+// A round is replayed either eagerly (three launches per layer, ingress pointers passed by value)
+// or as one captured hipGraph per (T, k) whose kernels read the ingress pointers and the weight
+// table from fixed device buffers, so new per-request pointers never force a recapture
+// ("How AlphaInfer makes local decoding fast", section 2: per-request data is ingress written
+// into fixed buffers and the graph is never rebuilt).
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <map>
+#include <vector>
+
+#include "moe_internal.h"
+#include "moe_kernels.h"
+
+using namespace moe;
+
+// ------------------------------------------------------------------------------------------
+// Host side: the handle and the C ABI
+// ------------------------------------------------------------------------------------------
+
+namespace {
+
+struct Launch {
+  KernelFn fn;
+  dim3 grid;
+  int threads;
+  int shmem;
+  int layer;
+};
+
+constexpr int kKernelsPerLayer = 4;  // logits, select, gate/up, down
+
+struct GraphEntry {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+constexpr int kStagingSlots = 16;
+
+}  // namespace
+
+struct moe_round {
+  moe_round_config cfg{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  int Ucap = 0, Pcap = 0;
+  int Gh = 0, NBh = 0, Gi = 0, NBi = 0;
+  // device scratch
+  Ingress* d_ing = nullptr;            // graph-mode ingress
+  moe_layer_weights* d_wtab = nullptr; // graph-mode weight table [L]
+  float* xbuf[2] = {nullptr, nullptr};
+  double* logits = nullptr;
+  int32_t* n_unique = nullptr;
+  int32_t* uniq = nullptr;
+  int32_t* offs = nullptr;
+  int32_t* pairs = nullptr;
+  float* pair_w = nullptr;
+  int32_t* rec = nullptr;
+  float* hbuf = nullptr;
+  // host state
+  Ingress h_ing{};                     // last ingress of a run
+  bool dev_ing_valid = false;          // d_ing holds h_ing
+  std::vector<moe_layer_weights> h_wtab;
+  bool dev_wtab_valid = false;         // d_wtab holds h_wtab
+  unsigned char* staging = nullptr;    // pinned ring for graph-mode ingress uploads
+  size_t slot_bytes = 0;
+  hipEvent_t slot_ev[kStagingSlots] = {};
+  bool slot_used[kStagingSlots] = {};
+  int next_slot = 0;
+  std::map<int, GraphEntry> graphs;
+  int last_T = 0, last_k = 0;
+  int32_t last_hip = 0;
+};
+
+static moe_status hip_fail(moe_round* h, hipError_t e) {
+  if (h) h->last_hip = static_cast<int32_t>(e);
+  return e == hipErrorOutOfMemory ? MOE_ERR_OOM : MOE_ERR_HIP;
+}
+
+#define MOE_HIP(h, call)                              \
+  do {                                                \
+    hipError_t _e = (call);                           \
+    if (_e != hipSuccess) return hip_fail((h), _e);   \
+  } while (0)
+
+static int xstage_rows(int K) {
+  const int r = kXStageBytes / (static_cast<int>(sizeof(float)) * K);
+  return r < 1 ? 1 : (r > kXStageMax ? kXStageMax : r);
+}
+
+static Args base_args(const moe_round* h, int T, int k) {
+  Args a{};
+  a.xbuf0 = h->xbuf[0];
+  a.xbuf1 = h->xbuf[1];
+  a.logits = h->logits;
+  a.n_unique = h->n_unique;
+  a.uniq = h->uniq;
+  a.offs = h->offs;
+  a.pairs = h->pairs;
+  a.pair_w = h->pair_w;
+  a.rec = h->rec;
+  a.hbuf = h->hbuf;
+  a.H = h->cfg.hidden;
+  a.I = h->cfg.inter;
+  a.E = h->cfg.n_experts;
+  a.L = h->cfg.n_layers;
+  a.T = T;
+  a.k = k;
+  a.residual = h->cfg.residual;
+  a.Ucap = h->Ucap;
+  a.Pcap = h->Pcap;
+  a.xstage_h = xstage_rows(h->cfg.hidden);
+  a.xstage_i = xstage_rows(h->cfg.inter);
+  return a;
+}
+
+static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
+  const int E = h->cfg.n_experts, H = h->cfg.hidden, I = h->cfg.inter;
+  const int umax = (T * k < E) ? T * k : E;
+  const int RC = rows_per_pass(T);
+  KernelFn lg = pick_logits(H, T), sel = pick_select(E), gu = nullptr, dn = nullptr;
+  int rows_gu = 0, rows_dn = 0;
+  if (!lg || !pick_gemv(h->Gh, h->NBh, RC, true, &gu, &rows_gu) ||
+      !pick_gemv(h->Gi, h->NBi, RC, false, &dn, &rows_dn))
+    return false;
+  const int tc = logits_rows(T);
+  const dim3 grid_lg((E + kRouteExpertsPerBlock - 1) / kRouteExpertsPerBlock, (T + tc - 1) / tc);
+  const dim3 grid_gu(umax * ((I + rows_gu - 1) / rows_gu));
+  const dim3 grid_dn(umax * ((H + rows_dn - 1) / rows_dn));
+  const int shm_gu = T > 1 ? static_cast<int>(sizeof(float)) * xstage_rows(H) * H : 0;
+  const int shm_dn = T > 1 ? static_cast<int>(sizeof(float)) * xstage_rows(I) * I : 0;
+  out->clear();
+  for (int l = 0; l < h->cfg.n_layers; ++l) {
+    out->push_back({lg, grid_lg, kThreads, 0, l});
+    out->push_back({sel, dim3(1), kSelectThreads, 0, l});
+    out->push_back({gu, grid_gu, kThreads, shm_gu, l});
+    out->push_back({dn, grid_dn, kThreads, shm_dn, l});
+  }
+  return true;
+}
+
+static moe_status build_graph(moe_round* h, int T, int k, GraphEntry* ge) {
+  std::vector<Launch> ls;
+  if (!plan(h, T, k, &ls)) return MOE_ERR_UNSUPPORTED;
+  Args a = base_args(h, T, k);
+  a.ing = h->d_ing;
+  a.wtab = h->d_wtab;
+  hipGraph_t g = nullptr;
+  MOE_HIP(h, hipGraphCreate(&g, 0));
+  hipGraphNode_t prev = nullptr;
+  for (const Launch& L : ls) {
+    int layer = L.layer;
+    void* params[] = {&a, &layer};
+    hipKernelNodeParams p{};
+    p.func = reinterpret_cast<void*>(L.fn);
+    p.gridDim = L.grid;
+    p.blockDim = dim3(L.threads);
+    p.sharedMemBytes = L.shmem;
+    p.kernelParams = params;
+    p.extra = nullptr;
+    hipGraphNode_t node = nullptr;
+    hipError_t e = hipGraphAddKernelNode(&node, g, prev ? &prev : nullptr, prev ? 1 : 0, &p);
+    if (e != hipSuccess) {
+      (void)hipGraphDestroy(g);
+      return hip_fail(h, e);
+    }
+    prev = node;
+  }
+  hipGraphExec_t x = nullptr;
+  hipError_t e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_fail(h, e);
+  }
+  ge->graph = g;
+  ge->exec = x;
+  return MOE_OK;
+}
+
+// Eager: every launch carries the ingress pointers and its layer's weights by value.
+static moe_status launch_eager(moe_round* h, int T, int k, hipEvent_t* evs) {
+  std::vector<Launch> ls;
+  if (!plan(h, T, k, &ls)) return MOE_ERR_UNSUPPORTED;
+  Args a = base_args(h, T, k);
+  a.in = h->h_ing;
+  int i = 0;
+  for (const Launch& L : ls) {
+    a.w = h->h_wtab[L.layer];
+    int layer = L.layer;
+    void* params[] = {&a, &layer};
+    if (evs) MOE_HIP(h, hipEventRecord(evs[2 * i], h->stream));
+    MOE_HIP(h, hipLaunchKernel(reinterpret_cast<const void*>(L.fn), L.grid, dim3(L.threads), params, L.shmem,
+                               h->stream));
+    if (evs) MOE_HIP(h, hipEventRecord(evs[2 * i + 1], h->stream));
+    ++i;
+  }
+  return MOE_OK;
+}
+
+// Graph mode: upload changed ingress pointers and/or the weight table through a pinned slot.
+static moe_status sync_device_ingress(moe_round* h) {
+  const size_t wbytes = sizeof(moe_layer_weights) * h->cfg.n_layers;
+  if (h->dev_ing_valid && h->dev_wtab_valid) return MOE_OK;
+  const int s = h->next_slot;
+  h->next_slot = (s + 1) % kStagingSlots;
+  if (h->slot_used[s]) MOE_HIP(h, hipEventSynchronize(h->slot_ev[s]));
+  unsigned char* slot = h->staging + static_cast<size_t>(s) * h->slot_bytes;
+  if (!h->dev_ing_valid) {
+    std::memcpy(slot, &h->h_ing, sizeof(Ingress));
+    MOE_HIP(h, hipMemcpyAsync(h->d_ing, slot, sizeof(Ingress), hipMemcpyHostToDevice, h->stream));
+    h->dev_ing_valid = true;
+  }
+  if (!h->dev_wtab_valid) {
+    std::memcpy(slot + 256, h->h_wtab.data(), wbytes);
+    MOE_HIP(h, hipMemcpyAsync(h->d_wtab, slot + 256, wbytes, hipMemcpyHostToDevice, h->stream));
+    h->dev_wtab_valid = true;
+  }
+  MOE_HIP(h, hipEventRecord(h->slot_ev[s], h->stream));
+  h->slot_used[s] = true;
+  return MOE_OK;
+}
+
+static void free_handle(moe_round* h) {
+  if (!h) return;
+  if (h->stream) (void)hipStreamSynchronize(h->stream);
+  for (auto& kv : h->graphs) {
+    if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
+    if (kv.second.graph) (void)hipGraphDestroy(kv.second.graph);
+  }
+  for (int i = 0; i < kStagingSlots; ++i)
+    if (h->slot_ev[i]) (void)hipEventDestroy(h->slot_ev[i]);
+  if (h->staging) (void)hipHostFree(h->staging);
+  void* ptrs[] = {h->d_ing, h->d_wtab, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique,
+                  h->uniq, h->offs, h->pairs, h->pair_w, h->rec, h->hbuf};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  delete h;
+}
+
+extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_layer_weights* layers,
+                                     void* stream, moe_round** out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  moe_status st = validate_config(cfg);
+  if (st != MOE_OK) return st;
+  st = validate_layers(cfg, layers);
+  if (st != MOE_OK) return st;
+
+  moe_round* h = new moe_round();
+  h->cfg = *cfg;
+  h->stream = static_cast<hipStream_t>(stream);
+  split_blocks(cfg->hidden, &h->Gh, &h->NBh);
+  split_blocks(cfg->inter, &h->Gi, &h->NBi);
+  const int T = cfg->max_rows, E = cfg->n_experts, K = cfg->top_k_max, L = cfg->n_layers;
+  const int H = cfg->hidden, I = cfg->inter;
+  h->Pcap = T * K;
+  h->Ucap = (T * K < E) ? T * K : E;
+  h->h_wtab.assign(layers, layers + L);
+
+  auto fail = [&](hipError_t e) {
+    moe_status s = hip_fail(h, e);
+    free_handle(h);
+    return s;
+  };
+  hipError_t e;
+  if ((e = hipGetDevice(&h->device)) != hipSuccess) return fail(e);
+#define MOE_ALLOC(ptr, bytes) \
+  if ((e = hipMalloc(reinterpret_cast<void**>(&(ptr)), (bytes))) != hipSuccess) return fail(e);
+  MOE_ALLOC(h->d_ing, sizeof(Ingress));
+  MOE_ALLOC(h->d_wtab, sizeof(moe_layer_weights) * L);
+  MOE_ALLOC(h->xbuf[0], sizeof(float) * T * H);
+  MOE_ALLOC(h->xbuf[1], sizeof(float) * T * H);
+  MOE_ALLOC(h->logits, sizeof(double) * T * E);
+  MOE_ALLOC(h->n_unique, sizeof(int32_t) * L);
+  MOE_ALLOC(h->uniq, sizeof(int32_t) * L * h->Ucap);
+  MOE_ALLOC(h->offs, sizeof(int32_t) * L * (h->Ucap + 1));
+  MOE_ALLOC(h->pairs, sizeof(int32_t) * L * h->Pcap);
+  MOE_ALLOC(h->pair_w, sizeof(float) * L * h->Pcap);
+  MOE_ALLOC(h->rec, sizeof(int32_t) * L * h->Ucap * kRecWords);
+  MOE_ALLOC(h->hbuf, sizeof(float) * h->Pcap * I);
+#undef MOE_ALLOC
+  h->slot_bytes = 256 + ((sizeof(moe_layer_weights) * L + 255) / 256) * 256;
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->staging), h->slot_bytes * kStagingSlots, 0)) !=
+      hipSuccess)
+    return fail(e);
+  for (int i = 0; i < kStagingSlots; ++i)
+    if ((e = hipEventCreateWithFlags(&h->slot_ev[i], hipEventDisableTiming)) != hipSuccess) return fail(e);
+  if ((e = hipMemsetAsync(h->n_unique, 0, sizeof(int32_t) * L, h->stream)) != hipSuccess) return fail(e);
+  if ((e = hipMemsetAsync(h->rec, 0, sizeof(int32_t) * L * h->Ucap * kRecWords, h->stream)) != hipSuccess)
+    return fail(e);
+  if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return fail(e);
+  *out = h;
+  return MOE_OK;
+}
+
+static moe_status prepare_run(moe_round* h, const float* hidden, int32_t T, int32_t k,
+                              const moe_layer_weights* layers, float* out, int32_t* ids, float* rw) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  moe_status st = validate_run(&h->cfg, hidden, T, k, out, ids, rw);
+  if (st != MOE_OK) return st;
+  if (layers) {
+    st = validate_layers(&h->cfg, layers);
+    if (st != MOE_OK) return st;
+    if (std::memcmp(layers, h->h_wtab.data(), sizeof(moe_layer_weights) * h->cfg.n_layers) != 0) {
+      std::memcpy(h->h_wtab.data(), layers, sizeof(moe_layer_weights) * h->cfg.n_layers);
+      h->dev_wtab_valid = false;
+    }
+  }
+  const Ingress ing{hidden, out, ids, rw};
+  if (std::memcmp(&ing, &h->h_ing, sizeof(Ingress)) != 0) {
+    h->h_ing = ing;
+    h->dev_ing_valid = false;
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_run(moe_round* h, const float* hidden, int32_t T, int32_t k,
+                                    const moe_layer_weights* layers, float* out, int32_t* expert_ids,
+                                    float* route_w) {
+  moe_status st = prepare_run(h, hidden, T, k, layers, out, expert_ids, route_w);
+  if (st != MOE_OK) return st;
+  if (h->cfg.use_graph) {
+    st = sync_device_ingress(h);
+    if (st != MOE_OK) return st;
+    const int key = T * 64 + k;
+    auto it = h->graphs.find(key);
+    if (it == h->graphs.end()) {
+      GraphEntry ge;
+      st = build_graph(h, T, k, &ge);
+      if (st != MOE_OK) return st;
+      it = h->graphs.emplace(key, ge).first;
+    }
+    MOE_HIP(h, hipGraphLaunch(it->second.exec, h->stream));
+  } else {
+    st = launch_eager(h, T, k, nullptr);
+    if (st != MOE_OK) return st;
+  }
+  h->last_T = T;
+  h->last_k = k;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_run_timed(moe_round* h, const float* hidden, int32_t T, int32_t k,
+                                          const moe_layer_weights* layers, float* out, int32_t* expert_ids,
+                                          float* route_w, float* kernel_ms) {
+  if (!kernel_ms) return MOE_ERR_INVALID_ARG;
+  moe_status st = prepare_run(h, hidden, T, k, layers, out, expert_ids, route_w);
+  if (st != MOE_OK) return st;
+  const int n = kKernelsPerLayer * h->cfg.n_layers;
+  std::vector<hipEvent_t> evs(2 * n, nullptr);
+  for (auto& ev : evs)
+    if (hipEventCreate(&ev) != hipSuccess) {
+      for (auto& e2 : evs)
+        if (e2) (void)hipEventDestroy(e2);
+      return MOE_ERR_HIP;
+    }
+  st = launch_eager(h, T, k, evs.data());
+  hipError_t e = hipSuccess;
+  if (st == MOE_OK) e = hipEventSynchronize(evs[2 * n - 1]);
+  if (st == MOE_OK && e == hipSuccess) {
+    for (int i = 0; i < n && e == hipSuccess; ++i) e = hipEventElapsedTime(&kernel_ms[i], evs[2 * i], evs[2 * i + 1]);
+  }
+  for (auto& ev : evs) (void)hipEventDestroy(ev);
+  if (st != MOE_OK) return st;
+  if (e != hipSuccess) return hip_fail(h, e);
+  h->last_T = T;
+  h->last_k = k;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t* n_unique, int32_t* uniq,
+                                         int32_t* offs, int32_t* pairs) {
+  if (!h || !n_unique) return MOE_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= h->cfg.n_layers) return MOE_ERR_INVALID_ARG;
+  if (h->last_T == 0) return MOE_ERR_STATE;
+  MOE_HIP(h, hipStreamSynchronize(h->stream));
+  int32_t nu = 0;
+  MOE_HIP(h, hipMemcpy(&nu, h->n_unique + layer, sizeof(int32_t), hipMemcpyDeviceToHost));
+  *n_unique = nu;
+  if (nu < 0 || nu > h->Ucap) return MOE_ERR_STATE;
+  if (uniq && nu)
+    MOE_HIP(h, hipMemcpy(uniq, h->uniq + static_cast<size_t>(layer) * h->Ucap, sizeof(int32_t) * nu,
+                         hipMemcpyDeviceToHost));
+  if (offs)
+    MOE_HIP(h, hipMemcpy(offs, h->offs + static_cast<size_t>(layer) * (h->Ucap + 1), sizeof(int32_t) * (nu + 1),
+                         hipMemcpyDeviceToHost));
+  if (pairs) {
+    const int np = h->last_T * h->last_k;
+    std::vector<int32_t> packed(np);
+    MOE_HIP(h, hipMemcpy(packed.data(), h->pairs + static_cast<size_t>(layer) * h->Pcap, sizeof(int32_t) * np,
+                         hipMemcpyDeviceToHost));
+    for (int i = 0; i < np; ++i) {
+      pairs[2 * i] = packed[i] & 0xFF;
+      pairs[2 * i + 1] = (packed[i] >> 8) & 0xFF;
+    }
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_last_unique(moe_round* h, int32_t* n_unique_per_layer) {
+  if (!h || !n_unique_per_layer) return MOE_ERR_INVALID_ARG;
+  if (h->last_T == 0) return MOE_ERR_STATE;
+  MOE_HIP(h, hipStreamSynchronize(h->stream));
+  MOE_HIP(h, hipMemcpy(n_unique_per_layer, h->n_unique, sizeof(int32_t) * h->cfg.n_layers, hipMemcpyDeviceToHost));
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_round_last_hip_error(const moe_round* h) { return h ? h->last_hip : 0; }
+
+extern "C" void moe_round_destroy(moe_round* h) { free_handle(h); }
