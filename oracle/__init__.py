@@ -15,6 +15,8 @@ from .moe_oracle import (  # noqa: F401
     selection_gap,
     routing_weights,
     silu,
+    expert_matrices,
+    swiglu_ffn,
     expert_forward,
     moe_layer,
     moe_round,

@@ -43,13 +43,11 @@ BLOCK = 32
 # ---------------------------------------------------------------------------
 
 def unpack_codes(codes: np.ndarray) -> np.ndarray:
-    """uint8 [..., K/2] -> int64 [..., K]: element 2j is byte j's low nibble, 2j+1 its high nibble."""
+    """uint8 [..., K/2] -> float64 [..., K]: element 2j is byte j's low nibble, 2j+1 its high nibble."""
     codes = np.asarray(codes, dtype=np.uint8)
-    lo = (codes & 0x0F).astype(np.int64)
-    hi = (codes >> 4).astype(np.int64)
-    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.int64)
-    out[..., 0::2] = lo
-    out[..., 1::2] = hi
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.float64)
+    out[..., 0::2] = codes & 0x0F
+    out[..., 1::2] = codes >> 4
     return out
 
 
@@ -63,11 +61,11 @@ def unpack_scale_min(sm: np.ndarray):
 
 def dequantize(codes: np.ndarray, sm: np.ndarray) -> np.ndarray:
     """W[r, c] = s[r, c//32] * q[r, c] + m[r, c//32], exact in fp64 (an 11-bit x 4-bit product plus an fp16)."""
-    q = unpack_codes(codes).astype(np.float64)
+    q = unpack_codes(codes)
     s, m = unpack_scale_min(sm)
     K = q.shape[-1]
-    blk = np.arange(K) // BLOCK
-    return s[..., blk] * q + m[..., blk]
+    qb = q.reshape(q.shape[:-1] + (K // BLOCK, BLOCK))
+    return (s[..., None] * qb + m[..., None]).reshape(q.shape)
 
 
 # ---------------------------------------------------------------------------
@@ -114,16 +112,23 @@ def silu(a: np.ndarray) -> np.ndarray:
     return a / (1.0 + np.exp(-a))
 
 
-def expert_forward(gate_q, gate_sm, up_q, up_sm, down_q, down_sm, x: np.ndarray) -> np.ndarray:
-    """One expert on one row: y = W_d (silu(W_g x) * (W_u x)), weights dequantised in fp64."""
+def expert_matrices(gate_q, gate_sm, up_q, up_sm, down_q, down_sm):
+    """Dequantise one expert: (W_g [I,H], W_u [I,H], W_d [H,I]) in fp64."""
+    return dequantize(gate_q, gate_sm), dequantize(up_q, up_sm), dequantize(down_q, down_sm)
+
+
+def swiglu_ffn(Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """y = W_d (silu(W_g x) * (W_u x))."""
     x = np.asarray(x, dtype=np.float64)
-    Wg = dequantize(gate_q, gate_sm)      # [I, H]
-    Wu = dequantize(up_q, up_sm)          # [I, H]
-    Wd = dequantize(down_q, down_sm)      # [H, I]
     g = Wg @ x
     v = Wu @ x
     h = silu(g) * v
     return Wd @ h
+
+
+def expert_forward(gate_q, gate_sm, up_q, up_sm, down_q, down_sm, x: np.ndarray) -> np.ndarray:
+    """One expert on one row, from its packed weights."""
+    return swiglu_ffn(*expert_matrices(gate_q, gate_sm, up_q, up_sm, down_q, down_sm), x)
 
 
 def _expert_arrays(layer: dict, e: int):
@@ -157,8 +162,8 @@ def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False):
         for j in range(k):
             e = int(sel[j])
             if e not in cache:
-                cache[e] = _expert_arrays(layer, e)
-            acc = acc + w[j] * expert_forward(*cache[e], X[t])
+                cache[e] = expert_matrices(*_expert_arrays(layer, e))
+            acc = acc + w[j] * swiglu_ffn(*cache[e], X[t])
         out[t] = X[t] + acc if residual else acc
         ids[t] = sel
         p[t] = w
