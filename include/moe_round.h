@@ -142,6 +142,13 @@ MOE_ROUND_API moe_status moe_round_run(moe_round* h, const float* hidden, int32_
 MOE_ROUND_API moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t* n_unique, int32_t* uniq,
                               int32_t* offs, int32_t* pairs);
 
+/*
+ * The gate/up stage's output of the last run's last layer, silu(W_g x_t) * (W_u x_t), one fp32 row of
+ * length I per (row, rank) pair in worklist order (pair slot p = the p-th entry of `pairs` above),
+ * into host float [T*k][I] (synchronises the stream).
+ */
+MOE_ROUND_API moe_status moe_round_swiglu_rows(moe_round* h, float* host_rows);
+
 /* n_unique of every layer of the last run into host int32 [L] (synchronises the stream). */
 MOE_ROUND_API moe_status moe_round_last_unique(moe_round* h, int32_t* n_unique_per_layer);
 

@@ -28,7 +28,7 @@ def declared():
 def test_header_declares_the_boundary():
     names = declared()
     assert "moe_round_init" in names and "moe_round_run" in names and "moe_round_destroy" in names
-    assert len(names) == 9
+    assert len(names) == 10
 
 
 def test_library_exports_exactly_the_declared_symbols(lib):

@@ -96,6 +96,27 @@ def test_wide(verify):
     g.close()
 
 
+@pytest.mark.parametrize("name,T", [("tiny", 1), ("verify", 1), ("verify", 3), ("verify", 8)])
+def test_gateup_stage(name, T, tiny, verify):
+    """The gate/up stage alone: silu(W_g x) * (W_u x) per (row, rank) pair against the oracle."""
+    cfg, layer, view = tiny if name == "tiny" else verify
+    say(f"case gate/up stage {name} T={T}")
+    g = GpuRound([layer], cfg, max_rows=max(T, 1))
+    X = synth.make_activations(cfg, T, seed=2, round_idx=T, device=DEV)
+    out, ids, _, _ = g.run(X)
+    h = g.h.swiglu_rows(T, cfg.k)
+    uniq, offs, pairs = g.h.worklist(0)
+    Xh = X.cpu().numpy().astype(np.float64)
+    ref = np.zeros_like(h, dtype=np.float64)
+    for p, (t, j) in enumerate(pairs):
+        e = int(ids[0, t, j])
+        Wg, Wu, _ = oracle.expert_matrices(view["gate_q"][e], view["gate_sm"][e], view["up_q"][e], view["up_sm"][e],
+                                           view["down_q"][e], view["down_sm"][e])
+        ref[p] = oracle.silu(Wg @ Xh[t]) * (Wu @ Xh[t])
+    assert_close(h, ref, f"gate/up {name} T={T}")
+    g.close()
+
+
 def test_rows_are_independent(verify):
     """A row's output does not depend on the other rows of the round (within fp32 rounding)."""
     cfg, layer, _ = verify

@@ -65,6 +65,7 @@ def load() -> ctypes.CDLL:
         "moe_round_run_timed": (i32, [vp, vp, i32, i32, P(LayerWeights), vp, vp, vp, P(ctypes.c_float)]),
         "moe_round_worklist": (i32, [vp, i32, P(i32), P(i32), P(i32), P(i32)]),
         "moe_round_last_unique": (i32, [vp, P(i32)]),
+        "moe_round_swiglu_rows": (i32, [vp, P(ctypes.c_float)]),
         "moe_round_last_hip_error": (i32, [vp]),
         "moe_round_strerror": (ctypes.c_char_p, [i32]),
         "moe_round_destroy": (None, [vp]),
@@ -206,6 +207,15 @@ class MoeRound:
             self._raise(st, "moe_round_worklist")
         nu = n.value
         return list(uniq[:nu]), list(offs[:nu + 1]), [tuple(pairs[2 * i:2 * i + 2]) for i in range(offs[nu])]
+
+    def swiglu_rows(self, T: int, k: int):
+        """The last run's last-layer gate/up output: [T*k][I] rows in worklist pair order."""
+        import numpy as np
+        buf = np.zeros((T * k, self.I), dtype=np.float32)
+        st = self.lib.moe_round_swiglu_rows(self.h, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+        if st != OK:
+            self._raise(st, "moe_round_swiglu_rows")
+        return buf
 
     def last_unique(self):
         arr = (ctypes.c_int32 * self.L)()

@@ -40,6 +40,11 @@ constexpr int kSelectWaves = kSelectThreads / 64;
 // [3] number of unique experts of the layer, [4..19] the rows' ids, one byte each, in slot order.
 constexpr int kRecWords = 32;
 constexpr int kRecRowWord = 4;
+// A 32-block of activations as three signed int8 digits of a 24-bit integer: x ~ step * (d2*65536 +
+// d1*256 + d0). Words [digit d][group g of 8][even/odd]: the even word packs elements 8g+0,2,4,6, the
+// odd word 8g+1,3,5,7, matching the nibble order of a weight code word.
+constexpr int kXqWords = 24;
+constexpr float kXqMax = 8355711.0f;  // 127*65536 + 127*256 + 127
 constexpr int kXStageMax = 8;        // activation rows staged in LDS at a time (T > 1) ...
 constexpr int kXStageBytes = 65536;  // ... within 64 KB of LDS
 
@@ -67,6 +72,8 @@ struct Args {
   float* pair_w;      // [L][Pcap]
   int32_t* rec;       // [L][Ucap][kRecWords] per-unique-expert records
   float* hbuf;        // [Pcap][I]
+  uint32_t* xq;       // [T_max][H/32][kXqWords] int8 digits of the layer input, per 32-block
+  float2* xss;        // [T_max][H/32] (digit step, block sum) of the layer input
   int32_t H, I, E, L, T, k, residual, Ucap, Pcap;
   int32_t xstage_h, xstage_i;  // activation rows staged in LDS at a time (gate/up: rows of H, down: of I)
 };
@@ -112,17 +119,28 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __builtin_bit_cast(double, dpp_u64<CTRL>(__builtin_bit_cast(uint64_t, v)));
 }
 
+// gfx950 lane swaps, written as inline asm: the compiler's two-result builtins for these were
+// observed to wire both results to one register when the inputs differ (sum s[0] + s[1] compiled
+// to s[0] + s[0]). Both operands are read and written: v_permlane32_swap exchanges lanes 32-63 of
+// `a` with lanes 0-31 of `b`; v_permlane16_swap exchanges the odd 16-lane rows of `a` with the
+// even rows of `b`. The s_nop covers the VALU-write -> swap-read hazard.
+__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
 // Exchange with the lane 16 (X16) or 32 (X32) apart: returns the partner's value.
 template <bool X32>
 __device__ __forceinline__ uint32_t swap_partner_u32(uint32_t v) {
+  uint32_t a = v, b = v;
   if constexpr (X32) {
-    auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    // s[0]: [lo half, lo half], s[1]: [hi half, hi half]; the partner is the other half
-    return (__lane_id() < 32) ? s[1] : s[0];
+    permlane32_swap(a, b);  // a: [lo half, lo half], b: [hi half, hi half]
+    return (__lane_id() < 32) ? b : a;
   } else {
-    auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    // s[0]: rows [r0, r0, r2, r2], s[1]: rows [r1, r1, r3, r3]
-    return ((__lane_id() >> 4) & 1) ? s[0] : s[1];
+    permlane16_swap(a, b);  // a: rows [r0, r0, r2, r2], b: rows [r1, r1, r3, r3]
+    return ((__lane_id() >> 4) & 1) ? a : b;
   }
 }
 template <bool X32>
@@ -174,12 +192,35 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Full sums over 64 lanes of 8 values at once (a transposed butterfly): the xor-32 and xor-16
+// levels pair values through the permlane swaps, so each level halves the registers instead of
+// repeating per value; the last four levels run inside 16-lane rows. Afterwards every lane of row
+// R (lanes 16R..16R+15) holds in `lo` the total of v[{0,2,1,3}[R]] and in `hi` of v[{4,6,5,7}[R]].
+__device__ __forceinline__ float pair_sum32(float a, float b) {
+  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
+  permlane32_swap(x, y);  // x: [a lo, b lo], y: [a hi, b hi]
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float pair_sum16(float a, float b) {
+  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
+  permlane16_swap(x, y);  // x: rows [a0, b0, a2, b2], y: rows [a1, b1, a3, b3]
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ void reduce8_wave(const float v[8], float& lo, float& hi) {
+  const float s01 = pair_sum32(v[0], v[1]), s23 = pair_sum32(v[2], v[3]);
+  const float s45 = pair_sum32(v[4], v[5]), s67 = pair_sum32(v[6], v[7]);
+  lo = group_sum<16>(pair_sum16(s01, s23));
+  hi = group_sum<16>(pair_sum16(s45, s67));
+}
+__device__ __forceinline__ int reduce8_slot(int row) { return (row == 1) ? 2 : (row == 2 ? 1 : row); }
+
 // ------------------------------------------------------------------------------------------
 // Small helpers
 // ------------------------------------------------------------------------------------------
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define MOE_GLOBAL __attribute__((address_space(1)))
 
@@ -207,18 +248,35 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
 }
 
-// 32 codes of one block (16 bytes, byte j = element 2j | element 2j+1 << 4) -> floats in order.
+// Single-instruction byte -> float conversions (v_cvt_f32_ubyte0..3).
+#define MOE_CVT_UBYTE(N)                                                            \
+  __device__ __forceinline__ float cvt_ubyte##N(uint32_t v) {                       \
+    float r;                                                                        \
+    asm("v_cvt_f32_ubyte" #N " %0, %1" : "=v"(r) : "v"(v));                         \
+    return r;                                                                       \
+  }
+MOE_CVT_UBYTE(0)
+MOE_CVT_UBYTE(1)
+MOE_CVT_UBYTE(2)
+MOE_CVT_UBYTE(3)
+#undef MOE_CVT_UBYTE
+
+// 32 codes of one block (16 bytes, byte j = element 2j | element 2j+1 << 4) -> floats in order,
+// 11 VALU instructions per 8 codes.
 __device__ __forceinline__ void unpack_block(const uint4 c, float q[32]) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = w[i] & 0x0F0F0F0Fu;
-    const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      q[8 * i + 2 * b] = static_cast<float>((lo >> (8 * b)) & 0xFFu);
-      q[8 * i + 2 * b + 1] = static_cast<float>((hi >> (8 * b)) & 0xFFu);
-    }
+    const uint32_t lo = w[i] & 0x0F0F0F0Fu;         // elements 8i+0, +2, +4, +6
+    const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;  // elements 8i+1, +3, +5, +7
+    q[8 * i + 0] = cvt_ubyte0(lo);
+    q[8 * i + 1] = cvt_ubyte0(hi);
+    q[8 * i + 2] = cvt_ubyte1(lo);
+    q[8 * i + 3] = cvt_ubyte1(hi);
+    q[8 * i + 4] = cvt_ubyte2(lo);
+    q[8 * i + 5] = cvt_ubyte2(hi);
+    q[8 * i + 6] = cvt_ubyte3(lo);
+    q[8 * i + 7] = cvt_ubyte3(hi);
   }
 }
 
@@ -251,6 +309,49 @@ __device__ __forceinline__ uint64_t logit_key(double z, int e) {
 __device__ __forceinline__ int key_expert(uint64_t key) { return 511 - static_cast<int>(key & 0x1FFull); }
 
 
+// Digits of one 32-block (see kXqWords). The integer q = rint(x / step) with step = max|x| / kXqMax
+// is split into balanced base-256 digits d0, d1, d2 in [-127, 127]; the block sum is kept in fp32.
+__device__ __forceinline__ void quantize_block(const float* src, uint32_t* dst, float2* ss) {
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float4 f = load_f4(src + 4 * q);
+    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+  }
+  float mx = 0.f, sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) { mx = fmaxf(mx, fabsf(v[i])); sum += v[i]; }
+  const float inv = mx > 0.f ? kXqMax / mx : 0.f;
+  uint32_t d[3][8];  // digit planes, 4 bytes per word in element order 0..31
+#pragma unroll
+  for (int w = 0; w < 8; ++w) { d[0][w] = 0u; d[1][w] = 0u; d[2][w] = 0u; }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    int q = static_cast<int>(rintf(v[i] * inv));
+    q = max(-static_cast<int>(kXqMax), min(static_cast<int>(kXqMax), q));
+    const int d0 = ((q + 128) & 255) - 128;
+    const int q1 = (q - d0) >> 8;
+    const int d1 = ((q1 + 128) & 255) - 128;
+    const int d2 = (q1 - d1) >> 8;
+    const int w = i >> 2, sh = 8 * (i & 3);
+    d[0][w] |= (static_cast<uint32_t>(d0) & 0xFFu) << sh;
+    d[1][w] |= (static_cast<uint32_t>(d1) & 0xFFu) << sh;
+    d[2][w] |= (static_cast<uint32_t>(d2) & 0xFFu) << sh;
+  }
+  // regroup each 8-element group into even (0,2,4,6) and odd (1,3,5,7) words
+#pragma unroll
+  for (int dg = 0; dg < 3; ++dg)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t a0 = d[dg][2 * g], a1 = d[dg][2 * g + 1];  // bytes of elements 8g..8g+3, 8g+4..8g+7
+      const uint32_t even = __builtin_amdgcn_perm(a1, a0, 0x06040200u);  // bytes e0 e2 | e4 e6
+      const uint32_t odd = __builtin_amdgcn_perm(a1, a0, 0x07050301u);   // bytes e1 e3 | e5 e7
+      dst[(dg * 4 + g) * 2 + 0] = even;
+      dst[(dg * 4 + g) * 2 + 1] = odd;
+    }
+  *ss = make_float2(mx / kXqMax, sum);
+}
+
 // ------------------------------------------------------------------------------------------
 // Kernel 1: router logits (+ output seeding)
 // ------------------------------------------------------------------------------------------
@@ -282,13 +383,17 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
   }
   const double bias = W.router_bias ? static_cast<double>(W.router_bias[e]) : 0.0;
 
-  // Seed this layer's output rows with the residual (deep stack) or zeros (blocks of row-chunk 0).
+  // Blocks of row-chunk 0 also seed this layer's output rows with the residual (deep stack) or
+  // zeros, and write the layer input as int8 digits per 32-block for the gate/up kernel.
   if (blockIdx.y == 0) {
     const int n4 = T * H / 4;
     const float4* x4 = reinterpret_cast<const float4*>(x);
     float4* xn4 = reinterpret_cast<float4*>(xn);
     for (int i = blockIdx.x * kThreads + tid; i < n4; i += gridDim.x * kThreads)
       xn4[i] = a.residual ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int nblk = H / 32;
+    for (int i = blockIdx.x * kThreads + tid; i < T * nblk; i += gridDim.x * kThreads)
+      quantize_block(x + static_cast<size_t>(i) * 32, a.xq + static_cast<size_t>(i) * kXqWords, a.xss + i);
   }
 
   double acc[TC];
@@ -319,7 +424,6 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
 struct SelectShared {
   int sel[MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK];     // [t][j] expert id
   float p[MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK];     // [t][j] routing weight
-  double z[MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK];    // [t][j] selected logit
   unsigned long long mask[MOE_ROUND_MAX_EXPERTS];      // rows choosing expert e
   int uidx[MOE_ROUND_MAX_EXPERTS];                     // e -> unique index
   int uniq[MOE_ROUND_MAX_EXPERTS];
@@ -329,45 +433,49 @@ struct SelectShared {
   int nu;
 };
 
-// Top-k of one row on one wave: k rounds of a wave-wide unsigned max over (logit, id) keys, then
-// the softmax of the k selected logits in fp64. NPL = logits per lane (E <= 64 * NPL).
+// Top-k of one row on one wave. Each lane sorts its NPL (logit, id) keys once; then k rounds of a
+// wave-wide unsigned max over the lanes' heads, the winning lane popping its head. Lane j records the
+// j-th id and re-reads its exact fp64 logit for the softmax over the k selected logits.
 template <int NPL>
 __device__ __forceinline__ void select_row(const Args& a, SelectShared& s, int t) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
-  double zv[NPL];
+  const double* zrow = a.logits + static_cast<size_t>(t) * E;
   uint64_t key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    zv[i] = a.logits[static_cast<size_t>(t) * E + min(e, E - 1)];  // all loads issued together
+    const double z = zrow[min(e, E - 1)];  // all loads issued together
+    key[i] = e < E ? logit_key(z, e) : 0ull;  // 0 is below every real key
   }
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? logit_key(zv[i], e) : 0ull;  // 0 is below every real key
-  }
+  for (int pass = 0; pass < NPL; ++pass)
+#pragma unroll
+    for (int i = pass & 1; i + 1 < NPL; i += 2)
+      if (key[i] < key[i + 1]) {
+        const uint64_t tmp = key[i];
+        key[i] = key[i + 1];
+        key[i + 1] = tmp;
+      }
+  int myid = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < NPL; ++i) best = umax64(best, key[i]);
-    best = wave_max_u64(best);
+    const uint64_t best = wave_max_u64(key[0]);
     const int e = key_expert(best);
     if (lane == (e & 63)) {
 #pragma unroll
-      for (int i = 0; i < NPL; ++i)
-        if (i == (e >> 6)) {
-          s.z[t * k + j] = zv[i];
-          key[i] = 0ull;
-        }
+      for (int i = 0; i + 1 < NPL; ++i) key[i] = key[i + 1];
+      key[NPL - 1] = 0ull;
     }
-    if (lane == 0) s.sel[t * k + j] = e;
+    if (lane == j) myid = e;
   }
-  const double zj = lane < k ? s.z[t * k + lane] : 0.0;
-  const double z0 = s.z[t * k];
+  const double zj = zrow[lane < k ? myid : 0];
+  const double z0 = __shfl(zj, 0, 64);  // rank 0 holds the largest selected logit
   const double ej = lane < k ? exp(zj - z0) : 0.0;
   const double sum = wave_sum_f64(ej);
-  if (lane < k) s.p[t * k + lane] = static_cast<float>(ej / sum);
+  if (lane < k) {
+    s.sel[t * k + lane] = myid;
+    s.p[t * k + lane] = static_cast<float>(ej / sum);
+  }
 }
 
 template <int NPL>
@@ -573,13 +681,42 @@ __device__ __forceinline__ void stage_rows(float* lds, const float* src, int K, 
   }
 }
 
-template <int G, int NB, int RC, int RW>
+// Gate/up: integer dot products of the 4-bit codes with the int8 digits of the layer input.
+// Codes are unpacked once into bytes (even / odd elements of each 8-group) and kept in registers;
+// each row routed to the expert then costs 24 v_dot4 per 32-weight block plus the fp32 fold
+// s * step * (65536 A2 + 256 A1 + A0) + m * sum(x).
+__device__ __forceinline__ float block_dot_q8(const uint32_t cw[8], const uint32_t xd[kXqWords], float step,
+                                              float xsum, uint32_t sm, float acc) {
+  int A[3] = {0, 0, 0};
+#pragma unroll
+  for (int dg = 0; dg < 3; ++dg)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      A[dg] = __builtin_amdgcn_sdot4(static_cast<int>(cw[2 * g]), static_cast<int>(xd[(dg * 4 + g) * 2]), A[dg], false);
+      A[dg] = __builtin_amdgcn_sdot4(static_cast<int>(cw[2 * g + 1]), static_cast<int>(xd[(dg * 4 + g) * 2 + 1]),
+                                     A[dg], false);
+    }
+  const float dot = fmaf(static_cast<float>(A[2]), 65536.f, fmaf(static_cast<float>(A[1]), 256.f, static_cast<float>(A[0])));
+  const float sc = half_bits_to_float(sm), mn = half_bits_to_float(sm >> 16);
+  return fmaf(sc * step, dot, fmaf(mn, xsum, acc));
+}
+
+__device__ __forceinline__ void unpack_bytes(const uint4 c, uint32_t cw[8]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cw[2 * i] = w[i] & 0x0F0F0F0Fu;
+    cw[2 * i + 1] = (w[i] >> 4) & 0x0F0F0F0Fu;
+  }
+}
+
+template <int G, int NB, int RW>
 __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
   constexpr int RPI = 64 / G;
   constexpr int ROWS_W = RW * RPI;
   constexpr int ROWS_B = kWaves * ROWS_W;
-  extern __shared__ float xlds[];  // [xstage_h][H] when T > 1
   const int I = a.I, H = a.H, T = a.T;
+  const int nblk = H / 32;
   const int tiles = (I + ROWS_B - 1) / ROWS_B;
   const int u = blockIdx.x / tiles, tile = blockIdx.x - u * tiles;
   const ExpertWork wk = load_work(a, layer, u);
@@ -587,9 +724,7 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane % G, rs = lane / G;
-  const Ingress in = get_ingress(a);
   const moe_layer_weights W = get_weights(a, layer);
-  const float* __restrict__ x = layer_input(a, in, layer);
   const int row0 = tile * ROWS_B + wave * ROWS_W + rs;
   const size_t rq = static_cast<size_t>(H) / 2, rsm = static_cast<size_t>(H) / 32;
 
@@ -608,53 +743,72 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
     }
   }
 
-  const int xst = T > 1 ? a.xstage_h : MOE_ROUND_MAX_ROWS;
-  for (int s0 = 0; s0 < wk.np; s0 += xst) {
-    const int ns = min(xst, wk.np - s0);
-    const float* src = x;
-    if (T > 1) {
-      __syncthreads();
-      stage_rows(xlds, x, H, ns, [&](int r) { return work_row(wk, s0 + r, T); });
-      __syncthreads();
-      src = xlds;
+  // Activation digits of one row: NB blocks x 24 words plus (step, block sum).
+  uint32_t xd[NB][kXqWords];
+  float xstep[NB], xsum[NB];
+#define MOE_LOAD_ROW(R)                                                                      \
+  {                                                                                          \
+    const int t_ = work_row(wk, (R), T);                                                     \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                      \
+      const size_t blk = static_cast<size_t>(t_) * nblk + g + nb * G;                        \
+      const MOE_GLOBAL u32x4* src = (const MOE_GLOBAL u32x4*)(a.xq + blk * kXqWords);        \
+      _Pragma("unroll") for (int q = 0; q < kXqWords / 4; ++q) {                             \
+        const u32x4 v = src[q];                                                              \
+        xd[nb][4 * q + 0] = v.x;                                                             \
+        xd[nb][4 * q + 1] = v.y;                                                             \
+        xd[nb][4 * q + 2] = v.z;                                                             \
+        xd[nb][4 * q + 3] = v.w;                                                             \
+      }                                                                                      \
+      const f32x2 ss = *((const MOE_GLOBAL f32x2*)(a.xss + blk));                            \
+      xstep[nb] = ss.x;                                                                      \
+      xsum[nb] = ss.y;                                                                       \
+    }                                                                                        \
+  }
+  MOE_LOAD_ROW(0)
+
+  uint32_t wg[RW][NB][8], wu[RW][NB][8];
+#pragma unroll
+  for (int w = 0; w < RW; ++w)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      unpack_bytes(cg[w][nb], wg[w][nb]);
+      unpack_bytes(cu[w][nb], wu[w][nb]);
     }
-    for (int c = 0; c < ns; c += RC) {
-      int row_of[RC];
+
+  for (int r = 0; r < wk.np; ++r) {
+    float acc[2 * RW];
 #pragma unroll
-      for (int r = 0; r < RC; ++r) row_of[r] = (T > 1) ? min(c + r, ns - 1) : work_row(wk, 0, T);
-      float xv[RC][NB][32], xs[RC][NB];
-      if (T > 1) load_x<NB, RC, G, true>(src, H, row_of, ns - c, g, xv, xs);
-      else load_x<NB, RC, G, false>(src, H, row_of, ns - c, g, xv, xs);
+    for (int w = 0; w < RW; ++w) {
+      float ag = 0.f, au = 0.f;
 #pragma unroll
-      for (int w = 0; w < RW; ++w)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) { opaque(cg[w][nb]); opaque(cu[w][nb]); }
-      float ag[RW][RC], au[RW][RC];
-#pragma unroll
-      for (int w = 0; w < RW; ++w) {
-        block_dots<NB, RC>(cg[w], sg[w], xv, xs, ag[w]);
-        block_dots<NB, RC>(cu[w], su[w], xv, xs, au[w]);
+      for (int nb = 0; nb < NB; ++nb) {
+        ag = block_dot_q8(wg[w][nb], xd[nb], xstep[nb], xsum[nb], sg[w][nb], ag);
+        au = block_dot_q8(wu[w][nb], xd[nb], xstep[nb], xsum[nb], su[w][nb], au);
       }
+      acc[w] = ag;       // gate partials: acc[0 .. RW-1]
+      acc[RW + w] = au;  // up partials:   acc[RW .. 2RW-1]
+    }
+    if (r + 1 < wk.np) MOE_LOAD_ROW(r + 1)  // uniform branch: the next row's digits, after this row's use
+    float* hrow = a.hbuf + static_cast<size_t>(wk.p0 + r) * I;
+    if constexpr (G == 64 && RW == 4) {
+      float gsum, usum;
+      reduce8_wave(acc, gsum, usum);
+      const int R = lane >> 4;
+      const int i = row0 + reduce8_slot(R);  // RPI == 1: row group w is row row0 + w
+      if ((lane & 15) == 0 && i < I) hrow[i] = silu(gsum) * usum;
+    } else {
 #pragma unroll
-      for (int w = 0; w < RW; ++w)
-#pragma unroll
-        for (int r = 0; r < RC; ++r) {
-          ag[w][r] = group_sum<G>(ag[w][r]);
-          au[w][r] = group_sum<G>(au[w][r]);
-        }
+      for (int w = 0; w < 2 * RW; ++w) acc[w] = group_sum<G>(acc[w]);
       if (g == 0) {
 #pragma unroll
         for (int w = 0; w < RW; ++w) {
           const int i = row0 + w * RPI;
-          if (i >= I) continue;
-#pragma unroll
-          for (int r = 0; r < RC; ++r)
-            if (c + r < ns)
-              a.hbuf[static_cast<size_t>(wk.p0 + s0 + c + r) * I + i] = silu(ag[w][r]) * au[w][r];
+          if (i < I) hrow[i] = silu(acc[w]) * acc[RW + w];
         }
       }
     }
   }
+#undef MOE_LOAD_ROW
 }
 
 template <int G, int NB, int RC, int RW>
@@ -751,18 +905,23 @@ constexpr int rows_per_lane_group(int NB) { return NB == 1 ? 4 : (NB == 2 ? 2 : 
 template <int G, int NB, int RC>
 struct GemvPick {
   static constexpr int RW = rows_per_lane_group(NB);
-  static KernelFn gateup() { return gateup_kernel<G, NB, RC, RW>; }
+  static KernelFn gateup() { return gateup_kernel<G, NB, RW>; }
   static KernelFn down() { return down_kernel<G, NB, RC, RW>; }
   static constexpr int rows_per_block() { return kWaves * RW * (64 / G); }
 };
 
 template <int G, int NB>
 inline bool pick_rc(int RC, bool up, KernelFn* fn, int* rows) {
+  if (up) {  // gate/up walks the expert's rows one at a time; no pass width
+    *fn = GemvPick<G, NB, 1>::gateup();
+    *rows = GemvPick<G, NB, 1>::rows_per_block();
+    return true;
+  }
   switch (RC) {
-#define MOE_RC(R)                                                          \
-  case R:                                                                  \
-    *fn = up ? GemvPick<G, NB, R>::gateup() : GemvPick<G, NB, R>::down(); \
-    *rows = GemvPick<G, NB, R>::rows_per_block();                          \
+#define MOE_RC(R)                                 \
+  case R:                                         \
+    *fn = GemvPick<G, NB, R>::down();             \
+    *rows = GemvPick<G, NB, R>::rows_per_block(); \
     return true;
     MOE_RC(1) MOE_RC(2) MOE_RC(4)
 #undef MOE_RC

@@ -60,6 +60,8 @@ struct moe_round {
   float* pair_w = nullptr;
   int32_t* rec = nullptr;
   float* hbuf = nullptr;
+  uint32_t* xq = nullptr;
+  float2* xss = nullptr;
   // host state
   Ingress h_ing{};                     // last ingress of a run
   bool dev_ing_valid = false;          // d_ing holds h_ing
@@ -103,6 +105,8 @@ static Args base_args(const moe_round* h, int T, int k) {
   a.pair_w = h->pair_w;
   a.rec = h->rec;
   a.hbuf = h->hbuf;
+  a.xq = h->xq;
+  a.xss = h->xss;
   a.H = h->cfg.hidden;
   a.I = h->cfg.inter;
   a.E = h->cfg.n_experts;
@@ -130,7 +134,7 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   const dim3 grid_lg((E + kRouteExpertsPerBlock - 1) / kRouteExpertsPerBlock, (T + tc - 1) / tc);
   const dim3 grid_gu(umax * ((I + rows_gu - 1) / rows_gu));
   const dim3 grid_dn(umax * ((H + rows_dn - 1) / rows_dn));
-  const int shm_gu = T > 1 ? static_cast<int>(sizeof(float)) * xstage_rows(H) * H : 0;
+  const int shm_gu = 0;  // gate/up reads the input digits from global memory (L2)
   const int shm_dn = T > 1 ? static_cast<int>(sizeof(float)) * xstage_rows(I) * I : 0;
   out->clear();
   for (int l = 0; l < h->cfg.n_layers; ++l) {
@@ -234,7 +238,7 @@ static void free_handle(moe_round* h) {
     if (h->slot_ev[i]) (void)hipEventDestroy(h->slot_ev[i]);
   if (h->staging) (void)hipHostFree(h->staging);
   void* ptrs[] = {h->d_ing, h->d_wtab, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique,
-                  h->uniq, h->offs, h->pairs, h->pair_w, h->rec, h->hbuf};
+                  h->uniq, h->offs, h->pairs, h->pair_w, h->rec, h->hbuf, h->xq, h->xss};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete h;
@@ -281,6 +285,8 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   MOE_ALLOC(h->pair_w, sizeof(float) * L * h->Pcap);
   MOE_ALLOC(h->rec, sizeof(int32_t) * L * h->Ucap * kRecWords);
   MOE_ALLOC(h->hbuf, sizeof(float) * h->Pcap * I);
+  MOE_ALLOC(h->xq, sizeof(uint32_t) * T * (H / 32) * kXqWords);
+  MOE_ALLOC(h->xss, sizeof(float2) * T * (H / 32));
 #undef MOE_ALLOC
   h->slot_bytes = 256 + ((sizeof(moe_layer_weights) * L + 255) / 256) * 256;
   if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->staging), h->slot_bytes * kStagingSlots, 0)) !=
@@ -397,6 +403,15 @@ extern "C" moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t* n
       pairs[2 * i + 1] = (packed[i] >> 8) & 0xFF;
     }
   }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_swiglu_rows(moe_round* h, float* host_rows) {
+  if (!h || !host_rows) return MOE_ERR_INVALID_ARG;
+  if (h->last_T == 0) return MOE_ERR_STATE;
+  MOE_HIP(h, hipStreamSynchronize(h->stream));
+  const size_t n = static_cast<size_t>(h->last_T) * h->last_k * h->cfg.inter;
+  MOE_HIP(h, hipMemcpy(host_rows, h->hbuf, sizeof(float) * n, hipMemcpyDeviceToHost));
   return MOE_OK;
 }
 
