@@ -153,13 +153,24 @@ MOE_ROUND_API moe_status moe_round_swiglu_rows(moe_round* h, float* host_rows);
 MOE_ROUND_API moe_status moe_round_last_unique(moe_round* h, int32_t* n_unique_per_layer);
 
 /*
- * Eager run with a HIP event pair around every kernel, for measurement: same arguments as
- * moe_round_run; synchronises; writes the per-kernel elapsed milliseconds into host float
- * [L][4] (router logits, selection + worklist, gate/up, down).  May be called on a graph handle.
+ * Kernel timing, for measurement.  moe_round_profile(h, 1) makes every following run launch its
+ * kernels eagerly (also on a graph handle: graph nodes carry no events) with a start/stop event
+ * pair per kernel that the runtime stamps with the dispatch's own start and end times, so each
+ * duration is the kernel's execution alone, without the launch gap before it.  The events form a
+ * ring per handle; a slot is read back (waiting for its run) before it is reused, so profiling
+ * costs no host synchronisation until the ring wraps.  moe_round_profile(h, 0) reads back what is
+ * outstanding and returns to normal launches; the sums are kept for a later read.
+ * Returns MOE_ERR_INVALID_ARG for enable outside {0, 1}; MOE_ERR_HIP if events cannot be created.
  */
-MOE_ROUND_API moe_status moe_round_run_timed(moe_round* h, const float* hidden, int32_t T, int32_t k,
-                               const moe_layer_weights* layers, float* out, int32_t* expert_ids,
-                               float* route_w, float* kernel_ms);
+MOE_ROUND_API moe_status moe_round_profile(moe_round* h, int32_t enable);
+
+/*
+ * Sum of the per-kernel durations (milliseconds) of the runs profiled since profiling was
+ * enabled or last read, into host double [L][4] (router logits, selection + worklist, gate/up,
+ * down), and their number of runs into *n_runs; then resets both.  Synchronises on the
+ * outstanding events.  MOE_ERR_STATE if profiling was never enabled on this handle.
+ */
+MOE_ROUND_API moe_status moe_round_profile_read(moe_round* h, double* kernel_ms, int32_t* n_runs);
 
 /* The hipError_t (as int) of the last MOE_ERR_HIP on this handle, 0 if none. */
 MOE_ROUND_API int32_t moe_round_last_hip_error(const moe_round* h);

@@ -28,7 +28,7 @@ def declared():
 def test_header_declares_the_boundary():
     names = declared()
     assert "moe_round_init" in names and "moe_round_run" in names and "moe_round_destroy" in names
-    assert len(names) == 10
+    assert len(names) == 11
 
 
 def test_library_exports_exactly_the_declared_symbols(lib):
@@ -108,6 +108,10 @@ def test_null_and_bad_arguments_are_refused_before_any_gpu_call(lib):
     assert lib.moe_round_worklist(None, 0, None, None, None, None) == -1
     assert lib.moe_round_last_unique(None, None) == -1
     assert lib.moe_round_last_hip_error(None) == 0
+    assert lib.moe_round_profile(None, 1) == -1
+    n = ctypes.c_int32()
+    ms = (ctypes.c_double * 4)()
+    assert lib.moe_round_profile_read(None, ms, ctypes.byref(n)) == -1
     lib.moe_round_destroy(None)
 
 

@@ -62,7 +62,8 @@ def load() -> ctypes.CDLL:
         "moe_round_validate_config": (i32, [P(Config)]),
         "moe_round_init": (i32, [P(Config), P(LayerWeights), vp, P(vp)]),
         "moe_round_run": (i32, [vp, vp, i32, i32, P(LayerWeights), vp, vp, vp]),
-        "moe_round_run_timed": (i32, [vp, vp, i32, i32, P(LayerWeights), vp, vp, vp, P(ctypes.c_float)]),
+        "moe_round_profile": (i32, [vp, i32]),
+        "moe_round_profile_read": (i32, [vp, P(ctypes.c_double), P(i32)]),
         "moe_round_worklist": (i32, [vp, i32, P(i32), P(i32), P(i32), P(i32)]),
         "moe_round_last_unique": (i32, [vp, P(i32)]),
         "moe_round_swiglu_rows": (i32, [vp, P(ctypes.c_float)]),
@@ -156,6 +157,7 @@ class MoeRound:
         if st != OK:
             raise MoeRoundError(st, "moe_round_init")
         self.h = h
+        self._profiling = False
 
     def _raise(self, st, what):
         raise MoeRoundError(st, what, self.lib.moe_round_last_hip_error(self.h))
@@ -186,14 +188,34 @@ class MoeRound:
         if st != OK:
             self._raise(st, "moe_round_run")
 
-    def run_timed(self, hidden, k, out, ids=None, route_w=None, layers=None):
-        """Eager run with HIP events around each kernel; returns [L][4] milliseconds
-        (router logits, selection + worklist, gate/up, down)."""
-        ms = (ctypes.c_float * (KERNELS_PER_LAYER * self.L))()
-        st = self.lib.moe_round_run_timed(*self._run_args(hidden, k, out, ids, route_w, layers), ms)
+    def profile(self, enable: bool = True):
+        """Start (or stop) per-kernel timing of the following runs (dispatch timestamps)."""
+        st = self.lib.moe_round_profile(self.h, int(bool(enable)))
         if st != OK:
-            self._raise(st, "moe_round_run_timed")
-        return [[ms[KERNELS_PER_LAYER * l + i] for i in range(KERNELS_PER_LAYER)] for l in range(self.L)]
+            self._raise(st, "moe_round_profile")
+        self._profiling = bool(enable)
+
+    def profile_read(self):
+        """(sum of milliseconds [L][4] per kernel: logits, select, gate/up, down; number of runs)
+        since profiling started or was last read."""
+        ms = (ctypes.c_double * (KERNELS_PER_LAYER * self.L))()
+        n = ctypes.c_int32()
+        st = self.lib.moe_round_profile_read(self.h, ms, ctypes.byref(n))
+        if st != OK:
+            self._raise(st, "moe_round_profile_read")
+        return [[ms[KERNELS_PER_LAYER * l + i] for i in range(KERNELS_PER_LAYER)] for l in range(self.L)], n.value
+
+    def run_timed(self, hidden, k, out, ids=None, route_w=None, layers=None):
+        """One run with per-kernel timing; returns [L][4] milliseconds (synchronises)."""
+        was = self._profiling
+        if not was:
+            self.profile(True)
+        self.profile_read()
+        self.run(hidden, k, out, ids, route_w, layers)
+        ms, _ = self.profile_read()
+        if not was:
+            self.profile(False)
+        return ms
 
     def worklist(self, layer: int = 0):
         T_k = self.max_rows * self.top_k_max

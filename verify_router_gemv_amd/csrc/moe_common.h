@@ -1,0 +1,355 @@
+// Device code of the MoE decode/verify round (gfx950, wave64): shared definitions.
+//
+// Per layer four kernels:
+//   logits_kernel  router GEMV z[t][e] = sum_h Wr[e][h] x[t][h] + b[e]: fp32 inputs, fp64 products
+//                  and sums; also seeds the layer's output rows (residual x, or zeros).
+//   select_kernel  one block: per-row top-k (k rounds of a wave-wide max over (logit, id) keys),
+//                  softmax over the k selected logits, the union of the rows' experts and a counting
+//                  sort of the (row, rank) pairs by expert; it writes one 128-byte record per unique
+//                  expert (id, pair offset, row count, unique count, packed row ids).
+//   gateup_kernel  streams one unique expert's 4-bit gate and up rows once for all rows routed to
+//                  it, dequantising in registers, and writes silu(g) * v per (row, rank) pair.
+//   down_kernel    streams the unique experts' 4-bit down rows and scatter-adds routing weight x
+//                  (W_d h) into the output rows.
+// Everything a GEMV block needs before its weight stream is in its expert's record, so it waits
+// for one dependent global round trip; every other load is issued up front, never inside a loop
+// whose trip count depends on the data (such loops serialise memory latency).
+//
+// Page references: "How AlphaInfer makes local decoding fast" section 2 (a decode round is one
+// forward pass over 1-8 rows, replayed as a captured graph, per-request data is ingress) and
+// section 3.1 (extra verified rows add the bytes of experts only they chose, so the union is read
+// once); infero README "Beyond plain text decode" (top-k routing at decode, counting sort into
+// per-expert work), "Layout" figure (the SwiGLU expert), "Design notes" (block weights consumed
+// in place; a float GEMV decoding one weight per thread runs far below the memory bound, so each
+// lane here decodes 32-weight blocks from 16-byte loads).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_round.h"
+
+namespace moe {
+
+constexpr int kThreads = 256;   // 4 waves per block
+constexpr int kWaves = kThreads / 64;
+constexpr int kSelectThreads = 1024;  // the select kernel's single block: 16 waves, one row each
+constexpr int kSelectWaves = kSelectThreads / 64;
+
+// Per-unique-expert record: [0] expert id, [1] first pair slot, [2] rows routed to the expert,
+// [3] number of unique experts of the layer, [4..19] the rows' ids, one byte each, in slot order.
+constexpr int kRecWords = 32;
+constexpr int kRecRowWord = 4;
+// A 32-block of activations as three signed int8 digits of a 24-bit integer: x ~ step * (d2*65536 +
+// d1*256 + d0). Words [digit d][group g of 8][even/odd]: the even word packs elements 8g+0,2,4,6, the
+// odd word 8g+1,3,5,7, matching the nibble order of a weight code word.
+constexpr int kXqWords = 24;
+constexpr float kXqMax = 8355711.0f;  // 127*65536 + 127*256 + 127
+constexpr int kXStageMax = 8;        // activation rows staged in LDS at a time (T > 1) ...
+constexpr int kXStageBytes = 65536;  // ... within 64 KB of LDS
+
+// Per-run pointers. Eager launches carry them by value; graph replays read them from a fixed
+// device copy (written when they change), so a captured graph is never rebuilt.
+struct Ingress {
+  const float* hidden;  // [T][H]
+  float* out;           // [T][H]
+  int32_t* ids;         // [L][T][k] or null
+  float* route_w;       // [L][T][k] or null
+};
+
+struct Args {
+  const Ingress* ing;              // graph mode: device ingress; eager mode: null
+  Ingress in;                      // eager mode ingress
+  const moe_layer_weights* wtab;   // graph mode: device table [L]; eager mode: null
+  moe_layer_weights w;             // eager mode: this layer's weights
+  float* xbuf0;
+  float* xbuf1;
+  double* logits;     // [T_max][E]
+  int32_t* n_unique;  // [L]
+  int32_t* uniq;      // [L][Ucap]
+  int32_t* offs;      // [L][Ucap + 1]
+  int32_t* pairs;     // [L][Pcap]  t | (j << 8)
+  float* pair_w;      // [L][Pcap]
+  int32_t* rec;       // [L][Ucap][kRecWords] per-unique-expert records
+  float* hbuf;        // [Pcap][I]
+  uint32_t* xq;       // [T_max][H/32][kXqWords] int8 digits of the layer input, per 32-block
+  float2* xss;        // [T_max][H/32] (digit step, block sum) of the layer input
+  int32_t H, I, E, L, T, k, residual, Ucap, Pcap;
+  int32_t xstage_h, xstage_i;  // activation rows staged in LDS at a time (gate/up: rows of H, down: of I)
+};
+
+__device__ __forceinline__ Ingress get_ingress(const Args& a) { return a.ing ? *a.ing : a.in; }
+__device__ __forceinline__ moe_layer_weights get_weights(const Args& a, int layer) {
+  return a.wtab ? a.wtab[layer] : a.w;
+}
+__device__ __forceinline__ const float* layer_input(const Args& a, const Ingress& in, int layer) {
+  if (layer == 0) return in.hidden;
+  return ((layer - 1) & 1) ? a.xbuf1 : a.xbuf0;
+}
+__device__ __forceinline__ float* layer_output(const Args& a, const Ingress& in, int layer) {
+  if (layer == a.L - 1) return in.out;
+  return (layer & 1) ? a.xbuf1 : a.xbuf0;
+}
+
+// ------------------------------------------------------------------------------------------
+// Cross-lane reductions on VALU only: DPP inside 16-lane rows, gfx950 permlane swaps across rows.
+// ------------------------------------------------------------------------------------------
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_u32<CTRL>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  return __builtin_bit_cast(double, dpp_u64<CTRL>(__builtin_bit_cast(uint64_t, v)));
+}
+
+// gfx950 lane swaps, written as inline asm: the compiler's two-result builtins for these were
+// observed to wire both results to one register when the inputs differ (sum s[0] + s[1] compiled
+// to s[0] + s[0]). Both operands are read and written: v_permlane32_swap exchanges lanes 32-63 of
+// `a` with lanes 0-31 of `b`; v_permlane16_swap exchanges the odd 16-lane rows of `a` with the
+// even rows of `b`. The s_nop covers the VALU-write -> swap-read hazard.
+__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Exchange with the lane 16 (X16) or 32 (X32) apart: returns the partner's value.
+template <bool X32>
+__device__ __forceinline__ uint32_t swap_partner_u32(uint32_t v) {
+  uint32_t a = v, b = v;
+  if constexpr (X32) {
+    permlane32_swap(a, b);  // a: [lo half, lo half], b: [hi half, hi half]
+    return (__lane_id() < 32) ? b : a;
+  } else {
+    permlane16_swap(a, b);  // a: rows [r0, r0, r2, r2], b: rows [r1, r1, r3, r3]
+    return ((__lane_id() >> 4) & 1) ? a : b;
+  }
+}
+template <bool X32>
+__device__ __forceinline__ float swap_partner_f32(float v) {
+  return __builtin_bit_cast(float, swap_partner_u32<X32>(__builtin_bit_cast(uint32_t, v)));
+}
+template <bool X32>
+__device__ __forceinline__ uint64_t swap_partner_u64(uint64_t v) {
+  const uint32_t lo = swap_partner_u32<X32>(static_cast<uint32_t>(v));
+  const uint32_t hi = swap_partner_u32<X32>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+template <bool X32>
+__device__ __forceinline__ double swap_partner_f64(double v) {
+  return __builtin_bit_cast(double, swap_partner_u64<X32>(__builtin_bit_cast(uint64_t, v)));
+}
+
+// Sum over groups of G consecutive lanes (G a power of two <= 64); every lane gets its group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp_f32<kDppXor1>(v);
+  if constexpr (G >= 4) v += dpp_f32<kDppXor2>(v);
+  if constexpr (G >= 8) v += dpp_f32<kDppHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp_f32<kDppMirror>(v);
+  if constexpr (G >= 32) v += swap_partner_f32<false>(v);
+  if constexpr (G >= 64) v += swap_partner_f32<true>(v);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  v += swap_partner_f64<false>(v);
+  v += swap_partner_f64<true>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = umax64(v, dpp_u64<kDppXor1>(v));
+  v = umax64(v, dpp_u64<kDppXor2>(v));
+  v = umax64(v, dpp_u64<kDppHalfMirror>(v));
+  v = umax64(v, dpp_u64<kDppMirror>(v));
+  v = umax64(v, swap_partner_u64<false>(v));
+  v = umax64(v, swap_partner_u64<true>(v));
+  return v;
+}
+
+// Full sums over 64 lanes of 8 values at once (a transposed butterfly): the xor-32 and xor-16
+// levels pair values through the permlane swaps, so each level halves the registers instead of
+// repeating per value; the last four levels run inside 16-lane rows. Afterwards every lane of row
+// R (lanes 16R..16R+15) holds in `lo` the total of v[{0,2,1,3}[R]] and in `hi` of v[{4,6,5,7}[R]].
+__device__ __forceinline__ float pair_sum32(float a, float b) {
+  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
+  permlane32_swap(x, y);  // x: [a lo, b lo], y: [a hi, b hi]
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float pair_sum16(float a, float b) {
+  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
+  permlane16_swap(x, y);  // x: rows [a0, b0, a2, b2], y: rows [a1, b1, a3, b3]
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ void reduce8_wave(const float v[8], float& lo, float& hi) {
+  const float s01 = pair_sum32(v[0], v[1]), s23 = pair_sum32(v[2], v[3]);
+  const float s45 = pair_sum32(v[4], v[5]), s67 = pair_sum32(v[6], v[7]);
+  lo = group_sum<16>(pair_sum16(s01, s23));
+  hi = group_sum<16>(pair_sum16(s45, s67));
+}
+__device__ __forceinline__ int reduce8_slot(int row) { return (row == 1) ? 2 : (row == 2 ? 1 : row); }
+
+// ------------------------------------------------------------------------------------------
+// Small helpers
+// ------------------------------------------------------------------------------------------
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+#define MOE_GLOBAL __attribute__((address_space(1)))
+
+// Streaming (non-temporal) loads through global (not flat) addressing: weights are read once per
+// round; keep them from evicting the small reused data (activations, logits, records).
+// Every load in the kernels below is unconditional with a clamped, in-bounds address: a load under
+// a divergent branch is followed by its own wait, which would serialise the memory latency.
+__device__ __forceinline__ uint4 load_stream_u4(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load((const MOE_GLOBAL u32x4*)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t load_stream_u32(const uint32_t* p) {
+  return __builtin_nontemporal_load((const MOE_GLOBAL uint32_t*)(p));
+}
+__device__ __forceinline__ float4 load_stream_f4(const void* p) {
+  const f32x4 v = __builtin_nontemporal_load((const MOE_GLOBAL f32x4*)(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load_f4(const void* p) {
+  const f32x4 v = *((const MOE_GLOBAL f32x4*)(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
+}
+
+// Single-instruction byte -> float conversions (v_cvt_f32_ubyte0..3).
+#define MOE_CVT_UBYTE(N)                                                            \
+  __device__ __forceinline__ float cvt_ubyte##N(uint32_t v) {                       \
+    float r;                                                                        \
+    asm("v_cvt_f32_ubyte" #N " %0, %1" : "=v"(r) : "v"(v));                         \
+    return r;                                                                       \
+  }
+MOE_CVT_UBYTE(0)
+MOE_CVT_UBYTE(1)
+MOE_CVT_UBYTE(2)
+MOE_CVT_UBYTE(3)
+#undef MOE_CVT_UBYTE
+
+// 32 codes of one block (16 bytes, byte j = element 2j | element 2j+1 << 4) -> floats in order,
+// 11 VALU instructions per 8 codes.
+__device__ __forceinline__ void unpack_block(const uint4 c, float q[32]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = w[i] & 0x0F0F0F0Fu;         // elements 8i+0, +2, +4, +6
+    const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;  // elements 8i+1, +3, +5, +7
+    q[8 * i + 0] = cvt_ubyte0(lo);
+    q[8 * i + 1] = cvt_ubyte0(hi);
+    q[8 * i + 2] = cvt_ubyte1(lo);
+    q[8 * i + 3] = cvt_ubyte1(hi);
+    q[8 * i + 4] = cvt_ubyte2(lo);
+    q[8 * i + 5] = cvt_ubyte2(hi);
+    q[8 * i + 6] = cvt_ubyte3(lo);
+    q[8 * i + 7] = cvt_ubyte3(hi);
+  }
+}
+
+__device__ __forceinline__ float dot32(const float q[32], const float x[32]) {
+  float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; i += 2) {
+    d0 = fmaf(q[i], x[i], d0);
+    d1 = fmaf(q[i + 1], x[i + 1], d1);
+  }
+  return d0 + d1;
+}
+
+// Make a value opaque to the optimiser so per-pass unpacking is not hoisted out of the pass loop
+// (hoisting keeps every unpacked code live across the loop and multiplies register use).
+__device__ __forceinline__ void opaque(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Order-preserving 64-bit key of a logit with the expert id in the low 9 bits, so one unsigned
+// max picks the largest logit and, among logits equal to 2^-43 relative, the lower id.
+__device__ __forceinline__ uint64_t logit_key(double z, int e) {
+  if (!(z == z)) z = -INFINITY;  // NaN ranks lowest
+  uint64_t b = __builtin_bit_cast(uint64_t, z);
+  b = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  return (b & ~0x1FFull) | static_cast<uint64_t>(511 - e);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return 511 - static_cast<int>(key & 0x1FFull); }
+
+
+// Digits of one 32-block (see kXqWords). The integer q = rint(x / step) with step = max|x| / kXqMax
+// is split into balanced base-256 digits d0, d1, d2 in [-127, 127]; the block sum is kept in fp32.
+__device__ __forceinline__ void quantize_block(const float* src, uint32_t* dst, float2* ss) {
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float4 f = load_f4(src + 4 * q);
+    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+  }
+  float mx = 0.f, sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) { mx = fmaxf(mx, fabsf(v[i])); sum += v[i]; }
+  const float inv = mx > 0.f ? kXqMax / mx : 0.f;
+  uint32_t d[3][8];  // digit planes, 4 bytes per word in element order 0..31
+#pragma unroll
+  for (int w = 0; w < 8; ++w) { d[0][w] = 0u; d[1][w] = 0u; d[2][w] = 0u; }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    int q = static_cast<int>(rintf(v[i] * inv));
+    q = max(-static_cast<int>(kXqMax), min(static_cast<int>(kXqMax), q));
+    const int d0 = ((q + 128) & 255) - 128;
+    const int q1 = (q - d0) >> 8;
+    const int d1 = ((q1 + 128) & 255) - 128;
+    const int d2 = (q1 - d1) >> 8;
+    const int w = i >> 2, sh = 8 * (i & 3);
+    d[0][w] |= (static_cast<uint32_t>(d0) & 0xFFu) << sh;
+    d[1][w] |= (static_cast<uint32_t>(d1) & 0xFFu) << sh;
+    d[2][w] |= (static_cast<uint32_t>(d2) & 0xFFu) << sh;
+  }
+  // regroup each 8-element group into even (0,2,4,6) and odd (1,3,5,7) words
+#pragma unroll
+  for (int dg = 0; dg < 3; ++dg)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t a0 = d[dg][2 * g], a1 = d[dg][2 * g + 1];  // bytes of elements 8g..8g+3, 8g+4..8g+7
+      const uint32_t even = __builtin_amdgcn_perm(a1, a0, 0x06040200u);  // bytes e0 e2 | e4 e6
+      const uint32_t odd = __builtin_amdgcn_perm(a1, a0, 0x07050301u);   // bytes e1 e3 | e5 e7
+      dst[(dg * 4 + g) * 2 + 0] = even;
+      dst[(dg * 4 + g) * 2 + 1] = odd;
+    }
+  *ss = make_float2(mx / kXqMax, sum);
+}
+
+}  // namespace moe

@@ -1,11 +1,12 @@
 // MoE decode/verify round for MI355X (gfx950): the handle, launch plans and the C ABI.
 // The kernels are in moe_kernels.h; this file only validates, allocates, launches and captures.
 //
-// A round is replayed either eagerly (three launches per layer, ingress pointers passed by value)
+// A round is replayed either eagerly (four launches per layer, ingress pointers passed by value)
 // or as one captured hipGraph per (T, k) whose kernels read the ingress pointers and the weight
 // table from fixed device buffers, so new per-request pointers never force a recapture
 // ("How AlphaInfer makes local decoding fast", section 2: per-request data is ingress written
 // into fixed buffers and the graph is never rebuilt).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -39,6 +40,7 @@ struct GraphEntry {
 };
 
 constexpr int kStagingSlots = 16;
+constexpr int kProfileEvents = 512;  // event budget of the profiling ring (two per kernel)
 
 }  // namespace
 
@@ -73,6 +75,14 @@ struct moe_round {
   bool slot_used[kStagingSlots] = {};
   int next_slot = 0;
   std::map<int, GraphEntry> graphs;
+  // profiling: a ring of runs, each with a start/stop event per kernel (dispatch timestamps)
+  bool profiling = false;
+  int prof_runs = 0;                   // ring capacity in runs
+  std::vector<hipEvent_t> prof_ev;     // [prof_runs][n kernels][2]
+  std::vector<int> prof_nk;            // kernels recorded in each ring slot (0 = free)
+  int prof_next = 0;
+  std::vector<double> prof_ms;         // accumulated milliseconds [L][4]
+  int32_t prof_count = 0;              // runs accumulated since the last read
   int last_T = 0, last_k = 0;
   int32_t last_hip = 0;
 };
@@ -195,10 +205,12 @@ static moe_status launch_eager(moe_round* h, int T, int k, hipEvent_t* evs) {
     a.w = h->h_wtab[L.layer];
     int layer = L.layer;
     void* params[] = {&a, &layer};
-    if (evs) MOE_HIP(h, hipEventRecord(evs[2 * i], h->stream));
-    MOE_HIP(h, hipLaunchKernel(reinterpret_cast<const void*>(L.fn), L.grid, dim3(L.threads), params, L.shmem,
-                               h->stream));
-    if (evs) MOE_HIP(h, hipEventRecord(evs[2 * i + 1], h->stream));
+    if (evs)  // events stamped with the dispatch's own start and end times
+      MOE_HIP(h, hipExtLaunchKernel(reinterpret_cast<const void*>(L.fn), L.grid, dim3(L.threads), params,
+                                    L.shmem, h->stream, evs[2 * i], evs[2 * i + 1], 0));
+    else
+      MOE_HIP(h, hipLaunchKernel(reinterpret_cast<const void*>(L.fn), L.grid, dim3(L.threads), params,
+                                 L.shmem, h->stream));
     ++i;
   }
   return MOE_OK;
@@ -227,9 +239,34 @@ static moe_status sync_device_ingress(moe_round* h) {
   return MOE_OK;
 }
 
+// Fold one ring slot's kernel durations into the accumulators (waits for its last kernel).
+static moe_status harvest(moe_round* h, int slot) {
+  const int nk = h->prof_nk[slot];
+  if (nk == 0) return MOE_OK;
+  hipEvent_t* ev = h->prof_ev.data() + static_cast<size_t>(slot) * 2 * kKernelsPerLayer * h->cfg.n_layers;
+  h->prof_nk[slot] = 0;
+  MOE_HIP(h, hipEventSynchronize(ev[2 * nk - 1]));
+  for (int i = 0; i < nk; ++i) {
+    float ms = 0.f;
+    MOE_HIP(h, hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]));
+    h->prof_ms[i] += ms;
+  }
+  ++h->prof_count;
+  return MOE_OK;
+}
+
+static void free_profile(moe_round* h) {
+  for (auto& ev : h->prof_ev)
+    if (ev) (void)hipEventDestroy(ev);
+  h->prof_ev.clear();
+  h->prof_nk.clear();
+  h->prof_runs = 0;
+}
+
 static void free_handle(moe_round* h) {
   if (!h) return;
   if (h->stream) (void)hipStreamSynchronize(h->stream);
+  free_profile(h);
   for (auto& kv : h->graphs) {
     if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
     if (kv.second.graph) (void)hipGraphDestroy(kv.second.graph);
@@ -328,7 +365,16 @@ extern "C" moe_status moe_round_run(moe_round* h, const float* hidden, int32_t T
                                     float* route_w) {
   moe_status st = prepare_run(h, hidden, T, k, layers, out, expert_ids, route_w);
   if (st != MOE_OK) return st;
-  if (h->cfg.use_graph) {
+  if (h->profiling) {
+    const int slot = h->prof_next;
+    h->prof_next = (slot + 1) % h->prof_runs;
+    st = harvest(h, slot);  // a slot is reused only after its previous run has been read
+    if (st != MOE_OK) return st;
+    hipEvent_t* ev = h->prof_ev.data() + static_cast<size_t>(slot) * 2 * kKernelsPerLayer * h->cfg.n_layers;
+    st = launch_eager(h, T, k, ev);
+    if (st != MOE_OK) return st;
+    h->prof_nk[slot] = kKernelsPerLayer * h->cfg.n_layers;
+  } else if (h->cfg.use_graph) {
     st = sync_device_ingress(h);
     if (st != MOE_OK) return st;
     const int key = T * 64 + k;
@@ -349,31 +395,52 @@ extern "C" moe_status moe_round_run(moe_round* h, const float* hidden, int32_t T
   return MOE_OK;
 }
 
-extern "C" moe_status moe_round_run_timed(moe_round* h, const float* hidden, int32_t T, int32_t k,
-                                          const moe_layer_weights* layers, float* out, int32_t* expert_ids,
-                                          float* route_w, float* kernel_ms) {
-  if (!kernel_ms) return MOE_ERR_INVALID_ARG;
-  moe_status st = prepare_run(h, hidden, T, k, layers, out, expert_ids, route_w);
-  if (st != MOE_OK) return st;
-  const int n = kKernelsPerLayer * h->cfg.n_layers;
-  std::vector<hipEvent_t> evs(2 * n, nullptr);
-  for (auto& ev : evs)
-    if (hipEventCreate(&ev) != hipSuccess) {
-      for (auto& e2 : evs)
-        if (e2) (void)hipEventDestroy(e2);
-      return MOE_ERR_HIP;
+extern "C" moe_status moe_round_profile(moe_round* h, int32_t enable) {
+  if (!h || (enable != 0 && enable != 1)) return MOE_ERR_INVALID_ARG;
+  if (enable == h->profiling) return MOE_OK;
+  if (enable) {
+    const int per_run = 2 * kKernelsPerLayer * h->cfg.n_layers;
+    const int runs = kProfileEvents / per_run > 2 ? kProfileEvents / per_run : 2;
+    h->prof_ev.assign(static_cast<size_t>(runs) * per_run, nullptr);
+    h->prof_nk.assign(runs, 0);
+    h->prof_runs = runs;
+    h->prof_next = 0;
+    for (auto& ev : h->prof_ev) {
+      hipError_t e = hipEventCreate(&ev);
+      if (e != hipSuccess) {
+        free_profile(h);
+        return hip_fail(h, e);
+      }
     }
-  st = launch_eager(h, T, k, evs.data());
-  hipError_t e = hipSuccess;
-  if (st == MOE_OK) e = hipEventSynchronize(evs[2 * n - 1]);
-  if (st == MOE_OK && e == hipSuccess) {
-    for (int i = 0; i < n && e == hipSuccess; ++i) e = hipEventElapsedTime(&kernel_ms[i], evs[2 * i], evs[2 * i + 1]);
+    h->prof_ms.assign(kKernelsPerLayer * h->cfg.n_layers, 0.0);
+    h->prof_count = 0;
+    h->profiling = true;
+    return MOE_OK;
   }
-  for (auto& ev : evs) (void)hipEventDestroy(ev);
-  if (st != MOE_OK) return st;
-  if (e != hipSuccess) return hip_fail(h, e);
-  h->last_T = T;
-  h->last_k = k;
+  // Disabling keeps the accumulated sums for a later read but drops the ring.
+  for (int s2 = 0; s2 < h->prof_runs; ++s2) {
+    moe_status st = harvest(h, (h->prof_next + s2) % h->prof_runs);
+    if (st != MOE_OK) return st;
+  }
+  MOE_HIP(h, hipStreamSynchronize(h->stream));
+  free_profile(h);
+  h->profiling = false;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_profile_read(moe_round* h, double* kernel_ms, int32_t* n_runs) {
+  if (!h || !kernel_ms || !n_runs) return MOE_ERR_INVALID_ARG;
+  if (h->prof_ms.empty()) return MOE_ERR_STATE;
+  for (int s2 = 0; s2 < h->prof_runs; ++s2) {  // oldest first
+    moe_status st = harvest(h, (h->prof_next + s2) % h->prof_runs);
+    if (st != MOE_OK) return st;
+  }
+  for (size_t i = 0; i < h->prof_ms.size(); ++i) {
+    kernel_ms[i] = h->prof_ms[i];
+    h->prof_ms[i] = 0.0;
+  }
+  *n_runs = h->prof_count;
+  h->prof_count = 0;
   return MOE_OK;
 }
 

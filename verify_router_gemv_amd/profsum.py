@@ -1,0 +1,109 @@
+"""Short text summaries of rocprofv3 output for the round's kernels.
+
+    python -m verify_router_gemv_amd.profsum stats  STATS_CSV OUT "COMMAND"
+        per-kernel dispatch durations (calls, average, min, max) of the moe:: kernels from a
+        `rocprofv3 --kernel-trace --stats` *_kernel_stats.csv
+    python -m verify_router_gemv_amd.profsum traffic FETCH_DIR WRITE_DIR OUT "COMMAND"
+        gate/up HBM traffic per dispatch from a FETCH_SIZE pass and a WRITE_SIZE pass of
+        `bench.py --pmc-calibrate`, each scaled by its own reading for the run's closing copy of
+        CALIB_BYTES in and out (torch.neg of a 1 GiB fp32 tensor)
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CALIB_BYTES = 1 << 30
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in
+                  ("moe_common.h", "moe_route.h", "moe_gemv.h", "moe_gateup.h", "moe_gemv_g64.hip")]
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources the gate/up kernel is compiled from (a traffic figure is valid for these)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path: str):
+    """traffic_bytes_per_launch of a traffic summary if it was taken on the current kernel sources."""
+    try:
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
+def stats(stats_csv: str, out_path: str, command: str) -> None:
+    rows = []
+    for r in csv.DictReader(open(stats_csv)):
+        n = r["Name"]
+        if "moe::" in n or "neg_kernel" in n:
+            short = n.split("(")[0].replace("void moe::", "") if "moe::" in n else "torch.neg copy (calibration)"
+            rows.append((short, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[1] * x[2])
+    with open(out_path, "w") as fh:
+        fh.write(f"# rocprofv3 kernel statistics\n# command: {command}\n")
+        fh.write(f"{'kernel':32s} {'calls':>7s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}\n")
+        for s in rows:
+            fh.write(f"{s[0]:32s} {s[1]:7d} {s[2]:8.3f} {s[3]:8.3f} {s[4]:8.3f} {s[5]:6.2f}\n")
+    print(open(out_path).read())
+
+
+def _per_dispatch(d: str, counter: str):
+    acc = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = "gateup" if "gateup_kernel" in name else ("copy" if "neg_kernel" in name else None)
+            if key:
+                disp = acc.setdefault(key, {})
+                did = r["Dispatch_Id"]
+                disp[did] = disp.get(did, 0.0) + float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def traffic(fetch_dir: str, write_dir: str, out_path: str, command: str) -> None:
+    fetch, nf = _per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, nw = _per_dispatch(write_dir, "WRITE_SIZE")
+    f_scale = CALIB_BYTES / (fetch["copy"] * 1024.0)
+    w_scale = CALIB_BYTES / (write["copy"] * 1024.0)
+    rd = fetch["gateup"] * 1024.0 * f_scale
+    wr = write["gateup"] * 1024.0 * w_scale
+    with open(out_path, "w") as fh:
+        fh.write("# gate/up HBM traffic per dispatch, verify sweep (T = 1, 3, 8; 32 weight replicas)\n"
+                 f"# command: {command}\n"
+                 "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) come from two rocprofv3 --pmc passes; each is\n"
+                 f"# scaled by its own reading for the closing copy of {CALIB_BYTES} bytes in and out.\n"
+                 f"kernel_source_sha256_16: {kernel_source_hash()}\n"
+                 f"gateup_dispatches: {nf['gateup']} / {nw['gateup']}\n"
+                 f"fetch_kib_per_dispatch_raw: {fetch['gateup']:.1f}\n"
+                 f"write_kib_per_dispatch_raw: {write['gateup']:.1f}\n"
+                 f"copy_fetch_kib_raw: {fetch['copy']:.1f}\n"
+                 f"copy_write_kib_raw: {write['copy']:.1f}\n"
+                 f"fetch_scale: {f_scale:.4f}\n"
+                 f"write_scale: {w_scale:.4f}\n"
+                 f"read_bytes_per_launch: {rd:.0f}\n"
+                 f"write_bytes_per_launch: {wr:.0f}\n"
+                 f"traffic_bytes_per_launch: {rd + wr:.0f}\n")
+    print(open(out_path).read())
+
+
+if __name__ == "__main__":
+    cmd, args = sys.argv[1], sys.argv[2:]
+    {"stats": stats, "traffic": traffic}[cmd](*args)
