@@ -199,3 +199,16 @@ def test_deep_stack_free_running():
     g.close()
     del layers
     torch.cuda.empty_cache()
+
+
+def test_many_rows_share_experts(verify):
+    """40 correlated rows: the hot experts get far more than 16 rows (several matrix-core passes)."""
+    cfg, layer, view = verify
+    g = GpuRound([layer], cfg, max_rows=64)
+    for T in (16, 40, 64):
+        say(f"case shared experts T={T}")
+        X = synth.make_activations(cfg, T, seed=4, round_idx=T, device=DEV)  # verify rows: base + 0.5 noise
+        rel, mabs, nu = check_layer_round(g, [view], X, cfg.k, f"shared T={T}")
+        _, offs, _ = g.h.worklist(0)
+        say(f"  n_unique={nu[0]} max rows per expert={int(np.diff(offs).max())} rel-L2={rel:.2e}")
+    g.close()

@@ -27,7 +27,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe_round.h"
+#include "moe_round.h"
 
 namespace moe {
 
@@ -36,8 +36,9 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kSelectThreads = 1024;  // the select kernel's single block: 16 waves, one row each
 constexpr int kSelectWaves = kSelectThreads / 64;
 
-// Per-unique-expert record: [0] expert id, [1] first pair slot, [2] rows routed to the expert,
-// [3] number of unique experts of the layer, [4..19] the rows' ids, one byte each, in slot order.
+// Per-work-item record (an item is one expert and up to rg of its rows): [0] expert id, [1] first
+// pair slot, [2] rows of the item, [3] number of items of the layer, [4..19] the rows' ids, one byte
+// each, in slot order.
 constexpr int kRecWords = 32;
 constexpr int kRecRowWord = 4;
 // A 32-block of activations as three signed int8 digits of a 24-bit integer: x ~ step * (d2*65536 +
@@ -70,12 +71,16 @@ struct Args {
   int32_t* offs;      // [L][Ucap + 1]
   int32_t* pairs;     // [L][Pcap]  t | (j << 8)
   float* pair_w;      // [L][Pcap]
-  int32_t* rec;       // [L][Ucap][kRecWords] per-unique-expert records
+  int32_t* rec;       // [L][Icap][kRecWords] per-work-item records
   float* hbuf;        // [Pcap][I]
   uint32_t* xq;       // [T_max][H/32][kXqWords] int8 digits of the layer input, per 32-block
   float2* xss;        // [T_max][H/32] (digit step, block sum) of the layer input
   int32_t H, I, E, L, T, k, residual, Ucap, Pcap;
-  int32_t xstage_h, xstage_i;  // activation rows staged in LDS at a time (gate/up: rows of H, down: of I)
+  int32_t Icap;       // record slots per layer (work items <= pairs)
+  int32_t rg;         // rows per work item at most (this launch)
+  int32_t xstage_h;  // gate/up: rows of input digits staged in LDS at a time (T > 1)
+  int32_t xstage_i;  // down: SwiGLU rows staged in LDS at a time (T > 1)
+  int32_t mfma_rows;  // gate/up: experts with at least this many rows use the matrix-core tile (0: never)
 };
 
 __device__ __forceinline__ Ingress get_ingress(const Args& a) { return a.ing ? *a.ing : a.in; }
@@ -181,6 +186,24 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 }
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Wave-wide maximum as a wave-uniform value: DPP inside each 16-lane row, then the four row maxima
+// read into scalar registers.
+__device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
+  v = max(v, dpp_u32<kDppXor1>(v));
+  v = max(v, dpp_u32<kDppXor2>(v));
+  v = max(v, dpp_u32<kDppHalfMirror>(v));
+  v = max(v, dpp_u32<kDppMirror>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   v = umax64(v, dpp_u64<kDppXor1>(v));

@@ -2,7 +2,7 @@
 #pragma once
 #include <stdint.h>
 
-#include "../../include/moe_round.h"
+#include "moe_round.h"
 
 namespace moe {
 

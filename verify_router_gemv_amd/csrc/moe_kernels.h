@@ -18,15 +18,19 @@ constexpr int rows_per_lane_group(int NB) { return NB == 1 ? 4 : (NB == 2 ? 2 : 
 template <int G, int NB, int RC>
 struct GemvPick {
   static constexpr int RW = rows_per_lane_group(NB);
-  static KernelFn gateup() { return gateup_kernel<G, NB, RW>; }
+  static KernelFn gateup(int mode) {
+    return mode == kGuOneRow ? gateup_kernel<G, NB, RW, kGuOneRow>
+           : mode == kGuPairs ? gateup_kernel<G, NB, RW, kGuPairs>
+                              : gateup_kernel<G, NB, RW, kGuStaged>;
+  }
   static KernelFn down() { return down_kernel<G, NB, RC, RW>; }
   static constexpr int rows_per_block() { return kWaves * RW * (64 / G); }
 };
 
 template <int G, int NB>
 inline bool pick_rc(int RC, bool up, KernelFn* fn, int* rows) {
-  if (up) {  // gate/up walks the expert's rows one at a time; no pass width
-    *fn = GemvPick<G, NB, 1>::gateup();
+  if (up) {  // for gate/up RC is the mode (kGuOneRow, kGuPairs, kGuStaged)
+    *fn = GemvPick<G, NB, 1>::gateup(RC);
     *rows = GemvPick<G, NB, 1>::rows_per_block();
     return true;
   }
@@ -94,6 +98,10 @@ inline KernelFn pick_select(int E) {
   if (E <= 256) return select_kernel<4>;
   return select_kernel<8>;
 }
+
+// Rounds of at least this many rows are "wide": gate/up stages the input digits in LDS and may use
+// the matrix-core tile.
+constexpr int kWideRows = 16;
 
 // Rows of one expert processed per register pass, by round width.
 inline int rows_per_pass(int T) { return T == 1 ? 1 : 2; }

@@ -9,6 +9,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <vector>
@@ -48,7 +49,7 @@ struct moe_round {
   moe_round_config cfg{};
   hipStream_t stream = nullptr;
   int device = 0;
-  int Ucap = 0, Pcap = 0;
+  int Ucap = 0, Pcap = 0, Icap = 0;
   int Gh = 0, NBh = 0, Gi = 0, NBi = 0;
   // device scratch
   Ingress* d_ing = nullptr;            // graph-mode ingress
@@ -85,6 +86,8 @@ struct moe_round {
   int32_t prof_count = 0;              // runs accumulated since the last read
   int last_T = 0, last_k = 0;
   int32_t last_hip = 0;
+  int mfma_rows = 3;                   // gate/up (wide rounds): matrix-core tile from this many rows per item
+  int rows_per_item = 0;               // 0: by round width
 };
 
 static moe_status hip_fail(moe_round* h, hipError_t e) {
@@ -101,6 +104,21 @@ static moe_status hip_fail(moe_round* h, hipError_t e) {
 static int xstage_rows(int K) {
   const int r = kXStageBytes / (static_cast<int>(sizeof(float)) * K);
   return r < 1 ? 1 : (r > kXStageMax ? kXStageMax : r);
+}
+
+// Rows of one expert handled by one work item: verify rounds split an expert shared by many rows
+// over several blocks (each re-reads the expert's tile, mostly from the memory-side cache) so no
+// block carries many rows; wide rounds keep larger items.
+static int rows_per_item(const moe_round* h, int T) {
+  if (h->rows_per_item > 0) return h->rows_per_item;
+  return T >= kWideRows ? 4 : 2;
+}
+
+// Upper bound of the work items of a round: sum over experts of ceil(rows / rg).
+static int items_bound(int pairs, int E, int rg) {
+  const int nu = pairs < E ? pairs : E;
+  const int b = (pairs + nu * (rg - 1)) / rg;
+  return b < pairs ? b : pairs;
 }
 
 static Args base_args(const moe_round* h, int T, int k) {
@@ -125,26 +143,33 @@ static Args base_args(const moe_round* h, int T, int k) {
   a.k = k;
   a.residual = h->cfg.residual;
   a.Ucap = h->Ucap;
+  a.Icap = h->Icap;
+  a.rg = rows_per_item(h, T);
   a.Pcap = h->Pcap;
-  a.xstage_h = xstage_rows(h->cfg.hidden);
+  a.xstage_h = gateup_stage_rows(h->cfg.hidden);
+  a.mfma_rows = h->mfma_rows;
   a.xstage_i = xstage_rows(h->cfg.inter);
   return a;
 }
 
 static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   const int E = h->cfg.n_experts, H = h->cfg.hidden, I = h->cfg.inter;
-  const int umax = (T * k < E) ? T * k : E;
+  const int umax = items_bound(T * k, E, rows_per_item(h, T));
   const int RC = rows_per_pass(T);
+  const bool stage = T >= kWideRows;
   KernelFn lg = pick_logits(H, T), sel = pick_select(E), gu = nullptr, dn = nullptr;
   int rows_gu = 0, rows_dn = 0;
-  if (!lg || !pick_gemv(h->Gh, h->NBh, RC, true, &gu, &rows_gu) ||
+  const int gu_mode = stage ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
+  if (!lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, &gu, &rows_gu) ||
       !pick_gemv(h->Gi, h->NBi, RC, false, &dn, &rows_dn))
     return false;
   const int tc = logits_rows(T);
   const dim3 grid_lg((E + kRouteExpertsPerBlock - 1) / kRouteExpertsPerBlock, (T + tc - 1) / tc);
   const dim3 grid_gu(umax * ((I + rows_gu - 1) / rows_gu));
   const dim3 grid_dn(umax * ((H + rows_dn - 1) / rows_dn));
-  const int shm_gu = 0;  // gate/up reads the input digits from global memory (L2)
+  int gu_words = gateup_stage_words(H);
+  if (h->Gh == 64 && h->NBh == 1) gu_words += kMfmaExtraWords;  // matrix-core tile: (s, m) tables, partial sums
+  const int shm_gu = stage ? static_cast<int>(sizeof(uint32_t)) * gu_words : 0;
   const int shm_dn = T > 1 ? static_cast<int>(sizeof(float)) * xstage_rows(I) * I : 0;
   out->clear();
   for (int l = 0; l < h->cfg.n_layers; ++l) {
@@ -299,7 +324,10 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   const int H = cfg->hidden, I = cfg->inter;
   h->Pcap = T * K;
   h->Ucap = (T * K < E) ? T * K : E;
+  h->Icap = T * K;  // work items never outnumber (row, rank) pairs
   h->h_wtab.assign(layers, layers + L);
+  if (const char* env = std::getenv("MOE_MFMA_ROWS")) h->mfma_rows = std::atoi(env);  // tuning experiments
+  if (const char* env = std::getenv("MOE_ROWS_PER_ITEM")) h->rows_per_item = std::atoi(env);
 
   auto fail = [&](hipError_t e) {
     moe_status s = hip_fail(h, e);
@@ -320,7 +348,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   MOE_ALLOC(h->offs, sizeof(int32_t) * L * (h->Ucap + 1));
   MOE_ALLOC(h->pairs, sizeof(int32_t) * L * h->Pcap);
   MOE_ALLOC(h->pair_w, sizeof(float) * L * h->Pcap);
-  MOE_ALLOC(h->rec, sizeof(int32_t) * L * h->Ucap * kRecWords);
+  MOE_ALLOC(h->rec, sizeof(int32_t) * L * h->Icap * kRecWords);
   MOE_ALLOC(h->hbuf, sizeof(float) * h->Pcap * I);
   MOE_ALLOC(h->xq, sizeof(uint32_t) * T * (H / 32) * kXqWords);
   MOE_ALLOC(h->xss, sizeof(float2) * T * (H / 32));
@@ -332,7 +360,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   for (int i = 0; i < kStagingSlots; ++i)
     if ((e = hipEventCreateWithFlags(&h->slot_ev[i], hipEventDisableTiming)) != hipSuccess) return fail(e);
   if ((e = hipMemsetAsync(h->n_unique, 0, sizeof(int32_t) * L, h->stream)) != hipSuccess) return fail(e);
-  if ((e = hipMemsetAsync(h->rec, 0, sizeof(int32_t) * L * h->Ucap * kRecWords, h->stream)) != hipSuccess)
+  if ((e = hipMemsetAsync(h->rec, 0, sizeof(int32_t) * L * h->Icap * kRecWords, h->stream)) != hipSuccess)
     return fail(e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return fail(e);
   *out = h;

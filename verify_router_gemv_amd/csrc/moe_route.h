@@ -82,24 +82,30 @@ struct SelectShared {
   int uniq[MOE_ROUND_MAX_EXPERTS];
   int offs[MOE_ROUND_MAX_EXPERTS + 1];
   int pairs[MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK];   // by pair slot: t | j << 8
+  int ioffs[MOE_ROUND_MAX_EXPERTS];                    // unique index -> first work item
+  int item_u[MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK];  // work item -> unique index
   int wsum[kSelectWaves];
+  int wsum2[kSelectWaves];
   int nu;
 };
 
-// Top-k of one row on one wave. Each lane sorts its NPL (logit, id) keys once; then k rounds of a
-// wave-wide unsigned max over the lanes' heads, the winning lane popping its head. Lane j records the
-// j-th id and re-reads its exact fp64 logit for the softmax over the k selected logits.
+// Top-k of one row on one wave. Each lane sorts its NPL (logit, id) keys once; then k rounds pick
+// the largest head: a 32-bit wave max over the heads' high words (sign, exponent and 20 mantissa
+// bits), then a ballot of the lanes holding it; only when several lanes tie there does a 64-bit
+// wave max over those lanes decide. The winner pops its head. Lane j records the j-th id and its
+// exact fp64 logit (read from the owner lane's registers) for the softmax over the k selected.
 template <int NPL>
 __device__ __forceinline__ void select_row(const Args& a, SelectShared& s, int t) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
   const double* zrow = a.logits + static_cast<size_t>(t) * E;
+  double z[NPL];
   uint64_t key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    const double z = zrow[min(e, E - 1)];  // all loads issued together
-    key[i] = e < E ? logit_key(z, e) : 0ull;  // 0 is below every real key
+    z[i] = zrow[min(e, E - 1)];  // all loads issued together
+    key[i] = e < E ? logit_key(z[i], e) : 0ull;  // 0 is below every real key
   }
 #pragma unroll
   for (int pass = 0; pass < NPL; ++pass)
@@ -111,19 +117,36 @@ __device__ __forceinline__ void select_row(const Args& a, SelectShared& s, int t
         key[i + 1] = tmp;
       }
   int myid = 0;
+  double myz = 0.0;
   for (int j = 0; j < k; ++j) {
-    const uint64_t best = wave_max_u64(key[0]);
+    const uint32_t hi = static_cast<uint32_t>(key[0] >> 32);
+    const uint32_t mhi = wave_max_u32_uniform(hi);
+    const uint64_t cand = __ballot(hi == mhi);
+    uint64_t best;
+    if (__popcll(cand) == 1) {
+      best = readlane_u64(key[0], __ffsll(static_cast<unsigned long long>(cand)) - 1);
+    } else {
+      best = wave_max_u64(hi == mhi ? key[0] : 0ull);
+    }
     const int e = key_expert(best);
-    if (lane == (e & 63)) {
+    const int owner = e & 63, slot = e >> 6;
+    if (lane == owner) {
 #pragma unroll
       for (int i = 0; i + 1 < NPL; ++i) key[i] = key[i + 1];
       key[NPL - 1] = 0ull;
     }
-    if (lane == j) myid = e;
+    double zs = z[0];
+#pragma unroll
+    for (int i = 1; i < NPL; ++i)
+      if (slot == i) zs = z[i];
+    const double ze = __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, zs), owner));
+    if (lane == j) {
+      myid = e;
+      myz = ze;
+    }
   }
-  const double zj = zrow[lane < k ? myid : 0];
-  const double z0 = __shfl(zj, 0, 64);  // rank 0 holds the largest selected logit
-  const double ej = lane < k ? exp(zj - z0) : 0.0;
+  const double z0 = __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, myz), 0));
+  const double ej = lane < k ? exp(myz - z0) : 0.0;  // rank 0 holds the largest selected logit
   const double sum = wave_sum_f64(ej);
   if (lane < k) {
     s.sel[t * k + lane] = myid;
@@ -146,31 +169,47 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int laye
   __syncthreads();
 
   // Block-wide exclusive scan over experts (one per thread, E <= 512 < 1024) of
-  // (rows choosing e, whether any row chose e).
+  // (rows choosing e, whether any row chose e) and of the work items of e: its rows split into
+  // groups of at most a.rg, so a GEMV block's share of an expert is bounded.
   const unsigned long long m = tid < E ? s.mask[tid] : 0ull;
   const int c = __popcll(m), f = c > 0;
   const int packed = c | (f << 16);
-  int incl = packed;
+  const int ng = (c + a.rg - 1) / a.rg;
+  int incl = packed, incl2 = ng;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
+    const int y2 = __shfl_up(incl2, off, 64);
+    if (lane >= off) {
+      incl += y;
+      incl2 += y2;
+    }
   }
-  if (lane == 63) s.wsum[wave] = incl;
+  if (lane == 63) {
+    s.wsum[wave] = incl;
+    s.wsum2[wave] = incl2;
+  }
   __syncthreads();
-  int wpre = 0, wtot = 0;
+  int wpre = 0, wtot = 0, wpre2 = 0, wtot2 = 0;
 #pragma unroll
   for (int w = 0; w < kSelectWaves; ++w) {
-    if (w < wave) wpre += s.wsum[w];
+    if (w < wave) {
+      wpre += s.wsum[w];
+      wpre2 += s.wsum2[w];
+    }
     wtot += s.wsum[w];
+    wtot2 += s.wsum2[w];
   }
   const int excl = incl - packed + wpre;
   const int u = excl >> 16, off0 = excl & 0xFFFF;
-  const int nu = wtot >> 16;
+  const int nu = wtot >> 16, ni = wtot2;
+  const int io = incl2 - ng + wpre2;
   if (f) {
     s.uidx[tid] = u;
     s.uniq[u] = tid;
     s.offs[u] = off0;
+    s.ioffs[u] = io;
+    for (int gi = 0; gi < ng; ++gi) s.item_u[io + gi] = u;
   }
   if (tid == 0) {
     s.nu = nu;
@@ -185,20 +224,22 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int laye
   }
   __syncthreads();
 
-  // Publish: per-expert records, the pair table, the caller's ids / routing weights.
-  int32_t* rec = a.rec + static_cast<size_t>(layer) * a.Ucap * kRecWords;
+  // Publish: per-item records, the unique list and pair table, the caller's ids / routing weights.
+  int32_t* rec = a.rec + static_cast<size_t>(layer) * a.Icap * kRecWords;
   int32_t* uniq = a.uniq + static_cast<size_t>(layer) * a.Ucap;
   int32_t* offs = a.offs + static_cast<size_t>(layer) * (a.Ucap + 1);
   int32_t* pairs = a.pairs + static_cast<size_t>(layer) * a.Pcap;
   float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
-  for (int i = tid; i < nu * kRecWords; i += kSelectThreads) {
-    const int uu = i / kRecWords, wd = i - uu * kRecWords;
-    const int p0 = s.offs[uu], np = s.offs[uu + 1] - p0;
+  for (int i = tid; i < ni * kRecWords; i += kSelectThreads) {
+    const int it = i / kRecWords, wd = i - it * kRecWords;
+    const int uu = s.item_u[it];
+    const int p0 = s.offs[uu] + (it - s.ioffs[uu]) * a.rg;
+    const int np = min(a.rg, s.offs[uu + 1] - p0);
     int v = 0;
     if (wd == 0) v = s.uniq[uu];
     else if (wd == 1) v = p0;
     else if (wd == 2) v = np;
-    else if (wd == 3) v = nu;
+    else if (wd == 3) v = ni;
     else if (wd >= kRecRowWord && wd < kRecRowWord + MOE_ROUND_MAX_ROWS / 4) {
       const int r0 = (wd - kRecRowWord) * 4;
 #pragma unroll
@@ -220,16 +261,17 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int laye
   if (tid == 0) a.n_unique[layer] = nu;
 }
 
-// Every GEMV block reads its expert's record and record 0 (whose unique count is always valid)
-// in one round trip; values are clamped so nothing read back can index out of bounds.
+// Every GEMV block reads its work item's record and record 0 (whose item count is always valid)
+// in one round trip; values are clamped so nothing read back can index out of bounds. An item is
+// one expert and at most a.rg of the rows routed to it (pair slots p0 .. p0 + np - 1).
 struct ExpertWork {
-  int e, p0, np, nu;
+  int e, p0, np, nu;  // nu: number of items of the layer
   int rows[MOE_ROUND_MAX_ROWS / 4];  // packed row ids, 4 per word
 };
 
 __device__ __forceinline__ ExpertWork load_work(const Args& a, int layer, int u) {
-  const int32_t* rec = a.rec + static_cast<size_t>(layer) * a.Ucap * kRecWords;
-  const int32_t* r = rec + static_cast<size_t>(min(u, a.Ucap - 1)) * kRecWords;
+  const int32_t* rec = a.rec + static_cast<size_t>(layer) * a.Icap * kRecWords;
+  const int32_t* r = rec + static_cast<size_t>(min(u, a.Icap - 1)) * kRecWords;
   ExpertWork w;
   const int nu = rec[3];
   w.e = r[0];
@@ -238,7 +280,7 @@ __device__ __forceinline__ ExpertWork load_work(const Args& a, int layer, int u)
 #pragma unroll
   for (int i = 0; i < MOE_ROUND_MAX_ROWS / 4; ++i) w.rows[i] = r[kRecRowWord + i];
   const int npairs = a.T * a.k;
-  w.nu = min(max(nu, 0), a.Ucap);
+  w.nu = min(max(nu, 0), a.Icap);
   w.e = min(max(w.e, 0), a.E - 1);
   w.p0 = min(max(w.p0, 0), npairs);
   w.np = min(max(w.np, 0), npairs - w.p0);
