@@ -216,7 +216,13 @@ constexpr int kGuOneRow = 0, kGuPairs = 1, kGuStaged = 2;
 
 // MODE: kGuOneRow (T == 1), kGuPairs (verify rounds: rows two at a time from L2), kGuStaged (wide
 // rounds: rows staged in LDS, matrix-core tile for items with many rows).
-template <int G, int NB, int RW, int MODE>
+// SEL > 0 (verify rounds): the block first computes the round's selection itself from the logits
+// (select_block with SEL keys per lane), finds its work item in LDS, and block 0 publishes the
+// records and outputs that the down kernel and the caller read; no separate selection launch.
+// SEL == 0: the work item comes from the records written by select_kernel.
+constexpr int kFusedPairs = 256;  // (row, rank) pairs of a round with the selection fused in
+
+template <int G, int NB, int RW, int MODE, int SEL>
 __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
   constexpr int RPI = 64 / G;
   constexpr int ROWS_W = RW * RPI;
@@ -227,8 +233,16 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
   const int nblk = H / 32;
   const int tiles = (I + ROWS_B - 1) / ROWS_B;
   const int u = blockIdx.x / tiles, tile = blockIdx.x - u * tiles;
-  const ExpertWork wk = load_work(a, layer, u);
-  if (u >= wk.nu) return;
+  ExpertWork wk;
+  if constexpr (SEL > 0) {
+    __shared__ SelectSharedT<kFusedPairs, kWaves> ssel;
+    select_block<SEL, kThreads>(a, layer, ssel, blockIdx.x == 0);
+    if (u >= ssel.ni) return;
+    wk = work_from_lds(a, ssel, u);
+  } else {
+    wk = load_work(a, layer, u);
+    if (u >= wk.nu) return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane % G, rs = lane / G;

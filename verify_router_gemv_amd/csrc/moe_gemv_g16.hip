@@ -2,5 +2,7 @@
 #include "moe_kernels.h"
 
 namespace moe {
-bool pick_gemv_g16(int NB, int RC, bool up, KernelFn* fn, int* rows) { return pick_nb<16>(NB, RC, up, fn, rows); }
+bool pick_gemv_g16(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
+  return pick_nb<16>(NB, RC, up, sel, fn, rows);
+}
 }  // namespace moe

@@ -18,19 +18,24 @@ constexpr int rows_per_lane_group(int NB) { return NB == 1 ? 4 : (NB == 2 ? 2 : 
 template <int G, int NB, int RC>
 struct GemvPick {
   static constexpr int RW = rows_per_lane_group(NB);
-  static KernelFn gateup(int mode) {
-    return mode == kGuOneRow ? gateup_kernel<G, NB, RW, kGuOneRow>
-           : mode == kGuPairs ? gateup_kernel<G, NB, RW, kGuPairs>
-                              : gateup_kernel<G, NB, RW, kGuStaged>;
+  // sel: keys per lane of the fused selection (4: E <= 256, 8: E <= 512), 0: read the records of
+  // the selection kernel (always for the staged form).
+  static KernelFn gateup(int mode, int sel) {
+    if (mode == kGuStaged) return gateup_kernel<G, NB, RW, kGuStaged, 0>;
+    if (mode == kGuOneRow)
+      return sel == 4 ? gateup_kernel<G, NB, RW, kGuOneRow, 4>
+             : sel == 8 ? gateup_kernel<G, NB, RW, kGuOneRow, 8> : gateup_kernel<G, NB, RW, kGuOneRow, 0>;
+    return sel == 4 ? gateup_kernel<G, NB, RW, kGuPairs, 4>
+           : sel == 8 ? gateup_kernel<G, NB, RW, kGuPairs, 8> : gateup_kernel<G, NB, RW, kGuPairs, 0>;
   }
   static KernelFn down() { return down_kernel<G, NB, RC, RW>; }
   static constexpr int rows_per_block() { return kWaves * RW * (64 / G); }
 };
 
 template <int G, int NB>
-inline bool pick_rc(int RC, bool up, KernelFn* fn, int* rows) {
+inline bool pick_rc(int RC, bool up, int sel, KernelFn* fn, int* rows) {
   if (up) {  // for gate/up RC is the mode (kGuOneRow, kGuPairs, kGuStaged)
-    *fn = GemvPick<G, NB, 1>::gateup(RC);
+    *fn = GemvPick<G, NB, 1>::gateup(RC, sel);
     *rows = GemvPick<G, NB, 1>::rows_per_block();
     return true;
   }
@@ -47,31 +52,31 @@ inline bool pick_rc(int RC, bool up, KernelFn* fn, int* rows) {
 }
 
 template <int G>
-inline bool pick_nb(int NB, int RC, bool up, KernelFn* fn, int* rows) {
+inline bool pick_nb(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
   switch (NB) {
-    case 1: return pick_rc<G, 1>(RC, up, fn, rows);
-    case 2: return pick_rc<G, 2>(RC, up, fn, rows);
-    case 3: return pick_rc<G, 3>(RC, up, fn, rows);
-    case 4: return pick_rc<G, 4>(RC, up, fn, rows);
+    case 1: return pick_rc<G, 1>(RC, up, sel, fn, rows);
+    case 2: return pick_rc<G, 2>(RC, up, sel, fn, rows);
+    case 3: return pick_rc<G, 3>(RC, up, sel, fn, rows);
+    case 4: return pick_rc<G, 4>(RC, up, sel, fn, rows);
   }
   return false;
 }
 
 // Each lane split G is instantiated in its own translation unit (moe_gemv_g<G>.hip) so the
 // library builds in parallel.
-bool pick_gemv_g4(int NB, int RC, bool up, KernelFn* fn, int* rows);
-bool pick_gemv_g8(int NB, int RC, bool up, KernelFn* fn, int* rows);
-bool pick_gemv_g16(int NB, int RC, bool up, KernelFn* fn, int* rows);
-bool pick_gemv_g32(int NB, int RC, bool up, KernelFn* fn, int* rows);
-bool pick_gemv_g64(int NB, int RC, bool up, KernelFn* fn, int* rows);
+bool pick_gemv_g4(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
+bool pick_gemv_g8(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
+bool pick_gemv_g16(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
+bool pick_gemv_g32(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
+bool pick_gemv_g64(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
 
-inline bool pick_gemv(int G, int NB, int RC, bool up, KernelFn* fn, int* rows) {
+inline bool pick_gemv(int G, int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
   switch (G) {
-    case 4: return pick_gemv_g4(NB, RC, up, fn, rows);
-    case 8: return pick_gemv_g8(NB, RC, up, fn, rows);
-    case 16: return pick_gemv_g16(NB, RC, up, fn, rows);
-    case 32: return pick_gemv_g32(NB, RC, up, fn, rows);
-    case 64: return pick_gemv_g64(NB, RC, up, fn, rows);
+    case 4: return pick_gemv_g4(NB, RC, up, sel, fn, rows);
+    case 8: return pick_gemv_g8(NB, RC, up, sel, fn, rows);
+    case 16: return pick_gemv_g16(NB, RC, up, sel, fn, rows);
+    case 32: return pick_gemv_g32(NB, RC, up, sel, fn, rows);
+    case 64: return pick_gemv_g64(NB, RC, up, sel, fn, rows);
   }
   return false;
 }
@@ -92,6 +97,9 @@ inline KernelFn pick_logits_tc(int H) {
 
 inline KernelFn pick_logits(int H, int T) { return logits_rows(T) == 1 ? pick_logits_tc<1>(H) : pick_logits_tc<2>(H); }
 
+// Keys per lane of the fused selection in the gate/up kernel (E <= 512).
+inline int fused_select_keys(int E) { return E <= 256 ? 4 : 8; }
+
 inline KernelFn pick_select(int E) {
   if (E <= 64) return select_kernel<1>;
   if (E <= 128) return select_kernel<2>;
@@ -102,6 +110,10 @@ inline KernelFn pick_select(int E) {
 // Rounds of at least this many rows are "wide": gate/up stages the input digits in LDS and may use
 // the matrix-core tile.
 constexpr int kWideRows = 16;
+// Rounds of at most this many rows fold the selection into the gate/up kernel: every block
+// recomputes it (cheap for a few rows), which saves a launch, its gap and a dependent load. Beyond,
+// the blocks that find no work item would each still pay for the whole selection.
+constexpr int kFusedMaxRows = 4;
 
 // Rows of one expert processed per register pass, by round width.
 inline int rows_per_pass(int T) { return T == 1 ? 1 : 2; }

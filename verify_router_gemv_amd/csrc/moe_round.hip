@@ -31,9 +31,10 @@ struct Launch {
   int threads;
   int shmem;
   int layer;
+  int kind;  // 0 logits, 1 selection, 2 gate/up, 3 down
 };
 
-constexpr int kKernelsPerLayer = 4;  // logits, select, gate/up, down
+constexpr int kKernelsPerLayer = 4;  // kinds of kernel per layer: logits, select, gate/up, down
 
 struct GraphEntry {
   hipGraph_t graph = nullptr;
@@ -81,6 +82,7 @@ struct moe_round {
   int prof_runs = 0;                   // ring capacity in runs
   std::vector<hipEvent_t> prof_ev;     // [prof_runs][n kernels][2]
   std::vector<int> prof_nk;            // kernels recorded in each ring slot (0 = free)
+  std::vector<int> prof_kind;          // [prof_runs][kernels] accumulator index (layer * 4 + kind)
   int prof_next = 0;
   std::vector<double> prof_ms;         // accumulated milliseconds [L][4]
   int32_t prof_count = 0;              // runs accumulated since the last read
@@ -88,6 +90,7 @@ struct moe_round {
   int32_t last_hip = 0;
   int mfma_rows = 3;                   // gate/up (wide rounds): matrix-core tile from this many rows per item
   int rows_per_item = 0;               // 0: by round width
+  int fused_max_rows = kFusedMaxRows;  // selection folded into gate/up up to this many rows
 };
 
 static moe_status hip_fail(moe_round* h, hipError_t e) {
@@ -152,16 +155,19 @@ static Args base_args(const moe_round* h, int T, int k) {
   return a;
 }
 
+// Launches of a round. Rounds of up to kFusedMaxRows rows run three kernels per layer: the gate/up
+// kernel computes the selection itself. Larger rounds run a separate selection kernel.
 static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   const int E = h->cfg.n_experts, H = h->cfg.hidden, I = h->cfg.inter;
   const int umax = items_bound(T * k, E, rows_per_item(h, T));
   const int RC = rows_per_pass(T);
-  const bool stage = T >= kWideRows;
+  const bool wide = T >= kWideRows;
+  const bool fused = T <= h->fused_max_rows;
   KernelFn lg = pick_logits(H, T), sel = pick_select(E), gu = nullptr, dn = nullptr;
   int rows_gu = 0, rows_dn = 0;
-  const int gu_mode = stage ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
-  if (!lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, &gu, &rows_gu) ||
-      !pick_gemv(h->Gi, h->NBi, RC, false, &dn, &rows_dn))
+  const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
+  if (!lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, fused ? fused_select_keys(E) : 0, &gu, &rows_gu) ||
+      !pick_gemv(h->Gi, h->NBi, RC, false, 0, &dn, &rows_dn))
     return false;
   const int tc = logits_rows(T);
   const dim3 grid_lg((E + kRouteExpertsPerBlock - 1) / kRouteExpertsPerBlock, (T + tc - 1) / tc);
@@ -169,14 +175,14 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   const dim3 grid_dn(umax * ((H + rows_dn - 1) / rows_dn));
   int gu_words = gateup_stage_words(H);
   if (h->Gh == 64 && h->NBh == 1) gu_words += kMfmaExtraWords;  // matrix-core tile: (s, m) tables, partial sums
-  const int shm_gu = stage ? static_cast<int>(sizeof(uint32_t)) * gu_words : 0;
+  const int shm_gu = wide ? static_cast<int>(sizeof(uint32_t)) * gu_words : 0;
   const int shm_dn = T > 1 ? static_cast<int>(sizeof(float)) * xstage_rows(I) * I : 0;
   out->clear();
   for (int l = 0; l < h->cfg.n_layers; ++l) {
-    out->push_back({lg, grid_lg, kThreads, 0, l});
-    out->push_back({sel, dim3(1), kSelectThreads, 0, l});
-    out->push_back({gu, grid_gu, kThreads, shm_gu, l});
-    out->push_back({dn, grid_dn, kThreads, shm_dn, l});
+    out->push_back({lg, grid_lg, kThreads, 0, l, 0});
+    if (!fused) out->push_back({sel, dim3(1), kSelectThreads, 0, l, 1});
+    out->push_back({gu, grid_gu, kThreads, shm_gu, l, 2});
+    out->push_back({dn, grid_dn, kThreads, shm_dn, l, 3});
   }
   return true;
 }
@@ -220,9 +226,13 @@ static moe_status build_graph(moe_round* h, int T, int k, GraphEntry* ge) {
 }
 
 // Eager: every launch carries the ingress pointers and its layer's weights by value.
-static moe_status launch_eager(moe_round* h, int T, int k, hipEvent_t* evs) {
+static moe_status launch_eager(moe_round* h, int T, int k, hipEvent_t* evs, int* kinds = nullptr,
+                               int* n_launched = nullptr) {
   std::vector<Launch> ls;
   if (!plan(h, T, k, &ls)) return MOE_ERR_UNSUPPORTED;
+  if (kinds)
+    for (size_t i = 0; i < ls.size(); ++i) kinds[i] = ls[i].layer * kKernelsPerLayer + ls[i].kind;
+  if (n_launched) *n_launched = static_cast<int>(ls.size());
   Args a = base_args(h, T, k);
   a.in = h->h_ing;
   int i = 0;
@@ -271,10 +281,11 @@ static moe_status harvest(moe_round* h, int slot) {
   hipEvent_t* ev = h->prof_ev.data() + static_cast<size_t>(slot) * 2 * kKernelsPerLayer * h->cfg.n_layers;
   h->prof_nk[slot] = 0;
   MOE_HIP(h, hipEventSynchronize(ev[2 * nk - 1]));
+  const int* kind = h->prof_kind.data() + static_cast<size_t>(slot) * kKernelsPerLayer * h->cfg.n_layers;
   for (int i = 0; i < nk; ++i) {
     float ms = 0.f;
     MOE_HIP(h, hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]));
-    h->prof_ms[i] += ms;
+    h->prof_ms[kind[i]] += ms;
   }
   ++h->prof_count;
   return MOE_OK;
@@ -285,6 +296,7 @@ static void free_profile(moe_round* h) {
     if (ev) (void)hipEventDestroy(ev);
   h->prof_ev.clear();
   h->prof_nk.clear();
+  h->prof_kind.clear();
   h->prof_runs = 0;
 }
 
@@ -328,6 +340,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   h->h_wtab.assign(layers, layers + L);
   if (const char* env = std::getenv("MOE_MFMA_ROWS")) h->mfma_rows = std::atoi(env);  // tuning experiments
   if (const char* env = std::getenv("MOE_ROWS_PER_ITEM")) h->rows_per_item = std::atoi(env);
+  if (const char* env = std::getenv("MOE_FUSED_MAX_ROWS")) h->fused_max_rows = std::atoi(env);
 
   auto fail = [&](hipError_t e) {
     moe_status s = hip_fail(h, e);
@@ -399,9 +412,11 @@ extern "C" moe_status moe_round_run(moe_round* h, const float* hidden, int32_t T
     st = harvest(h, slot);  // a slot is reused only after its previous run has been read
     if (st != MOE_OK) return st;
     hipEvent_t* ev = h->prof_ev.data() + static_cast<size_t>(slot) * 2 * kKernelsPerLayer * h->cfg.n_layers;
-    st = launch_eager(h, T, k, ev);
+    int* kinds = h->prof_kind.data() + static_cast<size_t>(slot) * kKernelsPerLayer * h->cfg.n_layers;
+    int nl = 0;
+    st = launch_eager(h, T, k, ev, kinds, &nl);
     if (st != MOE_OK) return st;
-    h->prof_nk[slot] = kKernelsPerLayer * h->cfg.n_layers;
+    h->prof_nk[slot] = nl;
   } else if (h->cfg.use_graph) {
     st = sync_device_ingress(h);
     if (st != MOE_OK) return st;
@@ -431,6 +446,7 @@ extern "C" moe_status moe_round_profile(moe_round* h, int32_t enable) {
     const int runs = kProfileEvents / per_run > 2 ? kProfileEvents / per_run : 2;
     h->prof_ev.assign(static_cast<size_t>(runs) * per_run, nullptr);
     h->prof_nk.assign(runs, 0);
+    h->prof_kind.assign(static_cast<size_t>(runs) * kKernelsPerLayer * h->cfg.n_layers, 0);
     h->prof_runs = runs;
     h->prof_next = 0;
     for (auto& ev : h->prof_ev) {

@@ -74,28 +74,31 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
 // Kernel 2: selection + worklist (one block)
 // ------------------------------------------------------------------------------------------
 
-struct SelectShared {
-  int sel[MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK];     // [t][j] expert id
-  float p[MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK];     // [t][j] routing weight
+// Selection state of one round in LDS, for up to PMAX (row, rank) pairs and NW waves.
+template <int PMAX, int NW>
+struct SelectSharedT {
+  int sel[PMAX];                                       // [t][j] expert id
+  float p[PMAX];                                       // [t][j] routing weight
   unsigned long long mask[MOE_ROUND_MAX_EXPERTS];      // rows choosing expert e
   int uidx[MOE_ROUND_MAX_EXPERTS];                     // e -> unique index
   int uniq[MOE_ROUND_MAX_EXPERTS];
   int offs[MOE_ROUND_MAX_EXPERTS + 1];
-  int pairs[MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK];   // by pair slot: t | j << 8
   int ioffs[MOE_ROUND_MAX_EXPERTS];                    // unique index -> first work item
-  int item_u[MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK];  // work item -> unique index
-  int wsum[kSelectWaves];
-  int wsum2[kSelectWaves];
-  int nu;
+  int pairs[PMAX];                                     // by pair slot: t | j << 8
+  int item_u[PMAX];                                    // work item -> unique index
+  int wsum[NW];
+  int wsum2[NW];
+  int nu, ni;
 };
+using SelectShared = SelectSharedT<MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK, kSelectWaves>;
 
 // Top-k of one row on one wave. Each lane sorts its NPL (logit, id) keys once; then k rounds pick
 // the largest head: a 32-bit wave max over the heads' high words (sign, exponent and 20 mantissa
 // bits), then a ballot of the lanes holding it; only when several lanes tie there does a 64-bit
 // wave max over those lanes decide. The winner pops its head. Lane j records the j-th id and its
 // exact fp64 logit (read from the owner lane's registers) for the softmax over the k selected.
-template <int NPL>
-__device__ __forceinline__ void select_row(const Args& a, SelectShared& s, int t) {
+template <int NPL, typename SS>
+__device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
   const double* zrow = a.logits + static_cast<size_t>(t) * E;
@@ -154,27 +157,40 @@ __device__ __forceinline__ void select_row(const Args& a, SelectShared& s, int t
   }
 }
 
-template <int NPL>
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int layer) {
-  __shared__ SelectShared s;
+// The selection of one round by one block of NT threads: per-row top-k and softmax, the union of
+// the rows' experts, the counting sort of the (row, rank) pairs by expert and the work items (an
+// expert and at most a.rg of its rows). Results stay in `s`; with `publish` the block also writes
+// the per-item records, the unique list, pair table and pair weights, and the caller's ids and
+// routing weights. Deterministic: every block computing it gets the same result.
+template <int NPL, int NT, typename SS>
+__device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bool publish) {
+  constexpr int NW = NT / 64;
+  constexpr int EPT = (MOE_ROUND_MAX_EXPERTS + NT - 1) / NT;  // experts per thread in the scan
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k, npairs = T * k;
-  const Ingress in = get_ingress(a);
 
-  for (int e = tid; e < E; e += kSelectThreads) s.mask[e] = 0ull;
-  for (int t = wave; t < T; t += kSelectWaves) select_row<NPL>(a, s, t);
+  for (int e = tid; e < E; e += NT) s.mask[e] = 0ull;
+  for (int t = wave; t < T; t += NW) select_row<NPL>(a, s, t);
   __syncthreads();
 
-  for (int idx = tid; idx < npairs; idx += kSelectThreads) atomicOr(&s.mask[s.sel[idx]], 1ull << (idx / k));
+  for (int idx = tid; idx < npairs; idx += NT) atomicOr(&s.mask[s.sel[idx]], 1ull << (idx / k));
   __syncthreads();
 
-  // Block-wide exclusive scan over experts (one per thread, E <= 512 < 1024) of
-  // (rows choosing e, whether any row chose e) and of the work items of e: its rows split into
-  // groups of at most a.rg, so a GEMV block's share of an expert is bounded.
-  const unsigned long long m = tid < E ? s.mask[tid] : 0ull;
-  const int c = __popcll(m), f = c > 0;
-  const int packed = c | (f << 16);
-  const int ng = (c + a.rg - 1) / a.rg;
+  // Block-wide exclusive scan over experts (EPT consecutive experts per thread) of (rows choosing
+  // e, whether any row chose e) and of the work items of e: its rows split into groups of at most
+  // a.rg, so a GEMV block's share of an expert is bounded.
+  int cnt[EPT], pk[EPT], ngs[EPT];
+  int packed = 0, ng = 0;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int e = tid * EPT + q;
+    const int c = e < E ? __popcll(s.mask[e]) : 0;
+    cnt[q] = c;
+    pk[q] = c | ((c > 0) << 16);
+    ngs[q] = (c + a.rg - 1) / a.rg;
+    packed += pk[q];
+    ng += ngs[q];
+  }
   int incl = packed, incl2 = ng;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -192,7 +208,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int laye
   __syncthreads();
   int wpre = 0, wtot = 0, wpre2 = 0, wtot2 = 0;
 #pragma unroll
-  for (int w = 0; w < kSelectWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (w < wave) {
       wpre += s.wsum[w];
       wpre2 += s.wsum2[w];
@@ -200,37 +216,45 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int laye
     wtot += s.wsum[w];
     wtot2 += s.wsum2[w];
   }
-  const int excl = incl - packed + wpre;
-  const int u = excl >> 16, off0 = excl & 0xFFFF;
-  const int nu = wtot >> 16, ni = wtot2;
-  const int io = incl2 - ng + wpre2;
-  if (f) {
-    s.uidx[tid] = u;
-    s.uniq[u] = tid;
-    s.offs[u] = off0;
-    s.ioffs[u] = io;
-    for (int gi = 0; gi < ng; ++gi) s.item_u[io + gi] = u;
+  const int nu = min(wtot >> 16, a.Ucap), ni = min(wtot2, a.Icap);
+  int excl = incl - packed + wpre, io = incl2 - ng + wpre2;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int e = tid * EPT + q;
+    if (cnt[q] > 0) {
+      const int u = excl >> 16;
+      s.uidx[e] = u;
+      s.uniq[u] = e;
+      s.offs[u] = excl & 0xFFFF;
+      s.ioffs[u] = io;
+      for (int gi = 0; gi < ngs[q]; ++gi) s.item_u[io + gi] = u;
+    }
+    excl += pk[q];
+    io += ngs[q];
   }
   if (tid == 0) {
     s.nu = nu;
+    s.ni = ni;
     s.offs[nu] = npairs;
   }
   __syncthreads();
-  for (int idx = tid; idx < npairs; idx += kSelectThreads) {
+  for (int idx = tid; idx < npairs; idx += NT) {
     const int t = idx / k, j = idx - t * k;
     const int e = s.sel[idx];
     const int pos = s.offs[s.uidx[e]] + __popcll(s.mask[e] & ((1ull << t) - 1ull));
     s.pairs[pos] = t | (j << 8);
   }
   __syncthreads();
+  if (!publish) return;
 
   // Publish: per-item records, the unique list and pair table, the caller's ids / routing weights.
+  const Ingress in = get_ingress(a);
   int32_t* rec = a.rec + static_cast<size_t>(layer) * a.Icap * kRecWords;
   int32_t* uniq = a.uniq + static_cast<size_t>(layer) * a.Ucap;
   int32_t* offs = a.offs + static_cast<size_t>(layer) * (a.Ucap + 1);
   int32_t* pairs = a.pairs + static_cast<size_t>(layer) * a.Pcap;
   float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
-  for (int i = tid; i < ni * kRecWords; i += kSelectThreads) {
+  for (int i = tid; i < ni * kRecWords; i += NT) {
     const int it = i / kRecWords, wd = i - it * kRecWords;
     const int uu = s.item_u[it];
     const int p0 = s.offs[uu] + (it - s.ioffs[uu]) * a.rg;
@@ -248,9 +272,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int laye
     }
     rec[i] = v;
   }
-  for (int i = tid; i < nu; i += kSelectThreads) uniq[i] = s.uniq[i];
-  for (int i = tid; i <= nu; i += kSelectThreads) offs[i] = s.offs[i];
-  for (int i = tid; i < npairs; i += kSelectThreads) {
+  for (int i = tid; i < nu; i += NT) uniq[i] = s.uniq[i];
+  for (int i = tid; i <= nu; i += NT) offs[i] = s.offs[i];
+  for (int i = tid; i < npairs; i += NT) {
     const int pr = s.pairs[i];
     pairs[i] = pr;
     pw[i] = s.p[(pr & 0xFF) * k + (pr >> 8)];
@@ -259,6 +283,12 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int laye
     if (in.route_w) in.route_w[o] = s.p[i];
   }
   if (tid == 0) a.n_unique[layer] = nu;
+}
+
+template <int NPL>
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int layer) {
+  __shared__ SelectShared s;
+  select_block<NPL, kSelectThreads>(a, layer, s, true);
 }
 
 // Every GEMV block reads its work item's record and record 0 (whose item count is always valid)
@@ -284,6 +314,27 @@ __device__ __forceinline__ ExpertWork load_work(const Args& a, int layer, int u)
   w.e = min(max(w.e, 0), a.E - 1);
   w.p0 = min(max(w.p0, 0), npairs);
   w.np = min(max(w.np, 0), npairs - w.p0);
+  return w;
+}
+
+// The work item `it` of a selection held in LDS (see select_block).
+template <typename SS>
+__device__ __forceinline__ ExpertWork work_from_lds(const Args& a, const SS& s, int it) {
+  ExpertWork w;
+  it = min(it, max(s.ni - 1, 0));
+  const int uu = s.item_u[it];
+  w.nu = s.ni;
+  w.e = s.uniq[uu];
+  w.p0 = s.offs[uu] + (it - s.ioffs[uu]) * a.rg;
+  w.np = min(a.rg, s.offs[uu + 1] - w.p0);
+#pragma unroll
+  for (int i = 0; i < MOE_ROUND_MAX_ROWS / 4; ++i) {
+    int v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (4 * i + b < w.np) v |= (s.pairs[w.p0 + 4 * i + b] & 0xFF) << (8 * b);
+    w.rows[i] = v;
+  }
   return w;
 }
 
