@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--pmc-calibrate", action="store_true",
                    help="finish with a copy of 1 GiB (torch.neg) that calibrates the HBM byte counters")
+    p.add_argument("--no-extra", action="store_true", help="skip the wide-round and deep-stack sections")
     p.add_argument("--no-profile", dest="profile", action="store_false",
                    help="skip the kernel-timing pass (no roofline)")
     return p.parse_args()
@@ -196,12 +197,17 @@ def main():
             "bytes_per_row": int((per_T[str(b)]["metric_bytes"] - per_T[str(a)]["metric_bytes"]) / (b - a)),
         } for a, b in ((1, 3), (3, 8))}
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(cfg, reps[0], acts, args.cpu_seconds)
-
     for h in handles:
         h.close()
+    del handles, reps
+    torch.cuda.empty_cache()
+
+    wide = None if args.no_extra else wide_rounds(cfg, base, torch, np, synth, MoeRound)
+    deep = None if args.no_extra else deep_stack(torch, np, synth, MoeRound)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, base, acts, args.cpu_seconds)
 
     line = {
         "metric": "MoE-round tok/s at T=1/3/8 rows; achieved HBM GB/s vs peak",
@@ -223,6 +229,8 @@ def main():
         "per_T": per_T,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "wide_rounds": wide,
+        "deep_stack": deep,
     }
     print(json.dumps(line), flush=True)
     if args.pmc_calibrate:
@@ -232,6 +240,114 @@ def main():
         for _ in range(3):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
+
+
+INT8_DENSE_PEAK_OPS = 5.0e15
+
+
+def timed_rounds(h, xs, k, out, n, torch):
+    """Median / p10 / p90 microseconds of n synchronised rounds, and the last per-kernel profile."""
+    import numpy as np
+    lat = []
+    for r in range(n):
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        h.run(xs[r % len(xs)], k, out)
+        e.record()
+        e.synchronize()
+        lat.append(s.elapsed_time(e) * 1e3)
+    return float(np.median(lat)), float(np.percentile(lat, 10)), float(np.percentile(lat, 90))
+
+
+def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
+    """Copy-heavy wide verify (T = 16, 32, 64 independent rows, same layer shape): round latency,
+    per-kernel time, unique experts and bytes, with the default tile choice and with the
+    matrix-core tile switched off; MFMA utilisation of the gate/up kernel."""
+    cfg = synth.config("wide")
+    reps = [layer] + [layer.clone() for _ in range(3)]  # 4 x 503 MB: beyond the 256 MB cache
+    res = {}
+    for T in cfg.T:
+        xs = [synth.make_activations(cfg, T, seed=0, round_idx=r, device="cuda") for r in range(16)]
+        out = torch.empty((T, cfg.H), device="cuda")
+        row = {}
+        for name, mfma in (("default", 0), ("no_mfma", -1)):
+            hs = [MoeRound([rp], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=64, use_graph=False, mfma_min_rows=mfma)
+                  for rp in reps]
+            for r in range(8):
+                hs[r % 4].run(xs[r], cfg.k, out)
+            lat = []
+            for r in range(24):
+                med = timed_rounds(hs[r % 4], [xs[r % 16]], cfg.k, out, 1, torch)[0]
+                lat.append(med)
+            nus, mfma_ops = [], 0.0
+            for h in hs:
+                h.profile(True)
+                h.profile_read()
+            for r in range(16):
+                h = hs[r % 4]
+                h.run(xs[r], cfg.k, out)
+                uniq, offs, _ = h.worklist(0)
+                nus.append(len(uniq))
+                for npr in np.diff(offs):  # items of <= 4 rows; those with >= 3 rows take the tile
+                    for it in range(0, int(npr), 4):
+                        rows = min(4, int(npr) - it)
+                        if mfma == 0 and rows >= 3:
+                            mfma_ops += 2.0 * 2 * cfg.I * cfg.H * rows
+            kms, runs = np.zeros(4), 0
+            for h in hs:
+                ms, n = h.profile_read()
+                kms += np.array(ms[0])
+                runs += n
+                h.profile(False)
+                h.close()
+            nu = float(np.mean(nus))
+            mb = synth.inputs.metric_bytes(cfg, nu, T)
+            med = float(np.median(lat))
+            gu_s = kms[2] * 1e-3
+            row[name] = {
+                "round_us_median": round(med, 2), "n_unique": round(nu, 1), "metric_bytes": int(mb),
+                "metric_GBps": round(mb / med / 1e3, 1), "tok_per_s": round(T / med * 1e6, 1),
+                "kernel_us": {n: round(float(v) * 1e3 / runs, 2)
+                              for n, v in zip(("logits", "select", "gateup", "down"), kms)},
+            }
+            if mfma == 0:
+                row[name]["mfma_useful_ops_per_round"] = mfma_ops / 16
+                row[name]["mfma_util_of_int8_peak"] = round(mfma_ops / gu_s / INT8_DENSE_PEAK_OPS, 6) if gu_s else 0.0
+        res[str(T)] = row
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
+def deep_stack(torch, np, synth, MoeRound):
+    """48 MoE layers (E=512, top-10, I=512), T=3, residual, ~48 GB of expert weights resident: one
+    round as one captured hipGraph, and eager, with per-layer unique experts and metric bytes."""
+    cfg = synth.config("deep")
+    t0 = time.perf_counter()
+    layers = [synth.make_layer(cfg, seed=0, layer=l, device="cuda") for l in range(cfg.L)]
+    gen_s = time.perf_counter() - t0
+    T = cfg.T[0]
+    xs = [synth.make_activations(cfg, T, seed=0, round_idx=r, device="cuda") for r in range(8)]
+    out = torch.empty((T, cfg.H), device="cuda")
+    res = {"layers": cfg.L, "T": T, "weights_GB": round(cfg.L * cfg.E * cfg.expert_bytes() / 1e9, 2),
+           "generate_s": round(gen_s, 1)}
+    for mode in ("graph", "eager"):
+        h = MoeRound(layers, cfg.H, cfg.I, cfg.E, cfg.k, max_rows=T, residual=True, use_graph=(mode == "graph"))
+        for r in range(3):
+            h.run(xs[r], cfg.k, out)
+        lat = [timed_rounds(h, [xs[r % 8]], cfg.k, out, 1, torch)[0] for r in range(12)]
+        nus = h.last_unique()
+        med = float(np.median(lat))
+        mb = sum(synth.inputs.metric_bytes(cfg, nu, T) for nu in nus)
+        res[mode] = {"round_us_median": round(med, 1), "per_layer_us": round(med / cfg.L, 2),
+                     "n_unique_mean": round(float(np.mean(nus)), 2), "metric_bytes": int(mb),
+                     "metric_GBps": round(mb / med / 1e3, 1), "tok_per_s": round(T / med * 1e6, 1)}
+        h.close()
+    del layers
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(cfg, layer, acts, seconds):

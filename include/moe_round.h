@@ -89,6 +89,14 @@ typedef struct moe_round_config {
   int32_t max_rows;    /* T_max: 1..64                                            */
   int32_t residual;    /* 0: out = MoE(x), needs L == 1; 1: x_{l+1} = x_l + MoE_l */
   int32_t use_graph;   /* 1: replay one captured hipGraph per (T, k); 0: eager    */
+  /* Launch-shape choices (0 = the default for each; none changes results beyond fp32 rounding
+   * order):                                                                               */
+  int32_t fused_max_rows; /* rounds of up to this many rows fold the selection into the
+                             gate/up kernel; default 4, -1 = never, at most 15             */
+  int32_t rows_per_item;  /* rows of one expert per GEMV work item; default 2 for rounds
+                             under 16 rows, 4 from 16 rows; 1..64                          */
+  int32_t mfma_min_rows;  /* rounds of 16+ rows: work items with at least this many rows
+                             use the int8 matrix-core gate/up tile; default 3, -1 = never  */
 } moe_round_config;
 
 /* One layer's weights (device pointers, caller-owned). router_bias may be NULL. */

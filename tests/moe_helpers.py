@@ -60,13 +60,13 @@ def assert_close(got, ref, what=""):
 class GpuRound:
     """A handle plus reusable device buffers for one shape."""
 
-    def __init__(self, layers, cfg: synth.ShapeConfig, max_rows: int, use_graph=True, k_max=None):
+    def __init__(self, layers, cfg: synth.ShapeConfig, max_rows: int, use_graph=True, k_max=None, **shape):
         from verify_router_gemv_amd import MoeRound
         self.cfg = cfg
         self.layers = layers
         self.k_max = k_max or cfg.k
         self.h = MoeRound(layers, cfg.H, cfg.I, cfg.E, self.k_max, max_rows=max_rows,
-                          residual=cfg.residual, use_graph=use_graph)
+                          residual=cfg.residual, use_graph=use_graph, **shape)
 
     def run(self, X: torch.Tensor, k=None, layers=None, timed=False):
         k = k or self.cfg.k

@@ -60,6 +60,10 @@ def cfg(**kw):
     dict(H=2048, I=512, E=256, top_k_max=8, max_rows=64),
     dict(H=768, I=384, E=40, top_k_max=5, max_rows=16),
     dict(H=8192, I=2048, E=512, top_k_max=16, max_rows=64),
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=8, raw_fused_max_rows=-1, raw_rows_per_item=1,
+         raw_mfma_min_rows=-1),
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=64, raw_fused_max_rows=15, raw_rows_per_item=64,
+         raw_mfma_min_rows=16),
 ])
 def test_supported_configs_validate(lib, kw):
     from verify_router_gemv_amd import binding
@@ -77,6 +81,11 @@ def test_supported_configs_validate(lib, kw):
     (dict(E=4, top_k_max=8), -1),
     (dict(raw_use_graph=2), -1),
     (dict(raw_residual=3), -1),
+    (dict(raw_fused_max_rows=16), -1),
+    (dict(raw_fused_max_rows=-2), -1),
+    (dict(raw_rows_per_item=-1), -1),
+    (dict(raw_rows_per_item=65), -1),
+    (dict(raw_mfma_min_rows=-3), -1),
     (dict(max_rows=65), -2),
     (dict(E=513, top_k_max=8), -2),
     (dict(top_k_max=17, E=256), -2),

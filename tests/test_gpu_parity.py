@@ -212,3 +212,31 @@ def test_many_rows_share_experts(verify):
         _, offs, _ = g.h.worklist(0)
         say(f"  n_unique={nu[0]} max rows per expert={int(np.diff(offs).max())} rel-L2={rel:.2e}")
     g.close()
+
+
+@pytest.mark.parametrize("shape", [
+    dict(fused_max_rows=-1, rows_per_item=1),   # separate selection kernel, one row per item
+    dict(fused_max_rows=15, rows_per_item=8),   # selection in gate/up up to 15 rows, big items
+])
+def test_launch_shape_choices(verify, shape):
+    """Other launch shapes give the same ids and worklists and outputs within tolerance."""
+    cfg, layer, view = verify
+    g = GpuRound([layer], cfg, max_rows=16, **shape)
+    for T in (1, 3, 8, 15):
+        say(f"case launch shape {shape} T={T}")
+        X = synth.make_activations(cfg, T, seed=6, round_idx=T, device=DEV)
+        check_layer_round(g, [view], X, cfg.k, f"shape {shape} T={T}")
+    g.close()
+
+
+@pytest.mark.parametrize("mfma_min_rows", [1, -1])
+def test_wide_tile_choice(verify, mfma_min_rows):
+    """Wide rounds with every work item on the matrix-core tile (1) or none (-1)."""
+    cfg = synth.config("wide")
+    _, layer, view = verify
+    g = GpuRound([layer], cfg, max_rows=64, mfma_min_rows=mfma_min_rows)
+    for T in (16, 64):
+        say(f"case wide T={T} mfma_min_rows={mfma_min_rows}")
+        X = synth.make_activations(cfg, T, seed=7, round_idx=T, device=DEV)
+        check_layer_round(g, [view], X, cfg.k, f"wide T={T} mfma {mfma_min_rows}")
+    g.close()

@@ -37,7 +37,7 @@ class MoeRoundError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "hidden", "inter", "n_experts", "top_k_max", "n_layers", "max_rows",
-        "residual", "use_graph")]
+        "residual", "use_graph", "fused_max_rows", "rows_per_item", "mfma_min_rows")]
 
 
 class LayerWeights(ctypes.Structure):
@@ -86,8 +86,11 @@ def strerror(status: int) -> str:
         return f"status {status}"
 
 
-def make_config(H, I, E, top_k_max, n_layers=1, max_rows=8, residual=False, use_graph=True) -> Config:
-    return Config(ABI_VERSION, H, I, E, top_k_max, n_layers, max_rows, int(bool(residual)), int(bool(use_graph)))
+def make_config(H, I, E, top_k_max, n_layers=1, max_rows=8, residual=False, use_graph=True,
+                fused_max_rows=0, rows_per_item=0, mfma_min_rows=0) -> Config:
+    """Launch-shape fields: 0 = default (see moe_round.h); -1 = never (fused_max_rows, mfma_min_rows)."""
+    return Config(ABI_VERSION, H, I, E, top_k_max, n_layers, max_rows, int(bool(residual)), int(bool(use_graph)),
+                  fused_max_rows, rows_per_item, mfma_min_rows)
 
 
 def validate_config(cfg: Config) -> int:
@@ -143,11 +146,13 @@ class MoeRound:
     """A handle over the C ABI: one MoE round evaluator bound to a stream."""
 
     def __init__(self, layers: Sequence, H: int, I: int, E: int, top_k_max: int, max_rows: int = 8,
-                 residual: bool = False, use_graph: bool = True, stream: Optional[torch.cuda.Stream] = None):
+                 residual: bool = False, use_graph: bool = True, stream: Optional[torch.cuda.Stream] = None,
+                 fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0):
         self.lib = load()
         self.H, self.I, self.E, self.L = H, I, E, len(layers)
         self.top_k_max, self.max_rows = top_k_max, max_rows
-        self.cfg = make_config(H, I, E, top_k_max, self.L, max_rows, residual, use_graph)
+        self.cfg = make_config(H, I, E, top_k_max, self.L, max_rows, residual, use_graph,
+                               fused_max_rows, rows_per_item, mfma_min_rows)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._layers = list(layers)          # keep the weight tensors alive
         self._wt = (LayerWeights * self.L)(*[layer_struct(l, H, I, E) for l in layers])

@@ -9,7 +9,6 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <vector>
@@ -338,9 +337,9 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   h->Ucap = (T * K < E) ? T * K : E;
   h->Icap = T * K;  // work items never outnumber (row, rank) pairs
   h->h_wtab.assign(layers, layers + L);
-  if (const char* env = std::getenv("MOE_MFMA_ROWS")) h->mfma_rows = std::atoi(env);  // tuning experiments
-  if (const char* env = std::getenv("MOE_ROWS_PER_ITEM")) h->rows_per_item = std::atoi(env);
-  if (const char* env = std::getenv("MOE_FUSED_MAX_ROWS")) h->fused_max_rows = std::atoi(env);
+  if (cfg->fused_max_rows != 0) h->fused_max_rows = cfg->fused_max_rows < 0 ? 0 : cfg->fused_max_rows;
+  h->rows_per_item = cfg->rows_per_item;
+  if (cfg->mfma_min_rows != 0) h->mfma_rows = cfg->mfma_min_rows < 0 ? 0 : cfg->mfma_min_rows;
 
   auto fail = [&](hipError_t e) {
     moe_status s = hip_fail(h, e);
