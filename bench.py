@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--pmc-calibrate", action="store_true",
                    help="finish with a copy of 1 GiB (torch.neg) that calibrates the HBM byte counters")
     p.add_argument("--no-extra", action="store_true", help="skip the wide-round and deep-stack sections")
+    p.add_argument("--launch", default="", help="launch-shape fields for the verify sweep, e.g. fused_max_rows=4,rows_per_item=2")
     p.add_argument("--no-profile", dest="profile", action="store_false",
                    help="skip the kernel-timing pass (no roofline)")
     return p.parse_args()
@@ -80,7 +81,8 @@ def main():
     acts = {T: torch.stack([synth.make_activations(cfg, T, seed=0, round_idx=r, device=dev)
                             for r in range(n_acts)]) for T in TS}
     outs = {T: torch.empty((T, cfg.H), device=dev) for T in TS}
-    handles = [MoeRound([reps[i]], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(TS), use_graph=args.graph)
+    shape = {kv.split("=")[0]: int(kv.split("=")[1]) for kv in args.launch.split(",") if kv}
+    handles = [MoeRound([reps[i]], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(TS), use_graph=args.graph, **shape)
                for i in range(args.replicas)]
     R = args.replicas
     nT = len(TS)
@@ -225,7 +227,8 @@ def main():
         "config": {"workload": "verify sweep: one MoE layer, H=2048, E=256, top-8, I=512, Q4 blocks of 32; "
                                "one step = rounds at T=1, 3, 8 (12 rows)",
                    "global_batch": tokens_per_step, "seq_len": 1, "parallelism": "none (1 GPU)",
-                   "mode": "hipGraph" if args.graph else "eager", "weight_replicas": args.replicas},
+                   "mode": "hipGraph" if args.graph else "eager", "weight_replicas": args.replicas,
+                   "launch": shape or "default"},
         "per_T": per_T,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -222,27 +222,15 @@ constexpr int kGuOneRow = 0, kGuPairs = 1, kGuStaged = 2;
 // SEL == 0: the work item comes from the records written by select_kernel.
 constexpr int kFusedPairs = 256;  // (row, rank) pairs of a round with the selection fused in
 
-template <int G, int NB, int RW, int MODE, int SEL>
-__global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
+// One unit of gate/up work: work item `wk`, rows tile * ROWS_B .. of I.
+template <int G, int NB, int RW, int MODE>
+__device__ __forceinline__ void gateup_unit(const Args& a, int layer, const ExpertWork& wk, int tile, uint32_t* xs) {
   constexpr int RPI = 64 / G;
   constexpr int ROWS_W = RW * RPI;
   constexpr int ROWS_B = kWaves * ROWS_W;
-  extern __shared__ uint32_t xs[];  // STAGE: gateup_stage_words(H) words
   const int I = a.I, H = a.H, T = a.T;
   constexpr bool STAGE = MODE == kGuStaged;
   const int nblk = H / 32;
-  const int tiles = (I + ROWS_B - 1) / ROWS_B;
-  const int u = blockIdx.x / tiles, tile = blockIdx.x - u * tiles;
-  ExpertWork wk;
-  if constexpr (SEL > 0) {
-    __shared__ SelectSharedT<kFusedPairs, kWaves> ssel;
-    select_block<SEL, kThreads>(a, layer, ssel, blockIdx.x == 0);
-    if (u >= ssel.ni) return;
-    wk = work_from_lds(a, ssel, u);
-  } else {
-    wk = load_work(a, layer, u);
-    if (u >= wk.nu) return;
-  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane % G, rs = lane / G;
@@ -406,6 +394,30 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
         do_row(0, r0 + rr);
       }
     }
+  }
+}
+
+// Blocks with the selection folded in (SEL > 0) compute it once and then take the units (item,
+// tile) blockIdx.x, blockIdx.x + gridDim.x, ...: the grid is sized for the chip, not for the
+// largest possible item count, so no block repeats the selection only to find no work.
+template <int G, int NB, int RW, int MODE, int SEL>
+__global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
+  constexpr int ROWS_B = kWaves * RW * (64 / G);
+  extern __shared__ uint32_t xs[];  // staged form: gateup_stage_words(H) (+ matrix-core tile) words
+  const int tiles = (a.I + ROWS_B - 1) / ROWS_B;
+  if constexpr (SEL > 0) {
+    __shared__ SelectSharedT<kFusedPairs, kWaves> ssel;
+    select_block<SEL, kThreads>(a, layer, ssel, blockIdx.x == 0);
+    const int units = ssel.ni * tiles;
+    for (int w = blockIdx.x; w < units; w += gridDim.x) {
+      const int u = w / tiles;
+      gateup_unit<G, NB, RW, MODE>(a, layer, work_from_lds(a, ssel, u), w - u * tiles, xs);
+    }
+  } else {
+    const int u = blockIdx.x / tiles, tile = blockIdx.x - u * tiles;
+    const ExpertWork wk = load_work(a, layer, u);
+    if (u >= wk.nu) return;
+    gateup_unit<G, NB, RW, MODE>(a, layer, wk, tile, xs);
   }
 }
 

@@ -111,9 +111,10 @@ inline KernelFn pick_select(int E) {
 // the matrix-core tile.
 constexpr int kWideRows = 16;
 // Rounds of at most this many rows fold the selection into the gate/up kernel: every block
-// recomputes it (cheap for a few rows), which saves a launch, its gap and a dependent load. Beyond,
-// the blocks that find no work item would each still pay for the whole selection.
+// recomputes it (cheap for a few rows), which saves a launch, its gap and a dependent load.
 constexpr int kFusedMaxRows = 4;
+// Gate/up blocks of a round with the selection folded in (each loops over its share of the units).
+constexpr int kFusedBlocks = 768;
 
 // Rows of one expert processed per register pass, by round width.
 inline int rows_per_pass(int T) { return T == 1 ? 1 : 2; }

@@ -170,7 +170,8 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
     return false;
   const int tc = logits_rows(T);
   const dim3 grid_lg((E + kRouteExpertsPerBlock - 1) / kRouteExpertsPerBlock, (T + tc - 1) / tc);
-  const dim3 grid_gu(umax * ((I + rows_gu - 1) / rows_gu));
+  const int units_gu = umax * ((I + rows_gu - 1) / rows_gu);
+  const dim3 grid_gu(fused && units_gu > kFusedBlocks ? kFusedBlocks : units_gu);
   const dim3 grid_dn(umax * ((H + rows_dn - 1) / rows_dn));
   int gu_words = gateup_stage_words(H);
   if (h->Gh == 64 && h->NBh == 1) gu_words += kMfmaExtraWords;  // matrix-core tile: (s, m) tables, partial sums
