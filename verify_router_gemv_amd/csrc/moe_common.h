@@ -332,47 +332,43 @@ __device__ __forceinline__ uint64_t logit_key(double z, int e) {
 __device__ __forceinline__ int key_expert(uint64_t key) { return 511 - static_cast<int>(key & 0x1FFull); }
 
 
-// Digits of one 32-block (see kXqWords). The integer q = rint(x / step) with step = max|x| / kXqMax
-// is split into balanced base-256 digits d0, d1, d2 in [-127, 127]; the block sum is kept in fp32.
-__device__ __forceinline__ void quantize_block(const float* src, uint32_t* dst, float2* ss) {
-  float v[32];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const float4 f = load_f4(src + 4 * q);
-    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
-  }
-  float mx = 0.f, sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) { mx = fmaxf(mx, fabsf(v[i])); sum += v[i]; }
+// Digits of two 32-blocks by one wave (see kXqWords): lanes 0-31 take block qb, lanes 32-63 block
+// qb + 1, one element per lane. The integer q = rint(x / step) with step = max|x| / kXqMax is split
+// into balanced base-256 digits d0, d1, d2 in [-127, 127], each lane storing its three digit bytes
+// at their places in the even / odd words; the block sum is kept in fp32. Blocks at or past nq are
+// skipped (their lanes still take part in the reductions, on a clamped block).
+__device__ __forceinline__ void quantize_block_pair(const float* x, uint32_t* xq, float2* xss, int qb, int nq) {
+  const int lane = threadIdx.x & 63, e = lane & 31;
+  const int b = qb + (lane >> 5);
+  const float v = x[static_cast<size_t>(min(b, nq - 1)) * 32 + e];
+  float mx = fabsf(v), sum = v;
+  mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
+  sum += dpp_f32<kDppXor1>(sum);
+  mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
+  sum += dpp_f32<kDppXor2>(sum);
+  mx = fmaxf(mx, dpp_f32<kDppHalfMirror>(mx));
+  sum += dpp_f32<kDppHalfMirror>(sum);
+  mx = fmaxf(mx, dpp_f32<kDppMirror>(mx));
+  sum += dpp_f32<kDppMirror>(sum);
+  mx = fmaxf(mx, swap_partner_f32<false>(mx));  // the other 16-lane row of this half
+  sum += swap_partner_f32<false>(sum);
   const float inv = mx > 0.f ? kXqMax / mx : 0.f;
-  uint32_t d[3][8];  // digit planes, 4 bytes per word in element order 0..31
-#pragma unroll
-  for (int w = 0; w < 8; ++w) { d[0][w] = 0u; d[1][w] = 0u; d[2][w] = 0u; }
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    int q = static_cast<int>(rintf(v[i] * inv));
-    q = max(-static_cast<int>(kXqMax), min(static_cast<int>(kXqMax), q));
-    const int d0 = ((q + 128) & 255) - 128;
-    const int q1 = (q - d0) >> 8;
-    const int d1 = ((q1 + 128) & 255) - 128;
-    const int d2 = (q1 - d1) >> 8;
-    const int w = i >> 2, sh = 8 * (i & 3);
-    d[0][w] |= (static_cast<uint32_t>(d0) & 0xFFu) << sh;
-    d[1][w] |= (static_cast<uint32_t>(d1) & 0xFFu) << sh;
-    d[2][w] |= (static_cast<uint32_t>(d2) & 0xFFu) << sh;
+  int q = static_cast<int>(rintf(v * inv));
+  q = max(-static_cast<int>(kXqMax), min(static_cast<int>(kXqMax), q));
+  const int d0 = ((q + 128) & 255) - 128;
+  const int q1 = (q - d0) >> 8;
+  const int d1 = ((q1 + 128) & 255) - 128;
+  const int d2 = (q1 - d1) >> 8;
+  if (b < nq) {
+    // element e = 8g + i sits in word (plane * 4 + g) * 2 + (i & 1), byte i >> 1
+    uint8_t* dst = reinterpret_cast<uint8_t*>(xq + static_cast<size_t>(b) * kXqWords);
+    const int g = e >> 3, i = e & 7;
+    const int off = ((g * 2 + (i & 1)) * 4) + (i >> 1);
+    dst[off] = static_cast<uint8_t>(d0 & 0xFF);
+    dst[32 + off] = static_cast<uint8_t>(d1 & 0xFF);
+    dst[64 + off] = static_cast<uint8_t>(d2 & 0xFF);
+    if (e == 0) xss[b] = make_float2(mx / kXqMax, sum);
   }
-  // regroup each 8-element group into even (0,2,4,6) and odd (1,3,5,7) words
-#pragma unroll
-  for (int dg = 0; dg < 3; ++dg)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t a0 = d[dg][2 * g], a1 = d[dg][2 * g + 1];  // bytes of elements 8g..8g+3, 8g+4..8g+7
-      const uint32_t even = __builtin_amdgcn_perm(a1, a0, 0x06040200u);  // bytes e0 e2 | e4 e6
-      const uint32_t odd = __builtin_amdgcn_perm(a1, a0, 0x07050301u);   // bytes e1 e3 | e5 e7
-      dst[(dg * 4 + g) * 2 + 0] = even;
-      dst[(dg * 4 + g) * 2 + 1] = odd;
-    }
-  *ss = make_float2(mx / kXqMax, sum);
 }
 
 }  // namespace moe

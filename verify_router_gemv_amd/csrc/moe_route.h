@@ -44,9 +44,9 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
     float4* xn4 = reinterpret_cast<float4*>(xn);
     for (int i = blockIdx.x * kThreads + tid; i < n4; i += gridDim.x * kThreads)
       xn4[i] = a.residual ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const int nblk = H / 32;
-    for (int i = blockIdx.x * kThreads + tid; i < T * nblk; i += gridDim.x * kThreads)
-      quantize_block(x + static_cast<size_t>(i) * 32, a.xq + static_cast<size_t>(i) * kXqWords, a.xss + i);
+    const int nq = T * (H / 32);  // 32-blocks of the layer input, two per wave
+    for (int qb = 2 * (blockIdx.x * kWaves + wave); qb < nq; qb += 2 * gridDim.x * kWaves)
+      quantize_block_pair(x, a.xq, a.xss, qb, nq);
   }
 
   double acc[TC];
