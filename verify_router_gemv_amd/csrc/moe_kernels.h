@@ -116,7 +116,8 @@ constexpr int kFusedMaxRows = 4;
 // Gate/up blocks of a round with the selection folded in (each loops over its share of the units).
 constexpr int kFusedBlocks = 768;
 
-// Rows of one expert processed per register pass, by round width.
-inline int rows_per_pass(int T) { return T == 1 ? 1 : 2; }
+// Rows of one item processed per register pass in the down kernel: two for small verify rounds;
+// one from 5 rows on, where the lighter one-row form (more blocks resident) wins.
+inline int rows_per_pass(int T) { return (T >= 2 && T <= 4) ? 2 : 1; }
 
 }  // namespace moe
