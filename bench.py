@@ -131,7 +131,7 @@ def main():
         first = sc[0]
         for _ in range(args.steps):
             step()
-        kms, runs = np.zeros(4), 0
+        kms, runs = np.zeros(5), 0
         for h in handles:
             ms, n = h.profile_read()
             kms += np.array(ms[0])
@@ -146,9 +146,9 @@ def main():
                     "avg_launch_us": round(kms[2] * 1e3 / runs, 3),
                     "avg_bytes_per_launch": int(gu_bytes / runs),
                     "kernel_share": {n: round(float(v / kms.sum()), 3)
-                                     for n, v in zip(("logits", "select", "gateup", "down"), kms)},
+                                     for n, v in zip(("logits", "select", "gateup", "down", "combine"), kms)},
                     "avg_kernel_us": {n: round(float(v) * 1e3 / runs, 3)
-                                      for n, v in zip(("logits", "select", "gateup", "down"), kms)}}
+                                      for n, v in zip(("logits", "select", "gateup", "down", "combine"), kms)}}
 
     # Per-width round latency (eager, events on torch's current stream = the handles' stream,
     # one synchronised round at a time) and per-kernel durations; outside the timed region.
@@ -171,7 +171,7 @@ def main():
             h.profile_read()
         for r in range(64):
             handles[(sc[0] + r) % R].run(acts[T][r % n_acts], cfg.k, outs[T])
-        kms, runs = np.zeros(4), 0
+        kms, runs = np.zeros(5), 0
         for h in handles:
             ms, n = h.profile_read()
             kms += np.array(ms[0])
@@ -190,7 +190,7 @@ def main():
             "metric_bytes": int(mb),
             "metric_GBps": round(mb / med / 1e3, 1),
             "kernel_us": {n: round(float(v) * 1e3 / runs, 2) for n, v in
-                          zip(("logits", "select", "gateup", "down"), kms)},
+                          zip(("logits", "select", "gateup", "down", "combine"), kms)},
         }
     # extra verify-row cost, T=1 -> 3 -> 8
     per_T["extra_row"] = {
@@ -204,6 +204,7 @@ def main():
     del handles, reps
     torch.cuda.empty_cache()
 
+    exact = None if args.no_extra else exact_rounds(cfg, base, acts, torch, np, MoeRound)
     wide = None if args.no_extra else wide_rounds(cfg, base, torch, np, synth, MoeRound)
     deep = None if args.no_extra else deep_stack(torch, np, synth, MoeRound)
 
@@ -232,6 +233,7 @@ def main():
         "per_T": per_T,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "exact_mode": exact,
         "wide_rounds": wide,
         "deep_stack": deep,
     }
@@ -262,6 +264,39 @@ def timed_rounds(h, xs, k, out, n, torch):
         e.synchronize()
         lat.append(s.elapsed_time(e) * 1e3)
     return float(np.median(lat)), float(np.percentile(lat, 10)), float(np.percentile(lat, 90))
+
+
+def exact_rounds(cfg, layer, acts, torch, np, MoeRound):
+    """The verify sweep in exact mode (fixed-order combine, bitwise row-independent outputs):
+    median round latency and per-kernel time per width, on 8 weight replicas."""
+    reps = [layer] + [layer.clone() for _ in range(7)]
+    hs = [MoeRound([rp], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(TS), use_graph=False, exact=True) for rp in reps]
+    res = {}
+    for T in TS:
+        out = torch.empty((T, cfg.H), device="cuda")
+        for r in range(8):
+            hs[r % 8].run(acts[T][r], cfg.k, out)
+        lat = [timed_rounds(hs[r % 8], [acts[T][r]], cfg.k, out, 1, torch)[0] for r in range(48)]
+        for h in hs:
+            h.profile(True)
+            h.profile_read()
+        for r in range(48):
+            hs[r % 8].run(acts[T][r], cfg.k, out)
+        kms, runs = np.zeros(5), 0
+        for h in hs:
+            ms, n = h.profile_read()
+            kms += np.array(ms[0])
+            runs += n
+            h.profile(False)
+        med = float(np.median(lat))
+        res[str(T)] = {"round_us_median": round(med, 2), "tok_per_s": round(T / med * 1e6, 1),
+                       "kernel_us": {n: round(float(v) * 1e3 / runs, 2)
+                                     for n, v in zip(("logits", "select", "gateup", "down", "combine"), kms)}}
+    for h in hs:
+        h.close()
+    del reps
+    torch.cuda.empty_cache()
+    return res
 
 
 def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
@@ -298,7 +333,7 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
                         rows = min(4, int(npr) - it)
                         if mfma == 0 and rows >= 3:
                             mfma_ops += 2.0 * 2 * cfg.I * cfg.H * rows
-            kms, runs = np.zeros(4), 0
+            kms, runs = np.zeros(5), 0
             for h in hs:
                 ms, n = h.profile_read()
                 kms += np.array(ms[0])
@@ -313,7 +348,7 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
                 "round_us_median": round(med, 2), "n_unique": round(nu, 1), "metric_bytes": int(mb),
                 "metric_GBps": round(mb / med / 1e3, 1), "tok_per_s": round(T / med * 1e6, 1),
                 "kernel_us": {n: round(float(v) * 1e3 / runs, 2)
-                              for n, v in zip(("logits", "select", "gateup", "down"), kms)},
+                              for n, v in zip(("logits", "select", "gateup", "down", "combine"), kms)},
             }
             if mfma == 0:
                 row[name]["mfma_useful_ops_per_round"] = mfma_ops / 16

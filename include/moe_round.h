@@ -97,6 +97,11 @@ typedef struct moe_round_config {
                              under 16 rows, 4 from 16 rows; 1..64                          */
   int32_t mfma_min_rows;  /* rounds of 16+ rows: work items with at least this many rows
                              use the int8 matrix-core gate/up tile; default 3, -1 = never  */
+  int32_t exact;          /* 1: fixed-order combine. The down stage stores each (row, rank)
+                             product W_d h and a combine kernel adds them to the residual in
+                             rank order: results are bitwise reproducible, and a row's output
+                             does not depend on the other rows of the round or on T. (The
+                             matrix-core tile is not used.) 0: fp32 atomics (faster).       */
 } moe_round_config;
 
 /* One layer's weights (device pointers, caller-owned). router_bias may be NULL. */
@@ -174,8 +179,9 @@ MOE_ROUND_API moe_status moe_round_profile(moe_round* h, int32_t enable);
 
 /*
  * Sum of the per-kernel durations (milliseconds) of the runs profiled since profiling was
- * enabled or last read, into host double [L][4] (router logits, selection + worklist, gate/up,
- * down), and their number of runs into *n_runs; then resets both.  Synchronises on the
+ * enabled or last read, into host double [L][5] (router logits, selection + worklist, gate/up,
+ * down, combine; a kind a round does not launch stays 0), and their number of runs into *n_runs;
+ * then resets both.  Synchronises on the
  * outstanding events.  MOE_ERR_STATE if profiling was never enabled on this handle.
  */
 MOE_ROUND_API moe_status moe_round_profile_read(moe_round* h, double* kernel_ms, int32_t* n_runs);

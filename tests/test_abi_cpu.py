@@ -86,6 +86,7 @@ def test_supported_configs_validate(lib, kw):
     (dict(raw_rows_per_item=-1), -1),
     (dict(raw_rows_per_item=65), -1),
     (dict(raw_mfma_min_rows=-3), -1),
+    (dict(raw_exact=2), -1),
     (dict(max_rows=65), -2),
     (dict(E=513, top_k_max=8), -2),
     (dict(top_k_max=17, E=256), -2),
@@ -119,7 +120,7 @@ def test_null_and_bad_arguments_are_refused_before_any_gpu_call(lib):
     assert lib.moe_round_last_hip_error(None) == 0
     assert lib.moe_round_profile(None, 1) == -1
     n = ctypes.c_int32()
-    ms = (ctypes.c_double * 4)()
+    ms = (ctypes.c_double * 5)()
     assert lib.moe_round_profile_read(None, ms, ctypes.byref(n)) == -1
     lib.moe_round_destroy(None)
 

@@ -1,0 +1,82 @@
+"""Exact mode (fixed-order combine): parity with the oracle, bitwise reproducibility, and bitwise
+independence of a row's output from the other rows of its round (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from moe_helpers import GpuRound, check_layer_round, oracle_view, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def verify():
+    cfg = synth.config("verify")
+    layer = synth.make_layer(cfg, seed=0, layer=0, device=DEV)
+    return cfg, layer, oracle_view(layer)
+
+
+def test_exact_parity(verify):
+    cfg, layer, view = verify
+    g = GpuRound([layer], cfg, max_rows=64, exact=True)
+    for T in (1, 3, 8, 13, 64):
+        say(f"case exact parity T={T}")
+        X = synth.make_activations(cfg, T, seed=8, round_idx=T, device=DEV)
+        check_layer_round(g, [view], X, cfg.k, f"exact T={T}")
+    g.close()
+
+
+def test_exact_is_reproducible(verify):
+    cfg, layer, _ = verify
+    g = GpuRound([layer], cfg, max_rows=64, exact=True)
+    for T in (3, 8, 40):
+        say(f"case exact reproducible T={T}")
+        X = synth.make_activations(cfg, T, seed=9, round_idx=T, device=DEV)
+        first = g.run(X)[0]
+        for _ in range(3):
+            assert np.array_equal(g.run(X)[0], first)
+    g.close()
+
+
+@pytest.mark.parametrize("T", [3, 8, 13, 24])
+def test_exact_row_outputs_do_not_depend_on_the_round(verify, T):
+    """Each row of a T-row round equals, bitwise, the same row evaluated alone, and reversing the
+    rows reverses the outputs bitwise: covers the folded selection (T <= 4), the selection kernel
+    (T >= 5) and the staged gate/up (T >= 16)."""
+    cfg, layer, _ = verify
+    g = GpuRound([layer], cfg, max_rows=64, exact=True)
+    say(f"case exact row invariance T={T}")
+    X = synth.make_activations(cfg, T, seed=10, round_idx=T, device=DEV)
+    out = g.run(X)[0]
+    for t in range(T):
+        alone = g.run(X[t:t + 1].contiguous())[0]
+        assert np.array_equal(alone[0], out[t]), f"row {t}"
+    rev = g.run(X.flip(0).contiguous())[0]
+    assert np.array_equal(rev[::-1], out)
+    g.close()
+
+
+def test_exact_stack_row_invariance():
+    """Six layers of the 512-expert stack (residual): rows evaluated together equal rows alone."""
+    cfg = synth.config("deep").replace(L=6)
+    layers = [synth.make_layer(cfg, seed=0, layer=l, device=DEV) for l in range(cfg.L)]
+    g = GpuRound(layers, cfg, max_rows=3, exact=True)
+    X = synth.make_activations(cfg, 3, seed=11, round_idx=0, device=DEV)
+    say("case exact 6-layer stack")
+    out, ids, _, _ = g.run(X)
+    views = [oracle_view(l) for l in layers]
+    ref, rids, _, gaps = oracle.moe_round(views, X.cpu().numpy(), cfg.k, residual=True)
+    if gaps.min() >= 1e-5:
+        for l in range(cfg.L):
+            assert np.array_equal(ids[l], rids[l]), f"layer {l}"
+        Xh = X.cpu().numpy()
+        rel = np.linalg.norm((out - Xh) - (ref - Xh)) / np.linalg.norm(ref - Xh)
+        assert rel < 1e-4, rel
+    for t in range(3):
+        alone = g.run(X[t:t + 1].contiguous())[0]
+        assert np.array_equal(alone[0], out[t]), f"row {t}"
+    g.close()

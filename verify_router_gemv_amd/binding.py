@@ -20,7 +20,8 @@ ABI_VERSION = 1
 MAX_ROWS = 64
 MAX_EXPERTS = 512
 MAX_TOPK = 16
-KERNELS_PER_LAYER = 4
+KERNELS_PER_LAYER = 5
+KERNEL_NAMES = ("logits", "select", "gateup", "down", "combine")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_OOM, ERR_STATE = 0, -1, -2, -3, -4, -5
 
@@ -37,7 +38,7 @@ class MoeRoundError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "hidden", "inter", "n_experts", "top_k_max", "n_layers", "max_rows",
-        "residual", "use_graph", "fused_max_rows", "rows_per_item", "mfma_min_rows")]
+        "residual", "use_graph", "fused_max_rows", "rows_per_item", "mfma_min_rows", "exact")]
 
 
 class LayerWeights(ctypes.Structure):
@@ -87,10 +88,11 @@ def strerror(status: int) -> str:
 
 
 def make_config(H, I, E, top_k_max, n_layers=1, max_rows=8, residual=False, use_graph=True,
-                fused_max_rows=0, rows_per_item=0, mfma_min_rows=0) -> Config:
-    """Launch-shape fields: 0 = default (see moe_round.h); -1 = never (fused_max_rows, mfma_min_rows)."""
+                fused_max_rows=0, rows_per_item=0, mfma_min_rows=0, exact=False) -> Config:
+    """Launch-shape fields: 0 = default (see moe_round.h); -1 = never (fused_max_rows, mfma_min_rows).
+    exact: fixed-order combine (bitwise reproducible, row outputs independent of the round)."""
     return Config(ABI_VERSION, H, I, E, top_k_max, n_layers, max_rows, int(bool(residual)), int(bool(use_graph)),
-                  fused_max_rows, rows_per_item, mfma_min_rows)
+                  fused_max_rows, rows_per_item, mfma_min_rows, int(bool(exact)))
 
 
 def validate_config(cfg: Config) -> int:
@@ -147,12 +149,12 @@ class MoeRound:
 
     def __init__(self, layers: Sequence, H: int, I: int, E: int, top_k_max: int, max_rows: int = 8,
                  residual: bool = False, use_graph: bool = True, stream: Optional[torch.cuda.Stream] = None,
-                 fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0):
+                 fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0, exact: bool = False):
         self.lib = load()
         self.H, self.I, self.E, self.L = H, I, E, len(layers)
         self.top_k_max, self.max_rows = top_k_max, max_rows
         self.cfg = make_config(H, I, E, top_k_max, self.L, max_rows, residual, use_graph,
-                               fused_max_rows, rows_per_item, mfma_min_rows)
+                               fused_max_rows, rows_per_item, mfma_min_rows, exact)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._layers = list(layers)          # keep the weight tensors alive
         self._wt = (LayerWeights * self.L)(*[layer_struct(l, H, I, E) for l in layers])
@@ -201,8 +203,8 @@ class MoeRound:
         self._profiling = bool(enable)
 
     def profile_read(self):
-        """(sum of milliseconds [L][4] per kernel: logits, select, gate/up, down; number of runs)
-        since profiling started or was last read."""
+        """(sum of milliseconds [L][5] per kernel kind (KERNEL_NAMES); number of runs) since profiling
+        started or was last read."""
         ms = (ctypes.c_double * (KERNELS_PER_LAYER * self.L))()
         n = ctypes.c_int32()
         st = self.lib.moe_round_profile_read(self.h, ms, ctypes.byref(n))
@@ -211,7 +213,7 @@ class MoeRound:
         return [[ms[KERNELS_PER_LAYER * l + i] for i in range(KERNELS_PER_LAYER)] for l in range(self.L)], n.value
 
     def run_timed(self, hidden, k, out, ids=None, route_w=None, layers=None):
-        """One run with per-kernel timing; returns [L][4] milliseconds (synchronises)."""
+        """One run with per-kernel timing; returns [L][5] milliseconds by KERNEL_NAMES (synchronises)."""
         was = self._profiling
         if not was:
             self.profile(True)

@@ -73,6 +73,8 @@ struct Args {
   float* pair_w;      // [L][Pcap]
   int32_t* rec;       // [L][Icap][kRecWords] per-work-item records
   float* hbuf;        // [Pcap][I]
+  float* ybuf;        // exact mode: [Pcap][H] down products W_d h per pair slot
+  int32_t* slot_of;   // [L][Pcap] pair slot of (row t, rank j) at t * k + j
   uint32_t* xq;       // [T_max][H/32][kXqWords] int8 digits of the layer input, per 32-block
   float2* xss;        // [T_max][H/32] (digit step, block sum) of the layer input
   int32_t H, I, E, L, T, k, residual, Ucap, Pcap;
@@ -81,6 +83,7 @@ struct Args {
   int32_t xstage_h;  // gate/up: rows of input digits staged in LDS at a time (T > 1)
   int32_t xstage_i;  // down: SwiGLU rows staged in LDS at a time (T > 1)
   int32_t mfma_rows;  // gate/up: experts with at least this many rows use the matrix-core tile (0: never)
+  int32_t exact;      // fixed-order combine (the logits kernel does not seed the output)
 };
 
 __device__ __forceinline__ Ingress get_ingress(const Args& a) { return a.ing ? *a.ing : a.in; }

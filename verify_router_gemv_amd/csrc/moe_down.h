@@ -6,7 +6,9 @@
 namespace moe {
 
 
-template <int G, int NB, int RC, int RW>
+// EXACT: store W_d h of each pair in its slot of ybuf (the combine kernel adds them in rank order)
+// instead of adding the weighted product into the output with an atomic.
+template <int G, int NB, int RC, int RW, bool EXACT>
 __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   constexpr int RPI = 64 / G;
   constexpr int ROWS_W = RW * RPI;
@@ -76,17 +78,50 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
         for (int r = 0; r < RC; ++r) {
           if (c + r >= ns) continue;
           const int slot = s0 + c + r;
-          const int t = work_row(wk, slot, T);
-          const float wgt = wpass[r];
+          if constexpr (EXACT) {
+            float* y = a.ybuf + static_cast<size_t>(wk.p0 + slot) * H;
 #pragma unroll
-          for (int w = 0; w < RW; ++w) {
-            const int hr = row0 + w * RPI;
-            if (hr < H) atomicAdd(xn + static_cast<size_t>(t) * H + hr, wgt * acc[w][r]);
+            for (int w = 0; w < RW; ++w) {
+              const int hr = row0 + w * RPI;
+              if (hr < H) y[hr] = acc[w][r];
+            }
+          } else {
+            const int t = work_row(wk, slot, T);
+            const float wgt = wpass[r];
+#pragma unroll
+            for (int w = 0; w < RW; ++w) {
+              const int hr = row0 + w * RPI;
+              if (hr < H) atomicAdd(xn + static_cast<size_t>(t) * H + hr, wgt * acc[w][r]);
+            }
           }
         }
       }
     }
   }
+}
+
+// Exact mode: out[t][h] = (residual ? x[t][h] : 0) + sum over ranks j = 0..k-1, in that order, of
+// p[t][j] * y[slot(t, j)][h]. Grid (T, ceil(H / 1024)) x 256 threads, four columns per thread.
+static __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int layer) {
+  const Ingress in = get_ingress(a);
+  const float* __restrict__ x = layer_input(a, in, layer);
+  float* __restrict__ xn = layer_output(a, in, layer);
+  const int t = blockIdx.x, H = a.H, k = a.k;
+  const int h = (blockIdx.y * kThreads + threadIdx.x) * 4;
+  if (h >= H) return;
+  const int32_t* slot_of = a.slot_of + static_cast<size_t>(layer) * a.Pcap + t * k;
+  const float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
+  float4 acc = a.residual ? load_f4(x + static_cast<size_t>(t) * H + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int s = min(max(slot_of[j], 0), a.Pcap - 1);
+    const float w = pw[s];
+    const float4 y = load_f4(a.ybuf + static_cast<size_t>(s) * H + h);
+    acc.x = fmaf(w, y.x, acc.x);
+    acc.y = fmaf(w, y.y, acc.y);
+    acc.z = fmaf(w, y.z, acc.z);
+    acc.w = fmaf(w, y.w, acc.w);
+  }
+  *reinterpret_cast<float4*>(xn + static_cast<size_t>(t) * H + h) = acc;
 }
 
 }  // namespace moe

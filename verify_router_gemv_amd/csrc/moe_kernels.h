@@ -28,13 +28,13 @@ struct GemvPick {
     return sel == 4 ? gateup_kernel<G, NB, RW, kGuPairs, 4>
            : sel == 8 ? gateup_kernel<G, NB, RW, kGuPairs, 8> : gateup_kernel<G, NB, RW, kGuPairs, 0>;
   }
-  static KernelFn down() { return down_kernel<G, NB, RC, RW>; }
+  static KernelFn down(bool exact) { return exact ? down_kernel<G, NB, RC, RW, true> : down_kernel<G, NB, RC, RW, false>; }
   static constexpr int rows_per_block() { return kWaves * RW * (64 / G); }
 };
 
 template <int G, int NB>
 inline bool pick_rc(int RC, bool up, int sel, KernelFn* fn, int* rows) {
-  if (up) {  // for gate/up RC is the mode (kGuOneRow, kGuPairs, kGuStaged)
+  if (up) {  // for gate/up RC is the mode (kGuOneRow, kGuPairs, kGuStaged); for down sel != 0: exact
     *fn = GemvPick<G, NB, 1>::gateup(RC, sel);
     *rows = GemvPick<G, NB, 1>::rows_per_block();
     return true;
@@ -42,7 +42,7 @@ inline bool pick_rc(int RC, bool up, int sel, KernelFn* fn, int* rows) {
   switch (RC) {
 #define MOE_RC(R)                                 \
   case R:                                         \
-    *fn = GemvPick<G, NB, R>::down();             \
+    *fn = GemvPick<G, NB, R>::down(sel != 0);     \
     *rows = GemvPick<G, NB, R>::rows_per_block(); \
     return true;
     MOE_RC(1) MOE_RC(2) MOE_RC(4)

@@ -30,10 +30,10 @@ struct Launch {
   int threads;
   int shmem;
   int layer;
-  int kind;  // 0 logits, 1 selection, 2 gate/up, 3 down
+  int kind;  // 0 logits, 1 selection, 2 gate/up, 3 down, 4 combine
 };
 
-constexpr int kKernelsPerLayer = 4;  // kinds of kernel per layer: logits, select, gate/up, down
+constexpr int kKernelsPerLayer = 5;  // kinds of kernel per layer: logits, select, gate/up, down, combine
 
 struct GraphEntry {
   hipGraph_t graph = nullptr;
@@ -63,6 +63,8 @@ struct moe_round {
   float* pair_w = nullptr;
   int32_t* rec = nullptr;
   float* hbuf = nullptr;
+  float* ybuf = nullptr;               // exact mode: [Pcap][H]
+  int32_t* slot_of = nullptr;          // [L][Pcap]
   uint32_t* xq = nullptr;
   float2* xss = nullptr;
   // host state
@@ -135,6 +137,9 @@ static Args base_args(const moe_round* h, int T, int k) {
   a.pair_w = h->pair_w;
   a.rec = h->rec;
   a.hbuf = h->hbuf;
+  a.ybuf = h->ybuf;
+  a.slot_of = h->slot_of;
+  a.exact = h->cfg.exact;
   a.xq = h->xq;
   a.xss = h->xss;
   a.H = h->cfg.hidden;
@@ -149,7 +154,7 @@ static Args base_args(const moe_round* h, int T, int k) {
   a.rg = rows_per_item(h, T);
   a.Pcap = h->Pcap;
   a.xstage_h = gateup_stage_rows(h->cfg.hidden);
-  a.mfma_rows = h->mfma_rows;
+  a.mfma_rows = h->cfg.exact ? 0 : h->mfma_rows;  // the tile's sums differ in order from the GEMV
   a.xstage_i = xstage_rows(h->cfg.inter);
   return a;
 }
@@ -166,7 +171,7 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   int rows_gu = 0, rows_dn = 0;
   const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
   if (!lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, fused ? fused_select_keys(E) : 0, &gu, &rows_gu) ||
-      !pick_gemv(h->Gi, h->NBi, RC, false, 0, &dn, &rows_dn))
+      !pick_gemv(h->Gi, h->NBi, RC, false, h->cfg.exact, &dn, &rows_dn))
     return false;
   const int tc = logits_rows(T);
   const dim3 grid_lg((E + kRouteExpertsPerBlock - 1) / kRouteExpertsPerBlock, (T + tc - 1) / tc);
@@ -183,6 +188,7 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
     if (!fused) out->push_back({sel, dim3(1), kSelectThreads, 0, l, 1});
     out->push_back({gu, grid_gu, kThreads, shm_gu, l, 2});
     out->push_back({dn, grid_dn, kThreads, shm_dn, l, 3});
+    if (h->cfg.exact) out->push_back({combine_kernel, dim3(T, (H + 4 * kThreads - 1) / (4 * kThreads)), kThreads, 0, l, 4});
   }
   return true;
 }
@@ -311,8 +317,8 @@ static void free_handle(moe_round* h) {
   for (int i = 0; i < kStagingSlots; ++i)
     if (h->slot_ev[i]) (void)hipEventDestroy(h->slot_ev[i]);
   if (h->staging) (void)hipHostFree(h->staging);
-  void* ptrs[] = {h->d_ing, h->d_wtab, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique,
-                  h->uniq, h->offs, h->pairs, h->pair_w, h->rec, h->hbuf, h->xq, h->xss};
+  void* ptrs[] = {h->d_ing, h->d_wtab, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique, h->uniq, h->offs,
+                  h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->xq, h->xss};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete h;
@@ -363,6 +369,8 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   MOE_ALLOC(h->pair_w, sizeof(float) * L * h->Pcap);
   MOE_ALLOC(h->rec, sizeof(int32_t) * L * h->Icap * kRecWords);
   MOE_ALLOC(h->hbuf, sizeof(float) * h->Pcap * I);
+  MOE_ALLOC(h->slot_of, sizeof(int32_t) * L * h->Pcap);
+  if (cfg->exact) MOE_ALLOC(h->ybuf, sizeof(float) * h->Pcap * H);
   MOE_ALLOC(h->xq, sizeof(uint32_t) * T * (H / 32) * kXqWords);
   MOE_ALLOC(h->xss, sizeof(float2) * T * (H / 32));
 #undef MOE_ALLOC

@@ -42,8 +42,9 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
     const int n4 = T * H / 4;
     const float4* x4 = reinterpret_cast<const float4*>(x);
     float4* xn4 = reinterpret_cast<float4*>(xn);
-    for (int i = blockIdx.x * kThreads + tid; i < n4; i += gridDim.x * kThreads)
-      xn4[i] = a.residual ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!a.exact)  // exact mode: the combine kernel writes the output rows whole
+      for (int i = blockIdx.x * kThreads + tid; i < n4; i += gridDim.x * kThreads)
+        xn4[i] = a.residual ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     const int nq = T * (H / 32);  // 32-blocks of the layer input, two per wave
     for (int qb = 2 * (blockIdx.x * kWaves + wave); qb < nq; qb += 2 * gridDim.x * kWaves)
       quantize_block_pair(x, a.xq, a.xss, qb, nq);
@@ -274,10 +275,12 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
   }
   for (int i = tid; i < nu; i += NT) uniq[i] = s.uniq[i];
   for (int i = tid; i <= nu; i += NT) offs[i] = s.offs[i];
+  int32_t* slot_of = a.slot_of + static_cast<size_t>(layer) * a.Pcap;
   for (int i = tid; i < npairs; i += NT) {
     const int pr = s.pairs[i];
     pairs[i] = pr;
     pw[i] = s.p[(pr & 0xFF) * k + (pr >> 8)];
+    slot_of[(pr & 0xFF) * k + (pr >> 8)] = i;
     const size_t o = static_cast<size_t>(layer) * npairs + i;  // [L][T][k] with i = t*k + j
     if (in.ids) in.ids[o] = s.sel[i];
     if (in.route_w) in.route_w[o] = s.p[i];

@@ -33,6 +33,7 @@ moe_status validate_config(const moe_round_config* c) {
   if (c->fused_max_rows < -1 || c->fused_max_rows > 15) return MOE_ERR_INVALID_ARG;
   if (c->rows_per_item < 0 || c->rows_per_item > MOE_ROUND_MAX_ROWS) return MOE_ERR_INVALID_ARG;
   if (c->mfma_min_rows < -1 || c->mfma_min_rows > MOE_ROUND_MAX_ROWS) return MOE_ERR_INVALID_ARG;
+  if (c->exact != 0 && c->exact != 1) return MOE_ERR_INVALID_ARG;
   if (c->top_k_max > c->n_experts) return MOE_ERR_INVALID_ARG;
   if (c->max_rows > MOE_ROUND_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts > MOE_ROUND_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
