@@ -188,34 +188,33 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Wave-wide maximum as a wave-uniform value: DPP inside each 16-lane row, then the four row maxima
-// read into scalar registers.
-__device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
+// Wave-wide maximum left in every lane, on VALU only (no round trip through scalar registers):
+// DPP inside each 16-lane row, then the two permlane swaps, whose two outputs together hold both
+// partners of a level, so the maximum of the pair needs no lane select.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u32<kDppXor1>(v));
   v = max(v, dpp_u32<kDppXor2>(v));
   v = max(v, dpp_u32<kDppHalfMirror>(v));
   v = max(v, dpp_u32<kDppMirror>(v));
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return max(max(r0, r1), max(r2, r3));
+  uint32_t a = v, b = v;
+  permlane16_swap(a, b);  // a: rows [r0, r0, r2, r2], b: rows [r1, r1, r3, r3]
+  v = max(a, b);
+  a = v;
+  b = v;
+  permlane32_swap(a, b);  // a: [lo half, lo half], b: [hi half, hi half]
+  return max(a, b);
+}
+
+// Number of bits of the wave mask m set below this lane.
+__device__ __forceinline__ int mbcnt64(uint64_t m) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
 }
 
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), lane);
   const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), lane);
   return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = umax64(v, dpp_u64<kDppXor1>(v));
-  v = umax64(v, dpp_u64<kDppXor2>(v));
-  v = umax64(v, dpp_u64<kDppHalfMirror>(v));
-  v = umax64(v, dpp_u64<kDppMirror>(v));
-  v = umax64(v, swap_partner_u64<false>(v));
-  v = umax64(v, swap_partner_u64<true>(v));
-  return v;
 }
 
 // Full sums over 64 lanes of 8 values at once (a transposed butterfly): the xor-32 and xor-16

@@ -217,7 +217,7 @@ constexpr int kGuOneRow = 0, kGuPairs = 1, kGuStaged = 2;
 // MODE: kGuOneRow (T == 1), kGuPairs (verify rounds: rows two at a time from L2), kGuStaged (wide
 // rounds: rows staged in LDS, matrix-core tile for items with many rows).
 // SEL > 0 (verify rounds): the block first computes the round's selection itself from the logits
-// (select_block with SEL keys per lane), finds its work item in LDS, and block 0 publishes the
+// (select_block with SEL keys per lane), finds its work item in LDS, and the last block publishes the
 // records and outputs that the down kernel and the caller read; no separate selection launch.
 // SEL == 0: the work item comes from the records written by select_kernel.
 constexpr int kFusedPairs = 256;  // (row, rank) pairs of a round with the selection fused in
@@ -407,7 +407,8 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
   const int tiles = (a.I + ROWS_B - 1) / ROWS_B;
   if constexpr (SEL > 0) {
     __shared__ SelectSharedT<kFusedPairs, kWaves> ssel;
-    select_block<SEL, kThreads>(a, layer, ssel, blockIdx.x == 0);
+    // The last block publishes: it is the one most likely to have no (item, tile) unit of its own.
+    select_block<SEL, kThreads>(a, layer, ssel, blockIdx.x == gridDim.x - 1);
     const int units = ssel.ni * tiles;
     for (int w = blockIdx.x; w < units; w += gridDim.x) {
       const int u = w / tiles;

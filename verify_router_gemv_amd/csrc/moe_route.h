@@ -87,17 +87,17 @@ struct SelectSharedT {
   int ioffs[MOE_ROUND_MAX_EXPERTS];                    // unique index -> first work item
   int pairs[PMAX];                                     // by pair slot: t | j << 8
   int item_u[PMAX];                                    // work item -> unique index
-  int wsum[NW];
-  int wsum2[NW];
+  unsigned long long ctot[MOE_ROUND_MAX_EXPERTS / 64];  // per 64-expert chunk: chosen, rows, items
   int nu, ni;
 };
 using SelectShared = SelectSharedT<MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK, kSelectWaves>;
 
-// Top-k of one row on one wave. Each lane sorts its NPL (logit, id) keys once; then k rounds pick
-// the largest head: a 32-bit wave max over the heads' high words (sign, exponent and 20 mantissa
-// bits), then a ballot of the lanes holding it; only when several lanes tie there does a 64-bit
-// wave max over those lanes decide. The winner pops its head. Lane j records the j-th id and its
-// exact fp64 logit (read from the owner lane's registers) for the softmax over the k selected.
+// Top-k of one row on one wave. Each lane sorts its NPL (logit, id) keys once; then each of k
+// rounds takes the largest head over the wave without any round trip through scalar registers: a
+// wave max of the heads' high words (sign, exponent and 20 mantissa bits), then of the low words
+// of the heads holding that high word (the low bits carry the id, so the winner is unique). The
+// lane owning the winner pops its head and lane j keeps the j-th id. The exact fp64 logits of the
+// k ids come from their owner lanes once, after the rounds, for the softmax over the k selected.
 template <int NPL, typename SS>
 __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
   const int lane = threadIdx.x & 63;
@@ -121,33 +121,25 @@ __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
         key[i + 1] = tmp;
       }
   int myid = 0;
-  double myz = 0.0;
   for (int j = 0; j < k; ++j) {
     const uint32_t hi = static_cast<uint32_t>(key[0] >> 32);
-    const uint32_t mhi = wave_max_u32_uniform(hi);
-    const uint64_t cand = __ballot(hi == mhi);
-    uint64_t best;
-    if (__popcll(cand) == 1) {
-      best = readlane_u64(key[0], __ffsll(static_cast<unsigned long long>(cand)) - 1);
-    } else {
-      best = wave_max_u64(hi == mhi ? key[0] : 0ull);
-    }
-    const int e = key_expert(best);
-    const int owner = e & 63, slot = e >> 6;
-    if (lane == owner) {
+    const uint32_t mhi = wave_max_u32(hi);
+    const uint32_t mlo = wave_max_u32(hi == mhi ? static_cast<uint32_t>(key[0]) : 0u);
+    const int e = key_expert(mlo);
+    if (lane == (e & 63)) {
 #pragma unroll
       for (int i = 0; i + 1 < NPL; ++i) key[i] = key[i + 1];
       key[NPL - 1] = 0ull;
     }
-    double zs = z[0];
+    if (lane == j) myid = e;
+  }
+  // Lane j < k: the logit of its id, from register slot id / 64 of lane id % 64.
+  const int own = myid & 63, slot = myid >> 6;
+  double myz = 0.0;
 #pragma unroll
-    for (int i = 1; i < NPL; ++i)
-      if (slot == i) zs = z[i];
-    const double ze = __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, zs), owner));
-    if (lane == j) {
-      myid = e;
-      myz = ze;
-    }
+  for (int i = 0; i < NPL; ++i) {
+    const double zi = __shfl(z[i], own, 64);
+    if (slot == i) myz = zi;
   }
   const double z0 = __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, myz), 0));
   const double ej = lane < k ? exp(myz - z0) : 0.0;  // rank 0 holds the largest selected logit
@@ -166,7 +158,6 @@ __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
 template <int NPL, int NT, typename SS>
 __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bool publish) {
   constexpr int NW = NT / 64;
-  constexpr int EPT = (MOE_ROUND_MAX_EXPERTS + NT - 1) / NT;  // experts per thread in the scan
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k, npairs = T * k;
 
@@ -177,61 +168,67 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
   for (int idx = tid; idx < npairs; idx += NT) atomicOr(&s.mask[s.sel[idx]], 1ull << (idx / k));
   __syncthreads();
 
-  // Block-wide exclusive scan over experts (EPT consecutive experts per thread) of (rows choosing
-  // e, whether any row chose e) and of the work items of e: its rows split into groups of at most
-  // a.rg, so a GEMV block's share of an expert is bounded.
-  int cnt[EPT], pk[EPT], ngs[EPT];
-  int packed = 0, ng = 0;
+  // The union and its prefix sums, with ballots instead of a shuffle scan. Chunk ch of 64
+  // consecutive experts (ch = q * NW + wave) gives each expert lane its rank among the chunk's
+  // chosen experts, and the sums below it of the row counts and of the work-item counts (an
+  // expert's rows split into items of at most a.rg), bit plane by bit plane: mbcnt of the ballot of
+  // each bit. Chunk totals meet once in LDS for the exclusive prefix over chunks.
+  constexpr int NCH = MOE_ROUND_MAX_EXPERTS / 64;
+  constexpr int CPW = (NCH + NW - 1) / NW;  // chunks per wave
+  const int rg = a.rg;
+  const int cbits = 32 - __clz(T);                  // bits of a row count (at most T)
+  const int gbits = 32 - __clz((T + rg - 1) / rg);  // bits of an item count
+  int cnt[CPW], ngs[CPW], uin[CPW], cin[CPW], gin[CPW];
 #pragma unroll
-  for (int q = 0; q < EPT; ++q) {
-    const int e = tid * EPT + q;
-    const int c = e < E ? __popcll(s.mask[e]) : 0;
+  for (int q = 0; q < CPW; ++q) {
+    const int ch = q * NW + wave, e = ch * 64 + lane;
+    const int c = (ch < NCH && e < E) ? __popcll(s.mask[min(e, MOE_ROUND_MAX_EXPERTS - 1)]) : 0;
     cnt[q] = c;
-    pk[q] = c | ((c > 0) << 16);
-    ngs[q] = (c + a.rg - 1) / a.rg;
-    packed += pk[q];
-    ng += ngs[q];
-  }
-  int incl = packed, incl2 = ng;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    const int y2 = __shfl_up(incl2, off, 64);
-    if (lane >= off) {
-      incl += y;
-      incl2 += y2;
+    ngs[q] = (c + rg - 1) / rg;
+    const uint64_t chosen = __ballot(c > 0);
+    uin[q] = mbcnt64(chosen);
+    uint64_t tot = static_cast<uint64_t>(__popcll(chosen));
+    int ci = 0, gi = 0;
+    for (int b = 0; b < cbits; ++b) {
+      const uint64_t mb = __ballot((c >> b) & 1);
+      ci += mbcnt64(mb) << b;
+      tot += static_cast<uint64_t>(__popcll(mb)) << (16 + b);
     }
-  }
-  if (lane == 63) {
-    s.wsum[wave] = incl;
-    s.wsum2[wave] = incl2;
+    for (int b = 0; b < gbits; ++b) {
+      const uint64_t mb = __ballot((ngs[q] >> b) & 1);
+      gi += mbcnt64(mb) << b;
+      tot += static_cast<uint64_t>(__popcll(mb)) << (32 + b);
+    }
+    cin[q] = ci;
+    gin[q] = gi;
+    if (lane == 0 && ch < NCH) s.ctot[ch] = tot;  // chosen | rows << 16 | items << 32
   }
   __syncthreads();
-  int wpre = 0, wtot = 0, wpre2 = 0, wtot2 = 0;
+  uint64_t all = 0, pre[CPW];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    if (w < wave) {
-      wpre += s.wsum[w];
-      wpre2 += s.wsum2[w];
-    }
-    wtot += s.wsum[w];
-    wtot2 += s.wsum2[w];
+  for (int q = 0; q < CPW; ++q) pre[q] = 0;
+#pragma unroll
+  for (int c2 = 0; c2 < NCH; ++c2) {
+    const uint64_t v = s.ctot[c2];
+    all += v;
+#pragma unroll
+    for (int q = 0; q < CPW; ++q)
+      if (c2 < q * NW + wave) pre[q] += v;
   }
-  const int nu = min(wtot >> 16, a.Ucap), ni = min(wtot2, a.Icap);
-  int excl = incl - packed + wpre, io = incl2 - ng + wpre2;
+  const int nu = min(static_cast<int>(all & 0xFFFF), a.Ucap);
+  const int ni = min(static_cast<int>((all >> 32) & 0xFFFF), a.Icap);
 #pragma unroll
-  for (int q = 0; q < EPT; ++q) {
-    const int e = tid * EPT + q;
+  for (int q = 0; q < CPW; ++q) {
+    const int e = (q * NW + wave) * 64 + lane;
     if (cnt[q] > 0) {
-      const int u = excl >> 16;
+      const int u = static_cast<int>(pre[q] & 0xFFFF) + uin[q];
+      const int io = static_cast<int>((pre[q] >> 32) & 0xFFFF) + gin[q];
       s.uidx[e] = u;
       s.uniq[u] = e;
-      s.offs[u] = excl & 0xFFFF;
+      s.offs[u] = static_cast<int>((pre[q] >> 16) & 0xFFFF) + cin[q];
       s.ioffs[u] = io;
-      for (int gi = 0; gi < ngs[q]; ++gi) s.item_u[io + gi] = u;
+      for (int g2 = 0; g2 < ngs[q]; ++g2) s.item_u[io + g2] = u;
     }
-    excl += pk[q];
-    io += ngs[q];
   }
   if (tid == 0) {
     s.nu = nu;
