@@ -252,23 +252,25 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
   int32_t* offs = a.offs + static_cast<size_t>(layer) * (a.Ucap + 1);
   int32_t* pairs = a.pairs + static_cast<size_t>(layer) * a.Pcap;
   float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
-  for (int i = tid; i < ni * kRecWords; i += NT) {
-    const int it = i / kRecWords, wd = i - it * kRecWords;
+  // One thread per item writes its record: the four header words and the row words an item of at
+  // most a.rg rows can use (readers never look at rows past np, so the rest are not written).
+  const int nrw = (a.rg + 3) / 4;
+  for (int it = tid; it < ni; it += NT) {
     const int uu = s.item_u[it];
     const int p0 = s.offs[uu] + (it - s.ioffs[uu]) * a.rg;
     const int np = min(a.rg, s.offs[uu + 1] - p0);
-    int v = 0;
-    if (wd == 0) v = s.uniq[uu];
-    else if (wd == 1) v = p0;
-    else if (wd == 2) v = np;
-    else if (wd == 3) v = ni;
-    else if (wd >= kRecRowWord && wd < kRecRowWord + MOE_ROUND_MAX_ROWS / 4) {
-      const int r0 = (wd - kRecRowWord) * 4;
+    int32_t* r = rec + static_cast<size_t>(it) * kRecWords;
+    r[0] = s.uniq[uu];
+    r[1] = p0;
+    r[2] = np;
+    r[3] = ni;
+    for (int wd = 0; wd < nrw; ++wd) {
+      int v = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        if (r0 + b < np) v |= (s.pairs[p0 + r0 + b] & 0xFF) << (8 * b);
+        if (4 * wd + b < np) v |= (s.pairs[p0 + 4 * wd + b] & 0xFF) << (8 * b);
+      r[kRecRowWord + wd] = v;
     }
-    rec[i] = v;
   }
   for (int i = tid; i < nu; i += NT) uniq[i] = s.uniq[i];
   for (int i = tid; i <= nu; i += NT) offs[i] = s.offs[i];
