@@ -10,6 +10,9 @@ from .moe_oracle import (  # noqa: F401
     unpack_codes,
     unpack_scale_min,
     dequantize,
+    unpack_superblocks,
+    dequantize_q4s256,
+    dequantize_any,
     router_logits,
     select_topk,
     selection_gap,

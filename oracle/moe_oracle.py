@@ -10,7 +10,9 @@ Written from the pages, row by row, with no blocking, fusion or reordering:
   * infero README, "Design notes": block-encoded weights are read in place;
     activations are fp32 so intermediates compare against a CPU reference.
   * infero README, "AWQ, FP8, and NVFP4 checkpoints": a 4-bit block format
-    keeps a scale and a minimum every 32 weights.
+    keeps a scale and a minimum every 32 weights; its K-quant unpacks a 6-bit
+    scale and a 6-bit minimum from a packed twelve-byte field every 32
+    weights, in 256-element super-blocks ("Supported weight encodings").
   * AlphaInfer page, section 2 ("One captured graph per decode round"): a
     round is one forward pass over 1-8 token rows; section 3.1: each extra
     verified row routes to experts the others did not need, so the set of
@@ -18,6 +20,10 @@ Written from the pages, row by row, with no blocking, fusion or reordering:
 
 Readings where the pages are silent (each also listed in the design notes):
   * dequantisation is w = s*q + m (fp16 scale s, fp16 minimum m, q in 0..15);
+  * in the 4.5-bit layout (Q4S256) a 256-weight super-block carries fp16 d and
+    dmin and, per 32-weight sub-block j, a 6-bit scale sc_j and a 6-bit
+    minimum m_j (12-bit field j at bit 12j of a 96-bit string); a weight is
+    d*sc_j*q - dmin*m_j;
   * byte j of a 32-block holds element 2j (low nibble) and 2j+1 (high nibble);
   * selection is the k largest logits in descending order, ties to the lower
     expert id;
@@ -36,6 +42,7 @@ from __future__ import annotations
 import numpy as np
 
 BLOCK = 32
+SUPER = 256
 
 
 # ---------------------------------------------------------------------------
@@ -66,6 +73,51 @@ def dequantize(codes: np.ndarray, sm: np.ndarray) -> np.ndarray:
     K = q.shape[-1]
     qb = q.reshape(q.shape[:-1] + (K // BLOCK, BLOCK))
     return (s[..., None] * qb + m[..., None]).reshape(q.shape)
+
+
+def unpack_superblocks(rec: np.ndarray):
+    """uint32 [..., K/256, 4] -> (d, dmin) f64 [..., K/256] and (sc, mn) f64 [..., K/256, 8].
+
+    Word 0 holds fp16 d (low half) and fp16 dmin (high half); words 1..3 are a little-endian 96-bit
+    string whose bits 12j..12j+11 are sub-block j's field: scale in bits 0-5, minimum in bits 6-11.
+    """
+    rec = np.asarray(rec).view(np.uint32)
+    d = (rec[..., 0] & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+    dmin = (rec[..., 0] >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+    # the 96-bit string as three 32-bit pieces; field j starts at bit 12j
+    words = [rec[..., 1].astype(np.uint64), rec[..., 2].astype(np.uint64), rec[..., 3].astype(np.uint64)]
+    sc = np.empty(rec.shape[:-1] + (8,), dtype=np.float64)
+    mn = np.empty(rec.shape[:-1] + (8,), dtype=np.float64)
+    for j in range(8):
+        start = 12 * j
+        field = np.zeros(rec.shape[:-1], dtype=np.uint64)
+        for bit in range(12):                      # gather the field bit by bit
+            pos = start + bit
+            b = (words[pos // 32] >> np.uint64(pos % 32)) & np.uint64(1)
+            field |= b << np.uint64(bit)
+        sc[..., j] = (field & np.uint64(63)).astype(np.float64)
+        mn[..., j] = (field >> np.uint64(6)).astype(np.float64)
+    return d, dmin, sc, mn
+
+
+def dequantize_q4s256(codes: np.ndarray, rec: np.ndarray) -> np.ndarray:
+    """W[r, c] = d*sc_j*q[r, c] - dmin*m_j with super-block c//256 and sub-block j = (c % 256)//32;
+    exact in fp64 (an 11-bit x 6-bit x 4-bit product and an 11-bit x 6-bit one)."""
+    q = unpack_codes(codes)
+    d, dmin, sc, mn = unpack_superblocks(rec)
+    K = q.shape[-1]
+    qb = q.reshape(q.shape[:-1] + (K // SUPER, SUPER // BLOCK, BLOCK))
+    w = d[..., None, None] * sc[..., None] * qb - dmin[..., None, None] * mn[..., None]
+    return w.reshape(q.shape)
+
+
+def dequantize_any(codes: np.ndarray, sm: np.ndarray, fmt: str = "q4b32") -> np.ndarray:
+    """The matrix of either weight layout ("q4b32" or "q4s256")."""
+    if fmt == "q4s256":
+        return dequantize_q4s256(codes, sm)
+    if fmt != "q4b32":
+        raise ValueError(f"unknown weight format {fmt!r}")
+    return dequantize(codes, sm)
 
 
 # ---------------------------------------------------------------------------
@@ -112,9 +164,10 @@ def silu(a: np.ndarray) -> np.ndarray:
     return a / (1.0 + np.exp(-a))
 
 
-def expert_matrices(gate_q, gate_sm, up_q, up_sm, down_q, down_sm):
+def expert_matrices(gate_q, gate_sm, up_q, up_sm, down_q, down_sm, fmt: str = "q4b32"):
     """Dequantise one expert: (W_g [I,H], W_u [I,H], W_d [H,I]) in fp64."""
-    return dequantize(gate_q, gate_sm), dequantize(up_q, up_sm), dequantize(down_q, down_sm)
+    return (dequantize_any(gate_q, gate_sm, fmt), dequantize_any(up_q, up_sm, fmt),
+            dequantize_any(down_q, down_sm, fmt))
 
 
 def swiglu_ffn(Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, x: np.ndarray) -> np.ndarray:
@@ -126,9 +179,9 @@ def swiglu_ffn(Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, x: np.ndarray) ->
     return Wd @ h
 
 
-def expert_forward(gate_q, gate_sm, up_q, up_sm, down_q, down_sm, x: np.ndarray) -> np.ndarray:
+def expert_forward(gate_q, gate_sm, up_q, up_sm, down_q, down_sm, x: np.ndarray, fmt: str = "q4b32") -> np.ndarray:
     """One expert on one row, from its packed weights."""
-    return swiglu_ffn(*expert_matrices(gate_q, gate_sm, up_q, up_sm, down_q, down_sm), x)
+    return swiglu_ffn(*expert_matrices(gate_q, gate_sm, up_q, up_sm, down_q, down_sm, fmt), x)
 
 
 def _expert_arrays(layer: dict, e: int):
@@ -144,8 +197,10 @@ def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False):
     """One MoE layer over rows X [T, H]; each row is evaluated on its own.
 
     `layer` maps the weight names (router_w, router_b, gate_q, gate_sm, up_q, up_sm, down_q, down_sm)
-    to arrays indexable by expert.  Returns (out [T,H] f64, ids [T,k] int64, p [T,k] f64, gaps [T]).
+    to arrays indexable by expert, and optionally "format" to the weight layout ("q4b32" when
+    absent).  Returns (out [T,H] f64, ids [T,k] int64, p [T,k] f64, gaps [T]).
     """
+    fmt = layer.get("format") or "q4b32"
     X = np.asarray(X, dtype=np.float64)
     T, H = X.shape
     out = np.zeros((T, H), dtype=np.float64)
@@ -162,7 +217,7 @@ def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False):
         for j in range(k):
             e = int(sel[j])
             if e not in cache:
-                cache[e] = expert_matrices(*_expert_arrays(layer, e))
+                cache[e] = expert_matrices(*_expert_arrays(layer, e), fmt=fmt)
             acc = acc + w[j] * swiglu_ffn(*cache[e], X[t])
         out[t] = X[t] + acc if residual else acc
         ids[t] = sel

@@ -1,8 +1,9 @@
 """Seeded synthetic inputs for the MoE decode/verify round.
 
 This package only draws random numbers and lays them out in the library's
-weight format (4-bit codes in blocks of 32 with an fp16 scale and an fp16
-minimum per block).  It holds none of the round's arithmetic: no
+weight formats (4-bit codes in blocks of 32 with an fp16 scale and an fp16
+minimum per block, or in 256-weight super-blocks with 6-bit sub-block scales
+and minima).  It holds none of the round's arithmetic: no
 dequantisation, no router, no top-k, no SwiGLU, no combine.  Both the CPU
 oracle and the HIP path consume what it produces.
 """
@@ -12,6 +13,7 @@ from .inputs import (  # noqa: F401
     LayerInputs,
     config,
     quantize_q4b32,
+    quantize_q4s256,
     make_layer,
     make_activations,
     derive_seed,

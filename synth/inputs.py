@@ -14,6 +14,19 @@ A block with a scale and a minimum per 32 weights follows the K-quant
 family described in the infero README ("AWQ, FP8, and NVFP4 checkpoints":
 a 6-bit scale and a 6-bit minimum every 32 weights); here both are fp16.
 
+Weight layout ("Q4S256", 4.5 bits per weight): the same codes, and per
+256-weight super-block (eight 32-weight sub-blocks, K a multiple of 256) one
+16-byte record, int32 [rows][K/256][4]:
+  * word 0: fp16 super-scale d in the low half, fp16 super-minimum dmin in
+    the high half;
+  * words 1..3: a 96-bit little-endian string of eight 12-bit fields, field
+    j at bits 12j..12j+11 holding the sub-block's 6-bit scale sc_j (bits
+    0-5) and 6-bit minimum m_j (bits 6-11).
+A weight of sub-block j is d*sc_j*q - dmin*m_j.  That is 128 B of codes and
+16 B of scales per 256 weights, the super-block size and the packed
+twelve-byte scale/minimum field the infero README describes for its 4-bit
+K-quant ("Supported weight encodings"; "AWQ, FP8, and NVFP4 checkpoints").
+
 Expert matrices are stored output-major: gate and up as [E][I][H] (reduce
 over H), down as [E][H][I] (reduce over I).  The router is fp32 [E][H] with
 an optional fp32 bias [E].
@@ -40,6 +53,8 @@ import numpy as np
 import torch
 
 BLOCK = 32
+SUPER = 256
+FORMATS = ("q4b32", "q4s256")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -54,9 +69,12 @@ class ShapeConfig:
     zipf_s: Optional[float] = None
     rows: str = "indep"          # "indep" | "correlated"
     residual: bool = False
+    fmt: str = "q4b32"           # weight layout: "q4b32" | "q4s256"
 
     def expert_bytes(self) -> int:
-        """Bytes of one expert's gate+up+down in the 4-bit block layout."""
+        """Bytes of one expert's gate+up+down in the configured weight layout."""
+        if self.fmt == "q4s256":
+            return 3 * self.H * self.I * (SUPER // 2 + 16) // SUPER   # 128 B codes + 16 B per 256
         per_weight_num = BLOCK // 2 + 4     # 16 B codes + 4 B scale/min per 32
         return 3 * self.H * self.I * per_weight_num // BLOCK
 
@@ -117,6 +135,54 @@ def quantize_q4b32(w: torch.Tensor):
     return codes.contiguous(), sm.contiguous()
 
 
+def _wrap_int32(v: torch.Tensor) -> torch.Tensor:
+    """int64 values in [0, 2^32) -> the int32 tensor with the same 32 bits."""
+    v = v & 0xFFFFFFFF
+    return torch.where(v >= (1 << 31), v - (1 << 32), v).to(torch.int32)
+
+
+def quantize_q4s256(w: torch.Tensor):
+    """Encode float weights [..., K] (K a multiple of 256) into (codes uint8 [..., K/2],
+    records int32 [..., K/256, 4]) in the Q4S256 layout described above.
+
+    Per super-block, for its sub-blocks j: range r_j = (max_j - min_j) / 15 and offset
+    o_j = max(-min_j, 0); d = fp16(max_j r_j / 63), dmin = fp16(max_j o_j / 63);
+    sc_j = clip(rint(r_j / d), 0, 63) and m_j = clip(rint(o_j / dmin), 0, 63) (0 where d or dmin is
+    0); q = clip(rint((w + dmin*m_j) / (d*sc_j)), 0, 15) (0 where d*sc_j is 0).  Input data only.
+    """
+    K = w.shape[-1]
+    assert K % SUPER == 0
+    lead = w.shape[:-1]
+    nsb = K // SUPER
+    b = w.float().reshape(*lead, nsb, SUPER // BLOCK, BLOCK)
+    mn = b.amin(dim=-1)
+    mx = b.amax(dim=-1)
+    rng = (mx - mn) / 15.0
+    off = (-mn).clamp(min=0.0)
+    d16 = (rng.amax(dim=-1) / 63.0).to(torch.float16)
+    dmin16 = (off.amax(dim=-1) / 63.0).to(torch.float16)
+    d = d16.float().unsqueeze(-1)
+    dmin = dmin16.float().unsqueeze(-1)
+    sc = torch.where(d > 0, torch.round(rng / torch.where(d > 0, d, torch.ones_like(d))), torch.zeros_like(rng))
+    sc = sc.clamp_(0, 63)
+    m6 = torch.where(dmin > 0, torch.round(off / torch.where(dmin > 0, dmin, torch.ones_like(dmin))),
+                     torch.zeros_like(off))
+    m6 = m6.clamp_(0, 63)
+    a = (d * sc).unsqueeze(-1)      # exact: an fp16 times an integer below 64
+    o = (dmin * m6).unsqueeze(-1)
+    safe = torch.where(a > 0, a, torch.ones_like(a))
+    q = torch.where(a > 0, torch.round((b + o) / safe), torch.zeros_like(b))
+    q = q.clamp_(0, 15).to(torch.uint8).reshape(*lead, K // 2, 2)
+    codes = q[..., 0] | (q[..., 1] << 4)
+    f = sc.to(torch.int64) | (m6.to(torch.int64) << 6)           # [..., nsb, 8] 12-bit fields
+    w1 = f[..., 0] | (f[..., 1] << 12) | ((f[..., 2] & 0xFF) << 24)
+    w2 = (f[..., 2] >> 8) | (f[..., 3] << 4) | (f[..., 4] << 16) | ((f[..., 5] & 0xF) << 28)
+    w3 = (f[..., 5] >> 4) | (f[..., 6] << 8) | (f[..., 7] << 20)
+    w0 = (d16.view(torch.int16).to(torch.int64) & 0xFFFF) | ((dmin16.view(torch.int16).to(torch.int64) & 0xFFFF) << 16)
+    rec = torch.stack([_wrap_int32(w0), _wrap_int32(w1), _wrap_int32(w2), _wrap_int32(w3)], dim=-1)
+    return codes.contiguous(), rec.contiguous()
+
+
 @dataclasses.dataclass
 class LayerInputs:
     """One MoE layer's weights in the library layout (torch tensors, any device)."""
@@ -127,13 +193,14 @@ class LayerInputs:
     up_q: torch.Tensor
     up_sm: torch.Tensor
     down_q: torch.Tensor              # u8  [E, H, I/2]
-    down_sm: torch.Tensor             # i32 [E, H, I/32]
+    down_sm: torch.Tensor             # i32 [E, H, I/32]  (q4s256: [E, H, I/256, 4])
+    fmt: str = "q4b32"                # "q4b32": *_sm per 32-block; "q4s256": super-block records
 
     FIELDS = ("router_w", "router_b", "gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")
 
     def map(self, fn) -> "LayerInputs":
         return LayerInputs(**{f: (None if getattr(self, f) is None else fn(getattr(self, f)))
-                              for f in self.FIELDS})
+                              for f in self.FIELDS}, fmt=self.fmt)
 
     def to(self, device) -> "LayerInputs":
         return self.map(lambda t: t.to(device))
@@ -153,6 +220,7 @@ class LayerInputs:
             if f.endswith("_sm"):
                 a = a.view(np.uint32)
             out[f] = a
+        out["format"] = self.fmt
         return out
 
     def expert_numpy(self, e: int) -> dict:
@@ -172,14 +240,19 @@ def _expert_matrix(cfg: ShapeConfig, seed: int, layer: int, stream: int, rows: i
                    device) -> tuple:
     E = cfg.E
     codes = torch.empty((E, rows, K // 2), dtype=torch.uint8, device=device)
-    sm = torch.empty((E, rows, K // BLOCK), dtype=torch.int32, device=device)
+    if cfg.fmt == "q4s256":
+        sm = torch.empty((E, rows, K // SUPER, 4), dtype=torch.int32, device=device)
+        quantize = quantize_q4s256
+    else:
+        sm = torch.empty((E, rows, K // BLOCK), dtype=torch.int32, device=device)
+        quantize = quantize_q4b32
     for e0 in range(0, E, _EXPERT_CHUNK):
         e1 = min(E, e0 + _EXPERT_CHUNK)
         w = torch.empty((e1 - e0, rows, K), dtype=torch.float32, device=device)
         for e in range(e0, e1):
             g = _gen(device, seed, 0, layer, stream, e)
             w[e - e0].normal_(0.0, 0.02, generator=g)
-        c, s = quantize_q4b32(w)
+        c, s = quantize(w)
         codes[e0:e1] = c
         sm[e0:e1] = s
         del w
@@ -201,7 +274,7 @@ def make_layer(cfg: ShapeConfig, seed: int = 0, layer: int = 0, device="cpu") ->
     gate_q, gate_sm = _expert_matrix(cfg, seed, layer, _STREAM_GATE, I, H, device)
     up_q, up_sm = _expert_matrix(cfg, seed, layer, _STREAM_UP, I, H, device)
     down_q, down_sm = _expert_matrix(cfg, seed, layer, _STREAM_DOWN, H, I, device)
-    return LayerInputs(router_w, router_b, gate_q, gate_sm, up_q, up_sm, down_q, down_sm)
+    return LayerInputs(router_w, router_b, gate_q, gate_sm, up_q, up_sm, down_q, down_sm, fmt=cfg.fmt)
 
 
 def make_activations(cfg: ShapeConfig, T: int, seed: int = 0, round_idx: int = 0,
@@ -235,3 +308,4 @@ def human(cfg: ShapeConfig) -> str:
 
 assert math.isclose(CONFIGS["verify"].expert_bytes(), 1_966_080)
 assert math.isclose(CONFIGS["decode"].expert_bytes(), 2_949_120)
+assert CONFIGS["verify"].replace(fmt="q4s256").expert_bytes() == 1_769_472

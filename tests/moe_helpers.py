@@ -40,6 +40,7 @@ def oracle_view(layer: synth.LayerInputs) -> dict:
         "gate_q": LazyExperts(layer.gate_q, False), "gate_sm": LazyExperts(layer.gate_sm, True),
         "up_q": LazyExperts(layer.up_q, False), "up_sm": LazyExperts(layer.up_sm, True),
         "down_q": LazyExperts(layer.down_q, False), "down_sm": LazyExperts(layer.down_sm, True),
+        "format": layer.fmt,
     }
 
 

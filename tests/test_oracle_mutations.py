@@ -36,6 +36,32 @@ def _swap_scale_min(sm):
     return m, s
 
 
+def _q4s_min_added(codes, rec):
+    q = om.unpack_codes(codes)
+    d, dmin, sc, mn = om.unpack_superblocks(rec)
+    qb = q.reshape(q.shape[:-1] + (q.shape[-1] // 256, 8, 32))
+    return (d[..., None, None] * sc[..., None] * qb + dmin[..., None, None] * mn[..., None]).reshape(q.shape)
+
+
+def _q4s_subblock_shifted(codes, rec):
+    q = om.unpack_codes(codes)
+    d, dmin, sc, mn = om.unpack_superblocks(rec)
+    sc, mn = np.roll(sc, 1, axis=-1), np.roll(mn, 1, axis=-1)
+    qb = q.reshape(q.shape[:-1] + (q.shape[-1] // 256, 8, 32))
+    return (d[..., None, None] * sc[..., None] * qb - dmin[..., None, None] * mn[..., None]).reshape(q.shape)
+
+
+def _q4s_fields_swapped(rec):
+    d, dmin, sc, mn = ORIG["unpack_superblocks"](rec)
+    return d, dmin, mn, sc
+
+
+def _q4s_first_superblock_only(codes, rec):
+    rec = np.asarray(rec).view(np.uint32)
+    rec0 = np.broadcast_to(rec[..., :1, :], rec.shape).copy()
+    return ORIG["dequantize_q4s256"](codes, rec0)
+
+
 def _router_no_bias(router_w, router_b, x):
     return np.asarray(router_w, dtype=np.float64) @ np.asarray(x, dtype=np.float64)
 
@@ -114,7 +140,8 @@ def _round_no_residual(layers, X, k, residual):
 
 
 ORIG = {name: getattr(om, name) for name in
-        ("unpack_codes", "unpack_scale_min", "dequantize", "router_logits", "select_topk",
+        ("unpack_codes", "unpack_scale_min", "dequantize", "unpack_superblocks", "dequantize_q4s256",
+         "router_logits", "select_topk",
          "routing_weights", "silu", "swiglu_ffn", "expert_forward", "moe_layer", "moe_round",
          "build_worklist")}
 
@@ -123,6 +150,10 @@ MUTATIONS = {
     "dropped minimum": ("dequantize", _dequant_no_min),
     "wrong block index": ("dequantize", _dequant_wrong_block),
     "scale/min swapped": ("unpack_scale_min", _swap_scale_min),
+    "super-block minimum added": ("dequantize_q4s256", _q4s_min_added),
+    "sub-block index shifted": ("dequantize_q4s256", _q4s_subblock_shifted),
+    "super-block scale/min fields swapped": ("unpack_superblocks", _q4s_fields_swapped),
+    "first super-block only": ("dequantize_q4s256", _q4s_first_superblock_only),
     "router bias dropped": ("router_logits", _router_no_bias),
     "router accumulates in fp32": ("router_logits", _router_fp32),
     "ties to higher id": ("select_topk", _topk_ties_high),

@@ -98,6 +98,95 @@ def test_quantise_then_dequantise_is_within_half_a_step():
 
 
 # ---------------------------------------------------------------------------
+# 4.5-bit super-block layout (Q4S256)
+# ---------------------------------------------------------------------------
+
+def golden_superblock_row():
+    recs, w = [], {}
+    for key, toks in read_golden("q4s256_superblocks.txt"):
+        if key == "record":
+            recs.append([int(t, 16) for t in toks])
+        elif key == "w":
+            w[int(toks[0])] = float(toks[1])
+    codes = np.tile(np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], dtype=np.uint8), 32)
+    return codes[None, :], np.array(recs, dtype=np.uint32)[None, :, :], w
+
+
+def test_golden_superblocks_dequantise_exactly():
+    codes, rec, expect = golden_superblock_row()
+    W = oracle.dequantize_q4s256(codes, rec)
+    assert W.shape == (1, 512)
+    for c, v in expect.items():
+        assert W[0, c] == v, (c, W[0, c], v)
+
+
+def _pow2_superblock_layer(seed, E=5, H=512, I=256):
+    """A random Q4S256 layer whose d and dmin are powers of two, so every sub-block's d*sc and
+    dmin*m are exact fp16 values; returns it with the equivalent Q4B32 layer (same codes, per-32
+    fp16 scale d*sc and minimum -dmin*m, built here from the definition)."""
+    rng = np.random.default_rng(seed)
+    cfg = synth.ShapeConfig("t", H=H, E=E, k=2, I=I)
+    base = synth.make_layer(cfg, seed=seed, layer=0, device="cpu").numpy()
+    q4s = dict(base)
+    q4b = dict(base)
+    q4s["format"] = "q4s256"
+    for name, K in (("gate", H), ("up", H), ("down", I)):
+        rows = base[name + "_q"].shape[1]
+        nsb = K // 256
+        e_d = rng.integers(-14, -8, size=(E, rows, nsb))
+        e_m = rng.integers(-15, -9, size=(E, rows, nsb))
+        sc = rng.integers(0, 64, size=(E, rows, nsb, 8))
+        mn = rng.integers(0, 64, size=(E, rows, nsb, 8))
+        d = np.ldexp(1.0, e_d)
+        dmin = np.ldexp(1.0, e_m)
+        rec = np.zeros((E, rows, nsb, 4), dtype=np.uint32)
+        rec[..., 0] = np.array(d, dtype=np.float16).view(np.uint16).astype(np.uint32) | (
+            np.array(dmin, dtype=np.float16).view(np.uint16).astype(np.uint32) << 16)
+        bits = [0] * 96
+        for idx in np.ndindex(E, rows, nsb):
+            string = 0
+            for j in range(8):
+                string |= (int(sc[idx + (j,)]) | (int(mn[idx + (j,)]) << 6)) << (12 * j)
+            for wd in range(3):
+                rec[idx + (wd + 1,)] = (string >> (32 * wd)) & 0xFFFFFFFF
+        q4s[name + "_sm"] = rec
+        s_blk = (d[..., None] * sc).reshape(E, rows, nsb * 8)
+        m_blk = (-dmin[..., None] * mn).reshape(E, rows, nsb * 8)
+        s16 = np.array(s_blk, dtype=np.float16)
+        m16 = np.array(m_blk, dtype=np.float16)
+        assert np.array_equal(s16.astype(np.float64), s_blk) and np.array_equal(m16.astype(np.float64), m_blk)
+        q4b[name + "_sm"] = s16.view(np.uint16).astype(np.uint32) | (m16.view(np.uint16).astype(np.uint32) << 16)
+    return q4s, q4b
+
+
+def test_superblock_layer_equals_equivalent_block_layer():
+    """The same weights in both layouts give bitwise the same round (the Q4B32 side is pinned by
+    the golden blocks above); random scales and minima per sub-block pin the field order, the
+    sub-block and super-block indexing and the sign of the minimum."""
+    q4s, q4b = _pow2_superblock_layer(seed=5)
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((3, q4s["router_w"].shape[1]))
+    a = oracle.moe_layer(q4s, X, 2)
+    b = oracle.moe_layer(q4b, X, 2)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    for name in ("gate", "up", "down"):
+        assert np.array_equal(oracle.dequantize_any(q4s[name + "_q"], q4s[name + "_sm"], "q4s256"),
+                              oracle.dequantize(q4b[name + "_q"], q4b[name + "_sm"]))
+
+
+def test_superblock_quantise_then_dequantise_is_within_a_step():
+    g = torch.Generator().manual_seed(7)
+    w = torch.randn((6, 512), generator=g) * 0.02
+    codes, rec = synth.quantize_q4s256(w)
+    W = oracle.dequantize_q4s256(codes.numpy(), rec.numpy())
+    b = w.double().numpy().reshape(6, 2, 8, 32)
+    step = (b.max(-1) - b.min(-1)) / 15.0           # the sub-block's own quantisation step
+    err = np.abs(W.reshape(6, 2, 8, 32) - b).max(-1)
+    assert np.all(err <= 1.5 * step + 1e-4), err.max()
+
+
+# ---------------------------------------------------------------------------
 # router and selection
 # ---------------------------------------------------------------------------
 
@@ -250,7 +339,7 @@ def test_permuting_experts_permutes_ids_only():
     X = np.random.default_rng(5).standard_normal((3, 64)).astype(np.float32)
     out, ids, p, _ = oracle.moe_layer(L, X, k=3)
     perm = np.random.default_rng(0).permutation(E)          # new expert i is old expert perm[i]
-    LP = {key: (None if v is None else v[perm]) for key, v in L.items()}
+    LP = {key: (v if v is None or isinstance(v, str) else v[perm]) for key, v in L.items()}
     outP, idsP, pP, _ = oracle.moe_layer(LP, X, k=3)
     np.testing.assert_array_equal(perm[idsP], ids)
     np.testing.assert_array_equal(pP, p)
