@@ -30,6 +30,20 @@
  *                                element 2j+1 in bits 4-7; 16-byte aligned
  *   scalemin uint32 [rows][K/32] bits 0-15: fp16 scale s, bits 16-31: fp16
  *                                minimum m; weight = s*q + m, q in 0..15
+ *                                (MOE_WEIGHT_Q4B32, the default)
+ *   or, with weight_format MOE_WEIGHT_Q4S256 (K % 256 == 0), the same codes and
+ *   superblk uint32 [rows][K/256][4], one 16-byte record per 256 weights:
+ *                                word 0 bits 0-15 fp16 d, bits 16-31 fp16
+ *                                dmin; words 1-3 a little-endian 96-bit
+ *                                string, bits 12j..12j+11 = sub-block j's
+ *                                6-bit scale sc_j (low) and 6-bit minimum m_j
+ *                                (high); a weight of the 32-weight sub-block
+ *                                j is d*sc_j*q - dmin*m_j (4.5 bits per
+ *                                weight: the 256-element super-block with a
+ *                                packed twelve-byte scale/minimum field of
+ *                                the infero README, "Supported weight
+ *                                encodings" and "AWQ, FP8, and NVFP4
+ *                                checkpoints")
  *   gate, up: [E][I][H] (K = H); down: [E][H][I] (K = I).
  *   router: fp32 [E][H], optional fp32 bias [E].
  *
@@ -102,18 +116,28 @@ typedef struct moe_round_config {
                              rank order: results are bitwise reproducible, and a row's output
                              does not depend on the other rows of the round or on T. (The
                              matrix-core tile is not used.) 0: fp32 atomics (faster).       */
+  int32_t weight_format;  /* layout of the expert weights' scales and minima (the codes are the
+                             same in both; see moe_layer_weights):
+                             MOE_WEIGHT_Q4B32 (0): one word per 32-weight block, 0.625 B/weight;
+                             MOE_WEIGHT_Q4S256 (1): one 16-byte record per 256-weight
+                             super-block, 0.5625 B/weight; needs I a multiple of 256 (H always
+                             is), else init returns MOE_ERR_UNSUPPORTED. The matrix-core tile
+                             is used with MOE_WEIGHT_Q4B32 only.                            */
 } moe_round_config;
+
+#define MOE_WEIGHT_Q4B32 0
+#define MOE_WEIGHT_Q4S256 1
 
 /* One layer's weights (device pointers, caller-owned). router_bias may be NULL. */
 typedef struct moe_layer_weights {
   const float* router_w;     /* [E][H]                 */
   const float* router_bias;  /* [E] or NULL            */
   const uint8_t* gate_q;     /* [E][I][H/2]            */
-  const uint32_t* gate_sm;   /* [E][I][H/32]           */
+  const uint32_t* gate_sm;   /* [E][I][H/32]  (Q4S256: [E][I][H/256][4]) */
   const uint8_t* up_q;       /* [E][I][H/2]            */
-  const uint32_t* up_sm;     /* [E][I][H/32]           */
+  const uint32_t* up_sm;     /* [E][I][H/32]  (Q4S256: [E][I][H/256][4]) */
   const uint8_t* down_q;     /* [E][H][I/2]            */
-  const uint32_t* down_sm;   /* [E][H][I/32]           */
+  const uint32_t* down_sm;   /* [E][H][I/32]  (Q4S256: [E][H][I/256][4]) */
 } moe_layer_weights;
 
 typedef struct moe_round moe_round; /* opaque handle */

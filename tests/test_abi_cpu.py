@@ -64,6 +64,9 @@ def cfg(**kw):
          raw_mfma_min_rows=-1),
     dict(H=2048, I=512, E=256, top_k_max=8, max_rows=64, raw_fused_max_rows=15, raw_rows_per_item=64,
          raw_mfma_min_rows=16),
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=8, raw_weight_format=1),
+    dict(H=2048, I=768, E=128, top_k_max=8, max_rows=1, raw_weight_format=1),
+    dict(H=768, I=256, E=40, top_k_max=5, max_rows=16, raw_weight_format=1),
 ])
 def test_supported_configs_validate(lib, kw):
     from verify_router_gemv_amd import binding
@@ -87,6 +90,10 @@ def test_supported_configs_validate(lib, kw):
     (dict(raw_rows_per_item=65), -1),
     (dict(raw_mfma_min_rows=-3), -1),
     (dict(raw_exact=2), -1),
+    (dict(raw_weight_format=2), -1),
+    (dict(raw_weight_format=-1), -1),
+    (dict(I=384, raw_weight_format=1), -2),   # super-blocks need I a multiple of 256
+    (dict(H=256, I=128, E=8, top_k_max=2, raw_weight_format=1), -2),
     (dict(max_rows=65), -2),
     (dict(E=513, top_k_max=8), -2),
     (dict(top_k_max=17, E=256), -2),

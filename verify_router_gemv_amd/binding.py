@@ -38,7 +38,8 @@ class MoeRoundError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "hidden", "inter", "n_experts", "top_k_max", "n_layers", "max_rows",
-        "residual", "use_graph", "fused_max_rows", "rows_per_item", "mfma_min_rows", "exact")]
+        "residual", "use_graph", "fused_max_rows", "rows_per_item", "mfma_min_rows", "exact",
+        "weight_format")]
 
 
 class LayerWeights(ctypes.Structure):
@@ -87,12 +88,23 @@ def strerror(status: int) -> str:
         return f"status {status}"
 
 
+WEIGHT_FORMATS = {"q4b32": 0, "q4s256": 1}   # MOE_WEIGHT_Q4B32, MOE_WEIGHT_Q4S256
+
+
+def weight_format_code(fmt) -> int:
+    """0 / 1, or the layout's name ("q4b32", "q4s256")."""
+    if isinstance(fmt, str):
+        return WEIGHT_FORMATS[fmt]
+    return int(fmt)
+
+
 def make_config(H, I, E, top_k_max, n_layers=1, max_rows=8, residual=False, use_graph=True,
-                fused_max_rows=0, rows_per_item=0, mfma_min_rows=0, exact=False) -> Config:
+                fused_max_rows=0, rows_per_item=0, mfma_min_rows=0, exact=False, weight_format=0) -> Config:
     """Launch-shape fields: 0 = default (see moe_round.h); -1 = never (fused_max_rows, mfma_min_rows).
-    exact: fixed-order combine (bitwise reproducible, row outputs independent of the round)."""
+    exact: fixed-order combine (bitwise reproducible, row outputs independent of the round).
+    weight_format: 0 / "q4b32" (per-32 fp16 scale and minimum) or 1 / "q4s256" (super-blocks)."""
     return Config(ABI_VERSION, H, I, E, top_k_max, n_layers, max_rows, int(bool(residual)), int(bool(use_graph)),
-                  fused_max_rows, rows_per_item, mfma_min_rows, int(bool(exact)))
+                  fused_max_rows, rows_per_item, mfma_min_rows, int(bool(exact)), weight_format_code(weight_format))
 
 
 def validate_config(cfg: Config) -> int:
@@ -121,17 +133,28 @@ def _check(t: torch.Tensor, name: str, dtypes, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
-def layer_struct(layer, H: int, I: int, E: int) -> LayerWeights:
+def layer_format(layer):
+    """The weight layout a layer object or dict declares ("fmt" / "format"), or None."""
+    if isinstance(layer, dict):
+        return layer.get("format")
+    return getattr(layer, "fmt", None)
+
+
+def layer_struct(layer, H: int, I: int, E: int, weight_format=0) -> LayerWeights:
     """Marshal one layer's weights (object or dict with the eight tensors) into the C struct."""
+    if weight_format_code(weight_format) == 1:
+        sm_g, sm_d = (E, I, H // 256, 4), (E, H, I // 256, 4)
+    else:
+        sm_g, sm_d = (E, I, H // 32), (E, H, I // 32)
     spec = {
         "router_w": ((torch.float32,), (E, H)),
         "router_bias": ((torch.float32,), (E,)),
         "gate_q": ((torch.uint8,), (E, I, H // 2)),
-        "gate_sm": ((torch.int32, torch.uint32), (E, I, H // 32)),
+        "gate_sm": ((torch.int32, torch.uint32), sm_g),
         "up_q": ((torch.uint8,), (E, I, H // 2)),
-        "up_sm": ((torch.int32, torch.uint32), (E, I, H // 32)),
+        "up_sm": ((torch.int32, torch.uint32), sm_g),
         "down_q": ((torch.uint8,), (E, H, I // 2)),
-        "down_sm": ((torch.int32, torch.uint32), (E, H, I // 32)),
+        "down_sm": ((torch.int32, torch.uint32), sm_d),
     }
     ptrs = {}
     for f in _FIELDS:
@@ -149,15 +172,20 @@ class MoeRound:
 
     def __init__(self, layers: Sequence, H: int, I: int, E: int, top_k_max: int, max_rows: int = 8,
                  residual: bool = False, use_graph: bool = True, stream: Optional[torch.cuda.Stream] = None,
-                 fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0, exact: bool = False):
+                 fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0, exact: bool = False,
+                 weight_format=None):
+        """weight_format: None = what the layers declare (default "q4b32"), else 0/1 or its name."""
         self.lib = load()
         self.H, self.I, self.E, self.L = H, I, E, len(layers)
         self.top_k_max, self.max_rows = top_k_max, max_rows
+        if weight_format is None:
+            weight_format = layer_format(layers[0]) or "q4b32"
+        self.weight_format = weight_format_code(weight_format)
         self.cfg = make_config(H, I, E, top_k_max, self.L, max_rows, residual, use_graph,
-                               fused_max_rows, rows_per_item, mfma_min_rows, exact)
+                               fused_max_rows, rows_per_item, mfma_min_rows, exact, self.weight_format)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._layers = list(layers)          # keep the weight tensors alive
-        self._wt = (LayerWeights * self.L)(*[layer_struct(l, H, I, E) for l in layers])
+        self._wt = (LayerWeights * self.L)(*[layer_struct(l, H, I, E, self.weight_format) for l in layers])
         h = ctypes.c_void_p()
         st = self.lib.moe_round_init(ctypes.byref(self.cfg), self._wt, ctypes.c_void_p(self.stream.cuda_stream),
                                      ctypes.byref(h))
@@ -173,7 +201,8 @@ class MoeRound:
         if len(layers) != self.L:
             raise ValueError("layer count must not change")
         self._layers = list(layers)
-        self._wt = (LayerWeights * self.L)(*[layer_struct(l, self.H, self.I, self.E) for l in layers])
+        self._wt = (LayerWeights * self.L)(*[layer_struct(l, self.H, self.I, self.E, self.weight_format)
+                                             for l in layers])
         return self._wt
 
     def _run_args(self, hidden, k, out, ids, route_w, layers):

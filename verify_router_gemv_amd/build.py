@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_round.so")
-SOURCES = ["moe_round.hip", "moe_validate.cpp"] + [f"moe_gemv_g{g}.hip" for g in (4, 8, 16, 32, 64)]
+SOURCES = (["moe_round.hip", "moe_validate.cpp"] + [f"moe_gemv_g{g}.hip" for g in (4, 8, 16, 32, 64)]
+           + [f"moe_gemv_g{g}_s256.hip" for g in (4, 8, 16, 32, 64)])
 
 ARCH = "gfx950"
 FLAGS = [

@@ -8,7 +8,7 @@ namespace moe {
 
 // EXACT: store W_d h of each pair in its slot of ybuf (the combine kernel adds them in rank order)
 // instead of adding the weighted product into the output with an atomic.
-template <int G, int NB, int RC, int RW, bool EXACT>
+template <int G, int NB, int RC, int RW, bool EXACT, int FMT>
 __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   constexpr int RPI = 64 / G;
   constexpr int ROWS_W = RW * RPI;
@@ -27,10 +27,10 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   const moe_layer_weights W = get_weights(a, layer);
   float* __restrict__ xn = layer_output(a, in, layer);
   const int row0 = tile * ROWS_B + wave * ROWS_W + rs;
-  const size_t rq = static_cast<size_t>(I) / 2, rsm = static_cast<size_t>(I) / 32;
+  const size_t rq = static_cast<size_t>(I) / 2, rsm = sm_row_words<FMT>(I);
 
   uint4 cd[RW][NB];
-  uint32_t sd[RW][NB];
+  BlockScale<FMT> sd[RW][NB];
 #pragma unroll
   for (int w = 0; w < RW; ++w) {
     const size_t r = static_cast<size_t>(wk.e) * H + min(row0 + w * RPI, H - 1);  // rows past H: not stored
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
     for (int nb = 0; nb < NB; ++nb) {
       const int b = g + nb * G;
       cd[w][nb] = load_stream_u4(W.down_q + r * rq + 16 * b);
-      sd[w][nb] = load_stream_u32(W.down_sm + r * rsm + b);
+      sd[w][nb].load(W.down_sm + r * rsm, b);
     }
   }
 

@@ -9,8 +9,9 @@ namespace moe {
 // Codes unpack into bytes (even / odd elements of each 8-group, two VALU per word); each row
 // routed to the expert then costs 24 v_dot4 per 32-weight block plus the fp32 fold
 // s * step * (65536 A2 + 256 A1 + A0) + m * sum(x).
+template <typename BS>
 __device__ __forceinline__ float block_dot_q8(const uint32_t cw[8], const uint32_t xd[kXqWords], float step,
-                                              float xsum, uint32_t sm, float acc) {
+                                              float xsum, const BS& sm, float acc) {
   int A[3] = {0, 0, 0};
 #pragma unroll
   for (int dg = 0; dg < 3; ++dg)
@@ -21,7 +22,7 @@ __device__ __forceinline__ float block_dot_q8(const uint32_t cw[8], const uint32
                                      A[dg], false);
     }
   const float dot = fmaf(static_cast<float>(A[2]), 65536.f, fmaf(static_cast<float>(A[1]), 256.f, static_cast<float>(A[0])));
-  const float sc = half_bits_to_float(sm), mn = half_bits_to_float(sm >> 16);
+  const float sc = sm.scale(), mn = sm.minv();
   return fmaf(sc * step, dot, fmaf(mn, xsum, acc));
 }
 
@@ -223,7 +224,7 @@ constexpr int kGuOneRow = 0, kGuPairs = 1, kGuStaged = 2;
 constexpr int kFusedPairs = 256;  // (row, rank) pairs of a round with the selection fused in
 
 // One unit of gate/up work: work item `wk`, rows tile * ROWS_B .. of I.
-template <int G, int NB, int RW, int MODE>
+template <int G, int NB, int RW, int MODE, int FMT>
 __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const ExpertWork& wk, int tile, uint32_t* xs) {
   constexpr int RPI = 64 / G;
   constexpr int ROWS_W = RW * RPI;
@@ -236,7 +237,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
   const int g = lane % G, rs = lane / G;
   const moe_layer_weights W = get_weights(a, layer);
   const int row0 = tile * ROWS_B + wave * ROWS_W + rs;
-  const size_t rq = static_cast<size_t>(H) / 2, rsm = static_cast<size_t>(H) / 32;
+  const size_t rq = static_cast<size_t>(H) / 2, rsm = sm_row_words<FMT>(H);
   const int SR = a.xstage_h;
 
   // Staging (STAGE): wave w issues the chunk copies w, w + 4, ...; a lane's 16-byte chunk c of the
@@ -263,7 +264,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
     }
   };
   if constexpr (STAGE) stage(0);
-  if constexpr (STAGE && G == 64 && NB == 1 && RW == 4) {  // 16-row tiles over H = 2048
+  if constexpr (STAGE && FMT == kFmtQ4B32 && G == 64 && NB == 1 && RW == 4) {  // 16-row tiles over H = 2048
     if (a.mfma_rows > 0 && wk.np >= a.mfma_rows) {
       gateup_mfma_tile(a, wk, W, tile * ROWS_B, xs_dig, reinterpret_cast<const float*>(xs_ss), SR,
                        xs + gateup_stage_words(H), stage);
@@ -272,7 +273,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
   }
 
   uint4 cg[RW][NB], cu[RW][NB];
-  uint32_t sg[RW][NB], su[RW][NB];
+  BlockScale<FMT> sg[RW][NB], su[RW][NB];
 #pragma unroll
   for (int w = 0; w < RW; ++w) {
     const size_t r = static_cast<size_t>(wk.e) * I + min(row0 + w * RPI, I - 1);  // rows past I: not stored
@@ -281,8 +282,8 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
       const int b = g + nb * G;
       cg[w][nb] = load_stream_u4(W.gate_q + r * rq + 16 * b);
       cu[w][nb] = load_stream_u4(W.up_q + r * rq + 16 * b);
-      sg[w][nb] = load_stream_u32(W.gate_sm + r * rsm + b);
-      su[w][nb] = load_stream_u32(W.up_sm + r * rsm + b);
+      sg[w][nb].load(W.gate_sm + r * rsm, b);
+      su[w][nb].load(W.up_sm + r * rsm, b);
     }
   }
 
@@ -400,7 +401,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
 // Blocks with the selection folded in (SEL > 0) compute it once and then take the units (item,
 // tile) blockIdx.x, blockIdx.x + gridDim.x, ...: the grid is sized for the chip, not for the
 // largest possible item count, so no block repeats the selection only to find no work.
-template <int G, int NB, int RW, int MODE, int SEL>
+template <int G, int NB, int RW, int MODE, int SEL, int FMT>
 __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
   constexpr int ROWS_B = kWaves * RW * (64 / G);
   extern __shared__ uint32_t xs[];  // staged form: gateup_stage_words(H) (+ matrix-core tile) words
@@ -412,13 +413,13 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
     const int units = ssel.ni * tiles;
     for (int w = blockIdx.x; w < units; w += gridDim.x) {
       const int u = w / tiles;
-      gateup_unit<G, NB, RW, MODE>(a, layer, work_from_lds(a, ssel, u), w - u * tiles, xs);
+      gateup_unit<G, NB, RW, MODE, FMT>(a, layer, work_from_lds(a, ssel, u), w - u * tiles, xs);
     }
   } else {
     const int u = blockIdx.x / tiles, tile = blockIdx.x - u * tiles;
     const ExpertWork wk = load_work(a, layer, u);
     if (u >= wk.nu) return;
-    gateup_unit<G, NB, RW, MODE>(a, layer, wk, tile, xs);
+    gateup_unit<G, NB, RW, MODE, FMT>(a, layer, wk, tile, xs);
   }
 }
 

@@ -59,8 +59,56 @@ __device__ __forceinline__ void load_x(const float* src, int row_stride, const i
   }
 }
 
-template <int NB, int RC>
-__device__ __forceinline__ void block_dots(const uint4 c[NB], const uint32_t sm[NB], const float xv[RC][NB][32],
+// ------------------------------------------------------------------------------------------
+// Weight formats: where a 32-weight block's scale s and minimum m come from (w = s*q + m).
+//   kFmtQ4B32:  one word per block, fp16 s (low half) and fp16 m (high half);
+//               a row has K/32 words.
+//   kFmtQ4S256: one 16-byte record per 256-weight super-block: word 0 holds fp16 d (low) and
+//               fp16 dmin (high); words 1..3 a 96-bit string of eight 12-bit fields, field j
+//               (bits 12j..12j+11) the 6-bit scale sc_j and 6-bit minimum m_j of sub-block j;
+//               s = d*sc_j and m = -dmin*m_j (both exact in fp32); a row has K/64 words.
+// The codes are the same in both.
+// ------------------------------------------------------------------------------------------
+constexpr int kFmtQ4B32 = 0, kFmtQ4S256 = 1;
+
+template <int FMT>
+__host__ __device__ constexpr size_t sm_row_words(size_t K) { return FMT == kFmtQ4S256 ? K / 64 : K / 32; }
+
+template <int FMT>
+struct BlockScale;
+
+template <>
+struct BlockScale<kFmtQ4B32> {
+  uint32_t w;
+  __device__ __forceinline__ void load(const uint32_t* sm_row, int b) { w = load_stream_u32(sm_row + b); }
+  __device__ __forceinline__ float scale() const { return half_bits_to_float(w); }
+  __device__ __forceinline__ float minv() const { return half_bits_to_float(w >> 16); }
+};
+
+template <>
+struct BlockScale<kFmtQ4S256> {
+  uint4 r;  // the super-block's record
+  int j;    // sub-block of this 32-weight block
+  __device__ __forceinline__ void load(const uint32_t* sm_row, int b) {
+    r = load_stream_u4(sm_row + 4 * (b >> 3));
+    j = b & 7;
+  }
+  __device__ __forceinline__ uint32_t field() const {
+    const uint64_t lo = static_cast<uint64_t>(r.y) | (static_cast<uint64_t>(r.z) << 32);  // bits 0..63
+    const uint64_t hi = static_cast<uint64_t>(r.z) | (static_cast<uint64_t>(r.w) << 32);  // bits 32..95
+    const uint64_t v = j < 5 ? (lo >> (12 * j)) : (hi >> (12 * j - 32));
+    return static_cast<uint32_t>(v) & 0xFFFu;
+  }
+  __device__ __forceinline__ float scale() const {
+    return half_bits_to_float(r.x) * static_cast<float>(field() & 63u);
+  }
+  __device__ __forceinline__ float minv() const {
+    return -half_bits_to_float(r.x >> 16) * static_cast<float>(field() >> 6);
+  }
+};
+
+template <int NB, int RC, typename BS>
+__device__ __forceinline__ void block_dots(const uint4 c[NB], const BS sm[NB], const float xv[RC][NB][32],
                                            const float xs[RC][NB], float acc[RC]) {
 #pragma unroll
   for (int r = 0; r < RC; ++r) acc[r] = 0.f;
@@ -68,7 +116,7 @@ __device__ __forceinline__ void block_dots(const uint4 c[NB], const uint32_t sm[
   for (int nb = 0; nb < NB; ++nb) {
     float q[32];
     unpack_block(c[nb], q);
-    const float sc = half_bits_to_float(sm[nb]), mn = half_bits_to_float(sm[nb] >> 16);
+    const float sc = sm[nb].scale(), mn = sm[nb].minv();
 #pragma unroll
     for (int r = 0; r < RC; ++r) acc[r] = fmaf(mn, xs[r][nb], fmaf(sc, dot32(q, xv[r][nb]), acc[r]));
   }

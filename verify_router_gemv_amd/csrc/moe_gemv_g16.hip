@@ -3,6 +3,6 @@
 
 namespace moe {
 bool pick_gemv_g16(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
-  return pick_nb<16>(NB, RC, up, sel, fn, rows);
+  return pick_nb<16, kFmtQ4B32>(NB, RC, up, sel, fn, rows);
 }
 }  // namespace moe

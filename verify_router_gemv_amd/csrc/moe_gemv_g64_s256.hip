@@ -1,0 +1,9 @@
+// GEMV kernels (gate/up and down) for rows split over 64 lanes, 4.5-bit super-block weights;
+// see moe_kernels.h.
+#include "moe_kernels.h"
+
+namespace moe {
+bool pick_gemv_g64_s256(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
+  return pick_nb<64, kFmtQ4S256>(NB, RC, up, sel, fn, rows);
+}
+}  // namespace moe

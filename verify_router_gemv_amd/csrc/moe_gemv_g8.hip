@@ -3,6 +3,6 @@
 
 namespace moe {
 bool pick_gemv_g8(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
-  return pick_nb<8>(NB, RC, up, sel, fn, rows);
+  return pick_nb<8, kFmtQ4B32>(NB, RC, up, sel, fn, rows);
 }
 }  // namespace moe

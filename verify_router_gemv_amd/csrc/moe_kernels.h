@@ -15,35 +15,39 @@ using KernelFn = void (*)(Args, int);
 
 constexpr int rows_per_lane_group(int NB) { return NB == 1 ? 4 : (NB == 2 ? 2 : 1); }
 
-template <int G, int NB, int RC>
+template <int G, int NB, int RC, int FMT>
 struct GemvPick {
   static constexpr int RW = rows_per_lane_group(NB);
   // sel: keys per lane of the fused selection (4: E <= 256, 8: E <= 512), 0: read the records of
   // the selection kernel (always for the staged form).
   static KernelFn gateup(int mode, int sel) {
-    if (mode == kGuStaged) return gateup_kernel<G, NB, RW, kGuStaged, 0>;
+    if (mode == kGuStaged) return gateup_kernel<G, NB, RW, kGuStaged, 0, FMT>;
     if (mode == kGuOneRow)
-      return sel == 4 ? gateup_kernel<G, NB, RW, kGuOneRow, 4>
-             : sel == 8 ? gateup_kernel<G, NB, RW, kGuOneRow, 8> : gateup_kernel<G, NB, RW, kGuOneRow, 0>;
-    return sel == 4 ? gateup_kernel<G, NB, RW, kGuPairs, 4>
-           : sel == 8 ? gateup_kernel<G, NB, RW, kGuPairs, 8> : gateup_kernel<G, NB, RW, kGuPairs, 0>;
+      return sel == 4   ? gateup_kernel<G, NB, RW, kGuOneRow, 4, FMT>
+             : sel == 8 ? gateup_kernel<G, NB, RW, kGuOneRow, 8, FMT>
+                        : gateup_kernel<G, NB, RW, kGuOneRow, 0, FMT>;
+    return sel == 4   ? gateup_kernel<G, NB, RW, kGuPairs, 4, FMT>
+           : sel == 8 ? gateup_kernel<G, NB, RW, kGuPairs, 8, FMT>
+                      : gateup_kernel<G, NB, RW, kGuPairs, 0, FMT>;
   }
-  static KernelFn down(bool exact) { return exact ? down_kernel<G, NB, RC, RW, true> : down_kernel<G, NB, RC, RW, false>; }
+  static KernelFn down(bool exact) {
+    return exact ? down_kernel<G, NB, RC, RW, true, FMT> : down_kernel<G, NB, RC, RW, false, FMT>;
+  }
   static constexpr int rows_per_block() { return kWaves * RW * (64 / G); }
 };
 
-template <int G, int NB>
+template <int G, int NB, int FMT>
 inline bool pick_rc(int RC, bool up, int sel, KernelFn* fn, int* rows) {
   if (up) {  // for gate/up RC is the mode (kGuOneRow, kGuPairs, kGuStaged); for down sel != 0: exact
-    *fn = GemvPick<G, NB, 1>::gateup(RC, sel);
-    *rows = GemvPick<G, NB, 1>::rows_per_block();
+    *fn = GemvPick<G, NB, 1, FMT>::gateup(RC, sel);
+    *rows = GemvPick<G, NB, 1, FMT>::rows_per_block();
     return true;
   }
   switch (RC) {
-#define MOE_RC(R)                                 \
-  case R:                                         \
-    *fn = GemvPick<G, NB, R>::down(sel != 0);     \
-    *rows = GemvPick<G, NB, R>::rows_per_block(); \
+#define MOE_RC(R)                                      \
+  case R:                                              \
+    *fn = GemvPick<G, NB, R, FMT>::down(sel != 0);     \
+    *rows = GemvPick<G, NB, R, FMT>::rows_per_block(); \
     return true;
     MOE_RC(1) MOE_RC(2) MOE_RC(4)
 #undef MOE_RC
@@ -51,26 +55,44 @@ inline bool pick_rc(int RC, bool up, int sel, KernelFn* fn, int* rows) {
   return false;
 }
 
-template <int G>
+template <int G, int FMT>
 inline bool pick_nb(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
   switch (NB) {
-    case 1: return pick_rc<G, 1>(RC, up, sel, fn, rows);
-    case 2: return pick_rc<G, 2>(RC, up, sel, fn, rows);
-    case 3: return pick_rc<G, 3>(RC, up, sel, fn, rows);
-    case 4: return pick_rc<G, 4>(RC, up, sel, fn, rows);
+    case 1: return pick_rc<G, 1, FMT>(RC, up, sel, fn, rows);
+    case 2: return pick_rc<G, 2, FMT>(RC, up, sel, fn, rows);
+    case 3: return pick_rc<G, 3, FMT>(RC, up, sel, fn, rows);
+    case 4: return pick_rc<G, 4, FMT>(RC, up, sel, fn, rows);
   }
   return false;
 }
 
-// Each lane split G is instantiated in its own translation unit (moe_gemv_g<G>.hip) so the
-// library builds in parallel.
-bool pick_gemv_g4(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
-bool pick_gemv_g8(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
-bool pick_gemv_g16(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
-bool pick_gemv_g32(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
-bool pick_gemv_g64(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
+// Each (lane split G, weight format) pair is instantiated in its own translation unit
+// (moe_gemv_g<G>.hip for the per-32 format, moe_gemv_g<G>_s256.hip for super-blocks) so the library
+// builds in parallel.
+#define MOE_DECLARE_PICK(NAME) bool NAME(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
+MOE_DECLARE_PICK(pick_gemv_g4)
+MOE_DECLARE_PICK(pick_gemv_g8)
+MOE_DECLARE_PICK(pick_gemv_g16)
+MOE_DECLARE_PICK(pick_gemv_g32)
+MOE_DECLARE_PICK(pick_gemv_g64)
+MOE_DECLARE_PICK(pick_gemv_g4_s256)
+MOE_DECLARE_PICK(pick_gemv_g8_s256)
+MOE_DECLARE_PICK(pick_gemv_g16_s256)
+MOE_DECLARE_PICK(pick_gemv_g32_s256)
+MOE_DECLARE_PICK(pick_gemv_g64_s256)
+#undef MOE_DECLARE_PICK
 
-inline bool pick_gemv(int G, int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
+inline bool pick_gemv(int G, int NB, int RC, bool up, int sel, int fmt, KernelFn* fn, int* rows) {
+  if (fmt == kFmtQ4S256) {
+    switch (G) {
+      case 4: return pick_gemv_g4_s256(NB, RC, up, sel, fn, rows);
+      case 8: return pick_gemv_g8_s256(NB, RC, up, sel, fn, rows);
+      case 16: return pick_gemv_g16_s256(NB, RC, up, sel, fn, rows);
+      case 32: return pick_gemv_g32_s256(NB, RC, up, sel, fn, rows);
+      case 64: return pick_gemv_g64_s256(NB, RC, up, sel, fn, rows);
+    }
+    return false;
+  }
   switch (G) {
     case 4: return pick_gemv_g4(NB, RC, up, sel, fn, rows);
     case 8: return pick_gemv_g8(NB, RC, up, sel, fn, rows);

@@ -170,8 +170,9 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   KernelFn lg = pick_logits(H, T), sel = pick_select(E), gu = nullptr, dn = nullptr;
   int rows_gu = 0, rows_dn = 0;
   const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
-  if (!lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, fused ? fused_select_keys(E) : 0, &gu, &rows_gu) ||
-      !pick_gemv(h->Gi, h->NBi, RC, false, h->cfg.exact, &dn, &rows_dn))
+  const int fmt = h->cfg.weight_format;
+  if (!lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, fused ? fused_select_keys(E) : 0, fmt, &gu, &rows_gu) ||
+      !pick_gemv(h->Gi, h->NBi, RC, false, h->cfg.exact, fmt, &dn, &rows_dn))
     return false;
   const int tc = logits_rows(T);
   const dim3 grid_lg((E + kRouteExpertsPerBlock - 1) / kRouteExpertsPerBlock, (T + tc - 1) / tc);
