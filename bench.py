@@ -207,6 +207,7 @@ def main():
     exact = None if args.no_extra else exact_rounds(cfg, base, acts, torch, np, MoeRound)
     wide = None if args.no_extra else wide_rounds(cfg, base, torch, np, synth, MoeRound)
     deep = None if args.no_extra else deep_stack(torch, np, synth, MoeRound)
+    superblock = None if args.no_extra else superblock_rounds(acts, args.replicas, torch, np, synth, MoeRound)
 
     cpu = None
     if not args.no_cpu:
@@ -236,6 +237,7 @@ def main():
         "exact_mode": exact,
         "wide_rounds": wide,
         "deep_stack": deep,
+        "superblock_format": superblock,
     }
     print(json.dumps(line), flush=True)
     if args.pmc_calibrate:
@@ -359,10 +361,11 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
     return res
 
 
-def deep_stack(torch, np, synth, MoeRound):
-    """48 MoE layers (E=512, top-10, I=512), T=3, residual, ~48 GB of expert weights resident: one
-    round as one captured hipGraph, and eager, with per-layer unique experts and metric bytes."""
-    cfg = synth.config("deep")
+def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager")):
+    """48 MoE layers (E=512, top-10, I=512), T=3, residual, ~48 GB of expert weights resident (43.5 GB
+    in the 4.5-bit layout): one round as one captured hipGraph, and eager, with per-layer unique
+    experts and metric bytes."""
+    cfg = synth.config("deep").replace(fmt=fmt)
     t0 = time.perf_counter()
     layers = [synth.make_layer(cfg, seed=0, layer=l, device="cuda") for l in range(cfg.L)]
     gen_s = time.perf_counter() - t0
@@ -371,7 +374,7 @@ def deep_stack(torch, np, synth, MoeRound):
     out = torch.empty((T, cfg.H), device="cuda")
     res = {"layers": cfg.L, "T": T, "weights_GB": round(cfg.L * cfg.E * cfg.expert_bytes() / 1e9, 2),
            "generate_s": round(gen_s, 1)}
-    for mode in ("graph", "eager"):
+    for mode in modes:
         h = MoeRound(layers, cfg.H, cfg.I, cfg.E, cfg.k, max_rows=T, residual=True, use_graph=(mode == "graph"))
         for r in range(3):
             h.run(xs[r], cfg.k, out)
@@ -385,6 +388,53 @@ def deep_stack(torch, np, synth, MoeRound):
         h.close()
     del layers
     torch.cuda.empty_cache()
+    return res
+
+
+def superblock_rounds(acts, replicas, torch, np, synth, MoeRound):
+    """The verify sweep with the 4.5-bit super-block layout (Q4S256): per width, round latency, per-kernel
+    time, unique experts and metric bytes, on as many weight replicas as the headline; then the
+    48-layer stack in that layout as one hipGraph."""
+    cfg = synth.config("verify").replace(fmt="q4s256")
+    base = synth.make_layer(cfg, seed=0, layer=0, device="cuda")
+    reps = [base] + [base.clone() for _ in range(replicas - 1)]
+    hs = [MoeRound([rp], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(TS), use_graph=False) for rp in reps]
+    R = len(hs)
+    res = {"format": "q4s256: 4-bit codes, 256-weight super-blocks, 6-bit sub-block scale/min (0.5625 B/weight)",
+           "expert_bytes": cfg.expert_bytes(), "verify": {}}
+    for T in TS:
+        out = torch.empty((T, cfg.H), device="cuda")
+        for r in range(2 * R):
+            hs[r % R].run(acts[T][r % len(acts[T])], cfg.k, out)
+        lat, nus = [], []
+        for r in range(64):
+            h = hs[r % R]
+            lat.append(timed_rounds(h, [acts[T][r % len(acts[T])]], cfg.k, out, 1, torch)[0])
+            nus.append(h.last_unique()[0])
+        for h in hs:
+            h.profile(True)
+            h.profile_read()
+        for r in range(64):
+            hs[r % R].run(acts[T][r % len(acts[T])], cfg.k, out)
+        kms, runs = np.zeros(5), 0
+        for h in hs:
+            ms, n = h.profile_read()
+            kms += np.array(ms[0])
+            runs += n
+            h.profile(False)
+        med = float(np.median(lat))
+        nu = float(np.mean(nus))
+        mb = synth.inputs.metric_bytes(cfg, nu, T)
+        res["verify"][str(T)] = {
+            "round_us_median": round(med, 2), "tok_per_s": round(T / med * 1e6, 1), "n_unique": round(nu, 2),
+            "metric_bytes": int(mb), "metric_GBps": round(mb / med / 1e3, 1),
+            "kernel_us": {n: round(float(v) * 1e3 / runs, 2)
+                          for n, v in zip(("logits", "select", "gateup", "down", "combine"), kms)}}
+    for h in hs:
+        h.close()
+    del hs, reps, base
+    torch.cuda.empty_cache()
+    res["deep_stack"] = deep_stack(torch, np, synth, MoeRound, fmt="q4s256", modes=("graph",))
     return res
 
 
