@@ -46,7 +46,7 @@ constexpr int kRecRowWord = 4;
 // odd word 8g+1,3,5,7, matching the nibble order of a weight code word.
 constexpr int kXqWords = 24;
 constexpr float kXqMax = 8355711.0f;  // 127*65536 + 127*256 + 127
-constexpr int kXStageMax = 8;        // activation rows staged in LDS at a time (T > 1) ...
+constexpr int kXStageMax = 8;        // SwiGLU rows the down kernel stages in LDS as digits at a time ...
 constexpr int kXStageBytes = 65536;  // ... within 64 KB of LDS
 
 // Per-run pointers. Eager launches carry them by value; graph replays read them from a fixed
@@ -271,48 +271,6 @@ __device__ __forceinline__ float4 load_f4(const void* p) {
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
-}
-
-// Single-instruction byte -> float conversions (v_cvt_f32_ubyte0..3).
-#define MOE_CVT_UBYTE(N)                                                            \
-  __device__ __forceinline__ float cvt_ubyte##N(uint32_t v) {                       \
-    float r;                                                                        \
-    asm("v_cvt_f32_ubyte" #N " %0, %1" : "=v"(r) : "v"(v));                         \
-    return r;                                                                       \
-  }
-MOE_CVT_UBYTE(0)
-MOE_CVT_UBYTE(1)
-MOE_CVT_UBYTE(2)
-MOE_CVT_UBYTE(3)
-#undef MOE_CVT_UBYTE
-
-// 32 codes of one block (16 bytes, byte j = element 2j | element 2j+1 << 4) -> floats in order,
-// 11 VALU instructions per 8 codes.
-__device__ __forceinline__ void unpack_block(const uint4 c, float q[32]) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = w[i] & 0x0F0F0F0Fu;         // elements 8i+0, +2, +4, +6
-    const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;  // elements 8i+1, +3, +5, +7
-    q[8 * i + 0] = cvt_ubyte0(lo);
-    q[8 * i + 1] = cvt_ubyte0(hi);
-    q[8 * i + 2] = cvt_ubyte1(lo);
-    q[8 * i + 3] = cvt_ubyte1(hi);
-    q[8 * i + 4] = cvt_ubyte2(lo);
-    q[8 * i + 5] = cvt_ubyte2(hi);
-    q[8 * i + 6] = cvt_ubyte3(lo);
-    q[8 * i + 7] = cvt_ubyte3(hi);
-  }
-}
-
-__device__ __forceinline__ float dot32(const float q[32], const float x[32]) {
-  float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; i += 2) {
-    d0 = fmaf(q[i], x[i], d0);
-    d1 = fmaf(q[i + 1], x[i + 1], d1);
-  }
-  return d0 + d1;
 }
 
 // Make a value opaque to the optimiser so per-pass unpacking is not hoisted out of the pass loop

@@ -1,20 +1,74 @@
 // Kernel 4: down dequant-GEMV with the routing-weighted scatter-add.
 #pragma once
 
-#include "moe_gemv.h"
+#include "moe_gateup.h"
 
 namespace moe {
 
 
+// The item's SwiGLU rows as int8 digits in LDS, by the whole block: 8 threads per 32-block, 4
+// elements each, in the layout and with the rounding of the layer input's digits (kXqWords words
+// per block: three balanced base-256 digits of rint(h / step), step = max|h| / kXqMax), plus the
+// block's (step, sum of h). `n` rows of length K, contiguous from `src`.
+__device__ __forceinline__ void stage_digits(const float* src, int K, int n, uint32_t* dig, float2* ss) {
+  const int nblk = K / 32, total = n * nblk;
+  const int tid = threadIdx.x, sub = tid & 7;
+  for (int blk0 = 0; blk0 < total; blk0 += kThreads / 8) {
+    const int blk = blk0 + (tid >> 3);
+    const int bc = min(blk, total - 1);  // past the end: a clamped block, still in the reductions
+    const float4 v = load_f4(src + static_cast<size_t>(bc) * 32 + 4 * sub);
+    float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    float sum = (v.x + v.y) + (v.z + v.w);
+    mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
+    sum += dpp_f32<kDppXor1>(sum);
+    mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
+    sum += dpp_f32<kDppXor2>(sum);
+    mx = fmaxf(mx, dpp_f32<kDppHalfMirror>(mx));  // the 8 lanes of this block
+    sum += dpp_f32<kDppHalfMirror>(sum);
+    const float inv = mx > 0.f ? kXqMax / mx : 0.f;
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    int d[3][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int q = static_cast<int>(rintf(e[i] * inv));
+      q = max(-static_cast<int>(kXqMax), min(static_cast<int>(kXqMax), q));
+      const int d0 = ((q + 128) & 255) - 128;
+      const int q1 = (q - d0) >> 8;
+      const int d1 = ((q1 + 128) & 255) - 128;
+      d[0][i] = d0;
+      d[1][i] = d1;
+      d[2][i] = (q1 - d1) >> 8;
+    }
+    if (blk < total) {
+      // element 4*sub + i: group sub / 2, even word for i = 0, 2 and odd for i = 1, 3, bytes
+      // 2*(sub % 2) + i / 2 of the word
+      uint16_t* base = reinterpret_cast<uint16_t*>(dig + static_cast<size_t>(blk) * kXqWords);
+      const int g = sub >> 1, half = sub & 1;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const uint16_t ev = static_cast<uint16_t>((d[p][0] & 0xFF) | ((d[p][2] & 0xFF) << 8));
+        const uint16_t od = static_cast<uint16_t>((d[p][1] & 0xFF) | ((d[p][3] & 0xFF) << 8));
+        base[((p * 4 + g) * 2 + 0) * 2 + half] = ev;
+        base[((p * 4 + g) * 2 + 1) * 2 + half] = od;
+      }
+      if (sub == 0) ss[blk] = make_float2(mx / kXqMax, sum);
+    }
+  }
+}
+
+// Down: W_d h for each pair of the work item, the same integer-digit dot product as gate/up: the
+// item's h rows are quantised into LDS (a chunk of a.xstage_i rows at a time), then each lane takes
+// its 32-blocks' digits row by row against its RW weight rows.
 // EXACT: store W_d h of each pair in its slot of ybuf (the combine kernel adds them in rank order)
 // instead of adding the weighted product into the output with an atomic.
-template <int G, int NB, int RC, int RW, bool EXACT, int FMT>
+template <int G, int NB, int RW, bool EXACT, int FMT>
 __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   constexpr int RPI = 64 / G;
   constexpr int ROWS_W = RW * RPI;
   constexpr int ROWS_B = kWaves * ROWS_W;
-  extern __shared__ float hlds[];  // [xstage_i][I] when T > 1
+  extern __shared__ uint32_t dlds[];  // [xstage_i][I/32][kXqWords] digits, then [xstage_i][I/32] (step, sum)
   const int I = a.I, H = a.H, T = a.T;
+  const int nblk = I / 32;
   const int tiles = (H + ROWS_B - 1) / ROWS_B;
   const int u = blockIdx.x / tiles, tile = blockIdx.x - u * tiles;
   const ExpertWork wk = load_work(a, layer, u);
@@ -42,57 +96,63 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
     }
   }
 
-  const int xst = T > 1 ? a.xstage_i : MOE_ROUND_MAX_ROWS;
+  const int xst = a.xstage_i;
+  uint32_t* dig = dlds;
+  float2* ss = reinterpret_cast<float2*>(dlds + static_cast<size_t>(xst) * nblk * kXqWords);
   for (int s0 = 0; s0 < wk.np; s0 += xst) {
     const int ns = min(xst, wk.np - s0);
-    const float* src = a.hbuf + static_cast<size_t>(wk.p0 + s0) * I;
-    if (T > 1) {
-      __syncthreads();
-      stage_rows(hlds, src, I, ns, [&](int r) { return r; });
-      __syncthreads();
-      src = hlds;
-    }
-    for (int c = 0; c < ns; c += RC) {
-      int row_of[RC];
+    if (s0 > 0) __syncthreads();  // the previous chunk has been read by every wave
+    stage_digits(a.hbuf + static_cast<size_t>(wk.p0 + s0) * I, I, ns, dig, ss);
+    __syncthreads();
+    for (int c = 0; c < ns; ++c) {
+      const float wgt = pw[wk.p0 + s0 + c];
+      uint32_t xd[NB][kXqWords];
+      float xstep[NB], xsum[NB];
 #pragma unroll
-      for (int r = 0; r < RC; ++r) row_of[r] = min(c + r, ns - 1);
-      float wpass[RC];
+      for (int nb = 0; nb < NB; ++nb) {
+        const int blk = c * nblk + g + nb * G;
+        const uint32_t* srcw = dig + static_cast<size_t>(blk) * kXqWords;
 #pragma unroll
-      for (int r = 0; r < RC; ++r) wpass[r] = pw[wk.p0 + s0 + min(c + r, ns - 1)];
-      float xv[RC][NB][32], xs[RC][NB];
-      if (T > 1) load_x<NB, RC, G, true>(src, I, row_of, ns - c, g, xv, xs);
-      else load_x<NB, RC, G, false>(src, I, row_of, ns - c, g, xv, xs);
+        for (int q = 0; q < kXqWords / 4; ++q) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(srcw + 4 * q);
+          xd[nb][4 * q + 0] = v.x;
+          xd[nb][4 * q + 1] = v.y;
+          xd[nb][4 * q + 2] = v.z;
+          xd[nb][4 * q + 3] = v.w;
+        }
+        const float2 t = ss[blk];
+        xstep[nb] = t.x;
+        xsum[nb] = t.y;
+      }
+      float acc[RW];
 #pragma unroll
-      for (int w = 0; w < RW; ++w)
+      for (int w = 0; w < RW; ++w) {
+        float ay = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) opaque(cd[w][nb]);
-      float acc[RW][RC];
-#pragma unroll
-      for (int w = 0; w < RW; ++w) block_dots<NB, RC>(cd[w], sd[w], xv, xs, acc[w]);
-#pragma unroll
-      for (int w = 0; w < RW; ++w)
-#pragma unroll
-        for (int r = 0; r < RC; ++r) acc[w][r] = group_sum<G>(acc[w][r]);
+        for (int nb = 0; nb < NB; ++nb) {
+          uint4 cc = cd[w][nb];
+          opaque(cc);  // unpack here, per row: not hoisted out of the row loop
+          uint32_t cw[8];
+          unpack_bytes(cc, cw);
+          ay = block_dot_q8(cw, xd[nb], xstep[nb], xsum[nb], sd[w][nb], ay);
+        }
+        acc[w] = group_sum<G>(ay);
+      }
       if (g == 0) {
+        const int slot = s0 + c;
+        if constexpr (EXACT) {
+          float* y = a.ybuf + static_cast<size_t>(wk.p0 + slot) * H;
 #pragma unroll
-        for (int r = 0; r < RC; ++r) {
-          if (c + r >= ns) continue;
-          const int slot = s0 + c + r;
-          if constexpr (EXACT) {
-            float* y = a.ybuf + static_cast<size_t>(wk.p0 + slot) * H;
+          for (int w = 0; w < RW; ++w) {
+            const int hr = row0 + w * RPI;
+            if (hr < H) y[hr] = acc[w];
+          }
+        } else {
+          const int t = work_row(wk, slot, T);
 #pragma unroll
-            for (int w = 0; w < RW; ++w) {
-              const int hr = row0 + w * RPI;
-              if (hr < H) y[hr] = acc[w][r];
-            }
-          } else {
-            const int t = work_row(wk, slot, T);
-            const float wgt = wpass[r];
-#pragma unroll
-            for (int w = 0; w < RW; ++w) {
-              const int hr = row0 + w * RPI;
-              if (hr < H) atomicAdd(xn + static_cast<size_t>(t) * H + hr, wgt * acc[w][r]);
-            }
+          for (int w = 0; w < RW; ++w) {
+            const int hr = row0 + w * RPI;
+            if (hr < H) atomicAdd(xn + static_cast<size_t>(t) * H + hr, wgt * acc[w]);
           }
         }
       }

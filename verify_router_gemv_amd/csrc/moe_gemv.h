@@ -1,4 +1,4 @@
-// Shared pieces of the dequant-GEMV kernels (lane layout, activation loads, LDS staging).
+// Shared pieces of the dequant-GEMV kernels (lane layout, weight formats).
 #pragma once
 
 #include "moe_route.h"
@@ -11,53 +11,9 @@ namespace moe {
 //
 // Lane layout: G lanes share one weight row, each owning NB of its 32-weight blocks (block
 // b = g + nb*G); a wave covers 64/G rows per load and RW such row groups (for gate/up: of both
-// matrices). Codes (16 B) and the scale/min word (4 B) of each block are loaded once into
-// registers. The activation rows routed to the expert are processed RC at a time from registers:
-// for T == 1 loaded directly, otherwise staged kXStage rows at a time in LDS. Per block the dot
-// product is s * sum(q*x) + m * sum(x).
-
-// Load RC activation rows' segments for this lane, from LDS rows (FROM_LDS) or global rows.
-template <int NB, int RC, int G, bool FROM_LDS>
-__device__ __forceinline__ void load_x(const float* src, int row_stride, const int* row_of, int nlive, int g,
-                                       float xv[RC][NB][32], float xs[RC][NB]) {
-#pragma unroll
-  for (int r = 0; r < RC; ++r) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const size_t off = static_cast<size_t>(row_of[r]) * row_stride + 32 * (g + nb * G);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float4 v;
-        if constexpr (FROM_LDS) {
-          const f32x4 t = *((const __attribute__((address_space(3))) f32x4*)(src + off) + q);
-          v = make_float4(t.x, t.y, t.z, t.w);
-        } else {
-          v = load_f4(src + off + 4 * q);  // row_of[] is always a valid row
-        }
-        xv[r][nb][4 * q + 0] = v.x;
-        xv[r][nb][4 * q + 1] = v.y;
-        xv[r][nb][4 * q + 2] = v.z;
-        xv[r][nb][4 * q + 3] = v.w;
-      }
-    }
-  }
-  // zero the rows past the live count after every load has been issued
-#pragma unroll
-  for (int r = 0; r < RC; ++r) {
-    const bool live = r < nlive;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float sum = 0.f;
-#pragma unroll
-      for (int q = 0; q < 32; ++q) {
-        xv[r][nb][q] = live ? xv[r][nb][q] : 0.f;
-      }
-#pragma unroll
-      for (int q = 0; q < 32; q += 4) sum += (xv[r][nb][q] + xv[r][nb][q + 1]) + (xv[r][nb][q + 2] + xv[r][nb][q + 3]);
-      xs[r][nb] = sum;
-    }
-  }
-}
+// matrices). Codes (16 B) and the block's scale/minimum source of each block are loaded once into
+// registers. The activation rows (the layer input for gate/up, the SwiGLU rows for down) are
+// int8 digits per 32-block; per block the dot product is s * step * (integer dot) + m * sum(x).
 
 // ------------------------------------------------------------------------------------------
 // Weight formats: where a 32-weight block's scale s and minimum m come from (w = s*q + m).
@@ -106,31 +62,5 @@ struct BlockScale<kFmtQ4S256> {
     return -half_bits_to_float(r.x >> 16) * static_cast<float>(field() >> 6);
   }
 };
-
-template <int NB, int RC, typename BS>
-__device__ __forceinline__ void block_dots(const uint4 c[NB], const BS sm[NB], const float xv[RC][NB][32],
-                                           const float xs[RC][NB], float acc[RC]) {
-#pragma unroll
-  for (int r = 0; r < RC; ++r) acc[r] = 0.f;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float q[32];
-    unpack_block(c[nb], q);
-    const float sc = sm[nb].scale(), mn = sm[nb].minv();
-#pragma unroll
-    for (int r = 0; r < RC; ++r) acc[r] = fmaf(mn, xs[r][nb], fmaf(sc, dot32(q, xv[r][nb]), acc[r]));
-  }
-}
-
-// Cooperative copy of up to `n` rows (row ids from `rowid(r)`) of length K into LDS.
-template <typename RowFn>
-__device__ __forceinline__ void stage_rows(float* lds, const float* src, int K, int n, RowFn rowid) {
-  const int k4 = K / 4;
-  float4* d4 = reinterpret_cast<float4*>(lds);
-  for (int idx = threadIdx.x; idx < n * k4; idx += kThreads) {
-    const int r = idx / k4, c4 = idx - r * k4;
-    d4[idx] = reinterpret_cast<const float4*>(src + static_cast<size_t>(rowid(r)) * K)[c4];
-  }
-}
 
 }  // namespace moe

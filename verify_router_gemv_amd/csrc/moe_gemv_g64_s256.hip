@@ -3,7 +3,7 @@
 #include "moe_kernels.h"
 
 namespace moe {
-bool pick_gemv_g64_s256(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
-  return pick_nb<64, kFmtQ4S256>(NB, RC, up, sel, fn, rows);
+bool pick_gemv_g64_s256(int NB, int mode, bool up, int sel, KernelFn* fn, int* rows) {
+  return pick_nb<64, kFmtQ4S256>(NB, mode, up, sel, fn, rows);
 }
 }  // namespace moe

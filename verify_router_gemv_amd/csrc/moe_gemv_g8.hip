@@ -2,7 +2,7 @@
 #include "moe_kernels.h"
 
 namespace moe {
-bool pick_gemv_g8(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
-  return pick_nb<8, kFmtQ4B32>(NB, RC, up, sel, fn, rows);
+bool pick_gemv_g8(int NB, int mode, bool up, int sel, KernelFn* fn, int* rows) {
+  return pick_nb<8, kFmtQ4B32>(NB, mode, up, sel, fn, rows);
 }
 }  // namespace moe

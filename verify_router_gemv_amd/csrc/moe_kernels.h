@@ -15,7 +15,7 @@ using KernelFn = void (*)(Args, int);
 
 constexpr int rows_per_lane_group(int NB) { return NB == 1 ? 4 : (NB == 2 ? 2 : 1); }
 
-template <int G, int NB, int RC, int FMT>
+template <int G, int NB, int FMT>
 struct GemvPick {
   static constexpr int RW = rows_per_lane_group(NB);
   // sel: keys per lane of the fused selection (4: E <= 256, 8: E <= 512), 0: read the records of
@@ -31,37 +31,27 @@ struct GemvPick {
                       : gateup_kernel<G, NB, RW, kGuPairs, 0, FMT>;
   }
   static KernelFn down(bool exact) {
-    return exact ? down_kernel<G, NB, RC, RW, true, FMT> : down_kernel<G, NB, RC, RW, false, FMT>;
+    return exact ? down_kernel<G, NB, RW, true, FMT> : down_kernel<G, NB, RW, false, FMT>;
   }
   static constexpr int rows_per_block() { return kWaves * RW * (64 / G); }
 };
 
+// up: the gate/up kernel of form `mode` (kGuOneRow, kGuPairs, kGuStaged) with `sel` keys per lane
+// of a folded selection (0: none); otherwise the down kernel (mode unused), exact mode if sel != 0.
 template <int G, int NB, int FMT>
-inline bool pick_rc(int RC, bool up, int sel, KernelFn* fn, int* rows) {
-  if (up) {  // for gate/up RC is the mode (kGuOneRow, kGuPairs, kGuStaged); for down sel != 0: exact
-    *fn = GemvPick<G, NB, 1, FMT>::gateup(RC, sel);
-    *rows = GemvPick<G, NB, 1, FMT>::rows_per_block();
-    return true;
-  }
-  switch (RC) {
-#define MOE_RC(R)                                      \
-  case R:                                              \
-    *fn = GemvPick<G, NB, R, FMT>::down(sel != 0);     \
-    *rows = GemvPick<G, NB, R, FMT>::rows_per_block(); \
-    return true;
-    MOE_RC(1) MOE_RC(2) MOE_RC(4)
-#undef MOE_RC
-  }
-  return false;
+inline bool pick_form(int mode, bool up, int sel, KernelFn* fn, int* rows) {
+  *fn = up ? GemvPick<G, NB, FMT>::gateup(mode, sel) : GemvPick<G, NB, FMT>::down(sel != 0);
+  *rows = GemvPick<G, NB, FMT>::rows_per_block();
+  return true;
 }
 
 template <int G, int FMT>
-inline bool pick_nb(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
+inline bool pick_nb(int NB, int mode, bool up, int sel, KernelFn* fn, int* rows) {
   switch (NB) {
-    case 1: return pick_rc<G, 1, FMT>(RC, up, sel, fn, rows);
-    case 2: return pick_rc<G, 2, FMT>(RC, up, sel, fn, rows);
-    case 3: return pick_rc<G, 3, FMT>(RC, up, sel, fn, rows);
-    case 4: return pick_rc<G, 4, FMT>(RC, up, sel, fn, rows);
+    case 1: return pick_form<G, 1, FMT>(mode, up, sel, fn, rows);
+    case 2: return pick_form<G, 2, FMT>(mode, up, sel, fn, rows);
+    case 3: return pick_form<G, 3, FMT>(mode, up, sel, fn, rows);
+    case 4: return pick_form<G, 4, FMT>(mode, up, sel, fn, rows);
   }
   return false;
 }
@@ -69,7 +59,7 @@ inline bool pick_nb(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows) {
 // Each (lane split G, weight format) pair is instantiated in its own translation unit
 // (moe_gemv_g<G>.hip for the per-32 format, moe_gemv_g<G>_s256.hip for super-blocks) so the library
 // builds in parallel.
-#define MOE_DECLARE_PICK(NAME) bool NAME(int NB, int RC, bool up, int sel, KernelFn* fn, int* rows);
+#define MOE_DECLARE_PICK(NAME) bool NAME(int NB, int mode, bool up, int sel, KernelFn* fn, int* rows);
 MOE_DECLARE_PICK(pick_gemv_g4)
 MOE_DECLARE_PICK(pick_gemv_g8)
 MOE_DECLARE_PICK(pick_gemv_g16)
@@ -82,23 +72,23 @@ MOE_DECLARE_PICK(pick_gemv_g32_s256)
 MOE_DECLARE_PICK(pick_gemv_g64_s256)
 #undef MOE_DECLARE_PICK
 
-inline bool pick_gemv(int G, int NB, int RC, bool up, int sel, int fmt, KernelFn* fn, int* rows) {
+inline bool pick_gemv(int G, int NB, int mode, bool up, int sel, int fmt, KernelFn* fn, int* rows) {
   if (fmt == kFmtQ4S256) {
     switch (G) {
-      case 4: return pick_gemv_g4_s256(NB, RC, up, sel, fn, rows);
-      case 8: return pick_gemv_g8_s256(NB, RC, up, sel, fn, rows);
-      case 16: return pick_gemv_g16_s256(NB, RC, up, sel, fn, rows);
-      case 32: return pick_gemv_g32_s256(NB, RC, up, sel, fn, rows);
-      case 64: return pick_gemv_g64_s256(NB, RC, up, sel, fn, rows);
+      case 4: return pick_gemv_g4_s256(NB, mode, up, sel, fn, rows);
+      case 8: return pick_gemv_g8_s256(NB, mode, up, sel, fn, rows);
+      case 16: return pick_gemv_g16_s256(NB, mode, up, sel, fn, rows);
+      case 32: return pick_gemv_g32_s256(NB, mode, up, sel, fn, rows);
+      case 64: return pick_gemv_g64_s256(NB, mode, up, sel, fn, rows);
     }
     return false;
   }
   switch (G) {
-    case 4: return pick_gemv_g4(NB, RC, up, sel, fn, rows);
-    case 8: return pick_gemv_g8(NB, RC, up, sel, fn, rows);
-    case 16: return pick_gemv_g16(NB, RC, up, sel, fn, rows);
-    case 32: return pick_gemv_g32(NB, RC, up, sel, fn, rows);
-    case 64: return pick_gemv_g64(NB, RC, up, sel, fn, rows);
+    case 4: return pick_gemv_g4(NB, mode, up, sel, fn, rows);
+    case 8: return pick_gemv_g8(NB, mode, up, sel, fn, rows);
+    case 16: return pick_gemv_g16(NB, mode, up, sel, fn, rows);
+    case 32: return pick_gemv_g32(NB, mode, up, sel, fn, rows);
+    case 64: return pick_gemv_g64(NB, mode, up, sel, fn, rows);
   }
   return false;
 }
@@ -138,8 +128,5 @@ constexpr int kFusedMaxRows = 4;
 // Gate/up blocks of a round with the selection folded in (each loops over its share of the units).
 constexpr int kFusedBlocks = 768;
 
-// Rows of one item processed per register pass in the down kernel: two for small verify rounds;
-// one from 5 rows on, where the lighter one-row form (more blocks resident) wins.
-inline int rows_per_pass(int T) { return (T >= 2 && T <= 4) ? 2 : 1; }
 
 }  // namespace moe

@@ -105,8 +105,10 @@ static moe_status hip_fail(moe_round* h, hipError_t e) {
     if (_e != hipSuccess) return hip_fail((h), _e);   \
   } while (0)
 
+// Rows of SwiGLU digits the down kernel stages in LDS at a time (per row: I/32 blocks of kXqWords
+// digit words and a (step, sum) pair).
 static int xstage_rows(int K) {
-  const int r = kXStageBytes / (static_cast<int>(sizeof(float)) * K);
+  const int r = kXStageBytes / (static_cast<int>(sizeof(uint32_t)) * (K / 32) * (kXqWords + 2));
   return r < 1 ? 1 : (r > kXStageMax ? kXStageMax : r);
 }
 
@@ -164,7 +166,6 @@ static Args base_args(const moe_round* h, int T, int k) {
 static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   const int E = h->cfg.n_experts, H = h->cfg.hidden, I = h->cfg.inter;
   const int umax = items_bound(T * k, E, rows_per_item(h, T));
-  const int RC = rows_per_pass(T);
   const bool wide = T >= kWideRows;
   const bool fused = T <= h->fused_max_rows;
   KernelFn lg = pick_logits(H, T), sel = pick_select(E), gu = nullptr, dn = nullptr;
@@ -172,7 +173,7 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
   const int fmt = h->cfg.weight_format;
   if (!lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, fused ? fused_select_keys(E) : 0, fmt, &gu, &rows_gu) ||
-      !pick_gemv(h->Gi, h->NBi, RC, false, h->cfg.exact, fmt, &dn, &rows_dn))
+      !pick_gemv(h->Gi, h->NBi, 0, false, h->cfg.exact, fmt, &dn, &rows_dn))
     return false;
   const int tc = logits_rows(T);
   const dim3 grid_lg((E + kRouteExpertsPerBlock - 1) / kRouteExpertsPerBlock, (T + tc - 1) / tc);
@@ -182,7 +183,7 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   int gu_words = gateup_stage_words(H);
   if (h->Gh == 64 && h->NBh == 1) gu_words += kMfmaExtraWords;  // matrix-core tile: (s, m) tables, partial sums
   const int shm_gu = wide ? static_cast<int>(sizeof(uint32_t)) * gu_words : 0;
-  const int shm_dn = T > 1 ? static_cast<int>(sizeof(float)) * xstage_rows(I) * I : 0;
+  const int shm_dn = static_cast<int>(sizeof(uint32_t)) * xstage_rows(I) * (I / 32) * (kXqWords + 2);
   out->clear();
   for (int l = 0; l < h->cfg.n_layers; ++l) {
     out->push_back({lg, grid_lg, kThreads, 0, l, 0});
