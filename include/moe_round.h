@@ -156,7 +156,9 @@ MOE_ROUND_API moe_status moe_round_init(const moe_round_config* cfg, const moe_l
 /*
  * Run one round, asynchronously on the handle's stream.
  *   hidden      device fp32 [T][H] input rows (read only; must not overlap `out`)
- *   T, k        1 <= T <= max_rows, 1 <= k <= top_k_max
+ *   T, k        0 <= T <= max_rows, 1 <= k <= top_k_max; T = 0 is an empty round: nothing is
+ *               enqueued, hidden/out/expert_ids/route_w may be NULL, MOE_OK is returned and the
+ *               introspection calls report MOE_ERR_STATE until the next round with rows
  *   layers      host array [L] of new weight pointers, or NULL to keep the current ones
  *               (new pointers are ingress: written into the handle's fixed table, no recapture)
  *   out         device fp32 [T][H] result: MoE(x) (residual = 0) or x_L (residual = 1)
@@ -175,6 +177,8 @@ MOE_ROUND_API moe_status moe_round_run(moe_round* h, const float* hidden, int32_
  *   offs         [n_unique + 1] exclusive prefix sum of rows per expert (may be NULL)
  *   pairs        [T*k][2] (row t, rank j) grouped by expert, t ascending (may be NULL)
  * Buffers must hold at least min(T*k, E) (uniq), that + 1 (offs) and 2*T*k (pairs) entries.
+ * This and the two calls below return MOE_ERR_STATE when there is no last run to report: none
+ * since init, or the last one was an empty round (T = 0).
  */
 MOE_ROUND_API moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t* n_unique, int32_t* uniq,
                               int32_t* offs, int32_t* pairs);

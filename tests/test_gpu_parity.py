@@ -240,3 +240,52 @@ def test_wide_tile_choice(verify, mfma_min_rows):
         X = synth.make_activations(cfg, T, seed=7, round_idx=T, device=DEV)
         check_layer_round(g, [view], X, cfg.k, f"wide T={T} mfma {mfma_min_rows}")
     g.close()
+
+
+def test_empty_round_is_a_no_op(verify):
+    """T = 0: MOE_OK, nothing written, introspection reports no round; the next round is normal."""
+    import ctypes
+    from verify_router_gemv_amd.binding import MoeRoundError
+    cfg, layer, view = verify
+    g = GpuRound([layer], cfg, max_rows=8)
+    say("case empty round T=0")
+    X0 = torch.empty((0, cfg.H), device=DEV)
+    out0 = torch.empty((0, cfg.H), device=DEV)
+    g.h.run(X0, cfg.k, out0)
+    torch.cuda.synchronize()
+    st = g.h.lib.moe_round_run(g.h.h, None, 0, cfg.k, None, None, None, None)
+    assert st == 0
+    with pytest.raises(MoeRoundError):
+        g.h.last_unique()
+    X = synth.make_activations(cfg, 3, seed=30, round_idx=0, device=DEV)
+    check_layer_round(g, [view], X, cfg.k, "after an empty round")
+    g.close()
+
+
+def test_largest_supported_shape():
+    """H = 8192, I = 2048, E = 512, k = 16, T = 64 (16 GB of expert weights): ids and the worklist of
+    every row against the oracle's router, and the full output of sampled rows (rows are evaluated
+    independently, so the oracle computes those rows alone)."""
+    cfg = synth.ShapeConfig("max", H=8192, E=512, k=16, I=2048, T=(64,), zipf_s=1.0)
+    say("case largest shape: generating 16 GB of weights")
+    layer = synth.make_layer(cfg, seed=3, layer=0, device=DEV)
+    view = oracle_view(layer)
+    g = GpuRound([layer], cfg, max_rows=64, use_graph=False)
+    X = synth.make_activations(cfg, 64, seed=31, round_idx=0, device=DEV)
+    say("case largest shape: GPU round")
+    out, ids, rw, _ = g.run(X)
+    Xh = X.cpu().numpy()
+    rids = np.stack([oracle.select_topk(oracle.router_logits(view["router_w"], view["router_b"], Xh[t]), cfg.k)
+                     for t in range(64)])
+    assert np.array_equal(ids[0], rids)
+    uniq, offs, pairs = g.h.worklist(0)
+    eu, eo, ep = oracle.build_worklist(rids)
+    assert uniq == eu.tolist() and offs == eo.tolist() and pairs == [tuple(p) for p in ep.tolist()]
+    for t in (0, 37, 63):
+        say(f"case largest shape: oracle row {t}")
+        ref, _, rp, _ = oracle.moe_layer(view, Xh[t:t + 1], cfg.k)
+        np.testing.assert_allclose(rw[0, t], rp[0], rtol=2e-6, atol=1e-7)
+        assert_close(out[t:t + 1], ref, f"largest shape row {t}")
+    g.close()
+    del layer, view
+    torch.cuda.empty_cache()

@@ -416,6 +416,10 @@ extern "C" moe_status moe_round_run(moe_round* h, const float* hidden, int32_t T
                                     float* route_w) {
   moe_status st = prepare_run(h, hidden, T, k, layers, out, expert_ids, route_w);
   if (st != MOE_OK) return st;
+  if (T == 0) {  // empty round: nothing to enqueue; introspection has no round to report
+    h->last_T = 0;
+    return MOE_OK;
+  }
   if (h->profiling) {
     const int slot = h->prof_next;
     h->prof_next = (slot + 1) % h->prof_runs;

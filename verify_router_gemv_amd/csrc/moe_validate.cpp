@@ -66,9 +66,10 @@ moe_status validate_layers(const moe_round_config* c, const moe_layer_weights* l
 
 moe_status validate_run(const moe_round_config* c, const float* hidden, int32_t T, int32_t k,
                         const float* out, const int32_t* ids, const float* rw) {
-  if (!hidden || !out) return MOE_ERR_INVALID_ARG;
-  if (T < 1 || T > c->max_rows) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || T > c->max_rows) return MOE_ERR_INVALID_ARG;
   if (k < 1 || k > c->top_k_max) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;  // an empty round: no buffer is touched
+  if (!hidden || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(hidden) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
   if ((ids && (reinterpret_cast<uintptr_t>(ids) & 3u)) || (rw && (reinterpret_cast<uintptr_t>(rw) & 3u)))
     return MOE_ERR_INVALID_ARG;
