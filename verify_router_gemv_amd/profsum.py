@@ -50,17 +50,30 @@ def stats(stats_csv: str, out_path: str, command: str) -> None:
     rows = []
     for r in csv.DictReader(open(stats_csv)):
         n = r["Name"]
-        if "moe::" in n or "neg_kernel" in n:
-            short = n.split("(")[0].replace("void moe::", "") if "moe::" in n else "torch.neg copy (calibration)"
+        if "moe::" in n:  # the library's kernels (input generation and copies are left out)
+            short = n.split("(")[0].replace("void moe::", "")
             rows.append((short, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                          float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     rows.sort(key=lambda x: -x[1] * x[2])
+    sweep = [r for r in rows if r[0] in VERIFY_SWEEP_GATEUP]
     with open(out_path, "w") as fh:
         fh.write(f"# rocprofv3 kernel statistics\n# command: {command}\n")
-        fh.write(f"{'kernel':32s} {'calls':>7s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}\n")
+        fh.write(f"{'kernel':36s} {'calls':>7s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}\n")
         for s in rows:
-            fh.write(f"{s[0]:32s} {s[1]:7d} {s[2]:8.3f} {s[3]:8.3f} {s[4]:8.3f} {s[5]:6.2f}\n")
+            fh.write(f"{s[0]:36s} {s[1]:7d} {s[2]:8.3f} {s[3]:8.3f} {s[4]:8.3f} {s[5]:6.2f}\n")
+        if sweep:
+            calls = sum(r[1] for r in sweep)
+            mean = sum(r[1] * r[2] for r in sweep) / calls
+            fh.write(f"# gate/up of the verify sweep (the forms T = 1, 3, 8 launch: {', '.join(VERIFY_SWEEP_GATEUP)};\n"
+                     f"# exact-mode rounds launch the same ones): {calls} calls, call-weighted mean {mean:.3f} us\n")
     print(open(out_path).read())
+
+
+# The gate/up instantiations the verify sweep launches (H = 2048: 64 lanes x 1 block, 4 rows per
+# lane group; one-row form with the folded selection at T = 1, row pairs with it at T = 3, row pairs
+# reading the selection kernel's records at T = 8; per-32 weight format).
+VERIFY_SWEEP_GATEUP = ("gateup_kernel<64, 1, 4, 0, 4, 0>", "gateup_kernel<64, 1, 4, 1, 4, 0>",
+                       "gateup_kernel<64, 1, 4, 1, 0, 0>")
 
 
 def _per_dispatch(d: str, counter: str):
