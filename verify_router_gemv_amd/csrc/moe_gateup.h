@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
   if constexpr (SEL > 0) {
     __shared__ SelectSharedT<kFusedPairs, kWaves> ssel;
     // The last block publishes: it is the one most likely to have no (item, tile) unit of its own.
-    select_block<SEL, kThreads>(a, layer, ssel, blockIdx.x == gridDim.x - 1);
+    select_block<SEL, kThreads, MODE == kGuOneRow>(a, layer, ssel, blockIdx.x == gridDim.x - 1);
     const int units = ssel.ni * tiles;
     for (int w = blockIdx.x; w < units; w += gridDim.x) {
       const int u = w / tiles;

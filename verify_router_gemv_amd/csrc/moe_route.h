@@ -155,94 +155,126 @@ __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
 // expert and at most a.rg of its rows). Results stay in `s`; with `publish` the block also writes
 // the per-item records, the unique list, pair table and pair weights, and the caller's ids and
 // routing weights. Deterministic: every block computing it gets the same result.
-template <int NPL, int NT, typename SS>
+template <int NPL, int NT, bool ONE_ROW = false, typename SS>
 __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bool publish) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k, npairs = T * k;
 
-  for (int e = tid; e < E; e += NT) s.mask[e] = 0ull;
-  for (int t = wave; t < T; t += NW) select_row<NPL>(a, s, t);
-  __syncthreads();
+  int nu, ni;
+  if constexpr (ONE_ROW) {
+    // Rounds of one row (callers that only run at T == 1): the union is its k ids, one row each,
+    // so one wave ranks them (ascending expert id) and writes the worklist directly.
+    if (wave == 0) {
+      select_row<NPL>(a, s, 0);
+      const int j = min(lane, k - 1);
+      const int id = s.sel[j];
+      int u = 0;
+#pragma unroll
+      for (int m = 0; m < MOE_ROUND_MAX_TOPK; ++m) {
+        const int v = s.sel[min(m, k - 1)];
+        u += (m < k && v < id) ? 1 : 0;
+      }
+      if (lane < k) {
+        s.uniq[u] = id;
+        s.offs[u] = u;
+        s.ioffs[u] = u;
+        s.item_u[u] = u;
+        s.pairs[u] = j << 8;  // row 0, rank j
+      }
+      if (lane == 0) {
+        s.nu = min(k, a.Ucap);
+        s.ni = min(k, a.Icap);
+        s.offs[k] = k;
+      }
+    }
+    __syncthreads();
+    nu = s.nu;
+    ni = s.ni;
+  } else {
+    for (int e = tid; e < E; e += NT) s.mask[e] = 0ull;
+    for (int t = wave; t < T; t += NW) select_row<NPL>(a, s, t);
+    __syncthreads();
 
-  for (int idx = tid; idx < npairs; idx += NT) atomicOr(&s.mask[s.sel[idx]], 1ull << (idx / k));
-  __syncthreads();
+    for (int idx = tid; idx < npairs; idx += NT) atomicOr(&s.mask[s.sel[idx]], 1ull << (idx / k));
+    __syncthreads();
 
-  // The union and its prefix sums, with ballots instead of a shuffle scan. Chunk ch of 64
-  // consecutive experts (ch = q * NW + wave) gives each expert lane its rank among the chunk's
-  // chosen experts, and the sums below it of the row counts and of the work-item counts (an
-  // expert's rows split into items of at most a.rg), bit plane by bit plane: mbcnt of the ballot of
-  // each bit. Chunk totals meet once in LDS for the exclusive prefix over chunks.
-  constexpr int NCH = MOE_ROUND_MAX_EXPERTS / 64;
-  constexpr int CPW = (NCH + NW - 1) / NW;  // chunks per wave
-  const int rg = a.rg;
-  const int cbits = 32 - __clz(T);                  // bits of a row count (at most T)
-  const int gbits = 32 - __clz((T + rg - 1) / rg);  // bits of an item count
-  int cnt[CPW], ngs[CPW], uin[CPW], cin[CPW], gin[CPW];
+    // The union and its prefix sums, with ballots instead of a shuffle scan. Chunk ch of 64
+    // consecutive experts (ch = q * NW + wave) gives each expert lane its rank among the chunk's
+    // chosen experts, and the sums below it of the row counts and of the work-item counts (an
+    // expert's rows split into items of at most a.rg), bit plane by bit plane: mbcnt of the ballot of
+    // each bit. Chunk totals meet once in LDS for the exclusive prefix over chunks.
+    constexpr int NCH = MOE_ROUND_MAX_EXPERTS / 64;
+    constexpr int CPW = (NCH + NW - 1) / NW;  // chunks per wave
+    const int rg = a.rg;
+    const int cbits = 32 - __clz(T);                  // bits of a row count (at most T)
+    const int gbits = 32 - __clz((T + rg - 1) / rg);  // bits of an item count
+    int cnt[CPW], ngs[CPW], uin[CPW], cin[CPW], gin[CPW];
 #pragma unroll
-  for (int q = 0; q < CPW; ++q) {
-    const int ch = q * NW + wave, e = ch * 64 + lane;
-    const int c = (ch < NCH && e < E) ? __popcll(s.mask[min(e, MOE_ROUND_MAX_EXPERTS - 1)]) : 0;
-    cnt[q] = c;
-    ngs[q] = (c + rg - 1) / rg;
-    const uint64_t chosen = __ballot(c > 0);
-    uin[q] = mbcnt64(chosen);
-    uint64_t tot = static_cast<uint64_t>(__popcll(chosen));
-    int ci = 0, gi = 0;
-    for (int b = 0; b < cbits; ++b) {
-      const uint64_t mb = __ballot((c >> b) & 1);
-      ci += mbcnt64(mb) << b;
-      tot += static_cast<uint64_t>(__popcll(mb)) << (16 + b);
+    for (int q = 0; q < CPW; ++q) {
+      const int ch = q * NW + wave, e = ch * 64 + lane;
+      const int c = (ch < NCH && e < E) ? __popcll(s.mask[min(e, MOE_ROUND_MAX_EXPERTS - 1)]) : 0;
+      cnt[q] = c;
+      ngs[q] = (c + rg - 1) / rg;
+      const uint64_t chosen = __ballot(c > 0);
+      uin[q] = mbcnt64(chosen);
+      uint64_t tot = static_cast<uint64_t>(__popcll(chosen));
+      int ci = 0, gi = 0;
+      for (int b = 0; b < cbits; ++b) {
+        const uint64_t mb = __ballot((c >> b) & 1);
+        ci += mbcnt64(mb) << b;
+        tot += static_cast<uint64_t>(__popcll(mb)) << (16 + b);
+      }
+      for (int b = 0; b < gbits; ++b) {
+        const uint64_t mb = __ballot((ngs[q] >> b) & 1);
+        gi += mbcnt64(mb) << b;
+        tot += static_cast<uint64_t>(__popcll(mb)) << (32 + b);
+      }
+      cin[q] = ci;
+      gin[q] = gi;
+      if (lane == 0 && ch < NCH) s.ctot[ch] = tot;  // chosen | rows << 16 | items << 32
     }
-    for (int b = 0; b < gbits; ++b) {
-      const uint64_t mb = __ballot((ngs[q] >> b) & 1);
-      gi += mbcnt64(mb) << b;
-      tot += static_cast<uint64_t>(__popcll(mb)) << (32 + b);
+    __syncthreads();
+    uint64_t all = 0, pre[CPW];
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) pre[q] = 0;
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2) {
+      const uint64_t v = s.ctot[c2];
+      all += v;
+#pragma unroll
+      for (int q = 0; q < CPW; ++q)
+        if (c2 < q * NW + wave) pre[q] += v;
     }
-    cin[q] = ci;
-    gin[q] = gi;
-    if (lane == 0 && ch < NCH) s.ctot[ch] = tot;  // chosen | rows << 16 | items << 32
-  }
-  __syncthreads();
-  uint64_t all = 0, pre[CPW];
+    nu = min(static_cast<int>(all & 0xFFFF), a.Ucap);
+    ni = min(static_cast<int>((all >> 32) & 0xFFFF), a.Icap);
 #pragma unroll
-  for (int q = 0; q < CPW; ++q) pre[q] = 0;
-#pragma unroll
-  for (int c2 = 0; c2 < NCH; ++c2) {
-    const uint64_t v = s.ctot[c2];
-    all += v;
-#pragma unroll
-    for (int q = 0; q < CPW; ++q)
-      if (c2 < q * NW + wave) pre[q] += v;
-  }
-  const int nu = min(static_cast<int>(all & 0xFFFF), a.Ucap);
-  const int ni = min(static_cast<int>((all >> 32) & 0xFFFF), a.Icap);
-#pragma unroll
-  for (int q = 0; q < CPW; ++q) {
-    const int e = (q * NW + wave) * 64 + lane;
-    if (cnt[q] > 0) {
-      const int u = static_cast<int>(pre[q] & 0xFFFF) + uin[q];
-      const int io = static_cast<int>((pre[q] >> 32) & 0xFFFF) + gin[q];
-      s.uidx[e] = u;
-      s.uniq[u] = e;
-      s.offs[u] = static_cast<int>((pre[q] >> 16) & 0xFFFF) + cin[q];
-      s.ioffs[u] = io;
-      for (int g2 = 0; g2 < ngs[q]; ++g2) s.item_u[io + g2] = u;
+    for (int q = 0; q < CPW; ++q) {
+      const int e = (q * NW + wave) * 64 + lane;
+      if (cnt[q] > 0) {
+        const int u = static_cast<int>(pre[q] & 0xFFFF) + uin[q];
+        const int io = static_cast<int>((pre[q] >> 32) & 0xFFFF) + gin[q];
+        s.uidx[e] = u;
+        s.uniq[u] = e;
+        s.offs[u] = static_cast<int>((pre[q] >> 16) & 0xFFFF) + cin[q];
+        s.ioffs[u] = io;
+        for (int g2 = 0; g2 < ngs[q]; ++g2) s.item_u[io + g2] = u;
+      }
     }
+    if (tid == 0) {
+      s.nu = nu;
+      s.ni = ni;
+      s.offs[nu] = npairs;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < npairs; idx += NT) {
+      const int t = idx / k, j = idx - t * k;
+      const int e = s.sel[idx];
+      const int pos = s.offs[s.uidx[e]] + __popcll(s.mask[e] & ((1ull << t) - 1ull));
+      s.pairs[pos] = t | (j << 8);
+    }
+    __syncthreads();
   }
-  if (tid == 0) {
-    s.nu = nu;
-    s.ni = ni;
-    s.offs[nu] = npairs;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < npairs; idx += NT) {
-    const int t = idx / k, j = idx - t * k;
-    const int e = s.sel[idx];
-    const int pos = s.offs[s.uidx[e]] + __popcll(s.mask[e] & ((1ull << t) - 1ull));
-    s.pairs[pos] = t | (j << 8);
-  }
-  __syncthreads();
   if (!publish) return;
 
   // Publish: per-item records, the unique list and pair table, the caller's ids / routing weights.
