@@ -81,7 +81,7 @@ struct Args {
   int32_t Icap;       // record slots per layer (work items <= pairs)
   int32_t rg;         // rows per work item at most (this launch)
   int32_t xstage_h;  // gate/up: rows of input digits staged in LDS at a time (T > 1)
-  int32_t xstage_i;  // down: SwiGLU rows staged in LDS at a time (T > 1)
+  int32_t xstage_i;  // down: SwiGLU rows staged in LDS (as digits) at a time
   int32_t mfma_rows;  // gate/up: experts with at least this many rows use the matrix-core tile (0: never)
   int32_t exact;      // fixed-order combine (the logits kernel does not seed the output)
 };
