@@ -42,7 +42,7 @@ def test_exact_is_reproducible(verify):
     g.close()
 
 
-@pytest.mark.parametrize("T", [3, 8, 13, 24])
+@pytest.mark.parametrize("T", [3, 8, 13, 24, 37])
 def test_exact_row_outputs_do_not_depend_on_the_round(verify, T):
     """Each row of a T-row round equals, bitwise, the same row evaluated alone, and reversing the
     rows reverses the outputs bitwise: covers the folded selection (T <= 4), the selection kernel

@@ -3,6 +3,8 @@
 Expert ids and the worklist must match bit-exactly; routing weights to fp32 rounding; the round's
 output within relative L2 1e-4 and max-abs 1e-3 * max|y|.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -211,6 +213,39 @@ def test_many_rows_share_experts(verify):
         rel, mabs, nu = check_layer_round(g, [view], X, cfg.k, f"shared T={T}")
         _, offs, _ = g.h.worklist(0)
         say(f"  n_unique={nu[0]} max rows per expert={int(np.diff(offs).max())} rel-L2={rel:.2e}")
+    g.close()
+
+
+@pytest.mark.parametrize("k", [7, 8])
+def test_tied_logits_go_to_the_lower_id(verify, k):
+    """Router rows duplicated in pairs, so experts 2m and 2m+1 get bitwise equal logits. Every
+    selection path (the one-row worklist, the selection folded into gate/up, the selection kernel,
+    ragged T) orders a tied pair lower id first, and a pair cut at rank k keeps the lower id: the
+    ids match the oracle's stable order, and the rule is also checked on the ids directly."""
+    cfg, layer, _ = verify
+    rw = layer.router_w.clone()
+    rw[1::2] = rw[0::2]
+    rb = None
+    if layer.router_b is not None:
+        rb = layer.router_b.clone()
+        rb[1::2] = rb[0::2]
+    tied = dataclasses.replace(layer, router_w=rw, router_b=rb)
+    view = oracle_view(tied)
+    g = GpuRound([tied], cfg, max_rows=64)
+    for T in (1, 3, 8, 24, 37):
+        say(f"case tied logits k={k} T={T}")
+        X = synth.make_activations(cfg, T, seed=8, round_idx=T, device=DEV)
+        z = oracle.router_logits(view["router_w"], view["router_b"], X[0].cpu().numpy())
+        assert np.array_equal(z[0::2], z[1::2])  # the oracle sees the ties too
+        check_layer_round(g, [view], X, k, f"tied k={k} T={T}")
+        _, ids, _, _ = g.run(X, k)
+        for t in range(T):
+            row = ids[0, t].tolist()
+            for j, e in enumerate(row):
+                if e % 2:
+                    assert j > 0 and row[j - 1] == e - 1, f"row {t}: {row}"
+                elif e + 1 not in row:
+                    assert j == k - 1, f"row {t}: {row}"
     g.close()
 
 
