@@ -3,7 +3,9 @@
  *
  * One call evaluates the mixture-of-experts feed-forward of one decode or
  * speculative-verify round over T token rows (1 <= T <= 64) and L stacked
- * MoE layers.  Per layer, on the GPU:
+ * MoE layers, or of a prefill round of more rows (see max_rows: the infero
+ * README, "Beyond plain text decode", routes prefill through a counting sort
+ * and a GEMM per expert).  Per layer, on the GPU:
  *   router GEMV (fp32 weights and activations, fp64 accumulation) -> top-k
  *   per row -> softmax over the k selected logits -> union of the rows'
  *   experts as a deterministic worklist -> fused dequant-GEMV of the unique
@@ -81,7 +83,8 @@ extern "C" {
  * Block set: a reduction length K (H for gate/up, I for down) is supported when K/32 = G * NB
  * with G the largest power of two <= 64 dividing K/32, G >= 4 and NB <= 4 (e.g. K = 128, 256,
  * 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192).  G lanes share one weight row. */
-#define MOE_ROUND_MAX_ROWS 64      /* T_max */
+#define MOE_ROUND_MAX_ROWS 64      /* T_max of decode/verify rounds                     */
+#define MOE_ROUND_MAX_PREFILL_ROWS 16384 /* T_max with the prefill path (see max_rows) */
 #define MOE_ROUND_MAX_EXPERTS 512  /* E     */
 #define MOE_ROUND_MAX_TOPK 16      /* k     */
 
@@ -100,7 +103,19 @@ typedef struct moe_round_config {
   int32_t n_experts;   /* E: 1..512                                               */
   int32_t top_k_max;   /* largest k a run may ask for: 1..min(E, 16)              */
   int32_t n_layers;    /* L >= 1                                                  */
-  int32_t max_rows;    /* T_max: 1..64                                            */
+  int32_t max_rows;    /* T_max: 1..MOE_ROUND_MAX_PREFILL_ROWS. Rounds of up to 64 rows
+                          are decode/verify rounds; rounds of more rows take the prefill
+                          path: per layer, a counting sort of the (row, rank) pairs into
+                          work items of up to 64 pairs of one expert, then gate/up and
+                          down as int8 matrix-core GEMMs over each item (activations as
+                          22-bit integers in three int8 planes, block scales folded in
+                          fp32), and a combine in rank order (so a row's output never
+                          depends on the other rows). Prefill rounds launch eagerly
+                          (use_graph applies to rounds of up to 64 rows), ignore the
+                          launch-shape fields and `exact` (their combine is always the
+                          fixed-order one), and need MOE_WEIGHT_Q4B32 (init returns
+                          MOE_ERR_UNSUPPORTED otherwise). Their scratch grows with
+                          max_rows * top_k_max * (4 H + 16 I) bytes.                  */
   int32_t residual;    /* 0: out = MoE(x), needs L == 1; 1: x_{l+1} = x_l + MoE_l */
   int32_t use_graph;   /* 1: replay one captured hipGraph per (T, k); 0: eager    */
   /* Launch-shape choices (0 = the default for each; none changes results beyond fp32 rounding

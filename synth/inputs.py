@@ -37,6 +37,7 @@ Workload shapes and distributions (all seeded):
   verify  H=2048 E=256 k=8  I=512 T in {1,2,3,4,5,8}, rows = base + 0.5*noise
   deep    H=2048 E=512 k=10 I=512 T=3, 48 layers, Zipf(s=1.0), residual
   wide    H=2048 E=256 k=8  I=512 T in {16,32,64}, independent rows
+  prefill H=2048 E=256 k=8  I=512 T in {512,4096}, independent rows (a prompt)
 Router weights ~ N(0, 0.02) fp32; expert weights ~ N(0, 0.02) then
 quantised; activations ~ N(0, 1).  The pages measure text benchmarks on
 trained models; these synthetic inputs stand in for them with the shapes of
@@ -90,6 +91,7 @@ CONFIGS = {
     "deep": ShapeConfig("deep", H=2048, E=512, k=10, I=512, L=48, T=(3,), zipf_s=1.0,
                         residual=True),
     "wide": ShapeConfig("wide", H=2048, E=256, k=8, I=512, T=(16, 32, 64)),
+    "prefill": ShapeConfig("prefill", H=2048, E=256, k=8, I=512, T=(512, 4096)),
 }
 
 

@@ -67,6 +67,10 @@ def cfg(**kw):
     dict(H=2048, I=512, E=256, top_k_max=8, max_rows=8, raw_weight_format=1),
     dict(H=2048, I=768, E=128, top_k_max=8, max_rows=1, raw_weight_format=1),
     dict(H=768, I=256, E=40, top_k_max=5, max_rows=16, raw_weight_format=1),
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=65),        # prefill rounds from 65 rows
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=4096),
+    dict(H=768, I=384, E=40, top_k_max=5, max_rows=1000),
+    dict(H=2048, I=512, E=512, top_k_max=10, n_layers=4, max_rows=16384, residual=True),
 ])
 def test_supported_configs_validate(lib, kw):
     from verify_router_gemv_amd import binding
@@ -94,7 +98,8 @@ def test_supported_configs_validate(lib, kw):
     (dict(raw_weight_format=-1), -1),
     (dict(I=384, raw_weight_format=1), -2),   # super-blocks need I a multiple of 256
     (dict(H=256, I=128, E=8, top_k_max=2, raw_weight_format=1), -2),
-    (dict(max_rows=65), -2),
+    (dict(max_rows=16385), -2),
+    (dict(max_rows=65, raw_weight_format=1), -2),  # prefill reads Q4B32 weights only
     (dict(E=513, top_k_max=8), -2),
     (dict(top_k_max=17, E=256), -2),
     (dict(H=2080), -2),          # not a multiple of 256
@@ -119,7 +124,7 @@ def test_null_and_bad_arguments_are_refused_before_any_gpu_call(lib):
     w[0] = binding.LayerWeights(*([0x1000] * 8))
     w[0].gate_q = 0x1008                                                            # misaligned codes
     assert lib.moe_round_init(ctypes.byref(c), w, None, ctypes.byref(h)) == -1
-    bad = cfg(max_rows=65)
+    bad = cfg(max_rows=16385)
     assert lib.moe_round_init(ctypes.byref(bad), w, None, ctypes.byref(h)) == -2
     assert lib.moe_round_run(None, None, 1, 1, None, None, None, None) == -1
     assert lib.moe_round_worklist(None, 0, None, None, None, None) == -1

@@ -1,0 +1,143 @@
+"""Prefill rounds (more than 64 rows) through the C ABI vs the fp64 oracle (needs an MI355X).
+
+The path: counting sort of the (row, rank) pairs into 64-pair work items, gate/up and down as int8
+matrix-core GEMMs, combine in rank order. Ids and the worklist must match bit-exactly, routing
+weights to fp32 rounding, outputs within relative L2 1e-4 and max-abs 1e-3 * max|y|. At 4096 rows
+the outputs are checked on sampled rows (the oracle evaluates each row on its own, so a row's
+expected output does not depend on the rest of the round).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from moe_helpers import GpuRound, assert_close, check_layer_round, oracle_view, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def prefill_layer():
+    cfg = synth.config("prefill")
+    layer = synth.make_layer(cfg, seed=0, layer=0, device=DEV)
+    return cfg, layer, oracle_view(layer)
+
+
+def test_prefill_ragged_shape_all_rows():
+    """H=768, I=384, E=40, k=5: T just above the decode limit, ragged T, and T = max_rows."""
+    cfg = synth.ShapeConfig("ragged", H=768, E=40, k=5, I=384, T=(65, 100, 257), zipf_s=0.7)
+    layer = synth.make_layer(cfg, seed=3, layer=0, device=DEV)
+    view = oracle_view(layer)
+    g = GpuRound([layer], cfg, max_rows=257)
+    for T in cfg.T:
+        say(f"case prefill ragged T={T}")
+        X = synth.make_activations(cfg, T, seed=11, round_idx=T, device=DEV)
+        rel, mabs, nu = check_layer_round(g, [view], X, cfg.k, f"prefill ragged T={T}")
+        _, offs, _ = g.h.worklist(0)
+        say(f"  n_unique={nu[0]} max pairs per expert={int(np.diff(offs).max())} rel-L2={rel:.2e}")
+    g.close()
+
+
+@pytest.mark.parametrize("k", [1, 8])
+def test_prefill_verify_shape_all_rows(prefill_layer, k):
+    """The prefill workload's layer at T = 65 and 200, every row against the oracle; k = 1 makes
+    routing weights exactly 1."""
+    cfg, layer, view = prefill_layer
+    g = GpuRound([layer], cfg, max_rows=256)
+    for T in (65, 200):
+        say(f"case prefill verify-shape T={T} k={k}")
+        X = synth.make_activations(cfg, T, seed=12, round_idx=T, device=DEV)
+        rel, mabs, nu = check_layer_round(g, [view], X, k, f"prefill T={T} k={k}")
+        say(f"  n_unique={nu[0]} rel-L2={rel:.2e}")
+    g.close()
+
+
+def test_prefill_hot_experts_split_into_items():
+    """Zipf-biased routing (E=128, k=8, I=768) at T=600: popular experts get several hundred rows,
+    so their pairs span several 64-pair work items."""
+    cfg = synth.config("decode").replace(T=(600,))
+    layer = synth.make_layer(cfg, seed=0, layer=0, device=DEV)
+    view = oracle_view(layer)
+    g = GpuRound([layer], cfg, max_rows=600)
+    say("case prefill zipf T=600")
+    X = synth.make_activations(cfg, 600, seed=13, round_idx=600, device=DEV)
+    rel, mabs, nu = check_layer_round(g, [view], X, cfg.k, "prefill zipf T=600")
+    _, offs, _ = g.h.worklist(0)
+    most = int(np.diff(offs).max())
+    say(f"  n_unique={nu[0]} max pairs per expert={most} rel-L2={rel:.2e}")
+    assert most > 2 * 64
+    g.close()
+
+
+def test_prefill_4096_rows_sampled(prefill_layer):
+    """T = 4096: ids, routing weights and the worklist of every row bit-exact / to fp32 rounding;
+    outputs of 48 sampled rows (first, last, and spread) within tolerance."""
+    cfg, layer, view = prefill_layer
+    T, k = 4096, cfg.k
+    g = GpuRound([layer], cfg, max_rows=T)
+    say(f"case prefill T={T}")
+    X = synth.make_activations(cfg, T, seed=14, round_idx=T, device=DEV)
+    out, ids, rw, _ = g.run(X, k)
+    Xh = X.cpu().numpy()
+    rids = np.zeros((T, k), dtype=np.int64)
+    rp = np.zeros((T, k))
+    for t in range(T):
+        z = oracle.router_logits(view["router_w"], view["router_b"], Xh[t])
+        rids[t] = oracle.select_topk(z, k)
+        rp[t] = oracle.routing_weights(z, rids[t])
+    assert np.array_equal(ids[0], rids)
+    np.testing.assert_allclose(rw[0], rp, rtol=2e-6, atol=1e-7)
+    uniq, offs, pairs = g.h.worklist(0)
+    eu, eo, ep = oracle.build_worklist(rids)
+    assert uniq == eu.tolist() and offs == eo.tolist()
+    assert np.array_equal(np.asarray(pairs), ep)
+    rng = np.random.default_rng(0)
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 46, replace=False)]))
+    ref, _, _, _ = oracle.moe_layer(view, Xh[sample], k)
+    rel, mabs = assert_close(out[sample], ref, f"prefill T={T} sampled rows")
+    say(f"  n_unique={len(uniq)} max pairs per expert={int(np.diff(offs).max())} rel-L2={rel:.2e}")
+    g.close()
+
+
+def test_prefill_rows_do_not_depend_on_the_round(prefill_layer):
+    """Every pair's products depend only on its own row and expert, and the combine adds the ranks
+    in order: rows 0..99 of a 300-row round equal a 100-row round of those rows bitwise, and so do
+    the reversed rows."""
+    cfg, layer, _ = prefill_layer
+    g = GpuRound([layer], cfg, max_rows=300)
+    say("case prefill row invariance")
+    X = synth.make_activations(cfg, 300, seed=15, round_idx=300, device=DEV)
+    full = g.run(X)[0]
+    part = g.run(X[:100].contiguous())[0]
+    assert np.array_equal(full[:100], part)
+    rev = g.run(X.flip(0).contiguous())[0]
+    assert np.array_equal(rev[::-1], full)
+    g.close()
+
+
+def test_prefill_residual_stack():
+    """Three layers with the residual between them (Zipf routing, E=64, k=4) at T=130, against the
+    oracle's free-running stack; ids of every layer bit-exact."""
+    cfg = synth.ShapeConfig("stack", H=1024, E=64, k=4, I=256, L=3, T=(130,), zipf_s=1.0, residual=True)
+    layers = [synth.make_layer(cfg, seed=0, layer=l, device=DEV) for l in range(cfg.L)]
+    views = [oracle_view(l) for l in layers]
+    g = GpuRound(layers, cfg, max_rows=130)
+    say("case prefill residual stack L=3 T=130")
+    X = synth.make_activations(cfg, 130, seed=16, round_idx=130, device=DEV)
+    rel, mabs, nu = check_layer_round(g, views, X, cfg.k, "prefill stack")
+    say(f"  n_unique per layer={nu} rel-L2={rel:.2e}")
+    g.close()
+
+
+def test_prefill_then_verify_rounds_on_one_handle(prefill_layer):
+    """One handle serves a prefill round, then verify rounds (graph replay), then prefill again."""
+    cfg, layer, view = prefill_layer
+    g = GpuRound([layer], cfg, max_rows=128)
+    for T in (128, 3, 8, 70):
+        say(f"case mixed handle T={T}")
+        X = synth.make_activations(cfg, T, seed=17, round_idx=T, device=DEV)
+        check_layer_round(g, [view], X, cfg.k, f"mixed T={T}")
+    g.close()

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_round.so")
 
 ABI_VERSION = 1
 MAX_ROWS = 64
+MAX_PREFILL_ROWS = 16384
 MAX_EXPERTS = 512
 MAX_TOPK = 16
 KERNELS_PER_LAYER = 5

@@ -5,7 +5,8 @@
 // or as one captured hipGraph per (T, k) whose kernels read the ingress pointers and the weight
 // table from fixed device buffers, so new per-request pointers never force a recapture
 // ("How AlphaInfer makes local decoding fast", section 2: per-request data is ingress written
-// into fixed buffers and the graph is never rebuilt).
+// into fixed buffers and the graph is never rebuilt). Rounds of more than MOE_ROUND_MAX_ROWS rows
+// (prefill) run the kernels of moe_prefill.h eagerly, eight per layer.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -15,6 +16,7 @@
 
 #include "moe_internal.h"
 #include "moe_kernels.h"
+#include "moe_prefill.h"
 
 using namespace moe;
 
@@ -34,6 +36,7 @@ struct Launch {
 };
 
 constexpr int kKernelsPerLayer = 5;  // kinds of kernel per layer: logits, select, gate/up, down, combine
+constexpr int kLaunchesPerLayer = 8;  // most launches of one layer (a prefill round)
 
 struct GraphEntry {
   hipGraph_t graph = nullptr;
@@ -92,6 +95,28 @@ struct moe_round {
   int mfma_rows = 3;                   // gate/up (wide rounds): matrix-core tile from this many rows per item
   int rows_per_item = 0;               // 0: by round width
   int fused_max_rows = kFusedMaxRows;  // selection folded into gate/up up to this many rows
+  // prefill scratch (max_rows > MOE_ROUND_MAX_ROWS): rows Tp, pair slots pfP, work items pfI
+  int Tp = 0, pfP = 0, pfI = 0;
+  float* pf_xbuf[2] = {nullptr, nullptr};
+  uint32_t* pf_xq = nullptr;
+  float* pf_xstep = nullptr;
+  float* pf_xsum = nullptr;
+  unsigned long long* pf_mask = nullptr;
+  int32_t* pf_wpre = nullptr;
+  int32_t* pf_sel = nullptr;
+  float* pf_selp = nullptr;
+  int32_t* pf_uniq = nullptr;
+  int32_t* pf_offs = nullptr;
+  int32_t* pf_pairs = nullptr;
+  float* pf_pair_w = nullptr;
+  int32_t* pf_slot_of = nullptr;
+  int4* pf_items = nullptr;
+  int32_t* pf_n_items = nullptr;
+  float* pf_hbuf = nullptr;
+  uint32_t* pf_hq = nullptr;
+  float* pf_hstep = nullptr;
+  float* pf_hsum = nullptr;
+  float* pf_ybuf = nullptr;
 };
 
 static moe_status hip_fail(moe_round* h, hipError_t e) {
@@ -259,6 +284,107 @@ static moe_status launch_eager(moe_round* h, int T, int k, hipEvent_t* evs, int*
   return MOE_OK;
 }
 
+// Work items of a prefill round bound: sum over experts of ceil(rows / 64).
+static int pf_items_bound(int pairs, int E) {
+  const int b = E + (pairs + pf::kTile - 1) / pf::kTile;
+  return b < pairs ? b : pairs;
+}
+
+typedef void (*PfKernelFn)(pf::PfArgs, int);
+
+static PfKernelFn pf_pick_topk(int E) {
+  if (E <= 64) return pf::pf_topk_kernel<1>;
+  if (E <= 128) return pf::pf_topk_kernel<2>;
+  if (E <= 256) return pf::pf_topk_kernel<4>;
+  return pf::pf_topk_kernel<8>;
+}
+
+// A prefill round (T > MOE_ROUND_MAX_ROWS), eagerly: per layer the digits of the layer input,
+// router logits, top-k, the counting sort, gate/up, the SwiGLU digits, down and the combine.
+// evs: with profiling, a start/stop pair per launch; kinds: their accumulator (layer, kind).
+static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, int* kinds, int* n_launched) {
+  const int E = h->cfg.n_experts, H = h->cfg.hidden, I = h->cfg.inter, L = h->cfg.n_layers;
+  pf::PfArgs a{};
+  a.in = h->h_ing;
+  a.xbuf0 = h->pf_xbuf[0];
+  a.xbuf1 = h->pf_xbuf[1];
+  a.logits = h->logits;
+  a.xq = h->pf_xq;
+  a.xstep = h->pf_xstep;
+  a.xsum = h->pf_xsum;
+  a.mask = h->pf_mask;
+  a.wpre = h->pf_wpre;
+  a.sel = h->pf_sel;
+  a.selp = h->pf_selp;
+  a.n_unique = h->n_unique;
+  a.uniq = h->pf_uniq;
+  a.offs = h->pf_offs;
+  a.pairs = h->pf_pairs;
+  a.pair_w = h->pf_pair_w;
+  a.slot_of = h->pf_slot_of;
+  a.items = h->pf_items;
+  a.n_items = h->pf_n_items;
+  a.hbuf = h->pf_hbuf;
+  a.hq = h->pf_hq;
+  a.hstep = h->pf_hstep;
+  a.hsum = h->pf_hsum;
+  a.ybuf = h->pf_ybuf;
+  a.H = H;
+  a.I = I;
+  a.E = E;
+  a.L = L;
+  a.T = T;
+  a.k = k;
+  a.residual = h->cfg.residual;
+  a.Pcap = h->pfP;
+  a.Icap = h->pfI;
+  a.W = (T + 63) / 64;
+  const int np = T * k;
+  const int ib = pf_items_bound(np, E);
+  const int gu_units = ((ib * (I / pf::kTile) + 7) / 8) * 8;
+  const int dn_units = ((ib * (H / pf::kTile) + 7) / 8) * 8;
+  const PfKernelFn topk = pf_pick_topk(E);
+  int i = 0;
+  auto launch = [&](const void* fn, dim3 grid, int threads, int shmem, void** params, int layer, int kind) {
+    if (kinds) kinds[i] = layer * kKernelsPerLayer + kind;
+    hipError_t e = evs ? hipExtLaunchKernel(fn, grid, dim3(threads), params, shmem, h->stream, evs[2 * i],
+                                            evs[2 * i + 1], 0)
+                       : hipLaunchKernel(fn, grid, dim3(threads), params, shmem, h->stream);
+    ++i;
+    return e;
+  };
+  for (int l = 0; l < L; ++l) {
+    a.w = h->h_wtab[l];
+    int layer = l;
+    void* gp[] = {&a, &layer};
+    const float* xin = l == 0 ? h->h_ing.hidden : h->pf_xbuf[(l - 1) & 1];
+    int kH = H, nT = T, zw = E * a.W, kI = I, nP = np, zero0 = 0;
+    unsigned long long* no_mask = nullptr;
+    void* qx[] = {&xin, &kH, &nT, &a.xq, &a.xstep, &a.xsum, &a.mask, &zw};
+    void* qh[] = {&a.hbuf, &kI, &nP, &a.hq, &a.hstep, &a.hsum, &no_mask, &zero0};
+    hipError_t e;
+    if ((e = launch(reinterpret_cast<const void*>(pf::quant_rows_kernel), dim3((T + kWaves - 1) / kWaves), kThreads, 0,
+                    qx, l, 0)) != hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(pf::pf_logits_kernel), dim3((E + 15) / 16, (T + 63) / 64), kThreads,
+                    0, gp, l, 0)) != hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(topk), dim3((T + kWaves - 1) / kWaves), kThreads, 0, gp, l, 1)) !=
+            hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(pf::pf_scan_kernel), dim3(1), pf::kScanThreads, 0, gp, l, 1)) !=
+            hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(pf::pf_gateup_kernel), dim3(gu_units), kThreads, pf::kGemmLds, gp,
+                    l, 2)) != hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(pf::quant_rows_kernel), dim3((np + kWaves - 1) / kWaves), kThreads,
+                    0, qh, l, 3)) != hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(pf::pf_down_kernel), dim3(dn_units), kThreads, pf::kGemmLds, gp, l,
+                    3)) != hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(pf::pf_combine_kernel), dim3(T, (H + 4 * kThreads - 1) / (4 * kThreads)),
+                    kThreads, 0, gp, l, 4)) != hipSuccess)
+      return hip_fail(h, e);
+  }
+  if (n_launched) *n_launched = i;
+  return MOE_OK;
+}
+
 // Graph mode: upload changed ingress pointers and/or the weight table through a pinned slot.
 static moe_status sync_device_ingress(moe_round* h) {
   const size_t wbytes = sizeof(moe_layer_weights) * h->cfg.n_layers;
@@ -286,10 +412,10 @@ static moe_status sync_device_ingress(moe_round* h) {
 static moe_status harvest(moe_round* h, int slot) {
   const int nk = h->prof_nk[slot];
   if (nk == 0) return MOE_OK;
-  hipEvent_t* ev = h->prof_ev.data() + static_cast<size_t>(slot) * 2 * kKernelsPerLayer * h->cfg.n_layers;
+  hipEvent_t* ev = h->prof_ev.data() + static_cast<size_t>(slot) * 2 * kLaunchesPerLayer * h->cfg.n_layers;
   h->prof_nk[slot] = 0;
   MOE_HIP(h, hipEventSynchronize(ev[2 * nk - 1]));
-  const int* kind = h->prof_kind.data() + static_cast<size_t>(slot) * kKernelsPerLayer * h->cfg.n_layers;
+  const int* kind = h->prof_kind.data() + static_cast<size_t>(slot) * kLaunchesPerLayer * h->cfg.n_layers;
   for (int i = 0; i < nk; ++i) {
     float ms = 0.f;
     MOE_HIP(h, hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]));
@@ -320,7 +446,10 @@ static void free_handle(moe_round* h) {
     if (h->slot_ev[i]) (void)hipEventDestroy(h->slot_ev[i]);
   if (h->staging) (void)hipHostFree(h->staging);
   void* ptrs[] = {h->d_ing, h->d_wtab, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique, h->uniq, h->offs,
-                  h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->xq, h->xss};
+                  h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->xq, h->xss,
+                  h->pf_xbuf[0], h->pf_xbuf[1], h->pf_xq, h->pf_xstep, h->pf_xsum, h->pf_mask, h->pf_wpre,
+                  h->pf_sel, h->pf_selp, h->pf_uniq, h->pf_offs, h->pf_pairs, h->pf_pair_w, h->pf_slot_of,
+                  h->pf_items, h->pf_n_items, h->pf_hbuf, h->pf_hq, h->pf_hstep, h->pf_hsum, h->pf_ybuf};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete h;
@@ -340,7 +469,9 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   h->stream = static_cast<hipStream_t>(stream);
   split_blocks(cfg->hidden, &h->Gh, &h->NBh);
   split_blocks(cfg->inter, &h->Gi, &h->NBi);
-  const int T = cfg->max_rows, E = cfg->n_experts, K = cfg->top_k_max, L = cfg->n_layers;
+  // decode/verify scratch for rounds of up to MOE_ROUND_MAX_ROWS rows; prefill scratch beyond
+  const int T = cfg->max_rows < MOE_ROUND_MAX_ROWS ? cfg->max_rows : MOE_ROUND_MAX_ROWS;
+  const int E = cfg->n_experts, K = cfg->top_k_max, L = cfg->n_layers;
   const int H = cfg->hidden, I = cfg->inter;
   h->Pcap = T * K;
   h->Ucap = (T * K < E) ? T * K : E;
@@ -363,7 +494,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   MOE_ALLOC(h->d_wtab, sizeof(moe_layer_weights) * L);
   MOE_ALLOC(h->xbuf[0], sizeof(float) * T * H);
   MOE_ALLOC(h->xbuf[1], sizeof(float) * T * H);
-  MOE_ALLOC(h->logits, sizeof(double) * T * E);
+  MOE_ALLOC(h->logits, sizeof(double) * cfg->max_rows * E);
   MOE_ALLOC(h->n_unique, sizeof(int32_t) * L);
   MOE_ALLOC(h->uniq, sizeof(int32_t) * L * h->Ucap);
   MOE_ALLOC(h->offs, sizeof(int32_t) * L * (h->Ucap + 1));
@@ -375,6 +506,35 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   if (cfg->exact) MOE_ALLOC(h->ybuf, sizeof(float) * h->Pcap * H);
   MOE_ALLOC(h->xq, sizeof(uint32_t) * T * (H / 32) * kXqWords);
   MOE_ALLOC(h->xss, sizeof(float2) * T * (H / 32));
+  if (cfg->max_rows > MOE_ROUND_MAX_ROWS) {
+    const size_t Tp = cfg->max_rows, P = Tp * K, W = (Tp + 63) / 64;
+    h->Tp = static_cast<int>(Tp);
+    h->pfP = static_cast<int>(P);
+    h->pfI = pf_items_bound(static_cast<int>(P), E);
+    if (L > 1) {
+      MOE_ALLOC(h->pf_xbuf[0], sizeof(float) * Tp * H);
+      MOE_ALLOC(h->pf_xbuf[1], sizeof(float) * Tp * H);
+    }
+    MOE_ALLOC(h->pf_xq, sizeof(uint32_t) * Tp * (H / 32) * kXqWords);
+    MOE_ALLOC(h->pf_xstep, sizeof(float) * Tp);
+    MOE_ALLOC(h->pf_xsum, sizeof(float) * Tp * (H / 32));
+    MOE_ALLOC(h->pf_mask, sizeof(unsigned long long) * E * W);
+    MOE_ALLOC(h->pf_wpre, sizeof(int32_t) * E * W);
+    MOE_ALLOC(h->pf_sel, sizeof(int32_t) * P);
+    MOE_ALLOC(h->pf_selp, sizeof(float) * P);
+    MOE_ALLOC(h->pf_uniq, sizeof(int32_t) * L * E);
+    MOE_ALLOC(h->pf_offs, sizeof(int32_t) * L * (E + 1));
+    MOE_ALLOC(h->pf_pairs, sizeof(int32_t) * L * P);
+    MOE_ALLOC(h->pf_pair_w, sizeof(float) * P);
+    MOE_ALLOC(h->pf_slot_of, sizeof(int32_t) * P);
+    MOE_ALLOC(h->pf_items, sizeof(int4) * h->pfI);
+    MOE_ALLOC(h->pf_n_items, sizeof(int32_t));
+    MOE_ALLOC(h->pf_hbuf, sizeof(float) * P * I);
+    MOE_ALLOC(h->pf_hq, sizeof(uint32_t) * P * (I / 32) * kXqWords);
+    MOE_ALLOC(h->pf_hstep, sizeof(float) * P);
+    MOE_ALLOC(h->pf_hsum, sizeof(float) * P * (I / 32));
+    MOE_ALLOC(h->pf_ybuf, sizeof(float) * P * H);
+  }
 #undef MOE_ALLOC
   h->slot_bytes = 256 + ((sizeof(moe_layer_weights) * L + 255) / 256) * 256;
   if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->staging), h->slot_bytes * kStagingSlots, 0)) !=
@@ -425,12 +585,15 @@ extern "C" moe_status moe_round_run(moe_round* h, const float* hidden, int32_t T
     h->prof_next = (slot + 1) % h->prof_runs;
     st = harvest(h, slot);  // a slot is reused only after its previous run has been read
     if (st != MOE_OK) return st;
-    hipEvent_t* ev = h->prof_ev.data() + static_cast<size_t>(slot) * 2 * kKernelsPerLayer * h->cfg.n_layers;
-    int* kinds = h->prof_kind.data() + static_cast<size_t>(slot) * kKernelsPerLayer * h->cfg.n_layers;
+    hipEvent_t* ev = h->prof_ev.data() + static_cast<size_t>(slot) * 2 * kLaunchesPerLayer * h->cfg.n_layers;
+    int* kinds = h->prof_kind.data() + static_cast<size_t>(slot) * kLaunchesPerLayer * h->cfg.n_layers;
     int nl = 0;
-    st = launch_eager(h, T, k, ev, kinds, &nl);
+    st = T > MOE_ROUND_MAX_ROWS ? launch_prefill(h, T, k, ev, kinds, &nl) : launch_eager(h, T, k, ev, kinds, &nl);
     if (st != MOE_OK) return st;
     h->prof_nk[slot] = nl;
+  } else if (T > MOE_ROUND_MAX_ROWS) {
+    st = launch_prefill(h, T, k, nullptr, nullptr, nullptr);
+    if (st != MOE_OK) return st;
   } else if (h->cfg.use_graph) {
     st = sync_device_ingress(h);
     if (st != MOE_OK) return st;
@@ -456,11 +619,11 @@ extern "C" moe_status moe_round_profile(moe_round* h, int32_t enable) {
   if (!h || (enable != 0 && enable != 1)) return MOE_ERR_INVALID_ARG;
   if (enable == h->profiling) return MOE_OK;
   if (enable) {
-    const int per_run = 2 * kKernelsPerLayer * h->cfg.n_layers;
+    const int per_run = 2 * kLaunchesPerLayer * h->cfg.n_layers;
     const int runs = kProfileEvents / per_run > 2 ? kProfileEvents / per_run : 2;
     h->prof_ev.assign(static_cast<size_t>(runs) * per_run, nullptr);
     h->prof_nk.assign(runs, 0);
-    h->prof_kind.assign(static_cast<size_t>(runs) * kKernelsPerLayer * h->cfg.n_layers, 0);
+    h->prof_kind.assign(static_cast<size_t>(runs) * kLaunchesPerLayer * h->cfg.n_layers, 0);
     h->prof_runs = runs;
     h->prof_next = 0;
     for (auto& ev : h->prof_ev) {
@@ -511,21 +674,26 @@ extern "C" moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t* n
   int32_t nu = 0;
   MOE_HIP(h, hipMemcpy(&nu, h->n_unique + layer, sizeof(int32_t), hipMemcpyDeviceToHost));
   *n_unique = nu;
-  if (nu < 0 || nu > h->Ucap) return MOE_ERR_STATE;
+  // prefill rounds: their own lists (capacity E per layer), pairs packed as t | j << 16
+  const bool pf = h->last_T > MOE_ROUND_MAX_ROWS;
+  const int ucap = pf ? h->cfg.n_experts : h->Ucap;
+  const int32_t* d_uniq = pf ? h->pf_uniq : h->uniq;
+  const int32_t* d_offs = pf ? h->pf_offs : h->offs;
+  const int32_t* d_pairs = pf ? h->pf_pairs + static_cast<size_t>(layer) * h->pfP
+                              : h->pairs + static_cast<size_t>(layer) * h->Pcap;
+  if (nu < 0 || nu > ucap) return MOE_ERR_STATE;
   if (uniq && nu)
-    MOE_HIP(h, hipMemcpy(uniq, h->uniq + static_cast<size_t>(layer) * h->Ucap, sizeof(int32_t) * nu,
-                         hipMemcpyDeviceToHost));
+    MOE_HIP(h, hipMemcpy(uniq, d_uniq + static_cast<size_t>(layer) * ucap, sizeof(int32_t) * nu, hipMemcpyDeviceToHost));
   if (offs)
-    MOE_HIP(h, hipMemcpy(offs, h->offs + static_cast<size_t>(layer) * (h->Ucap + 1), sizeof(int32_t) * (nu + 1),
+    MOE_HIP(h, hipMemcpy(offs, d_offs + static_cast<size_t>(layer) * (ucap + 1), sizeof(int32_t) * (nu + 1),
                          hipMemcpyDeviceToHost));
   if (pairs) {
     const int np = h->last_T * h->last_k;
     std::vector<int32_t> packed(np);
-    MOE_HIP(h, hipMemcpy(packed.data(), h->pairs + static_cast<size_t>(layer) * h->Pcap, sizeof(int32_t) * np,
-                         hipMemcpyDeviceToHost));
+    MOE_HIP(h, hipMemcpy(packed.data(), d_pairs, sizeof(int32_t) * np, hipMemcpyDeviceToHost));
     for (int i = 0; i < np; ++i) {
-      pairs[2 * i] = packed[i] & 0xFF;
-      pairs[2 * i + 1] = (packed[i] >> 8) & 0xFF;
+      pairs[2 * i] = pf ? (packed[i] & 0xFFFF) : (packed[i] & 0xFF);
+      pairs[2 * i + 1] = pf ? (packed[i] >> 16) : ((packed[i] >> 8) & 0xFF);
     }
   }
   return MOE_OK;
@@ -536,7 +704,8 @@ extern "C" moe_status moe_round_swiglu_rows(moe_round* h, float* host_rows) {
   if (h->last_T == 0) return MOE_ERR_STATE;
   MOE_HIP(h, hipStreamSynchronize(h->stream));
   const size_t n = static_cast<size_t>(h->last_T) * h->last_k * h->cfg.inter;
-  MOE_HIP(h, hipMemcpy(host_rows, h->hbuf, sizeof(float) * n, hipMemcpyDeviceToHost));
+  const float* src = h->last_T > MOE_ROUND_MAX_ROWS ? h->pf_hbuf : h->hbuf;
+  MOE_HIP(h, hipMemcpy(host_rows, src, sizeof(float) * n, hipMemcpyDeviceToHost));
   return MOE_OK;
 }
 

@@ -98,11 +98,10 @@ using SelectShared = SelectSharedT<MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK, kSel
 // of the heads holding that high word (the low bits carry the id, so the winner is unique). The
 // lane owning the winner pops its head and lane j keeps the j-th id. The exact fp64 logits of the
 // k ids come from their owner lanes once, after the rounds, for the softmax over the k selected.
-template <int NPL, typename SS>
-__device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
+// Lane j < k ends with rank j's id and routing weight.
+template <int NPL>
+__device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& id_out, float& p_out) {
   const int lane = threadIdx.x & 63;
-  const int E = a.E, k = a.k;
-  const double* zrow = a.logits + static_cast<size_t>(t) * E;
   double z[NPL];
   uint64_t key[NPL];
 #pragma unroll
@@ -144,9 +143,22 @@ __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
   const double z0 = __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, myz), 0));
   const double ej = lane < k ? exp(myz - z0) : 0.0;  // rank 0 holds the largest selected logit
   const double sum = wave_sum_f64(ej);
+  id_out = myid;
+  p_out = static_cast<float>(ej / sum);
+}
+
+// Top-k of row t into the selection state in LDS.
+template <int NPL, typename SS>
+__device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
+  const int lane = threadIdx.x & 63;
+  const int k = a.k;
+  const int slot = t * k + lane;
+  int id;
+  float p;
+  topk_row<NPL>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p);
   if (lane < k) {
-    s.sel[t * k + lane] = myid;
-    s.p[t * k + lane] = static_cast<float>(ej / sum);
+    s.sel[slot] = id;
+    s.p[slot] = p;
   }
 }
 
