@@ -208,6 +208,7 @@ def main():
     wide = None if args.no_extra else wide_rounds(cfg, base, torch, np, synth, MoeRound)
     deep = None if args.no_extra else deep_stack(torch, np, synth, MoeRound)
     superblock = None if args.no_extra else superblock_rounds(acts, args.replicas, torch, np, synth, MoeRound)
+    prefill = None if args.no_extra else prefill_rounds(base, torch, np, synth, MoeRound)
 
     cpu = None
     if not args.no_cpu:
@@ -238,6 +239,7 @@ def main():
         "wide_rounds": wide,
         "deep_stack": deep,
         "superblock_format": superblock,
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
     if args.pmc_calibrate:
@@ -359,6 +361,61 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
     del reps
     torch.cuda.empty_cache()
     return res
+
+
+# The prefill GEMMs fold every int32 block product into fp32 on the vector ALUs: per output
+# element and 32-weight block (32 multiply-adds of the model) the plane combine (2 ops), the
+# conversion and the scale FMA, 4 VALU lane-ops. 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12
+# lane-ops/s, so the fold alone caps the model rate at 39.3e12 * 32 / 4 multiply-adds/s.
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+PREFILL_FOLD_PEAK_OPS = VALU_LANE_OPS * 32 / 4 * 2
+
+
+def prefill_rounds(layer, torch, np, synth, MoeRound):
+    """Prefill rounds (T = 512, 4096 independent rows, the verify layer shape): rows per second,
+    per-kernel time, and the gate/up GEMM's model rate against the fold-bound peak and the int8
+    matrix-core peak (executed int8 work: three digit planes over 64-pair tiles)."""
+    cfg = synth.config("prefill")
+    Tmax = max(cfg.T)
+    h = MoeRound([layer], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=Tmax, use_graph=False)
+    res = {}
+    for T in cfg.T:
+        xs = [synth.make_activations(cfg, T, seed=0, round_idx=r, device="cuda") for r in range(4)]
+        out = torch.empty((T, cfg.H), device="cuda")
+        for r in range(2):
+            h.run(xs[r], cfg.k, out)
+        lat = [timed_rounds(h, [xs[r % 4]], cfg.k, out, 1, torch)[0] for r in range(10)]
+        h.profile(True)
+        h.profile_read()
+        tiles = 0
+        for r in range(4):
+            h.run(xs[r], cfg.k, out)
+            _, offs, _ = h.worklist(0)
+            tiles += int(sum((int(n) + 63) // 64 for n in np.diff(offs)))
+        ms, runs = h.profile_read()
+        h.profile(False)
+        kms = np.array(ms[0]) / runs
+        med = float(np.median(lat))
+        pairs = T * cfg.k
+        gu_model = 2.0 * 2 * cfg.I * cfg.H * pairs          # model ops (multiply-add = 2)
+        dn_model = 2.0 * cfg.I * cfg.H * pairs
+        gu_exec = 3 * 2.0 * 2 * cfg.I * cfg.H * 64 * tiles / runs   # int8 ops the matrix cores ran
+        gu_s = kms[2] * 1e-3
+        res[str(T)] = {
+            "round_us_median": round(med, 1),
+            "tok_per_s": round(T / med * 1e6, 1),
+            "kernel_us": {n: round(float(v) * 1e3, 1) for n, v in
+                          zip(("quant_x+logits", "topk+sort", "gateup", "quant_h+down", "combine"), kms)},
+            "model_TOPs_round": round((gu_model + dn_model) / med / 1e6, 1),
+            "gateup": {"model_TOPs": round(gu_model / gu_s / 1e12, 1),
+                       "frac_of_fold_peak": round(gu_model / gu_s / PREFILL_FOLD_PEAK_OPS, 3),
+                       "int8_mfma_util": round(gu_exec / gu_s / INT8_DENSE_PEAK_OPS, 3)},
+        }
+        del xs
+    h.close()
+    torch.cuda.empty_cache()
+    return {"workload": "one MoE layer, H=2048, E=256, top-8, I=512, Q4B32; independent rows",
+            "fold_peak_TOPs": round(PREFILL_FOLD_PEAK_OPS / 1e12, 1), "rounds": res}
 
 
 def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager")):

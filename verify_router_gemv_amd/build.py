@@ -27,6 +27,11 @@ FLAGS = [
     "-fvisibility=hidden",
     "-Wall", "-Wno-unused-result",
 ]
+# Per-source flags. moe_round.hip holds the prefill GEMMs, whose int32 matrix-core results are
+# shifted and converted on the vector ALUs: with the results in ordinary VGPRs (not accumulation
+# registers) that costs no register-to-register copies. No other kernel of that file uses the
+# matrix cores.
+SOURCE_FLAGS = {"moe_round.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -37,7 +42,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)

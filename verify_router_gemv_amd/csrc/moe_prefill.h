@@ -1,13 +1,15 @@
 // Prefill MoE: rounds of more than 64 rows, where the expert FFN is compute-bound.
 //
-// Per layer eight kernels, launched eagerly:
+// Per layer nine kernels, launched eagerly:
 //   quant_rows_kernel   the layer input as 22-bit integers per row (three int8 digit planes) and
 //                       per-32-block sums, for the int8 matrix cores
 //   pf_logits_kernel    router GEMM on fp64 matrix cores (fp32 inputs, fp64 products and sums)
 //   pf_topk_kernel      one wave per row: top-k, softmax over the selected, and the row's bit in
 //                       each chosen expert's row mask
-//   pf_scan_kernel      one block: counting sort of the (row, rank) pairs by expert (ascending
-//                       expert, rows ascending within one), 64-row work items, the caller's ids
+//   pf_scan_kernel      one block: rows per expert, their offsets, the unique list and the
+//                       64-pair work items
+//   pf_scatter_kernel   counting sort of the (row, rank) pairs by expert (ascending expert, rows
+//                       ascending within one); the caller's ids and routing weights
 //   pf_gateup_kernel    per work item and 64 rows of I: silu(W_g x) * (W_u x) as an int8 GEMM
 //   quant_rows_kernel   the SwiGLU rows as digits
 //   pf_down_kernel      per work item and 64 rows of H: W_d h per pair, into a slot buffer
@@ -31,8 +33,8 @@ namespace pf {
 constexpr int kTile = 64;                 // GEMM tile: 64 weight rows x 64 (row, rank) pairs
 constexpr float kQMax = 4194303.0f;       // 2^22 - 1: 32 * 15 * kQMax < 2^31 (int32 block dots)
 constexpr int kStepBlocks = 4;            // 32-blocks of the reduction per pipeline step
-// LDS per GEMM block: two buffers of [block][plane][group][column][even, odd] digit words.
-constexpr int kStageWords = kStepBlocks * 3 * 4 * kTile * 2;
+// LDS per GEMM block: two buffers of [block][plane][half][pair][4] digit words.
+constexpr int kStageWords = kStepBlocks * 3 * 2 * kTile * 4;
 constexpr int kGemmLds = 2 * kStageWords * 4;
 
 struct PfArgs {
@@ -51,6 +53,7 @@ struct PfArgs {
   int32_t* n_unique;     // [L]
   int32_t* uniq;         // [L][E]
   int32_t* offs;         // [L][E + 1]
+  int32_t* eoff;         // [E] first pair slot of expert e
   int32_t* pairs;        // [L][Pcap] t | j << 16, grouped by expert
   float* pair_w;         // [Pcap]
   int32_t* slot_of;      // [Pcap] pair slot of (t, j) at t * k + j
@@ -159,7 +162,8 @@ static __global__ __launch_bounds__(kThreads) void pf_logits_kernel(PfArgs a, in
   const float* wr = a.w.router_w + static_cast<size_t>(min(e0 + c, E - 1)) * H + 4 * q;
   const float* xr = x + static_cast<size_t>(min(t0 + c, T - 1)) * H + 4 * q;
   f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  for (int h0 = 0; h0 < H; h0 += 16) {
+#pragma unroll 8
+  for (int h0 = 0; h0 < H; h0 += 16) {  // H / 16 is a multiple of 16
     const float4 wv = load_stream_f4(wr + h0);
     const float4 xv = load_f4(xr + h0);
     acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv.x), static_cast<double>(xv.x), acc, 0, 0, 0);
@@ -201,24 +205,35 @@ __global__ __launch_bounds__(kThreads) void pf_topk_kernel(PfArgs a, int layer) 
 }
 
 // ------------------------------------------------------------------------------------------
-// Counting sort by expert, one block of 1024 threads. Thread e < E counts expert e's rows word by
-// word (recording the count before each word), a block scan turns counts into pair offsets, unique
-// indices and work-item offsets, and each (row t, rank j) pair lands at its expert's offset plus
-// the rows of that expert below t (the words before, then the bits below t in t's word): slots
-// are grouped by ascending expert with rows ascending inside, as in the decode worklist.
+// Counting sort by expert. pf_scan_kernel (one block of 1024 threads): thread e < E counts expert
+// e's rows word by word (recording the count before each word), and a block scan turns the counts
+// into pair offsets, unique indices and work-item offsets. pf_scatter_kernel (one thread per pair)
+// then puts (row t, rank j) at its expert's offset plus the rows of that expert below t (the words
+// before, then the bits below t in t's word): slots are grouped by ascending expert with rows
+// ascending inside, as in the decode worklist.
 // ------------------------------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
 
 static __global__ __launch_bounds__(kScanThreads) void pf_scan_kernel(PfArgs a, int layer) {
   __shared__ unsigned long long s_scan[kScanThreads];
-  __shared__ int s_off[MOE_ROUND_MAX_EXPERTS];
-  const int tid = threadIdx.x, E = a.E, W = a.W, T = a.T, k = a.k;
-  const int npairs = T * k;
+  const int tid = threadIdx.x, E = a.E, W = a.W;
+  const int npairs = a.T * a.k;
   int cnt = 0;
   if (tid < E) {
     const unsigned long long* m = a.mask + static_cast<size_t>(tid) * W;
     int32_t* wp = a.wpre + static_cast<size_t>(tid) * W;
-    for (int w = 0; w < W; ++w) {
+    int w = 0;
+    for (; w + 8 <= W; w += 8) {  // eight loads in flight
+      unsigned long long v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = m[w + j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        wp[w + j] = cnt;
+        cnt += __popcll(v[j]);
+      }
+    }
+    for (; w < W; ++w) {
       wp[w] = cnt;
       cnt += __popcll(m[w]);
     }
@@ -243,7 +258,7 @@ static __global__ __launch_bounds__(kScanThreads) void pf_scan_kernel(PfArgs a, 
   int32_t* uniq = a.uniq + static_cast<size_t>(layer) * E;
   int32_t* offs = a.offs + static_cast<size_t>(layer) * (E + 1);
   if (tid < E) {
-    s_off[tid] = p0;
+    a.eoff[tid] = p0;
     if (cnt > 0) {
       uniq[u] = tid;
       offs[u] = p0;
@@ -255,161 +270,179 @@ static __global__ __launch_bounds__(kScanThreads) void pf_scan_kernel(PfArgs a, 
     a.n_unique[layer] = nu;
     *a.n_items = nitems;
   }
-  __threadfence_block();
-  __syncthreads();  // wpre and s_off written
-  int32_t* pairs = a.pairs + static_cast<size_t>(layer) * a.Pcap;
-  for (int idx = tid; idx < npairs; idx += kScanThreads) {
-    const int t = idx / k, j = idx - t * k;
-    const int e = a.sel[idx];
-    const size_t mw = static_cast<size_t>(e) * W + (t >> 6);
-    const int pos = min(s_off[e] + a.wpre[mw] + __popcll(a.mask[mw] & ((1ull << (t & 63)) - 1ull)), npairs - 1);
-    const float p = a.selp[idx];
-    pairs[pos] = t | (j << 16);
-    a.pair_w[pos] = p;
-    a.slot_of[idx] = pos;
-    const size_t o = static_cast<size_t>(layer) * npairs + idx;  // [L][T][k]
-    if (a.in.ids) a.in.ids[o] = e;
-    if (a.in.route_w) a.in.route_w[o] = p;
-  }
+}
+
+// Grid: ceil(T * k / 256) x 256 threads, one (row, rank) pair each.
+static __global__ __launch_bounds__(kThreads) void pf_scatter_kernel(PfArgs a, int layer) {
+  const int npairs = a.T * a.k;
+  const int idx = blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= npairs) return;
+  const int t = idx / a.k, j = idx - t * a.k;
+  const int e = a.sel[idx];
+  const float p = a.selp[idx];
+  const size_t mw = static_cast<size_t>(e) * a.W + (t >> 6);
+  const int pos = min(a.eoff[e] + a.wpre[mw] + __popcll(a.mask[mw] & ((1ull << (t & 63)) - 1ull)), npairs - 1);
+  a.pairs[static_cast<size_t>(layer) * a.Pcap + pos] = t | (j << 16);
+  a.pair_w[pos] = p;
+  a.slot_of[idx] = pos;
+  const size_t o = static_cast<size_t>(layer) * npairs + idx;  // [L][T][k]
+  if (a.in.ids) a.in.ids[o] = e;
+  if (a.in.route_w) a.in.route_w[o] = p;
 }
 
 // ------------------------------------------------------------------------------------------
-// GEMM tiles on v_mfma_i32_16x16x32_i8, one 32-weight block per instruction: A = 16 weight rows'
-// 4-bit codes as bytes (even elements of each 8-group, then the odd ones: the digit order), B = one
-// digit plane of 16 pair rows; lane l supplies A row / B column l % 16 and elements 8(l/16)..+7, and
-// D lane l holds rows 4(l/16)..+3 of column l % 16. Per block and (A, B) tile the three plane
-// products combine exactly in int32 (P = P0 + 256 P1 + 65536 P2, with wrapping shifts: the sum
-// fits) and fold into fp32 as acc += s * P. The minimum's term sum_b m_b * sum(x)_b / step runs
-// on v_mfma_f32_16x16x4f32 into the same accumulators (A = 16 rows' m over 4 blocks, B = the block
-// sums; the same D layout), and the row's step multiplies the total at the end.
+// GEMM tiles on v_mfma_i32_32x32x32_i8, one 32-weight block per instruction (the full-rate int8
+// form on gfx950; the 16x16x32 form runs at half rate). A = 32 pair rows' digits of one plane,
+// B = 32 weight rows' 4-bit codes as bytes; lane l supplies A row / B column l % 32 and elements
+// 16(l/32)..+15 (the even elements of each 8-group, then the odd ones: the order both the weight
+// nibbles and the stored digits have), and D register i of lane l holds row 8(i/4) + 4(l/32) + i%4
+// (a pair) of column l % 32 (a weight row), so a lane's block scale is one value. The three digit
+// planes chain through the accumulator, high plane first (D = (D << 8) + A_p B), which forms
+// P = P0 + 256 P1 + 65536 P2 exactly in wrapping int32 (the sum fits); the fold is acc += s * P. The
+// minimum's term sum_b m_b * sum(x)_b / step runs on v_mfma_f32_32x32x2f32 into the same
+// accumulators (A = the pairs' block sums, B = the rows' minima, two blocks per instruction; the
+// same D layout), and each pair's step multiplies its total at the end.
 //
-// The 64 pair rows' digits of each 4-block step are gathered into LDS (double-buffered, one
-// barrier per step) in [block][plane][group][column][even, odd] order, so the 16 lanes of a group
-// read 16 consecutive 8-byte words. Columns past the item's pairs repeat its last pair.
+// Block tile: 64 weight rows x 64 pairs, wave w taking rows 32 (w & 1).. and pairs 32 (w >> 1)...
+// The 64 pairs' digits of each 4-block step go through LDS (double-buffered, one barrier per step)
+// in [block][plane][half][pair][16 bytes] order, so a lane reads its 16 bytes next to its
+// neighbours'. The next step's digits are loaded into registers while the current step computes
+// and written to LDS after it: LDS DMA loads would make the compiler wait for them before the
+// step's first LDS read, as it cannot tell the two buffers apart. Pairs past the item's last
+// repeat it.
 // ------------------------------------------------------------------------------------------
 typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16v __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Stage the digits of blocks kb0..kb0+3 of the 64 source rows into LDS: 96 wave-instructions of a
-// 4-byte gather each (word `half` of group q, plane p, block bs of column c), split over 4 waves.
-__device__ __forceinline__ void stage_step(const uint32_t* const* rows, int kb0, uint32_t* buf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane & 1;  // lane l moves word `half` of column 32 ch + l / 2
+// The digits of blocks kb0..kb0+3 of the 64 pairs are 24 chunks (block, plane, half) of 16 bytes
+// per pair; wave w moves chunks 6w..6w+5 with lane l taking pair l (from its digit row `src`).
+__device__ __forceinline__ void fetch_step(const uint32_t* src, int kb0, u32x4 (&v)[6]) {
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int n = 0; n < 24; ++n) {
-    const int ins = wave * 24 + n;           // 0..95: (bs, p, q, column half)
-    const int ch = ins & 1, q = (ins >> 1) & 3, p = (ins >> 3) % 3, bs = (ins >> 3) / 3;
-    const uint32_t* src = rows[ch] + static_cast<size_t>(kb0 + bs) * kXqWords + p * 8 + 2 * q + half;
-    uint32_t* dst = buf + ((((bs * 3 + p) * 4 + q) * kTile) + 32 * ch) * 2;
-    __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void*)src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+  for (int n = 0; n < 6; ++n) {
+    const int ins = wave * 6 + n;  // (bs * 3 + p) * 2 + h
+    const int h = ins & 1, p = (ins >> 1) % 3, bs = (ins >> 1) / 3;
+    v[n] = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(kb0 + bs) * kXqWords + p * 8 + 4 * h);
   }
 }
-
-// Combine the three plane products of one D element and fold it with the row's block scale.
-__device__ __forceinline__ float fold3(int p0, int p1, int p2, float s, float acc) {
-  const uint32_t v = static_cast<uint32_t>(p0) + (static_cast<uint32_t>(p1) << 8) + (static_cast<uint32_t>(p2) << 16);
-  return fmaf(s, static_cast<float>(static_cast<int32_t>(v)), acc);
+__device__ __forceinline__ void store_step(const u32x4 (&v)[6], uint32_t* buf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int n = 0; n < 6; ++n) *reinterpret_cast<u32x4*>(buf + ((wave * 6 + n) * kTile + lane) * 4) = v[n];
 }
 
-// Byte codes of one 32-bit code word (8 weights) in the digit order.
-__device__ __forceinline__ long codes8(uint32_t w) {
-  const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
-  return static_cast<long>(static_cast<uint64_t>(ev) | (static_cast<uint64_t>(od) << 32));
+// 16 code bytes (elements 16h..16h+15 of a block) from its 8 packed bytes, in the digit order.
+__device__ __forceinline__ i32x4v codes16(uint2 w) {
+  return i32x4v{static_cast<int32_t>(w.x & 0x0F0F0F0Fu), static_cast<int32_t>((w.x >> 4) & 0x0F0F0F0Fu),
+                static_cast<int32_t>(w.y & 0x0F0F0F0Fu), static_cast<int32_t>((w.y >> 4) & 0x0F0F0F0Fu)};
 }
 
-// 4x4 transpose of dwords across the four 16-lane groups: before, group g holds words 0..3 of
-// block g; after, group g holds word g of blocks 0..3.
-__device__ __forceinline__ void transpose4(uint4& v) {
-  permlane32_swap(v.x, v.z);
-  permlane32_swap(v.y, v.w);
-  permlane16_swap(v.x, v.y);
-  permlane16_swap(v.z, v.w);
+// A lane's 8-byte code halves of blocks kb0..kb0+3 (half l / 32 of each): lane (c, h) loads blocks
+// kb0 + 2h and kb0 + 2h + 1 of row c whole (so the 32 lanes of a half-wave read 32 rows' 64 bytes in
+// two 16-byte loads per lane), then the two half-waves trade the halves the other needs.
+// Ordinary cached loads: a line is touched by the two steps that share it, and items of one
+// expert re-read its rows.
+__device__ __forceinline__ void load_codes(const uint8_t* row, int kb0, uint2 (&cw)[kStepBlocks]) {
+  const int h = (threadIdx.x & 63) >> 5;
+  const u32x4 p = *reinterpret_cast<const u32x4*>(row + 16 * (kb0 + 2 * h));
+  const u32x4 q = *reinterpret_cast<const u32x4*>(row + 16 * (kb0 + 2 * h + 1));
+  // before: low half-wave P = block kb0 (lo, hi words), upper half-wave P = block kb0 + 2
+  uint32_t p0 = p.x, p1 = p.y, p2 = p.z, p3 = p.w, q0 = q.x, q1 = q.y, q2 = q.z, q3 = q.w;
+  permlane32_swap(p0, p2);  // low: (p0, p2) = kb0 lo, kb0 + 2 lo; upper: kb0 hi, kb0 + 2 hi
+  permlane32_swap(p1, p3);
+  permlane32_swap(q0, q2);
+  permlane32_swap(q1, q3);
+  cw[0] = make_uint2(p0, p1);
+  cw[1] = make_uint2(q0, q1);
+  cw[2] = make_uint2(p2, p3);
+  cw[3] = make_uint2(q2, q3);
 }
 
 // Work unit of GEMM block `bid` of `nb` (a multiple of 8): consecutive units (the tiles of one
 // work item) go to one XCD, whose L2 then holds that item's digit rows once.
 __device__ __forceinline__ int xcd_unit(int bid, int nb) { return (bid & 7) * (nb >> 3) + (bid >> 3); }
 
-// One wave's 16 consecutive weight rows of NM matrices against the 64 staged columns. codes0 /
-// sm0: the code and scale/min rows of the wave's first row in each matrix. acc[m][c4][i]: D row
-// 4(l/16)+i (weight row), column 16 c4 + l % 16 (pair), in units of the column's step. Each
-// pipeline step also stages the next step's digits.
+// One wave's 32 weight rows (starting at codes0 / sm0 in each of NM matrices) against 32 of the
+// block's 64 staged pairs (half ph). src: this lane's staging source row (pair lane % 64); xs: the
+// block sums of pair 32 ph + lane % 32. live = false (no pair of this half exists): the wave only
+// stages and waits. acc[m][i]: D element i, in units of the pair's step.
 template <int NM>
 __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const uint32_t* const* sm0, int K,
-                                          const uint32_t* const* src_rows, const float* const* xs_rows,
-                                          uint32_t* lds, f32x4 (&acc)[NM][4]) {
+                                          const uint32_t* src, const float* xs, int ph, bool live, uint32_t* lds,
+                                          f32x16 (&acc)[NM]) {
   const int lane = threadIdx.x & 63;
-  const int r = lane & 15, q = lane >> 4;
+  const int c = lane & 31, h = lane >> 5;
   const int nblk = K / 32, nstep = nblk / kStepBlocks;
+  live = __builtin_amdgcn_readfirstlane(static_cast<int>(live)) != 0;  // one value per wave
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) acc[m][c4] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stage_step(src_rows, 0, lds);
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
+  u32x4 nxt[6];
+  fetch_step(src, 0, nxt);
+  store_step(nxt, lds);
   __syncthreads();
   for (int st = 0; st < nstep; ++st) {
     const int kb0 = st * kStepBlocks;
-    uint32_t* cur = lds + (st & 1) * kStageWords;
-    if (st + 1 < nstep) stage_step(src_rows, kb0 + kStepBlocks, lds + ((st + 1) & 1) * kStageWords);
-    // A: lane (r, q) loads block kb0 + q of row r; after the transpose it holds word q of blocks
-    // kb0..kb0+3. Scales of the D rows 4q..4q+3 for the 4 blocks; the minimum of (row r, block q).
-    uint4 cw[NM];
-    float s[NM][kStepBlocks][4];
-    float mq[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      cw[m] = load_stream_u4(codes0[m] + static_cast<size_t>(r) * (K / 2) + 16 * (kb0 + q));
-      mq[m] = half_bits_to_float(load_stream_u32(sm0[m] + static_cast<size_t>(r) * nblk + kb0 + q) >> 16);
-    }
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 w4 = *reinterpret_cast<const uint4*>(sm0[m] + static_cast<size_t>(4 * q + i) * nblk + kb0);
-        s[m][0][i] = half_bits_to_float(w4.x);
-        s[m][1][i] = half_bits_to_float(w4.y);
-        s[m][2][i] = half_bits_to_float(w4.z);
-        s[m][3][i] = half_bits_to_float(w4.w);
-      }
-      transpose4(cw[m]);
-    }
-    // The minimum's term of the 4 blocks, into the accumulators.
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      const float xs = xs_rows[c4][kb0 + q];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) acc[m][c4] = __builtin_amdgcn_mfma_f32_16x16x4f32(mq[m], xs, acc[m][c4], 0, 0, 0);
-    }
-#pragma unroll
-    for (int bs = 0; bs < kStepBlocks; ++bs) {
-      long a8[NM];
+    const uint32_t* cur = lds + (st & 1) * kStageWords;
+    // This step's weight codes and scale/min words first, then the next step's digits: waiting
+    // for the former then leaves the latter in flight.
+    uint2 cw[NM][kStepBlocks];
+    uint4 smw[NM];
+    float x2[2];
+    if (live) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const uint32_t word = bs == 0 ? cw[m].x : bs == 1 ? cw[m].y : bs == 2 ? cw[m].z : cw[m].w;
-        a8[m] = codes8(word);
+        load_codes(codes0[m] + static_cast<size_t>(c) * (K / 2), kb0, cw[m]);
+        smw[m] = *reinterpret_cast<const uint4*>(sm0[m] + static_cast<size_t>(c) * nblk + kb0);
+      }
+      x2[0] = xs[kb0 + h];
+      x2[1] = xs[kb0 + 2 + h];
+    }
+    if (st + 1 < nstep) fetch_step(src, kb0 + kStepBlocks, nxt);
+    if (live) {
+      // The minimum's term of the 4 blocks: instruction j takes blocks kb0 + 2j + (l / 32).
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint32_t hm = 0u - static_cast<uint32_t>(h);  // all ones in the upper half-wave
+        const float m0 = half_bits_to_float((smw[m].x ^ ((smw[m].x ^ smw[m].y) & hm)) >> 16);
+        const float m1 = half_bits_to_float((smw[m].z ^ ((smw[m].z ^ smw[m].w) & hm)) >> 16);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[0], m0, acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[1], m1, acc[m], 0, 0, 0);
       }
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        long b8[3];
+      for (int bs = 0; bs < kStepBlocks; ++bs) {
+        i32x4v ap[3];
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          b8[p] = *reinterpret_cast<const long*>(cur + ((((bs * 3 + p) * 4 + q) * kTile) + 16 * c4 + r) * 2);
-        const i32x4v z = {0, 0, 0, 0};
+          ap[p] = *reinterpret_cast<const i32x4v*>(cur + (((bs * 3 + p) * 2 + h) * kTile + 32 * ph + c) * 4);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          const i32x4v d0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a8[m], b8[0], z, 0, 0, 0);
-          const i32x4v d1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a8[m], b8[1], z, 0, 0, 0);
-          const i32x4v d2 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a8[m], b8[2], z, 0, 0, 0);
+          const i32x4v b = codes16(cw[m][bs]);
+          const uint32_t sw = bs == 0 ? smw[m].x : bs == 1 ? smw[m].y : bs == 2 ? smw[m].z : smw[m].w;
+          const float sc = half_bits_to_float(sw);
+          const i32x16v z = {};
+          i32x16v d = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap[2], b, z, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap[1], b, d << 8, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap[0], b, d << 8, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][c4][i] = fold3(d0[i], d1[i], d2[i], s[m][bs][i], acc[m][c4][i]);
+          for (int i = 0; i < 16; ++i) acc[m][i] = fmaf(sc, static_cast<float>(d[i]), acc[m][i]);
         }
       }
     }
+    if (st + 1 < nstep) store_step(nxt, lds + ((st + 1) & 1) * kStageWords);  // read two steps ago
     __syncthreads();  // step st read by every wave; step st + 1 staged
   }
 }
 
-// Gate/up: work unit = (item, 64 rows of I). Wave w takes rows i0 + 16w .. +15 of both gate and
-// up, and writes silu(g) * v of its rows for the item's pairs into hbuf (by pair slot).
+// Pair (within the block's 64) of D element i for this lane.
+__device__ __forceinline__ int d_pair(int ph, int i) {
+  return 32 * ph + 8 * (i >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (i & 3);
+}
+
+// Gate/up: work unit = (item, 64 rows of I). Writes silu(g) * v of the block's rows for the item's
+// pairs into hbuf (by pair slot).
 static __global__ __launch_bounds__(kThreads) void pf_gateup_kernel(PfArgs a, int layer) {
   extern __shared__ uint32_t lds[];
   const int I = a.I, H = a.H;
@@ -419,44 +452,31 @@ static __global__ __launch_bounds__(kThreads) void pf_gateup_kernel(PfArgs a, in
   if (it >= *a.n_items) return;  // whole blocks leave together
   const int4 item = a.items[it];
   const int e = item.x, p0 = item.y, np = item.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, q = lane >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rh = wave & 1, ph = wave >> 1;
   const int32_t* pairs = a.pairs + static_cast<size_t>(layer) * a.Pcap;
-  // Source rows of the staged columns: the staging lanes need columns lane / 2 and 32 + lane / 2;
-  // the accumulation lanes need the block sums of columns 16 c4 + r.
-  const uint32_t* src[2];
-#pragma unroll
-  for (int ch = 0; ch < 2; ++ch) {
-    const int t = pairs[p0 + min(32 * ch + (lane >> 1), np - 1)] & 0xFFFF;
-    src[ch] = a.xq + static_cast<size_t>(t) * (H / 32) * kXqWords;
-  }
-  const float* xs[4];
-  int tcol[4];
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    tcol[c4] = pairs[p0 + min(16 * c4 + r, np - 1)] & 0xFFFF;
-    xs[c4] = a.xsum + static_cast<size_t>(tcol[c4]) * (H / 32);
-  }
-  const size_t row = static_cast<size_t>(e) * I + i0 + 16 * wave;  // the wave's first row
+  __shared__ float s_step[kTile];  // the item's pairs' steps, for the epilogue
+  const int tsrc = pairs[p0 + min(lane, np - 1)] & 0xFFFF;                  // staging: pair lane
+  if (wave == 0) s_step[lane] = a.xstep[tsrc];  // visible after the GEMM's first barrier
+  const int tsum = pairs[p0 + min(32 * ph + (lane & 31), np - 1)] & 0xFFFF;  // block sums: A row
+  const uint32_t* src = a.xq + static_cast<size_t>(tsrc) * (H / 32) * kXqWords;
+  const float* xs = a.xsum + static_cast<size_t>(tsum) * (H / 32);
+  const size_t row = static_cast<size_t>(e) * I + i0 + 32 * rh;  // the wave's first weight row
   const uint8_t* codes[2] = {a.w.gate_q + row * (H / 2), a.w.up_q + row * (H / 2)};
   const uint32_t* sm[2] = {a.w.gate_sm + row * (H / 32), a.w.up_sm + row * (H / 32)};
-  f32x4 acc[2][4];
-  gemm_rows<2>(codes, sm, H, src, xs, lds, acc);
+  f32x16 acc[2];
+  gemm_rows<2>(codes, sm, H, src, xs, ph, 32 * ph < np, lds, acc);
+  const int col = i0 + 32 * rh + (lane & 31);
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    const int c = 16 * c4 + r;
-    const float step = a.xstep[tcol[c4]];
-    float4 h;
-    h.x = silu(step * acc[0][c4][0]) * (step * acc[1][c4][0]);
-    h.y = silu(step * acc[0][c4][1]) * (step * acc[1][c4][1]);
-    h.z = silu(step * acc[0][c4][2]) * (step * acc[1][c4][2]);
-    h.w = silu(step * acc[0][c4][3]) * (step * acc[1][c4][3]);
-    if (c < np)
-      *reinterpret_cast<float4*>(a.hbuf + static_cast<size_t>(p0 + c) * I + i0 + 16 * wave + 4 * q) = h;
+  for (int i = 0; i < 16; ++i) {
+    const int pr = d_pair(ph, i);
+    const float step = s_step[pr];
+    if (pr < np) a.hbuf[static_cast<size_t>(p0 + pr) * I + col] = silu(step * acc[0][i]) * (step * acc[1][i]);
   }
 }
 
-// Down: work unit = (item, 64 rows of H). Wave w takes rows h0 + 16w .. +15 of W_d and writes
-// W_d h of its rows for the item's pairs into ybuf (by pair slot).
+// Down: work unit = (item, 64 rows of H). Writes W_d h of the block's rows for the item's pairs
+// into ybuf (by pair slot).
 static __global__ __launch_bounds__(kThreads) void pf_down_kernel(PfArgs a, int layer) {
   extern __shared__ uint32_t lds[];
   const int I = a.I, H = a.H;
@@ -466,25 +486,23 @@ static __global__ __launch_bounds__(kThreads) void pf_down_kernel(PfArgs a, int 
   if (it >= *a.n_items) return;
   const int4 item = a.items[it];
   const int e = item.x, p0 = item.y, np = item.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, q = lane >> 4;
-  const uint32_t* src[2];
-#pragma unroll
-  for (int ch = 0; ch < 2; ++ch)
-    src[ch] = a.hq + static_cast<size_t>(p0 + min(32 * ch + (lane >> 1), np - 1)) * (I / 32) * kXqWords;
-  const float* xs[4];
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) xs[c4] = a.hsum + static_cast<size_t>(p0 + min(16 * c4 + r, np - 1)) * (I / 32);
-  const size_t row = static_cast<size_t>(e) * H + h0 + 16 * wave;  // the wave's first row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rh = wave & 1, ph = wave >> 1;
+  __shared__ float s_step[kTile];
+  const uint32_t* src = a.hq + static_cast<size_t>(p0 + min(lane, np - 1)) * (I / 32) * kXqWords;
+  if (wave == 0) s_step[lane] = a.hstep[p0 + min(lane, np - 1)];  // visible after the first barrier
+  const float* xs = a.hsum + static_cast<size_t>(p0 + min(32 * ph + (lane & 31), np - 1)) * (I / 32);
+  const size_t row = static_cast<size_t>(e) * H + h0 + 32 * rh;
   const uint8_t* codes[1] = {a.w.down_q + row * (I / 2)};
   const uint32_t* sm[1] = {a.w.down_sm + row * (I / 32)};
-  f32x4 acc[1][4];
-  gemm_rows<1>(codes, sm, I, src, xs, lds, acc);
+  f32x16 acc[1];
+  gemm_rows<1>(codes, sm, I, src, xs, ph, 32 * ph < np, lds, acc);
+  const int col = h0 + 32 * rh + (lane & 31);
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    const int c = 16 * c4 + r;
-    const float step = a.hstep[p0 + min(c, np - 1)];
-    const float4 y = make_float4(step * acc[0][c4][0], step * acc[0][c4][1], step * acc[0][c4][2], step * acc[0][c4][3]);
-    if (c < np) *reinterpret_cast<float4*>(a.ybuf + static_cast<size_t>(p0 + c) * H + h0 + 16 * wave + 4 * q) = y;
+  for (int i = 0; i < 16; ++i) {
+    const int pr = d_pair(ph, i);
+    const float step = s_step[pr];
+    if (pr < np) a.ybuf[static_cast<size_t>(p0 + pr) * H + col] = step * acc[0][i];
   }
 }
 

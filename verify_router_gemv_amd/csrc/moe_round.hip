@@ -6,7 +6,7 @@
 // table from fixed device buffers, so new per-request pointers never force a recapture
 // ("How AlphaInfer makes local decoding fast", section 2: per-request data is ingress written
 // into fixed buffers and the graph is never rebuilt). Rounds of more than MOE_ROUND_MAX_ROWS rows
-// (prefill) run the kernels of moe_prefill.h eagerly, eight per layer.
+// (prefill) run the kernels of moe_prefill.h eagerly, nine per layer.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -36,7 +36,7 @@ struct Launch {
 };
 
 constexpr int kKernelsPerLayer = 5;  // kinds of kernel per layer: logits, select, gate/up, down, combine
-constexpr int kLaunchesPerLayer = 8;  // most launches of one layer (a prefill round)
+constexpr int kLaunchesPerLayer = 9;  // most launches of one layer (a prefill round)
 
 struct GraphEntry {
   hipGraph_t graph = nullptr;
@@ -107,6 +107,7 @@ struct moe_round {
   float* pf_selp = nullptr;
   int32_t* pf_uniq = nullptr;
   int32_t* pf_offs = nullptr;
+  int32_t* pf_eoff = nullptr;
   int32_t* pf_pairs = nullptr;
   float* pf_pair_w = nullptr;
   int32_t* pf_slot_of = nullptr;
@@ -300,7 +301,8 @@ static PfKernelFn pf_pick_topk(int E) {
 }
 
 // A prefill round (T > MOE_ROUND_MAX_ROWS), eagerly: per layer the digits of the layer input,
-// router logits, top-k, the counting sort, gate/up, the SwiGLU digits, down and the combine.
+// router logits, top-k, the counting sort (offsets, then the scatter), gate/up, the SwiGLU
+// digits, down and the combine.
 // evs: with profiling, a start/stop pair per launch; kinds: their accumulator (layer, kind).
 static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, int* kinds, int* n_launched) {
   const int E = h->cfg.n_experts, H = h->cfg.hidden, I = h->cfg.inter, L = h->cfg.n_layers;
@@ -319,6 +321,7 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
   a.n_unique = h->n_unique;
   a.uniq = h->pf_uniq;
   a.offs = h->pf_offs;
+  a.eoff = h->pf_eoff;
   a.pairs = h->pf_pairs;
   a.pair_w = h->pf_pair_w;
   a.slot_of = h->pf_slot_of;
@@ -371,6 +374,8 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
             hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::pf_scan_kernel), dim3(1), pf::kScanThreads, 0, gp, l, 1)) !=
             hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(pf::pf_scatter_kernel), dim3((np + kThreads - 1) / kThreads),
+                    kThreads, 0, gp, l, 1)) != hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::pf_gateup_kernel), dim3(gu_units), kThreads, pf::kGemmLds, gp,
                     l, 2)) != hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::quant_rows_kernel), dim3((np + kWaves - 1) / kWaves), kThreads,
@@ -448,7 +453,7 @@ static void free_handle(moe_round* h) {
   void* ptrs[] = {h->d_ing, h->d_wtab, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique, h->uniq, h->offs,
                   h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->xq, h->xss,
                   h->pf_xbuf[0], h->pf_xbuf[1], h->pf_xq, h->pf_xstep, h->pf_xsum, h->pf_mask, h->pf_wpre,
-                  h->pf_sel, h->pf_selp, h->pf_uniq, h->pf_offs, h->pf_pairs, h->pf_pair_w, h->pf_slot_of,
+                  h->pf_sel, h->pf_selp, h->pf_uniq, h->pf_offs, h->pf_eoff, h->pf_pairs, h->pf_pair_w, h->pf_slot_of,
                   h->pf_items, h->pf_n_items, h->pf_hbuf, h->pf_hq, h->pf_hstep, h->pf_hsum, h->pf_ybuf};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
@@ -524,6 +529,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
     MOE_ALLOC(h->pf_selp, sizeof(float) * P);
     MOE_ALLOC(h->pf_uniq, sizeof(int32_t) * L * E);
     MOE_ALLOC(h->pf_offs, sizeof(int32_t) * L * (E + 1));
+    MOE_ALLOC(h->pf_eoff, sizeof(int32_t) * E);
     MOE_ALLOC(h->pf_pairs, sizeof(int32_t) * L * P);
     MOE_ALLOC(h->pf_pair_w, sizeof(float) * P);
     MOE_ALLOC(h->pf_slot_of, sizeof(int32_t) * P);
