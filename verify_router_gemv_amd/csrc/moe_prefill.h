@@ -30,7 +30,9 @@
 namespace moe {
 namespace pf {
 
-constexpr int kTile = 64;                 // GEMM tile: 64 weight rows x 64 (row, rank) pairs
+constexpr int kTile = 64;                 // GEMM tile: 64 (row, rank) pairs by 64 or 128 weight rows
+constexpr int kGemmThreads = 512;         // GEMM blocks: 8 waves, each 32 weight rows x 32 pairs of one matrix
+constexpr int kGemmWaves = kGemmThreads / 64;
 constexpr float kQMax = 4194303.0f;       // 2^22 - 1: 32 * 15 * kQMax < 2^31 (int32 block dots)
 constexpr int kStepBlocks = 4;            // 32-blocks of the reduction per pipeline step
 // LDS per GEMM block: two buffers of [block][plane][half][pair][4] digit words.
@@ -303,8 +305,8 @@ static __global__ __launch_bounds__(kThreads) void pf_scatter_kernel(PfArgs a, i
 // accumulators (A = the pairs' block sums, B = the rows' minima, two blocks per instruction; the
 // same D layout), and each pair's step multiplies its total at the end.
 //
-// Block tile: 64 weight rows x 64 pairs, wave w taking rows 32 (w & 1).. and pairs 32 (w >> 1)...
-// The 64 pairs' digits of each 4-block step go through LDS (double-buffered, one barrier per step)
+// Block tile: 64 pairs by 64 rows of gate and of up (gate/up) or by 128 rows (down), eight waves
+// of 32 rows x 32 pairs of one matrix each (at most 128 VGPRs: four waves per SIMD). The 64 pairs' digits of each 4-block step go through LDS (double-buffered, one barrier per step)
 // in [block][plane][half][pair][16 bytes] order, so a lane reads its 16 bytes next to its
 // neighbours'. The next step's digits are loaded into registers while the current step computes
 // and written to LDS after it: LDS DMA loads would make the compiler wait for them before the
@@ -316,20 +318,22 @@ typedef int32_t i32x16v __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // The digits of blocks kb0..kb0+3 of the 64 pairs are 24 chunks (block, plane, half) of 16 bytes
-// per pair; wave w moves chunks 6w..6w+5 with lane l taking pair l (from its digit row `src`).
-__device__ __forceinline__ void fetch_step(const uint32_t* src, int kb0, u32x4 (&v)[6]) {
+// per pair; wave w moves chunks 3w..3w+2 with lane l taking pair l (from its digit row `src`).
+constexpr int kChunksPerWave = 24 / kGemmWaves;
+__device__ __forceinline__ void fetch_step(const uint32_t* src, int kb0, u32x4 (&v)[kChunksPerWave]) {
   const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int n = 0; n < 6; ++n) {
-    const int ins = wave * 6 + n;  // (bs * 3 + p) * 2 + h
+  for (int n = 0; n < kChunksPerWave; ++n) {
+    const int ins = wave * kChunksPerWave + n;  // (bs * 3 + p) * 2 + h
     const int h = ins & 1, p = (ins >> 1) % 3, bs = (ins >> 1) / 3;
     v[n] = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(kb0 + bs) * kXqWords + p * 8 + 4 * h);
   }
 }
-__device__ __forceinline__ void store_step(const u32x4 (&v)[6], uint32_t* buf) {
+__device__ __forceinline__ void store_step(const u32x4 (&v)[kChunksPerWave], uint32_t* buf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int n = 0; n < 6; ++n) *reinterpret_cast<u32x4*>(buf + ((wave * 6 + n) * kTile + lane) * 4) = v[n];
+  for (int n = 0; n < kChunksPerWave; ++n)
+    *reinterpret_cast<u32x4*>(buf + ((wave * kChunksPerWave + n) * kTile + lane) * 4) = v[n];
 }
 
 // 16 code bytes (elements 16h..16h+15 of a block) from its 8 packed bytes, in the digit order.
@@ -343,12 +347,19 @@ __device__ __forceinline__ i32x4v codes16(uint2 w) {
 // two 16-byte loads per lane), then the two half-waves trade the halves the other needs.
 // Ordinary cached loads: a line is touched by the two steps that share it, and items of one
 // expert re-read its rows.
-__device__ __forceinline__ void load_codes(const uint8_t* row, int kb0, uint2 (&cw)[kStepBlocks]) {
+struct StepCodes {
+  u32x4 p, q;  // blocks kb0 + 2h and kb0 + 2h + 1 of this lane's row, as loaded
+  uint4 smw;   // scale/min words of blocks kb0..kb0+3
+};
+__device__ __forceinline__ void load_step_codes(const uint8_t* row, const uint32_t* smrow, int kb0, StepCodes& w) {
   const int h = (threadIdx.x & 63) >> 5;
-  const u32x4 p = *reinterpret_cast<const u32x4*>(row + 16 * (kb0 + 2 * h));
-  const u32x4 q = *reinterpret_cast<const u32x4*>(row + 16 * (kb0 + 2 * h + 1));
-  // before: low half-wave P = block kb0 (lo, hi words), upper half-wave P = block kb0 + 2
-  uint32_t p0 = p.x, p1 = p.y, p2 = p.z, p3 = p.w, q0 = q.x, q1 = q.y, q2 = q.z, q3 = q.w;
+  w.p = *reinterpret_cast<const u32x4*>(row + 16 * (kb0 + 2 * h));
+  w.q = *reinterpret_cast<const u32x4*>(row + 16 * (kb0 + 2 * h + 1));
+  w.smw = *reinterpret_cast<const uint4*>(smrow + kb0);
+}
+__device__ __forceinline__ void trade_halves(const StepCodes& w, uint2 (&cw)[kStepBlocks]) {
+  // before: low half-wave p = block kb0 (lo, hi words), upper half-wave p = block kb0 + 2
+  uint32_t p0 = w.p.x, p1 = w.p.y, p2 = w.p.z, p3 = w.p.w, q0 = w.q.x, q1 = w.q.y, q2 = w.q.z, q3 = w.q.w;
   permlane32_swap(p0, p2);  // low: (p0, p2) = kb0 lo, kb0 + 2 lo; upper: kb0 hi, kb0 + 2 hi
   permlane32_swap(p1, p3);
   permlane32_swap(q0, q2);
@@ -379,38 +390,37 @@ __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const ui
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
-  u32x4 nxt[6];
+  u32x4 nxt[kChunksPerWave];
+  StepCodes cur_w[NM], nxt_w[NM];
+  float x2[2], nx2[2];
+  if (live) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) load_step_codes(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + static_cast<size_t>(c) * nblk, 0, cur_w[m]);
+    x2[0] = xs[h];
+    x2[1] = xs[2 + h];
+  }
   fetch_step(src, 0, nxt);
   store_step(nxt, lds);
   __syncthreads();
   for (int st = 0; st < nstep; ++st) {
     const int kb0 = st * kStepBlocks;
     const uint32_t* cur = lds + (st & 1) * kStageWords;
-    // This step's weight codes and scale/min words first, then the next step's digits: waiting
-    // for the former then leaves the latter in flight.
-    uint2 cw[NM][kStepBlocks];
-    uint4 smw[NM];
-    float x2[2];
-    if (live) {
+    const bool more = st + 1 < nstep;
+    // The next step's codes, scale/min words, block sums and digits are loaded while this step
+    // computes (its own arrived during the previous step).
+    if (live && more) {
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        load_codes(codes0[m] + static_cast<size_t>(c) * (K / 2), kb0, cw[m]);
-        smw[m] = *reinterpret_cast<const uint4*>(sm0[m] + static_cast<size_t>(c) * nblk + kb0);
-      }
-      x2[0] = xs[kb0 + h];
-      x2[1] = xs[kb0 + 2 + h];
+      for (int m = 0; m < NM; ++m)
+        load_step_codes(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + static_cast<size_t>(c) * nblk,
+                        kb0 + kStepBlocks, nxt_w[m]);
+      nx2[0] = xs[kb0 + kStepBlocks + h];
+      nx2[1] = xs[kb0 + kStepBlocks + 2 + h];
     }
-    if (st + 1 < nstep) fetch_step(src, kb0 + kStepBlocks, nxt);
+    if (more) fetch_step(src, kb0 + kStepBlocks, nxt);
     if (live) {
-      // The minimum's term of the 4 blocks: instruction j takes blocks kb0 + 2j + (l / 32).
+      uint2 cw[NM][kStepBlocks];
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const uint32_t hm = 0u - static_cast<uint32_t>(h);  // all ones in the upper half-wave
-        const float m0 = half_bits_to_float((smw[m].x ^ ((smw[m].x ^ smw[m].y) & hm)) >> 16);
-        const float m1 = half_bits_to_float((smw[m].z ^ ((smw[m].z ^ smw[m].w) & hm)) >> 16);
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[0], m0, acc[m], 0, 0, 0);
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[1], m1, acc[m], 0, 0, 0);
-      }
+      for (int m = 0; m < NM; ++m) trade_halves(cur_w[m], cw[m]);
 #pragma unroll
       for (int bs = 0; bs < kStepBlocks; ++bs) {
         i32x4v ap[3];
@@ -420,7 +430,8 @@ __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const ui
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           const i32x4v b = codes16(cw[m][bs]);
-          const uint32_t sw = bs == 0 ? smw[m].x : bs == 1 ? smw[m].y : bs == 2 ? smw[m].z : smw[m].w;
+          const uint4 smw = cur_w[m].smw;
+          const uint32_t sw = bs == 0 ? smw.x : bs == 1 ? smw.y : bs == 2 ? smw.z : smw.w;
           const float sc = half_bits_to_float(sw);
           const i32x16v z = {};
           i32x16v d = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap[2], b, z, 0, 0, 0);
@@ -430,9 +441,26 @@ __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const ui
           for (int i = 0; i < 16; ++i) acc[m][i] = fmaf(sc, static_cast<float>(d[i]), acc[m][i]);
         }
       }
+      // The minimum's term of the 4 blocks (instruction j takes blocks kb0 + 2j + l / 32), after the
+      // folds: the next step's integer products then cover its latency before acc is needed again.
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint4 smw = cur_w[m].smw;
+        const uint32_t hm = 0u - static_cast<uint32_t>(h);  // all ones in the upper half-wave
+        const float m0 = half_bits_to_float((smw.x ^ ((smw.x ^ smw.y) & hm)) >> 16);
+        const float m1 = half_bits_to_float((smw.z ^ ((smw.z ^ smw.w) & hm)) >> 16);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[0], m0, acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[1], m1, acc[m], 0, 0, 0);
+      }
     }
-    if (st + 1 < nstep) store_step(nxt, lds + ((st + 1) & 1) * kStageWords);  // read two steps ago
+    if (more) store_step(nxt, lds + ((st + 1) & 1) * kStageWords);  // read two steps ago
     __syncthreads();  // step st read by every wave; step st + 1 staged
+    if (live && more) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) cur_w[m] = nxt_w[m];
+      x2[0] = nx2[0];
+      x2[1] = nx2[1];
+    }
   }
 }
 
@@ -441,9 +469,10 @@ __device__ __forceinline__ int d_pair(int ph, int i) {
   return 32 * ph + 8 * (i >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (i & 3);
 }
 
-// Gate/up: work unit = (item, 64 rows of I). Writes silu(g) * v of the block's rows for the item's
-// pairs into hbuf (by pair slot).
-static __global__ __launch_bounds__(kThreads) void pf_gateup_kernel(PfArgs a, int layer) {
+// Gate/up: work unit = (item, 64 rows of I). Waves 0-3 take gate, 4-7 up (rows 32 (w & 1)..,
+// pairs 32 ((w >> 1) & 1)..); the up waves hand their sums to the gate waves through LDS, which
+// write silu(g) * v of the block's rows for the item's pairs into hbuf (by pair slot).
+static __global__ __launch_bounds__(kGemmThreads) void pf_gateup_kernel(PfArgs a, int layer) {
   extern __shared__ uint32_t lds[];
   const int I = a.I, H = a.H;
   const int tiles = I / kTile;
@@ -453,7 +482,7 @@ static __global__ __launch_bounds__(kThreads) void pf_gateup_kernel(PfArgs a, in
   const int4 item = a.items[it];
   const int e = item.x, p0 = item.y, np = item.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rh = wave & 1, ph = wave >> 1;
+  const int mt = wave >> 2, rh = wave & 1, ph = (wave >> 1) & 1;
   const int32_t* pairs = a.pairs + static_cast<size_t>(layer) * a.Pcap;
   __shared__ float s_step[kTile];  // the item's pairs' steps, for the epilogue
   const int tsrc = pairs[p0 + min(lane, np - 1)] & 0xFFFF;                  // staging: pair lane
@@ -462,42 +491,52 @@ static __global__ __launch_bounds__(kThreads) void pf_gateup_kernel(PfArgs a, in
   const uint32_t* src = a.xq + static_cast<size_t>(tsrc) * (H / 32) * kXqWords;
   const float* xs = a.xsum + static_cast<size_t>(tsum) * (H / 32);
   const size_t row = static_cast<size_t>(e) * I + i0 + 32 * rh;  // the wave's first weight row
-  const uint8_t* codes[2] = {a.w.gate_q + row * (H / 2), a.w.up_q + row * (H / 2)};
-  const uint32_t* sm[2] = {a.w.gate_sm + row * (H / 32), a.w.up_sm + row * (H / 32)};
-  f32x16 acc[2];
-  gemm_rows<2>(codes, sm, H, src, xs, ph, 32 * ph < np, lds, acc);
-  const int col = i0 + 32 * rh + (lane & 31);
+  const uint8_t* codes[1] = {(mt ? a.w.up_q : a.w.gate_q) + row * (H / 2)};
+  const uint32_t* sm[1] = {(mt ? a.w.up_sm : a.w.gate_sm) + row * (H / 32)};
+  f32x16 acc[1];
+  gemm_rows<1>(codes, sm, H, src, xs, ph, 32 * ph < np, lds, acc);
+  // The staging buffers are free (the GEMM ends on a barrier): up sums [rh][ph][i][lane].
+  float* xch = reinterpret_cast<float*>(lds) + ((rh * 2 + ph) * 16) * 64 + lane;
+  if (mt == 1) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int pr = d_pair(ph, i);
-    const float step = s_step[pr];
-    if (pr < np) a.hbuf[static_cast<size_t>(p0 + pr) * I + col] = silu(step * acc[0][i]) * (step * acc[1][i]);
+    for (int i = 0; i < 16; ++i) xch[i * 64] = acc[0][i];
+  }
+  __syncthreads();
+  if (mt == 0) {
+    const int col = i0 + 32 * rh + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int pr = d_pair(ph, i);
+      const float step = s_step[pr];
+      if (pr < np) a.hbuf[static_cast<size_t>(p0 + pr) * I + col] = silu(step * acc[0][i]) * (step * xch[i * 64]);
+    }
   }
 }
 
-// Down: work unit = (item, 64 rows of H). Writes W_d h of the block's rows for the item's pairs
-// into ybuf (by pair slot).
-static __global__ __launch_bounds__(kThreads) void pf_down_kernel(PfArgs a, int layer) {
+// Down: work unit = (item, 128 rows of H); wave w takes rows 32 (w & 3).. and pairs 32 (w >> 2)...
+// Writes W_d h of the block's rows for the item's pairs into ybuf (by pair slot).
+constexpr int kDownRows = 128;
+static __global__ __launch_bounds__(kGemmThreads) void pf_down_kernel(PfArgs a, int layer) {
   extern __shared__ uint32_t lds[];
   const int I = a.I, H = a.H;
-  const int tiles = H / kTile;
+  const int tiles = H / kDownRows;
   const int unit = xcd_unit(blockIdx.x, gridDim.x);
-  const int it = unit / tiles, h0 = (unit - it * tiles) * kTile;
+  const int it = unit / tiles, h0 = (unit - it * tiles) * kDownRows;
   if (it >= *a.n_items) return;
   const int4 item = a.items[it];
   const int e = item.x, p0 = item.y, np = item.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rh = wave & 1, ph = wave >> 1;
+  const int rq = wave & 3, ph = wave >> 2;
   __shared__ float s_step[kTile];
   const uint32_t* src = a.hq + static_cast<size_t>(p0 + min(lane, np - 1)) * (I / 32) * kXqWords;
   if (wave == 0) s_step[lane] = a.hstep[p0 + min(lane, np - 1)];  // visible after the first barrier
   const float* xs = a.hsum + static_cast<size_t>(p0 + min(32 * ph + (lane & 31), np - 1)) * (I / 32);
-  const size_t row = static_cast<size_t>(e) * H + h0 + 32 * rh;
+  const size_t row = static_cast<size_t>(e) * H + h0 + 32 * rq;
   const uint8_t* codes[1] = {a.w.down_q + row * (I / 2)};
   const uint32_t* sm[1] = {a.w.down_sm + row * (I / 32)};
   f32x16 acc[1];
   gemm_rows<1>(codes, sm, I, src, xs, ph, 32 * ph < np, lds, acc);
-  const int col = h0 + 32 * rh + (lane & 31);
+  const int col = h0 + 32 * rq + (lane & 31);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int pr = d_pair(ph, i);

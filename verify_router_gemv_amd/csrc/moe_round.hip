@@ -345,7 +345,7 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
   const int np = T * k;
   const int ib = pf_items_bound(np, E);
   const int gu_units = ((ib * (I / pf::kTile) + 7) / 8) * 8;
-  const int dn_units = ((ib * (H / pf::kTile) + 7) / 8) * 8;
+  const int dn_units = ((ib * (H / pf::kDownRows) + 7) / 8) * 8;
   const PfKernelFn topk = pf_pick_topk(E);
   int i = 0;
   auto launch = [&](const void* fn, dim3 grid, int threads, int shmem, void** params, int layer, int kind) {
@@ -376,12 +376,12 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
             hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::pf_scatter_kernel), dim3((np + kThreads - 1) / kThreads),
                     kThreads, 0, gp, l, 1)) != hipSuccess ||
-        (e = launch(reinterpret_cast<const void*>(pf::pf_gateup_kernel), dim3(gu_units), kThreads, pf::kGemmLds, gp,
-                    l, 2)) != hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(pf::pf_gateup_kernel), dim3(gu_units), pf::kGemmThreads,
+                    pf::kGemmLds, gp, l, 2)) != hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::quant_rows_kernel), dim3((np + kWaves - 1) / kWaves), kThreads,
                     0, qh, l, 3)) != hipSuccess ||
-        (e = launch(reinterpret_cast<const void*>(pf::pf_down_kernel), dim3(dn_units), kThreads, pf::kGemmLds, gp, l,
-                    3)) != hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(pf::pf_down_kernel), dim3(dn_units), pf::kGemmThreads,
+                    pf::kGemmLds, gp, l, 3)) != hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::pf_combine_kernel), dim3(T, (H + 4 * kThreads - 1) / (4 * kThreads)),
                     kThreads, 0, gp, l, 4)) != hipSuccess)
       return hip_fail(h, e);
