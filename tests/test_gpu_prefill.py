@@ -102,6 +102,41 @@ def test_prefill_4096_rows_sampled(prefill_layer):
     g.close()
 
 
+def test_prefill_largest_round():
+    """The largest prefill round: T = MOE_ROUND_MAX_PREFILL_ROWS = 16384, k = 16, E = 512 (262144
+    pairs: the counting sort's packed counters at their widest). Ids, routing weights and the
+    worklist of every row bit-exact / to fp32 rounding; outputs of 12 sampled rows."""
+    from verify_router_gemv_amd import binding
+    T = binding.MAX_PREFILL_ROWS
+    cfg = synth.ShapeConfig("prefill-max", H=2048, E=512, k=16, I=512, T=(T,), zipf_s=1.0)
+    layer = synth.make_layer(cfg, seed=1, layer=0, device=DEV)
+    view = oracle_view(layer)
+    g = GpuRound([layer], cfg, max_rows=T)
+    say(f"case prefill largest T={T} k={cfg.k} E={cfg.E}")
+    X = synth.make_activations(cfg, T, seed=18, round_idx=T, device=DEV)
+    out, ids, rw, _ = g.run(X, cfg.k)
+    Xh = X.cpu().numpy()
+    rids = np.zeros((T, cfg.k), dtype=np.int64)
+    rp = np.zeros((T, cfg.k))
+    for t in range(T):
+        z = oracle.router_logits(view["router_w"], view["router_b"], Xh[t])
+        rids[t] = oracle.select_topk(z, cfg.k)
+        rp[t] = oracle.routing_weights(z, rids[t])
+    assert np.array_equal(ids[0], rids)
+    np.testing.assert_allclose(rw[0], rp, rtol=2e-6, atol=1e-7)
+    uniq, offs, pairs = g.h.worklist(0)
+    eu, eo, ep = oracle.build_worklist(rids)
+    assert uniq == eu.tolist() and offs == eo.tolist()
+    assert np.array_equal(np.asarray(pairs), ep)
+    sample = np.array([0, 1, 777, 4095, 4096, 8191, 9000, 12345, 15000, 16000, T - 2, T - 1])
+    ref, _, _, _ = oracle.moe_layer(view, Xh[sample], cfg.k)
+    rel, mabs = assert_close(out[sample], ref, "prefill largest sampled rows")
+    say(f"  n_unique={len(uniq)} max pairs per expert={int(np.diff(offs).max())} rel-L2={rel:.2e}")
+    g.close()
+    del layer, view
+    torch.cuda.empty_cache()
+
+
 def test_prefill_rows_do_not_depend_on_the_round(prefill_layer):
     """Every pair's products depend only on its own row and expert, and the combine adds the ranks
     in order: rows 0..99 of a 300-row round equal a 100-row round of those rows bitwise, and so do
