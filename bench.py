@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--launch", default="", help="launch-shape fields for the verify sweep, e.g. fused_max_rows=4,rows_per_item=2")
     p.add_argument("--no-profile", dest="profile", action="store_false",
                    help="skip the kernel-timing pass (no roofline)")
+    p.add_argument("--prefill-only", type=int, default=0, metavar="T",
+                   help="only the prefill section, at T rows (for profiling it); prints its JSON")
     return p.parse_args()
 
 
@@ -76,6 +78,9 @@ def main():
     dev = "cuda:0"
     cfg = synth.config("verify")
     base = synth.make_layer(cfg, seed=0, layer=0, device=dev)
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_rounds(base, torch, np, synth, MoeRound, (args.prefill_only,))}), flush=True)
+        return
     reps = [base] + [base.clone() for _ in range(args.replicas - 1)]
     n_acts = 256
     acts = {T: torch.stack([synth.make_activations(cfg, T, seed=0, round_idx=r, device=dev)
@@ -371,15 +376,15 @@ VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
 PREFILL_FOLD_PEAK_OPS = VALU_LANE_OPS * 32 / 4 * 2
 
 
-def prefill_rounds(layer, torch, np, synth, MoeRound):
+def prefill_rounds(layer, torch, np, synth, MoeRound, widths=None):
     """Prefill rounds (T = 512, 4096 independent rows, the verify layer shape): rows per second,
     per-kernel time, and the gate/up GEMM's model rate against the fold-bound peak and the int8
     matrix-core peak (executed int8 work: three digit planes over 64-pair tiles)."""
     cfg = synth.config("prefill")
-    Tmax = max(cfg.T)
-    h = MoeRound([layer], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=Tmax, use_graph=False)
+    widths = tuple(widths or cfg.T)
+    h = MoeRound([layer], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(widths), use_graph=False)
     res = {}
-    for T in cfg.T:
+    for T in widths:
         xs = [synth.make_activations(cfg, T, seed=0, round_idx=r, device="cuda") for r in range(4)]
         out = torch.empty((T, cfg.H), device="cuda")
         for r in range(2):
