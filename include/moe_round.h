@@ -113,9 +113,8 @@ typedef struct moe_round_config {
                           depends on the other rows). Prefill rounds launch eagerly
                           (use_graph applies to rounds of up to 64 rows), ignore the
                           launch-shape fields and `exact` (their combine is always the
-                          fixed-order one), and need MOE_WEIGHT_Q4B32 (init returns
-                          MOE_ERR_UNSUPPORTED otherwise). Their scratch grows with
-                          max_rows * top_k_max * (4 H + 16 I) bytes.                  */
+                          fixed-order one) and read either weight format. Their scratch
+                          grows with max_rows * top_k_max * (4 H + 16 I) bytes.        */
   int32_t residual;    /* 0: out = MoE(x), needs L == 1; 1: x_{l+1} = x_l + MoE_l */
   int32_t use_graph;   /* 1: replay one captured hipGraph per (T, k); 0: eager    */
   /* Launch-shape choices (0 = the default for each; none changes results beyond fp32 rounding

@@ -71,6 +71,7 @@ def cfg(**kw):
     dict(H=2048, I=512, E=256, top_k_max=8, max_rows=4096),
     dict(H=768, I=384, E=40, top_k_max=5, max_rows=1000),
     dict(H=2048, I=512, E=512, top_k_max=10, n_layers=4, max_rows=16384, residual=True),
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=4096, raw_weight_format=1),  # prefill, 4.5-bit
 ])
 def test_supported_configs_validate(lib, kw):
     from verify_router_gemv_amd import binding
@@ -99,7 +100,6 @@ def test_supported_configs_validate(lib, kw):
     (dict(I=384, raw_weight_format=1), -2),   # super-blocks need I a multiple of 256
     (dict(H=256, I=128, E=8, top_k_max=2, raw_weight_format=1), -2),
     (dict(max_rows=16385), -2),
-    (dict(max_rows=65, raw_weight_format=1), -2),  # prefill reads Q4B32 weights only
     (dict(E=513, top_k_max=8), -2),
     (dict(top_k_max=17, E=256), -2),
     (dict(H=2080), -2),          # not a multiple of 256

@@ -102,6 +102,31 @@ def test_prefill_4096_rows_sampled(prefill_layer):
     g.close()
 
 
+def test_prefill_superblock_format():
+    """Prefill rounds on the 4.5-bit super-block layout (Q4S256): the prefill layer at T = 65 and
+    300, and a 3-layer residual stack (H=1024, I=256, E=64, k=4) at T = 100, every row against the
+    oracle."""
+    cfg = synth.config("prefill").replace(fmt="q4s256")
+    layer = synth.make_layer(cfg, seed=2, layer=0, device=DEV)
+    view = oracle_view(layer)
+    g = GpuRound([layer], cfg, max_rows=300)
+    for T in (65, 300):
+        say(f"case prefill q4s256 T={T}")
+        X = synth.make_activations(cfg, T, seed=19, round_idx=T, device=DEV)
+        rel, mabs, nu = check_layer_round(g, [view], X, cfg.k, f"prefill q4s256 T={T}")
+        say(f"  n_unique={nu[0]} rel-L2={rel:.2e}")
+    g.close()
+    scfg = synth.ShapeConfig("stack", H=1024, E=64, k=4, I=256, L=3, T=(100,), zipf_s=1.0, residual=True,
+                             fmt="q4s256")
+    layers = [synth.make_layer(scfg, seed=0, layer=l, device=DEV) for l in range(scfg.L)]
+    g = GpuRound(layers, scfg, max_rows=100)
+    say("case prefill q4s256 stack L=3 T=100")
+    X = synth.make_activations(scfg, 100, seed=20, round_idx=100, device=DEV)
+    rel, mabs, nu = check_layer_round(g, [oracle_view(l) for l in layers], X, scfg.k, "prefill q4s256 stack")
+    say(f"  n_unique per layer={nu} rel-L2={rel:.2e}")
+    g.close()
+
+
 def test_prefill_largest_round():
     """The largest prefill round: T = MOE_ROUND_MAX_PREFILL_ROWS = 16384, k = 16, E = 512 (262144
     pairs: the counting sort's packed counters at their widest). Ids, routing weights and the

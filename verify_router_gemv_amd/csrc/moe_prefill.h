@@ -25,6 +25,7 @@
 #pragma once
 
 #include "moe_common.h"
+#include "moe_gemv.h"
 #include "moe_route.h"
 
 namespace moe {
@@ -349,13 +350,40 @@ __device__ __forceinline__ i32x4v codes16(uint2 w) {
 // expert re-read its rows.
 struct StepCodes {
   u32x4 p, q;  // blocks kb0 + 2h and kb0 + 2h + 1 of this lane's row, as loaded
-  uint4 smw;   // scale/min words of blocks kb0..kb0+3
+  uint4 smw;   // Q4B32: the scale/min words of blocks kb0..kb0+3; Q4S256: the record of their
+               // super-block (a step of 4 blocks never crosses one)
 };
+template <int FMT>
 __device__ __forceinline__ void load_step_codes(const uint8_t* row, const uint32_t* smrow, int kb0, StepCodes& w) {
   const int h = (threadIdx.x & 63) >> 5;
   w.p = *reinterpret_cast<const u32x4*>(row + 16 * (kb0 + 2 * h));
   w.q = *reinterpret_cast<const u32x4*>(row + 16 * (kb0 + 2 * h + 1));
-  w.smw = *reinterpret_cast<const uint4*>(smrow + kb0);
+  w.smw = *reinterpret_cast<const uint4*>(smrow + (FMT == kFmtQ4S256 ? 4 * (kb0 >> 3) : kb0));
+}
+// Scale and minimum of block kb0 + bs from a step's words (bs may differ between lanes).
+template <int FMT>
+__device__ __forceinline__ float step_scale(const uint4& smw, int kb0, int bs) {
+  if constexpr (FMT == kFmtQ4S256) {
+    BlockScale<kFmtQ4S256> b;
+    b.r = smw;
+    b.j = (kb0 & 7) + bs;
+    return b.scale();
+  } else {
+    return half_bits_to_float(bs == 0 ? smw.x : bs == 1 ? smw.y : bs == 2 ? smw.z : smw.w);
+  }
+}
+template <int FMT>
+__device__ __forceinline__ float step_min(const uint4& smw, int kb0, int bs) {
+  if constexpr (FMT == kFmtQ4S256) {
+    BlockScale<kFmtQ4S256> b;
+    b.r = smw;
+    b.j = (kb0 & 7) + bs;
+    return b.minv();
+  } else {  // bs is 0/1 or 2/3 by half-wave: a select, not an indexed register
+    const uint32_t hm = 0u - static_cast<uint32_t>(bs & 1);
+    const uint32_t w = bs < 2 ? (smw.x ^ ((smw.x ^ smw.y) & hm)) : (smw.z ^ ((smw.z ^ smw.w) & hm));
+    return half_bits_to_float(w >> 16);
+  }
 }
 __device__ __forceinline__ void trade_halves(const StepCodes& w, uint2 (&cw)[kStepBlocks]) {
   // before: low half-wave p = block kb0 (lo, hi words), upper half-wave p = block kb0 + 2
@@ -378,13 +406,14 @@ __device__ __forceinline__ int xcd_unit(int bid, int nb) { return (bid & 7) * (n
 // block's 64 staged pairs (half ph). src: this lane's staging source row (pair lane % 64); xs: the
 // block sums of pair 32 ph + lane % 32. live = false (no pair of this half exists): the wave only
 // stages and waits. acc[m][i]: D element i, in units of the pair's step.
-template <int NM>
+template <int NM, int FMT>
 __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const uint32_t* const* sm0, int K,
                                           const uint32_t* src, const float* xs, int ph, bool live, uint32_t* lds,
                                           f32x16 (&acc)[NM]) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int nblk = K / 32, nstep = nblk / kStepBlocks;
+  const size_t rsm = sm_row_words<FMT>(K);
   live = __builtin_amdgcn_readfirstlane(static_cast<int>(live)) != 0;  // one value per wave
 #pragma unroll
   for (int m = 0; m < NM; ++m)
@@ -395,7 +424,8 @@ __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const ui
   float x2[2], nx2[2];
   if (live) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) load_step_codes(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + static_cast<size_t>(c) * nblk, 0, cur_w[m]);
+    for (int m = 0; m < NM; ++m)
+      load_step_codes<FMT>(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + c * rsm, 0, cur_w[m]);
     x2[0] = xs[h];
     x2[1] = xs[2 + h];
   }
@@ -411,8 +441,8 @@ __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const ui
     if (live && more) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
-        load_step_codes(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + static_cast<size_t>(c) * nblk,
-                        kb0 + kStepBlocks, nxt_w[m]);
+        load_step_codes<FMT>(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + c * rsm, kb0 + kStepBlocks,
+                             nxt_w[m]);
       nx2[0] = xs[kb0 + kStepBlocks + h];
       nx2[1] = xs[kb0 + kStepBlocks + 2 + h];
     }
@@ -430,9 +460,7 @@ __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const ui
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           const i32x4v b = codes16(cw[m][bs]);
-          const uint4 smw = cur_w[m].smw;
-          const uint32_t sw = bs == 0 ? smw.x : bs == 1 ? smw.y : bs == 2 ? smw.z : smw.w;
-          const float sc = half_bits_to_float(sw);
+          const float sc = step_scale<FMT>(cur_w[m].smw, kb0, bs);
           const i32x16v z = {};
           i32x16v d = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap[2], b, z, 0, 0, 0);
           d = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap[1], b, d << 8, 0, 0, 0);
@@ -445,10 +473,8 @@ __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const ui
       // folds: the next step's integer products then cover its latency before acc is needed again.
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const uint4 smw = cur_w[m].smw;
-        const uint32_t hm = 0u - static_cast<uint32_t>(h);  // all ones in the upper half-wave
-        const float m0 = half_bits_to_float((smw.x ^ ((smw.x ^ smw.y) & hm)) >> 16);
-        const float m1 = half_bits_to_float((smw.z ^ ((smw.z ^ smw.w) & hm)) >> 16);
+        const float m0 = step_min<FMT>(cur_w[m].smw, kb0, h);
+        const float m1 = step_min<FMT>(cur_w[m].smw, kb0, 2 + h);
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[0], m0, acc[m], 0, 0, 0);
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[1], m1, acc[m], 0, 0, 0);
       }
@@ -472,7 +498,8 @@ __device__ __forceinline__ int d_pair(int ph, int i) {
 // Gate/up: work unit = (item, 64 rows of I). Waves 0-3 take gate, 4-7 up (rows 32 (w & 1)..,
 // pairs 32 ((w >> 1) & 1)..); the up waves hand their sums to the gate waves through LDS, which
 // write silu(g) * v of the block's rows for the item's pairs into hbuf (by pair slot).
-static __global__ __launch_bounds__(kGemmThreads) void pf_gateup_kernel(PfArgs a, int layer) {
+template <int FMT>
+__global__ __launch_bounds__(kGemmThreads) void pf_gateup_kernel(PfArgs a, int layer) {
   extern __shared__ uint32_t lds[];
   const int I = a.I, H = a.H;
   const int tiles = I / kTile;
@@ -492,9 +519,9 @@ static __global__ __launch_bounds__(kGemmThreads) void pf_gateup_kernel(PfArgs a
   const float* xs = a.xsum + static_cast<size_t>(tsum) * (H / 32);
   const size_t row = static_cast<size_t>(e) * I + i0 + 32 * rh;  // the wave's first weight row
   const uint8_t* codes[1] = {(mt ? a.w.up_q : a.w.gate_q) + row * (H / 2)};
-  const uint32_t* sm[1] = {(mt ? a.w.up_sm : a.w.gate_sm) + row * (H / 32)};
+  const uint32_t* sm[1] = {(mt ? a.w.up_sm : a.w.gate_sm) + row * sm_row_words<FMT>(H)};
   f32x16 acc[1];
-  gemm_rows<1>(codes, sm, H, src, xs, ph, 32 * ph < np, lds, acc);
+  gemm_rows<1, FMT>(codes, sm, H, src, xs, ph, 32 * ph < np, lds, acc);
   // The staging buffers are free (the GEMM ends on a barrier): up sums [rh][ph][i][lane].
   float* xch = reinterpret_cast<float*>(lds) + ((rh * 2 + ph) * 16) * 64 + lane;
   if (mt == 1) {
@@ -516,7 +543,8 @@ static __global__ __launch_bounds__(kGemmThreads) void pf_gateup_kernel(PfArgs a
 // Down: work unit = (item, 128 rows of H); wave w takes rows 32 (w & 3).. and pairs 32 (w >> 2)...
 // Writes W_d h of the block's rows for the item's pairs into ybuf (by pair slot).
 constexpr int kDownRows = 128;
-static __global__ __launch_bounds__(kGemmThreads) void pf_down_kernel(PfArgs a, int layer) {
+template <int FMT>
+__global__ __launch_bounds__(kGemmThreads) void pf_down_kernel(PfArgs a, int layer) {
   extern __shared__ uint32_t lds[];
   const int I = a.I, H = a.H;
   const int tiles = H / kDownRows;
@@ -533,9 +561,9 @@ static __global__ __launch_bounds__(kGemmThreads) void pf_down_kernel(PfArgs a, 
   const float* xs = a.hsum + static_cast<size_t>(p0 + min(32 * ph + (lane & 31), np - 1)) * (I / 32);
   const size_t row = static_cast<size_t>(e) * H + h0 + 32 * rq;
   const uint8_t* codes[1] = {a.w.down_q + row * (I / 2)};
-  const uint32_t* sm[1] = {a.w.down_sm + row * (I / 32)};
+  const uint32_t* sm[1] = {a.w.down_sm + row * sm_row_words<FMT>(I)};
   f32x16 acc[1];
-  gemm_rows<1>(codes, sm, I, src, xs, ph, 32 * ph < np, lds, acc);
+  gemm_rows<1, FMT>(codes, sm, I, src, xs, ph, 32 * ph < np, lds, acc);
   const int col = h0 + 32 * rq + (lane & 31);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {

@@ -347,6 +347,9 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
   const int gu_units = ((ib * (I / pf::kTile) + 7) / 8) * 8;
   const int dn_units = ((ib * (H / pf::kDownRows) + 7) / 8) * 8;
   const PfKernelFn topk = pf_pick_topk(E);
+  const bool s256 = h->cfg.weight_format == MOE_WEIGHT_Q4S256;
+  const PfKernelFn gateup = s256 ? pf::pf_gateup_kernel<kFmtQ4S256> : pf::pf_gateup_kernel<kFmtQ4B32>;
+  const PfKernelFn down = s256 ? pf::pf_down_kernel<kFmtQ4S256> : pf::pf_down_kernel<kFmtQ4B32>;
   int i = 0;
   auto launch = [&](const void* fn, dim3 grid, int threads, int shmem, void** params, int layer, int kind) {
     if (kinds) kinds[i] = layer * kKernelsPerLayer + kind;
@@ -376,11 +379,11 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
             hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::pf_scatter_kernel), dim3((np + kThreads - 1) / kThreads),
                     kThreads, 0, gp, l, 1)) != hipSuccess ||
-        (e = launch(reinterpret_cast<const void*>(pf::pf_gateup_kernel), dim3(gu_units), pf::kGemmThreads,
+        (e = launch(reinterpret_cast<const void*>(gateup), dim3(gu_units), pf::kGemmThreads,
                     pf::kGemmLds, gp, l, 2)) != hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::quant_rows_kernel), dim3((np + kWaves - 1) / kWaves), kThreads,
                     0, qh, l, 3)) != hipSuccess ||
-        (e = launch(reinterpret_cast<const void*>(pf::pf_down_kernel), dim3(dn_units), pf::kGemmThreads,
+        (e = launch(reinterpret_cast<const void*>(down), dim3(dn_units), pf::kGemmThreads,
                     pf::kGemmLds, gp, l, 3)) != hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::pf_combine_kernel), dim3(T, (H + 4 * kThreads - 1) / (4 * kThreads)),
                     kThreads, 0, gp, l, 4)) != hipSuccess)

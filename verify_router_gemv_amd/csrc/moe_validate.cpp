@@ -37,8 +37,6 @@ moe_status validate_config(const moe_round_config* c) {
   if (c->weight_format != MOE_WEIGHT_Q4B32 && c->weight_format != MOE_WEIGHT_Q4S256) return MOE_ERR_INVALID_ARG;
   if (c->top_k_max > c->n_experts) return MOE_ERR_INVALID_ARG;
   if (c->max_rows > MOE_ROUND_MAX_PREFILL_ROWS) return MOE_ERR_UNSUPPORTED;
-  // prefill rounds (more than MOE_ROUND_MAX_ROWS rows) read Q4B32 weights only
-  if (c->max_rows > MOE_ROUND_MAX_ROWS && c->weight_format != MOE_WEIGHT_Q4B32) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts > MOE_ROUND_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
   if (c->top_k_max > MOE_ROUND_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (c->hidden % 256 != 0 || c->hidden > 8192) return MOE_ERR_UNSUPPORTED;
