@@ -12,7 +12,7 @@
 //                       ascending within one); the caller's ids and routing weights
 //   pf_gateup_kernel    per work item and 64 rows of I: silu(W_g x) * (W_u x) as an int8 GEMM
 //   quant_rows_kernel   the SwiGLU rows as digits
-//   pf_down_kernel      per work item and 64 rows of H: W_d h per pair, into a slot buffer
+//   pf_down_kernel      per work item and 128 rows of H: W_d h per pair, into a slot buffer
 //   pf_combine_kernel   each row adds its k products in rank order (and the residual)
 //
 // The infero README, "Beyond plain text decode", routes prefill through a counting sort followed
@@ -307,8 +307,9 @@ static __global__ __launch_bounds__(kThreads) void pf_scatter_kernel(PfArgs a, i
 // same D layout), and each pair's step multiplies its total at the end.
 //
 // Block tile: 64 pairs by 64 rows of gate and of up (gate/up) or by 128 rows (down), eight waves
-// of 32 rows x 32 pairs of one matrix each (at most 128 VGPRs: four waves per SIMD). The 64 pairs' digits of each 4-block step go through LDS (double-buffered, one barrier per step)
-// in [block][plane][half][pair][16 bytes] order, so a lane reads its 16 bytes next to its
+// of 32 rows x 32 pairs of one matrix each (at most 128 VGPRs: four waves per SIMD). The 64 pairs'
+// digits of each 4-block step go through LDS (double-buffered, one barrier per step) in
+// [block][plane][half][pair][16 bytes] order, so a lane reads its 16 bytes next to its
 // neighbours'. The next step's digits are loaded into registers while the current step computes
 // and written to LDS after it: LDS DMA loads would make the compiler wait for them before the
 // step's first LDS read, as it cannot tell the two buffers apart. Pairs past the item's last
