@@ -220,8 +220,9 @@ def test_many_rows_share_experts(verify):
 def test_tied_logits_go_to_the_lower_id(verify, k):
     """Router rows duplicated in pairs, so experts 2m and 2m+1 get bitwise equal logits. Every
     selection path (the one-row worklist, the selection folded into gate/up, the selection kernel,
-    ragged T) orders a tied pair lower id first, and a pair cut at rank k keeps the lower id: the
-    ids match the oracle's stable order, and the rule is also checked on the ids directly."""
+    ragged T, a prefill round) orders a tied pair lower id first, and a pair cut at rank k keeps
+    the lower id: the ids match the oracle's stable order, and the rule is also checked on the ids
+    directly."""
     cfg, layer, _ = verify
     rw = layer.router_w.clone()
     rw[1::2] = rw[0::2]
@@ -231,8 +232,8 @@ def test_tied_logits_go_to_the_lower_id(verify, k):
         rb[1::2] = rb[0::2]
     tied = dataclasses.replace(layer, router_w=rw, router_b=rb)
     view = oracle_view(tied)
-    g = GpuRound([tied], cfg, max_rows=64)
-    for T in (1, 3, 8, 24, 37):
+    g = GpuRound([tied], cfg, max_rows=130)
+    for T in (1, 3, 8, 24, 37, 130):
         say(f"case tied logits k={k} T={T}")
         X = synth.make_activations(cfg, T, seed=8, round_idx=T, device=DEV)
         z = oracle.router_logits(view["router_w"], view["router_b"], X[0].cpu().numpy())
