@@ -412,8 +412,10 @@ def prefill_rounds(layer, torch, np, synth, MoeRound, widths=None):
             "kernel_us": {n: round(float(v) * 1e3, 1) for n, v in
                           zip(("quant_x+logits", "topk+sort", "gateup", "quant_h+down", "combine"), kms)},
             "model_TOPs_round": round((gu_model + dn_model) / med / 1e6, 1),
-            "gateup": {"model_TOPs": round(gu_model / gu_s / 1e12, 1),
-                       "frac_of_fold_peak": round(gu_model / gu_s / PREFILL_FOLD_PEAK_OPS, 3),
+            "gateup": {"bound": "alu", "achieved": round(gu_model / gu_s / 1e12, 1),
+                       "peak": round(PREFILL_FOLD_PEAK_OPS / 1e12, 1), "unit": "TOP/s (model ops)",
+                       "frac": round(gu_model / gu_s / PREFILL_FOLD_PEAK_OPS, 3),
+                       "avg_launch_us": round(float(kms[2]) * 1e3, 1),
                        "int8_mfma_util": round(gu_exec / gu_s / INT8_DENSE_PEAK_OPS, 3)},
         }
         del xs
