@@ -55,6 +55,32 @@ def test_prefill_verify_shape_all_rows(prefill_layer, k):
     g.close()
 
 
+def test_prefill_gateup_stage(prefill_layer):
+    """The prefill gate/up stage alone: silu(W_g x) * (W_u x) per pair slot (read back through
+    moe_round_swiglu_rows) against the oracle, at T = 200 (every pair slot of the round)."""
+    cfg, layer, view = prefill_layer
+    T = 200
+    g = GpuRound([layer], cfg, max_rows=T)
+    say(f"case prefill gate/up stage T={T}")
+    X = synth.make_activations(cfg, T, seed=21, round_idx=T, device=DEV)
+    out, ids, _, _ = g.run(X)
+    h = g.h.swiglu_rows(T, cfg.k)
+    uniq, offs, pairs = g.h.worklist(0)
+    Xh = X.cpu().numpy().astype(np.float64)
+    ref = np.zeros_like(h, dtype=np.float64)
+    mats = {}
+    for p, (t, j) in enumerate(pairs):
+        e = int(ids[0, t, j])
+        if e not in mats:
+            mats[e] = oracle.expert_matrices(view["gate_q"][e], view["gate_sm"][e], view["up_q"][e],
+                                             view["up_sm"][e], view["down_q"][e], view["down_sm"][e])
+        Wg, Wu, _ = mats[e]
+        ref[p] = oracle.silu(Wg @ Xh[t]) * (Wu @ Xh[t])
+    rel, _ = assert_close(h, ref, f"prefill gate/up T={T}")
+    say(f"  rel-L2={rel:.2e}")
+    g.close()
+
+
 def test_prefill_hot_experts_split_into_items():
     """Zipf-biased routing (E=128, k=8, I=768) at T=600: popular experts get several hundred rows,
     so their pairs span several 64-pair work items."""
