@@ -187,6 +187,47 @@ static __global__ __launch_bounds__(kThreads) void pf_logits_kernel(PfArgs a, in
   }
 }
 
+// The same product with the reduction split over the block's four waves (for rounds too small to
+// fill the chip with one wave per 16 x 16 tile): grid (ceil(E / 16), ceil(T / 16)); wave w sums
+// h in [w H / 4, (w + 1) H / 4) and wave 0 adds the four partial sums in wave order.
+static __global__ __launch_bounds__(kThreads) void pf_logits_splitk_kernel(PfArgs a, int layer) {
+  __shared__ f64x4 part[kWaves - 1][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, q = lane >> 4;
+  const int E = a.E, T = a.T, H = a.H;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int hq = H / kWaves;  // a multiple of 64
+  const float* x = pf_layer_input(a, layer);
+  const float* wr = a.w.router_w + static_cast<size_t>(min(e0 + c, E - 1)) * H + wave * hq + 4 * q;
+  const float* xr = x + static_cast<size_t>(min(t0 + c, T - 1)) * H + wave * hq + 4 * q;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+  for (int h0 = 0; h0 < hq; h0 += 16) {
+    const float4 wv = load_stream_f4(wr + h0);
+    const float4 xv = load_f4(xr + h0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv.x), static_cast<double>(xv.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv.y), static_cast<double>(xv.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv.z), static_cast<double>(xv.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv.w), static_cast<double>(xv.w), acc, 0, 0, 0);
+  }
+  if (wave > 0) part[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < kWaves - 1; ++w) acc += part[w][lane];
+  const int t = t0 + c;
+  if (t < T) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + q + 4 * i;
+      if (e < E) {
+        const double b = a.w.router_bias ? static_cast<double>(a.w.router_bias[e]) : 0.0;
+        a.logits[static_cast<size_t>(t) * E + e] = acc[i] + b;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Top-k per row (one wave each, the decode path's routine), then the row's bit in the mask of
 // each chosen expert. Grid: ceil(T / 4) x 256 threads.
