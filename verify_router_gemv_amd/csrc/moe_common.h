@@ -75,6 +75,8 @@ struct Args {
   float* hbuf;        // [Pcap][I]
   float* ybuf;        // exact mode: [Pcap][H] down products W_d h per pair slot
   int32_t* slot_of;   // [L][Pcap] pair slot of (row t, rank j) at t * k + j
+  int32_t* tsel;      // [Pcap] wide rounds: expert ids by (row, rank) from the top-k kernel
+  float* tp;          // [Pcap] and their routing weights
   uint32_t* xq;       // [T_max][H/32][kXqWords] int8 digits of the layer input, per 32-block
   float2* xss;        // [T_max][H/32] (digit step, block sum) of the layer input
   int32_t H, I, E, L, T, k, residual, Ucap, Pcap;

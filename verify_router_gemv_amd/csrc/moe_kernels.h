@@ -112,12 +112,21 @@ inline KernelFn pick_logits(int H, int T) { return logits_rows(T) == 1 ? pick_lo
 // Keys per lane of the fused selection in the gate/up kernel (E <= 512).
 inline int fused_select_keys(int E) { return E <= 256 ? 4 : 8; }
 
-inline KernelFn pick_select(int E) {
-  if (E <= 64) return select_kernel<1>;
-  if (E <= 128) return select_kernel<2>;
-  if (E <= 256) return select_kernel<4>;
-  return select_kernel<8>;
+// presel: the round's top-k runs in topk_rows_kernel (pick_topk_rows) before the select kernel.
+inline KernelFn pick_select(int E, bool presel) {
+  if (E <= 64) return presel ? select_kernel<1, true> : select_kernel<1>;
+  if (E <= 128) return presel ? select_kernel<2, true> : select_kernel<2>;
+  if (E <= 256) return presel ? select_kernel<4, true> : select_kernel<4>;
+  return presel ? select_kernel<8, true> : select_kernel<8>;
 }
+inline KernelFn pick_topk_rows(int E) {
+  if (E <= 64) return topk_rows_kernel<1>;
+  if (E <= 128) return topk_rows_kernel<2>;
+  if (E <= 256) return topk_rows_kernel<4>;
+  return topk_rows_kernel<8>;
+}
+// Rounds of at least this many rows run the top-k as its own many-block kernel.
+constexpr int kSplitTopkRows = 32;
 
 // Rounds of at least this many rows are "wide": gate/up stages the input digits in LDS and may use
 // the matrix-core tile.

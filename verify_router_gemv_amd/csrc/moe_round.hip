@@ -68,6 +68,8 @@ struct moe_round {
   float* hbuf = nullptr;
   float* ybuf = nullptr;               // exact mode: [Pcap][H]
   int32_t* slot_of = nullptr;          // [L][Pcap]
+  int32_t* tsel = nullptr;             // [Pcap] wide rounds: top-k ids by (row, rank)
+  float* tp = nullptr;                 // [Pcap] and their routing weights
   uint32_t* xq = nullptr;
   float2* xss = nullptr;
   // host state
@@ -167,6 +169,8 @@ static Args base_args(const moe_round* h, int T, int k) {
   a.hbuf = h->hbuf;
   a.ybuf = h->ybuf;
   a.slot_of = h->slot_of;
+  a.tsel = h->tsel;
+  a.tp = h->tp;
   a.exact = h->cfg.exact;
   a.xq = h->xq;
   a.xss = h->xss;
@@ -194,7 +198,8 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   const int umax = items_bound(T * k, E, rows_per_item(h, T));
   const bool wide = T >= kWideRows;
   const bool fused = T <= h->fused_max_rows;
-  KernelFn lg = pick_logits(H, T), sel = pick_select(E), gu = nullptr, dn = nullptr;
+  const bool split_topk = T >= kSplitTopkRows;
+  KernelFn lg = pick_logits(H, T), sel = pick_select(E, split_topk), gu = nullptr, dn = nullptr;
   int rows_gu = 0, rows_dn = 0;
   const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
   const int fmt = h->cfg.weight_format;
@@ -213,6 +218,7 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   out->clear();
   for (int l = 0; l < h->cfg.n_layers; ++l) {
     out->push_back({lg, grid_lg, kThreads, 0, l, 0});
+    if (split_topk) out->push_back({pick_topk_rows(E), dim3((T + kWaves - 1) / kWaves), kThreads, 0, l, 1});
     if (!fused) out->push_back({sel, dim3(1), kSelectThreads, 0, l, 1});
     out->push_back({gu, grid_gu, kThreads, shm_gu, l, 2});
     out->push_back({dn, grid_dn, kThreads, shm_dn, l, 3});
@@ -462,7 +468,7 @@ static void free_handle(moe_round* h) {
     if (h->slot_ev[i]) (void)hipEventDestroy(h->slot_ev[i]);
   if (h->staging) (void)hipHostFree(h->staging);
   void* ptrs[] = {h->d_ing, h->d_wtab, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique, h->uniq, h->offs,
-                  h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->xq, h->xss,
+                  h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->tsel, h->tp, h->xq, h->xss,
                   h->pf_xbuf[0], h->pf_xbuf[1], h->pf_xq, h->pf_xstep, h->pf_xsum, h->pf_mask, h->pf_wpre,
                   h->pf_sel, h->pf_selp, h->pf_uniq, h->pf_offs, h->pf_eoff, h->pf_pairs, h->pf_pair_w, h->pf_slot_of,
                   h->pf_items, h->pf_n_items, h->pf_hbuf, h->pf_hq, h->pf_hstep, h->pf_hsum, h->pf_ybuf};
@@ -519,6 +525,8 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   MOE_ALLOC(h->rec, sizeof(int32_t) * L * h->Icap * kRecWords);
   MOE_ALLOC(h->hbuf, sizeof(float) * h->Pcap * I);
   MOE_ALLOC(h->slot_of, sizeof(int32_t) * L * h->Pcap);
+  MOE_ALLOC(h->tsel, sizeof(int32_t) * h->Pcap);
+  MOE_ALLOC(h->tp, sizeof(float) * h->Pcap);
   if (cfg->exact) MOE_ALLOC(h->ybuf, sizeof(float) * h->Pcap * H);
   MOE_ALLOC(h->xq, sizeof(uint32_t) * T * (H / 32) * kXqWords);
   MOE_ALLOC(h->xss, sizeof(float2) * T * (H / 32));

@@ -167,7 +167,9 @@ __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
 // expert and at most a.rg of its rows). Results stay in `s`; with `publish` the block also writes
 // the per-item records, the unique list, pair table and pair weights, and the caller's ids and
 // routing weights. Deterministic: every block computing it gets the same result.
-template <int NPL, int NT, bool ONE_ROW = false, typename SS>
+// PRESEL: the rows' top-k already ran (topk_rows_kernel); their ids and weights are read from
+// a.tsel / a.tp instead of computed here.
+template <int NPL, int NT, bool ONE_ROW = false, bool PRESEL = false, typename SS>
 __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bool publish) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -205,7 +207,14 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
     ni = s.ni;
   } else {
     for (int e = tid; e < E; e += NT) s.mask[e] = 0ull;
-    for (int t = wave; t < T; t += NW) select_row<NPL>(a, s, t);
+    if constexpr (PRESEL) {
+      for (int idx = tid; idx < npairs; idx += NT) {
+        s.sel[idx] = min(max(a.tsel[idx], 0), E - 1);
+        s.p[idx] = a.tp[idx];
+      }
+    } else {
+      for (int t = wave; t < T; t += NW) select_row<NPL>(a, s, t);
+    }
     __syncthreads();
 
     for (int idx = tid; idx < npairs; idx += NT) atomicOr(&s.mask[s.sel[idx]], 1ull << (idx / k));
@@ -331,10 +340,28 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
   if (tid == 0) a.n_unique[layer] = nu;
 }
 
-template <int NPL>
+template <int NPL, bool PRESEL = false>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(Args a, int layer) {
   __shared__ SelectShared s;
-  select_block<NPL, kSelectThreads>(a, layer, s, true);
+  select_block<NPL, kSelectThreads, false, PRESEL>(a, layer, s, true);
+}
+
+// Wide rounds: the rows' top-k on many CUs, one wave per row (the one-block selection's top-k is
+// bound by that block's one CU from about 16 rows on), into a.tsel / a.tp for the select kernel.
+// Grid: ceil(T / 4) x 256 threads.
+template <int NPL>
+__global__ __launch_bounds__(kThreads) void topk_rows_kernel(Args a, int layer) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (t >= a.T) return;  // whole waves leave together
+  const int k = a.k;
+  int id;
+  float p;
+  topk_row<NPL>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p);
+  if (lane < k) {
+    a.tsel[t * k + lane] = id;
+    a.tp[t * k + lane] = p;
+  }
 }
 
 // Every GEMV block reads its work item's record and record 0 (whose item count is always valid)
