@@ -218,6 +218,28 @@ def test_prefill_residual_stack():
     g.close()
 
 
+def test_prefill_profiling(prefill_layer):
+    """Kernel timing of prefill rounds: the nine launches of a layer fold into the five kinds
+    (digits + logits, top-k + sort, gate/up, SwiGLU digits + down, combine), every kind timed, and
+    the run count matches; the outputs equal an unprofiled run's bitwise."""
+    cfg, layer, _ = prefill_layer
+    g = GpuRound([layer], cfg, max_rows=300)
+    say("case prefill profiling T=300")
+    X = synth.make_activations(cfg, 300, seed=22, round_idx=300, device=DEV)
+    plain = g.run(X)[0]
+    g.h.profile(True)
+    g.h.profile_read()
+    outs = [g.run(X)[0] for _ in range(3)]
+    ms, runs = g.h.profile_read()
+    g.h.profile(False)
+    assert runs == 3
+    assert all(v > 0 for v in ms[0]), ms
+    for o in outs:
+        assert np.array_equal(o, plain)
+    say(f"  ms per kind over 3 runs: {[round(v, 3) for v in ms[0]]}")
+    g.close()
+
+
 def test_prefill_then_verify_rounds_on_one_handle(prefill_layer):
     """One handle serves a prefill round, then verify rounds (graph replay), then prefill again."""
     cfg, layer, view = prefill_layer
