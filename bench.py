@@ -56,6 +56,8 @@ def gateup_bytes(cfg, n_unique, T):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_kernel_verify_sweep_traffic.txt")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_gateup_T4096_traffic.txt")
+PREFILL_TRAFFIC_T = 4096
 CALIB_BYTES = 1 << 30
 
 
@@ -80,6 +82,8 @@ def main():
     base = synth.make_layer(cfg, seed=0, layer=0, device=dev)
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_rounds(base, torch, np, synth, MoeRound, (args.prefill_only,))}), flush=True)
+        if args.pmc_calibrate:
+            calibration_copy(torch, dev)
         return
     reps = [base] + [base.clone() for _ in range(args.replicas - 1)]
     n_acts = 256
@@ -248,12 +252,17 @@ def main():
     }
     print(json.dumps(line), flush=True)
     if args.pmc_calibrate:
-        src = torch.randn(CALIB_BYTES // 4, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
+        calibration_copy(torch, dev)
+
+
+def calibration_copy(torch, dev):
+    """A copy of CALIB_BYTES in and out (torch.neg of fp32), whose byte counters scale the kernels'."""
+    src = torch.randn(CALIB_BYTES // 4, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
 
 
 INT8_DENSE_PEAK_OPS = 5.0e15
@@ -380,6 +389,8 @@ def prefill_rounds(layer, torch, np, synth, MoeRound, widths=None):
     """Prefill rounds (T = 512, 4096 independent rows, the verify layer shape): rows per second,
     per-kernel time, and the gate/up GEMM's model rate against the fold-bound peak and the int8
     matrix-core peak (executed int8 work: three digit planes over 64-pair tiles)."""
+    from verify_router_gemv_amd.profsum import read_traffic
+
     cfg = synth.config("prefill")
     widths = tuple(widths or cfg.T)
     h = MoeRound([layer], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(widths), use_graph=False)
@@ -416,7 +427,9 @@ def prefill_rounds(layer, torch, np, synth, MoeRound, widths=None):
                        "peak": round(PREFILL_FOLD_PEAK_OPS / 1e12, 1), "unit": "TOP/s (model ops)",
                        "frac": round(gu_model / gu_s / PREFILL_FOLD_PEAK_OPS, 3),
                        "avg_launch_us": round(float(kms[2]) * 1e3, 1),
-                       "int8_mfma_util": round(gu_exec / gu_s / INT8_DENSE_PEAK_OPS, 3)},
+                       "int8_mfma_util": round(gu_exec / gu_s / INT8_DENSE_PEAK_OPS, 3),
+                       "traffic": (read_traffic(PREFILL_TRAFFIC_FILE, "pf_gateup")
+                                   if T == PREFILL_TRAFFIC_T else None)},
         }
         del xs
     h.close()

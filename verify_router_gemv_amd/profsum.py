@@ -3,10 +3,11 @@
     python -m verify_router_gemv_amd.profsum stats  STATS_CSV OUT "COMMAND"
         per-kernel dispatch durations (calls, average, min, max) of the moe:: kernels from a
         `rocprofv3 --kernel-trace --stats` *_kernel_stats.csv
-    python -m verify_router_gemv_amd.profsum traffic FETCH_DIR WRITE_DIR OUT "COMMAND"
+    python -m verify_router_gemv_amd.profsum traffic FETCH_DIR WRITE_DIR OUT "COMMAND" [KERNEL]
         gate/up HBM traffic per dispatch from a FETCH_SIZE pass and a WRITE_SIZE pass of
         `bench.py --pmc-calibrate`, each scaled by its own reading for the run's closing copy of
-        CALIB_BYTES in and out (torch.neg of a 1 GiB fp32 tensor)
+        CALIB_BYTES in and out (torch.neg of a 1 GiB fp32 tensor). KERNEL is "gateup" (the decode
+        gate/up, default) or "pf_gateup" (the prefill gate/up GEMM).
 """
 from __future__ import annotations
 
@@ -20,18 +21,29 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CALIB_BYTES = 1 << 30
 KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in
                   ("moe_common.h", "moe_route.h", "moe_gemv.h", "moe_gateup.h", "moe_gemv_g64.hip")]
+PREFILL_SOURCES = [os.path.join(PKG, "csrc", f) for f in
+                   ("moe_common.h", "moe_route.h", "moe_gemv.h", "moe_prefill.h")]
+
+# Traffic targets: the kernel-name prefix a dispatch must carry, the sources its code comes from,
+# and the workload line of the summary.
+TRAFFIC_KERNELS = {
+    "gateup": ("moe::gateup_kernel<", KERNEL_SOURCES,
+               "gate/up HBM traffic per dispatch, verify sweep (T = 1, 3, 8; 32 weight replicas)"),
+    "pf_gateup": ("moe::pf::pf_gateup_kernel<", PREFILL_SOURCES,
+                  "prefill gate/up GEMM HBM traffic per dispatch (T = 4096 rows, top-8, E = 256)"),
+}
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources the gate/up kernel is compiled from (a traffic figure is valid for these)."""
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the sources a kernel is compiled from (a traffic figure is valid for these)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(path: str):
+def read_traffic(path: str, kernel: str = "gateup"):
     """traffic_bytes_per_launch of a traffic summary if it was taken on the current kernel sources."""
     try:
         kv = {}
@@ -41,7 +53,7 @@ def read_traffic(path: str):
                 kv[k.strip()] = v.strip()
     except OSError:
         return None
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(TRAFFIC_KERNELS[kernel][1]):
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
 
@@ -76,14 +88,14 @@ VERIFY_SWEEP_GATEUP = ("gateup_kernel<64, 1, 4, 0, 4, 0>", "gateup_kernel<64, 1,
                        "gateup_kernel<64, 1, 4, 1, 0, 0>")
 
 
-def _per_dispatch(d: str, counter: str):
+def _per_dispatch(d: str, counter: str, prefix: str):
     acc = {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r.get("Counter_Name") != counter:
                 continue
             name = r["Kernel_Name"]
-            key = "gateup" if "gateup_kernel" in name else ("copy" if "neg_kernel" in name else None)
+            key = "gateup" if prefix in name else ("copy" if "neg_kernel" in name else None)
             if key:
                 disp = acc.setdefault(key, {})
                 did = r["Dispatch_Id"]
@@ -91,19 +103,20 @@ def _per_dispatch(d: str, counter: str):
     return {k: sum(v.values()) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
-def traffic(fetch_dir: str, write_dir: str, out_path: str, command: str) -> None:
-    fetch, nf = _per_dispatch(fetch_dir, "FETCH_SIZE")
-    write, nw = _per_dispatch(write_dir, "WRITE_SIZE")
+def traffic(fetch_dir: str, write_dir: str, out_path: str, command: str, kernel: str = "gateup") -> None:
+    prefix, sources, title = TRAFFIC_KERNELS[kernel]
+    fetch, nf = _per_dispatch(fetch_dir, "FETCH_SIZE", prefix)
+    write, nw = _per_dispatch(write_dir, "WRITE_SIZE", prefix)
     f_scale = CALIB_BYTES / (fetch["copy"] * 1024.0)
     w_scale = CALIB_BYTES / (write["copy"] * 1024.0)
     rd = fetch["gateup"] * 1024.0 * f_scale
     wr = write["gateup"] * 1024.0 * w_scale
     with open(out_path, "w") as fh:
-        fh.write("# gate/up HBM traffic per dispatch, verify sweep (T = 1, 3, 8; 32 weight replicas)\n"
+        fh.write(f"# {title}\n"
                  f"# command: {command}\n"
                  "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) come from two rocprofv3 --pmc passes; each is\n"
                  f"# scaled by its own reading for the closing copy of {CALIB_BYTES} bytes in and out.\n"
-                 f"kernel_source_sha256_16: {kernel_source_hash()}\n"
+                 f"kernel_source_sha256_16: {kernel_source_hash(sources)}\n"
                  f"gateup_dispatches: {nf['gateup']} / {nw['gateup']}\n"
                  f"fetch_kib_per_dispatch_raw: {fetch['gateup']:.1f}\n"
                  f"write_kib_per_dispatch_raw: {write['gateup']:.1f}\n"
