@@ -107,9 +107,10 @@ typedef struct moe_round_config {
                           are decode/verify rounds; rounds of more rows take the prefill
                           path: per layer, a counting sort of the (row, rank) pairs into
                           work items of up to 64 pairs of one expert, then gate/up and
-                          down as int8 matrix-core GEMMs over each item (activations as
-                          22-bit integers in three int8 planes, block scales folded in
-                          fp32), and a combine in rank order (so a row's output never
+                          down as fp16 matrix-core GEMMs over each item (each activation
+                          row scaled by a power of two and split into two fp16 values,
+                          22 significant bits; block scales folded in fp32), and a
+                          combine in rank order (so a row's output never
                           depends on the other rows). Prefill rounds launch eagerly
                           (use_graph applies to rounds of up to 64 rows), ignore the
                           launch-shape fields and `exact` (their combine is always the

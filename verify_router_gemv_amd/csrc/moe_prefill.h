@@ -1,8 +1,8 @@
 // Prefill MoE: rounds of more than 64 rows, where the expert FFN is compute-bound.
 //
 // Per layer nine kernels, launched eagerly:
-//   quant_rows_kernel   the layer input as 22-bit integers per row (three int8 digit planes) and
-//                       per-32-block sums, for the int8 matrix cores
+//   quant_rows_kernel   the layer input, scaled per row by a power of two, as pairs of fp16 values
+//                       (hi + lo) and per-32-block sums, for the fp16 matrix cores
 //   pf_logits_kernel    router GEMM on fp64 matrix cores (fp32 inputs, fp64 products and sums)
 //   pf_topk_kernel      one wave per row: top-k, softmax over the selected, and the row's bit in
 //                       each chosen expert's row mask
@@ -10,17 +10,18 @@
 //                       64-pair work items
 //   pf_scatter_kernel   counting sort of the (row, rank) pairs by expert (ascending expert, rows
 //                       ascending within one); the caller's ids and routing weights
-//   pf_gateup_kernel    per work item and 64 rows of I: silu(W_g x) * (W_u x) as an int8 GEMM
-//   quant_rows_kernel   the SwiGLU rows as digits
+//   pf_gateup_kernel    per work item and 64 rows of I: silu(W_g x) * (W_u x) as an fp16 GEMM
+//   quant_rows_kernel   the SwiGLU rows as fp16 pairs
 //   pf_down_kernel      per work item and 128 rows of H: W_d h per pair, into a slot buffer
 //   pf_combine_kernel   each row adds its k products in rank order (and the residual)
 //
 // The infero README, "Beyond plain text decode", routes prefill through a counting sort followed
 // by a GEMM per expert; its "Design notes" run batched projections straight off the quantised
-// weights on integer matrix instructions, one instruction per 32-weight block, with the block
-// scales applied in float afterwards. Here the activations are 22-bit integers split into three
-// int8 planes, so the int32 block products are exact and the fp32 fold keeps the round within the
-// fp32-accumulation tolerance of the decode path; the block minimum's term sum_b m * sum(x) runs
+// weights on matrix instructions, per 32-weight block, with the block scales applied in float
+// afterwards. Here each activation is split into two fp16 values, hi + lo, after a power-of-two
+// scaling of its row, which keeps 22 significant bits; the 4-bit codes are exact in fp16, so each
+// block product is an fp32 sum of exact products and the fp32 fold keeps the round within the
+// fp32-accumulation tolerance of the decode path. The block minimum's term sum_b m * sum(x) runs
 // on fp32 matrix instructions.
 #pragma once
 
@@ -34,10 +35,18 @@ namespace pf {
 constexpr int kTile = 64;                 // GEMM tile: 64 (row, rank) pairs by 64 or 128 weight rows
 constexpr int kGemmThreads = 512;         // GEMM blocks: 8 waves, each 32 weight rows x 32 pairs of one matrix
 constexpr int kGemmWaves = kGemmThreads / 64;
-constexpr float kQMax = 4194303.0f;       // 2^22 - 1: 32 * 15 * kQMax < 2^31 (int32 block dots)
+constexpr int kRowExp = 14;               // scaled rows: |x / step| < 2^14, well inside fp16's range
+constexpr int kPfWords = 32;              // words per 32-block of a row: [hi/lo][group of 8][4 words]
 constexpr int kStepBlocks = 4;            // 32-blocks of the reduction per pipeline step
-// LDS per GEMM block: two buffers of [block][plane][half][pair][4] digit words.
-constexpr int kStageWords = kStepBlocks * 3 * 2 * kTile * 4;
+constexpr int kStepChunks = kStepBlocks * 8;  // 16-byte chunks of one row per step: (block, plane, group)
+// A row is stored as steps of 4 blocks: the blocks' 32 chunks, then their 4 sums (blocks 0, 2, 1, 3).
+constexpr int kStepWords = kStepChunks * 4 + 4;
+__host__ __device__ constexpr int pf_row_words(int K) { return K / (32 * kStepBlocks) * kStepWords; }
+// LDS per GEMM block: two buffers of [pair][step words]. The 4 words of sums keep both the 16-byte
+// writes (one pair's chunks across a half-wave) and the 16-byte reads (one chunk of 32 consecutive
+// pairs) free of bank conflicts.
+constexpr int kPairStride = kStepWords;
+constexpr int kStageWords = kTile * kPairStride;
 constexpr int kGemmLds = 2 * kStageWords * 4;
 
 struct PfArgs {
@@ -46,9 +55,8 @@ struct PfArgs {
   float* xbuf0;          // [Tp][H] layer outputs between layers (L > 1)
   float* xbuf1;
   double* logits;        // [Tp][E]
-  uint32_t* xq;          // [Tp][H/32][kXqWords] digits of the layer input
-  float* xstep;          // [Tp] its per-row step
-  float* xsum;           // [Tp][H/32] block sums divided by the step
+  uint32_t* xq;          // [Tp][pf_row_words(H)] fp16 pairs and block sums of the layer input
+  float* xstep;          // [Tp] its per-row step (a power of two)
   unsigned long long* mask;  // [E][W] rows choosing expert e, 64 per word
   int32_t* wpre;         // [E][W] rows of expert e in the words before
   int32_t* sel;          // [Tp][k] expert ids
@@ -63,9 +71,8 @@ struct PfArgs {
   int4* items;           // [Icap] (expert, first pair slot, pairs, 0)
   int32_t* n_items;      // [1]
   float* hbuf;           // [Pcap][I] SwiGLU rows by pair slot
-  uint32_t* hq;          // [Pcap][I/32][kXqWords]
+  uint32_t* hq;          // [Pcap][pf_row_words(I)]
   float* hstep;          // [Pcap]
-  float* hsum;           // [Pcap][I/32]
   float* ybuf;           // [Pcap][H] W_d h by pair slot
   int32_t H, I, E, L, T, k, residual, Pcap, Icap, W;
 };
@@ -80,15 +87,17 @@ __device__ __forceinline__ float* pf_layer_output(const PfArgs& a, int layer) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Rows as digits: one wave per row of K floats. q = rint(x / step) with step = max|x| / kQMax over
-// the row, split into balanced base-256 digits d0, d1 in [-128, 127] and d2 (|d2| <= 64), stored
-// per 32-block in the gate/up digit layout (words [plane][group of 8][even/odd], the even word
-// holding elements 8g+0,2,4,6, the odd one 8g+1,3,5,7: the order of the weight nibbles). The
-// block sums (of x, in fp32) are stored divided by the step. Grid: ceil(n / 4) x 256 threads.
-// zero_words / zero: words of `zero` cleared by the grid on the side (the layer's row masks).
+// Rows as fp16 pairs: one wave per row of K floats. The row is scaled by step = 2^(e - kRowExp),
+// where max|x| < 2^e, so |x / step| < 2^14 (an exact scaling); each scaled value v becomes
+// hi = fp16(v) and lo = fp16(v - hi), both rounded to nearest (v - hi is exact in fp32), which
+// leaves |v - hi - lo| <= 2^-22 |v| + 2^-25. Stored per 32-block as [plane hi, lo][group g of 8]
+// [word j = 0..3], word j holding elements 8g + j (low half) and 8g + 4 + j (high half): the order
+// in which a weight code word's nibbles unpack; each 4 blocks are followed by their sums of v (fp32).
+// Grid: ceil(n / 4) x 256 threads. zero_words / zero: words of `zero` cleared by the grid on the
+// side (the layer's row masks).
 // ------------------------------------------------------------------------------------------
 static __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const float* __restrict__ src, int K, int n,
-                                                                   uint32_t* dig, float* step_out, float* bsum,
+                                                                   uint32_t* dig, float* step_out,
                                                                    unsigned long long* zero, int zero_words) {
   const int lane = threadIdx.x & 63;
   for (int i = blockIdx.x * kThreads + threadIdx.x; i < zero_words; i += gridDim.x * kThreads) zero[i] = 0ull;
@@ -103,44 +112,36 @@ static __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const float
     mx = max(mx, __builtin_bit_cast(uint32_t, m4));  // non-negative floats order as integers
   }
   const float rmax = __builtin_bit_cast(float, wave_max_u32(mx));
-  const float step = rmax / kQMax;
-  const float inv = rmax > 0.f ? kQMax / rmax : 0.f;
-  const float sinv = rmax > 0.f ? 1.f / step : 0.f;
+  int ex = 0;
+  frexpf(rmax, &ex);       // rmax < 2^ex
+  ex = max(ex, -100);      // keeps step a normal float
+  const float step = rmax > 0.f ? ldexpf(1.f, ex - kRowExp) : 1.f;
+  const float inv = rmax > 0.f ? ldexpf(1.f, kRowExp - ex) : 0.f;
   if (lane == 0) step_out[row] = step;
-  uint32_t* drow = dig + static_cast<size_t>(row) * (K / 32) * kXqWords;
+  uint32_t* drow = dig + static_cast<size_t>(row) * pf_row_words(K);
   for (int c0 = 0; c0 < n4; c0 += 64) {  // K / 4 is a multiple of 8: a block's 8 lanes are all in or out
     const int c = c0 + lane;
     const bool in = c < n4;
     const float4 v = load_f4(x + 4 * min(c, n4 - 1));
-    float sum = (v.x + v.y) + (v.z + v.w);
+    const float e[4] = {v.x * inv, v.y * inv, v.z * inv, v.w * inv};
+    float sum = (e[0] + e[1]) + (e[2] + e[3]);
     sum += dpp_f32<kDppXor1>(sum);
     sum += dpp_f32<kDppXor2>(sum);
     sum += dpp_f32<kDppHalfMirror>(sum);  // the 8 lanes of this block
-    const float e[4] = {v.x, v.y, v.z, v.w};
-    int d[3][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int q = static_cast<int>(rintf(e[i] * inv));
-      q = max(-static_cast<int>(kQMax), min(static_cast<int>(kQMax), q));
-      const int d0 = ((q + 128) & 255) - 128;
-      const int q1 = (q - d0) >> 8;
-      const int d1 = ((q1 + 128) & 255) - 128;
-      d[0][i] = d0;
-      d[1][i] = d1;
-      d[2][i] = (q1 - d1) >> 8;
-    }
     if (in) {
+      // elements 4*sub + i of the block: group sub / 2, word i, low half for even sub, high for odd
       const int b = c >> 3, sub = c & 7;
-      // elements 4*sub + i: group sub / 2, even word for i = 0, 2 and odd for i = 1, 3, bytes
-      // 2*(sub % 2) + i / 2 of the word
-      uint16_t* base = reinterpret_cast<uint16_t*>(drow + static_cast<size_t>(b) * kXqWords);
+      uint32_t* step_w = drow + (b >> 2) * kStepWords;
+      uint16_t* base = reinterpret_cast<uint16_t*>(step_w + (b & 3) * kPfWords);
       const int g = sub >> 1, half = sub & 1;
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        base[((p * 4 + g) * 2 + 0) * 2 + half] = static_cast<uint16_t>((d[p][0] & 0xFF) | ((d[p][2] & 0xFF) << 8));
-        base[((p * 4 + g) * 2 + 1) * 2 + half] = static_cast<uint16_t>((d[p][1] & 0xFF) | ((d[p][3] & 0xFF) << 8));
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 hi = static_cast<_Float16>(e[i]);
+        const _Float16 lo = static_cast<_Float16>(e[i] - static_cast<float>(hi));
+        base[((0 * 4 + g) * 4 + i) * 2 + half] = __builtin_bit_cast(uint16_t, hi);
+        base[((1 * 4 + g) * 4 + i) * 2 + half] = __builtin_bit_cast(uint16_t, lo);
       }
-      if (sub == 0) bsum[static_cast<size_t>(row) * (K / 32) + b] = sum * sinv;
+      if (sub == 0) reinterpret_cast<float*>(step_w)[kStepChunks * 4 + (b & 1) * 2 + ((b >> 1) & 1)] = sum;
     }
   }
 }
@@ -335,54 +336,75 @@ static __global__ __launch_bounds__(kThreads) void pf_scatter_kernel(PfArgs a, i
 }
 
 // ------------------------------------------------------------------------------------------
-// GEMM tiles on v_mfma_i32_32x32x32_i8, one 32-weight block per instruction (the full-rate int8
-// form on gfx950; the 16x16x32 form runs at half rate). A = 32 pair rows' digits of one plane,
-// B = 32 weight rows' 4-bit codes as bytes; lane l supplies A row / B column l % 32 and elements
-// 16(l/32)..+15 (the even elements of each 8-group, then the odd ones: the order both the weight
-// nibbles and the stored digits have), and D register i of lane l holds row 8(i/4) + 4(l/32) + i%4
-// (a pair) of column l % 32 (a weight row), so a lane's block scale is one value. The three digit
-// planes chain through the accumulator, high plane first (D = (D << 8) + A_p B), which forms
-// P = P0 + 256 P1 + 65536 P2 exactly in wrapping int32 (the sum fits); the fold is acc += s * P. The
-// minimum's term sum_b m_b * sum(x)_b / step runs on v_mfma_f32_32x32x2f32 into the same
-// accumulators (A = the pairs' block sums, B = the rows' minima, two blocks per instruction; the
-// same D layout), and each pair's step multiplies its total at the end.
+// GEMM tiles on v_mfma_f32_32x32x16_f16, two instructions per 32-weight block and plane. A = 32
+// pair rows' fp16 values of one plane, B = 32 weight rows' 4-bit codes as exact fp16 values; lane
+// l supplies A row / B column l % 32 and 8 elements of the instruction's 16, and D register i of
+// lane l holds row 8(i/4) + 4(l/32) + i%4 (a pair) of column l % 32 (a weight row), so a lane's
+// block scale is one value. Instruction s of a block takes group 2(l/32) + s of it in both
+// operands (in the order of the unpacked code nibbles), which covers the block's 32 elements. The
+// block's four products (lo plane first, then hi) sum in the matrix core's fp32 accumulator and
+// the fold is acc += s * P. The minimum's term sum_b m_b * sum(x)_b / step runs on
+// v_mfma_f32_32x32x2f32 into the same accumulators (A = the pairs' block sums, B = the rows'
+// minima, two blocks per instruction; the same D layout; the sums come with the staged values),
+// and each pair's step multiplies its total at the end.
 //
 // Block tile: 64 pairs by 64 rows of gate and of up (gate/up) or by 128 rows (down), eight waves
 // of 32 rows x 32 pairs of one matrix each (at most 128 VGPRs: four waves per SIMD). The 64 pairs'
-// digits of each 4-block step go through LDS (double-buffered, one barrier per step) in
-// [block][plane][half][pair][16 bytes] order, so a lane reads its 16 bytes next to its
-// neighbours'. The next step's digits are loaded into registers while the current step computes
+// values of each 4-block step go through LDS (double-buffered, one barrier per step). A step of a
+// pair's row is 528 contiguous bytes, and a half-wave loads its 512 bytes of values whole, so a
+// load instruction touches 8 cache lines rather than one per lane (one more load per wave takes its
+// 8 pairs' sums). The next step's values are loaded
+// into registers while the current step computes
 // and written to LDS after it: LDS DMA loads would make the compiler wait for them before the
 // step's first LDS read, as it cannot tell the two buffers apart. Pairs past the item's last
 // repeat it.
 // ------------------------------------------------------------------------------------------
-typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
-typedef int32_t i32x16v __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// The digits of blocks kb0..kb0+3 of the 64 pairs are 24 chunks (block, plane, half) of 16 bytes
-// per pair; wave w moves chunks 3w..3w+2 with lane l taking pair l (from its digit row `src`).
-constexpr int kChunksPerWave = 24 / kGemmWaves;
-__device__ __forceinline__ void fetch_step(const uint32_t* src, int kb0, u32x4 (&v)[kChunksPerWave]) {
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int n = 0; n < kChunksPerWave; ++n) {
-    const int ins = wave * kChunksPerWave + n;  // (bs * 3 + p) * 2 + h
-    const int h = ins & 1, p = (ins >> 1) % 3, bs = (ins >> 1) / 3;
-    v[n] = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(kb0 + bs) * kXqWords + p * 8 + 4 * h);
-  }
+// Step st of the 64 pairs' rows: 32 chunks (block, plane, group) of 16 bytes per pair, then the
+// chunk of block sums. Load n of wave w moves pair 2(4w + n) + l / 32, whose row starts at word
+// offs[n] of `base`, with lane l taking chunk l % 32; the last load takes the sums of pair
+// 8w + l % 8 (row offset soff), which lanes 0..7 store.
+constexpr int kPairsPerWave = kTile / kGemmWaves;
+constexpr int kChunksPerWave = kPairsPerWave / 2;
+__device__ __forceinline__ int staged_pair(int n) {
+  return 2 * ((threadIdx.x >> 6) * kChunksPerWave + n) + ((threadIdx.x & 63) >> 5);
 }
-__device__ __forceinline__ void store_step(const u32x4 (&v)[kChunksPerWave], uint32_t* buf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void fetch_step(const uint32_t* base, const uint32_t (&offs)[kChunksPerWave], uint32_t soff,
+                                           int st, u32x4 (&v)[kChunksPerWave + 1]) {
+  const uint32_t j = threadIdx.x & 31, sw = static_cast<uint32_t>(st) * kStepWords;
 #pragma unroll
   for (int n = 0; n < kChunksPerWave; ++n)
-    *reinterpret_cast<u32x4*>(buf + ((wave * kChunksPerWave + n) * kTile + lane) * 4) = v[n];
+    v[n] = *reinterpret_cast<const u32x4*>(base + (offs[n] + sw + 4 * j));
+  v[kChunksPerWave] = *reinterpret_cast<const u32x4*>(base + (soff + sw + kStepChunks * 4));
+}
+__device__ __forceinline__ void store_step(const u32x4 (&v)[kChunksPerWave + 1], uint32_t* buf) {
+  const int lane = threadIdx.x & 63, j = lane & 31;
+#pragma unroll
+  for (int n = 0; n < kChunksPerWave; ++n)
+    *reinterpret_cast<u32x4*>(buf + staged_pair(n) * kPairStride + 4 * j) = v[n];
+  if (lane < kPairsPerWave)
+    *reinterpret_cast<u32x4*>(buf + ((threadIdx.x >> 6) * kPairsPerWave + lane) * kPairStride + kStepChunks * 4) =
+        v[kChunksPerWave];
 }
 
-// 16 code bytes (elements 16h..16h+15 of a block) from its 8 packed bytes, in the digit order.
-__device__ __forceinline__ i32x4v codes16(uint2 w) {
-  return i32x4v{static_cast<int32_t>(w.x & 0x0F0F0F0Fu), static_cast<int32_t>((w.x >> 4) & 0x0F0F0F0Fu),
-                static_cast<int32_t>(w.y & 0x0F0F0F0Fu), static_cast<int32_t>((w.y >> 4) & 0x0F0F0F0Fu)};
+// The 8 codes of one code word (a group of 8 weights, nibble j = element j) as fp16 values in the
+// order elements j, 4 + j for j = 0..3: each nibble pair goes into the mantissas of 1024.0 (fp16
+// 0x6400, whose unit in the last place is 1), and 1024 is subtracted exactly.
+// `magic` holds 0x64006400 in a register, so that mask-and-insert is one v_and_or_b32 (a VOP3 form,
+// which takes no second literal).
+__device__ __forceinline__ f16x8 codes8(uint32_t w, uint32_t magic) {
+  const f16x2 off = {static_cast<_Float16>(1024.f), static_cast<_Float16>(1024.f)};
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16x2 v = __builtin_bit_cast(f16x2, ((w >> (4 * j)) & 0x000F000Fu) | magic) - off;
+    r[2 * j] = v[0];
+    r[2 * j + 1] = v[1];
+  }
+  return r;
 }
 
 // A lane's 8-byte code halves of blocks kb0..kb0+3 (half l / 32 of each): lane (c, h) loads blocks
@@ -441,74 +463,82 @@ __device__ __forceinline__ void trade_halves(const StepCodes& w, uint2 (&cw)[kSt
 }
 
 // Work unit of GEMM block `bid` of `nb` (a multiple of 8): consecutive units (the tiles of one
-// work item) go to one XCD, whose L2 then holds that item's digit rows once.
+// work item) go to one XCD, whose L2 then holds that item's activation rows once.
 __device__ __forceinline__ int xcd_unit(int bid, int nb) { return (bid & 7) * (nb >> 3) + (bid >> 3); }
 
 // One wave's 32 weight rows (starting at codes0 / sm0 in each of NM matrices) against 32 of the
-// block's 64 staged pairs (half ph). src: this lane's staging source row (pair lane % 64); xs: the
-// block sums of pair 32 ph + lane % 32. live = false (no pair of this half exists): the wave only
-// stages and waits. acc[m][i]: D element i, in units of the pair's step.
+// block's 64 staged pairs (half ph). base + src: this lane's pair's row (pair lane % 64, as a word
+// offset below 2^32). live = false (no pair of this half exists): the wave only stages and waits.
+// acc[m][i]: D element i, in units of the pair's step.
 template <int NM, int FMT>
 __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const uint32_t* const* sm0, int K,
-                                          const uint32_t* src, const float* xs, int ph, bool live, uint32_t* lds,
+                                          const uint32_t* base, uint32_t src, int ph, bool live,
+                                          uint32_t* lds,
                                           f32x16 (&acc)[NM]) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int nblk = K / 32, nstep = nblk / kStepBlocks;
   const size_t rsm = sm_row_words<FMT>(K);
   live = __builtin_amdgcn_readfirstlane(static_cast<int>(live)) != 0;  // one value per wave
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));  // kept in a VGPR (see codes8)
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
-  u32x4 nxt[kChunksPerWave];
+  // The rows this lane stages: those of pairs staged_pair(n), whose lanes hold them as `src`.
+  uint32_t srcs[kChunksPerWave];
+#pragma unroll
+  for (int n = 0; n < kChunksPerWave; ++n) srcs[n] = __shfl(src, staged_pair(n));
+  const uint32_t ssrc = __shfl(src, (threadIdx.x >> 6) * kPairsPerWave + (lane & (kPairsPerWave - 1)));
+  u32x4 nxt[kChunksPerWave + 1];
   StepCodes cur_w[NM], nxt_w[NM];
-  float x2[2], nx2[2];
   if (live) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
       load_step_codes<FMT>(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + c * rsm, 0, cur_w[m]);
-    x2[0] = xs[h];
-    x2[1] = xs[2 + h];
   }
-  fetch_step(src, 0, nxt);
+  fetch_step(base, srcs, ssrc, 0, nxt);
   store_step(nxt, lds);
   __syncthreads();
   for (int st = 0; st < nstep; ++st) {
     const int kb0 = st * kStepBlocks;
     const uint32_t* cur = lds + (st & 1) * kStageWords;
     const bool more = st + 1 < nstep;
-    // The next step's codes, scale/min words, block sums and digits are loaded while this step
+    // The next step's codes, scale/min words, block sums and values are loaded while this step
     // computes (its own arrived during the previous step).
     if (live && more) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
         load_step_codes<FMT>(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + c * rsm, kb0 + kStepBlocks,
                              nxt_w[m]);
-      nx2[0] = xs[kb0 + kStepBlocks + h];
-      nx2[1] = xs[kb0 + kStepBlocks + 2 + h];
     }
-    if (more) fetch_step(src, kb0 + kStepBlocks, nxt);
+    if (more) fetch_step(base, srcs, ssrc, st + 1, nxt);
     if (live) {
+      const float2 x2 = *reinterpret_cast<const float2*>(cur + (32 * ph + c) * kPairStride + kStepChunks * 4 + 2 * h);
       uint2 cw[NM][kStepBlocks];
 #pragma unroll
       for (int m = 0; m < NM; ++m) trade_halves(cur_w[m], cw[m]);
 #pragma unroll
       for (int bs = 0; bs < kStepBlocks; ++bs) {
-        i32x4v ap[3];
+        f16x8 ap[2][2];  // [plane][instruction]: group 2h + s of the block
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-          ap[p] = *reinterpret_cast<const i32x4v*>(cur + (((bs * 3 + p) * 2 + h) * kTile + 32 * ph + c) * 4);
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            ap[p][q] = *reinterpret_cast<const f16x8*>(
+                cur + (32 * ph + c) * kPairStride + ((bs * 2 + p) * 4 + 2 * h + q) * 4);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          const i32x4v b = codes16(cw[m][bs]);
+          const f16x8 b0 = codes8(cw[m][bs].x, magic), b1 = codes8(cw[m][bs].y, magic);
           const float sc = step_scale<FMT>(cur_w[m].smw, kb0, bs);
-          const i32x16v z = {};
-          i32x16v d = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap[2], b, z, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap[1], b, d << 8, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap[0], b, d << 8, 0, 0, 0);
+          const f32x16 z = {};
+          f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[1][0], b0, z, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[1][1], b1, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[0][0], b0, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[0][1], b1, d, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[m][i] = fmaf(sc, static_cast<float>(d[i]), acc[m][i]);
+          for (int i = 0; i < 16; ++i) acc[m][i] = fmaf(sc, d[i], acc[m][i]);
         }
       }
       // The minimum's term of the 4 blocks (instruction j takes blocks kb0 + 2j + l / 32), after the
@@ -517,8 +547,8 @@ __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const ui
       for (int m = 0; m < NM; ++m) {
         const float m0 = step_min<FMT>(cur_w[m].smw, kb0, h);
         const float m1 = step_min<FMT>(cur_w[m].smw, kb0, 2 + h);
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[0], m0, acc[m], 0, 0, 0);
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[1], m1, acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2.x, m0, acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2.y, m1, acc[m], 0, 0, 0);
       }
     }
     if (more) store_step(nxt, lds + ((st + 1) & 1) * kStageWords);  // read two steps ago
@@ -526,8 +556,6 @@ __device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const ui
     if (live && more) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) cur_w[m] = nxt_w[m];
-      x2[0] = nx2[0];
-      x2[1] = nx2[1];
     }
   }
 }
@@ -541,7 +569,7 @@ __device__ __forceinline__ int d_pair(int ph, int i) {
 // pairs 32 ((w >> 1) & 1)..); the up waves hand their sums to the gate waves through LDS, which
 // write silu(g) * v of the block's rows for the item's pairs into hbuf (by pair slot).
 template <int FMT>
-__global__ __launch_bounds__(kGemmThreads) void pf_gateup_kernel(PfArgs a, int layer) {
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4))) void pf_gateup_kernel(PfArgs a, int layer) {
   extern __shared__ uint32_t lds[];
   const int I = a.I, H = a.H;
   const int tiles = I / kTile;
@@ -556,14 +584,12 @@ __global__ __launch_bounds__(kGemmThreads) void pf_gateup_kernel(PfArgs a, int l
   __shared__ float s_step[kTile];  // the item's pairs' steps, for the epilogue
   const int tsrc = pairs[p0 + min(lane, np - 1)] & 0xFFFF;                  // staging: pair lane
   if (wave == 0) s_step[lane] = a.xstep[tsrc];  // visible after the GEMM's first barrier
-  const int tsum = pairs[p0 + min(32 * ph + (lane & 31), np - 1)] & 0xFFFF;  // block sums: A row
-  const uint32_t* src = a.xq + static_cast<size_t>(tsrc) * (H / 32) * kXqWords;
-  const float* xs = a.xsum + static_cast<size_t>(tsum) * (H / 32);
+  const uint32_t src = static_cast<uint32_t>(tsrc) * static_cast<uint32_t>(pf_row_words(H));
   const size_t row = static_cast<size_t>(e) * I + i0 + 32 * rh;  // the wave's first weight row
   const uint8_t* codes[1] = {(mt ? a.w.up_q : a.w.gate_q) + row * (H / 2)};
   const uint32_t* sm[1] = {(mt ? a.w.up_sm : a.w.gate_sm) + row * sm_row_words<FMT>(H)};
   f32x16 acc[1];
-  gemm_rows<1, FMT>(codes, sm, H, src, xs, ph, 32 * ph < np, lds, acc);
+  gemm_rows<1, FMT>(codes, sm, H, a.xq, src, ph, 32 * ph < np, lds, acc);
   // The staging buffers are free (the GEMM ends on a barrier): up sums [rh][ph][i][lane].
   float* xch = reinterpret_cast<float*>(lds) + ((rh * 2 + ph) * 16) * 64 + lane;
   if (mt == 1) {
@@ -586,7 +612,7 @@ __global__ __launch_bounds__(kGemmThreads) void pf_gateup_kernel(PfArgs a, int l
 // Writes W_d h of the block's rows for the item's pairs into ybuf (by pair slot).
 constexpr int kDownRows = 128;
 template <int FMT>
-__global__ __launch_bounds__(kGemmThreads) void pf_down_kernel(PfArgs a, int layer) {
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4))) void pf_down_kernel(PfArgs a, int layer) {
   extern __shared__ uint32_t lds[];
   const int I = a.I, H = a.H;
   const int tiles = H / kDownRows;
@@ -598,14 +624,13 @@ __global__ __launch_bounds__(kGemmThreads) void pf_down_kernel(PfArgs a, int lay
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rq = wave & 3, ph = wave >> 2;
   __shared__ float s_step[kTile];
-  const uint32_t* src = a.hq + static_cast<size_t>(p0 + min(lane, np - 1)) * (I / 32) * kXqWords;
+  const uint32_t src = static_cast<uint32_t>(p0 + min(lane, np - 1)) * static_cast<uint32_t>(pf_row_words(I));
   if (wave == 0) s_step[lane] = a.hstep[p0 + min(lane, np - 1)];  // visible after the first barrier
-  const float* xs = a.hsum + static_cast<size_t>(p0 + min(32 * ph + (lane & 31), np - 1)) * (I / 32);
   const size_t row = static_cast<size_t>(e) * H + h0 + 32 * rq;
   const uint8_t* codes[1] = {a.w.down_q + row * (I / 2)};
   const uint32_t* sm[1] = {a.w.down_sm + row * sm_row_words<FMT>(I)};
   f32x16 acc[1];
-  gemm_rows<1, FMT>(codes, sm, I, src, xs, ph, 32 * ph < np, lds, acc);
+  gemm_rows<1, FMT>(codes, sm, I, a.hq, src, ph, 32 * ph < np, lds, acc);
   const int col = h0 + 32 * rq + (lane & 31);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {

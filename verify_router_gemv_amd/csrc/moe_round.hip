@@ -102,7 +102,6 @@ struct moe_round {
   float* pf_xbuf[2] = {nullptr, nullptr};
   uint32_t* pf_xq = nullptr;
   float* pf_xstep = nullptr;
-  float* pf_xsum = nullptr;
   unsigned long long* pf_mask = nullptr;
   int32_t* pf_wpre = nullptr;
   int32_t* pf_sel = nullptr;
@@ -118,7 +117,6 @@ struct moe_round {
   float* pf_hbuf = nullptr;
   uint32_t* pf_hq = nullptr;
   float* pf_hstep = nullptr;
-  float* pf_hsum = nullptr;
   float* pf_ybuf = nullptr;
 };
 
@@ -324,7 +322,6 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
   a.logits = h->logits;
   a.xq = h->pf_xq;
   a.xstep = h->pf_xstep;
-  a.xsum = h->pf_xsum;
   a.mask = h->pf_mask;
   a.wpre = h->pf_wpre;
   a.sel = h->pf_sel;
@@ -341,7 +338,6 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
   a.hbuf = h->pf_hbuf;
   a.hq = h->pf_hq;
   a.hstep = h->pf_hstep;
-  a.hsum = h->pf_hsum;
   a.ybuf = h->pf_ybuf;
   a.H = H;
   a.I = I;
@@ -377,8 +373,8 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
     const float* xin = l == 0 ? h->h_ing.hidden : h->pf_xbuf[(l - 1) & 1];
     int kH = H, nT = T, zw = E * a.W, kI = I, nP = np, zero0 = 0;
     unsigned long long* no_mask = nullptr;
-    void* qx[] = {&xin, &kH, &nT, &a.xq, &a.xstep, &a.xsum, &a.mask, &zw};
-    void* qh[] = {&a.hbuf, &kI, &nP, &a.hq, &a.hstep, &a.hsum, &no_mask, &zero0};
+    void* qx[] = {&xin, &kH, &nT, &a.xq, &a.xstep, &a.mask, &zw};
+    void* qh[] = {&a.hbuf, &kI, &nP, &a.hq, &a.hstep, &no_mask, &zero0};
     hipError_t e;
     if ((e = launch(reinterpret_cast<const void*>(pf::quant_rows_kernel), dim3((T + kWaves - 1) / kWaves), kThreads, 0,
                     qx, l, 0)) != hipSuccess ||
@@ -469,9 +465,9 @@ static void free_handle(moe_round* h) {
   if (h->staging) (void)hipHostFree(h->staging);
   void* ptrs[] = {h->d_ing, h->d_wtab, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique, h->uniq, h->offs,
                   h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->tsel, h->tp, h->xq, h->xss,
-                  h->pf_xbuf[0], h->pf_xbuf[1], h->pf_xq, h->pf_xstep, h->pf_xsum, h->pf_mask, h->pf_wpre,
+                  h->pf_xbuf[0], h->pf_xbuf[1], h->pf_xq, h->pf_xstep, h->pf_mask, h->pf_wpre,
                   h->pf_sel, h->pf_selp, h->pf_uniq, h->pf_offs, h->pf_eoff, h->pf_pairs, h->pf_pair_w, h->pf_slot_of,
-                  h->pf_items, h->pf_n_items, h->pf_hbuf, h->pf_hq, h->pf_hstep, h->pf_hsum, h->pf_ybuf};
+                  h->pf_items, h->pf_n_items, h->pf_hbuf, h->pf_hq, h->pf_hstep, h->pf_ybuf};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete h;
@@ -539,9 +535,8 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
       MOE_ALLOC(h->pf_xbuf[0], sizeof(float) * Tp * H);
       MOE_ALLOC(h->pf_xbuf[1], sizeof(float) * Tp * H);
     }
-    MOE_ALLOC(h->pf_xq, sizeof(uint32_t) * Tp * (H / 32) * kXqWords);
+    MOE_ALLOC(h->pf_xq, sizeof(uint32_t) * Tp * pf::pf_row_words(H));
     MOE_ALLOC(h->pf_xstep, sizeof(float) * Tp);
-    MOE_ALLOC(h->pf_xsum, sizeof(float) * Tp * (H / 32));
     MOE_ALLOC(h->pf_mask, sizeof(unsigned long long) * E * W);
     MOE_ALLOC(h->pf_wpre, sizeof(int32_t) * E * W);
     MOE_ALLOC(h->pf_sel, sizeof(int32_t) * P);
@@ -555,9 +550,8 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
     MOE_ALLOC(h->pf_items, sizeof(int4) * h->pfI);
     MOE_ALLOC(h->pf_n_items, sizeof(int32_t));
     MOE_ALLOC(h->pf_hbuf, sizeof(float) * P * I);
-    MOE_ALLOC(h->pf_hq, sizeof(uint32_t) * P * (I / 32) * kXqWords);
+    MOE_ALLOC(h->pf_hq, sizeof(uint32_t) * P * pf::pf_row_words(I));
     MOE_ALLOC(h->pf_hstep, sizeof(float) * P);
-    MOE_ALLOC(h->pf_hsum, sizeof(float) * P * (I / 32));
     MOE_ALLOC(h->pf_ybuf, sizeof(float) * P * H);
   }
 #undef MOE_ALLOC
