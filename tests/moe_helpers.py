@@ -54,6 +54,7 @@ def errors(got: np.ndarray, ref: np.ndarray):
 
 def assert_close(got, ref, what=""):
     rel, mabs = errors(got, ref)
+    print(f"[close] {what}: rel-L2 {rel:.3e}, max-abs/max|y| {mabs:.3e}")
     assert rel <= REL_L2 and mabs <= MAX_ABS_FRAC, f"{what}: rel-L2 {rel:.3e}, max-abs/max|y| {mabs:.3e}"
     return rel, mabs
 

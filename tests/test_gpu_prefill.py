@@ -220,7 +220,7 @@ def test_prefill_residual_stack():
 
 def test_prefill_profiling(prefill_layer):
     """Kernel timing of prefill rounds: the nine launches of a layer fold into the five kinds
-    (digits + logits, top-k + sort, gate/up, SwiGLU digits + down, combine), every kind timed, and
+    (input split + logits, top-k + sort, gate/up, SwiGLU split + down, combine), every kind timed, and
     the run count matches; the outputs equal an unprofiled run's bitwise."""
     cfg, layer, _ = prefill_layer
     g = GpuRound([layer], cfg, max_rows=300)

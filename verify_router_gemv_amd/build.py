@@ -27,10 +27,10 @@ FLAGS = [
     "-fvisibility=hidden",
     "-Wall", "-Wno-unused-result",
 ]
-# Per-source flags. moe_round.hip holds the prefill GEMMs, whose int32 matrix-core results are
-# shifted and converted on the vector ALUs: with the results in ordinary VGPRs (not accumulation
-# registers) that costs no register-to-register copies. No other kernel of that file uses the
-# matrix cores.
+# Per-source flags. moe_round.hip holds the prefill GEMMs, whose matrix-core results are folded
+# into the accumulators on the vector ALUs: with the results in ordinary VGPRs (not accumulation
+# registers) that costs no register-to-register copies. Its other matrix-core kernel (the fp64
+# router GEMM) only stores its results.
 SOURCE_FLAGS = {"moe_round.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

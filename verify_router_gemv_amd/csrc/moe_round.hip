@@ -309,9 +309,9 @@ static PfKernelFn pf_pick_topk(int E) {
   return pf::pf_topk_kernel<8>;
 }
 
-// A prefill round (T > MOE_ROUND_MAX_ROWS), eagerly: per layer the digits of the layer input,
-// router logits, top-k, the counting sort (offsets, then the scatter), gate/up, the SwiGLU
-// digits, down and the combine.
+// A prefill round (T > MOE_ROUND_MAX_ROWS), eagerly: per layer the fp16 pairs of the layer input,
+// router logits, top-k, the counting sort (offsets, then the scatter), gate/up, the SwiGLU rows'
+// fp16 pairs, down and the combine.
 // evs: with profiling, a start/stop pair per launch; kinds: their accumulator (layer, kind).
 static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, int* kinds, int* n_launched) {
   const int E = h->cfg.n_experts, H = h->cfg.hidden, I = h->cfg.inter, L = h->cfg.n_layers;
