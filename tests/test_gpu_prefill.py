@@ -1,7 +1,8 @@
 """Prefill rounds (more than 64 rows) through the C ABI vs the fp64 oracle (needs an MI355X).
 
-The path: counting sort of the (row, rank) pairs into 64-pair work items, gate/up and down as int8
-matrix-core GEMMs, combine in rank order. Ids and the worklist must match bit-exactly, routing
+The path: counting sort of the (row, rank) pairs into 64-pair work items, gate/up and down as fp16
+matrix-core GEMMs (each activation row scaled by a power of two and split into two fp16 values),
+combine in rank order. Ids and the worklist must match bit-exactly, routing
 weights to fp32 rounding, outputs within relative L2 1e-4 and max-abs 1e-3 * max|y|. At 4096 rows
 the outputs are checked on sampled rows (the oracle evaluates each row on its own, so a row's
 expected output does not depend on the rest of the round).
@@ -52,6 +53,39 @@ def test_prefill_verify_shape_all_rows(prefill_layer, k):
         X = synth.make_activations(cfg, T, seed=12, round_idx=T, device=DEV)
         rel, mabs, nu = check_layer_round(g, [view], X, k, f"prefill T={T} k={k}")
         say(f"  n_unique={nu[0]} rel-L2={rel:.2e}")
+    g.close()
+
+
+def test_prefill_row_scales_heavy_tails_and_zero_rows(prefill_layer):
+    """The activation split at the edges of its row scaling: rows scaled by 2^u, u uniform in
+    [-40, 40] (the per-row power-of-two step), heavy-tailed rows (four elements 10^4 times the
+    rest), and all-zero rows. Ids and routing weights as always; each row's output is checked on
+    its own scale (relative L2 and max-abs against that row of the oracle), and zero rows give
+    exact zeros."""
+    cfg, layer, view = prefill_layer
+    T = 160
+    g = GpuRound([layer], cfg, max_rows=T)
+    say(f"case prefill row scales T={T}")
+    rng = np.random.default_rng(31)
+    X = synth.make_activations(cfg, T, seed=31, round_idx=T, device="cpu").numpy().astype(np.float32)
+    X *= (2.0 ** rng.uniform(-40.0, 40.0, size=T)).astype(np.float32)[:, None]
+    for t in range(10, 20):
+        X[t, rng.choice(cfg.H, size=4, replace=False)] *= np.float32(1e4)
+    zero_rows = [0, 77, T - 1]
+    X[zero_rows] = 0.0
+    out, ids, rw, _ = g.run(torch.from_numpy(X).to(DEV))
+    with np.errstate(over="ignore"):  # silu(a) = a / (1 + e^-a) at a << 0: e^-a overflows, silu -> -0
+        ref, rids, rp, _ = oracle.moe_round([view], X, cfg.k, residual=False)
+    assert np.array_equal(ids[0], rids[0]), "ids differ"
+    np.testing.assert_allclose(rw[0], rp[0], rtol=2e-6, atol=1e-7, err_msg="routing weights")
+    worst = 0.0
+    for t in range(T):
+        if t in zero_rows:
+            assert np.all(out[t] == 0.0), f"zero row {t} gave nonzero output"
+            continue
+        rel, _ = assert_close(out[t], ref[t], f"prefill scaled row {t}")
+        worst = max(worst, rel)
+    say(f"  worst row rel-L2={worst:.2e}")
     g.close()
 
 
