@@ -42,6 +42,22 @@ def test_prefill_ragged_shape_all_rows():
     g.close()
 
 
+@pytest.mark.parametrize("fmt", ["q4b32", "q4s256"])
+def test_prefill_wide_inter_all_rows(fmt):
+    """A wider expert than the other prefill shapes: I = 768 (6 steps of down's reduction, 12 gate/up
+    row tiles), H=512, E=24, k=4, T = 70 and 133 (ragged tiles), both weight formats."""
+    cfg = synth.ShapeConfig("wide_inter", H=512, E=24, k=4, I=768, T=(70, 133), zipf_s=0.7).replace(fmt=fmt)
+    layer = synth.make_layer(cfg, seed=5, layer=0, device=DEV)
+    view = oracle_view(layer)
+    g = GpuRound([layer], cfg, max_rows=133)
+    for T in cfg.T:
+        say(f"case prefill I=768 {fmt} T={T}")
+        X = synth.make_activations(cfg, T, seed=13, round_idx=T, device=DEV)
+        rel, mabs, nu = check_layer_round(g, [view], X, cfg.k, f"prefill I=768 {fmt} T={T}")
+        say(f"  n_unique={nu[0]} rel-L2={rel:.2e}")
+    g.close()
+
+
 @pytest.mark.parametrize("k", [1, 8])
 def test_prefill_verify_shape_all_rows(prefill_layer, k):
     """The prefill workload's layer at T = 65 and 200, every row against the oracle; k = 1 makes
