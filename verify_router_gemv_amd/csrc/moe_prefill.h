@@ -153,36 +153,62 @@ static __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const float
 // l / 16, and D register i of lane l holds row l/16 + 4i (an expert) of column l % 16 (a token row;
 // measured: unlike the fp32 form's rows 4(l/16)+i, the fp64 form interleaves its rows). A float4
 // per lane feeds four instructions: instruction i takes elements h0 + 4(l/16) + i, the same on both
-// sides. Grid: (ceil(E / 16), ceil(T / 64)); wave w takes rows 16w..16w+15 of the block's 64.
+// sides.
 // ------------------------------------------------------------------------------------------
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
+// Large rounds: a block computes 32 experts x 32 rows, its four waves splitting the reduction in
+// quarters (wave w sums h in [w H / 4, (w + 1) H / 4)), each wave holding the four 16 x 16 tiles of
+// the block's output; wave 0 adds the quarters in wave order. Four loads (two router rows' and two
+// input rows' float4 per lane) feed sixteen matrix instructions, twice the work per loaded byte of
+// a 16 x 16 tile. Grid: (ceil(E / 32), ceil(T / 32)).
 static __global__ __launch_bounds__(kThreads) void pf_logits_kernel(PfArgs a, int layer) {
+  __shared__ f64x4 part[kWaves - 1][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, q = lane >> 4;
   const int E = a.E, T = a.T, H = a.H;
-  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 64 + wave * 16;
+  const int e0 = blockIdx.x * 32, t0 = blockIdx.y * 32;
+  const int hq = H / kWaves;  // a multiple of 64
   const float* x = pf_layer_input(a, layer);
-  const float* wr = a.w.router_w + static_cast<size_t>(min(e0 + c, E - 1)) * H + 4 * q;
-  const float* xr = x + static_cast<size_t>(min(t0 + c, T - 1)) * H + 4 * q;
-  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
-  for (int h0 = 0; h0 < H; h0 += 16) {  // H / 16 is a multiple of 16
-    const float4 wv = load_stream_f4(wr + h0);
-    const float4 xv = load_f4(xr + h0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv.x), static_cast<double>(xv.x), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv.y), static_cast<double>(xv.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv.z), static_cast<double>(xv.z), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv.w), static_cast<double>(xv.w), acc, 0, 0, 0);
-  }
-  const int t = t0 + c;
-  if (t < T) {
+  const float* wr0 = a.w.router_w + static_cast<size_t>(min(e0 + c, E - 1)) * H + wave * hq + 4 * q;
+  const float* wr1 = a.w.router_w + static_cast<size_t>(min(e0 + 16 + c, E - 1)) * H + wave * hq + 4 * q;
+  const float* xr0 = x + static_cast<size_t>(min(t0 + c, T - 1)) * H + wave * hq + 4 * q;
+  const float* xr1 = x + static_cast<size_t>(min(t0 + 16 + c, T - 1)) * H + wave * hq + 4 * q;
+  f64x4 acc[4] = {};  // [expert half * 2 + row half]
+#pragma unroll 4
+  for (int h0 = 0; h0 < hq; h0 += 16) {
+    const float4 w0 = load_stream_f4(wr0 + h0), w1 = load_stream_f4(wr1 + h0);
+    const float4 x0 = load_f4(xr0 + h0), x1 = load_f4(xr1 + h0);
+    const float wv[2][4] = {{w0.x, w0.y, w0.z, w0.w}, {w1.x, w1.y, w1.z, w1.w}};
+    const float xv[2][4] = {{x0.x, x0.y, x0.z, x0.w}, {x1.x, x1.y, x1.z, x1.w}};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + q + 4 * i;
-      if (e < E) {
-        const double b = a.w.router_bias ? static_cast<double>(a.w.router_bias[e]) : 0.0;
-        a.logits[static_cast<size_t>(t) * E + e] = acc[i] + b;
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(wv[b >> 1][j]), static_cast<double>(xv[b & 1][j]),
+                                                      acc[b], 0, 0, 0);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) part[wave - 1][b][lane] = acc[b];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < kWaves - 1; ++w)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] += part[w][b][lane];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int t = t0 + 16 * (b & 1) + c;
+    if (t < T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + 16 * (b >> 1) + q + 4 * i;
+        if (e < E) {
+          const double bias = a.w.router_bias ? static_cast<double>(a.w.router_bias[e]) : 0.0;
+          a.logits[static_cast<size_t>(t) * E + e] = acc[b][i] + bias;
+        }
       }
     }
   }

@@ -381,7 +381,7 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
         (e = (T <= kPfSplitKRows
                   ? launch(reinterpret_cast<const void*>(pf::pf_logits_splitk_kernel), dim3((E + 15) / 16, (T + 15) / 16),
                            kThreads, 0, gp, l, 0)
-                  : launch(reinterpret_cast<const void*>(pf::pf_logits_kernel), dim3((E + 15) / 16, (T + 63) / 64),
+                  : launch(reinterpret_cast<const void*>(pf::pf_logits_kernel), dim3((E + 31) / 32, (T + 31) / 32),
                            kThreads, 0, gp, l, 0))) != hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(topk), dim3((T + kWaves - 1) / kWaves), kThreads, 0, gp, l, 1)) !=
             hipSuccess ||
