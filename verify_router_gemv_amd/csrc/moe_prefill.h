@@ -33,8 +33,7 @@ namespace moe {
 namespace pf {
 
 constexpr int kTile = 64;                 // GEMM tile: 64 (row, rank) pairs by 64 or 128 weight rows
-constexpr int kGemmThreads = 512;         // GEMM blocks: 8 waves, each 32 weight rows x 32 pairs of one matrix
-constexpr int kGemmWaves = kGemmThreads / 64;
+constexpr int kGemmThreads = 512;         // down GEMM blocks: 8 waves, each 32 weight rows x 32 pairs
 constexpr int kRowExp = 14;               // scaled rows: |x / step| < 2^14, well inside fp16's range
 constexpr int kPfWords = 32;              // words per 32-block of a row: [hi/lo][group of 8][4 words]
 constexpr int kStepBlocks = 4;            // 32-blocks of the reduction per pipeline step
@@ -374,12 +373,13 @@ static __global__ __launch_bounds__(kThreads) void pf_scatter_kernel(PfArgs a, i
 // minima, two blocks per instruction; the same D layout; the sums come with the staged values),
 // and each pair's step multiplies its total at the end.
 //
-// Block tile: 64 pairs by 64 rows of gate and of up (gate/up) or by 128 rows (down), eight waves
-// of 32 rows x 32 pairs of one matrix each (at most 128 VGPRs: four waves per SIMD). The 64 pairs'
-// values of each 4-block step go through LDS (double-buffered, one barrier per step). A step of a
-// pair's row is 528 contiguous bytes, and a half-wave loads its 512 bytes of values whole, so a
-// load instruction touches 8 cache lines rather than one per lane (one more load per wave takes its
-// 8 pairs' sums). The next step's values are loaded
+// Block tile: 64 pairs by 64 rows of gate and of up (gate/up) or by 128 rows (down). Down has
+// eight waves of 32 rows x 32 pairs (at most 128 VGPRs: four waves per SIMD). Gate/up has four
+// waves of 32 rows x 64 pairs, as two 32-pair tiles that share every unpacked code word (at most
+// 256 VGPRs: two waves per SIMD). The 64 pairs' values of each 4-block step go through LDS
+// (double-buffered, one barrier per step). A step of a pair's row is 528 contiguous bytes, and a
+// half-wave loads its 512 bytes of values whole, so a load instruction touches 8 cache lines
+// rather than one per lane (one more load per wave takes its pairs' sums). The next step's values are loaded
 // into registers while the current step computes
 // and written to LDS after it: LDS DMA loads would make the compiler wait for them before the
 // step's first LDS read, as it cannot tell the two buffers apart. Pairs past the item's last
@@ -390,31 +390,32 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Step st of the 64 pairs' rows: 32 chunks (block, plane, group) of 16 bytes per pair, then the
-// chunk of block sums. Load n of wave w moves pair 2(4w + n) + l / 32, whose row starts at word
-// offs[n] of `base`, with lane l taking chunk l % 32; the last load takes the sums of pair
-// 8w + l % 8 (row offset soff), which lanes 0..7 store.
-constexpr int kPairsPerWave = kTile / kGemmWaves;
-constexpr int kChunksPerWave = kPairsPerWave / 2;
-__device__ __forceinline__ int staged_pair(int n) {
-  return 2 * ((threadIdx.x >> 6) * kChunksPerWave + n) + ((threadIdx.x & 63) >> 5);
-}
-__device__ __forceinline__ void fetch_step(const uint32_t* base, const uint32_t (&offs)[kChunksPerWave], uint32_t soff,
-                                           int st, u32x4 (&v)[kChunksPerWave + 1]) {
-  const uint32_t j = threadIdx.x & 31, sw = static_cast<uint32_t>(st) * kStepWords;
+// chunk of block sums. With NW waves per block, wave w stages pairs P w.. P w + P - 1 (P = 64 / NW):
+// load n moves pair P w + 2n + l / 32, whose row starts at word offs[n] of `base`, with lane l
+// taking chunk l % 32; the last load takes the sums of pair P w + l % P (row offset soff), which
+// lanes 0..P-1 store.
+template <int NW>
+struct Staging {
+  static constexpr int kPairs = kTile / NW;      // pairs staged per wave
+  static constexpr int kLoads = kPairs / 2;      // 512-byte loads per wave and step (two pairs each)
+  __device__ static __forceinline__ int pair(int n) {
+    return (threadIdx.x >> 6) * kPairs + 2 * n + ((threadIdx.x & 63) >> 5);
+  }
+  __device__ static __forceinline__ void fetch(const uint32_t* base, const uint32_t (&offs)[kLoads], uint32_t soff,
+                                               int st, u32x4 (&v)[kLoads + 1]) {
+    const uint32_t j = threadIdx.x & 31, sw = static_cast<uint32_t>(st) * kStepWords;
 #pragma unroll
-  for (int n = 0; n < kChunksPerWave; ++n)
-    v[n] = *reinterpret_cast<const u32x4*>(base + (offs[n] + sw + 4 * j));
-  v[kChunksPerWave] = *reinterpret_cast<const u32x4*>(base + (soff + sw + kStepChunks * 4));
-}
-__device__ __forceinline__ void store_step(const u32x4 (&v)[kChunksPerWave + 1], uint32_t* buf) {
-  const int lane = threadIdx.x & 63, j = lane & 31;
+    for (int n = 0; n < kLoads; ++n) v[n] = *reinterpret_cast<const u32x4*>(base + (offs[n] + sw + 4 * j));
+    v[kLoads] = *reinterpret_cast<const u32x4*>(base + (soff + sw + kStepChunks * 4));
+  }
+  __device__ static __forceinline__ void store(const u32x4 (&v)[kLoads + 1], uint32_t* buf) {
+    const int lane = threadIdx.x & 63, j = lane & 31;
 #pragma unroll
-  for (int n = 0; n < kChunksPerWave; ++n)
-    *reinterpret_cast<u32x4*>(buf + staged_pair(n) * kPairStride + 4 * j) = v[n];
-  if (lane < kPairsPerWave)
-    *reinterpret_cast<u32x4*>(buf + ((threadIdx.x >> 6) * kPairsPerWave + lane) * kPairStride + kStepChunks * 4) =
-        v[kChunksPerWave];
-}
+    for (int n = 0; n < kLoads; ++n) *reinterpret_cast<u32x4*>(buf + pair(n) * kPairStride + 4 * j) = v[n];
+    if (lane < kPairs)
+      *reinterpret_cast<u32x4*>(buf + ((threadIdx.x >> 6) * kPairs + lane) * kPairStride + kStepChunks * 4) = v[kLoads];
+  }
+};
 
 // The 8 codes of one code word (a group of 8 weights, nibble j = element j) as fp16 values in the
 // order elements j, 4 + j for j = 0..3: each nibble pair goes into the mantissas of 1024.0 (fp16
@@ -492,110 +493,112 @@ __device__ __forceinline__ void trade_halves(const StepCodes& w, uint2 (&cw)[kSt
 // work item) go to one XCD, whose L2 then holds that item's activation rows once.
 __device__ __forceinline__ int xcd_unit(int bid, int nb) { return (bid & 7) * (nb >> 3) + (bid >> 3); }
 
-// One wave's 32 weight rows (starting at codes0 / sm0 in each of NM matrices) against 32 of the
-// block's 64 staged pairs (half ph). base + src: this lane's pair's row (pair lane % 64, as a word
-// offset below 2^32). live = false (no pair of this half exists): the wave only stages and waits.
-// acc[m][i]: D element i, in units of the pair's step.
-template <int NM, int FMT>
-__device__ __forceinline__ void gemm_rows(const uint8_t* const* codes0, const uint32_t* const* sm0, int K,
-                                          const uint32_t* base, uint32_t src, int ph, bool live,
-                                          uint32_t* lds,
-                                          f32x16 (&acc)[NM]) {
+// One wave's 32 weight rows (codes0 / sm0) against NT 32-pair tiles of the block's 64 staged
+// pairs, halves ph0 .. ph0 + NT - 1 (the block has 8 / NT waves); two tiles share every unpacked
+// code word. base + src: this lane's pair's row (pair lane % 64, as a word offset below 2^32).
+// ntiles: how many of the NT tiles hold pairs (0 for a wave of one empty tile: it only stages and
+// waits). acc[t][i]: D element i of tile t, in units of the pair's step.
+template <int FMT, int NT>
+__device__ __forceinline__ void gemm_rows(const uint8_t* codes0, const uint32_t* sm0, int K, const uint32_t* base,
+                                          uint32_t src, int ph0, int ntiles, uint32_t* lds, f32x16 (&acc)[NT]) {
+  using S = Staging<8 / NT>;
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int nblk = K / 32, nstep = nblk / kStepBlocks;
   const size_t rsm = sm_row_words<FMT>(K);
-  live = __builtin_amdgcn_readfirstlane(static_cast<int>(live)) != 0;  // one value per wave
+  ntiles = __builtin_amdgcn_readfirstlane(ntiles);  // one value per wave
+  const bool live = ntiles > 0;
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));  // kept in a VGPR (see codes8)
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
-  // The rows this lane stages: those of pairs staged_pair(n), whose lanes hold them as `src`.
-  uint32_t srcs[kChunksPerWave];
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+  // The rows this lane stages: those of pairs S::pair(n), whose lanes hold them as `src`.
+  uint32_t srcs[S::kLoads];
 #pragma unroll
-  for (int n = 0; n < kChunksPerWave; ++n) srcs[n] = __shfl(src, staged_pair(n));
-  const uint32_t ssrc = __shfl(src, (threadIdx.x >> 6) * kPairsPerWave + (lane & (kPairsPerWave - 1)));
-  u32x4 nxt[kChunksPerWave + 1];
-  StepCodes cur_w[NM], nxt_w[NM];
-  if (live) {
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-      load_step_codes<FMT>(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + c * rsm, 0, cur_w[m]);
-  }
-  fetch_step(base, srcs, ssrc, 0, nxt);
-  store_step(nxt, lds);
+  for (int n = 0; n < S::kLoads; ++n) srcs[n] = __shfl(src, S::pair(n));
+  const uint32_t ssrc = __shfl(src, (threadIdx.x >> 6) * S::kPairs + (lane & (S::kPairs - 1)));
+  u32x4 nxt[S::kLoads + 1];
+  StepCodes cur_w, nxt_w;
+  if (live) load_step_codes<FMT>(codes0 + static_cast<size_t>(c) * (K / 2), sm0 + c * rsm, 0, cur_w);
+  S::fetch(base, srcs, ssrc, 0, nxt);
+  S::store(nxt, lds);
   __syncthreads();
   for (int st = 0; st < nstep; ++st) {
     const int kb0 = st * kStepBlocks;
     const uint32_t* cur = lds + (st & 1) * kStageWords;
     const bool more = st + 1 < nstep;
-    // The next step's codes, scale/min words, block sums and values are loaded while this step
+    // The next step's codes, scale/min words and staged values are loaded while this step
     // computes (its own arrived during the previous step).
-    if (live && more) {
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-        load_step_codes<FMT>(codes0[m] + static_cast<size_t>(c) * (K / 2), sm0[m] + c * rsm, kb0 + kStepBlocks,
-                             nxt_w[m]);
-    }
-    if (more) fetch_step(base, srcs, ssrc, st + 1, nxt);
+    if (live && more)
+      load_step_codes<FMT>(codes0 + static_cast<size_t>(c) * (K / 2), sm0 + c * rsm, kb0 + kStepBlocks, nxt_w);
+    if (more) S::fetch(base, srcs, ssrc, st + 1, nxt);
     if (live) {
-      const float2 x2 = *reinterpret_cast<const float2*>(cur + (32 * ph + c) * kPairStride + kStepChunks * 4 + 2 * h);
-      uint2 cw[NM][kStepBlocks];
+      uint2 cw[kStepBlocks];
+      trade_halves(cur_w, cw);
+      const uint32_t* prow[NT];
+      float2 x2[NT];  // the step's block sums of the tile's pairs (blocks kb0 + h, kb0 + 2 + h)
 #pragma unroll
-      for (int m = 0; m < NM; ++m) trade_halves(cur_w[m], cw[m]);
+      for (int t = 0; t < NT; ++t) {
+        prow[t] = cur + (32 * (ph0 + t) + c) * kPairStride;
+        x2[t] = *reinterpret_cast<const float2*>(prow[t] + kStepChunks * 4 + 2 * h);
+      }
 #pragma unroll
       for (int bs = 0; bs < kStepBlocks; ++bs) {
-        f16x8 ap[2][2];  // [plane][instruction]: group 2h + s of the block
+        const f16x8 b0 = codes8(cw[bs].x, magic), b1 = codes8(cw[bs].y, magic);
+        const float sc = step_scale<FMT>(cur_w.smw, kb0, bs);
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (NT > 1) {
+            if (t >= ntiles) break;
+          }
+          f16x8 ap[2][2];  // [plane][instruction]: group 2h + s of the block
 #pragma unroll
-          for (int q = 0; q < 2; ++q)
-            ap[p][q] = *reinterpret_cast<const f16x8*>(
-                cur + (32 * ph + c) * kPairStride + ((bs * 2 + p) * 4 + 2 * h + q) * 4);
+          for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const f16x8 b0 = codes8(cw[m][bs].x, magic), b1 = codes8(cw[m][bs].y, magic);
-          const float sc = step_scale<FMT>(cur_w[m].smw, kb0, bs);
+            for (int q = 0; q < 2; ++q)
+              ap[p][q] = *reinterpret_cast<const f16x8*>(prow[t] + ((bs * 2 + p) * 4 + 2 * h + q) * 4);
           const f32x16 z = {};
           f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[1][0], b0, z, 0, 0, 0);
           d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[1][1], b1, d, 0, 0, 0);
           d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[0][0], b0, d, 0, 0, 0);
           d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[0][1], b1, d, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[m][i] = fmaf(sc, d[i], acc[m][i]);
+          for (int i = 0; i < 16; ++i) acc[t][i] = fmaf(sc, d[i], acc[t][i]);
         }
       }
-      // The minimum's term of the 4 blocks (instruction j takes blocks kb0 + 2j + l / 32), after the
-      // folds: the next step's integer products then cover its latency before acc is needed again.
+      // The minimum's term of the 4 blocks (instruction j takes blocks kb0 + 2j + l / 32), after
+      // the folds: the next step's products then cover its latency before acc is needed again.
+      const float m0 = step_min<FMT>(cur_w.smw, kb0, h), m1 = step_min<FMT>(cur_w.smw, kb0, 2 + h);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const float m0 = step_min<FMT>(cur_w[m].smw, kb0, h);
-        const float m1 = step_min<FMT>(cur_w[m].smw, kb0, 2 + h);
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2.x, m0, acc[m], 0, 0, 0);
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2.y, m1, acc[m], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (NT > 1) {
+          if (t >= ntiles) break;
+        }
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[t].x, m0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(x2[t].y, m1, acc[t], 0, 0, 0);
       }
     }
-    if (more) store_step(nxt, lds + ((st + 1) & 1) * kStageWords);  // read two steps ago
+    if (more) S::store(nxt, lds + ((st + 1) & 1) * kStageWords);  // read two steps ago
     __syncthreads();  // step st read by every wave; step st + 1 staged
-    if (live && more) {
-#pragma unroll
-      for (int m = 0; m < NM; ++m) cur_w[m] = nxt_w[m];
-    }
+    if (live && more) cur_w = nxt_w;
   }
 }
 
-// Pair (within the block's 64) of D element i for this lane.
+// Pair (within the block's 64) of D element i of pair half ph for this lane.
 __device__ __forceinline__ int d_pair(int ph, int i) {
   return 32 * ph + 8 * (i >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (i & 3);
 }
 
-// Gate/up: work unit = (item, 64 rows of I). Waves 0-3 take gate, 4-7 up (rows 32 (w & 1)..,
-// pairs 32 ((w >> 1) & 1)..); the up waves hand their sums to the gate waves through LDS, which
-// write silu(g) * v of the block's rows for the item's pairs into hbuf (by pair slot).
-template <int FMT>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4))) void pf_gateup_kernel(PfArgs a, int layer) {
+// Gate/up: work unit = (item, 64 rows of I), 8 / NT waves. NT = 2 (the form launched): waves 0-1
+// take gate, 2-3 up (rows 32 (w & 1)..), each against all 64 pairs as two tiles. NT = 1: waves 0-3
+// gate, 4-7 up (rows 32 (w & 1).., pairs 32 ((w >> 1) & 1)..). The up waves hand their sums to the
+// gate waves through LDS, which write silu(g) * v of the block's rows for the item's pairs into
+// hbuf (by pair slot).
+template <int FMT, int NT>
+__global__ __launch_bounds__(64 * 8 / NT) __attribute__((amdgpu_waves_per_eu(4 / NT))) void pf_gateup_kernel(
+    PfArgs a, int layer) {
   extern __shared__ uint32_t lds[];
   const int I = a.I, H = a.H;
   const int tiles = I / kTile;
@@ -605,37 +608,48 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4)
   const int4 item = a.items[it];
   const int e = item.x, p0 = item.y, np = item.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int mt = wave >> 2, rh = wave & 1, ph = (wave >> 1) & 1;
+  const int mt = NT == 2 ? wave >> 1 : wave >> 2, rh = wave & 1, ph0 = NT == 2 ? 0 : (wave >> 1) & 1;
+  const int ntiles = NT == 2 ? (np > 32 ? 2 : 1) : (32 * ph0 < np ? 1 : 0);
   const int32_t* pairs = a.pairs + static_cast<size_t>(layer) * a.Pcap;
   __shared__ float s_step[kTile];  // the item's pairs' steps, for the epilogue
-  const int tsrc = pairs[p0 + min(lane, np - 1)] & 0xFFFF;                  // staging: pair lane
+  const int tsrc = pairs[p0 + min(lane, np - 1)] & 0xFFFF;  // staging: pair lane
   if (wave == 0) s_step[lane] = a.xstep[tsrc];  // visible after the GEMM's first barrier
   const uint32_t src = static_cast<uint32_t>(tsrc) * static_cast<uint32_t>(pf_row_words(H));
   const size_t row = static_cast<size_t>(e) * I + i0 + 32 * rh;  // the wave's first weight row
-  const uint8_t* codes[1] = {(mt ? a.w.up_q : a.w.gate_q) + row * (H / 2)};
-  const uint32_t* sm[1] = {(mt ? a.w.up_sm : a.w.gate_sm) + row * sm_row_words<FMT>(H)};
-  f32x16 acc[1];
-  gemm_rows<1, FMT>(codes, sm, H, a.xq, src, ph, 32 * ph < np, lds, acc);
-  // The staging buffers are free (the GEMM ends on a barrier): up sums [rh][ph][i][lane].
-  float* xch = reinterpret_cast<float*>(lds) + ((rh * 2 + ph) * 16) * 64 + lane;
+  const uint8_t* codes = (mt ? a.w.up_q : a.w.gate_q) + row * (H / 2);
+  const uint32_t* sm = (mt ? a.w.up_sm : a.w.gate_sm) + row * sm_row_words<FMT>(H);
+  f32x16 acc[NT];
+  gemm_rows<FMT, NT>(codes, sm, H, a.xq, src, ph0, ntiles, lds, acc);
+  // The staging buffers are free (the GEMM ends on a barrier): up sums [rh][pair half][i][lane].
+  float* xch = reinterpret_cast<float*>(lds) + lane;
   if (mt == 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) xch[i * 64] = acc[0][i];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xch[((rh * 2 + ph0 + t) * 16 + i) * 64] = acc[t][i];
   }
   __syncthreads();
   if (mt == 0) {
     const int col = i0 + 32 * rh + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int pr = d_pair(ph, i);
-      const float step = s_step[pr];
-      if (pr < np) a.hbuf[static_cast<size_t>(p0 + pr) * I + col] = silu(step * acc[0][i]) * (step * xch[i * 64]);
-    }
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int pr = d_pair(ph0 + t, i);
+        const float step = s_step[pr];
+        if (pr < np)
+          a.hbuf[static_cast<size_t>(p0 + pr) * I + col] =
+              silu(step * acc[t][i]) * (step * xch[((rh * 2 + ph0 + t) * 16 + i) * 64]);
+      }
   }
 }
+constexpr int kGateupTiles = 2;  // tiles per gate/up wave: 4 waves of 32 rows x 64 pairs
+constexpr int kGateupThreads = 64 * 8 / kGateupTiles;
 
-// Down: work unit = (item, 128 rows of H); wave w takes rows 32 (w & 3).. and pairs 32 (w >> 2)...
-// Writes W_d h of the block's rows for the item's pairs into ybuf (by pair slot).
+// Down: work unit = (item, 128 rows of H), 8 waves; wave w takes rows 32 (w & 3).. and pairs
+// 32 (w >> 2)... (Down's reduction is 4 steps at I = 512; with two tiles per wave and so two waves
+// per SIMD it was slower.) Writes W_d h of the block's rows for the item's pairs into ybuf (by pair
+// slot).
 constexpr int kDownRows = 128;
 template <int FMT>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4))) void pf_down_kernel(PfArgs a, int layer) {
@@ -653,10 +667,10 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4)
   const uint32_t src = static_cast<uint32_t>(p0 + min(lane, np - 1)) * static_cast<uint32_t>(pf_row_words(I));
   if (wave == 0) s_step[lane] = a.hstep[p0 + min(lane, np - 1)];  // visible after the first barrier
   const size_t row = static_cast<size_t>(e) * H + h0 + 32 * rq;
-  const uint8_t* codes[1] = {a.w.down_q + row * (I / 2)};
-  const uint32_t* sm[1] = {a.w.down_sm + row * sm_row_words<FMT>(I)};
+  const uint8_t* codes = a.w.down_q + row * (I / 2);
+  const uint32_t* sm = a.w.down_sm + row * sm_row_words<FMT>(I);
   f32x16 acc[1];
-  gemm_rows<1, FMT>(codes, sm, I, a.hq, src, ph, 32 * ph < np, lds, acc);
+  gemm_rows<FMT, 1>(codes, sm, I, a.hq, src, ph, 32 * ph < np ? 1 : 0, lds, acc);
   const int col = h0 + 32 * rq + (lane & 31);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {

@@ -355,7 +355,8 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
   const int dn_units = ((ib * (H / pf::kDownRows) + 7) / 8) * 8;
   const PfKernelFn topk = pf_pick_topk(E);
   const bool s256 = h->cfg.weight_format == MOE_WEIGHT_Q4S256;
-  const PfKernelFn gateup = s256 ? pf::pf_gateup_kernel<kFmtQ4S256> : pf::pf_gateup_kernel<kFmtQ4B32>;
+  const PfKernelFn gateup = s256 ? pf::pf_gateup_kernel<kFmtQ4S256, pf::kGateupTiles>
+                                 : pf::pf_gateup_kernel<kFmtQ4B32, pf::kGateupTiles>;
   const PfKernelFn down = s256 ? pf::pf_down_kernel<kFmtQ4S256> : pf::pf_down_kernel<kFmtQ4B32>;
   int i = 0;
   auto launch = [&](const void* fn, dim3 grid, int threads, int shmem, void** params, int layer, int kind) {
@@ -389,7 +390,7 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
             hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::pf_scatter_kernel), dim3((np + kThreads - 1) / kThreads),
                     kThreads, 0, gp, l, 1)) != hipSuccess ||
-        (e = launch(reinterpret_cast<const void*>(gateup), dim3(gu_units), pf::kGemmThreads,
+        (e = launch(reinterpret_cast<const void*>(gateup), dim3(gu_units), pf::kGateupThreads,
                     pf::kGemmLds, gp, l, 2)) != hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::quant_rows_kernel), dim3((np + kWaves - 1) / kWaves), kThreads,
                     0, qh, l, 3)) != hipSuccess ||
