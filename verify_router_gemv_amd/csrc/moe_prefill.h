@@ -127,20 +127,24 @@ static __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const float
     sum += dpp_f32<kDppXor1>(sum);
     sum += dpp_f32<kDppXor2>(sum);
     sum += dpp_f32<kDppHalfMirror>(sum);  // the 8 lanes of this block
-    if (in) {
-      // elements 4*sub + i of the block: group sub / 2, word i, low half for even sub, high for odd
-      const int b = c >> 3, sub = c & 7;
-      uint32_t* step_w = drow + (b >> 2) * kStepWords;
-      uint16_t* base = reinterpret_cast<uint16_t*>(step_w + (b & 3) * kPfWords);
-      const int g = sub >> 1, half = sub & 1;
+    // Elements 4 sub + i of the block (sub = lane % 8) are word i of group sub / 2 in each plane:
+    // the low half for even sub, the high half for odd. Lanes 2m and 2m + 1 trade halves, so the
+    // even lane stores the group's 4 hi-plane words and the odd lane its 4 lo-plane words.
+    const int half = lane & 1;
+    uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 hi = static_cast<_Float16>(e[i]);
-        const _Float16 lo = static_cast<_Float16>(e[i] - static_cast<float>(hi));
-        base[((0 * 4 + g) * 4 + i) * 2 + half] = __builtin_bit_cast(uint16_t, hi);
-        base[((1 * 4 + g) * 4 + i) * 2 + half] = __builtin_bit_cast(uint16_t, lo);
-      }
-      if (sub == 0) reinterpret_cast<float*>(step_w)[kStepChunks * 4 + (b & 1) * 2 + ((b >> 1) & 1)] = sum;
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 hi = static_cast<_Float16>(e[i]);
+      const _Float16 lo = static_cast<_Float16>(e[i] - static_cast<float>(hi));
+      const uint32_t hb = __builtin_bit_cast(uint16_t, hi), lb = __builtin_bit_cast(uint16_t, lo);
+      const uint32_t got = dpp_u32<kDppXor1>(half ? hb : lb);  // the partner's hi (to an even lane) or lo
+      w[i] = half ? (got | (lb << 16)) : (hb | (got << 16));
+    }
+    if (in) {
+      const int b = c >> 3, g = (c & 7) >> 1;
+      uint32_t* step_w = drow + (b >> 2) * kStepWords;
+      *reinterpret_cast<uint4*>(step_w + (b & 3) * kPfWords + (half * 4 + g) * 4) = make_uint4(w[0], w[1], w[2], w[3]);
+      if ((c & 7) == 0) reinterpret_cast<float*>(step_w)[kStepChunks * 4 + (b & 1) * 2 + ((b >> 1) & 1)] = sum;
     }
   }
 }
