@@ -684,6 +684,107 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4)
   }
 }
 
+// Down for I <= kDown32MaxI (NSTEP = I / 128 steps): work unit = (item, pair half, 256 rows of H),
+// 8 waves, wave w taking rows 32 w.. against the half's (up to) 32 pairs. The block copies those
+// pairs' whole rows into LDS once (70 KB at I = 512, so two blocks share a CU and one block's copy
+// overlaps the other's compute; a row's words in order, consecutive lanes reading consecutive 16
+// bytes of one row), then each wave runs its NSTEP steps with no barrier, its codes loaded two steps
+// ahead; the step loop is unrolled, so the code registers rotate without copies. Per unit of work
+// this copies the rows half as often as pf_down_kernel. Each pair's row is padded to a stride of
+// 4 words mod 32, so the 16-byte reads of 32 consecutive pairs are free of bank conflicts.
+constexpr int kDown32Rows = 256;
+constexpr int kDown32MaxI = 512;
+__host__ __device__ constexpr int down32_stride(int I) { return pf_row_words(I) + (36 - pf_row_words(I) % 32) % 32; }
+__host__ __device__ constexpr int down32_lds(int I) { return 32 * down32_stride(I) * 4; }
+template <int FMT, int NSTEP>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4))) void pf_down32_kernel(PfArgs a, int layer) {
+  extern __shared__ uint32_t lds[];
+  constexpr int I = NSTEP * 32 * kStepBlocks;
+  constexpr int RW = pf_row_words(I), PS = down32_stride(I), RQ = RW / 4;
+  constexpr int kCopies = (32 * RQ + kGemmThreads - 1) / kGemmThreads;
+  const int H = a.H;
+  const int tiles = H / kDown32Rows;
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int it = unit / (2 * tiles), rem = unit - it * 2 * tiles, half = rem / tiles;
+  const int h0 = (rem - half * tiles) * kDown32Rows;
+  if (it >= *a.n_items) return;  // whole blocks leave together
+  const int4 item = a.items[it];
+  const int e = item.x, q0 = item.y + 32 * half, nq = min(32, item.z - 32 * half);
+  if (nq <= 0) return;           // an item of at most 32 pairs has no second half
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
+  __shared__ float s_step[32];
+  if (tid < 32) s_step[tid] = a.hstep[q0 + min(tid, nq - 1)];
+  // The wave's weight rows and the first two steps' codes, issued before the copy.
+  const size_t row = static_cast<size_t>(e) * H + h0 + 32 * wave + c;
+  const uint8_t* codes = a.w.down_q + row * (I / 2);
+  const uint32_t* sm = a.w.down_sm + row * sm_row_words<FMT>(I);
+  StepCodes w[NSTEP];
+#pragma unroll
+  for (int st = 0; st < (NSTEP < 2 ? NSTEP : 2); ++st) load_step_codes<FMT>(codes, sm, st * kStepBlocks, w[st]);
+  // The half's 32 pair rows (pairs past nq repeat the last): 16-byte chunk q is chunk q % RQ of pair q / RQ.
+  {
+    u32x4 v[kCopies];
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int q = min(tid + i * kGemmThreads, 32 * RQ - 1);
+      const int pr = q / RQ, r = q - pr * RQ;
+      v[i] = *reinterpret_cast<const u32x4*>(a.hq + static_cast<size_t>(q0 + min(pr, nq - 1)) * RW + 4 * r);
+    }
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int q = tid + i * kGemmThreads;
+      if (q < 32 * RQ) {
+        const int pr = q / RQ, r = q - pr * RQ;
+        *reinterpret_cast<u32x4*>(lds + pr * PS + 4 * r) = v[i];
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));  // kept in a VGPR (see codes8)
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const uint32_t* prow0 = lds + c * PS;
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st) {
+    if (st + 2 < NSTEP) load_step_codes<FMT>(codes, sm, (st + 2) * kStepBlocks, w[st + 2]);
+    const int kb0 = st * kStepBlocks;
+    const uint32_t* prow = prow0 + st * kStepWords;
+    const float2 x2 = *reinterpret_cast<const float2*>(prow + kStepChunks * 4 + 2 * h);
+    uint2 cw[kStepBlocks];
+    trade_halves(w[st], cw);
+#pragma unroll
+    for (int bs = 0; bs < kStepBlocks; ++bs) {
+      const f16x8 b0 = codes8(cw[bs].x, magic), b1 = codes8(cw[bs].y, magic);
+      const float sc = step_scale<FMT>(w[st].smw, kb0, bs);
+      f16x8 ap[2][2];  // [plane][instruction]: group 2h + s of the block
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          ap[p][q] = *reinterpret_cast<const f16x8*>(prow + ((bs * 2 + p) * 4 + 2 * h + q) * 4);
+      const f32x16 z = {};
+      f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[1][0], b0, z, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[1][1], b1, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[0][0], b0, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[0][1], b1, d, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = fmaf(sc, d[i], acc[i]);
+    }
+    const float m0 = step_min<FMT>(w[st].smw, kb0, h), m1 = step_min<FMT>(w[st].smw, kb0, 2 + h);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x2.x, m0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x2.y, m1, acc, 0, 0, 0);
+  }
+  const int col = h0 + 32 * wave + c;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int pr = d_pair(0, i);
+    const float step = s_step[pr];
+    if (pr < nq) a.ybuf[static_cast<size_t>(q0 + pr) * H + col] = step * acc[i];
+  }
+}
+
 // out[t][h] = (residual ? x[t][h] : 0) + sum over ranks j = 0..k-1, in that order, of
 // p[t][j] * y[slot(t, j)][h]. Grid (T, ceil(H / 1024)) x 256 threads, four columns per thread.
 static __global__ __launch_bounds__(kThreads) void pf_combine_kernel(PfArgs a, int layer) {

@@ -302,6 +302,16 @@ typedef void (*PfKernelFn)(pf::PfArgs, int);
 // (68 -> 32 us); at 4096 rows the split is slightly slower (159 vs 148 us).
 constexpr int kPfSplitKRows = 2048;
 
+// The down kernel that copies rows once, for the round's weight format and I / 128 steps (1..4).
+static PfKernelFn pf_pick_down32(bool s256, int nstep) {
+  switch (nstep) {
+    case 1: return s256 ? pf::pf_down32_kernel<kFmtQ4S256, 1> : pf::pf_down32_kernel<kFmtQ4B32, 1>;
+    case 2: return s256 ? pf::pf_down32_kernel<kFmtQ4S256, 2> : pf::pf_down32_kernel<kFmtQ4B32, 2>;
+    case 3: return s256 ? pf::pf_down32_kernel<kFmtQ4S256, 3> : pf::pf_down32_kernel<kFmtQ4B32, 3>;
+    default: return s256 ? pf::pf_down32_kernel<kFmtQ4S256, 4> : pf::pf_down32_kernel<kFmtQ4B32, 4>;
+  }
+}
+
 static PfKernelFn pf_pick_topk(int E) {
   if (E <= 64) return pf::pf_topk_kernel<1>;
   if (E <= 128) return pf::pf_topk_kernel<2>;
@@ -352,12 +362,16 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
   const int np = T * k;
   const int ib = pf_items_bound(np, E);
   const int gu_units = ((ib * (I / pf::kTile) + 7) / 8) * 8;
-  const int dn_units = ((ib * (H / pf::kDownRows) + 7) / 8) * 8;
+  // Down: rows copied once per (item half, 256 rows of H) where they fit (I <= 512), else per step.
+  const bool dn32 = I <= pf::kDown32MaxI;
+  const int dn_units = ((ib * (dn32 ? 2 * (H / pf::kDown32Rows) : H / pf::kDownRows) + 7) / 8) * 8;
+  const int dn_lds = dn32 ? pf::down32_lds(I) : pf::kGemmLds;
   const PfKernelFn topk = pf_pick_topk(E);
   const bool s256 = h->cfg.weight_format == MOE_WEIGHT_Q4S256;
   const PfKernelFn gateup = s256 ? pf::pf_gateup_kernel<kFmtQ4S256, pf::kGateupTiles>
                                  : pf::pf_gateup_kernel<kFmtQ4B32, pf::kGateupTiles>;
-  const PfKernelFn down = s256 ? pf::pf_down_kernel<kFmtQ4S256> : pf::pf_down_kernel<kFmtQ4B32>;
+  const PfKernelFn down = dn32 ? pf_pick_down32(s256, I / (32 * pf::kStepBlocks))
+                                : s256 ? pf::pf_down_kernel<kFmtQ4S256> : pf::pf_down_kernel<kFmtQ4B32>;
   int i = 0;
   auto launch = [&](const void* fn, dim3 grid, int threads, int shmem, void** params, int layer, int kind) {
     if (kinds) kinds[i] = layer * kKernelsPerLayer + kind;
@@ -394,8 +408,8 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
                     pf::kGemmLds, gp, l, 2)) != hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::quant_rows_kernel), dim3((np + kWaves - 1) / kWaves), kThreads,
                     0, qh, l, 3)) != hipSuccess ||
-        (e = launch(reinterpret_cast<const void*>(down), dim3(dn_units), pf::kGemmThreads,
-                    pf::kGemmLds, gp, l, 3)) != hipSuccess ||
+        (e = launch(reinterpret_cast<const void*>(down), dim3(dn_units), pf::kGemmThreads, dn_lds, gp, l, 3)) !=
+            hipSuccess ||
         (e = launch(reinterpret_cast<const void*>(pf::pf_combine_kernel), dim3(T, (H + 4 * kThreads - 1) / (4 * kThreads)),
                     kThreads, 0, gp, l, 4)) != hipSuccess)
       return hip_fail(h, e);
