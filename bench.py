@@ -25,7 +25,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TS = (1, 3, 8)
+TS = (1, 3, 8)                 # the headline step's widths
+TS_SWEEP = (1, 2, 3, 4, 5, 8)  # the verify sweep's widths, reported per width
+CONTROL_BUF_BYTES = 2 << 30
 
 
 def parse():
@@ -36,7 +38,7 @@ def parse():
     p.add_argument("--replicas", type=int, default=32)
     p.add_argument("--graph", action="store_true", help="replay captured hipGraphs instead of eager launches")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="seconds per CPU-baseline setting")
     p.add_argument("--pmc-calibrate", action="store_true",
                    help="finish with a copy of 1 GiB (torch.neg) that calibrates the HBM byte counters")
     p.add_argument("--no-extra", action="store_true", help="skip the wide-round and deep-stack sections")
@@ -160,21 +162,23 @@ def main():
                                       for n, v in zip(("logits", "select", "gateup", "down", "combine"), kms)}}
 
     # Per-width round latency (eager, events on torch's current stream = the handles' stream,
-    # one synchronised round at a time) and per-kernel durations; outside the timed region.
+    # one synchronised round at a time) and per-kernel durations; outside the timed region. All six
+    # verify widths (the headline step covers 1, 3 and 8); the rounds of the widths the step does
+    # not run use the same handles (max_rows 8).
     per_T = {}
-    for T in TS:
-        lat = []
+    ctl_buf = torch.empty(CONTROL_BUF_BYTES // 4, device=dev)
+    ctl_off = [0]
+    for T in TS_SWEEP:
+        if T not in acts:
+            acts[T] = torch.stack([synth.make_activations(cfg, T, seed=0, round_idx=r, device=dev)
+                                   for r in range(n_acts)])
+            outs[T] = torch.empty((T, cfg.H), device=dev)
+        lat, nus = [], []
         for r in range(64):
             h = handles[(sc[0] + r) % R]
             a = acts[T][r % n_acts]
-            torch.cuda.synchronize()
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record()
-            h.run(a, cfg.k, outs[T])
-            e.record()
-            e.synchronize()
-            lat.append(s.elapsed_time(e) * 1e3)
+            lat.append(event_us(torch, lambda: h.run(a, cfg.k, outs[T])))
+            nus.append(h.last_unique()[0])
         for h in handles:
             h.profile(True)
             h.profile_read()
@@ -187,10 +191,28 @@ def main():
             runs += n
             h.profile(False)
         sc[0] += 64
-        nus = [nu[(T, r % n_acts)] for r in range(64)]
         n_u = float(np.mean(nus))
         mb = synth.inputs.metric_bytes(cfg, n_u, T)
         med = float(np.median(lat))
+        # Byte floor: every handle runs a round at T, then (R - 1 rounds later, its bytes long out of
+        # the 256 MB cache) replays only its weight reads, with the same launches per layer.
+        flo = []
+        for rep in range(2):
+            for r in range(R):
+                handles[r].run(acts[T][(rep * R + r) % n_acts], cfg.k, outs[T])
+            for r in range(R):
+                flo.append(event_us(torch, handles[r].floor))
+        # Streaming control: the same number of bytes, one contiguous read, each from a new window of
+        # a 2 GB buffer (no window is read again before the buffer has cycled).
+        ctl = []
+        nbytes = (int(mb) + 15) // 16 * 16
+        for r in range(32):
+            if ctl_off[0] + nbytes > CONTROL_BUF_BYTES:
+                ctl_off[0] = 0
+            view = ctl_buf[ctl_off[0] // 4:(ctl_off[0] + nbytes) // 4]
+            ctl_off[0] += nbytes
+            ctl.append(event_us(torch, lambda: handles[0].stream_read(view)))
+        fmed, cmed = float(np.median(flo)), float(np.median(ctl))
         per_T[str(T)] = {
             "round_us_median": round(med, 2),
             "round_us_p10_p90": [round(float(np.percentile(lat, 10)), 2), round(float(np.percentile(lat, 90)), 2)],
@@ -198,21 +220,52 @@ def main():
             "n_unique": round(n_u, 2),
             "metric_bytes": int(mb),
             "metric_GBps": round(mb / med / 1e3, 1),
+            "frac_of_peak": round(mb / med / 1e3 / HBM_PEAK_GBS, 4),
             "kernel_us": {n: round(float(v) * 1e3 / runs, 2) for n, v in
                           zip(("logits", "select", "gateup", "down", "combine"), kms)},
+            "byte_floor": {"us_median": round(fmed, 2), "GBps": round(mb / fmed / 1e3, 1),
+                           "round_frac_of_floor": round(fmed / med, 3),
+                           "what": "the round's weight reads alone (router, unique experts' gate/up, down) "
+                                   "at the same addresses, 3 launches per layer"},
+            "stream_control": {"us_median": round(cmed, 2), "GBps": round(mb / cmed / 1e3, 1),
+                               "what": "one contiguous read of the metric bytes, one launch, same session"},
         }
-    # extra verify-row cost, T=1 -> 3 -> 8
-    per_T["extra_row"] = {
-        f"{a}->{b}": {
-            "us_per_row": round((per_T[str(b)]["round_us_median"] - per_T[str(a)]["round_us_median"]) / (b - a), 2),
-            "bytes_per_row": int((per_T[str(b)]["metric_bytes"] - per_T[str(a)]["metric_bytes"]) / (b - a)),
-        } for a, b in ((1, 3), (3, 8))}
+    del ctl_buf
+    # extra verify-row cost between consecutive widths and against T = 1
+    per_T["extra_row"] = {}
+    for a_, b_ in list(zip(TS_SWEEP[:-1], TS_SWEEP[1:])) + [(1, 8)]:
+        pa, pb = per_T[str(a_)], per_T[str(b_)]
+        per_T["extra_row"][f"{a_}->{b_}"] = {
+            "us_per_row": round((pb["round_us_median"] - pa["round_us_median"]) / (b_ - a_), 2),
+            "bytes_per_row": int((pb["metric_bytes"] - pa["metric_bytes"]) / (b_ - a_)),
+            "unique_experts_per_row": round((pb["n_unique"] - pa["n_unique"]) / (b_ - a_), 2),
+        }
+
+    # Labelled extra: the same widths replayed as captured hipGraphs (one graph per (T, k) and handle;
+    # each round names a new input buffer, so each replay first uploads the ingress pointers).
+    graph_per_T = None
+    if not args.no_extra and not args.graph:
+        ghs = [MoeRound([reps[i]], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(TS_SWEEP), use_graph=True, **shape)
+               for i in range(R)]
+        graph_per_T = {"mode": "hipGraph replay, one graph per (T, k), ingress upload per round"}
+        for T in TS_SWEEP:
+            for r in range(R):
+                ghs[r].run(acts[T][r % n_acts], cfg.k, outs[T])  # capture
+            lat = [event_us(torch, lambda: ghs[r % R].run(acts[T][(r + 7) % n_acts], cfg.k, outs[T]))
+                   for r in range(64)]
+            med = float(np.median(lat))
+            graph_per_T[str(T)] = {"round_us_median": round(med, 2), "tok_per_s": round(T / med * 1e6, 1),
+                                   "eager_round_us_median": per_T[str(T)]["round_us_median"]}
+        for h in ghs:
+            h.close()
+        del ghs
 
     for h in handles:
         h.close()
     del handles, reps
     torch.cuda.empty_cache()
 
+    decode = None if args.no_extra else decode_rounds(torch, np, synth, MoeRound)
     exact = None if args.no_extra else exact_rounds(cfg, base, acts, torch, np, MoeRound)
     wide = None if args.no_extra else wide_rounds(cfg, base, torch, np, synth, MoeRound)
     deep = None if args.no_extra else deep_stack(torch, np, synth, MoeRound)
@@ -242,6 +295,8 @@ def main():
                    "mode": "hipGraph" if args.graph else "eager", "weight_replicas": args.replicas,
                    "launch": shape or "default"},
         "per_T": per_T,
+        "graph_per_T": graph_per_T,
+        "decode": decode,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "exact_mode": exact,
@@ -266,6 +321,19 @@ def calibration_copy(torch, dev):
 
 
 INT8_DENSE_PEAK_OPS = 5.0e15
+BF16_DENSE_PEAK_FLOPS = 2.5e15
+
+
+def event_us(torch, fn):
+    """Microseconds between events recorded on the current stream around fn(), synchronised."""
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) * 1e3
 
 
 def timed_rounds(h, xs, k, out, n, torch):
@@ -282,6 +350,58 @@ def timed_rounds(h, xs, k, out, n, torch):
         e.synchronize()
         lat.append(s.elapsed_time(e) * 1e3)
     return float(np.median(lat)), float(np.percentile(lat, 10)), float(np.percentile(lat, 90))
+
+
+def decode_rounds(torch, np, synth, MoeRound, n_rounds=1000, replicas=8):
+    """Batch-1 decode, one layer (H=2048, E=128 with a Zipf(1.1) router bias, top-8, I=768): 1000
+    rounds with fresh seeded activations over 8 weight replicas (3 GB, beyond the 256 MB cache):
+    latency, unique experts, metric bytes, per-kernel time and the byte floor."""
+    cfg = synth.config("decode")
+    base = synth.make_layer(cfg, seed=0, layer=0, device="cuda")
+    reps = [base] + [base.clone() for _ in range(replicas - 1)]
+    hs = [MoeRound([rp], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=1, use_graph=False) for rp in reps]
+    xs = torch.stack([synth.make_activations(cfg, 1, seed=0, round_idx=r, device="cuda") for r in range(n_rounds)])
+    out = torch.empty((1, cfg.H), device="cuda")
+    for r in range(2 * replicas):
+        hs[r % replicas].run(xs[r], cfg.k, out)
+    lat, nus = [], []
+    for r in range(n_rounds):
+        h = hs[r % replicas]
+        lat.append(event_us(torch, lambda: h.run(xs[r], cfg.k, out)))
+        nus.append(h.last_unique()[0])
+    for h in hs:
+        h.profile(True)
+        h.profile_read()
+    for r in range(64):
+        hs[r % replicas].run(xs[r], cfg.k, out)
+    kms, runs = np.zeros(5), 0
+    for h in hs:
+        ms, n = h.profile_read()
+        kms += np.array(ms[0])
+        runs += n
+        h.profile(False)
+    flo = []
+    for rep in range(4):
+        for r in range(replicas):
+            hs[r].run(xs[rep * replicas + r], cfg.k, out)
+        for r in range(replicas):
+            flo.append(event_us(torch, hs[r].floor))
+    for h in hs:
+        h.close()
+    med, fmed = float(np.median(lat)), float(np.median(flo))
+    nu = float(np.mean(nus))
+    mb = synth.inputs.metric_bytes(cfg, nu, 1)
+    del reps, hs, base
+    torch.cuda.empty_cache()
+    return {"workload": "one MoE layer, H=2048, E=128 (Zipf 1.1 bias), top-8, I=768, T=1; 1000 fresh rounds",
+            "rounds": n_rounds, "round_us_median": round(med, 2),
+            "round_us_p10_p90": [round(float(np.percentile(lat, 10)), 2), round(float(np.percentile(lat, 90)), 2)],
+            "tok_per_s": round(1 / med * 1e6, 1), "n_unique": round(nu, 2), "metric_bytes": int(mb),
+            "metric_GBps": round(mb / med / 1e3, 1), "frac_of_peak": round(mb / med / 1e3 / HBM_PEAK_GBS, 4),
+            "kernel_us": {n: round(float(v) * 1e3 / runs, 2)
+                          for n, v in zip(("logits", "select", "gateup", "down", "combine"), kms)},
+            "byte_floor": {"us_median": round(fmed, 2), "GBps": round(mb / fmed / 1e3, 1),
+                           "round_frac_of_floor": round(fmed / med, 3)}}
 
 
 def exact_rounds(cfg, layer, acts, torch, np, MoeRound):
@@ -319,8 +439,9 @@ def exact_rounds(cfg, layer, acts, torch, np, MoeRound):
 
 def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
     """Copy-heavy wide verify (T = 16, 32, 64 independent rows, same layer shape): round latency,
-    per-kernel time, unique experts and bytes, with the default tile choice and with the
-    matrix-core tile switched off; MFMA utilisation of the gate/up kernel."""
+    per-kernel time, unique experts and bytes, with the default (the integer-dot GEMV for every work
+    item) and with the int8 matrix-core gate/up tile for items of 3+ rows; the round's useful expert
+    flops (2 T k 3 H I) against the dense bf16 matrix peak."""
     cfg = synth.config("wide")
     reps = [layer] + [layer.clone() for _ in range(3)]  # 4 x 503 MB: beyond the 256 MB cache
     res = {}
@@ -328,7 +449,7 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
         xs = [synth.make_activations(cfg, T, seed=0, round_idx=r, device="cuda") for r in range(16)]
         out = torch.empty((T, cfg.H), device="cuda")
         row = {}
-        for name, mfma in (("default", 0), ("no_mfma", -1)):
+        for name, mfma in (("default", 0), ("mfma_tile", 3)):
             hs = [MoeRound([rp], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=64, use_graph=False, mfma_min_rows=mfma)
                   for rp in reps]
             for r in range(8):
@@ -349,7 +470,7 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
                 for npr in np.diff(offs):  # items of <= 4 rows; those with >= 3 rows take the tile
                     for it in range(0, int(npr), 4):
                         rows = min(4, int(npr) - it)
-                        if mfma == 0 and rows >= 3:
+                        if mfma > 0 and rows >= mfma:
                             mfma_ops += 2.0 * 2 * cfg.I * cfg.H * rows
             kms, runs = np.zeros(5), 0
             for h in hs:
@@ -368,9 +489,10 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
                 "kernel_us": {n: round(float(v) * 1e3 / runs, 2)
                               for n, v in zip(("logits", "select", "gateup", "down", "combine"), kms)},
             }
-            if mfma == 0:
-                row[name]["mfma_useful_ops_per_round"] = mfma_ops / 16
-                row[name]["mfma_util_of_int8_peak"] = round(mfma_ops / gu_s / INT8_DENSE_PEAK_OPS, 6) if gu_s else 0.0
+            useful = 2.0 * T * cfg.k * 3 * cfg.H * cfg.I   # the round's expert multiply-adds x 2
+            row[name]["useful_TFLOPs_round"] = round(useful / med / 1e6, 2)
+            row[name]["useful_frac_of_bf16_peak"] = round(useful / (med * 1e-6) / BF16_DENSE_PEAK_FLOPS, 5)
+            row[name]["mfma_tile_ops_per_round"] = mfma_ops / 16
         res[str(T)] = row
     del reps
     torch.cuda.empty_cache()
@@ -436,10 +558,12 @@ def prefill_rounds(layer, torch, np, synth, MoeRound, widths=None):
             "fp16_dense_peak_TFLOPs": round(FP16_DENSE_PEAK_FLOPS / 1e12, 1), "rounds": res}
 
 
-def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager")):
+def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager"), split=True):
     """48 MoE layers (E=512, top-10, I=512), T=3, residual, ~48 GB of expert weights resident (43.5 GB
     in the 4.5-bit layout): one round as one captured hipGraph, and eager, with per-layer unique
-    experts and metric bytes."""
+    experts and metric bytes; the per-kernel split of a layer (dispatch timestamps of eager rounds,
+    averaged over layers and rounds) and the round's byte floor (its weight reads alone, 3 launches
+    per layer, after a 1 GB read that pushes the round's bytes out of the cache)."""
     cfg = synth.config("deep").replace(fmt=fmt)
     t0 = time.perf_counter()
     layers = [synth.make_layer(cfg, seed=0, layer=l, device="cuda") for l in range(cfg.L)]
@@ -449,6 +573,7 @@ def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager")
     out = torch.empty((T, cfg.H), device="cuda")
     res = {"layers": cfg.L, "T": T, "weights_GB": round(cfg.L * cfg.E * cfg.expert_bytes() / 1e9, 2),
            "generate_s": round(gen_s, 1)}
+    flush = torch.empty(CONTROL_BUF_BYTES // 8, device="cuda")
     for mode in modes:
         h = MoeRound(layers, cfg.H, cfg.I, cfg.E, cfg.k, max_rows=T, residual=True, use_graph=(mode == "graph"))
         for r in range(3):
@@ -459,9 +584,29 @@ def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager")
         mb = sum(synth.inputs.metric_bytes(cfg, nu, T) for nu in nus)
         res[mode] = {"round_us_median": round(med, 1), "per_layer_us": round(med / cfg.L, 2),
                      "n_unique_mean": round(float(np.mean(nus)), 2), "metric_bytes": int(mb),
-                     "metric_GBps": round(mb / med / 1e3, 1), "tok_per_s": round(T / med * 1e6, 1)}
+                     "metric_GBps": round(mb / med / 1e3, 1), "frac_of_peak": round(mb / med / 1e3 / HBM_PEAK_GBS, 4),
+                     "tok_per_s": round(T / med * 1e6, 1)}
+        if split and mode == "graph":
+            flo = []
+            for r in range(6):
+                h.run(xs[r], cfg.k, out)
+                h.stream_read(flush)
+                flo.append(event_us(torch, h.floor))
+            fmed = float(np.median(flo))
+            res[mode]["byte_floor"] = {"us_median": round(fmed, 1), "per_layer_us": round(fmed / cfg.L, 2),
+                                       "GBps": round(mb / fmed / 1e3, 1), "round_frac_of_floor": round(fmed / med, 3)}
+        if split and mode == "eager":
+            h.profile(True)
+            h.profile_read()
+            for r in range(6):
+                h.run(xs[r], cfg.k, out)
+            ms, n = h.profile_read()
+            h.profile(False)
+            per = np.array(ms).sum(axis=0) / (n * cfg.L)
+            res[mode]["per_layer_kernel_us"] = {nm: round(float(v) * 1e3, 2) for nm, v in
+                                                zip(("logits", "select", "gateup", "down", "combine"), per)}
         h.close()
-    del layers
+    del layers, flush
     torch.cuda.empty_cache()
     return res
 
@@ -509,12 +654,44 @@ def superblock_rounds(acts, replicas, torch, np, synth, MoeRound):
         h.close()
     del hs, reps, base
     torch.cuda.empty_cache()
-    res["deep_stack"] = deep_stack(torch, np, synth, MoeRound, fmt="q4s256", modes=("graph",))
+    res["deep_stack"] = deep_stack(torch, np, synth, MoeRound, fmt="q4s256", modes=("graph",), split=False)
     return res
 
 
+def host_description():
+    """nproc, the CPU model and this process's affinity mask, as reported by the host."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = []
+    return {"nproc": os.cpu_count(), "cpu_model": model, "affinity": compress_ranges(aff),
+            "usable_cpus": len(aff)}
+
+
+def compress_ranges(ids):
+    out, i = [], 0
+    while i < len(ids):
+        j = i
+        while j + 1 < len(ids) and ids[j + 1] == ids[j] + 1:
+            j += 1
+        out.append(f"{ids[i]}-{ids[j]}" if j > i else f"{ids[i]}")
+        i = j + 1
+    return ",".join(out)
+
+
 def cpu_baseline(cfg, layer, acts, seconds):
-    """The fp64 oracle on the host cores over a bounded sample of the same rounds."""
+    """The fp64 oracle on the host cores over a bounded sample of the same rounds (T = 1, 3, 8
+    cycling): once with the BLAS pool at its default size (all usable cores) and once with one
+    thread."""
     import numpy as np
 
     import oracle
@@ -524,24 +701,37 @@ def cpu_baseline(cfg, layer, acts, seconds):
                else getattr(layer, f).cpu().numpy())
            for f in ("gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")},
     }
-    done_rows, t0, n_rounds = 0, time.perf_counter(), 0
-    r = 0
-    while time.perf_counter() - t0 < seconds or n_rounds < 3:
-        for T in TS:
-            X = acts[T][r % acts[T].shape[0]].cpu().numpy()
-            oracle.moe_round([view], X, cfg.k, residual=False)
-            done_rows += T
-            n_rounds += 1
-        r += 1
-    el = time.perf_counter() - t0
+
+    def sample(limit):
+        done_rows, n_rounds, r = 0, 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < limit or n_rounds < 3:
+            for T in TS:
+                X = acts[T][r % acts[T].shape[0]].cpu().numpy()
+                oracle.moe_round([view], X, cfg.k, residual=False)
+                done_rows += T
+                n_rounds += 1
+            r += 1
+        el = time.perf_counter() - t0
+        return done_rows / el, n_rounds, el
+
+    threads = None
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count()
-    return {"value": round(done_rows / el, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_rounds} rounds ({r} steps of T=1,3,8) of the same workload in {el:.1f}s, "
-                      f"fp64 numpy, weights copied to host"}
+        threadpool_limits = None
+    rate, n_all, el_all = sample(seconds)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            r1, n1, el1 = sample(seconds)
+        one = {"value": round(r1, 2), "unit": "tok/s", "cores": 1,
+               "sample": f"{n1} rounds in {el1:.1f}s"}
+    return {"value": round(rate, 2), "unit": "tok/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"{n_all} rounds (T=1,3,8 cycling) of the same workload in {el_all:.1f}s, fp64 numpy, "
+                      f"weights copied to host; BLAS threads = the pool's default",
+            "one_thread": one, "host": host_description()}
 
 
 if __name__ == "__main__":

@@ -79,10 +79,12 @@ extern "C" {
 #define MOE_ROUND_API
 #endif
 
-/* Supported set (outside it, init refuses with MOE_ERR_UNSUPPORTED).
- * Block set: a reduction length K (H for gate/up, I for down) is supported when K/32 = G * NB
- * with G the largest power of two <= 64 dividing K/32, G >= 4 and NB <= 4 (e.g. K = 128, 256,
- * 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192).  G lanes share one weight row. */
+/* Supported set (outside it, init refuses with MOE_ERR_UNSUPPORTED): H a multiple of 256 up to
+ * 8192; I a multiple of 32 up to 8192 (a multiple of 256 with MOE_WEIGHT_Q4S256, of 128 when
+ * max_rows exceeds 64); E up to 512; k up to min(E, 16); T up to 64 (decode/verify) or 16384
+ * (prefill).  A reduction length K (H for gate/up, I for down) is split over G lanes per weight row
+ * and NB 32-weight blocks per lane (G in 4..64, NB in 1..4); when K/32 has no exact split the
+ * spare block slots are masked, so e.g. I = 64 (an 8-way tensor-parallel shard of I = 512) runs. */
 #define MOE_ROUND_MAX_ROWS 64      /* T_max of decode/verify rounds                     */
 #define MOE_ROUND_MAX_PREFILL_ROWS 16384 /* T_max with the prefill path (see max_rows) */
 #define MOE_ROUND_MAX_EXPERTS 512  /* E     */
@@ -90,7 +92,7 @@ extern "C" {
 
 typedef int32_t moe_status;
 #define MOE_OK 0
-#define MOE_ERR_INVALID_ARG -1  /* null/misaligned pointer, bad size, aliasing  */
+#define MOE_ERR_INVALID_ARG -1  /* null/misaligned pointer, bad size, overlap   */
 #define MOE_ERR_UNSUPPORTED -2  /* a shape outside the supported set            */
 #define MOE_ERR_HIP -3          /* a HIP runtime call failed                    */
 #define MOE_ERR_OOM -4          /* scratch allocation failed                    */
@@ -98,8 +100,8 @@ typedef int32_t moe_status;
 
 typedef struct moe_round_config {
   int32_t abi_version; /* must equal MOE_ROUND_ABI_VERSION                        */
-  int32_t hidden;      /* H: multiple of 256, at most 8192, H/32 in the block set */
-  int32_t inter;       /* I: multiple of 32, I/32 in the block set                */
+  int32_t hidden;      /* H: multiple of 256, at most 8192                       */
+  int32_t inter;       /* I: multiple of 32, at most 8192                        */
   int32_t n_experts;   /* E: 1..512                                               */
   int32_t top_k_max;   /* largest k a run may ask for: 1..min(E, 16)              */
   int32_t n_layers;    /* L >= 1                                                  */
@@ -125,7 +127,9 @@ typedef struct moe_round_config {
   int32_t rows_per_item;  /* rows of one expert per GEMV work item; default 2 for rounds
                              under 16 rows, 4 from 16 rows; 1..64                          */
   int32_t mfma_min_rows;  /* rounds of 16+ rows: work items with at least this many rows
-                             use the int8 matrix-core gate/up tile; default 3, -1 = never  */
+                             use the int8 matrix-core gate/up tile; default -1 = never (the
+                             integer-dot GEMV measured faster at the rows per expert wide
+                             verify rounds produce), 1..64 = from that many rows            */
   int32_t exact;          /* 1: fixed-order combine. The down stage stores each (row, rank)
                              product W_d h and a combine kernel adds them to the residual in
                              rank order: results are bitwise reproducible, and a row's output
@@ -157,20 +161,33 @@ typedef struct moe_layer_weights {
 
 typedef struct moe_round moe_round; /* opaque handle */
 
-/* Pure host check of a configuration; touches no GPU. MOE_OK if init would accept its shape. */
+/* Pure host check of a configuration; touches no GPU. MOE_OK if init would accept its shape.
+ * Refusing unsupported shapes instead of mishandling them: infero README, "Status" (the
+ * tensor-parallel item). */
 MOE_ROUND_API moe_status moe_round_validate_config(const moe_round_config* cfg);
 
 /*
  * Create a handle: validates cfg and layers[0..L-1] (host array of structs holding device
  * pointers), allocates scratch on the current device and binds the handle to `stream`
  * (a hipStream_t; NULL = the null stream).  Graphs are captured lazily, once per (T, k).
+ * Passage: "How AlphaInfer makes local decoding fast", section 2 (one captured graph per decode
+ * round; its buffers are fixed once, and per-request data is written into them).
+ * Errors: MOE_ERR_INVALID_ARG (null or misaligned pointer, bad field), MOE_ERR_UNSUPPORTED (shape
+ * outside the supported set), MOE_ERR_OOM / MOE_ERR_HIP (allocation); *out is NULL on failure.
  */
 MOE_ROUND_API moe_status moe_round_init(const moe_round_config* cfg, const moe_layer_weights* layers,
                           void* stream, moe_round** out);
 
 /*
  * Run one round, asynchronously on the handle's stream.
- *   hidden      device fp32 [T][H] input rows (read only; must not overlap `out`)
+ * Passages: infero README, "Beyond plain text decode" (MoE: a router picks the top-k experts per
+ * row at decode and a counting sort groups the (row, expert) pairs per expert), "Layout" (the
+ * expert is silu(W_g x) * (W_u x) -> W_d), "Design notes" (block weights read in place);
+ * "How AlphaInfer makes local decoding fast", section 2 (per-request data, including which
+ * weights to read, is ingress into fixed buffers: new pointers never rebuild a graph) and
+ * section 3.1 (a verify round's rows share the experts they have in common).
+ *   hidden      device fp32 [T][H] input rows; may be `out` itself (then overwritten), but must
+ *               not partly overlap it
  *   T, k        0 <= T <= max_rows, 1 <= k <= top_k_max; T = 0 is an empty round: nothing is
  *               enqueued, hidden/out/expert_ids/route_w may be NULL, MOE_OK is returned and the
  *               introspection calls report MOE_ERR_STATE until the next round with rows
@@ -179,7 +196,9 @@ MOE_ROUND_API moe_status moe_round_init(const moe_round_config* cfg, const moe_l
  *   out         device fp32 [T][H] result: MoE(x) (residual = 0) or x_L (residual = 1)
  *   expert_ids  device int32 [L][T][k] selected experts per row, descending logit, or NULL
  *   route_w     device fp32 [L][T][k] routing weights (softmax of the selected logits), or NULL
- * Pointers must be 16-byte aligned.  Returns after enqueueing; no host synchronisation.
+ * Pointers must be 16-byte aligned (expert_ids, route_w: 4-byte).  Returns after enqueueing; no
+ * host synchronisation.  A rejected call (MOE_ERR_INVALID_ARG) enqueues nothing and leaves the
+ * handle's weights unchanged.
  */
 MOE_ROUND_API moe_status moe_round_run(moe_round* h, const float* hidden, int32_t T, int32_t k,
                          const moe_layer_weights* layers, float* out, int32_t* expert_ids,
@@ -187,12 +206,14 @@ MOE_ROUND_API moe_status moe_round_run(moe_round* h, const float* hidden, int32_
 
 /*
  * Introspection of the last run (synchronises the stream; host outputs).
+ * Passage: infero README, "Beyond plain text decode" (the counting sort of (row, expert) pairs into
+ * per-expert work); the worklist is that sort's result.
  *   n_unique     number of distinct experts layer `layer` touched
  *   uniq         [n_unique] those experts, ascending                   (may be NULL)
  *   offs         [n_unique + 1] exclusive prefix sum of rows per expert (may be NULL)
  *   pairs        [T*k][2] (row t, rank j) grouped by expert, t ascending (may be NULL)
  * Buffers must hold at least min(T*k, E) (uniq), that + 1 (offs) and 2*T*k (pairs) entries.
- * This and the two calls below return MOE_ERR_STATE when there is no last run to report: none
+ * This and the calls below return MOE_ERR_STATE when there is no last run to report: none
  * since init, or the last one was an empty round (T = 0).
  */
 MOE_ROUND_API moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t* n_unique, int32_t* uniq,
@@ -201,15 +222,62 @@ MOE_ROUND_API moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t
 /*
  * The gate/up stage's output of the last run's last layer, silu(W_g x_t) * (W_u x_t), one fp32 row of
  * length I per (row, rank) pair in worklist order (pair slot p = the p-th entry of `pairs` above),
- * into host float [T*k][I] (synchronises the stream).
+ * into host float [T*k][I] (synchronises the stream).  Passage: infero README, "Layout" (the
+ * expert's SwiGLU) and "Design notes" (intermediates are kept comparable with a CPU reference).
  */
 MOE_ROUND_API moe_status moe_round_swiglu_rows(moe_round* h, float* host_rows);
 
-/* n_unique of every layer of the last run into host int32 [L] (synchronises the stream). */
+/* n_unique of every layer of the last run into host int32 [L] (synchronises the stream).
+ * Passage: "How AlphaInfer makes local decoding fast", section 3.1 (an extra verified row costs
+ * the experts only it routes to). */
 MOE_ROUND_API moe_status moe_round_last_unique(moe_round* h, int32_t* n_unique_per_layer);
 
+/* What the last run moved (host outputs; synchronises the stream). */
+typedef struct moe_round_stats {
+  int32_t n_layers;       /* L                                                          */
+  int32_t rows;           /* T of the last run                                          */
+  int32_t top_k;          /* k of the last run                                          */
+  int32_t reserved;       /* 0                                                          */
+  int64_t expert_bytes;   /* bytes of one expert's gate, up and down codes and scales    */
+  int64_t metric_bytes;   /* sum over layers of n_unique * expert_bytes + 2 * T * H * 4  */
+} moe_round_stats;
+
 /*
- * Kernel timing, for measurement.  moe_round_profile(h, 1) makes every following run launch its
+ * Per-layer statistics of the last run: the unique experts each layer read (n_unique, host int32
+ * [L] or NULL) and each layer's metric bytes (host int64 [L] or NULL): the unique experts' weight
+ * bytes (codes and scales) plus the T input and T output rows.  Passages: "How AlphaInfer makes
+ * local decoding fast", section 3.1 (the price of a verified row is the bytes of the experts only it
+ * needs); infero README, "CPU offload" (a decode step's rate read as bytes moved per second).
+ * Errors: MOE_ERR_INVALID_ARG (h or stats NULL), MOE_ERR_STATE (no last run).
+ */
+MOE_ROUND_API moe_status moe_round_last_stats(moe_round* h, moe_round_stats* stats, int32_t* n_unique,
+                                int64_t* layer_metric_bytes);
+
+/*
+ * The byte floor of the last run, enqueued on the handle's stream (asynchronous): per layer three
+ * launches that only read, at the last run's addresses, the router matrix, the gate and up codes and
+ * scales of the layer's unique experts, and their down codes and scales, and do no arithmetic beyond
+ * folding the loaded words together.  Timing it beside the round splits the round's time into what
+ * moving its bytes with that many launches costs and what the rest (routing, arithmetic) adds.
+ * Passage: infero README, "Where the time goes" (a decode-floor program that replays exactly the
+ * matrix-vector reads of a step, as the floor a step cannot beat).  Reads the worklist the last run
+ * left in device memory, so the weights it names must still be valid.
+ * Errors: MOE_ERR_INVALID_ARG (h NULL), MOE_ERR_STATE (no last run), MOE_ERR_HIP (launch).
+ */
+MOE_ROUND_API moe_status moe_round_floor(moe_round* h);
+
+/*
+ * A control measurement: one launch of the byte floor's read kernel over `bytes` contiguous bytes at
+ * device address `buf` (16-byte aligned, bytes a positive multiple of 16), on the handle's stream.
+ * Passage: "How AlphaInfer makes local decoding fast", section 7, rule 2 (always run a same-session
+ * control arm).  Errors: MOE_ERR_INVALID_ARG (bad pointer or size), MOE_ERR_HIP (launch).
+ */
+MOE_ROUND_API moe_status moe_round_stream_read(moe_round* h, const void* buf, int64_t bytes);
+
+/*
+ * Kernel timing, for measurement ("How AlphaInfer makes local decoding fast", section 7: time
+ * uninstrumented, decompose before crediting; the per-kernel times here come from events the runtime
+ * stamps with each dispatch's own start and end).  moe_round_profile(h, 1) makes every following run launch its
  * kernels eagerly (also on a graph handle: graph nodes carry no events) with a start/stop event
  * pair per kernel that the runtime stamps with the dispatch's own start and end times, so each
  * duration is the kernel's execution alone, without the launch gap before it.  The events form a

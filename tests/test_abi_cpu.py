@@ -28,7 +28,8 @@ def declared():
 def test_header_declares_the_boundary():
     names = declared()
     assert "moe_round_init" in names and "moe_round_run" in names and "moe_round_destroy" in names
-    assert len(names) == 11
+    assert len(names) == 14
+    assert {"moe_round_last_stats", "moe_round_floor", "moe_round_stream_read"} <= set(names)
 
 
 def test_library_exports_exactly_the_declared_symbols(lib):
@@ -72,6 +73,15 @@ def cfg(**kw):
     dict(H=768, I=384, E=40, top_k_max=5, max_rows=1000),
     dict(H=2048, I=512, E=512, top_k_max=10, n_layers=4, max_rows=16384, residual=True),
     dict(H=2048, I=512, E=256, top_k_max=8, max_rows=4096, raw_weight_format=1),  # prefill, 4.5-bit
+    # reduction lengths with no exact lane split: the spare block slots are masked
+    dict(H=1280, I=512, E=64, top_k_max=8, max_rows=8),      # H/32 = 40: 16 lanes x 3 blocks
+    dict(H=2048, I=640, E=64, top_k_max=8, max_rows=8),      # I/32 = 20: 8 lanes x 3 blocks
+    dict(H=2048, I=96, E=64, top_k_max=8, max_rows=8),       # I/32 = 3
+    dict(H=2048, I=64, E=256, top_k_max=8, max_rows=8),      # I = 512 / 8: one tensor-parallel shard
+    dict(H=2048, I=32, E=16, top_k_max=4, max_rows=8),
+    dict(H=2048, I=160, E=16, top_k_max=4, max_rows=8),
+    dict(H=2304, I=8160, E=8, top_k_max=2, max_rows=4),      # H/32 = 72, I/32 = 255
+    dict(H=2048, I=8192, E=8, top_k_max=2, max_rows=4),
 ])
 def test_supported_configs_validate(lib, kw):
     from verify_router_gemv_amd import binding
@@ -103,9 +113,9 @@ def test_supported_configs_validate(lib, kw):
     (dict(E=513, top_k_max=8), -2),
     (dict(top_k_max=17, E=256), -2),
     (dict(H=2080), -2),          # not a multiple of 256
-    (dict(H=1280), -2),          # H/32 = 40 = 8 * 5: five blocks per lane
-    (dict(I=640), -2),           # I/32 = 20 = 4 * 5
-    (dict(I=96), -2),            # I/32 = 3: fewer than 4 lanes per row
+    (dict(I=8224), -2),          # I/32 = 257: more than 256 blocks per row
+    (dict(I=48), -2),            # not a multiple of 32
+    (dict(I=96, max_rows=100), -2),   # prefill needs I a multiple of 128
     (dict(H=16384), -2),
 ])
 def test_unsupported_or_invalid_configs_are_refused(lib, kw, expect):
@@ -135,6 +145,47 @@ def test_null_and_bad_arguments_are_refused_before_any_gpu_call(lib):
     ms = (ctypes.c_double * 5)()
     assert lib.moe_round_profile_read(None, ms, ctypes.byref(n)) == -1
     lib.moe_round_destroy(None)
+
+
+def test_new_entry_points_refuse_null_handles(lib):
+    st = (ctypes.c_int32 * 8)()
+    assert lib.moe_round_last_stats(None, None, None, None) == -1
+    assert lib.moe_round_floor(None) == -1
+    assert lib.moe_round_stream_read(None, None, 16) == -1
+
+
+def test_rejected_layers_keep_the_old_weights_referenced(lib, monkeypatch):
+    """A run with new layers that the binding or the library rejects leaves the handle's Python
+    references to the previous weight tensors in place (the library keeps reading them)."""
+    from verify_router_gemv_amd import binding
+    E, H, I = 4, 256, 128
+    h = binding.MoeRound.__new__(binding.MoeRound)
+    h.lib, h.h, h.H, h.I, h.E, h.L, h.weight_format = lib, None, H, I, E, 1, 0
+    old = [object()]
+    h._layers, h._wt = old, "old-array"
+    host_layer = dict(router_w=torch.zeros(E, H), router_b=None,
+                      gate_q=torch.zeros(E, I, H // 2, dtype=torch.uint8),
+                      gate_sm=torch.zeros(E, I, H // 32, dtype=torch.int32),
+                      up_q=torch.zeros(E, I, H // 2, dtype=torch.uint8),
+                      up_sm=torch.zeros(E, I, H // 32, dtype=torch.int32),
+                      down_q=torch.zeros(E, H, I // 2, dtype=torch.uint8),
+                      down_sm=torch.zeros(E, H, I // 32, dtype=torch.int32))
+    x = torch.zeros(1, H)
+    with pytest.raises(ValueError):          # the binding refuses host tensors
+        h.run(x, 1, x, layers=[host_layer])
+    assert h._layers is old and h._wt == "old-array"
+    # the library refuses the call (e.g. a misaligned pointer): nothing is committed either
+    monkeypatch.setattr(binding.MoeRound, "_marshal_layers", lambda self, layers: "new-array")
+    monkeypatch.setattr(binding.MoeRound, "_run_args", lambda self, *a: ())
+    monkeypatch.setattr(binding.MoeRound, "_raise", lambda self, st, what: (_ for _ in ()).throw(RuntimeError(what)))
+
+    class FakeLib:
+        def moe_round_run(self, *a):
+            return binding.ERR_INVALID_ARG
+    h.lib = FakeLib()
+    with pytest.raises(RuntimeError):
+        h.run(x, 1, x, layers=[object()])
+    assert h._layers is old and h._wt == "old-array"
 
 
 def test_status_strings(lib):

@@ -48,6 +48,11 @@ class LayerWeights(ctypes.Structure):
         "router_w", "router_bias", "gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")]
 
 
+class Stats(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("rows", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("expert_bytes", ctypes.c_int64), ("metric_bytes", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -70,6 +75,9 @@ def load() -> ctypes.CDLL:
         "moe_round_worklist": (i32, [vp, i32, P(i32), P(i32), P(i32), P(i32)]),
         "moe_round_last_unique": (i32, [vp, P(i32)]),
         "moe_round_swiglu_rows": (i32, [vp, P(ctypes.c_float)]),
+        "moe_round_last_stats": (i32, [vp, P(Stats), P(i32), P(ctypes.c_int64)]),
+        "moe_round_floor": (i32, [vp]),
+        "moe_round_stream_read": (i32, [vp, vp, ctypes.c_int64]),
         "moe_round_last_hip_error": (i32, [vp]),
         "moe_round_strerror": (ctypes.c_char_p, [i32]),
         "moe_round_destroy": (None, [vp]),
@@ -198,15 +206,14 @@ class MoeRound:
     def _raise(self, st, what):
         raise MoeRoundError(st, what, self.lib.moe_round_last_hip_error(self.h))
 
-    def set_layers(self, layers: Sequence):
+    def _marshal_layers(self, layers: Sequence):
+        """The C array for `layers` (checked), without touching the handle's current weights."""
         if len(layers) != self.L:
             raise ValueError("layer count must not change")
-        self._layers = list(layers)
-        self._wt = (LayerWeights * self.L)(*[layer_struct(l, self.H, self.I, self.E, self.weight_format)
-                                             for l in layers])
-        return self._wt
+        return (LayerWeights * self.L)(*[layer_struct(l, self.H, self.I, self.E, self.weight_format)
+                                         for l in layers])
 
-    def _run_args(self, hidden, k, out, ids, route_w, layers):
+    def _run_args(self, hidden, k, out, ids, route_w, wt):
         T = hidden.shape[0]
         _check(hidden, "hidden", (torch.float32,), (T, self.H))
         _check(out, "out", (torch.float32,), (T, self.H))
@@ -214,16 +221,20 @@ class MoeRound:
             _check(ids, "expert_ids", (torch.int32,), (self.L, T, k))
         if route_w is not None:
             _check(route_w, "route_w", (torch.float32,), (self.L, T, k))
-        wt = self.set_layers(layers) if layers is not None else None
         return (self.h, ctypes.c_void_p(hidden.data_ptr()), T, k, wt, ctypes.c_void_p(out.data_ptr()),
                 ctypes.c_void_p(ids.data_ptr() if ids is not None else 0),
                 ctypes.c_void_p(route_w.data_ptr() if route_w is not None else 0))
 
     def run(self, hidden: torch.Tensor, k: int, out: torch.Tensor, ids: Optional[torch.Tensor] = None,
             route_w: Optional[torch.Tensor] = None, layers: Optional[Sequence] = None):
-        st = self.lib.moe_round_run(*self._run_args(hidden, k, out, ids, route_w, layers))
+        """One round. `layers`: new weights for this and later rounds; the handle keeps referencing
+        the old tensors until the library has accepted the new ones (a rejected call changes nothing)."""
+        wt = self._marshal_layers(layers) if layers is not None else None
+        st = self.lib.moe_round_run(*self._run_args(hidden, k, out, ids, route_w, wt))
         if st != OK:
             self._raise(st, "moe_round_run")
+        if layers is not None:
+            self._layers, self._wt = list(layers), wt
 
     def profile(self, enable: bool = True):
         """Start (or stop) per-kernel timing of the following runs (dispatch timestamps)."""
@@ -275,6 +286,31 @@ class MoeRound:
         if st != OK:
             self._raise(st, "moe_round_swiglu_rows")
         return buf
+
+    def last_stats(self):
+        """(Stats of the last run, per-layer n_unique list, per-layer metric bytes list)."""
+        st_ = Stats()
+        nu = (ctypes.c_int32 * self.L)()
+        mb = (ctypes.c_int64 * self.L)()
+        st = self.lib.moe_round_last_stats(self.h, ctypes.byref(st_), nu, mb)
+        if st != OK:
+            self._raise(st, "moe_round_last_stats")
+        return st_, list(nu), list(mb)
+
+    def floor(self):
+        """Enqueue the byte floor of the last run (its weight reads alone, same launches per layer)."""
+        st = self.lib.moe_round_floor(self.h)
+        if st != OK:
+            self._raise(st, "moe_round_floor")
+
+    def stream_read(self, buf: torch.Tensor):
+        """Enqueue one streaming read of the whole of `buf` (a device tensor; the control arm)."""
+        if buf.device.type != "cuda" or not buf.is_contiguous():
+            raise ValueError("stream_read needs a contiguous device tensor")
+        st = self.lib.moe_round_stream_read(self.h, ctypes.c_void_p(buf.data_ptr()),
+                                            buf.numel() * buf.element_size())
+        if st != OK:
+            self._raise(st, "moe_round_stream_read")
 
     def last_unique(self):
         arr = (ctypes.c_int32 * self.L)()

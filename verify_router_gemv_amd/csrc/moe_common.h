@@ -2,7 +2,8 @@
 //
 // Per layer four kernels:
 //   logits_kernel  router GEMV z[t][e] = sum_h Wr[e][h] x[t][h] + b[e]: fp32 inputs, fp64 products
-//                  and sums; also seeds the layer's output rows (residual x, or zeros).
+//                  and sums; its extra blocks write the input's int8 digits and seed the output rows
+//                  with the residual (the gate/up kernel zeroes them when there is none).
 //   select_kernel  one block: per-row top-k (k rounds of a wave-wide max over (logit, id) keys),
 //                  softmax over the k selected logits, the union of the rows' experts and a counting
 //                  sort of the (row, rank) pairs by expert; it writes one 128-byte record per unique
@@ -298,8 +299,10 @@ __device__ __forceinline__ int key_expert(uint64_t key) { return 511 - static_ca
 // qb + 1, one element per lane. The integer q = rint(x / step) with step = max|x| / kXqMax is split
 // into balanced base-256 digits d0, d1, d2 in [-127, 127], each lane storing its three digit bytes
 // at their places in the even / odd words; the block sum is kept in fp32. Blocks at or past nq are
-// skipped (their lanes still take part in the reductions, on a clamped block).
-__device__ __forceinline__ void quantize_block_pair(const float* x, uint32_t* xq, float2* xss, int qb, int nq) {
+// skipped (their lanes still take part in the reductions, on a clamped block). seed: if not null,
+// each element is also copied there (the residual the layer's output rows start from).
+__device__ __forceinline__ void quantize_block_pair(const float* x, uint32_t* xq, float2* xss, int qb, int nq,
+                                                    float* seed) {
   const int lane = threadIdx.x & 63, e = lane & 31;
   const int b = qb + (lane >> 5);
   const float v = x[static_cast<size_t>(min(b, nq - 1)) * 32 + e];
@@ -322,6 +325,7 @@ __device__ __forceinline__ void quantize_block_pair(const float* x, uint32_t* xq
   const int d1 = ((q1 + 128) & 255) - 128;
   const int d2 = (q1 - d1) >> 8;
   if (b < nq) {
+    if (seed) seed[static_cast<size_t>(b) * 32 + e] = v;
     // element e = 8g + i sits in word (plane * 4 + g) * 2 + (i & 1), byte i >> 1
     uint8_t* dst = reinterpret_cast<uint8_t*>(xq + static_cast<size_t>(b) * kXqWords);
     const int g = e >> 3, i = e & 7;

@@ -90,9 +90,10 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
     const size_t r = static_cast<size_t>(wk.e) * H + min(row0 + w * RPI, H - 1);  // rows past H: not stored
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int b = g + nb * G;
+      const int bl = g + nb * G, b = min(bl, nblk - 1);
       cd[w][nb] = load_stream_u4(W.down_q + r * rq + 16 * b);
       sd[w][nb].load(W.down_sm + r * rsm, b);
+      sd[w][nb].mask(bl < nblk);
     }
   }
 
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
       float xstep[NB], xsum[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int blk = c * nblk + g + nb * G;
+        const int blk = c * nblk + min(g + nb * G, nblk - 1);
         const uint32_t* srcw = dig + static_cast<size_t>(blk) * kXqWords;
 #pragma unroll
         for (int q = 0; q < kXqWords / 4; ++q) {
@@ -164,8 +165,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
 // p[t][j] * y[slot(t, j)][h]. Grid (T, ceil(H / 1024)) x 256 threads, four columns per thread.
 static __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int layer) {
   const Ingress in = get_ingress(a);
-  const float* __restrict__ x = layer_input(a, in, layer);
-  float* __restrict__ xn = layer_output(a, in, layer);
+  const float* x = layer_input(a, in, layer);  // may be xn itself (the caller's hidden == out)
+  float* xn = layer_output(a, in, layer);
   const int t = blockIdx.x, H = a.H, k = a.k;
   const int h = (blockIdx.y * kThreads + threadIdx.x) * 4;
   if (h >= H) return;

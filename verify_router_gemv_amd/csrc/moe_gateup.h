@@ -279,11 +279,13 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
     const size_t r = static_cast<size_t>(wk.e) * I + min(row0 + w * RPI, I - 1);  // rows past I: not stored
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int b = g + nb * G;
+      const int bl = g + nb * G, b = min(bl, nblk - 1);
       cg[w][nb] = load_stream_u4(W.gate_q + r * rq + 16 * b);
       cu[w][nb] = load_stream_u4(W.up_q + r * rq + 16 * b);
       sg[w][nb].load(W.gate_sm + r * rsm, b);
       su[w][nb].load(W.up_sm + r * rsm, b);
+      sg[w][nb].mask(bl < nblk);
+      su[w][nb].mask(bl < nblk);
     }
   }
 
@@ -297,7 +299,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
     const int t = work_row(wk, rr, T);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const size_t blk = static_cast<size_t>(t) * nblk + g + nb * G;
+      const size_t blk = static_cast<size_t>(t) * nblk + min(g + nb * G, nblk - 1);
       const MOE_GLOBAL u32x4* src = (const MOE_GLOBAL u32x4*)(a.xq + blk * kXqWords);
 #pragma unroll
       for (int q = 0; q < kXqWords / 4; ++q) {
@@ -315,7 +317,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
   auto stage_row = [&](int slot, int rr) {  // STAGE: row rr of the current chunk, from LDS
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int blk = rr * nblk + g + nb * G;
+      const int blk = rr * nblk + min(g + nb * G, nblk - 1);
       const uint32_t* src = xs_dig + blk * kXqWords;
 #pragma unroll
       for (int q = 0; q < kXqWords / 4; ++q) {
@@ -398,6 +400,16 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
   }
 }
 
+// Rounds without the residual (and with the atomic combine) start the output rows at zero: the down
+// kernel adds into them. Stores only, spread over the grid.
+__device__ __forceinline__ void zero_output(const Args& a, int layer) {
+  const Ingress in = get_ingress(a);
+  float4* o = reinterpret_cast<float4*>(layer_output(a, in, layer));
+  const int n4 = a.T * a.H / 4;
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n4; i += gridDim.x * kThreads)
+    o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 // Blocks with the selection folded in (SEL > 0) compute it once and then take the units (item,
 // tile) blockIdx.x, blockIdx.x + gridDim.x, ...: the grid is sized for the chip, not for the
 // largest possible item count, so no block repeats the selection only to find no work.
@@ -406,6 +418,7 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
   constexpr int ROWS_B = kWaves * RW * (64 / G);
   extern __shared__ uint32_t xs[];  // staged form: gateup_stage_words(H) (+ matrix-core tile) words
   const int tiles = (a.I + ROWS_B - 1) / ROWS_B;
+  if (!a.residual && !a.exact) zero_output(a, layer);
   if constexpr (SEL > 0) {
     __shared__ SelectSharedT<kFusedPairs, kWaves> ssel;
     // The last block publishes: it is the one most likely to have no (item, tile) unit of its own.

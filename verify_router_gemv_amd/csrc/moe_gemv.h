@@ -10,7 +10,8 @@ namespace moe {
 // ------------------------------------------------------------------------------------------
 //
 // Lane layout: G lanes share one weight row, each owning NB of its 32-weight blocks (block
-// b = g + nb*G); a wave covers 64/G rows per load and RW such row groups (for gate/up: of both
+// b = g + nb*G; when G * NB exceeds the row's K/32 blocks, the slots past the end load the row's
+// last block and are masked to add zero); a wave covers 64/G rows per load and RW such row groups (for gate/up: of both
 // matrices). Codes (16 B) and the block's scale/minimum source of each block are loaded once into
 // registers. The activation rows (the layer input for gate/up, the SwiGLU rows for down) are
 // int8 digits per 32-block; per block the dot product is s * step * (integer dot) + m * sum(x).
@@ -37,6 +38,8 @@ template <>
 struct BlockScale<kFmtQ4B32> {
   uint32_t w;
   __device__ __forceinline__ void load(const uint32_t* sm_row, int b) { w = load_stream_u32(sm_row + b); }
+  // An idle block slot of a padded lane split: scale and minimum 0, so the block adds nothing.
+  __device__ __forceinline__ void mask(bool live) { w = live ? w : 0u; }
   __device__ __forceinline__ float scale() const { return half_bits_to_float(w); }
   __device__ __forceinline__ float minv() const { return half_bits_to_float(w >> 16); }
 };
@@ -49,6 +52,7 @@ struct BlockScale<kFmtQ4S256> {
     r = load_stream_u4(sm_row + 4 * (b >> 3));
     j = b & 7;
   }
+  __device__ __forceinline__ void mask(bool live) { r.x = live ? r.x : 0u; }  // d = dmin = 0
   __device__ __forceinline__ uint32_t field() const {
     const uint64_t lo = static_cast<uint64_t>(r.y) | (static_cast<uint64_t>(r.z) << 32);  // bits 0..63
     const uint64_t hi = static_cast<uint64_t>(r.z) | (static_cast<uint64_t>(r.w) << 32);  // bits 32..95

@@ -6,8 +6,9 @@
 
 namespace moe {
 
-// Split a reduction length K into G lanes per matrix row and NB 32-weight blocks per lane
-// (K/32 = G * NB, G = largest power of two <= 64 dividing K/32, G >= 4, NB <= 4).
+// Split a reduction length K (a multiple of 32, K/32 <= 256) into G lanes per matrix row and NB
+// 32-weight blocks per lane, G in {4..64} a power of two, NB <= 4, G * NB >= K/32: the exact split
+// when one exists, else the one with the fewest idle block slots (the kernels mask those).
 bool split_blocks(int K, int* G, int* NB);
 
 moe_status validate_config(const moe_round_config* c);

@@ -93,21 +93,35 @@ inline bool pick_gemv(int G, int NB, int mode, bool up, int sel, int fmt, Kernel
   return false;
 }
 
-// Router rows per wave: one at T == 1, two otherwise.
-inline int logits_rows(int T) { return T == 1 ? 1 : 2; }
+// Rows per logits block: the round's rows up to 8 (rounded up to 1, 2, 4 or 8), so a block reads
+// its router row once for all of them; wider rounds use ceil(T / 8) row chunks.
+inline int logits_rows(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)); }
 
 template <int TC>
 inline KernelFn pick_logits_tc(int H) {
-  switch (H / 256) {
+  switch ((H + 1023) / 1024) {
 #define MOE_NJ(N) \
   case N: return logits_kernel<N, TC>;
-    MOE_NJ(1) MOE_NJ(2) MOE_NJ(3) MOE_NJ(4) MOE_NJ(6) MOE_NJ(8) MOE_NJ(12) MOE_NJ(16) MOE_NJ(24) MOE_NJ(32)
+    MOE_NJ(1) MOE_NJ(2) MOE_NJ(3) MOE_NJ(4) MOE_NJ(5) MOE_NJ(6) MOE_NJ(7) MOE_NJ(8)
 #undef MOE_NJ
   }
   return nullptr;
 }
 
-inline KernelFn pick_logits(int H, int T) { return logits_rows(T) == 1 ? pick_logits_tc<1>(H) : pick_logits_tc<2>(H); }
+inline KernelFn pick_logits(int H, int T) {
+  switch (logits_rows(T)) {
+    case 1: return pick_logits_tc<1>(H);
+    case 2: return pick_logits_tc<2>(H);
+    case 4: return pick_logits_tc<4>(H);
+  }
+  return pick_logits_tc<8>(H);
+}
+
+// Grid of the logits kernel: E router blocks plus the blocks that write the input's digits.
+inline dim3 logits_grid(int E, int H, int T) {
+  const int tc = logits_rows(T);
+  return dim3(E + (T * H + 255) / 256, (T + tc - 1) / tc);
+}
 
 // Keys per lane of the fused selection in the gate/up kernel (E <= 512).
 inline int fused_select_keys(int E) { return E <= 256 ? 4 : 8; }

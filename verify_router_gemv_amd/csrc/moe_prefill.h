@@ -788,8 +788,8 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4)
 // out[t][h] = (residual ? x[t][h] : 0) + sum over ranks j = 0..k-1, in that order, of
 // p[t][j] * y[slot(t, j)][h]. Grid (T, ceil(H / 1024)) x 256 threads, four columns per thread.
 static __global__ __launch_bounds__(kThreads) void pf_combine_kernel(PfArgs a, int layer) {
-  const float* __restrict__ x = pf_layer_input(a, layer);
-  float* __restrict__ xn = pf_layer_output(a, layer);
+  const float* x = pf_layer_input(a, layer);  // may be xn itself (the caller's hidden == out)
+  float* xn = pf_layer_output(a, layer);
   const int t = blockIdx.x, H = a.H, k = a.k;
   const int h = (blockIdx.y * kThreads + threadIdx.x) * 4;
   if (h >= H) return;

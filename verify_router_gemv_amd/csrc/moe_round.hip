@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "moe_internal.h"
+#include "moe_floor.h"
 #include "moe_kernels.h"
 #include "moe_prefill.h"
 
@@ -94,7 +95,7 @@ struct moe_round {
   int32_t prof_count = 0;              // runs accumulated since the last read
   int last_T = 0, last_k = 0;
   int32_t last_hip = 0;
-  int mfma_rows = 3;                   // gate/up (wide rounds): matrix-core tile from this many rows per item
+  int mfma_rows = 0;                   // gate/up (wide rounds): matrix-core tile from this many rows per item (0: never)
   int rows_per_item = 0;               // 0: by round width
   int fused_max_rows = kFusedMaxRows;  // selection folded into gate/up up to this many rows
   // prefill scratch (max_rows > MOE_ROUND_MAX_ROWS): rows Tp, pair slots pfP, work items pfI
@@ -118,6 +119,7 @@ struct moe_round {
   uint32_t* pf_hq = nullptr;
   float* pf_hstep = nullptr;
   float* pf_ybuf = nullptr;
+  uint32_t* floor_sink = nullptr;      // [kFloorMaxBlocks] measurement kernels' sink
 };
 
 static moe_status hip_fail(moe_round* h, hipError_t e) {
@@ -204,8 +206,7 @@ static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
   if (!lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, fused ? fused_select_keys(E) : 0, fmt, &gu, &rows_gu) ||
       !pick_gemv(h->Gi, h->NBi, 0, false, h->cfg.exact, fmt, &dn, &rows_dn))
     return false;
-  const int tc = logits_rows(T);
-  const dim3 grid_lg((E + kRouteExpertsPerBlock - 1) / kRouteExpertsPerBlock, (T + tc - 1) / tc);
+  const dim3 grid_lg = logits_grid(E, H, T);
   const int units_gu = umax * ((I + rows_gu - 1) / rows_gu);
   const dim3 grid_gu(fused && units_gu > kFusedBlocks ? kFusedBlocks : units_gu);
   const dim3 grid_dn(umax * ((H + rows_dn - 1) / rows_dn));
@@ -482,7 +483,7 @@ static void free_handle(moe_round* h) {
                   h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->tsel, h->tp, h->xq, h->xss,
                   h->pf_xbuf[0], h->pf_xbuf[1], h->pf_xq, h->pf_xstep, h->pf_mask, h->pf_wpre,
                   h->pf_sel, h->pf_selp, h->pf_uniq, h->pf_offs, h->pf_eoff, h->pf_pairs, h->pf_pair_w, h->pf_slot_of,
-                  h->pf_items, h->pf_n_items, h->pf_hbuf, h->pf_hq, h->pf_hstep, h->pf_ybuf};
+                  h->pf_items, h->pf_n_items, h->pf_hbuf, h->pf_hq, h->pf_hstep, h->pf_ybuf, h->floor_sink};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete h;
@@ -541,6 +542,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   if (cfg->exact) MOE_ALLOC(h->ybuf, sizeof(float) * h->Pcap * H);
   MOE_ALLOC(h->xq, sizeof(uint32_t) * T * (H / 32) * kXqWords);
   MOE_ALLOC(h->xss, sizeof(float2) * T * (H / 32));
+  MOE_ALLOC(h->floor_sink, sizeof(uint32_t) * kFloorMaxBlocks);
   if (cfg->max_rows > MOE_ROUND_MAX_ROWS) {
     const size_t Tp = cfg->max_rows, P = Tp * K, W = (Tp + 63) / 64;
     h->Tp = static_cast<int>(Tp);
@@ -749,6 +751,108 @@ extern "C" moe_status moe_round_last_unique(moe_round* h, int32_t* n_unique_per_
   MOE_HIP(h, hipStreamSynchronize(h->stream));
   MOE_HIP(h, hipMemcpy(n_unique_per_layer, h->n_unique, sizeof(int32_t) * h->cfg.n_layers, hipMemcpyDeviceToHost));
   return MOE_OK;
+}
+
+// Bytes of one expert's gate, up and down codes and scales (or super-block records) in the layout.
+static int64_t expert_bytes(const moe_round_config& c) {
+  const int64_t w = static_cast<int64_t>(c.hidden) * c.inter;
+  const int64_t per = c.weight_format == MOE_WEIGHT_Q4S256 ? (128 + 16) : (16 + 4);  // per 256 / per 32
+  const int64_t blk = c.weight_format == MOE_WEIGHT_Q4S256 ? 256 : 32;
+  return 3 * w / blk * per;
+}
+
+extern "C" moe_status moe_round_last_stats(moe_round* h, moe_round_stats* stats, int32_t* n_unique,
+                                           int64_t* layer_metric_bytes) {
+  if (!h || !stats) return MOE_ERR_INVALID_ARG;
+  if (h->last_T == 0) return MOE_ERR_STATE;
+  const int L = h->cfg.n_layers;
+  std::vector<int32_t> nu(L);
+  MOE_HIP(h, hipStreamSynchronize(h->stream));
+  MOE_HIP(h, hipMemcpy(nu.data(), h->n_unique, sizeof(int32_t) * L, hipMemcpyDeviceToHost));
+  const int64_t eb = expert_bytes(h->cfg);
+  const int64_t act = 2LL * h->last_T * h->cfg.hidden * static_cast<int64_t>(sizeof(float));
+  int64_t total = 0;
+  for (int l = 0; l < L; ++l) {
+    const int64_t mb = nu[l] * eb + act;
+    if (n_unique) n_unique[l] = nu[l];
+    if (layer_metric_bytes) layer_metric_bytes[l] = mb;
+    total += mb;
+  }
+  stats->n_layers = L;
+  stats->rows = h->last_T;
+  stats->top_k = h->last_k;
+  stats->reserved = 0;
+  stats->expert_bytes = eb;
+  stats->metric_bytes = total;
+  return MOE_OK;
+}
+
+static moe_status launch_floor(moe_round* h, FloorArgs fa, int units_max, int grid_cap = 16384) {
+  int grid = units_max < grid_cap ? units_max : grid_cap;
+  if (grid < 1) grid = 1;
+  fa.magic = 0x9E3779B9u;
+  fa.sink = h->floor_sink;
+  fa.chunks_per_expert = 0;
+  for (int i = 0; i < fa.nr; ++i)
+    fa.chunks_per_expert += static_cast<int>((fa.r[i].bytes + kFloorChunk - 1) / kFloorChunk);
+  void* params[] = {&fa};
+  MOE_HIP(h, hipLaunchKernel(reinterpret_cast<const void*>(floor_read_kernel), dim3(grid), dim3(kThreads), params, 0,
+                             h->stream));
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_floor(moe_round* h) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (h->last_T == 0) return MOE_ERR_STATE;
+  const moe_round_config& c = h->cfg;
+  const int64_t H = c.hidden, I = c.inter, E = c.n_experts;
+  const bool pf = h->last_T > MOE_ROUND_MAX_ROWS;
+  const int ucap = pf ? c.n_experts : h->Ucap;
+  const int32_t* uniq = pf ? h->pf_uniq : h->uniq;
+  const bool s256 = c.weight_format == MOE_WEIGHT_Q4S256;
+  const int64_t smh = (s256 ? H / 64 : H / 32) * 4, smi = (s256 ? I / 64 : I / 32) * 4;  // bytes per row
+  for (int l = 0; l < c.n_layers; ++l) {
+    const moe_layer_weights& w = h->h_wtab[l];
+    FloorArgs r{};
+    r.nr = 1;
+    r.r[0] = {reinterpret_cast<const uint8_t*>(w.router_w), 0, E * H * 4};
+    moe_status st = launch_floor(h, r, static_cast<int>((E * H * 4 + kFloorChunk - 1) / kFloorChunk));
+    if (st != MOE_OK) return st;
+    FloorArgs g{};
+    g.nr = 4;
+    g.r[0] = {w.gate_q, I * H / 2, I * H / 2};
+    g.r[1] = {reinterpret_cast<const uint8_t*>(w.gate_sm), I * smh, I * smh};
+    g.r[2] = {w.up_q, I * H / 2, I * H / 2};
+    g.r[3] = {reinterpret_cast<const uint8_t*>(w.up_sm), I * smh, I * smh};
+    g.uniq = uniq + static_cast<size_t>(l) * ucap;
+    g.n_unique = h->n_unique + l;
+    g.ucap = ucap;
+    g.emax = c.n_experts - 1;
+    const int cg = static_cast<int>(2 * ((I * H / 2 + kFloorChunk - 1) / kFloorChunk + (I * smh + kFloorChunk - 1) / kFloorChunk));
+    st = launch_floor(h, g, ucap * cg);
+    if (st != MOE_OK) return st;
+    FloorArgs d{};
+    d.nr = 2;
+    d.r[0] = {w.down_q, H * I / 2, H * I / 2};
+    d.r[1] = {reinterpret_cast<const uint8_t*>(w.down_sm), H * smi, H * smi};
+    d.uniq = g.uniq;
+    d.n_unique = g.n_unique;
+    d.ucap = ucap;
+    d.emax = c.n_experts - 1;
+    const int cd = static_cast<int>((H * I / 2 + kFloorChunk - 1) / kFloorChunk + (H * smi + kFloorChunk - 1) / kFloorChunk);
+    st = launch_floor(h, d, ucap * cd);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_stream_read(moe_round* h, const void* buf, int64_t bytes) {
+  if (!h || !buf || bytes < 16 || (bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15u)) return MOE_ERR_INVALID_ARG;
+  FloorArgs f{};
+  f.nr = 1;
+  f.r[0] = {static_cast<const uint8_t*>(buf), 0, bytes};
+  const int64_t chunks = (bytes + kFloorChunk - 1) / kFloorChunk;
+  return launch_floor(h, f, static_cast<int>(chunks < (1 << 20) ? chunks : (1 << 20)), 1 << 20);
 }
 
 extern "C" int32_t moe_round_last_hip_error(const moe_round* h) { return h ? h->last_hip : 0; }

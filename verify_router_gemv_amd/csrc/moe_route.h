@@ -9,46 +9,48 @@ namespace moe {
 // Kernel 1: router logits (+ output seeding)
 // ------------------------------------------------------------------------------------------
 
-constexpr int kRouteExpertsPerBlock = kWaves;  // one expert per wave
-
-// Grid: (ceil(E / 4), ceil(T / TC)). Each wave takes one expert and TC rows; every load of the
-// wave (its router row and its TC activation rows) is issued before any arithmetic.
-template <int NJ, int TC>  // NJ = H / 256: float4 chunks of a row per lane
+// Grid: (E + ceil(T * H / 256), ceil(T / TC)) x 256 threads.
+//  * Blocks x < E: expert x's logits for rows y * TC .. y * TC + TC - 1. The reduction over H is split
+//    over the block's four waves (thread i takes float4 chunks i, i + 256, ... of the row), every load
+//    of the thread (its router chunks and the TC rows' chunks) is issued before any arithmetic, each
+//    wave sums its part in fp64 and wave 0 adds the four parts in wave order (a fixed order).
+//  * Blocks x >= E (row chunk 0 only): the layer input as int8 digits per 32-block for the gate/up
+//    kernel, two 32-blocks per wave; with the residual (and the atomic combine) they also seed the
+//    layer's output rows with the input rows. These blocks read no router row, so the router waves
+//    finish after one load round trip. (Without the residual the output rows are zeroed by the gate/up
+//    kernel instead: nothing may write the output while the router reads the input, since a caller
+//    may pass the same buffer as both.)
+template <int NJ, int TC>  // NJ = ceil(H / 1024): float4 chunks of a row per thread
 __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, H = a.H;
   const Ingress in = get_ingress(a);
-  const moe_layer_weights W = get_weights(a, layer);
   const float* __restrict__ x = layer_input(a, in, layer);
-  float* __restrict__ xn = layer_output(a, in, layer);
 
-  const int e = min(blockIdx.x * kRouteExpertsPerBlock + wave, E - 1);
+  if (static_cast<int>(blockIdx.x) >= E) {
+    if (blockIdx.y != 0) return;
+    const int nq = T * (H / 32);  // 32-blocks of the layer input, two per wave
+    const int qb = 2 * ((blockIdx.x - E) * kWaves + wave);
+    if (qb >= nq) return;
+    float* seed = (a.residual && !a.exact) ? layer_output(a, in, layer) : nullptr;
+    quantize_block_pair(x, a.xq, a.xss, qb, nq, seed);
+    return;
+  }
+  const moe_layer_weights W = get_weights(a, layer);
+  const int e = blockIdx.x;
   const int t0 = blockIdx.y * TC;
+  const int n4 = H / 4;
   float4 w[NJ], xv[TC][NJ];
   const float4* wr = reinterpret_cast<const float4*>(W.router_w + static_cast<size_t>(e) * H);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) w[j] = load_stream_f4(wr + lane + 64 * j);
+  for (int j = 0; j < NJ; ++j) w[j] = load_stream_f4(wr + min(tid + kThreads * j, n4 - 1));
 #pragma unroll
   for (int r = 0; r < TC; ++r) {
     const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(min(t0 + r, T - 1)) * H);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) xv[r][j] = load_f4(xr + lane + 64 * j);
+    for (int j = 0; j < NJ; ++j) xv[r][j] = load_f4(xr + min(tid + kThreads * j, n4 - 1));
   }
   const double bias = W.router_bias ? static_cast<double>(W.router_bias[e]) : 0.0;
-
-  // Blocks of row-chunk 0 also seed this layer's output rows with the residual (deep stack) or
-  // zeros, and write the layer input as int8 digits per 32-block for the gate/up kernel.
-  if (blockIdx.y == 0) {
-    const int n4 = T * H / 4;
-    const float4* x4 = reinterpret_cast<const float4*>(x);
-    float4* xn4 = reinterpret_cast<float4*>(xn);
-    if (!a.exact)  // exact mode: the combine kernel writes the output rows whole
-      for (int i = blockIdx.x * kThreads + tid; i < n4; i += gridDim.x * kThreads)
-        xn4[i] = a.residual ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const int nq = T * (H / 32);  // 32-blocks of the layer input, two per wave
-    for (int qb = 2 * (blockIdx.x * kWaves + wave); qb < nq; qb += 2 * gridDim.x * kWaves)
-      quantize_block_pair(x, a.xq, a.xss, qb, nq);
-  }
 
   double acc[TC];
 #pragma unroll
@@ -56,18 +58,26 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
     acc[r] = 0.0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+      if (tid + kThreads * j >= n4) continue;  // past the end of the row (its load was clamped)
       acc[r] = fma(static_cast<double>(w[j].x), static_cast<double>(xv[r][j].x), acc[r]);
       acc[r] = fma(static_cast<double>(w[j].y), static_cast<double>(xv[r][j].y), acc[r]);
       acc[r] = fma(static_cast<double>(w[j].z), static_cast<double>(xv[r][j].z), acc[r]);
       acc[r] = fma(static_cast<double>(w[j].w), static_cast<double>(xv[r][j].w), acc[r]);
     }
   }
+  __shared__ double part[kWaves][TC];
 #pragma unroll
-  for (int r = 0; r < TC; ++r) acc[r] = wave_sum_f64(acc[r]);
-  if (lane == 0 && blockIdx.x * kRouteExpertsPerBlock + wave < E) {
+  for (int r = 0; r < TC; ++r) {
+    acc[r] = wave_sum_f64(acc[r]);
+    if (lane == 0) part[wave][r] = acc[r];
+  }
+  __syncthreads();
+  if (tid < TC && t0 + tid < T) {
+    double z = part[0][0];
 #pragma unroll
     for (int r = 0; r < TC; ++r)
-      if (t0 + r < T) a.logits[static_cast<size_t>(t0 + r) * E + e] = acc[r] + bias;
+      if (r == tid) z = ((part[0][r] + part[1][r]) + part[2][r]) + part[3][r];
+    a.logits[static_cast<size_t>(t0 + tid) * E + e] = z + bias;
   }
 }
 

@@ -4,20 +4,35 @@
 
 namespace moe {
 
-static int gcd_pow2_64(int v) {
-  int g = 1;
-  while (g < 64 && (v % (g * 2)) == 0) g *= 2;
-  return g;
-}
-
 bool split_blocks(int K, int* G, int* NB) {
   if (K <= 0 || K % 32 != 0) return false;
   const int bpr = K / 32;
-  const int g = gcd_pow2_64(bpr);
-  const int nb = bpr / g;
-  if (g < 4 || nb < 1 || nb > 4) return false;
-  *G = g;
-  *NB = nb;
+  if (bpr > 256) return false;
+  // An exact split (no idle lane) when there is one: G the largest power of two <= 64 dividing
+  // K/32, with G >= 4 and NB <= 4.
+  int g = 1;
+  while (g < 64 && (bpr % (g * 2)) == 0) g *= 2;
+  if (g >= 4 && bpr / g <= 4) {
+    *G = g;
+    *NB = bpr / g;
+    return true;
+  }
+  // Otherwise the split with the fewest idle block slots (G * NB - K/32, ties to the smaller G):
+  // the kernels clamp the idle slots' loads into the row and zero their scale and minimum.
+  int best_g = 0, best_nb = 0, best_waste = 1 << 30;
+  for (int gg = 4; gg <= 64; gg *= 2) {
+    const int nb = (bpr + gg - 1) / gg;
+    if (nb > 4) continue;
+    const int waste = gg * nb - bpr;
+    if (waste < best_waste) {
+      best_g = gg;
+      best_nb = nb;
+      best_waste = waste;
+    }
+  }
+  if (!best_g) return false;
+  *G = best_g;
+  *NB = best_nb;
   return true;
 }
 
@@ -45,6 +60,8 @@ moe_status validate_config(const moe_round_config* c) {
   if (!split_blocks(c->inter, &g, &nb)) return MOE_ERR_UNSUPPORTED;
   if (c->n_layers > 4096) return MOE_ERR_UNSUPPORTED;
   if (c->weight_format == MOE_WEIGHT_Q4S256 && c->inter % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  // Prefill GEMMs step through the reduction four 32-blocks at a time and tile I by 64 rows.
+  if (c->max_rows > MOE_ROUND_MAX_ROWS && c->inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -73,9 +90,10 @@ moe_status validate_run(const moe_round_config* c, const float* hidden, int32_t 
   if (!aligned16(hidden) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
   if ((ids && (reinterpret_cast<uintptr_t>(ids) & 3u)) || (rw && (reinterpret_cast<uintptr_t>(rw) & 3u)))
     return MOE_ERR_INVALID_ARG;
+  // hidden may be out itself (the round then overwrites its input), but not a shifted view of it.
   const uintptr_t bytes = static_cast<uintptr_t>(T) * c->hidden * sizeof(float);
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(hidden), a1 = reinterpret_cast<uintptr_t>(out);
-  if (a0 < a1 + bytes && a1 < a0 + bytes) return MOE_ERR_INVALID_ARG;  // hidden overlaps out
+  if (a0 != a1 && a0 < a1 + bytes && a1 < a0 + bytes) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
