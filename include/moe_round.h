@@ -297,6 +297,27 @@ MOE_ROUND_API moe_status moe_round_profile(moe_round* h, int32_t enable);
  */
 MOE_ROUND_API moe_status moe_round_profile_read(moe_round* h, double* kernel_ms, int32_t* n_runs);
 
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): one decode/verify round exactly like moe_round_run on a handle made from
+ * cfg and layers, eager, with no handle and no allocation.  Its scratch is a fixed device array of
+ * MOE_ROUND_NOALLOC_SCRATCH_BYTES per device, held until the process ends; the library looks up its
+ * device address on the first call on each device (that device must be current).
+ *   cfg, layers  as for moe_round_init (use_graph is ignored: the launches are eager)
+ *   hidden .. route_w, T, k   as for moe_round_run (T <= min(max_rows, 64): no prefill rounds)
+ *   stream       the hipStream_t to enqueue on (NULL = the null stream)
+ *   hip_error    if not NULL, the hipError_t (as int) behind a MOE_ERR_HIP, else 0
+ * Returns MOE_ERR_UNSUPPORTED when the round's scratch (about T*k*(I + H*exact)*4 bytes plus the
+ * per-layer worklists) exceeds MOE_ROUND_NOALLOC_SCRATCH_BYTES; every other error as moe_round_run.
+ * No scratch word needs to start at zero: every word a kernel reads is written earlier in the same
+ * call.  Calls on one device share the array: calls that overlap in time on one device (on
+ * different streams, or from different host threads) race and give wrong results; serialise them.
+ */
+#define MOE_ROUND_NOALLOC_SCRATCH_BYTES (16u << 20)
+MOE_ROUND_API moe_status moe_round_run_noalloc(const moe_round_config* cfg, const moe_layer_weights* layers,
+                                 const float* hidden, int32_t T, int32_t k, float* out,
+                                 int32_t* expert_ids, float* route_w, void* stream, int32_t* hip_error);
+
 /* The hipError_t (as int) of the last MOE_ERR_HIP on this handle, 0 if none. */
 MOE_ROUND_API int32_t moe_round_last_hip_error(const moe_round* h);
 

@@ -28,7 +28,7 @@ def declared():
 def test_header_declares_the_boundary():
     names = declared()
     assert "moe_round_init" in names and "moe_round_run" in names and "moe_round_destroy" in names
-    assert len(names) == 14
+    assert len(names) == 15
     assert {"moe_round_last_stats", "moe_round_floor", "moe_round_stream_read"} <= set(names)
 
 
@@ -147,8 +147,27 @@ def test_null_and_bad_arguments_are_refused_before_any_gpu_call(lib):
     lib.moe_round_destroy(None)
 
 
+def test_noalloc_checks_happen_before_any_gpu_call(lib):
+    """moe_round_run_noalloc refuses bad arguments and rounds whose scratch exceeds its fixed array
+    on the host, and an empty round is a no-op, all without touching a GPU."""
+    from verify_router_gemv_amd import binding
+    w = (binding.LayerWeights * 1)(binding.LayerWeights(*([0x100000] * 8)))
+    herr = ctypes.c_int32(7)
+    big = cfg(H=8192, I=2048, E=16, top_k_max=16, max_rows=64)
+    big.exact = 1                               # ybuf alone: 64 * 16 * 8192 * 4 B = 32 MiB
+    assert lib.moe_round_run_noalloc(ctypes.byref(big), w, 0x200000, 64, 16, 0x4000000, None, None, None,
+                                     ctypes.byref(herr)) == -2
+    assert herr.value == 0
+    ok = cfg()
+    assert lib.moe_round_run_noalloc(ctypes.byref(ok), w, None, 0, 8, None, None, None, None, None) == 0
+    assert lib.moe_round_run_noalloc(ctypes.byref(ok), w, 0x200000, 9, 8, 0x4000000, None, None, None, None) == -1
+    assert lib.moe_round_run_noalloc(None, w, 0x200000, 1, 8, 0x4000000, None, None, None, None) == -1
+    assert lib.moe_round_run_noalloc(ctypes.byref(ok), None, 0x200000, 1, 8, 0x4000000, None, None, None, None) == -1
+    pf = cfg(max_rows=100)
+    assert lib.moe_round_run_noalloc(ctypes.byref(pf), w, 0x200000, 100, 8, 0x4000000, None, None, None, None) == -2
+
+
 def test_new_entry_points_refuse_null_handles(lib):
-    st = (ctypes.c_int32 * 8)()
     assert lib.moe_round_last_stats(None, None, None, None) == -1
     assert lib.moe_round_floor(None) == -1
     assert lib.moe_round_stream_read(None, None, 16) == -1

@@ -78,6 +78,7 @@ def load() -> ctypes.CDLL:
         "moe_round_last_stats": (i32, [vp, P(Stats), P(i32), P(ctypes.c_int64)]),
         "moe_round_floor": (i32, [vp]),
         "moe_round_stream_read": (i32, [vp, vp, ctypes.c_int64]),
+        "moe_round_run_noalloc": (i32, [P(Config), P(LayerWeights), vp, i32, i32, vp, vp, vp, vp, P(i32)]),
         "moe_round_last_hip_error": (i32, [vp]),
         "moe_round_strerror": (ctypes.c_char_p, [i32]),
         "moe_round_destroy": (None, [vp]),
@@ -174,6 +175,39 @@ def layer_struct(layer, H: int, I: int, E: int, weight_format=0) -> LayerWeights
         _check(t, f, *spec[f])
         ptrs[f] = t.data_ptr()
     return LayerWeights(*[ptrs[f] for f in _FIELDS])
+
+
+def run_noalloc(layers: Sequence, H: int, I: int, E: int, top_k_max: int, hidden: torch.Tensor, k: int,
+                out: torch.Tensor, ids: Optional[torch.Tensor] = None, route_w: Optional[torch.Tensor] = None,
+                max_rows: Optional[int] = None, residual: bool = False, exact: bool = False, weight_format=None,
+                fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0,
+                stream: Optional[torch.cuda.Stream] = None):
+    """One decode/verify round through moe_round_run_noalloc: no handle, no allocation (the library's
+    fixed per-device scratch array). Same arguments and results as MoeRound(...).run(...)."""
+    lib = load()
+    L = len(layers)
+    T = hidden.shape[0]
+    if weight_format is None:
+        weight_format = layer_format(layers[0]) or "q4b32"
+    fmt = weight_format_code(weight_format)
+    cfg = make_config(H, I, E, top_k_max, L, max_rows or max(T, 1), residual, False, fused_max_rows,
+                      rows_per_item, mfma_min_rows, exact, fmt)
+    wt = (LayerWeights * L)(*[layer_struct(l, H, I, E, fmt) for l in layers])
+    _check(hidden, "hidden", (torch.float32,), (T, H))
+    _check(out, "out", (torch.float32,), (T, H))
+    if ids is not None:
+        _check(ids, "expert_ids", (torch.int32,), (L, T, k))
+    if route_w is not None:
+        _check(route_w, "route_w", (torch.float32,), (L, T, k))
+    st_ = stream if stream is not None else torch.cuda.current_stream()
+    herr = ctypes.c_int32()
+    st = lib.moe_round_run_noalloc(ctypes.byref(cfg), wt, ctypes.c_void_p(hidden.data_ptr()), T, k,
+                                   ctypes.c_void_p(out.data_ptr()),
+                                   ctypes.c_void_p(ids.data_ptr() if ids is not None else 0),
+                                   ctypes.c_void_p(route_w.data_ptr() if route_w is not None else 0),
+                                   ctypes.c_void_p(st_.cuda_stream), ctypes.byref(herr))
+    if st != OK:
+        raise MoeRoundError(st, "moe_round_run_noalloc", herr.value)
 
 
 class MoeRound:

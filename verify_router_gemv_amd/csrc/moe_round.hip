@@ -10,6 +10,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <vector>
@@ -77,6 +78,7 @@ struct moe_round {
   Ingress h_ing{};                     // last ingress of a run
   bool dev_ing_valid = false;          // d_ing holds h_ing
   std::vector<moe_layer_weights> h_wtab;
+  const moe_layer_weights* wts = nullptr;  // the current weights [L] (h_wtab's data, or the caller's)
   bool dev_wtab_valid = false;         // d_wtab holds h_wtab
   unsigned char* staging = nullptr;    // pinned ring for graph-mode ingress uploads
   size_t slot_bytes = 0;
@@ -192,66 +194,88 @@ static Args base_args(const moe_round* h, int T, int k) {
 }
 
 // Launches of a round. Rounds of up to kFusedMaxRows rows run three kernels per layer: the gate/up
-// kernel computes the selection itself. Larger rounds run a separate selection kernel.
-static bool plan(const moe_round* h, int T, int k, std::vector<Launch>* out) {
+// kernel computes the selection itself. Larger rounds run a separate selection kernel (and, from
+// kSplitTopkRows rows, a many-block top-k before it); exact mode adds the combine.
+struct RoundPlan {
+  KernelFn lg = nullptr, sel = nullptr, gu = nullptr, dn = nullptr, topk = nullptr;
+  dim3 grid_lg, grid_gu, grid_dn, grid_topk, grid_comb;
+  int shm_gu = 0, shm_dn = 0;
+  bool fused = false, split_topk = false, exact = false;
+};
+constexpr int kMaxLaunchesPerLayer = 6;  // logits, top-k, select, gate/up, down, combine
+
+static bool make_plan(const moe_round* h, int T, int k, RoundPlan* p) {
   const int E = h->cfg.n_experts, H = h->cfg.hidden, I = h->cfg.inter;
   const int umax = items_bound(T * k, E, rows_per_item(h, T));
   const bool wide = T >= kWideRows;
-  const bool fused = T <= h->fused_max_rows;
-  const bool split_topk = T >= kSplitTopkRows;
-  KernelFn lg = pick_logits(H, T), sel = pick_select(E, split_topk), gu = nullptr, dn = nullptr;
+  p->fused = T <= h->fused_max_rows;
+  p->split_topk = T >= kSplitTopkRows;
+  p->exact = h->cfg.exact != 0;
+  p->lg = pick_logits(H, T);
+  p->sel = pick_select(E, p->split_topk);
+  p->topk = pick_topk_rows(E);
   int rows_gu = 0, rows_dn = 0;
   const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
   const int fmt = h->cfg.weight_format;
-  if (!lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, fused ? fused_select_keys(E) : 0, fmt, &gu, &rows_gu) ||
-      !pick_gemv(h->Gi, h->NBi, 0, false, h->cfg.exact, fmt, &dn, &rows_dn))
+  if (!p->lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, p->fused ? fused_select_keys(E) : 0, fmt, &p->gu, &rows_gu) ||
+      !pick_gemv(h->Gi, h->NBi, 0, false, h->cfg.exact, fmt, &p->dn, &rows_dn))
     return false;
-  const dim3 grid_lg = logits_grid(E, H, T);
+  p->grid_lg = logits_grid(E, H, T);
   const int units_gu = umax * ((I + rows_gu - 1) / rows_gu);
-  const dim3 grid_gu(fused && units_gu > kFusedBlocks ? kFusedBlocks : units_gu);
-  const dim3 grid_dn(umax * ((H + rows_dn - 1) / rows_dn));
+  p->grid_gu = dim3(p->fused && units_gu > kFusedBlocks ? kFusedBlocks : units_gu);
+  p->grid_dn = dim3(umax * ((H + rows_dn - 1) / rows_dn));
+  p->grid_topk = dim3((T + kWaves - 1) / kWaves);
+  p->grid_comb = dim3(T, (H + 4 * kThreads - 1) / (4 * kThreads));
   int gu_words = gateup_stage_words(H);
   if (h->Gh == 64 && h->NBh == 1) gu_words += kMfmaExtraWords;  // matrix-core tile: (s, m) tables, partial sums
-  const int shm_gu = wide ? static_cast<int>(sizeof(uint32_t)) * gu_words : 0;
-  const int shm_dn = static_cast<int>(sizeof(uint32_t)) * xstage_rows(I) * (I / 32) * (kXqWords + 2);
-  out->clear();
-  for (int l = 0; l < h->cfg.n_layers; ++l) {
-    out->push_back({lg, grid_lg, kThreads, 0, l, 0});
-    if (split_topk) out->push_back({pick_topk_rows(E), dim3((T + kWaves - 1) / kWaves), kThreads, 0, l, 1});
-    if (!fused) out->push_back({sel, dim3(1), kSelectThreads, 0, l, 1});
-    out->push_back({gu, grid_gu, kThreads, shm_gu, l, 2});
-    out->push_back({dn, grid_dn, kThreads, shm_dn, l, 3});
-    if (h->cfg.exact) out->push_back({combine_kernel, dim3(T, (H + 4 * kThreads - 1) / (4 * kThreads)), kThreads, 0, l, 4});
-  }
+  p->shm_gu = wide ? static_cast<int>(sizeof(uint32_t)) * gu_words : 0;
+  p->shm_dn = static_cast<int>(sizeof(uint32_t)) * xstage_rows(I) * (I / 32) * (kXqWords + 2);
   return true;
 }
 
+// The launches of layer l, in stream order, into out[0 .. kMaxLaunchesPerLayer - 1]; returns their number.
+static int layer_launches(const RoundPlan& p, int l, Launch* out) {
+  int n = 0;
+  out[n++] = {p.lg, p.grid_lg, kThreads, 0, l, 0};
+  if (!p.fused && p.split_topk) out[n++] = {p.topk, p.grid_topk, kThreads, 0, l, 1};
+  if (!p.fused) out[n++] = {p.sel, dim3(1), kSelectThreads, 0, l, 1};
+  out[n++] = {p.gu, p.grid_gu, kThreads, p.shm_gu, l, 2};
+  out[n++] = {p.dn, p.grid_dn, kThreads, p.shm_dn, l, 3};
+  if (p.exact) out[n++] = {combine_kernel, p.grid_comb, kThreads, 0, l, 4};
+  return n;
+}
+
 static moe_status build_graph(moe_round* h, int T, int k, GraphEntry* ge) {
-  std::vector<Launch> ls;
-  if (!plan(h, T, k, &ls)) return MOE_ERR_UNSUPPORTED;
+  RoundPlan p;
+  if (!make_plan(h, T, k, &p)) return MOE_ERR_UNSUPPORTED;
   Args a = base_args(h, T, k);
   a.ing = h->d_ing;
   a.wtab = h->d_wtab;
   hipGraph_t g = nullptr;
   MOE_HIP(h, hipGraphCreate(&g, 0));
   hipGraphNode_t prev = nullptr;
-  for (const Launch& L : ls) {
-    int layer = L.layer;
-    void* params[] = {&a, &layer};
-    hipKernelNodeParams p{};
-    p.func = reinterpret_cast<void*>(L.fn);
-    p.gridDim = L.grid;
-    p.blockDim = dim3(L.threads);
-    p.sharedMemBytes = L.shmem;
-    p.kernelParams = params;
-    p.extra = nullptr;
-    hipGraphNode_t node = nullptr;
-    hipError_t e = hipGraphAddKernelNode(&node, g, prev ? &prev : nullptr, prev ? 1 : 0, &p);
-    if (e != hipSuccess) {
-      (void)hipGraphDestroy(g);
-      return hip_fail(h, e);
+  for (int l = 0; l < h->cfg.n_layers; ++l) {
+    Launch ls[kMaxLaunchesPerLayer];
+    const int n = layer_launches(p, l, ls);
+    for (int i = 0; i < n; ++i) {
+      const Launch& L = ls[i];
+      int layer = L.layer;
+      void* params[] = {&a, &layer};
+      hipKernelNodeParams kp{};
+      kp.func = reinterpret_cast<void*>(L.fn);
+      kp.gridDim = L.grid;
+      kp.blockDim = dim3(L.threads);
+      kp.sharedMemBytes = L.shmem;
+      kp.kernelParams = params;
+      kp.extra = nullptr;
+      hipGraphNode_t node = nullptr;
+      hipError_t e = hipGraphAddKernelNode(&node, g, prev ? &prev : nullptr, prev ? 1 : 0, &kp);
+      if (e != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        return hip_fail(h, e);
+      }
+      prev = node;
     }
-    prev = node;
   }
   hipGraphExec_t x = nullptr;
   hipError_t e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
@@ -264,29 +288,33 @@ static moe_status build_graph(moe_round* h, int T, int k, GraphEntry* ge) {
   return MOE_OK;
 }
 
-// Eager: every launch carries the ingress pointers and its layer's weights by value.
+// Eager: every launch carries the ingress pointers and its layer's weights by value. No host
+// allocation: the plan is a fixed struct and the launches are expanded one layer at a time.
 static moe_status launch_eager(moe_round* h, int T, int k, hipEvent_t* evs, int* kinds = nullptr,
                                int* n_launched = nullptr) {
-  std::vector<Launch> ls;
-  if (!plan(h, T, k, &ls)) return MOE_ERR_UNSUPPORTED;
-  if (kinds)
-    for (size_t i = 0; i < ls.size(); ++i) kinds[i] = ls[i].layer * kKernelsPerLayer + ls[i].kind;
-  if (n_launched) *n_launched = static_cast<int>(ls.size());
+  RoundPlan p;
+  if (!make_plan(h, T, k, &p)) return MOE_ERR_UNSUPPORTED;
   Args a = base_args(h, T, k);
   a.in = h->h_ing;
   int i = 0;
-  for (const Launch& L : ls) {
-    a.w = h->h_wtab[L.layer];
-    int layer = L.layer;
-    void* params[] = {&a, &layer};
-    if (evs)  // events stamped with the dispatch's own start and end times
-      MOE_HIP(h, hipExtLaunchKernel(reinterpret_cast<const void*>(L.fn), L.grid, dim3(L.threads), params,
-                                    L.shmem, h->stream, evs[2 * i], evs[2 * i + 1], 0));
-    else
-      MOE_HIP(h, hipLaunchKernel(reinterpret_cast<const void*>(L.fn), L.grid, dim3(L.threads), params,
-                                 L.shmem, h->stream));
-    ++i;
+  for (int l = 0; l < h->cfg.n_layers; ++l) {
+    Launch ls[kMaxLaunchesPerLayer];
+    const int n = layer_launches(p, l, ls);
+    a.w = h->wts[l];
+    for (int j = 0; j < n; ++j, ++i) {
+      const Launch& L = ls[j];
+      if (kinds) kinds[i] = L.layer * kKernelsPerLayer + L.kind;
+      int layer = L.layer;
+      void* params[] = {&a, &layer};
+      if (evs)  // events stamped with the dispatch's own start and end times
+        MOE_HIP(h, hipExtLaunchKernel(reinterpret_cast<const void*>(L.fn), L.grid, dim3(L.threads), params,
+                                      L.shmem, h->stream, evs[2 * i], evs[2 * i + 1], 0));
+      else
+        MOE_HIP(h, hipLaunchKernel(reinterpret_cast<const void*>(L.fn), L.grid, dim3(L.threads), params,
+                                   L.shmem, h->stream));
+    }
   }
+  if (n_launched) *n_launched = i;
   return MOE_OK;
 }
 
@@ -383,7 +411,7 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
     return e;
   };
   for (int l = 0; l < L; ++l) {
-    a.w = h->h_wtab[l];
+    a.w = h->wts[l];
     int layer = l;
     void* gp[] = {&a, &layer};
     const float* xin = l == 0 ? h->h_ing.hidden : h->pf_xbuf[(l - 1) & 1];
@@ -511,6 +539,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   h->Ucap = (T * K < E) ? T * K : E;
   h->Icap = T * K;  // work items never outnumber (row, rank) pairs
   h->h_wtab.assign(layers, layers + L);
+  h->wts = h->h_wtab.data();
   if (cfg->fused_max_rows != 0) h->fused_max_rows = cfg->fused_max_rows < 0 ? 0 : cfg->fused_max_rows;
   h->rows_per_item = cfg->rows_per_item;
   if (cfg->mfma_min_rows != 0) h->mfma_rows = cfg->mfma_min_rows < 0 ? 0 : cfg->mfma_min_rows;
@@ -812,7 +841,7 @@ extern "C" moe_status moe_round_floor(moe_round* h) {
   const bool s256 = c.weight_format == MOE_WEIGHT_Q4S256;
   const int64_t smh = (s256 ? H / 64 : H / 32) * 4, smi = (s256 ? I / 64 : I / 32) * 4;  // bytes per row
   for (int l = 0; l < c.n_layers; ++l) {
-    const moe_layer_weights& w = h->h_wtab[l];
+    const moe_layer_weights& w = h->wts[l];
     FloorArgs r{};
     r.nr = 1;
     r.r[0] = {reinterpret_cast<const uint8_t*>(w.router_w), 0, E * H * 4};
@@ -853,6 +882,113 @@ extern "C" moe_status moe_round_stream_read(moe_round* h, const void* buf, int64
   f.r[0] = {static_cast<const uint8_t*>(buf), 0, bytes};
   const int64_t chunks = (bytes + kFloorChunk - 1) / kFloorChunk;
   return launch_floor(h, f, static_cast<int>(chunks < (1 << 20) ? chunks : (1 << 20)), 1 << 20);
+}
+
+// ------------------------------------------------------------------------------------------
+// The no-allocation entry point: a decode/verify round whose scratch lives in a fixed device array
+// ------------------------------------------------------------------------------------------
+
+// Scratch of moe_round_run_noalloc: one array per device, alive until the process ends. Host code
+// never uses this name as an address (on the host it is only a stand-in for the symbol); the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = MOE_ROUND_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::atomic<unsigned char*> g_scratch_ptr[kMaxDevices];
+
+static moe_status noalloc_scratch(int dev, unsigned char** out, int32_t* hip_err) {
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  unsigned char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {  // first call on this device (the device is current): look the symbol up once
+    void* addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !addr) {
+      *hip_err = static_cast<int32_t>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return MOE_ERR_HIP;
+    }
+    p = static_cast<unsigned char*>(addr);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+// Carve the round's scratch out of `base` (or, with base null, only count it): returns the bytes.
+static size_t noalloc_layout(moe_round* h, int T, unsigned char* base) {
+  const moe_round_config& c = h->cfg;
+  const size_t L = c.n_layers, H = c.hidden, I = c.inter, E = c.n_experts;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> unsigned char* {
+    off = (off + 255) & ~size_t(255);
+    unsigned char* q = base ? base + off : nullptr;
+    off += bytes;
+    return q;
+  };
+  const size_t P = h->Pcap, U = h->Ucap, It = h->Icap;
+  h->xbuf[0] = reinterpret_cast<float*>(L > 1 ? take(sizeof(float) * T * H) : nullptr);
+  h->xbuf[1] = reinterpret_cast<float*>(L > 1 ? take(sizeof(float) * T * H) : nullptr);
+  h->logits = reinterpret_cast<double*>(take(sizeof(double) * T * E));
+  h->n_unique = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * L));
+  h->uniq = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * L * U));
+  h->offs = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * L * (U + 1)));
+  h->pairs = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * L * P));
+  h->pair_w = reinterpret_cast<float*>(take(sizeof(float) * L * P));
+  h->rec = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * L * It * kRecWords));
+  h->hbuf = reinterpret_cast<float*>(take(sizeof(float) * P * I));
+  h->slot_of = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * L * P));
+  h->tsel = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * P));
+  h->tp = reinterpret_cast<float*>(take(sizeof(float) * P));
+  h->ybuf = reinterpret_cast<float*>(c.exact ? take(sizeof(float) * P * H) : nullptr);
+  h->xq = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * T * (H / 32) * kXqWords));
+  h->xss = reinterpret_cast<float2*>(take(sizeof(float2) * T * (H / 32)));
+  return off;
+}
+
+extern "C" moe_status moe_round_run_noalloc(const moe_round_config* cfg, const moe_layer_weights* layers,
+                                            const float* hidden, int32_t T, int32_t k, float* out,
+                                            int32_t* expert_ids, float* route_w, void* stream,
+                                            int32_t* hip_error) {
+  if (hip_error) *hip_error = 0;
+  moe_status st = validate_config(cfg);
+  if (st != MOE_OK) return st;
+  st = validate_layers(cfg, layers);
+  if (st != MOE_OK) return st;
+  st = validate_run(cfg, hidden, T, k, out, expert_ids, route_w);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (T > MOE_ROUND_MAX_ROWS) return MOE_ERR_UNSUPPORTED;  // prefill rounds need handle scratch
+  // A handle on the stack over the fixed array: nothing here allocates, on the host or the device.
+  moe_round h;
+  h.cfg = *cfg;
+  h.stream = static_cast<hipStream_t>(stream);
+  split_blocks(cfg->hidden, &h.Gh, &h.NBh);
+  split_blocks(cfg->inter, &h.Gi, &h.NBi);
+  h.Pcap = T * k;
+  h.Ucap = (T * k < cfg->n_experts) ? T * k : cfg->n_experts;
+  h.Icap = T * k;
+  if (cfg->fused_max_rows != 0) h.fused_max_rows = cfg->fused_max_rows < 0 ? 0 : cfg->fused_max_rows;
+  h.rows_per_item = cfg->rows_per_item;
+  if (cfg->mfma_min_rows != 0) h.mfma_rows = cfg->mfma_min_rows < 0 ? 0 : cfg->mfma_min_rows;
+  if (noalloc_layout(&h, T, nullptr) > kNoAllocScratchBytes) return MOE_ERR_UNSUPPORTED;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    if (hip_error) *hip_error = static_cast<int32_t>(e);
+    return MOE_ERR_HIP;
+  }
+  unsigned char* base = nullptr;
+  int32_t herr = 0;
+  st = noalloc_scratch(dev, &base, &herr);
+  if (st != MOE_OK) {
+    if (hip_error) *hip_error = herr;
+    return st;
+  }
+  noalloc_layout(&h, T, base);
+  h.h_ing = Ingress{hidden, out, expert_ids, route_w};
+  h.wts = layers;
+  st = launch_eager(&h, T, k, nullptr);
+  if (hip_error) *hip_error = h.last_hip;
+  return st;
 }
 
 extern "C" int32_t moe_round_last_hip_error(const moe_round* h) { return h ? h->last_hip : 0; }
