@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MOE_ROUND_ABI_VERSION 1
+#define MOE_ROUND_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define MOE_ROUND_API __attribute__((visibility("default")))
@@ -142,6 +142,12 @@ typedef struct moe_round_config {
                              super-block, 0.5625 B/weight; needs I a multiple of 256 (H always
                              is), else init returns MOE_ERR_UNSUPPORTED. The matrix-core tile
                              is used with MOE_WEIGHT_Q4B32 only.                            */
+  int32_t prefetch;       /* 1: overlap independent reads across the layer's kernels: each gate/up
+                             block touches the down rows the down block with the same index will
+                             read, and each down block the next layer's router row of the logits
+                             block with its index (no extra HBM bytes, results unchanged); 0
+                             (default): off (measured slower: the touches queue behind the
+                             weight loads in each CU's load path)                          */
 } moe_round_config;
 
 #define MOE_WEIGHT_Q4B32 0

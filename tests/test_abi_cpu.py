@@ -89,7 +89,10 @@ def test_supported_configs_validate(lib, kw):
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(raw_abi_version=2), -1),
+    (dict(raw_abi_version=1), -1),     # the configuration struct of ABI 1 lacks `prefetch`
+    (dict(raw_abi_version=3), -1),
+    (dict(raw_prefetch=2), -1),
+    (dict(raw_prefetch=-1), -1),
     (dict(H=0), -1),
     (dict(I=-32), -1),
     (dict(E=0), -1),

@@ -203,6 +203,21 @@ def test_deep_stack_free_running():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("use_graph", [False, True])
+def test_stack_with_prefetch(use_graph):
+    """A 4-layer residual stack with the early touches on (down blocks touch the next layer's router
+    rows): the same ids and outputs as the oracle, eager and as a graph."""
+    cfg = synth.config("deep").replace(L=4, E=128)
+    layers = [synth.make_layer(cfg, seed=9, layer=l, device=DEV) for l in range(cfg.L)]
+    views = [oracle_view(l) for l in layers]
+    g = GpuRound(layers, cfg, max_rows=8, use_graph=use_graph, prefetch=1)
+    for T in (1, 3, 8):
+        say(f"case stack prefetch graph={use_graph} T={T}")
+        X = synth.make_activations(cfg, T, seed=19, round_idx=T, device=DEV)
+        check_layer_round(g, views, X, cfg.k, f"stack prefetch T={T}")
+    g.close()
+
+
 def test_many_rows_share_experts(verify):
     """40 correlated rows: the hot experts get far more than 16 rows (several matrix-core passes)."""
     cfg, layer, view = verify
@@ -253,6 +268,7 @@ def test_tied_logits_go_to_the_lower_id(verify, k):
 @pytest.mark.parametrize("shape", [
     dict(fused_max_rows=-1, rows_per_item=1),   # separate selection kernel, one row per item
     dict(fused_max_rows=15, rows_per_item=8),   # selection in gate/up up to 15 rows, big items
+    dict(prefetch=1),                           # gate/up touches the down rows of its index
 ])
 def test_launch_shape_choices(verify, shape):
     """Other launch shapes give the same ids and worklists and outputs within tolerance."""

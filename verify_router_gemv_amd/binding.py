@@ -16,7 +16,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_round.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_ROWS = 64
 MAX_PREFILL_ROWS = 16384
 MAX_EXPERTS = 512
@@ -40,7 +40,7 @@ class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "hidden", "inter", "n_experts", "top_k_max", "n_layers", "max_rows",
         "residual", "use_graph", "fused_max_rows", "rows_per_item", "mfma_min_rows", "exact",
-        "weight_format")]
+        "weight_format", "prefetch")]
 
 
 class LayerWeights(ctypes.Structure):
@@ -109,12 +109,15 @@ def weight_format_code(fmt) -> int:
 
 
 def make_config(H, I, E, top_k_max, n_layers=1, max_rows=8, residual=False, use_graph=True,
-                fused_max_rows=0, rows_per_item=0, mfma_min_rows=0, exact=False, weight_format=0) -> Config:
+                fused_max_rows=0, rows_per_item=0, mfma_min_rows=0, exact=False, weight_format=0,
+                prefetch=0) -> Config:
     """Launch-shape fields: 0 = default (see moe_round.h); -1 = never (fused_max_rows, mfma_min_rows).
     exact: fixed-order combine (bitwise reproducible, row outputs independent of the round).
-    weight_format: 0 / "q4b32" (per-32 fp16 scale and minimum) or 1 / "q4s256" (super-blocks)."""
+    weight_format: 0 / "q4b32" (per-32 fp16 scale and minimum) or 1 / "q4s256" (super-blocks).
+    prefetch: 1 = touch the next kernel's weight lines early, 0 = off (default)."""
     return Config(ABI_VERSION, H, I, E, top_k_max, n_layers, max_rows, int(bool(residual)), int(bool(use_graph)),
-                  fused_max_rows, rows_per_item, mfma_min_rows, int(bool(exact)), weight_format_code(weight_format))
+                  fused_max_rows, rows_per_item, mfma_min_rows, int(bool(exact)), weight_format_code(weight_format),
+                  prefetch)
 
 
 def validate_config(cfg: Config) -> int:
@@ -180,7 +183,7 @@ def layer_struct(layer, H: int, I: int, E: int, weight_format=0) -> LayerWeights
 def run_noalloc(layers: Sequence, H: int, I: int, E: int, top_k_max: int, hidden: torch.Tensor, k: int,
                 out: torch.Tensor, ids: Optional[torch.Tensor] = None, route_w: Optional[torch.Tensor] = None,
                 max_rows: Optional[int] = None, residual: bool = False, exact: bool = False, weight_format=None,
-                fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0,
+                fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0, prefetch: int = 0,
                 stream: Optional[torch.cuda.Stream] = None):
     """One decode/verify round through moe_round_run_noalloc: no handle, no allocation (the library's
     fixed per-device scratch array). Same arguments and results as MoeRound(...).run(...)."""
@@ -191,7 +194,7 @@ def run_noalloc(layers: Sequence, H: int, I: int, E: int, top_k_max: int, hidden
         weight_format = layer_format(layers[0]) or "q4b32"
     fmt = weight_format_code(weight_format)
     cfg = make_config(H, I, E, top_k_max, L, max_rows or max(T, 1), residual, False, fused_max_rows,
-                      rows_per_item, mfma_min_rows, exact, fmt)
+                      rows_per_item, mfma_min_rows, exact, fmt, prefetch)
     wt = (LayerWeights * L)(*[layer_struct(l, H, I, E, fmt) for l in layers])
     _check(hidden, "hidden", (torch.float32,), (T, H))
     _check(out, "out", (torch.float32,), (T, H))
@@ -216,7 +219,7 @@ class MoeRound:
     def __init__(self, layers: Sequence, H: int, I: int, E: int, top_k_max: int, max_rows: int = 8,
                  residual: bool = False, use_graph: bool = True, stream: Optional[torch.cuda.Stream] = None,
                  fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0, exact: bool = False,
-                 weight_format=None):
+                 weight_format=None, prefetch: int = 0):
         """weight_format: None = what the layers declare (default "q4b32"), else 0/1 or its name."""
         self.lib = load()
         self.H, self.I, self.E, self.L = H, I, E, len(layers)
@@ -225,7 +228,7 @@ class MoeRound:
             weight_format = layer_format(layers[0]) or "q4b32"
         self.weight_format = weight_format_code(weight_format)
         self.cfg = make_config(H, I, E, top_k_max, self.L, max_rows, residual, use_graph,
-                               fused_max_rows, rows_per_item, mfma_min_rows, exact, self.weight_format)
+                               fused_max_rows, rows_per_item, mfma_min_rows, exact, self.weight_format, prefetch)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._layers = list(layers)          # keep the weight tensors alive
         self._wt = (LayerWeights * self.L)(*[layer_struct(l, H, I, E, self.weight_format) for l in layers])

@@ -51,7 +51,7 @@ constexpr int kXStageMax = 8;        // SwiGLU rows the down kernel stages in LD
 constexpr int kXStageBytes = 65536;  // ... within 64 KB of LDS
 
 // Per-run pointers. Eager launches carry them by value; graph replays read them from a fixed
-// device copy (written when they change), so a captured graph is never rebuilt.
+// device copy (written when they change), so a captured graph is never rebuilt for a new request.
 struct Ingress {
   const float* hidden;  // [T][H]
   float* out;           // [T][H]
@@ -62,8 +62,7 @@ struct Ingress {
 struct Args {
   const Ingress* ing;              // graph mode: device ingress; eager mode: null
   Ingress in;                      // eager mode ingress
-  const moe_layer_weights* wtab;   // graph mode: device table [L]; eager mode: null
-  moe_layer_weights w;             // eager mode: this layer's weights
+  moe_layer_weights w;             // this layer's weights (a graph node's parameters in graph mode)
   float* xbuf0;
   float* xbuf1;
   double* logits;     // [T_max][E]
@@ -87,12 +86,14 @@ struct Args {
   int32_t xstage_i;  // down: SwiGLU rows staged in LDS (as digits) at a time
   int32_t mfma_rows;  // gate/up: experts with at least this many rows use the matrix-core tile (0: never)
   int32_t exact;      // fixed-order combine (the logits kernel does not seed the output)
+  int32_t prefetch;   // touch the next kernel's weight lines (see touch_lines)
+  const float* router_next;  // the next layer's router matrix (null on the last layer)
 };
 
 __device__ __forceinline__ Ingress get_ingress(const Args& a) { return a.ing ? *a.ing : a.in; }
-__device__ __forceinline__ moe_layer_weights get_weights(const Args& a, int layer) {
-  return a.wtab ? a.wtab[layer] : a.w;
-}
+// A layer's weight pointers are always kernel arguments (so every weight address is known without a
+// load); graph replays pick up new weights through their nodes' parameters, not a device table.
+__device__ __forceinline__ const moe_layer_weights& get_weights(const Args& a, int) { return a.w; }
 __device__ __forceinline__ const float* layer_input(const Args& a, const Ingress& in, int layer) {
   if (layer == 0) return in.hidden;
   return ((layer - 1) & 1) ? a.xbuf1 : a.xbuf0;
@@ -251,6 +252,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define MOE_GLOBAL __attribute__((address_space(1)))
+#define MOE_LDS __attribute__((address_space(3)))
 
 // Streaming (non-temporal) loads through global (not flat) addressing: weights are read once per
 // round; keep them from evicting the small reused data (activations, logits, records).
@@ -283,6 +285,35 @@ __device__ __forceinline__ void opaque(uint4& v) {
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Load one word of every 64-byte line of [p, p + bytes) (bytes a positive multiple of 4), spread
+// over the block's threads (at most N lines per thread). Plain loads (not the streaming ones) so the
+// lines are kept in L2: a kernel reads, a few microseconds early, lines that the next kernel's block
+// with the same index will read, and blocks with equal indices of consecutive launches run on the
+// same XCD (one L2). The words are kept apart and only consumed by keep_live at the end of the
+// block's work: any earlier use would make the wave wait for them, and (the memory counter being in
+// order) for every load issued before them.
+template <int N>
+struct Touched {
+  uint32_t v[N];
+};
+template <int N>
+__device__ __forceinline__ Touched<N> touch_lines(const void* p, size_t bytes, int tid, int nthreads) {
+  const uint8_t* b = static_cast<const uint8_t*>(p);
+  Touched<N> t;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const size_t off = (static_cast<size_t>(i) * nthreads + tid) * 64;
+    t.v[i] = *(const MOE_GLOBAL uint32_t*)(b + (off < bytes ? off : bytes - 4));
+  }
+  return t;
+}
+// Marks the words as used without storing them (the wave waits for them here).
+template <int N>
+__device__ __forceinline__ void keep_live(const Touched<N>& t) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(t.v[i]));
+}
 
 // Order-preserving 64-bit key of a logit with the expert id in the low 9 bits, so one unsigned
 // max picks the largest logit and, among logits equal to 2^-43 relative, the lower id.

@@ -10,13 +10,23 @@ namespace moe {
 // elements each, in the layout and with the rounding of the layer input's digits (kXqWords words
 // per block: three balanced base-256 digits of rint(h / step), step = max|h| / kXqMax), plus the
 // block's (step, sum of h). `n` rows of length K, contiguous from `src`.
-__device__ __forceinline__ void stage_digits(const float* src, int K, int n, uint32_t* dig, float2* ss) {
+// The four values this thread quantises in the pass starting at block blk0 (blocks past the end:
+// the last block again, still in the reductions).
+__device__ __forceinline__ float4 stage_load(const float* src, int K, int n, int blk0) {
+  const int total = n * (K / 32), sub = threadIdx.x & 7;
+  const int bc = min(blk0 + static_cast<int>(threadIdx.x >> 3), total - 1);
+  return load_f4(src + static_cast<size_t>(bc) * 32 + 4 * sub);
+}
+
+// first: the first pass's values, stage_load(src, K, n, 0), which the caller loads (early).
+__device__ __forceinline__ void stage_digits(const float* src, int K, int n, uint32_t* dig, float2* ss,
+                                             float4 first) {
   const int nblk = K / 32, total = n * nblk;
   const int tid = threadIdx.x, sub = tid & 7;
+  float4 v = first;
   for (int blk0 = 0; blk0 < total; blk0 += kThreads / 8) {
+    if (blk0 > 0) v = stage_load(src, K, n, blk0);
     const int blk = blk0 + (tid >> 3);
-    const int bc = min(blk, total - 1);  // past the end: a clamped block, still in the reductions
-    const float4 v = load_f4(src + static_cast<size_t>(bc) * 32 + 4 * sub);
     float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     float sum = (v.x + v.y) + (v.z + v.w);
     mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
@@ -78,10 +88,26 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   const int g = lane % G, rs = lane / G;
   const float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
   const Ingress in = get_ingress(a);
-  const moe_layer_weights W = get_weights(a, layer);
   float* __restrict__ xn = layer_output(a, in, layer);
   const int row0 = tile * ROWS_B + wave * ROWS_W + rs;
   const size_t rq = static_cast<size_t>(I) / 2, rsm = sm_row_words<FMT>(I);
+
+  // The next layer's router row of the logits block with this block's index, touched (see
+  // touch_lines) after the record (whose wait must not include it) and before the weights (whose
+  // wait covers it); issued in any case (without a next layer: the first line of this layer's codes).
+  const float* rnext = a.router_next;
+  const moe_layer_weights& W = get_weights(a, layer);
+  const bool pf_on = a.prefetch != 0 && rnext != nullptr && static_cast<int>(blockIdx.x) < a.E;
+  const Touched<1> pfr = touch_lines<1>(pf_on ? static_cast<const void*>(rnext + static_cast<size_t>(blockIdx.x) * H)
+                                              : static_cast<const void*>(W.down_q),
+                                        pf_on ? static_cast<size_t>(H) * 4 : 64, threadIdx.x, kThreads);
+
+  // The first chunk's SwiGLU values, loaded before the weights (they return sooner and are needed
+  // first: the chunk is quantised into LDS before any weight is used). The scheduling barrier keeps
+  // these loads (and the touch) ahead of the weight loads.
+  const int xst = a.xstage_i;
+  const float4 h0 = stage_load(a.hbuf + static_cast<size_t>(wk.p0) * I, I, min(xst, wk.np), 0);
+  __builtin_amdgcn_sched_barrier(0);
 
   uint4 cd[RW][NB];
   BlockScale<FMT> sd[RW][NB];
@@ -97,13 +123,13 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
     }
   }
 
-  const int xst = a.xstage_i;
   uint32_t* dig = dlds;
   float2* ss = reinterpret_cast<float2*>(dlds + static_cast<size_t>(xst) * nblk * kXqWords);
   for (int s0 = 0; s0 < wk.np; s0 += xst) {
     const int ns = min(xst, wk.np - s0);
     if (s0 > 0) __syncthreads();  // the previous chunk has been read by every wave
-    stage_digits(a.hbuf + static_cast<size_t>(wk.p0 + s0) * I, I, ns, dig, ss);
+    const float* hsrc = a.hbuf + static_cast<size_t>(wk.p0 + s0) * I;
+    stage_digits(hsrc, I, ns, dig, ss, s0 == 0 ? h0 : stage_load(hsrc, I, ns, 0));
     __syncthreads();
     for (int c = 0; c < ns; ++c) {
       const float wgt = pw[wk.p0 + s0 + c];
@@ -159,6 +185,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
       }
     }
   }
+  keep_live(pfr);
 }
 
 // Exact mode: out[t][h] = (residual ? x[t][h] : 0) + sum over ranks j = 0..k-1, in that order, of

@@ -235,7 +235,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane % G, rs = lane / G;
-  const moe_layer_weights W = get_weights(a, layer);
+  const moe_layer_weights& W = get_weights(a, layer);
   const int row0 = tile * ROWS_B + wave * ROWS_W + rs;
   const size_t rq = static_cast<size_t>(H) / 2, rsm = sm_row_words<FMT>(H);
   const int SR = a.xstage_h;
@@ -272,26 +272,12 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
     }
   }
 
-  uint4 cg[RW][NB], cu[RW][NB];
-  BlockScale<FMT> sg[RW][NB], su[RW][NB];
-#pragma unroll
-  for (int w = 0; w < RW; ++w) {
-    const size_t r = static_cast<size_t>(wk.e) * I + min(row0 + w * RPI, I - 1);  // rows past I: not stored
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int bl = g + nb * G, b = min(bl, nblk - 1);
-      cg[w][nb] = load_stream_u4(W.gate_q + r * rq + 16 * b);
-      cu[w][nb] = load_stream_u4(W.up_q + r * rq + 16 * b);
-      sg[w][nb].load(W.gate_sm + r * rsm, b);
-      su[w][nb].load(W.up_sm + r * rsm, b);
-      sg[w][nb].mask(bl < nblk);
-      su[w][nb].mask(bl < nblk);
-    }
-  }
-
   // Digits of the item's rows for this lane's blocks (NB x 24 words plus (step, block sum) per row).
   // Without STAGE (verify rounds, at most two rows per item in the usual split) they come from
   // global memory (L2) two rows at a time, both loaded before either is used; with STAGE from LDS.
+  // The first rows' loads are issued before the weight loads: they return sooner and are needed
+  // first, and no wait the compiler places before the row loop (for converted scales) can then
+  // hold them back behind the weights.
   constexpr int SLOTS = MODE == kGuPairs ? 2 : 1;
   uint32_t xd[SLOTS][NB][kXqWords];
   float xstep[SLOTS][NB], xsum[SLOTS][NB];
@@ -314,6 +300,48 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
       xsum[slot][nb] = ss.y;
     }
   };
+  const int np = wk.np;
+  if constexpr (MODE == kGuOneRow) {
+    load_row(0, 0);
+  } else if constexpr (MODE == kGuPairs) {
+    load_row(0, 0);
+    load_row(SLOTS - 1, min(1, np - 1));
+  }
+
+  // This unit's share of its expert's down rows (H split like I over the item's tiles), touched now
+  // so the down kernel's block with the same index finds them in cache (see touch_lines). Issued
+  // before the weight loads, so the wait for the weights covers them; issued in any case (without
+  // prefetching they touch the gate row this block reads anyway).
+  const int pf_tiles = (I + ROWS_B - 1) / ROWS_B;
+  const int pf_r0 = static_cast<int>(static_cast<long>(tile) * H / pf_tiles);
+  const int pf_r1 = static_cast<int>(static_cast<long>(tile + 1) * H / pf_tiles);
+  const bool pf_on = a.prefetch != 0 && pf_r1 > pf_r0;
+  const size_t pf_q = static_cast<size_t>(I) / 2, pf_s = sm_row_words<FMT>(I) * 4;  // bytes per down row
+  const size_t pf_d0 = static_cast<size_t>(wk.e) * H + pf_r0;
+  const Touched<2> pfq = touch_lines<2>(pf_on ? W.down_q + pf_d0 * pf_q : W.gate_q,
+                                        pf_on ? (pf_r1 - pf_r0) * pf_q : 64, tid, kThreads);
+  const Touched<1> pfs = touch_lines<1>(pf_on ? reinterpret_cast<const uint8_t*>(W.down_sm) + pf_d0 * pf_s
+                                              : reinterpret_cast<const uint8_t*>(W.gate_sm),
+                                        pf_on ? (pf_r1 - pf_r0) * pf_s : 64, tid, kThreads);
+
+  __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of the weight loads
+  uint4 cg[RW][NB], cu[RW][NB];
+  BlockScale<FMT> sg[RW][NB], su[RW][NB];
+#pragma unroll
+  for (int w = 0; w < RW; ++w) {
+    const size_t r = static_cast<size_t>(wk.e) * I + min(row0 + w * RPI, I - 1);  // rows past I: not stored
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int bl = g + nb * G, b = min(bl, nblk - 1);
+      cg[w][nb] = load_stream_u4(W.gate_q + r * rq + 16 * b);
+      cu[w][nb] = load_stream_u4(W.up_q + r * rq + 16 * b);
+      sg[w][nb].load(W.gate_sm + r * rsm, b);
+      su[w][nb].load(W.up_sm + r * rsm, b);
+      sg[w][nb].mask(bl < nblk);
+      su[w][nb].mask(bl < nblk);
+    }
+  }
+
   auto stage_row = [&](int slot, int rr) {  // STAGE: row rr of the current chunk, from LDS
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -373,12 +401,12 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
     }
   };
 
-  const int np = wk.np;
   if constexpr (MODE == kGuOneRow) {
-    load_row(0, 0);
     do_row(0, 0);
   } else if constexpr (MODE == kGuPairs) {
-    for (int r0 = 0; r0 < np; r0 += 2) {  // pairs of rows; the usual item is one pair
+    do_row(0, 0);  // the first pair, loaded before the weights (peeled off the loop so that the
+    if (np > 1) do_row(SLOTS - 1, 1);  // compiler keeps those loads where they are)
+    for (int r0 = 2; r0 < np; r0 += 2) {  // further pairs; the usual item is one pair
       load_row(0, r0);
       load_row(SLOTS - 1, min(r0 + 1, np - 1));
       do_row(0, r0);
@@ -398,6 +426,8 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
       }
     }
   }
+  keep_live(pfq);
+  keep_live(pfs);
 }
 
 // Rounds without the residual (and with the atomic combine) start the output rows at zero: the down
@@ -406,7 +436,7 @@ __device__ __forceinline__ void zero_output(const Args& a, int layer) {
   const Ingress in = get_ingress(a);
   float4* o = reinterpret_cast<float4*>(layer_output(a, in, layer));
   const int n4 = a.T * a.H / 4;
-  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n4; i += gridDim.x * kThreads)
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x)
     o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 

@@ -43,6 +43,10 @@ constexpr int kLaunchesPerLayer = 9;  // most launches of one layer (a prefill r
 struct GraphEntry {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  std::vector<hipGraphNode_t> nodes;  // kernel nodes in stream order
+  std::vector<int> node_launch;       // index of each node's launch in `launches`
+  std::vector<struct Launch> launches;
+  unsigned weights_version = 0;       // the handle's weights the nodes' parameters carry
 };
 
 constexpr int kStagingSlots = 16;
@@ -58,7 +62,6 @@ struct moe_round {
   int Gh = 0, NBh = 0, Gi = 0, NBi = 0;
   // device scratch
   Ingress* d_ing = nullptr;            // graph-mode ingress
-  moe_layer_weights* d_wtab = nullptr; // graph-mode weight table [L]
   float* xbuf[2] = {nullptr, nullptr};
   double* logits = nullptr;
   int32_t* n_unique = nullptr;
@@ -79,7 +82,7 @@ struct moe_round {
   bool dev_ing_valid = false;          // d_ing holds h_ing
   std::vector<moe_layer_weights> h_wtab;
   const moe_layer_weights* wts = nullptr;  // the current weights [L] (h_wtab's data, or the caller's)
-  bool dev_wtab_valid = false;         // d_wtab holds h_wtab
+  unsigned weights_version = 1;        // bumped when a run names new weights (graph nodes follow it)
   unsigned char* staging = nullptr;    // pinned ring for graph-mode ingress uploads
   size_t slot_bytes = 0;
   hipEvent_t slot_ev[kStagingSlots] = {};
@@ -190,6 +193,7 @@ static Args base_args(const moe_round* h, int T, int k) {
   a.xstage_h = gateup_stage_rows(h->cfg.hidden);
   a.mfma_rows = h->cfg.exact ? 0 : h->mfma_rows;  // the tile's sums differ in order from the GEMV
   a.xstage_i = xstage_rows(h->cfg.inter);
+  a.prefetch = h->cfg.prefetch;
   return a;
 }
 
@@ -245,18 +249,29 @@ static int layer_launches(const RoundPlan& p, int l, Launch* out) {
   return n;
 }
 
+// The parameters of a launch of layer `layer`: the round's arguments with that layer's weights
+// and the next layer's router (for the down kernel's early touch of it).
+static Args layer_args(const moe_round* h, Args a, int layer) {
+  a.w = h->wts[layer];
+  a.router_next = layer + 1 < h->cfg.n_layers ? h->wts[layer + 1].router_w : nullptr;
+  return a;
+}
+
+// Graph mode: one graph per (T, k) whose kernels read the per-run pointers from the fixed ingress
+// buffer; each node carries its layer's weight pointers as parameters, rewritten in place in the
+// instantiated graph when a run names new weights (no recapture).
 static moe_status build_graph(moe_round* h, int T, int k, GraphEntry* ge) {
   RoundPlan p;
   if (!make_plan(h, T, k, &p)) return MOE_ERR_UNSUPPORTED;
-  Args a = base_args(h, T, k);
-  a.ing = h->d_ing;
-  a.wtab = h->d_wtab;
+  Args base = base_args(h, T, k);
+  base.ing = h->d_ing;
   hipGraph_t g = nullptr;
   MOE_HIP(h, hipGraphCreate(&g, 0));
   hipGraphNode_t prev = nullptr;
   for (int l = 0; l < h->cfg.n_layers; ++l) {
     Launch ls[kMaxLaunchesPerLayer];
     const int n = layer_launches(p, l, ls);
+    Args a = layer_args(h, base, l);
     for (int i = 0; i < n; ++i) {
       const Launch& L = ls[i];
       int layer = L.layer;
@@ -275,6 +290,9 @@ static moe_status build_graph(moe_round* h, int T, int k, GraphEntry* ge) {
         return hip_fail(h, e);
       }
       prev = node;
+      ge->nodes.push_back(node);
+      ge->node_launch.push_back(static_cast<int>(ge->launches.size()));
+      ge->launches.push_back(L);
     }
   }
   hipGraphExec_t x = nullptr;
@@ -285,6 +303,29 @@ static moe_status build_graph(moe_round* h, int T, int k, GraphEntry* ge) {
   }
   ge->graph = g;
   ge->exec = x;
+  ge->weights_version = h->weights_version;
+  return MOE_OK;
+}
+
+// New weights for a captured graph: every node's parameters rewritten in the instantiated graph.
+static moe_status update_graph_weights(moe_round* h, GraphEntry* ge, int T, int k) {
+  Args base = base_args(h, T, k);
+  base.ing = h->d_ing;
+  for (size_t i = 0; i < ge->nodes.size(); ++i) {
+    const Launch& L = ge->launches[ge->node_launch[i]];
+    Args a = layer_args(h, base, L.layer);
+    int layer = L.layer;
+    void* params[] = {&a, &layer};
+    hipKernelNodeParams kp{};
+    kp.func = reinterpret_cast<void*>(L.fn);
+    kp.gridDim = L.grid;
+    kp.blockDim = dim3(L.threads);
+    kp.sharedMemBytes = L.shmem;
+    kp.kernelParams = params;
+    kp.extra = nullptr;
+    MOE_HIP(h, hipGraphExecKernelNodeSetParams(ge->exec, ge->nodes[i], &kp));
+  }
+  ge->weights_version = h->weights_version;
   return MOE_OK;
 }
 
@@ -300,7 +341,7 @@ static moe_status launch_eager(moe_round* h, int T, int k, hipEvent_t* evs, int*
   for (int l = 0; l < h->cfg.n_layers; ++l) {
     Launch ls[kMaxLaunchesPerLayer];
     const int n = layer_launches(p, l, ls);
-    a.w = h->wts[l];
+    a = layer_args(h, a, l);
     for (int j = 0; j < n; ++j, ++i) {
       const Launch& L = ls[j];
       if (kinds) kinds[i] = L.layer * kKernelsPerLayer + L.kind;
@@ -447,24 +488,16 @@ static moe_status launch_prefill(moe_round* h, int T, int k, hipEvent_t* evs, in
   return MOE_OK;
 }
 
-// Graph mode: upload changed ingress pointers and/or the weight table through a pinned slot.
+// Graph mode: upload changed ingress pointers through a pinned slot.
 static moe_status sync_device_ingress(moe_round* h) {
-  const size_t wbytes = sizeof(moe_layer_weights) * h->cfg.n_layers;
-  if (h->dev_ing_valid && h->dev_wtab_valid) return MOE_OK;
+  if (h->dev_ing_valid) return MOE_OK;
   const int s = h->next_slot;
   h->next_slot = (s + 1) % kStagingSlots;
   if (h->slot_used[s]) MOE_HIP(h, hipEventSynchronize(h->slot_ev[s]));
   unsigned char* slot = h->staging + static_cast<size_t>(s) * h->slot_bytes;
-  if (!h->dev_ing_valid) {
-    std::memcpy(slot, &h->h_ing, sizeof(Ingress));
-    MOE_HIP(h, hipMemcpyAsync(h->d_ing, slot, sizeof(Ingress), hipMemcpyHostToDevice, h->stream));
-    h->dev_ing_valid = true;
-  }
-  if (!h->dev_wtab_valid) {
-    std::memcpy(slot + 256, h->h_wtab.data(), wbytes);
-    MOE_HIP(h, hipMemcpyAsync(h->d_wtab, slot + 256, wbytes, hipMemcpyHostToDevice, h->stream));
-    h->dev_wtab_valid = true;
-  }
+  std::memcpy(slot, &h->h_ing, sizeof(Ingress));
+  MOE_HIP(h, hipMemcpyAsync(h->d_ing, slot, sizeof(Ingress), hipMemcpyHostToDevice, h->stream));
+  h->dev_ing_valid = true;
   MOE_HIP(h, hipEventRecord(h->slot_ev[s], h->stream));
   h->slot_used[s] = true;
   return MOE_OK;
@@ -507,7 +540,7 @@ static void free_handle(moe_round* h) {
   for (int i = 0; i < kStagingSlots; ++i)
     if (h->slot_ev[i]) (void)hipEventDestroy(h->slot_ev[i]);
   if (h->staging) (void)hipHostFree(h->staging);
-  void* ptrs[] = {h->d_ing, h->d_wtab, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique, h->uniq, h->offs,
+  void* ptrs[] = {h->d_ing, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique, h->uniq, h->offs,
                   h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->tsel, h->tp, h->xq, h->xss,
                   h->pf_xbuf[0], h->pf_xbuf[1], h->pf_xq, h->pf_xstep, h->pf_mask, h->pf_wpre,
                   h->pf_sel, h->pf_selp, h->pf_uniq, h->pf_offs, h->pf_eoff, h->pf_pairs, h->pf_pair_w, h->pf_slot_of,
@@ -554,7 +587,6 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
 #define MOE_ALLOC(ptr, bytes) \
   if ((e = hipMalloc(reinterpret_cast<void**>(&(ptr)), (bytes))) != hipSuccess) return fail(e);
   MOE_ALLOC(h->d_ing, sizeof(Ingress));
-  MOE_ALLOC(h->d_wtab, sizeof(moe_layer_weights) * L);
   MOE_ALLOC(h->xbuf[0], sizeof(float) * T * H);
   MOE_ALLOC(h->xbuf[1], sizeof(float) * T * H);
   MOE_ALLOC(h->logits, sizeof(double) * cfg->max_rows * E);
@@ -601,7 +633,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
     MOE_ALLOC(h->pf_ybuf, sizeof(float) * P * H);
   }
 #undef MOE_ALLOC
-  h->slot_bytes = 256 + ((sizeof(moe_layer_weights) * L + 255) / 256) * 256;
+  h->slot_bytes = 256;
   if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->staging), h->slot_bytes * kStagingSlots, 0)) !=
       hipSuccess)
     return fail(e);
@@ -625,7 +657,7 @@ static moe_status prepare_run(moe_round* h, const float* hidden, int32_t T, int3
     if (st != MOE_OK) return st;
     if (std::memcmp(layers, h->h_wtab.data(), sizeof(moe_layer_weights) * h->cfg.n_layers) != 0) {
       std::memcpy(h->h_wtab.data(), layers, sizeof(moe_layer_weights) * h->cfg.n_layers);
-      h->dev_wtab_valid = false;
+      ++h->weights_version;
     }
   }
   const Ingress ing{hidden, out, ids, rw};
@@ -668,7 +700,10 @@ extern "C" moe_status moe_round_run(moe_round* h, const float* hidden, int32_t T
       GraphEntry ge;
       st = build_graph(h, T, k, &ge);
       if (st != MOE_OK) return st;
-      it = h->graphs.emplace(key, ge).first;
+      it = h->graphs.emplace(key, std::move(ge)).first;
+    } else if (it->second.weights_version != h->weights_version) {
+      st = update_graph_weights(h, &it->second, T, k);
+      if (st != MOE_OK) return st;
     }
     MOE_HIP(h, hipGraphLaunch(it->second.exec, h->stream));
   } else {

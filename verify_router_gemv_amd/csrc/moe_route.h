@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
     quantize_block_pair(x, a.xq, a.xss, qb, nq, seed);
     return;
   }
-  const moe_layer_weights W = get_weights(a, layer);
+  const moe_layer_weights& W = get_weights(a, layer);
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * TC;
   const int n4 = H / 4;
@@ -172,7 +172,95 @@ __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
   }
 }
 
-// The selection of one round by one block of NT threads: per-row top-k and softmax, the union of
+// The union of a round by the whole block (any number of pairs; s.mask zero, s.sel written).
+template <int NT, typename SS>
+__device__ __forceinline__ void union_block(const Args& a, SS& s, int npairs, int& nu, int& ni) {
+  constexpr int NWMIN = NT / 64;  // fewest waves a caller launches (sizes the per-wave arrays)
+  const int nt = blockDim.x, nw = nt >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T, E = a.E, k = a.k;
+  for (int idx = tid; idx < npairs; idx += nt) atomicOr(&s.mask[s.sel[idx]], 1ull << (idx / k));
+  __syncthreads();
+
+  // The union and its prefix sums, with ballots instead of a shuffle scan. Chunk ch of 64
+  // consecutive experts (ch = q * nw + wave) gives each expert lane its rank among the chunk's
+  // chosen experts, and the sums below it of the row counts and of the work-item counts (an
+  // expert's rows split into items of at most a.rg), bit plane by bit plane: mbcnt of the ballot of
+  // each bit. Chunk totals meet once in LDS for the exclusive prefix over chunks.
+  constexpr int NCH = MOE_ROUND_MAX_EXPERTS / 64;
+  constexpr int CPW = (NCH + NWMIN - 1) / NWMIN;  // chunks per wave (at most)
+  const int rg = a.rg;
+  const int cbits = 32 - __clz(T);                  // bits of a row count (at most T)
+  const int gbits = 32 - __clz((T + rg - 1) / rg);  // bits of an item count
+  int cnt[CPW], ngs[CPW], uin[CPW], cin[CPW], gin[CPW];
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    const int ch = q * nw + wave, e = ch * 64 + lane;
+    const int c = (ch < NCH && e < E) ? __popcll(s.mask[min(e, MOE_ROUND_MAX_EXPERTS - 1)]) : 0;
+    cnt[q] = c;
+    ngs[q] = (c + rg - 1) / rg;
+    const uint64_t chosen = __ballot(c > 0);
+    uin[q] = mbcnt64(chosen);
+    uint64_t tot = static_cast<uint64_t>(__popcll(chosen));
+    int ci = 0, gi = 0;
+    for (int b = 0; b < cbits; ++b) {
+      const uint64_t mb = __ballot((c >> b) & 1);
+      ci += mbcnt64(mb) << b;
+      tot += static_cast<uint64_t>(__popcll(mb)) << (16 + b);
+    }
+    for (int b = 0; b < gbits; ++b) {
+      const uint64_t mb = __ballot((ngs[q] >> b) & 1);
+      gi += mbcnt64(mb) << b;
+      tot += static_cast<uint64_t>(__popcll(mb)) << (32 + b);
+    }
+    cin[q] = ci;
+    gin[q] = gi;
+    if (lane == 0 && ch < NCH) s.ctot[ch] = tot;  // chosen | rows << 16 | items << 32
+  }
+  __syncthreads();
+  uint64_t all = 0, pre[CPW];
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) pre[q] = 0;
+#pragma unroll
+  for (int c2 = 0; c2 < NCH; ++c2) {
+    const uint64_t v = s.ctot[c2];
+    all += v;
+#pragma unroll
+    for (int q = 0; q < CPW; ++q)
+      if (c2 < q * nw + wave) pre[q] += v;
+  }
+  nu = min(static_cast<int>(all & 0xFFFF), a.Ucap);
+  ni = min(static_cast<int>((all >> 32) & 0xFFFF), a.Icap);
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    const int e = (q * nw + wave) * 64 + lane;
+    if (cnt[q] > 0) {
+      const int u = static_cast<int>(pre[q] & 0xFFFF) + uin[q];
+      const int io = static_cast<int>((pre[q] >> 32) & 0xFFFF) + gin[q];
+      s.uidx[e] = u;
+      s.uniq[u] = e;
+      s.offs[u] = static_cast<int>((pre[q] >> 16) & 0xFFFF) + cin[q];
+      s.ioffs[u] = io;
+      for (int g2 = 0; g2 < ngs[q]; ++g2) s.item_u[io + g2] = u;
+    }
+  }
+  if (tid == 0) {
+    s.nu = nu;
+    s.ni = ni;
+    s.offs[nu] = npairs;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < npairs; idx += nt) {
+    const int t = idx / k, j = idx - t * k;
+    const int e = s.sel[idx];
+    const int pos = s.offs[s.uidx[e]] + __popcll(s.mask[e] & ((1ull << t) - 1ull));
+    s.pairs[pos] = t | (j << 8);
+  }
+  __syncthreads();
+}
+
+// The selection of one round by one block (of at least NT threads; the strides use the launched
+// block size): per-row top-k and softmax, the union of
 // the rows' experts, the counting sort of the (row, rank) pairs by expert and the work items (an
 // expert and at most a.rg of its rows). Results stay in `s`; with `publish` the block also writes
 // the per-item records, the unique list, pair table and pair weights, and the caller's ids and
@@ -181,7 +269,7 @@ __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
 // a.tsel / a.tp instead of computed here.
 template <int NPL, int NT, bool ONE_ROW = false, bool PRESEL = false, typename SS>
 __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bool publish) {
-  constexpr int NW = NT / 64;
+  const int nt = blockDim.x, nw = nt >> 6;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k, npairs = T * k;
 
@@ -216,95 +304,17 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
     nu = s.nu;
     ni = s.ni;
   } else {
-    for (int e = tid; e < E; e += NT) s.mask[e] = 0ull;
+    for (int e = tid; e < E; e += nt) s.mask[e] = 0ull;
     if constexpr (PRESEL) {
-      for (int idx = tid; idx < npairs; idx += NT) {
+      for (int idx = tid; idx < npairs; idx += nt) {
         s.sel[idx] = min(max(a.tsel[idx], 0), E - 1);
         s.p[idx] = a.tp[idx];
       }
     } else {
-      for (int t = wave; t < T; t += NW) select_row<NPL>(a, s, t);
+      for (int t = wave; t < T; t += nw) select_row<NPL>(a, s, t);
     }
     __syncthreads();
-
-    for (int idx = tid; idx < npairs; idx += NT) atomicOr(&s.mask[s.sel[idx]], 1ull << (idx / k));
-    __syncthreads();
-
-    // The union and its prefix sums, with ballots instead of a shuffle scan. Chunk ch of 64
-    // consecutive experts (ch = q * NW + wave) gives each expert lane its rank among the chunk's
-    // chosen experts, and the sums below it of the row counts and of the work-item counts (an
-    // expert's rows split into items of at most a.rg), bit plane by bit plane: mbcnt of the ballot of
-    // each bit. Chunk totals meet once in LDS for the exclusive prefix over chunks.
-    constexpr int NCH = MOE_ROUND_MAX_EXPERTS / 64;
-    constexpr int CPW = (NCH + NW - 1) / NW;  // chunks per wave
-    const int rg = a.rg;
-    const int cbits = 32 - __clz(T);                  // bits of a row count (at most T)
-    const int gbits = 32 - __clz((T + rg - 1) / rg);  // bits of an item count
-    int cnt[CPW], ngs[CPW], uin[CPW], cin[CPW], gin[CPW];
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      const int ch = q * NW + wave, e = ch * 64 + lane;
-      const int c = (ch < NCH && e < E) ? __popcll(s.mask[min(e, MOE_ROUND_MAX_EXPERTS - 1)]) : 0;
-      cnt[q] = c;
-      ngs[q] = (c + rg - 1) / rg;
-      const uint64_t chosen = __ballot(c > 0);
-      uin[q] = mbcnt64(chosen);
-      uint64_t tot = static_cast<uint64_t>(__popcll(chosen));
-      int ci = 0, gi = 0;
-      for (int b = 0; b < cbits; ++b) {
-        const uint64_t mb = __ballot((c >> b) & 1);
-        ci += mbcnt64(mb) << b;
-        tot += static_cast<uint64_t>(__popcll(mb)) << (16 + b);
-      }
-      for (int b = 0; b < gbits; ++b) {
-        const uint64_t mb = __ballot((ngs[q] >> b) & 1);
-        gi += mbcnt64(mb) << b;
-        tot += static_cast<uint64_t>(__popcll(mb)) << (32 + b);
-      }
-      cin[q] = ci;
-      gin[q] = gi;
-      if (lane == 0 && ch < NCH) s.ctot[ch] = tot;  // chosen | rows << 16 | items << 32
-    }
-    __syncthreads();
-    uint64_t all = 0, pre[CPW];
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) pre[q] = 0;
-#pragma unroll
-    for (int c2 = 0; c2 < NCH; ++c2) {
-      const uint64_t v = s.ctot[c2];
-      all += v;
-#pragma unroll
-      for (int q = 0; q < CPW; ++q)
-        if (c2 < q * NW + wave) pre[q] += v;
-    }
-    nu = min(static_cast<int>(all & 0xFFFF), a.Ucap);
-    ni = min(static_cast<int>((all >> 32) & 0xFFFF), a.Icap);
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      const int e = (q * NW + wave) * 64 + lane;
-      if (cnt[q] > 0) {
-        const int u = static_cast<int>(pre[q] & 0xFFFF) + uin[q];
-        const int io = static_cast<int>((pre[q] >> 32) & 0xFFFF) + gin[q];
-        s.uidx[e] = u;
-        s.uniq[u] = e;
-        s.offs[u] = static_cast<int>((pre[q] >> 16) & 0xFFFF) + cin[q];
-        s.ioffs[u] = io;
-        for (int g2 = 0; g2 < ngs[q]; ++g2) s.item_u[io + g2] = u;
-      }
-    }
-    if (tid == 0) {
-      s.nu = nu;
-      s.ni = ni;
-      s.offs[nu] = npairs;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < npairs; idx += NT) {
-      const int t = idx / k, j = idx - t * k;
-      const int e = s.sel[idx];
-      const int pos = s.offs[s.uidx[e]] + __popcll(s.mask[e] & ((1ull << t) - 1ull));
-      s.pairs[pos] = t | (j << 8);
-    }
-    __syncthreads();
+    union_block<NT>(a, s, npairs, nu, ni);
   }
   if (!publish) return;
 
@@ -318,7 +328,7 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
   // One thread per item writes its record: the four header words and the row words an item of at
   // most a.rg rows can use (readers never look at rows past np, so the rest are not written).
   const int nrw = (a.rg + 3) / 4;
-  for (int it = tid; it < ni; it += NT) {
+  for (int it = tid; it < ni; it += nt) {
     const int uu = s.item_u[it];
     const int p0 = s.offs[uu] + (it - s.ioffs[uu]) * a.rg;
     const int np = min(a.rg, s.offs[uu + 1] - p0);
@@ -335,10 +345,10 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
       r[kRecRowWord + wd] = v;
     }
   }
-  for (int i = tid; i < nu; i += NT) uniq[i] = s.uniq[i];
-  for (int i = tid; i <= nu; i += NT) offs[i] = s.offs[i];
+  for (int i = tid; i < nu; i += nt) uniq[i] = s.uniq[i];
+  for (int i = tid; i <= nu; i += nt) offs[i] = s.offs[i];
   int32_t* slot_of = a.slot_of + static_cast<size_t>(layer) * a.Pcap;
-  for (int i = tid; i < npairs; i += NT) {
+  for (int i = tid; i < npairs; i += nt) {
     const int pr = s.pairs[i];
     pairs[i] = pr;
     pw[i] = s.p[(pr & 0xFF) * k + (pr >> 8)];
@@ -379,7 +389,8 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Args a, int layer) 
 // one expert and at most a.rg of the rows routed to it (pair slots p0 .. p0 + np - 1).
 struct ExpertWork {
   int e, p0, np, nu;  // nu: number of items of the layer
-  int rows[MOE_ROUND_MAX_ROWS / 4];  // packed row ids, 4 per word
+  int rows[MOE_ROUND_MAX_ROWS / 4];  // packed row ids, 4 per word (from a record)
+  const MOE_LDS int* lrows;  // or, with the selection in LDS: the item's pair entries (t | j << 8) there
 };
 
 __device__ __forceinline__ ExpertWork load_work(const Args& a, int layer, int u) {
@@ -393,6 +404,7 @@ __device__ __forceinline__ ExpertWork load_work(const Args& a, int layer, int u)
 #pragma unroll
   for (int i = 0; i < MOE_ROUND_MAX_ROWS / 4; ++i) w.rows[i] = r[kRecRowWord + i];
   const int npairs = a.T * a.k;
+  w.lrows = nullptr;
   w.nu = min(max(nu, 0), a.Icap);
   w.e = min(max(w.e, 0), a.E - 1);
   w.p0 = min(max(w.p0, 0), npairs);
@@ -400,7 +412,9 @@ __device__ __forceinline__ ExpertWork load_work(const Args& a, int layer, int u)
   return w;
 }
 
-// The work item `it` of a selection held in LDS (see select_block).
+// The work item `it` of a selection held in LDS (see select_block). Only the item's expert and pair
+// range are read here, so the weight loads can be issued before the item's row ids are fetched;
+// work_row reads those from the pair list in LDS when they are used.
 template <typename SS>
 __device__ __forceinline__ ExpertWork work_from_lds(const Args& a, const SS& s, int it) {
   ExpertWork w;
@@ -410,18 +424,14 @@ __device__ __forceinline__ ExpertWork work_from_lds(const Args& a, const SS& s, 
   w.e = s.uniq[uu];
   w.p0 = s.offs[uu] + (it - s.ioffs[uu]) * a.rg;
   w.np = min(a.rg, s.offs[uu + 1] - w.p0);
-#pragma unroll
-  for (int i = 0; i < MOE_ROUND_MAX_ROWS / 4; ++i) {
-    int v = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (4 * i + b < w.np) v |= (s.pairs[w.p0 + 4 * i + b] & 0xFF) << (8 * b);
-    w.rows[i] = v;
-  }
+  // an LDS pointer, not a generic one: a generic load would also count against the vector-memory
+  // counter and so wait for every weight load issued before it
+  w.lrows = (const MOE_LDS int*)(s.pairs + w.p0);
   return w;
 }
 
 __device__ __forceinline__ int work_row(const ExpertWork& w, int r, int T) {
+  if (w.lrows) return min(w.lrows[r] & 0xFF, T - 1);
   // r is wave-uniform; select the packed word without dynamic register indexing
   int word = 0;
 #pragma unroll
