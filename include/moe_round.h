@@ -148,6 +148,11 @@ typedef struct moe_round_config {
                              block with its index (no extra HBM bytes, results unchanged); 0
                              (default): off (measured slower: the touches queue behind the
                              weight loads in each CU's load path)                          */
+  int32_t record_layers;  /* 1: keep every layer's input of decode/verify rounds (L - 1 buffers of
+                             max_rows x H floats instead of two reused ones), readable with
+                             moe_round_layer_input, for checking each layer on its own input
+                             ("How AlphaInfer makes local decoding fast", section 4: a
+                             teacher-forced comparator); 0 (default): no                    */
 } moe_round_config;
 
 #define MOE_WEIGHT_Q4B32 0
@@ -232,6 +237,16 @@ MOE_ROUND_API moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t
  * expert's SwiGLU) and "Design notes" (intermediates are kept comparable with a CPU reference).
  */
 MOE_ROUND_API moe_status moe_round_swiglu_rows(moe_round* h, float* host_rows);
+
+/*
+ * The input rows of layer `layer` in the last decode/verify run, into host float [T][H] (synchronises
+ * the stream): layer 0's is the caller's `hidden`; later layers' need record_layers = 1.  Passage:
+ * "How AlphaInfer makes local decoding fast", section 4 (a teacher-forced comparator checks each
+ * layer on the input the engine actually fed it).  Errors: MOE_ERR_INVALID_ARG (bad handle, layer
+ * or buffer), MOE_ERR_STATE (no last decode/verify run; the layer's input was not kept; or, for
+ * layer 0, `hidden` was `out` and has been overwritten).
+ */
+MOE_ROUND_API moe_status moe_round_layer_input(moe_round* h, int32_t layer, float* host_rows);
 
 /* n_unique of every layer of the last run into host int32 [L] (synchronises the stream).
  * Passage: "How AlphaInfer makes local decoding fast", section 3.1 (an extra verified row costs

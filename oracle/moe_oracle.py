@@ -193,12 +193,14 @@ def _expert_arrays(layer: dict, e: int):
 # One layer, one round
 # ---------------------------------------------------------------------------
 
-def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False):
+def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False, cache=None):
     """One MoE layer over rows X [T, H]; each row is evaluated on its own.
 
     `layer` maps the weight names (router_w, router_b, gate_q, gate_sm, up_q, up_sm, down_q, down_sm)
     to arrays indexable by expert, and optionally "format" to the weight layout ("q4b32" when
-    absent).  Returns (out [T,H] f64, ids [T,k] int64, p [T,k] f64, gaps [T]).
+    absent).  `cache`, if given, is a dict expert id -> that expert's dequantised matrices
+    (expert_matrices) shared across calls on the same layer; missing entries are added.  It only
+    saves repeated dequantisation.  Returns (out [T,H] f64, ids [T,k] int64, p [T,k] f64, gaps [T]).
     """
     fmt = layer.get("format") or "q4b32"
     X = np.asarray(X, dtype=np.float64)
@@ -207,7 +209,8 @@ def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False):
     ids = np.zeros((T, k), dtype=np.int64)
     p = np.zeros((T, k), dtype=np.float64)
     gaps = np.zeros(T, dtype=np.float64)
-    cache = {}
+    if cache is None:
+        cache = {}
     for t in range(T):
         z = router_logits(layer["router_w"], layer.get("router_b"), X[t])
         sel = select_topk(z, k)

@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -42,6 +43,44 @@ def oracle_view(layer: synth.LayerInputs) -> dict:
         "down_q": LazyExperts(layer.down_q, False), "down_sm": LazyExperts(layer.down_sm, True),
         "format": layer.fmt,
     }
+
+
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max_workers=16)
+    return _POOL
+
+
+class DequantCache(dict):
+    """Expert id -> the oracle's dequantised (W_g, W_u, W_d) for one layer view, shared by many
+    rounds; missing experts are dequantised in parallel threads (the oracle's own routine)."""
+
+    def __init__(self, view):
+        super().__init__()
+        self.view = view
+
+    def ensure(self, experts):
+        missing = sorted(set(int(e) for e in experts) - set(self))
+        v = self.view
+        arrays = {e: [v[f][e] for f in ("gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")] for e in missing}
+        futs = {e: _pool().submit(oracle.expert_matrices, *arrays[e], fmt=v.get("format") or "q4b32")
+                for e in missing}
+        for e, f in futs.items():
+            self[e] = f.result()
+        return self
+
+
+def oracle_layer_cached(view, cache: DequantCache, X: np.ndarray, k: int, residual: bool):
+    """oracle.moe_layer with its experts taken from (and added to) a shared cache."""
+    need = set()
+    for t in range(X.shape[0]):
+        need.update(oracle.select_topk(oracle.router_logits(view["router_w"], view["router_b"], X[t]), k).tolist())
+    cache.ensure(need)
+    return oracle.moe_layer(view, X, k, residual=residual, cache=cache)
 
 
 def errors(got: np.ndarray, ref: np.ndarray):
@@ -88,11 +127,20 @@ class GpuRound:
         self.h.close()
 
 
-def check_layer_round(g: GpuRound, views, X: torch.Tensor, k: int, what: str, worklist=True):
-    """Run one round on the GPU and check it against the oracle; returns (rel, mabs, n_unique)."""
+def check_layer_round(g: GpuRound, views, X: torch.Tensor, k: int, what: str, worklist=True, caches=None):
+    """Run one round on the GPU and check it against the oracle; returns (rel, mabs, n_unique).
+    caches: one DequantCache per layer (optional), so repeated rounds dequantise each expert once."""
     out, ids, rw, _ = g.run(X, k)
     Xh = X.cpu().numpy()
-    ref, rids, rp, gaps = oracle.moe_round(views, Xh, k, residual=g.cfg.residual)
+    if caches is None:
+        ref, rids, rp, gaps = oracle.moe_round(views, Xh, k, residual=g.cfg.residual)
+    else:
+        x, rids, rp = Xh.astype(np.float64), [], []
+        for view, cache in zip(views, caches):
+            x, i, p, _ = oracle_layer_cached(view, cache, x, k, g.cfg.residual)
+            rids.append(i)
+            rp.append(p)
+        ref, rids, rp = x, np.stack(rids), np.stack(rp)
     L = len(views)
     for l in range(L):
         assert np.array_equal(ids[l], rids[l]), f"{what}: layer {l} ids differ\nGPU {ids[l]}\nref {rids[l]}"

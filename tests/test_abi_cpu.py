@@ -28,7 +28,7 @@ def declared():
 def test_header_declares_the_boundary():
     names = declared()
     assert "moe_round_init" in names and "moe_round_run" in names and "moe_round_destroy" in names
-    assert len(names) == 15
+    assert len(names) == 16
     assert {"moe_round_last_stats", "moe_round_floor", "moe_round_stream_read"} <= set(names)
 
 
@@ -93,6 +93,7 @@ def test_supported_configs_validate(lib, kw):
     (dict(raw_abi_version=3), -1),
     (dict(raw_prefetch=2), -1),
     (dict(raw_prefetch=-1), -1),
+    (dict(raw_record_layers=2), -1),
     (dict(H=0), -1),
     (dict(I=-32), -1),
     (dict(E=0), -1),
@@ -173,6 +174,7 @@ def test_noalloc_checks_happen_before_any_gpu_call(lib):
 def test_new_entry_points_refuse_null_handles(lib):
     assert lib.moe_round_last_stats(None, None, None, None) == -1
     assert lib.moe_round_floor(None) == -1
+    assert lib.moe_round_layer_input(None, 0, None) == -1
     assert lib.moe_round_stream_read(None, None, 16) == -1
 
 

@@ -65,17 +65,25 @@ def test_exact_stack_row_invariance():
     cfg = synth.config("deep").replace(L=6)
     layers = [synth.make_layer(cfg, seed=0, layer=l, device=DEV) for l in range(cfg.L)]
     g = GpuRound(layers, cfg, max_rows=3, exact=True)
-    X = synth.make_activations(cfg, 3, seed=11, round_idx=0, device=DEV)
-    say("case exact 6-layer stack")
-    out, ids, _, _ = g.run(X)
     views = [oracle_view(l) for l in layers]
-    ref, rids, _, gaps = oracle.moe_round(views, X.cpu().numpy(), cfg.k, residual=True)
-    if gaps.min() >= 1e-5:
-        for l in range(cfg.L):
-            assert np.array_equal(ids[l], rids[l]), f"layer {l}"
-        Xh = X.cpu().numpy()
-        rel = np.linalg.norm((out - Xh) - (ref - Xh)) / np.linalg.norm(ref - Xh)
-        assert rel < 1e-4, rel
+    # the first of the seeded inputs whose 6 selections are all clear of a tie (gap >= 1e-5: there
+    # fp32 rounding upstream cannot flip a selection); the oracle comparison must run on one
+    checked = None
+    for r in range(8):
+        X = synth.make_activations(cfg, 3, seed=11, round_idx=r, device=DEV)
+        ref, rids, _, gaps = oracle.moe_round(views, X.cpu().numpy(), cfg.k, residual=True)
+        if gaps.min() >= 1e-5:
+            checked = r
+            break
+        say(f"  input {r}: selection gap {gaps.min():.2e}, next input")
+    assert checked is not None, "no well-conditioned input among 8"
+    say(f"case exact 6-layer stack (input {checked})")
+    out, ids, _, _ = g.run(X)
+    for l in range(cfg.L):
+        assert np.array_equal(ids[l], rids[l]), f"layer {l}"
+    Xh = X.cpu().numpy()
+    rel = np.linalg.norm((out - Xh) - (ref - Xh)) / np.linalg.norm(ref - Xh)
+    assert rel < 1e-4, rel
     for t in range(3):
         alone = g.run(X[t:t + 1].contiguous())[0]
         assert np.array_equal(alone[0], out[t]), f"row {t}"

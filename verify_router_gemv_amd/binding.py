@@ -40,7 +40,7 @@ class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "hidden", "inter", "n_experts", "top_k_max", "n_layers", "max_rows",
         "residual", "use_graph", "fused_max_rows", "rows_per_item", "mfma_min_rows", "exact",
-        "weight_format", "prefetch")]
+        "weight_format", "prefetch", "record_layers")]
 
 
 class LayerWeights(ctypes.Structure):
@@ -75,6 +75,7 @@ def load() -> ctypes.CDLL:
         "moe_round_worklist": (i32, [vp, i32, P(i32), P(i32), P(i32), P(i32)]),
         "moe_round_last_unique": (i32, [vp, P(i32)]),
         "moe_round_swiglu_rows": (i32, [vp, P(ctypes.c_float)]),
+        "moe_round_layer_input": (i32, [vp, i32, P(ctypes.c_float)]),
         "moe_round_last_stats": (i32, [vp, P(Stats), P(i32), P(ctypes.c_int64)]),
         "moe_round_floor": (i32, [vp]),
         "moe_round_stream_read": (i32, [vp, vp, ctypes.c_int64]),
@@ -110,14 +111,15 @@ def weight_format_code(fmt) -> int:
 
 def make_config(H, I, E, top_k_max, n_layers=1, max_rows=8, residual=False, use_graph=True,
                 fused_max_rows=0, rows_per_item=0, mfma_min_rows=0, exact=False, weight_format=0,
-                prefetch=0) -> Config:
+                prefetch=0, record_layers=False) -> Config:
     """Launch-shape fields: 0 = default (see moe_round.h); -1 = never (fused_max_rows, mfma_min_rows).
     exact: fixed-order combine (bitwise reproducible, row outputs independent of the round).
     weight_format: 0 / "q4b32" (per-32 fp16 scale and minimum) or 1 / "q4s256" (super-blocks).
-    prefetch: 1 = touch the next kernel's weight lines early, 0 = off (default)."""
+    prefetch: 1 = touch the next kernel's weight lines early, 0 = off (default).
+    record_layers: keep every layer's input rows (read back with MoeRound.layer_input)."""
     return Config(ABI_VERSION, H, I, E, top_k_max, n_layers, max_rows, int(bool(residual)), int(bool(use_graph)),
                   fused_max_rows, rows_per_item, mfma_min_rows, int(bool(exact)), weight_format_code(weight_format),
-                  prefetch)
+                  prefetch, int(bool(record_layers)))
 
 
 def validate_config(cfg: Config) -> int:
@@ -219,7 +221,7 @@ class MoeRound:
     def __init__(self, layers: Sequence, H: int, I: int, E: int, top_k_max: int, max_rows: int = 8,
                  residual: bool = False, use_graph: bool = True, stream: Optional[torch.cuda.Stream] = None,
                  fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0, exact: bool = False,
-                 weight_format=None, prefetch: int = 0):
+                 weight_format=None, prefetch: int = 0, record_layers: bool = False):
         """weight_format: None = what the layers declare (default "q4b32"), else 0/1 or its name."""
         self.lib = load()
         self.H, self.I, self.E, self.L = H, I, E, len(layers)
@@ -228,7 +230,8 @@ class MoeRound:
             weight_format = layer_format(layers[0]) or "q4b32"
         self.weight_format = weight_format_code(weight_format)
         self.cfg = make_config(H, I, E, top_k_max, self.L, max_rows, residual, use_graph,
-                               fused_max_rows, rows_per_item, mfma_min_rows, exact, self.weight_format, prefetch)
+                               fused_max_rows, rows_per_item, mfma_min_rows, exact, self.weight_format, prefetch,
+                               record_layers)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._layers = list(layers)          # keep the weight tensors alive
         self._wt = (LayerWeights * self.L)(*[layer_struct(l, H, I, E, self.weight_format) for l in layers])
@@ -322,6 +325,15 @@ class MoeRound:
         st = self.lib.moe_round_swiglu_rows(self.h, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
         if st != OK:
             self._raise(st, "moe_round_swiglu_rows")
+        return buf
+
+    def layer_input(self, layer: int, T: int):
+        """The last run's input rows of `layer` ([T][H] fp32 numpy; later layers need record_layers)."""
+        import numpy as np
+        buf = np.zeros((T, self.H), dtype=np.float32)
+        st = self.lib.moe_round_layer_input(self.h, layer, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+        if st != OK:
+            self._raise(st, "moe_round_layer_input")
         return buf
 
     def last_stats(self):

@@ -63,8 +63,9 @@ struct Args {
   const Ingress* ing;              // graph mode: device ingress; eager mode: null
   Ingress in;                      // eager mode ingress
   moe_layer_weights w;             // this layer's weights (a graph node's parameters in graph mode)
-  float* xbuf0;
-  float* xbuf1;
+  float* xall;        // layer outputs before the last: slot s at xall + s * xstride
+  int32_t xslots;     // 2 (slots reused alternately) or L - 1 (every layer's input kept)
+  int32_t xstride;    // floats per slot (T_max * H)
   double* logits;     // [T_max][E]
   int32_t* n_unique;  // [L]
   int32_t* uniq;      // [L][Ucap]
@@ -96,11 +97,11 @@ __device__ __forceinline__ Ingress get_ingress(const Args& a) { return a.ing ? *
 __device__ __forceinline__ const moe_layer_weights& get_weights(const Args& a, int) { return a.w; }
 __device__ __forceinline__ const float* layer_input(const Args& a, const Ingress& in, int layer) {
   if (layer == 0) return in.hidden;
-  return ((layer - 1) & 1) ? a.xbuf1 : a.xbuf0;
+  return a.xall + static_cast<size_t>((layer - 1) % a.xslots) * a.xstride;
 }
 __device__ __forceinline__ float* layer_output(const Args& a, const Ingress& in, int layer) {
   if (layer == a.L - 1) return in.out;
-  return (layer & 1) ? a.xbuf1 : a.xbuf0;
+  return a.xall + static_cast<size_t>(layer % a.xslots) * a.xstride;
 }
 
 // ------------------------------------------------------------------------------------------

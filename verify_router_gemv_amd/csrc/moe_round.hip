@@ -62,7 +62,9 @@ struct moe_round {
   int Gh = 0, NBh = 0, Gi = 0, NBi = 0;
   // device scratch
   Ingress* d_ing = nullptr;            // graph-mode ingress
-  float* xbuf[2] = {nullptr, nullptr};
+  float* xall = nullptr;               // layer outputs before the last (xslots slots of xstride floats)
+  int xslots = 2;
+  int xstride = 0;
   double* logits = nullptr;
   int32_t* n_unique = nullptr;
   int32_t* uniq = nullptr;
@@ -162,8 +164,9 @@ static int items_bound(int pairs, int E, int rg) {
 
 static Args base_args(const moe_round* h, int T, int k) {
   Args a{};
-  a.xbuf0 = h->xbuf[0];
-  a.xbuf1 = h->xbuf[1];
+  a.xall = h->xall;
+  a.xslots = h->xslots;
+  a.xstride = h->xstride;
   a.logits = h->logits;
   a.n_unique = h->n_unique;
   a.uniq = h->uniq;
@@ -540,7 +543,7 @@ static void free_handle(moe_round* h) {
   for (int i = 0; i < kStagingSlots; ++i)
     if (h->slot_ev[i]) (void)hipEventDestroy(h->slot_ev[i]);
   if (h->staging) (void)hipHostFree(h->staging);
-  void* ptrs[] = {h->d_ing, h->xbuf[0], h->xbuf[1], h->logits, h->n_unique, h->uniq, h->offs,
+  void* ptrs[] = {h->d_ing, h->xall, h->logits, h->n_unique, h->uniq, h->offs,
                   h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->tsel, h->tp, h->xq, h->xss,
                   h->pf_xbuf[0], h->pf_xbuf[1], h->pf_xq, h->pf_xstep, h->pf_mask, h->pf_wpre,
                   h->pf_sel, h->pf_selp, h->pf_uniq, h->pf_offs, h->pf_eoff, h->pf_pairs, h->pf_pair_w, h->pf_slot_of,
@@ -587,8 +590,9 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
 #define MOE_ALLOC(ptr, bytes) \
   if ((e = hipMalloc(reinterpret_cast<void**>(&(ptr)), (bytes))) != hipSuccess) return fail(e);
   MOE_ALLOC(h->d_ing, sizeof(Ingress));
-  MOE_ALLOC(h->xbuf[0], sizeof(float) * T * H);
-  MOE_ALLOC(h->xbuf[1], sizeof(float) * T * H);
+  h->xslots = (cfg->record_layers && L > 2) ? L - 1 : 2;
+  h->xstride = T * H;
+  MOE_ALLOC(h->xall, sizeof(float) * h->xslots * T * H);
   MOE_ALLOC(h->logits, sizeof(double) * cfg->max_rows * E);
   MOE_ALLOC(h->n_unique, sizeof(int32_t) * L);
   MOE_ALLOC(h->uniq, sizeof(int32_t) * L * h->Ucap);
@@ -799,6 +803,19 @@ extern "C" moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t* n
   return MOE_OK;
 }
 
+extern "C" moe_status moe_round_layer_input(moe_round* h, int32_t layer, float* host_rows) {
+  if (!h || !host_rows) return MOE_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= h->cfg.n_layers) return MOE_ERR_INVALID_ARG;
+  if (h->last_T == 0 || h->last_T > MOE_ROUND_MAX_ROWS) return MOE_ERR_STATE;
+  if (layer > 0 && h->xslots < h->cfg.n_layers - 1) return MOE_ERR_STATE;  // not recorded
+  MOE_HIP(h, hipStreamSynchronize(h->stream));
+  const size_t n = static_cast<size_t>(h->last_T) * h->cfg.hidden;
+  const float* src = layer == 0 ? h->h_ing.hidden : h->xall + static_cast<size_t>(layer - 1) * h->xstride;
+  if (layer == 0 && h->h_ing.hidden == h->h_ing.out) return MOE_ERR_STATE;  // overwritten by the round
+  MOE_HIP(h, hipMemcpy(host_rows, src, sizeof(float) * n, hipMemcpyDeviceToHost));
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_round_swiglu_rows(moe_round* h, float* host_rows) {
   if (!h || !host_rows) return MOE_ERR_INVALID_ARG;
   if (h->last_T == 0) return MOE_ERR_STATE;
@@ -960,8 +977,9 @@ static size_t noalloc_layout(moe_round* h, int T, unsigned char* base) {
     return q;
   };
   const size_t P = h->Pcap, U = h->Ucap, It = h->Icap;
-  h->xbuf[0] = reinterpret_cast<float*>(L > 1 ? take(sizeof(float) * T * H) : nullptr);
-  h->xbuf[1] = reinterpret_cast<float*>(L > 1 ? take(sizeof(float) * T * H) : nullptr);
+  h->xslots = (c.record_layers && L > 2) ? static_cast<int>(L) - 1 : 2;
+  h->xstride = static_cast<int>(T * H);
+  h->xall = reinterpret_cast<float*>(L > 1 ? take(sizeof(float) * h->xslots * T * H) : nullptr);
   h->logits = reinterpret_cast<double*>(take(sizeof(double) * T * E));
   h->n_unique = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * L));
   h->uniq = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * L * U));

@@ -51,6 +51,7 @@ moe_status validate_config(const moe_round_config* c) {
   if (c->exact != 0 && c->exact != 1) return MOE_ERR_INVALID_ARG;
   if (c->weight_format != MOE_WEIGHT_Q4B32 && c->weight_format != MOE_WEIGHT_Q4S256) return MOE_ERR_INVALID_ARG;
   if (c->prefetch != 0 && c->prefetch != 1) return MOE_ERR_INVALID_ARG;
+  if (c->record_layers != 0 && c->record_layers != 1) return MOE_ERR_INVALID_ARG;
   if (c->top_k_max > c->n_experts) return MOE_ERR_INVALID_ARG;
   if (c->max_rows > MOE_ROUND_MAX_PREFILL_ROWS) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts > MOE_ROUND_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
