@@ -24,4 +24,5 @@ from .moe_oracle import (  # noqa: F401
     moe_layer,
     moe_round,
     build_worklist,
+    tail_skip_keep,
 )

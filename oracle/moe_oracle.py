@@ -30,7 +30,13 @@ Readings where the pages are silent (each also listed in the design notes):
   * routing weights are the softmax of the k selected logits, nothing else;
   * SiLU is applied to the gate projection; no shared expert, no norm;
   * a multi-layer round adds each layer's MoE output to its input
-    (residual), and a single-layer round returns the MoE output alone.
+    (residual), and a single-layer round returns the MoE output alone;
+  * tail skip (Avalon README, results section): an expert is "missed" when it
+    is not resident in GPU memory; ranks are the 1-based positions of the
+    descending top-k; a missed expert is skipped for the whole round when
+    every row that selected it ranks it at the skip rank or below (rank >=
+    skip_rank), so its (row, rank) pairs add nothing; the other pairs keep
+    their routing weights (no renormalisation: the page names none).
 
 Parity pins (tests/test_oracle_pins.py): every function below is pinned by a
 check independent of its own formula (hand-written golden blocks, closed
@@ -193,9 +199,38 @@ def _expert_arrays(layer: dict, e: int):
 # One layer, one round
 # ---------------------------------------------------------------------------
 
-def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False, cache=None):
-    """One MoE layer over rows X [T, H]; each row is evaluated on its own.
+def tail_skip_keep(ids: np.ndarray, resident, skip_rank: int) -> np.ndarray:
+    """Which (row, rank) pairs of one round survive the tail skip (Avalon README, results section).
 
+    ids [T, k] are the rows' selections, rank j + 1 at column j; resident[e] says whether expert e
+    is resident (missed when False).  A missed expert that every row selecting it ranks at
+    skip_rank or below (1-based rank >= skip_rank) is skipped: keep[t, j] is False for each of its
+    pairs.  skip_rank <= 0 or resident None: nothing is skipped.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    keep = np.ones(ids.shape, dtype=bool)
+    if skip_rank <= 0 or resident is None:
+        return keep
+    T, k = ids.shape
+    best = {}  # expert -> its smallest 1-based rank over the round's rows
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            best[e] = min(best.get(e, j + 1), j + 1)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if not bool(resident[e]) and best[e] >= skip_rank:
+                keep[t, j] = False
+    return keep
+
+
+def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False, cache=None,
+              resident=None, skip_rank: int = 0):
+    """One MoE layer over rows X [T, H].
+
+    Each row's selection and routing weights are its own; only the tail skip (resident, skip_rank:
+    see tail_skip_keep) looks across the round's rows, to decide which experts are skipped.
     `layer` maps the weight names (router_w, router_b, gate_q, gate_sm, up_q, up_sm, down_q, down_sm)
     to arrays indexable by expert, and optionally "format" to the weight layout ("q4b32" when
     absent).  `cache`, if given, is a dict expert id -> that expert's dequantised matrices
@@ -213,24 +248,27 @@ def moe_layer(layer: dict, X: np.ndarray, k: int, residual: bool = False, cache=
         cache = {}
     for t in range(T):
         z = router_logits(layer["router_w"], layer.get("router_b"), X[t])
-        sel = select_topk(z, k)
-        w = routing_weights(z, sel)
+        ids[t] = select_topk(z, k)
+        p[t] = routing_weights(z, ids[t])
         gaps[t] = selection_gap(z, k)
+    keep = tail_skip_keep(ids, resident, skip_rank)
+    for t in range(T):
         acc = np.zeros(H, dtype=np.float64)
         for j in range(k):
-            e = int(sel[j])
+            if not keep[t, j]:
+                continue
+            e = int(ids[t, j])
             if e not in cache:
                 cache[e] = expert_matrices(*_expert_arrays(layer, e), fmt=fmt)
-            acc = acc + w[j] * swiglu_ffn(*cache[e], X[t])
+            acc = acc + p[t, j] * swiglu_ffn(*cache[e], X[t])
         out[t] = X[t] + acc if residual else acc
-        ids[t] = sel
-        p[t] = w
     return out, ids, p, gaps
 
 
-def moe_round(layers, X: np.ndarray, k: int, residual: bool):
+def moe_round(layers, X: np.ndarray, k: int, residual: bool, resident=None, skip_rank: int = 0):
     """A round over L layers: X^{l+1} = X^l + MoE_l(X^l) with residual, else a single MoE layer.
 
+    resident: None, or per layer a boolean [E] (the tail skip's residency; see tail_skip_keep).
     Returns (out [T,H] f64, ids [L,T,k], p [L,T,k], gaps [L,T]).
     """
     layers = list(layers)
@@ -238,8 +276,9 @@ def moe_round(layers, X: np.ndarray, k: int, residual: bool):
         raise ValueError("a round without residual has exactly one layer")
     x = np.asarray(X, dtype=np.float64)
     all_ids, all_p, all_gaps = [], [], []
-    for layer in layers:
-        x, ids, p, gaps = moe_layer(layer, x, k, residual)
+    for l, layer in enumerate(layers):
+        res = None if resident is None else resident[l]
+        x, ids, p, gaps = moe_layer(layer, x, k, residual, resident=res, skip_rank=skip_rank)
         all_ids.append(ids)
         all_p.append(p)
         all_gaps.append(gaps)
@@ -250,30 +289,37 @@ def moe_round(layers, X: np.ndarray, k: int, residual: bool):
 # Worklist: counting sort of (row, rank) pairs by expert
 # ---------------------------------------------------------------------------
 
-def build_worklist(ids: np.ndarray):
+def build_worklist(ids: np.ndarray, keep=None):
     """Group the T*k (row t, rank j) pairs by expert.
 
+    keep: None, or a boolean [T, k] (tail_skip_keep); pairs with keep False are left out, and an
+    expert none of whose pairs is kept is not in the union.
     Returns (uniq, offs, pairs):
-      uniq  : the union of the rows' selected experts, ascending;
-      offs  : exclusive prefix sum of how many rows chose each unique expert (len n_unique + 1);
-      pairs : [T*k, 2] (t, j), grouped by expert in uniq order, t ascending within an expert.
+      uniq  : the union of the rows' selected experts (of kept pairs), ascending;
+      offs  : exclusive prefix sum of how many kept pairs each unique expert has (len n_unique + 1);
+      pairs : [n_kept, 2] (t, j), grouped by expert in uniq order, t ascending within an expert.
     """
     ids = np.asarray(ids, dtype=np.int64)
     T, k = ids.shape
+    if keep is None:
+        keep = np.ones((T, k), dtype=bool)
     E = int(ids.max()) + 1 if ids.size else 0
     count = np.zeros(E, dtype=np.int64)
     for t in range(T):
         for j in range(k):
-            count[ids[t, j]] += 1
+            if keep[t, j]:
+                count[ids[t, j]] += 1
     uniq = np.array([e for e in range(E) if count[e] > 0], dtype=np.int64)
     offs = np.zeros(len(uniq) + 1, dtype=np.int64)
     for u, e in enumerate(uniq):
         offs[u + 1] = offs[u] + count[e]
-    pairs = np.zeros((T * k, 2), dtype=np.int64)
+    pairs = np.zeros((int(offs[-1]), 2), dtype=np.int64)
     fill = offs[:-1].copy()
     pos = {int(e): u for u, e in enumerate(uniq)}
     for t in range(T):
         for j in range(k):
+            if not keep[t, j]:
+                continue
             u = pos[int(ids[t, j])]
             pairs[fill[u]] = (t, j)
             fill[u] += 1

@@ -16,5 +16,6 @@ from .inputs import (  # noqa: F401
     quantize_q4s256,
     make_layer,
     make_activations,
+    make_residency,
     derive_seed,
 )

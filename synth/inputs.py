@@ -235,7 +235,7 @@ class LayerInputs:
 
 
 _EXPERT_CHUNK = 16
-_STREAM_ROUTER, _STREAM_BIAS, _STREAM_GATE, _STREAM_UP, _STREAM_DOWN = range(5)
+_STREAM_ROUTER, _STREAM_BIAS, _STREAM_GATE, _STREAM_UP, _STREAM_DOWN, _STREAM_RESIDENT = range(6)
 
 
 def _expert_matrix(cfg: ShapeConfig, seed: int, layer: int, stream: int, rows: int, K: int,
@@ -289,6 +289,25 @@ def make_activations(cfg: ShapeConfig, T: int, seed: int = 0, round_idx: int = 0
         noise = torch.randn((T, cfg.H), generator=g, device=device, dtype=torch.float32)
         return (base + 0.5 * noise).contiguous()
     return torch.randn((T, cfg.H), generator=g, device=device, dtype=torch.float32)
+
+
+def make_residency(cfg: ShapeConfig, frac: float, seed: int = 0, layer: int = 0) -> np.ndarray:
+    """Which experts of a layer sit in GPU memory (bool [E]): round(frac * E) of them.
+
+    With a Zipf router bias they are the most popular experts (the bias's rank permutation, as a
+    cache filled with the hottest experts of a ranking: Avalon README, hardware section); without
+    one, a seeded random subset.  The rest are "missed" experts, kept in host memory.
+    """
+    E = cfg.E
+    n = int(round(frac * E))
+    if cfg.zipf_s is not None:
+        gp = _gen("cpu", seed, 0, layer, _STREAM_BIAS)
+        rank = torch.randperm(E, generator=gp).numpy() + 1   # the same draw as make_layer's bias
+        return rank <= n
+    g = _gen("cpu", seed, 0, layer, _STREAM_RESIDENT)
+    res = np.zeros(E, dtype=bool)
+    res[torch.randperm(E, generator=g)[:n].numpy()] = True
+    return res
 
 
 def metric_bytes(cfg: ShapeConfig, n_unique: int, T: int) -> int:

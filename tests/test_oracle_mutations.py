@@ -139,11 +139,47 @@ def _round_no_residual(layers, X, k, residual):
             np.stack([o[2] for o in outs]))
 
 
+def _skip_ignores_residency(ids, resident, skip_rank):
+    return ORIG["tail_skip_keep"](ids, None if resident is None else np.zeros(len(resident), bool), skip_rank)
+
+
+def _skip_rank_off_by_one(ids, resident, skip_rank):
+    return ORIG["tail_skip_keep"](ids, resident, skip_rank + 1 if skip_rank > 0 else skip_rank)
+
+
+def _skip_per_pair(ids, resident, skip_rank):
+    ids = np.asarray(ids)
+    keep = np.ones(ids.shape, dtype=bool)
+    if skip_rank <= 0 or resident is None:
+        return keep
+    for (t, j), e in np.ndenumerate(ids):
+        keep[t, j] = bool(resident[e]) or j + 1 < skip_rank
+    return keep
+
+
+def _layer_renormalised_after_skip(layer, X, k, residual=False, cache=None, resident=None, skip_rank=0):
+    out, ids, p, gaps = ORIG["moe_layer"](layer, X, k, residual, cache, resident, skip_rank)
+    keep = ORIG["tail_skip_keep"](ids, resident, skip_rank)
+    if keep.all():
+        return out, ids, p, gaps
+    X = np.asarray(X, dtype=np.float64)
+    out2 = X.copy() if residual else np.zeros_like(out)
+    for t in range(X.shape[0]):
+        tot = p[t][keep[t]].sum()
+        for j in range(k):
+            if keep[t, j]:
+                e = int(ids[t, j])
+                out2[t] += p[t, j] / tot * om.expert_forward(
+                    layer["gate_q"][e], layer["gate_sm"][e], layer["up_q"][e], layer["up_sm"][e],
+                    layer["down_q"][e], layer["down_sm"][e], X[t])
+    return out2, ids, p, gaps
+
+
 ORIG = {name: getattr(om, name) for name in
         ("unpack_codes", "unpack_scale_min", "dequantize", "unpack_superblocks", "dequantize_q4s256",
          "router_logits", "select_topk",
          "routing_weights", "silu", "swiglu_ffn", "expert_forward", "moe_layer", "moe_round",
-         "build_worklist")}
+         "build_worklist", "tail_skip_keep")}
 
 MUTATIONS = {
     "swapped nibbles": ("unpack_codes", _swap_nibbles),
@@ -166,6 +202,10 @@ MUTATIONS = {
     "unweighted combine": ("moe_layer", _layer_unweighted),
     "rows descending in worklist": ("build_worklist", _worklist_rows_descending),
     "residual dropped": ("moe_round", _round_no_residual),
+    "tail skip ignores residency": ("tail_skip_keep", _skip_ignores_residency),
+    "tail skip rank off by one": ("tail_skip_keep", _skip_rank_off_by_one),
+    "tail skip decided per pair": ("tail_skip_keep", _skip_per_pair),
+    "weights renormalised after the skip": ("moe_layer", _layer_renormalised_after_skip),
 }
 
 

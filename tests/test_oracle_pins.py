@@ -413,3 +413,129 @@ def test_worklist_invariants(T, k, E):
         seg = pairs[offs[u]:offs[u + 1]]
         assert all(ids[t, j] == e for t, j in seg)
         assert np.all(np.diff(seg[:, 0]) > 0)           # rows ascending within an expert
+
+
+# ---------------------------------------------------------------------------
+# tail skip (Avalon README, results section)
+# ---------------------------------------------------------------------------
+
+def golden_tail_skip():
+    parse = lambda toks: [[int(v) for v in grp.split()] for grp in " ".join(toks).split("/") if grp.strip()]
+    head, cases, cur = {}, [], None
+    for key, toks in read_golden("tail_skip.txt"):
+        if key == "ids":
+            head["ids"] = np.array(parse(toks))
+        elif key == "resident":
+            head["resident"] = [int(v) for v in toks]
+        elif key == "case":
+            cur = {"rank": int(toks[0])}
+            cases.append(cur)
+        elif key in ("skipped", "uniq", "offs"):
+            cur[key] = [int(v) for v in toks]
+        elif key in ("dropped", "pairs"):
+            cur[key] = parse(toks)
+    return head, cases
+
+
+def test_tail_skip_golden():
+    head, cases = golden_tail_skip()
+    ids = head["ids"]
+    E = 16
+    resident = np.zeros(E, dtype=bool)
+    resident[head["resident"]] = True
+    assert [c["rank"] for c in cases] == [7, 6, 1, 9]
+    for c in cases:
+        keep = oracle.tail_skip_keep(ids, resident, c["rank"])
+        skipped = sorted(set(ids[~keep].tolist()))
+        assert skipped == c["skipped"], c["rank"]
+        # a skipped expert loses every pair, a kept one none
+        assert not set(ids[keep].tolist()) & set(skipped)
+        if "dropped" in c:
+            assert sorted(map(list, np.argwhere(~keep).tolist())) == sorted(c["dropped"])
+        if "uniq" in c:
+            uniq, offs, pairs = oracle.build_worklist(ids, keep)
+            assert uniq.tolist() == c["uniq"]
+            assert offs.tolist() == c["offs"]
+            assert pairs.tolist() == c["pairs"]
+
+
+def test_tail_skip_off_cases_keep_everything():
+    rng = np.random.default_rng(5)
+    ids = np.stack([rng.choice(64, size=8, replace=False) for _ in range(4)])
+    missed = np.zeros(64, dtype=bool)
+    for rank in (0, -1, 9, 100):  # off, or past k
+        assert oracle.tail_skip_keep(ids, missed, rank).all()
+    assert oracle.tail_skip_keep(ids, None, 7).all()
+    assert oracle.tail_skip_keep(ids, np.ones(64, dtype=bool), 1).all()  # nothing missed
+    assert oracle.build_worklist(ids, np.ones(ids.shape, dtype=bool))[1][-1] == ids.size
+
+
+def test_tail_skip_brute_force_over_subsets():
+    """Per expert, straight from the rule's wording: skipped iff missed and no selecting row ranks
+    it above skip_rank; checked on random rounds against the expert-by-expert evaluation."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        T, k, E = int(rng.integers(1, 6)), int(rng.integers(1, 9)), 12
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+        resident = rng.random(E) < 0.4
+        r = int(rng.integers(1, k + 2))
+        keep = oracle.tail_skip_keep(ids, resident, r)
+        for e in range(E):
+            rows = [(t, j) for t in range(T) for j in range(k) if ids[t, j] == e]
+            if not rows:
+                continue
+            skipped = (not resident[e]) and all(j + 1 >= r for _, j in rows)
+            assert all(keep[t, j] == (not skipped) for t, j in rows)
+
+
+def test_tail_skip_layer_drops_exactly_the_skipped_terms():
+    """out(skip) + sum over dropped pairs of p * expert(x) == out(no skip), routing weights and ids
+    unchanged (no renormalisation)."""
+    layer = small_layer(E=12, H=64, I=32, seed=7)
+    X = np.random.default_rng(3).standard_normal((4, 64))
+    k = 6
+    resident = np.zeros(12, dtype=bool)
+    resident[[0, 4, 8]] = True
+    full, ids, p, _ = oracle.moe_layer(layer, X, k)
+    for r in (1, 3, 5, 6):
+        out, ids2, p2, _ = oracle.moe_layer(layer, X, k, resident=resident, skip_rank=r)
+        assert np.array_equal(ids2, ids) and np.array_equal(p2, p)
+        keep = oracle.tail_skip_keep(ids, resident, r)
+        back = out.copy()
+        for t, j in np.argwhere(~keep):
+            e = int(ids[t, j])
+            w = [layer[n][e] for n in ("gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")]
+            back[t] += p[t, j] * oracle.expert_forward(*w, X[t])
+        np.testing.assert_allclose(back, full, rtol=1e-12, atol=1e-12)
+    # skip_rank 1: only resident experts contribute, each row on its own ranks
+    out1, _, _, _ = oracle.moe_layer(layer, X, k, resident=resident, skip_rank=1)
+    for t in range(4):
+        acc = np.zeros(64)
+        for j in range(k):
+            e = int(ids[t, j])
+            if resident[e]:
+                w = [layer[n][e] for n in ("gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")]
+                acc += p[t, j] * oracle.expert_forward(*w, X[t])
+        np.testing.assert_allclose(out1[t], acc, rtol=1e-12, atol=1e-14)
+
+
+def test_tail_skip_depends_on_the_round():
+    """A missed expert at rank 7 of one row is skipped alone, and kept once another row of the
+    same round ranks it higher."""
+    resident = np.zeros(16, dtype=bool)
+    a = np.array([[0, 1, 2, 3, 4, 5, 6, 7]])
+    b = np.array([[6, 8, 9, 10, 11, 12, 13, 14]])
+    assert not oracle.tail_skip_keep(a, resident, 7)[0, 6]
+    both = oracle.tail_skip_keep(np.concatenate([a, b]), resident, 7)
+    assert both[0, 6] and both[1, 0]
+
+
+def test_residency_generator_keeps_the_hottest_experts():
+    """With a Zipf router bias the resident experts are those with the largest bias."""
+    cfg = synth.config("deep").replace(H=256, I=32)
+    res = synth.make_residency(cfg, 0.25, seed=0, layer=2)
+    assert res.sum() == cfg.E // 4
+    b = synth.make_layer(cfg, seed=0, layer=2).router_b.numpy()
+    assert b[res].min() >= b[~res].max()
+    plain = synth.make_residency(synth.config("verify"), 0.5, seed=1)
+    assert plain.sum() == 128
