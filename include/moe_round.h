@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MOE_ROUND_ABI_VERSION 2
+#define MOE_ROUND_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define MOE_ROUND_API __attribute__((visibility("default")))
@@ -153,6 +153,26 @@ typedef struct moe_round_config {
                              moe_round_layer_input, for checking each layer on its own input
                              ("How AlphaInfer makes local decoding fast", section 4: a
                              teacher-forced comparator); 0 (default): no                    */
+  int32_t expert_table;   /* 1: every expert's weights are read through a per-(layer, expert) table
+                             of pointers (moe_expert_ref, bound with moe_round_bind_experts), so
+                             each expert may sit at any address: in device memory or in pinned
+                             host memory (hipHostMalloc) that the kernels read in place over the
+                             host link.  The layers' expert pointers must then be NULL (only the
+                             router is taken from them).  Costs one dependent load of the
+                             expert's table entry per kernel that reads its weights.  Rounds of
+                             up to 64 rows only (init refuses it with max_rows > 64).
+                             "How AlphaInfer makes local decoding fast", "Fused-infer: three
+                             memory tiers as one expert store" (decode reads each routed expert
+                             through a table; residency is per-request data).  0 (default): the
+                             layers' contiguous [E][..] arrays                                */
+  int32_t tail_skip_rank; /* r > 0: a round skips each missed expert (its residency bit clear, see
+                             moe_round_bind_experts) that every row selecting it ranks at r or
+                             below (rank = 1-based position in the row's descending top-k); its
+                             (row, rank) pairs add nothing and the other pairs keep their routing
+                             weights (no renormalisation).  An approximation: results differ from
+                             the plain round by the skipped terms.  Avalon README, results section
+                             (rank 7 or lower, on by default there).  0 (default): off.  At most
+                             MOE_ROUND_MAX_TOPK + 1; rounds of up to 64 rows only           */
 } moe_round_config;
 
 #define MOE_WEIGHT_Q4B32 0
@@ -169,6 +189,18 @@ typedef struct moe_layer_weights {
   const uint8_t* down_q;     /* [E][H][I/2]            */
   const uint32_t* down_sm;   /* [E][H][I/32]  (Q4S256: [E][H][I/256][4]) */
 } moe_layer_weights;
+
+/* One expert's weights for the table mode (expert_table = 1): device-readable pointers to its own
+ * matrices, gate and up [I][H] (K = H), down [H][I] (K = I), in the layout above; codes 16-byte
+ * aligned, scales 4-byte (Q4S256: 16-byte).  48 bytes; the table is an array [L][E] of these. */
+typedef struct moe_expert_ref {
+  const uint8_t* gate_q;
+  const uint32_t* gate_sm;
+  const uint8_t* up_q;
+  const uint32_t* up_sm;
+  const uint8_t* down_q;
+  const uint32_t* down_sm;
+} moe_expert_ref;
 
 typedef struct moe_round moe_round; /* opaque handle */
 
@@ -216,14 +248,49 @@ MOE_ROUND_API moe_status moe_round_run(moe_round* h, const float* hidden, int32_
                          float* route_w);
 
 /*
+ * Bind the expert table and the residency bits that later runs read (on the GPU, when each round
+ * executes: the caller may rewrite their contents between rounds, in stream order, without any call
+ * here and without a graph rebuild; binding other arrays updates captured graphs in place).
+ * Passages: "How AlphaInfer makes local decoding fast", "Fused-infer: three memory tiers as one
+ * expert store" (each routed expert is read through a device-resolved table; a non-resident expert
+ * is not copied to the GPU first) and section 2 (per-request data is ingress into fixed buffers);
+ * Avalon README, results section (the tail skip applies to missed experts only).
+ *   table     device moe_expert_ref [L][E], 16-byte aligned: required when cfg.expert_table = 1,
+ *             must be NULL otherwise.  Every entry a round may select must name valid memory the
+ *             GPU can read (device memory, or pinned host memory mapped for the device); entries
+ *             of experts the tail skip leaves out are not read.
+ *   resident  device uint32 [L][ceil(E/32)]: bit e % 32 of word e / 32 of layer l is 1 when expert
+ *             e of layer l is resident (in device memory), 0 when it is missed.  Required when
+ *             cfg.tail_skip_rank > 0, must be NULL otherwise.
+ * Both are caller-owned and borrowed until the handle is destroyed or other arrays are bound.
+ * Errors: MOE_ERR_INVALID_ARG (null handle, misaligned pointer, a pointer the configuration does
+ * not take or a required one missing).  Runs of a handle that needs them before they are bound
+ * return MOE_ERR_STATE.
+ */
+MOE_ROUND_API moe_status moe_round_bind_experts(moe_round* h, const moe_expert_ref* table,
+                                                const uint32_t* resident);
+
+/*
+ * The device address of pinned host memory for an expert table entry (the host tier read in place):
+ * `host_ptr` must lie in memory allocated with hipHostMalloc (mapped for the device); *device_ptr
+ * receives the address kernels use for it.  Passage: "How AlphaInfer makes local decoding fast",
+ * "Fused-infer: three memory tiers as one expert store" (experts stay where they sit in RAM instead
+ * of being copied to the GPU first).  Errors: MOE_ERR_INVALID_ARG (NULL argument, or memory that is
+ * not pinned host memory known to the runtime; *device_ptr is then NULL).
+ */
+MOE_ROUND_API moe_status moe_round_host_tier_pointer(const void* host_ptr, void** device_ptr);
+
+/*
  * Introspection of the last run (synchronises the stream; host outputs).
  * Passage: infero README, "Beyond plain text decode" (the counting sort of (row, expert) pairs into
  * per-expert work); the worklist is that sort's result.
  *   n_unique     number of distinct experts layer `layer` touched
  *   uniq         [n_unique] those experts, ascending                   (may be NULL)
  *   offs         [n_unique + 1] exclusive prefix sum of rows per expert (may be NULL)
- *   pairs        [T*k][2] (row t, rank j) grouped by expert, t ascending (may be NULL)
+ *   pairs        [T*k][2] (row t, rank j) grouped by expert, t ascending (may be NULL); with the
+ *                tail skip the first offs[n_unique] entries are the kept pairs and the rest -1
  * Buffers must hold at least min(T*k, E) (uniq), that + 1 (offs) and 2*T*k (pairs) entries.
+ * Experts the tail skip left out are not in the worklist.
  * This and the calls below return MOE_ERR_STATE when there is no last run to report: none
  * since init, or the last one was an empty round (T = 0).
  */
@@ -258,9 +325,10 @@ typedef struct moe_round_stats {
   int32_t n_layers;       /* L                                                          */
   int32_t rows;           /* T of the last run                                          */
   int32_t top_k;          /* k of the last run                                          */
-  int32_t reserved;       /* 0                                                          */
+  int32_t skipped;        /* experts the tail skip left out, summed over layers (0 off)  */
   int64_t expert_bytes;   /* bytes of one expert's gate, up and down codes and scales    */
-  int64_t metric_bytes;   /* sum over layers of n_unique * expert_bytes + 2 * T * H * 4  */
+  int64_t metric_bytes;   /* sum over layers of n_unique * expert_bytes + 2 * T * H * 4
+                             (n_unique counts the experts read: skipped ones excluded)   */
 } moe_round_stats;
 
 /*
@@ -283,7 +351,8 @@ MOE_ROUND_API moe_status moe_round_last_stats(moe_round* h, moe_round_stats* sta
  * Passage: infero README, "Where the time goes" (a decode-floor program that replays exactly the
  * matrix-vector reads of a step, as the floor a step cannot beat).  Reads the worklist the last run
  * left in device memory, so the weights it names must still be valid.
- * Errors: MOE_ERR_INVALID_ARG (h NULL), MOE_ERR_STATE (no last run), MOE_ERR_HIP (launch).
+ * Errors: MOE_ERR_INVALID_ARG (h NULL), MOE_ERR_STATE (no last run), MOE_ERR_UNSUPPORTED (a handle
+ * with expert_table = 1: its experts have no common base address), MOE_ERR_HIP (launch).
  */
 MOE_ROUND_API moe_status moe_round_floor(moe_round* h);
 
@@ -324,7 +393,8 @@ MOE_ROUND_API moe_status moe_round_profile_read(moe_round* h, double* kernel_ms,
  * cfg and layers, eager, with no handle and no allocation.  Its scratch is a fixed device array of
  * MOE_ROUND_NOALLOC_SCRATCH_BYTES per device, held until the process ends; the library looks up its
  * device address on the first call on each device (that device must be current).
- *   cfg, layers  as for moe_round_init (use_graph is ignored: the launches are eager)
+ *   cfg, layers  as for moe_round_init (use_graph is ignored: the launches are eager; expert_table
+ *                and tail_skip_rank must be 0: there is no handle to bind a table to)
  *   hidden .. route_w, T, k   as for moe_round_run (T <= min(max_rows, 64): no prefill rounds)
  *   stream       the hipStream_t to enqueue on (NULL = the null stream)
  *   hip_error    if not NULL, the hipError_t (as int) behind a MOE_ERR_HIP, else 0

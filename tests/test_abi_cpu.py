@@ -28,7 +28,7 @@ def declared():
 def test_header_declares_the_boundary():
     names = declared()
     assert "moe_round_init" in names and "moe_round_run" in names and "moe_round_destroy" in names
-    assert len(names) == 16
+    assert len(names) == 18
     assert {"moe_round_last_stats", "moe_round_floor", "moe_round_stream_read"} <= set(names)
 
 
@@ -82,6 +82,12 @@ def cfg(**kw):
     dict(H=2048, I=160, E=16, top_k_max=4, max_rows=8),
     dict(H=2304, I=8160, E=8, top_k_max=2, max_rows=4),      # H/32 = 72, I/32 = 255
     dict(H=2048, I=8192, E=8, top_k_max=2, max_rows=4),
+    # the expert table and the tail skip (decode/verify rounds)
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=8, raw_expert_table=1),
+    dict(H=2048, I=512, E=256, top_k_max=8, max_rows=8, raw_tail_skip_rank=7),
+    dict(H=2048, I=512, E=512, top_k_max=10, n_layers=48, max_rows=3, residual=True, raw_expert_table=1,
+         raw_tail_skip_rank=7),
+    dict(H=2048, I=512, E=256, top_k_max=16, max_rows=64, raw_tail_skip_rank=17),   # past k: never skips
 ])
 def test_supported_configs_validate(lib, kw):
     from verify_router_gemv_amd import binding
@@ -90,7 +96,13 @@ def test_supported_configs_validate(lib, kw):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(raw_abi_version=1), -1),     # the configuration struct of ABI 1 lacks `prefetch`
-    (dict(raw_abi_version=3), -1),
+    (dict(raw_abi_version=2), -1),     # ... of ABI 2 lacks `expert_table` and `tail_skip_rank`
+    (dict(raw_abi_version=4), -1),
+    (dict(raw_expert_table=2), -1),
+    (dict(raw_tail_skip_rank=-1), -1),
+    (dict(raw_tail_skip_rank=18), -1),
+    (dict(max_rows=100, raw_expert_table=1), -2),   # prefill rounds read the contiguous arrays
+    (dict(max_rows=100, raw_tail_skip_rank=7), -2),
     (dict(raw_prefetch=2), -1),
     (dict(raw_prefetch=-1), -1),
     (dict(raw_record_layers=2), -1),
@@ -171,6 +183,39 @@ def test_noalloc_checks_happen_before_any_gpu_call(lib):
     assert lib.moe_round_run_noalloc(ctypes.byref(pf), w, 0x200000, 100, 8, 0x4000000, None, None, None, None) == -2
 
 
+def test_table_mode_checks_happen_before_any_gpu_call(lib):
+    """Table mode takes only the routers from the layers; the no-allocation entry point refuses the
+    table and the tail skip (nothing to bind them to); null arguments are refused."""
+    from verify_router_gemv_amd import binding
+    h = ctypes.c_void_p()
+    c = cfg(raw_expert_table=1)
+    full = (binding.LayerWeights * 1)(binding.LayerWeights(*([0x100000] * 8)))
+    assert lib.moe_round_init(ctypes.byref(c), full, None, ctypes.byref(h)) == -1   # expert pointers set
+    router_only = (binding.LayerWeights * 1)(binding.LayerWeights(0x100000, None, *([None] * 6)))
+    assert lib.moe_round_run_noalloc(ctypes.byref(c), router_only, 0x200000, 1, 8, 0x4000000, None, None, None,
+                                     None) == -2
+    skip = cfg(raw_tail_skip_rank=7)
+    assert lib.moe_round_run_noalloc(ctypes.byref(skip), full, 0x200000, 1, 8, 0x4000000, None, None, None,
+                                     None) == -2
+    assert lib.moe_round_run_noalloc(ctypes.byref(c), full, 0x200000, 1, 8, 0x4000000, None, None, None,
+                                     None) == -1
+    assert lib.moe_round_bind_experts(None, 0x100000, None) == -1
+    dev = ctypes.c_void_p()
+    assert lib.moe_round_host_tier_pointer(None, ctypes.byref(dev)) == -1
+    assert lib.moe_round_host_tier_pointer(0x100000, None) == -1
+
+
+def test_residency_words_pack_bit_e_of_word_e_over_32():
+    from verify_router_gemv_amd import binding
+    res = torch.zeros(2, 70, dtype=torch.bool)
+    res[0, [0, 31, 32, 69]] = True
+    res[1, 5] = True
+    w = binding.residency_bits(res.numpy(), device="cpu").view(torch.uint32).to(torch.int64) & 0xFFFFFFFF
+    assert w.shape == (2, 3)
+    assert w[0].tolist() == [1 | (1 << 31), 1, 1 << 5]
+    assert w[1].tolist() == [1 << 5, 0, 0]
+
+
 def test_new_entry_points_refuse_null_handles(lib):
     assert lib.moe_round_last_stats(None, None, None, None) == -1
     assert lib.moe_round_floor(None) == -1
@@ -184,7 +229,7 @@ def test_rejected_layers_keep_the_old_weights_referenced(lib, monkeypatch):
     from verify_router_gemv_amd import binding
     E, H, I = 4, 256, 128
     h = binding.MoeRound.__new__(binding.MoeRound)
-    h.lib, h.h, h.H, h.I, h.E, h.L, h.weight_format = lib, None, H, I, E, 1, 0
+    h.lib, h.h, h.H, h.I, h.E, h.L, h.weight_format, h.expert_table = lib, None, H, I, E, 1, 0, False
     old = [object()]
     h._layers, h._wt = old, "old-array"
     host_layer = dict(router_w=torch.zeros(E, H), router_b=None,

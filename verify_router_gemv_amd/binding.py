@@ -16,7 +16,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_round.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_ROWS = 64
 MAX_PREFILL_ROWS = 16384
 MAX_EXPERTS = 512
@@ -40,7 +40,7 @@ class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "hidden", "inter", "n_experts", "top_k_max", "n_layers", "max_rows",
         "residual", "use_graph", "fused_max_rows", "rows_per_item", "mfma_min_rows", "exact",
-        "weight_format", "prefetch", "record_layers")]
+        "weight_format", "prefetch", "record_layers", "expert_table", "tail_skip_rank")]
 
 
 class LayerWeights(ctypes.Structure):
@@ -48,9 +48,17 @@ class LayerWeights(ctypes.Structure):
         "router_w", "router_bias", "gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")]
 
 
+EXPERT_FIELDS = ("gate_q", "gate_sm", "up_q", "up_sm", "down_q", "down_sm")
+
+
+class ExpertRef(ctypes.Structure):
+    """moe_expert_ref: one expert's six device-readable pointers (48 bytes)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in EXPERT_FIELDS]
+
+
 class Stats(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("rows", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("expert_bytes", ctypes.c_int64), ("metric_bytes", ctypes.c_int64)]
+                ("skipped", ctypes.c_int32), ("expert_bytes", ctypes.c_int64), ("metric_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -80,6 +88,8 @@ def load() -> ctypes.CDLL:
         "moe_round_floor": (i32, [vp]),
         "moe_round_stream_read": (i32, [vp, vp, ctypes.c_int64]),
         "moe_round_run_noalloc": (i32, [P(Config), P(LayerWeights), vp, i32, i32, vp, vp, vp, vp, P(i32)]),
+        "moe_round_bind_experts": (i32, [vp, vp, vp]),
+        "moe_round_host_tier_pointer": (i32, [vp, P(vp)]),
         "moe_round_last_hip_error": (i32, [vp]),
         "moe_round_strerror": (ctypes.c_char_p, [i32]),
         "moe_round_destroy": (None, [vp]),
@@ -111,15 +121,17 @@ def weight_format_code(fmt) -> int:
 
 def make_config(H, I, E, top_k_max, n_layers=1, max_rows=8, residual=False, use_graph=True,
                 fused_max_rows=0, rows_per_item=0, mfma_min_rows=0, exact=False, weight_format=0,
-                prefetch=0, record_layers=False) -> Config:
+                prefetch=0, record_layers=False, expert_table=False, tail_skip_rank=0) -> Config:
     """Launch-shape fields: 0 = default (see moe_round.h); -1 = never (fused_max_rows, mfma_min_rows).
     exact: fixed-order combine (bitwise reproducible, row outputs independent of the round).
     weight_format: 0 / "q4b32" (per-32 fp16 scale and minimum) or 1 / "q4s256" (super-blocks).
     prefetch: 1 = touch the next kernel's weight lines early, 0 = off (default).
-    record_layers: keep every layer's input rows (read back with MoeRound.layer_input)."""
+    record_layers: keep every layer's input rows (read back with MoeRound.layer_input).
+    expert_table: read the experts through a bound per-(layer, expert) pointer table (MoeRound.bind_experts).
+    tail_skip_rank: r > 0 skips missed experts that every row selecting them ranks at r or below."""
     return Config(ABI_VERSION, H, I, E, top_k_max, n_layers, max_rows, int(bool(residual)), int(bool(use_graph)),
                   fused_max_rows, rows_per_item, mfma_min_rows, int(bool(exact)), weight_format_code(weight_format),
-                  prefetch, int(bool(record_layers)))
+                  prefetch, int(bool(record_layers)), int(bool(expert_table)), int(tail_skip_rank))
 
 
 def validate_config(cfg: Config) -> int:
@@ -155,8 +167,10 @@ def layer_format(layer):
     return getattr(layer, "fmt", None)
 
 
-def layer_struct(layer, H: int, I: int, E: int, weight_format=0) -> LayerWeights:
-    """Marshal one layer's weights (object or dict with the eight tensors) into the C struct."""
+def layer_struct(layer, H: int, I: int, E: int, weight_format=0, router_only=False) -> LayerWeights:
+    """Marshal one layer's weights (object or dict with the eight tensors) into the C struct.
+    router_only: the expert table mode, where only the router comes from the layer (the expert
+    pointers are left NULL)."""
     if weight_format_code(weight_format) == 1:
         sm_g, sm_d = (E, I, H // 256, 4), (E, H, I // 256, 4)
     else:
@@ -173,6 +187,9 @@ def layer_struct(layer, H: int, I: int, E: int, weight_format=0) -> LayerWeights
     }
     ptrs = {}
     for f in _FIELDS:
+        if router_only and f in EXPERT_FIELDS:
+            ptrs[f] = None
+            continue
         t = _get(layer, f)
         if t is None and f == "router_bias":
             ptrs[f] = None
@@ -180,6 +197,64 @@ def layer_struct(layer, H: int, I: int, E: int, weight_format=0) -> LayerWeights
         _check(t, f, *spec[f])
         ptrs[f] = t.data_ptr()
     return LayerWeights(*[ptrs[f] for f in _FIELDS])
+
+
+def host_tier_pointer(t: torch.Tensor) -> int:
+    """The device address of pinned host memory (a tensor made with pin_memory=True), checked by the
+    library: raises if the memory is not pinned and mapped for the GPU."""
+    if t.device.type != "cpu" or not t.is_pinned():
+        raise ValueError("a host-tier tensor must be pinned CPU memory")
+    dev = ctypes.c_void_p()
+    st = load().moe_round_host_tier_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(dev))
+    if st != OK:
+        raise MoeRoundError(st, "moe_round_host_tier_pointer")
+    return int(dev.value)
+
+
+def expert_slices(layer, e: int) -> dict:
+    """Expert e's six matrices of a layer (views of its [E][..] tensors)."""
+    return {f: _get(layer, f)[e] for f in EXPERT_FIELDS}
+
+
+def make_expert_table(entries, H: int, I: int, weight_format=0, device="cuda") -> torch.Tensor:
+    """The moe_expert_ref [L][E] table as a device int64 tensor [L, E, 6] from entries[l][e], a dict
+    of the expert's six tensors (device tensors, or pinned host tensors read in place). Shapes and
+    dtypes are checked; the caller keeps the tensors alive while the table is bound."""
+    fmt = weight_format_code(weight_format)
+    sm_g = (I, H // 256, 4) if fmt == 1 else (I, H // 32)
+    sm_d = (H, I // 256, 4) if fmt == 1 else (H, I // 32)
+    spec = {"gate_q": ((torch.uint8,), (I, H // 2)), "gate_sm": ((torch.int32, torch.uint32), sm_g),
+            "up_q": ((torch.uint8,), (I, H // 2)), "up_sm": ((torch.int32, torch.uint32), sm_g),
+            "down_q": ((torch.uint8,), (H, I // 2)), "down_sm": ((torch.int32, torch.uint32), sm_d)}
+    rows = []
+    for layer_entries in entries:
+        lrow = []
+        for ent in layer_entries:
+            ptrs = []
+            for f in EXPERT_FIELDS:
+                t = ent[f]
+                dtypes, shape = spec[f]
+                if t.dtype not in dtypes or tuple(t.shape) != shape or not t.is_contiguous():
+                    raise ValueError(f"{f}: {t.dtype} {tuple(t.shape)} (want {shape}, contiguous)")
+                p = t.data_ptr() if t.device.type == "cuda" else host_tier_pointer(t)
+                if p % 16:
+                    raise ValueError(f"{f} must be 16-byte aligned")
+                ptrs.append(p)
+            lrow.append(ptrs)
+        rows.append(lrow)
+    return torch.tensor(rows, dtype=torch.int64).to(device)
+
+
+def residency_bits(resident, device="cuda") -> torch.Tensor:
+    """Per layer a boolean [E] (True = resident in device memory) packed as the library's residency
+    words: int32 [L][ceil(E/32)], bit e % 32 of word e / 32."""
+    import numpy as np
+    res = np.asarray(resident, dtype=bool)
+    L, E = res.shape
+    words = np.zeros((L, (E + 31) // 32), dtype=np.uint32)
+    for e in range(E):
+        words[:, e // 32] |= res[:, e].astype(np.uint32) << np.uint32(e % 32)
+    return torch.from_numpy(words.view(np.int32)).to(device)
 
 
 def run_noalloc(layers: Sequence, H: int, I: int, E: int, top_k_max: int, hidden: torch.Tensor, k: int,
@@ -221,20 +296,25 @@ class MoeRound:
     def __init__(self, layers: Sequence, H: int, I: int, E: int, top_k_max: int, max_rows: int = 8,
                  residual: bool = False, use_graph: bool = True, stream: Optional[torch.cuda.Stream] = None,
                  fused_max_rows: int = 0, rows_per_item: int = 0, mfma_min_rows: int = 0, exact: bool = False,
-                 weight_format=None, prefetch: int = 0, record_layers: bool = False):
-        """weight_format: None = what the layers declare (default "q4b32"), else 0/1 or its name."""
+                 weight_format=None, prefetch: int = 0, record_layers: bool = False, expert_table: bool = False,
+                 tail_skip_rank: int = 0):
+        """weight_format: None = what the layers declare (default "q4b32"), else 0/1 or its name.
+        expert_table: the layers supply the routers only; bind the experts with bind_experts()."""
         self.lib = load()
         self.H, self.I, self.E, self.L = H, I, E, len(layers)
         self.top_k_max, self.max_rows = top_k_max, max_rows
         if weight_format is None:
             weight_format = layer_format(layers[0]) or "q4b32"
         self.weight_format = weight_format_code(weight_format)
+        self.expert_table = bool(expert_table)
         self.cfg = make_config(H, I, E, top_k_max, self.L, max_rows, residual, use_graph,
                                fused_max_rows, rows_per_item, mfma_min_rows, exact, self.weight_format, prefetch,
-                               record_layers)
+                               record_layers, expert_table, tail_skip_rank)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._layers = list(layers)          # keep the weight tensors alive
-        self._wt = (LayerWeights * self.L)(*[layer_struct(l, H, I, E, self.weight_format) for l in layers])
+        self._wt = (LayerWeights * self.L)(*[layer_struct(l, H, I, E, self.weight_format, self.expert_table)
+                                             for l in layers])
+        self._bound = (None, None)
         h = ctypes.c_void_p()
         st = self.lib.moe_round_init(ctypes.byref(self.cfg), self._wt, ctypes.c_void_p(self.stream.cuda_stream),
                                      ctypes.byref(h))
@@ -250,8 +330,21 @@ class MoeRound:
         """The C array for `layers` (checked), without touching the handle's current weights."""
         if len(layers) != self.L:
             raise ValueError("layer count must not change")
-        return (LayerWeights * self.L)(*[layer_struct(l, self.H, self.I, self.E, self.weight_format)
-                                         for l in layers])
+        return (LayerWeights * self.L)(*[layer_struct(l, self.H, self.I, self.E, self.weight_format,
+                                                      self.expert_table) for l in layers])
+
+    def bind_experts(self, table: Optional[torch.Tensor] = None, resident: Optional[torch.Tensor] = None):
+        """Bind the expert table (device int64 [L, E, 6], make_expert_table) and the residency words
+        (device int32 [L, ceil(E/32)], residency_bits); their contents are read by each later round."""
+        if table is not None:
+            _check(table, "table", (torch.int64,), (self.L, self.E, 6))
+        if resident is not None:
+            _check(resident, "resident", (torch.int32, torch.uint32), (self.L, (self.E + 31) // 32))
+        st = self.lib.moe_round_bind_experts(self.h, ctypes.c_void_p(table.data_ptr() if table is not None else 0),
+                                             ctypes.c_void_p(resident.data_ptr() if resident is not None else 0))
+        if st != OK:
+            self._raise(st, "moe_round_bind_experts")
+        self._bound = (table, resident)
 
     def _run_args(self, hidden, k, out, ids, route_w, wt):
         T = hidden.shape[0]

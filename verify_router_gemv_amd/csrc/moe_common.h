@@ -89,6 +89,10 @@ struct Args {
   int32_t exact;      // fixed-order combine (the logits kernel does not seed the output)
   int32_t prefetch;   // touch the next kernel's weight lines (see touch_lines)
   const float* router_next;  // the next layer's router matrix (null on the last layer)
+  const moe_expert_ref* etab;  // table mode: this layer's [E] expert pointers (null: the w arrays)
+  const uint32_t* resident;    // tail skip: this layer's residency bits [ceil(E/32)] (null: off)
+  int32_t skip_j;              // tail skip: 0-based rank from which a missed expert's pair is a tail pair
+  int32_t* n_skipped;          // [L] experts the tail skip left out
 };
 
 __device__ __forceinline__ Ingress get_ingress(const Args& a) { return a.ing ? *a.ing : a.in; }

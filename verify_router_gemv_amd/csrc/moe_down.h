@@ -94,12 +94,12 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
 
   // The next layer's router row of the logits block with this block's index, touched (see
   // touch_lines) after the record (whose wait must not include it) and before the weights (whose
-  // wait covers it); issued in any case (without a next layer: the first line of this layer's codes).
+  // wait covers it); issued in any case (without prefetching: the first line of the item's SwiGLU rows).
   const float* rnext = a.router_next;
-  const moe_layer_weights& W = get_weights(a, layer);
+  const ExpertPtrs W = expert_ptrs<FMT>(a, wk.e);
   const bool pf_on = a.prefetch != 0 && rnext != nullptr && static_cast<int>(blockIdx.x) < a.E;
   const Touched<1> pfr = touch_lines<1>(pf_on ? static_cast<const void*>(rnext + static_cast<size_t>(blockIdx.x) * H)
-                                              : static_cast<const void*>(W.down_q),
+                                              : static_cast<const void*>(a.hbuf + static_cast<size_t>(wk.p0) * I),
                                         pf_on ? static_cast<size_t>(H) * 4 : 64, threadIdx.x, kThreads);
 
   // The first chunk's SwiGLU values, loaded before the weights (they return sooner and are needed
@@ -113,12 +113,12 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   BlockScale<FMT> sd[RW][NB];
 #pragma unroll
   for (int w = 0; w < RW; ++w) {
-    const size_t r = static_cast<size_t>(wk.e) * H + min(row0 + w * RPI, H - 1);  // rows past H: not stored
+    const size_t r = min(row0 + w * RPI, H - 1);  // rows past H: not stored
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int bl = g + nb * G, b = min(bl, nblk - 1);
-      cd[w][nb] = load_stream_u4(W.down_q + r * rq + 16 * b);
-      sd[w][nb].load(W.down_sm + r * rsm, b);
+      cd[w][nb] = load_stream_u4(W.dq + r * rq + 16 * b);
+      sd[w][nb].load(W.ds + r * rsm, b);
       sd[w][nb].mask(bl < nblk);
     }
   }
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
 }
 
 // Exact mode: out[t][h] = (residual ? x[t][h] : 0) + sum over ranks j = 0..k-1, in that order, of
-// p[t][j] * y[slot(t, j)][h]. Grid (T, ceil(H / 1024)) x 256 threads, four columns per thread.
+// p[t][j] * y[slot(t, j)][h] (ranks whose pair the tail skip left out add nothing). Grid (T, ceil(H / 1024)) x 256 threads, four columns per thread.
 static __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int layer) {
   const Ingress in = get_ingress(a);
   const float* x = layer_input(a, in, layer);  // may be xn itself (the caller's hidden == out)
@@ -201,7 +201,8 @@ static __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int la
   const float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
   float4 acc = a.residual ? load_f4(x + static_cast<size_t>(t) * H + h) : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
-    const int s = min(max(slot_of[j], 0), a.Pcap - 1);
+    if (slot_of[j] < 0) continue;  // a pair the tail skip left out
+    const int s = min(slot_of[j], a.Pcap - 1);
     const float w = pw[s];
     const float4 y = load_f4(a.ybuf + static_cast<size_t>(s) * H + h);
     acc.x = fmaf(w, y.x, acc.x);

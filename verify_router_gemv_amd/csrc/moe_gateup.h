@@ -102,7 +102,7 @@ __device__ __forceinline__ float fold_block(const i32x4& d0, const i32x4& d1, co
 }
 
 template <typename StageFn>
-__device__ __forceinline__ void gateup_mfma_tile(const Args& a, const ExpertWork& wk, const moe_layer_weights& W,
+__device__ __forceinline__ void gateup_mfma_tile(const Args& a, const ExpertWork& wk, const ExpertPtrs& W,
                                                  int row0, const uint32_t* xs_dig, const float* xs_ss, int SR,
                                                  uint32_t* lds, StageFn stage) {
   const int I = a.I;
@@ -110,7 +110,7 @@ __device__ __forceinline__ void gateup_mfma_tile(const Args& a, const ExpertWork
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int kb0 = wave * kMfmaBlocksPerWave;
-  const size_t rg = static_cast<size_t>(wk.e) * I + min(row0 + r, I - 1);
+  const size_t rg = min(row0 + r, I - 1);  // row of the expert's gate and up matrices
   const size_t rq = static_cast<size_t>(nblk) * 16, rsm = nblk;
 
   // Codes: for group j lane (r, q) loads block kb0 + 4j + q of row r; after the transpose lane
@@ -118,11 +118,11 @@ __device__ __forceinline__ void gateup_mfma_tile(const Args& a, const ExpertWork
   uint4 cg[4], cu[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    cg[j] = load_stream_u4(W.gate_q + rg * rq + 16 * (kb0 + 4 * j + q));
-    cu[j] = load_stream_u4(W.up_q + rg * rq + 16 * (kb0 + 4 * j + q));
+    cg[j] = load_stream_u4(W.gq + rg * rq + 16 * (kb0 + 4 * j + q));
+    cu[j] = load_stream_u4(W.uq + rg * rq + 16 * (kb0 + 4 * j + q));
   }
-  const uint4 smg = load_stream_u4(W.gate_sm + rg * rsm + kb0 + 4 * q);
-  const uint4 smu = load_stream_u4(W.up_sm + rg * rsm + kb0 + 4 * q);
+  const uint4 smg = load_stream_u4(W.gs + rg * rsm + kb0 + 4 * q);
+  const uint4 smu = load_stream_u4(W.us + rg * rsm + kb0 + 4 * q);
 
   float* sm_lds = reinterpret_cast<float*>(lds) + wave * kMfmaSmWords;  // [matrix][block][row] (s, m)
   float* red = reinterpret_cast<float*>(lds) + kWaves * kMfmaSmWords;   // [wave][matrix][row][column]
@@ -235,7 +235,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane % G, rs = lane / G;
-  const moe_layer_weights& W = get_weights(a, layer);
+  const ExpertPtrs W = expert_ptrs<FMT>(a, wk.e);  // issued first: every weight address needs it
   const int row0 = tile * ROWS_B + wave * ROWS_W + rs;
   const size_t rq = static_cast<size_t>(H) / 2, rsm = sm_row_words<FMT>(H);
   const int SR = a.xstage_h;
@@ -311,17 +311,17 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
   // This unit's share of its expert's down rows (H split like I over the item's tiles), touched now
   // so the down kernel's block with the same index finds them in cache (see touch_lines). Issued
   // before the weight loads, so the wait for the weights covers them; issued in any case (without
-  // prefetching they touch the gate row this block reads anyway).
+  // prefetching they touch a line of the input digits, read anyway).
   const int pf_tiles = (I + ROWS_B - 1) / ROWS_B;
   const int pf_r0 = static_cast<int>(static_cast<long>(tile) * H / pf_tiles);
   const int pf_r1 = static_cast<int>(static_cast<long>(tile + 1) * H / pf_tiles);
   const bool pf_on = a.prefetch != 0 && pf_r1 > pf_r0;
   const size_t pf_q = static_cast<size_t>(I) / 2, pf_s = sm_row_words<FMT>(I) * 4;  // bytes per down row
-  const size_t pf_d0 = static_cast<size_t>(wk.e) * H + pf_r0;
-  const Touched<2> pfq = touch_lines<2>(pf_on ? W.down_q + pf_d0 * pf_q : W.gate_q,
+  const size_t pf_d0 = pf_r0;
+  const uint8_t* pf_idle = reinterpret_cast<const uint8_t*>(a.xq);  // a line read anyway (no weight address)
+  const Touched<2> pfq = touch_lines<2>(pf_on ? W.dq + pf_d0 * pf_q : pf_idle,
                                         pf_on ? (pf_r1 - pf_r0) * pf_q : 64, tid, kThreads);
-  const Touched<1> pfs = touch_lines<1>(pf_on ? reinterpret_cast<const uint8_t*>(W.down_sm) + pf_d0 * pf_s
-                                              : reinterpret_cast<const uint8_t*>(W.gate_sm),
+  const Touched<1> pfs = touch_lines<1>(pf_on ? reinterpret_cast<const uint8_t*>(W.ds) + pf_d0 * pf_s : pf_idle,
                                         pf_on ? (pf_r1 - pf_r0) * pf_s : 64, tid, kThreads);
 
   __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of the weight loads
@@ -329,14 +329,14 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
   BlockScale<FMT> sg[RW][NB], su[RW][NB];
 #pragma unroll
   for (int w = 0; w < RW; ++w) {
-    const size_t r = static_cast<size_t>(wk.e) * I + min(row0 + w * RPI, I - 1);  // rows past I: not stored
+    const size_t r = min(row0 + w * RPI, I - 1);  // rows past I: not stored
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int bl = g + nb * G, b = min(bl, nblk - 1);
-      cg[w][nb] = load_stream_u4(W.gate_q + r * rq + 16 * b);
-      cu[w][nb] = load_stream_u4(W.up_q + r * rq + 16 * b);
-      sg[w][nb].load(W.gate_sm + r * rsm, b);
-      su[w][nb].load(W.up_sm + r * rsm, b);
+      cg[w][nb] = load_stream_u4(W.gq + r * rq + 16 * b);
+      cu[w][nb] = load_stream_u4(W.uq + r * rq + 16 * b);
+      sg[w][nb].load(W.gs + r * rsm, b);
+      su[w][nb].load(W.us + r * rsm, b);
       sg[w][nb].mask(bl < nblk);
       su[w][nb].mask(bl < nblk);
     }

@@ -31,6 +31,41 @@ constexpr int kFmtQ4B32 = 0, kFmtQ4S256 = 1;
 template <int FMT>
 __host__ __device__ constexpr size_t sm_row_words(size_t K) { return FMT == kFmtQ4S256 ? K / 64 : K / 32; }
 
+// One expert's matrices: from the layer's contiguous [E][..] arrays, or, in table mode, from the
+// expert's table entry (one dependent load; e is uniform over the block, so the entry's address is).
+struct ExpertPtrs {
+  const uint8_t* gq;
+  const uint32_t* gs;
+  const uint8_t* uq;
+  const uint32_t* us;
+  const uint8_t* dq;
+  const uint32_t* ds;
+};
+
+template <int FMT>
+__device__ __forceinline__ ExpertPtrs expert_ptrs(const Args& a, int e) {
+  e = __builtin_amdgcn_readfirstlane(e);
+  ExpertPtrs p;
+  if (a.etab) {
+    const moe_expert_ref r = a.etab[e];
+    p.gq = r.gate_q;
+    p.gs = r.gate_sm;
+    p.uq = r.up_q;
+    p.us = r.up_sm;
+    p.dq = r.down_q;
+    p.ds = r.down_sm;
+    return p;
+  }
+  const size_t H = a.H, I = a.I, ex = static_cast<size_t>(e);
+  p.gq = a.w.gate_q + ex * I * (H / 2);
+  p.gs = a.w.gate_sm + ex * I * sm_row_words<FMT>(H);
+  p.uq = a.w.up_q + ex * I * (H / 2);
+  p.us = a.w.up_sm + ex * I * sm_row_words<FMT>(H);
+  p.dq = a.w.down_q + ex * H * (I / 2);
+  p.ds = a.w.down_sm + ex * H * sm_row_words<FMT>(I);
+  return p;
+}
+
 template <int FMT>
 struct BlockScale;
 

@@ -127,6 +127,10 @@ struct moe_round {
   float* pf_hstep = nullptr;
   float* pf_ybuf = nullptr;
   uint32_t* floor_sink = nullptr;      // [kFloorMaxBlocks] measurement kernels' sink
+  // expert table mode and tail skip (caller-owned device arrays, bound with moe_round_bind_experts)
+  const moe_expert_ref* etab = nullptr;  // [L][E]
+  const uint32_t* resident = nullptr;    // [L][ceil(E/32)]
+  int32_t* n_skipped = nullptr;          // [L] experts the tail skip left out
 };
 
 static moe_status hip_fail(moe_round* h, hipError_t e) {
@@ -197,6 +201,8 @@ static Args base_args(const moe_round* h, int T, int k) {
   a.mfma_rows = h->cfg.exact ? 0 : h->mfma_rows;  // the tile's sums differ in order from the GEMV
   a.xstage_i = xstage_rows(h->cfg.inter);
   a.prefetch = h->cfg.prefetch;
+  a.skip_j = h->cfg.tail_skip_rank > 0 ? h->cfg.tail_skip_rank - 1 : (1 << 30);
+  a.n_skipped = h->n_skipped;
   return a;
 }
 
@@ -257,6 +263,9 @@ static int layer_launches(const RoundPlan& p, int l, Launch* out) {
 static Args layer_args(const moe_round* h, Args a, int layer) {
   a.w = h->wts[layer];
   a.router_next = layer + 1 < h->cfg.n_layers ? h->wts[layer + 1].router_w : nullptr;
+  const size_t E = h->cfg.n_experts;
+  a.etab = h->etab ? h->etab + layer * E : nullptr;
+  a.resident = h->resident ? h->resident + layer * ((E + 31) / 32) : nullptr;
   return a;
 }
 
@@ -547,7 +556,8 @@ static void free_handle(moe_round* h) {
                   h->pairs, h->pair_w, h->rec, h->hbuf, h->ybuf, h->slot_of, h->tsel, h->tp, h->xq, h->xss,
                   h->pf_xbuf[0], h->pf_xbuf[1], h->pf_xq, h->pf_xstep, h->pf_mask, h->pf_wpre,
                   h->pf_sel, h->pf_selp, h->pf_uniq, h->pf_offs, h->pf_eoff, h->pf_pairs, h->pf_pair_w, h->pf_slot_of,
-                  h->pf_items, h->pf_n_items, h->pf_hbuf, h->pf_hq, h->pf_hstep, h->pf_ybuf, h->floor_sink};
+                  h->pf_items, h->pf_n_items, h->pf_hbuf, h->pf_hq, h->pf_hstep, h->pf_ybuf, h->floor_sink,
+                  h->n_skipped};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete h;
@@ -595,6 +605,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   MOE_ALLOC(h->xall, sizeof(float) * h->xslots * T * H);
   MOE_ALLOC(h->logits, sizeof(double) * cfg->max_rows * E);
   MOE_ALLOC(h->n_unique, sizeof(int32_t) * L);
+  MOE_ALLOC(h->n_skipped, sizeof(int32_t) * L);
   MOE_ALLOC(h->uniq, sizeof(int32_t) * L * h->Ucap);
   MOE_ALLOC(h->offs, sizeof(int32_t) * L * (h->Ucap + 1));
   MOE_ALLOC(h->pairs, sizeof(int32_t) * L * h->Pcap);
@@ -644,6 +655,7 @@ extern "C" moe_status moe_round_init(const moe_round_config* cfg, const moe_laye
   for (int i = 0; i < kStagingSlots; ++i)
     if ((e = hipEventCreateWithFlags(&h->slot_ev[i], hipEventDisableTiming)) != hipSuccess) return fail(e);
   if ((e = hipMemsetAsync(h->n_unique, 0, sizeof(int32_t) * L, h->stream)) != hipSuccess) return fail(e);
+  if ((e = hipMemsetAsync(h->n_skipped, 0, sizeof(int32_t) * L, h->stream)) != hipSuccess) return fail(e);
   if ((e = hipMemsetAsync(h->rec, 0, sizeof(int32_t) * L * h->Icap * kRecWords, h->stream)) != hipSuccess)
     return fail(e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return fail(e);
@@ -656,6 +668,8 @@ static moe_status prepare_run(moe_round* h, const float* hidden, int32_t T, int3
   if (!h) return MOE_ERR_INVALID_ARG;
   moe_status st = validate_run(&h->cfg, hidden, T, k, out, ids, rw);
   if (st != MOE_OK) return st;
+  if (T > 0 && ((h->cfg.expert_table && !h->etab) || (h->cfg.tail_skip_rank > 0 && !h->resident)))
+    return MOE_ERR_STATE;  // the table or the residency bits are not bound yet
   if (layers) {
     st = validate_layers(&h->cfg, layers);
     if (st != MOE_OK) return st;
@@ -669,6 +683,39 @@ static moe_status prepare_run(moe_round* h, const float* hidden, int32_t T, int3
     h->h_ing = ing;
     h->dev_ing_valid = false;
   }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_bind_experts(moe_round* h, const moe_expert_ref* table,
+                                             const uint32_t* resident) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if ((table != nullptr) != (h->cfg.expert_table != 0)) return MOE_ERR_INVALID_ARG;
+  if ((resident != nullptr) != (h->cfg.tail_skip_rank > 0)) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(table) & 15u) || (reinterpret_cast<uintptr_t>(resident) & 3u))
+    return MOE_ERR_INVALID_ARG;
+  if (table != h->etab || resident != h->resident) {
+    h->etab = table;
+    h->resident = resident;
+    ++h->weights_version;  // captured graphs' nodes carry the per-layer pointers
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_round_host_tier_pointer(const void* host_ptr, void** device_ptr) {
+  if (!host_ptr || !device_ptr) return MOE_ERR_INVALID_ARG;
+  *device_ptr = nullptr;
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, host_ptr) != hipSuccess) {
+    (void)hipGetLastError();  // not memory the runtime knows: clear the sticky error
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (attr.type != hipMemoryTypeHost) return MOE_ERR_INVALID_ARG;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void*>(host_ptr), 0) != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return MOE_ERR_INVALID_ARG;
+  }
+  *device_ptr = d;
   return MOE_OK;
 }
 
@@ -793,11 +840,16 @@ extern "C" moe_status moe_round_worklist(moe_round* h, int32_t layer, int32_t* n
                          hipMemcpyDeviceToHost));
   if (pairs) {
     const int np = h->last_T * h->last_k;
+    int kept = np;  // the tail skip may leave pairs out: the worklist holds offs[n_unique] of them
+    if (!pf)
+      MOE_HIP(h, hipMemcpy(&kept, d_offs + static_cast<size_t>(layer) * (ucap + 1) + nu, sizeof(int32_t),
+                           hipMemcpyDeviceToHost));
+    if (kept < 0 || kept > np) return MOE_ERR_STATE;
     std::vector<int32_t> packed(np);
-    MOE_HIP(h, hipMemcpy(packed.data(), d_pairs, sizeof(int32_t) * np, hipMemcpyDeviceToHost));
+    if (kept) MOE_HIP(h, hipMemcpy(packed.data(), d_pairs, sizeof(int32_t) * kept, hipMemcpyDeviceToHost));
     for (int i = 0; i < np; ++i) {
-      pairs[2 * i] = pf ? (packed[i] & 0xFFFF) : (packed[i] & 0xFF);
-      pairs[2 * i + 1] = pf ? (packed[i] >> 16) : ((packed[i] >> 8) & 0xFF);
+      pairs[2 * i] = i >= kept ? -1 : pf ? (packed[i] & 0xFFFF) : (packed[i] & 0xFF);
+      pairs[2 * i + 1] = i >= kept ? -1 : pf ? (packed[i] >> 16) : ((packed[i] >> 8) & 0xFF);
     }
   }
   return MOE_OK;
@@ -847,9 +899,13 @@ extern "C" moe_status moe_round_last_stats(moe_round* h, moe_round_stats* stats,
   if (!h || !stats) return MOE_ERR_INVALID_ARG;
   if (h->last_T == 0) return MOE_ERR_STATE;
   const int L = h->cfg.n_layers;
-  std::vector<int32_t> nu(L);
+  std::vector<int32_t> nu(L), ns(L, 0);
   MOE_HIP(h, hipStreamSynchronize(h->stream));
   MOE_HIP(h, hipMemcpy(nu.data(), h->n_unique, sizeof(int32_t) * L, hipMemcpyDeviceToHost));
+  if (h->cfg.tail_skip_rank > 0 && h->last_T <= MOE_ROUND_MAX_ROWS)
+    MOE_HIP(h, hipMemcpy(ns.data(), h->n_skipped, sizeof(int32_t) * L, hipMemcpyDeviceToHost));
+  int32_t skipped = 0;
+  for (int l = 0; l < L; ++l) skipped += ns[l];
   const int64_t eb = expert_bytes(h->cfg);
   const int64_t act = 2LL * h->last_T * h->cfg.hidden * static_cast<int64_t>(sizeof(float));
   int64_t total = 0;
@@ -862,7 +918,7 @@ extern "C" moe_status moe_round_last_stats(moe_round* h, moe_round_stats* stats,
   stats->n_layers = L;
   stats->rows = h->last_T;
   stats->top_k = h->last_k;
-  stats->reserved = 0;
+  stats->skipped = skipped;
   stats->expert_bytes = eb;
   stats->metric_bytes = total;
   return MOE_OK;
@@ -885,6 +941,7 @@ static moe_status launch_floor(moe_round* h, FloorArgs fa, int units_max, int gr
 extern "C" moe_status moe_round_floor(moe_round* h) {
   if (!h) return MOE_ERR_INVALID_ARG;
   if (h->last_T == 0) return MOE_ERR_STATE;
+  if (h->cfg.expert_table) return MOE_ERR_UNSUPPORTED;  // no common base address per layer
   const moe_round_config& c = h->cfg;
   const int64_t H = c.hidden, I = c.inter, E = c.n_experts;
   const bool pf = h->last_T > MOE_ROUND_MAX_ROWS;
@@ -1010,6 +1067,7 @@ extern "C" moe_status moe_round_run_noalloc(const moe_round_config* cfg, const m
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (T > MOE_ROUND_MAX_ROWS) return MOE_ERR_UNSUPPORTED;  // prefill rounds need handle scratch
+  if (cfg->expert_table || cfg->tail_skip_rank) return MOE_ERR_UNSUPPORTED;  // no handle to bind a table to
   // A handle on the stack over the fixed array: nothing here allocates, on the host or the device.
   moe_round h;
   h.cfg = *cfg;

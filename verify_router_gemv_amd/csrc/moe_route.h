@@ -97,8 +97,13 @@ struct SelectSharedT {
   int ioffs[MOE_ROUND_MAX_EXPERTS];                    // unique index -> first work item
   int pairs[PMAX];                                     // by pair slot: t | j << 8
   int item_u[PMAX];                                    // work item -> unique index
-  unsigned long long ctot[MOE_ROUND_MAX_EXPERTS / 64];  // per 64-expert chunk: chosen, rows, items
+  unsigned long long ctot[MOE_ROUND_MAX_EXPERTS / 64];  // per 64-expert chunk: chosen, rows, items, skipped
+  unsigned long long tmask[MOE_ROUND_MAX_EXPERTS];     // tail skip: rows whose pair with e is a tail pair
+  int slot[PMAX];                                      // [t][j] the pair's worklist slot, -1 if skipped
+  uint32_t res[MOE_ROUND_MAX_EXPERTS / 32];            // tail skip: the layer's residency bits
   int nu, ni;
+  int np;     // pairs kept (all of them without the tail skip)
+  int nskip;  // experts the tail skip left out
 };
 using SelectShared = SelectSharedT<MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK, kSelectWaves>;
 
@@ -172,14 +177,26 @@ __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
   }
 }
 
-// The union of a round by the whole block (any number of pairs; s.mask zero, s.sel written).
+// Tail skip: is the pair (rank j, expert e) a tail pair, i.e. e is missed (its residency bit is
+// clear) and j is at or past the skip rank? A missed expert is skipped when all its pairs are.
+template <typename SS>
+__device__ __forceinline__ bool tail_pair(const Args& a, const SS& s, int j, int e) {
+  return j >= a.skip_j && !((s.res[e >> 5] >> (e & 31)) & 1u);
+}
+
+// The union of a round by the whole block (any number of pairs; s.mask zero, s.sel written; with
+// `skip`, s.tmask zero and s.res written). Experts the tail skip leaves out get no pairs, slot -1.
 template <int NT, typename SS>
-__device__ __forceinline__ void union_block(const Args& a, SS& s, int npairs, int& nu, int& ni) {
+__device__ __forceinline__ void union_block(const Args& a, SS& s, int npairs, bool skip, int& nu, int& ni) {
   constexpr int NWMIN = NT / 64;  // fewest waves a caller launches (sizes the per-wave arrays)
   const int nt = blockDim.x, nw = nt >> 6;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k;
-  for (int idx = tid; idx < npairs; idx += nt) atomicOr(&s.mask[s.sel[idx]], 1ull << (idx / k));
+  for (int idx = tid; idx < npairs; idx += nt) {
+    const int e = s.sel[idx], t = idx / k;
+    const bool tail = skip && tail_pair(a, s, idx - t * k, e);
+    atomicOr(tail ? &s.tmask[e] : &s.mask[e], 1ull << t);
+  }
   __syncthreads();
 
   // The union and its prefix sums, with ballots instead of a shuffle scan. Chunk ch of 64
@@ -196,7 +213,20 @@ __device__ __forceinline__ void union_block(const Args& a, SS& s, int npairs, in
 #pragma unroll
   for (int q = 0; q < CPW; ++q) {
     const int ch = q * nw + wave, e = ch * 64 + lane;
-    const int c = (ch < NCH && e < E) ? __popcll(s.mask[min(e, MOE_ROUND_MAX_EXPERTS - 1)]) : 0;
+    const bool valid = ch < NCH && e < E;
+    const int ec = min(e, MOE_ROUND_MAX_EXPERTS - 1);
+    uint64_t m = valid ? s.mask[ec] : 0ull;
+    bool skipped = false;
+    if (skip && valid) {  // an expert with a kept pair keeps its tail pairs too; one without is skipped
+      const uint64_t tm = s.tmask[ec];
+      if (m != 0ull) {
+        m |= tm;
+        s.mask[ec] = m;
+      } else {
+        skipped = tm != 0ull;
+      }
+    }
+    const int c = __popcll(m);
     cnt[q] = c;
     ngs[q] = (c + rg - 1) / rg;
     const uint64_t chosen = __ballot(c > 0);
@@ -213,9 +243,10 @@ __device__ __forceinline__ void union_block(const Args& a, SS& s, int npairs, in
       gi += mbcnt64(mb) << b;
       tot += static_cast<uint64_t>(__popcll(mb)) << (32 + b);
     }
+    tot += static_cast<uint64_t>(__popcll(__ballot(skipped))) << 48;
     cin[q] = ci;
     gin[q] = gi;
-    if (lane == 0 && ch < NCH) s.ctot[ch] = tot;  // chosen | rows << 16 | items << 32
+    if (lane == 0 && ch < NCH) s.ctot[ch] = tot;  // chosen | rows << 16 | items << 32 | skipped << 48
   }
   __syncthreads();
   uint64_t all = 0, pre[CPW];
@@ -245,16 +276,25 @@ __device__ __forceinline__ void union_block(const Args& a, SS& s, int npairs, in
     }
   }
   if (tid == 0) {
+    const int kept = static_cast<int>((all >> 16) & 0xFFFF);
     s.nu = nu;
     s.ni = ni;
-    s.offs[nu] = npairs;
+    s.np = kept;
+    s.nskip = static_cast<int>((all >> 48) & 0xFFFF);
+    s.offs[nu] = kept;
   }
   __syncthreads();
   for (int idx = tid; idx < npairs; idx += nt) {
     const int t = idx / k, j = idx - t * k;
     const int e = s.sel[idx];
-    const int pos = s.offs[s.uidx[e]] + __popcll(s.mask[e] & ((1ull << t) - 1ull));
+    const uint64_t m = s.mask[e];
+    if (!((m >> t) & 1ull)) {  // a pair of a skipped expert
+      s.slot[idx] = -1;
+      continue;
+    }
+    const int pos = s.offs[s.uidx[e]] + __popcll(m & ((1ull << t) - 1ull));
     s.pairs[pos] = t | (j << 8);
+    s.slot[idx] = pos;
   }
   __syncthreads();
 }
@@ -273,38 +313,61 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k, npairs = T * k;
 
+  // Tail skip: the layer's residency words, loaded before the top-k (which hides their latency) and
+  // put into LDS after it.
+  const bool skip = a.resident != nullptr && a.skip_j < k;
+  const int nres = (E + 31) >> 5;
+  uint32_t resw = 0u;
+  if (skip && tid < nres) resw = a.resident[tid];
+
   int nu, ni;
   if constexpr (ONE_ROW) {
     // Rounds of one row (callers that only run at T == 1): the union is its k ids, one row each,
-    // so one wave ranks them (ascending expert id) and writes the worklist directly.
+    // so one wave ranks them (ascending expert id) and writes the worklist directly. With the tail
+    // skip an expert is skipped exactly when its one pair is a tail pair.
     if (wave == 0) {
       select_row<NPL>(a, s, 0);
       const int j = min(lane, k - 1);
       const int id = s.sel[j];
+      bool keep = true;
+      if (skip) {
+        const uint32_t word = static_cast<uint32_t>(__shfl(static_cast<int>(resw), id >> 5, 64));
+        keep = j < a.skip_j || ((word >> (id & 31)) & 1u);
+      }
+      const uint64_t kb = __ballot(lane < k && keep);
       int u = 0;
 #pragma unroll
       for (int m = 0; m < MOE_ROUND_MAX_TOPK; ++m) {
         const int v = s.sel[min(m, k - 1)];
-        u += (m < k && v < id) ? 1 : 0;
+        u += (m < k && ((kb >> m) & 1ull) && v < id) ? 1 : 0;
       }
+      const int nk = __popcll(kb);
       if (lane < k) {
-        s.uniq[u] = id;
-        s.offs[u] = u;
-        s.ioffs[u] = u;
-        s.item_u[u] = u;
-        s.pairs[u] = j << 8;  // row 0, rank j
+        s.slot[lane] = keep ? u : -1;
+        if (keep) {
+          s.uniq[u] = id;
+          s.offs[u] = u;
+          s.ioffs[u] = u;
+          s.item_u[u] = u;
+          s.pairs[u] = j << 8;  // row 0, rank j
+        }
       }
       if (lane == 0) {
-        s.nu = min(k, a.Ucap);
-        s.ni = min(k, a.Icap);
-        s.offs[k] = k;
+        s.nu = min(nk, a.Ucap);
+        s.ni = min(nk, a.Icap);
+        s.np = nk;
+        s.nskip = k - nk;
+        s.offs[nk] = nk;
       }
     }
     __syncthreads();
     nu = s.nu;
     ni = s.ni;
   } else {
-    for (int e = tid; e < E; e += nt) s.mask[e] = 0ull;
+    for (int e = tid; e < E; e += nt) {
+      s.mask[e] = 0ull;
+      if (skip) s.tmask[e] = 0ull;
+    }
     if constexpr (PRESEL) {
       for (int idx = tid; idx < npairs; idx += nt) {
         s.sel[idx] = min(max(a.tsel[idx], 0), E - 1);
@@ -313,8 +376,9 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
     } else {
       for (int t = wave; t < T; t += nw) select_row<NPL>(a, s, t);
     }
+    if (skip && tid < nres) s.res[tid] = resw;
     __syncthreads();
-    union_block<NT>(a, s, npairs, nu, ni);
+    union_block<NT>(a, s, npairs, skip, nu, ni);
   }
   if (!publish) return;
 
@@ -345,19 +409,28 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
       r[kRecRowWord + wd] = v;
     }
   }
+  // Record 0 carries the item count every GEMV block reads; a round whose pairs the tail skip left
+  // out entirely has no item to write it, so it is written here.
+  if (tid == 0 && ni == 0) rec[3] = 0;
   for (int i = tid; i < nu; i += nt) uniq[i] = s.uniq[i];
   for (int i = tid; i <= nu; i += nt) offs[i] = s.offs[i];
   int32_t* slot_of = a.slot_of + static_cast<size_t>(layer) * a.Pcap;
-  for (int i = tid; i < npairs; i += nt) {
+  const int kept = s.np;
+  for (int i = tid; i < kept; i += nt) {  // the worklist's pair slots
     const int pr = s.pairs[i];
     pairs[i] = pr;
     pw[i] = s.p[(pr & 0xFF) * k + (pr >> 8)];
-    slot_of[(pr & 0xFF) * k + (pr >> 8)] = i;
-    const size_t o = static_cast<size_t>(layer) * npairs + i;  // [L][T][k] with i = t*k + j
+  }
+  for (int i = tid; i < npairs; i += nt) {  // by (row, rank): i = t*k + j
+    slot_of[i] = s.slot[i];
+    const size_t o = static_cast<size_t>(layer) * npairs + i;  // [L][T][k]
     if (in.ids) in.ids[o] = s.sel[i];
     if (in.route_w) in.route_w[o] = s.p[i];
   }
-  if (tid == 0) a.n_unique[layer] = nu;
+  if (tid == 0) {
+    a.n_unique[layer] = nu;
+    if (a.n_skipped) a.n_skipped[layer] = s.nskip;
+  }
 }
 
 template <int NPL, bool PRESEL = false>

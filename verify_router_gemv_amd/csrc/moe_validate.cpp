@@ -52,6 +52,8 @@ moe_status validate_config(const moe_round_config* c) {
   if (c->weight_format != MOE_WEIGHT_Q4B32 && c->weight_format != MOE_WEIGHT_Q4S256) return MOE_ERR_INVALID_ARG;
   if (c->prefetch != 0 && c->prefetch != 1) return MOE_ERR_INVALID_ARG;
   if (c->record_layers != 0 && c->record_layers != 1) return MOE_ERR_INVALID_ARG;
+  if (c->expert_table != 0 && c->expert_table != 1) return MOE_ERR_INVALID_ARG;
+  if (c->tail_skip_rank < 0 || c->tail_skip_rank > MOE_ROUND_MAX_TOPK + 1) return MOE_ERR_INVALID_ARG;
   if (c->top_k_max > c->n_experts) return MOE_ERR_INVALID_ARG;
   if (c->max_rows > MOE_ROUND_MAX_PREFILL_ROWS) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts > MOE_ROUND_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
@@ -64,6 +66,9 @@ moe_status validate_config(const moe_round_config* c) {
   if (c->weight_format == MOE_WEIGHT_Q4S256 && c->inter % 256 != 0) return MOE_ERR_UNSUPPORTED;
   // Prefill GEMMs step through the reduction four 32-blocks at a time and tile I by 64 rows.
   if (c->max_rows > MOE_ROUND_MAX_ROWS && c->inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  // The expert table and the tail skip are decode/verify features (the prefill GEMMs address the
+  // contiguous expert arrays and sort every pair).
+  if (c->max_rows > MOE_ROUND_MAX_ROWS && (c->expert_table || c->tail_skip_rank)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -73,12 +78,17 @@ moe_status validate_layers(const moe_round_config* c, const moe_layer_weights* l
   if (!layers) return MOE_ERR_INVALID_ARG;
   for (int l = 0; l < c->n_layers; ++l) {
     const moe_layer_weights& w = layers[l];
-    if (!w.router_w || !w.gate_q || !w.gate_sm || !w.up_q || !w.up_sm || !w.down_q || !w.down_sm)
-      return MOE_ERR_INVALID_ARG;
-    if (!aligned16(w.router_w) || !aligned16(w.gate_q) || !aligned16(w.up_q) || !aligned16(w.down_q) ||
-        !aligned16(w.gate_sm) || !aligned16(w.up_sm) || !aligned16(w.down_sm))
-      return MOE_ERR_INVALID_ARG;
+    if (!w.router_w || !aligned16(w.router_w)) return MOE_ERR_INVALID_ARG;
     if (w.router_bias && (reinterpret_cast<uintptr_t>(w.router_bias) & 3u)) return MOE_ERR_INVALID_ARG;
+    if (c->expert_table) {  // the experts come from the bound table: these must be unset
+      if (w.gate_q || w.gate_sm || w.up_q || w.up_sm || w.down_q || w.down_sm) return MOE_ERR_INVALID_ARG;
+      continue;
+    }
+    if (!w.gate_q || !w.gate_sm || !w.up_q || !w.up_sm || !w.down_q || !w.down_sm)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(w.gate_q) || !aligned16(w.up_q) || !aligned16(w.down_q) || !aligned16(w.gate_sm) ||
+        !aligned16(w.up_sm) || !aligned16(w.down_sm))
+      return MOE_ERR_INVALID_ARG;
   }
   return MOE_OK;
 }
