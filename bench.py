@@ -47,6 +47,8 @@ def parse():
                    help="skip the kernel-timing pass (no roofline)")
     p.add_argument("--prefill-only", type=int, default=0, metavar="T",
                    help="only the prefill section, at T rows (for profiling it); prints its JSON")
+    p.add_argument("--only", default="", choices=("", "decode", "wide", "deep", "tier"),
+                   help="only that extra section (for profiling it); prints its JSON")
     return p.parse_args()
 
 
@@ -86,6 +88,13 @@ def main():
         print(json.dumps({"prefill": prefill_rounds(base, torch, np, synth, MoeRound, (args.prefill_only,))}), flush=True)
         if args.pmc_calibrate:
             calibration_copy(torch, dev)
+        return
+    if args.only:
+        run_one = {"decode": lambda: decode_rounds(torch, np, synth, MoeRound),
+                   "wide": lambda: wide_rounds(cfg, base, torch, np, synth, MoeRound),
+                   "deep": lambda: deep_stack(torch, np, synth, MoeRound),
+                   "tier": lambda: tier_rounds(torch, np, synth, MoeRound)}[args.only]
+        print(json.dumps({args.only: run_one()}), flush=True)
         return
     reps = [base] + [base.clone() for _ in range(args.replicas - 1)]
     n_acts = 256
@@ -254,7 +263,10 @@ def main():
             lat = [event_us(torch, lambda: ghs[r % R].run(acts[T][(r + 7) % n_acts], cfg.k, outs[T]))
                    for r in range(64)]
             med = float(np.median(lat))
+            # the same graphs with the round's input always in the same buffer: no ingress upload
+            fixed = [event_us(torch, lambda: ghs[r % R].run(acts[T][0], cfg.k, outs[T])) for r in range(64)]
             graph_per_T[str(T)] = {"round_us_median": round(med, 2), "tok_per_s": round(T / med * 1e6, 1),
+                                   "fixed_buffers_round_us_median": round(float(np.median(fixed)), 2),
                                    "eager_round_us_median": per_T[str(T)]["round_us_median"]}
         for h in ghs:
             h.close()
@@ -271,6 +283,7 @@ def main():
     deep = None if args.no_extra else deep_stack(torch, np, synth, MoeRound)
     superblock = None if args.no_extra else superblock_rounds(acts, args.replicas, torch, np, synth, MoeRound)
     prefill = None if args.no_extra else prefill_rounds(base, torch, np, synth, MoeRound)
+    tier = None if args.no_extra else tier_rounds(torch, np, synth, MoeRound)
 
     cpu = None
     if not args.no_cpu:
@@ -304,6 +317,7 @@ def main():
         "deep_stack": deep,
         "superblock_format": superblock,
         "prefill": prefill,
+        "expert_tier": tier,
     }
     print(json.dumps(line), flush=True)
     if args.pmc_calibrate:
@@ -609,6 +623,100 @@ def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager")
     del layers, flush
     torch.cuda.empty_cache()
     return res
+
+
+def tier_rounds(torch, np, synth, MoeRound, L=8, resident_frac=0.25, skip_rank=7):
+    """Both residency patterns of tier_placement: the hottest experts resident (a cache filled by
+    popularity) and a random quarter resident (a cold cache: most routed experts are missed)."""
+    return {"hottest_resident": tier_placement(torch, np, synth, MoeRound, L, resident_frac, skip_rank, "hot"),
+            "random_resident": tier_placement(torch, np, synth, MoeRound, L, resident_frac, skip_rank, "random")}
+
+
+def tier_placement(torch, np, synth, MoeRound, L, resident_frac, skip_rank, placement):
+    """Experts read through the pointer table (T=3 rounds of the 512-expert, top-10 stack's shape,
+    8 layers): the contiguous arrays; the table with every expert in device memory (the cost of the
+    indirection); a quarter of each layer's experts in device memory (placement "hot": the most
+    popular under the router's Zipf bias; "random": a seeded random quarter) and the rest in pinned
+    host memory read in place over the host link, without and with the tail skip at rank 7; and the
+    tail skip over the same residency with every expert in device memory. Per mode: round latency,
+    unique experts read, missed experts read from the host tier and the host-link rate they imply,
+    experts skipped and their bytes."""
+    from verify_router_gemv_amd import binding
+    cfg = synth.config("deep").replace(L=L)
+    T = cfg.T[0]
+    layers = [synth.make_layer(cfg, seed=0, layer=l, device="cuda") for l in range(L)]
+    rcfg = cfg if placement == "hot" else cfg.replace(zipf_s=None)  # no bias: a seeded random subset
+    res = [synth.make_residency(rcfg, resident_frac, seed=0, layer=l) for l in range(L)]
+    t0 = time.perf_counter()
+    host = []  # per layer: the missed experts' matrices in pinned host memory
+    for l in range(L):
+        missed = torch.as_tensor(np.flatnonzero(~res[l]), device="cuda")
+        hl = {}
+        for f in binding.EXPERT_FIELDS:
+            src = getattr(layers[l], f)
+            hl[f] = torch.empty((len(missed),) + tuple(src.shape[1:]), dtype=src.dtype, pin_memory=True)
+            hl[f].copy_(src[missed].cpu())
+        host.append(hl)
+    pin_s = time.perf_counter() - t0
+
+    def entries(tiered):
+        rows = []
+        for l in range(L):
+            slot = {int(e): i for i, e in enumerate(np.flatnonzero(~res[l]))}
+            rows.append([{f: (host[l][f][slot[e]] if tiered and not res[l][e] else getattr(layers[l], f)[e])
+                          for f in binding.EXPERT_FIELDS} for e in range(cfg.E)])
+        return rows
+
+    dev_table = binding.make_expert_table(entries(False), cfg.H, cfg.I)
+    tier_table = binding.make_expert_table(entries(True), cfg.H, cfg.I)
+    bits = binding.residency_bits(np.stack(res))
+    routers = [{"router_w": l.router_w, "router_b": l.router_b} for l in layers]
+    xs = [synth.make_activations(cfg, T, seed=0, round_idx=r, device="cuda") for r in range(8)]
+    out = torch.empty((T, cfg.H), device="cuda")
+    eb = cfg.expert_bytes()
+    result = {"layers": L, "T": T, "E": cfg.E, "k": cfg.k, "resident_frac": resident_frac,
+              "skip_rank": skip_rank, "host_tier_GB": round(sum(v.numel() * v.element_size()
+                                                                for hl in host for v in hl.values()) / 1e9, 2),
+              "pin_and_copy_s": round(pin_s, 1)}
+    modes = {
+        "contiguous": (dict(), layers, None, None),
+        "table_device": (dict(expert_table=True), routers, dev_table, None),
+        "table_host_tier": (dict(expert_table=True), routers, tier_table, None),
+        "table_host_tier_skip": (dict(expert_table=True, tail_skip_rank=skip_rank), routers, tier_table, bits),
+        "contiguous_skip": (dict(tail_skip_rank=skip_rank), layers, None, bits),
+    }
+    for name, (kw, lays, table, rbits) in modes.items():
+        h = MoeRound(lays, cfg.H, cfg.I, cfg.E, cfg.k, max_rows=T, residual=True, use_graph=True, **kw)
+        if table is not None or rbits is not None:
+            h.bind_experts(table, rbits)
+        for r in range(3):
+            h.run(xs[r], cfg.k, out)
+        lat, nus, missed_read, skipped = [], [], [], []
+        for r in range(8):
+            lat.append(timed_rounds(h, [xs[r]], cfg.k, out, 1, torch)[0])
+            st, nu, _ = h.last_stats()
+            nus.append(float(np.mean(nu)))
+            skipped.append(st.skipped / L)
+            m = 0
+            for l in range(L):
+                uniq = h.worklist(l)[0]
+                m += sum(1 for e in uniq if not res[l][e])
+            missed_read.append(m / L)
+        med = float(np.median(lat))
+        per_layer = med / L
+        mr = float(np.mean(missed_read))
+        tiered = name.startswith("table_host")
+        result[name] = {"round_us_median": round(med, 1), "per_layer_us": round(per_layer, 2),
+                        "n_unique_per_layer": round(float(np.mean(nus)), 2),
+                        "missed_experts_read_per_layer": round(mr, 2),
+                        "skipped_experts_per_layer": round(float(np.mean(skipped)), 2),
+                        "skipped_bytes_per_layer": int(float(np.mean(skipped)) * eb),
+                        "host_link_GBps": round(mr * eb / per_layer / 1e3, 1) if tiered else None,
+                        "tok_per_s": round(T / med * 1e6, 1)}
+        h.close()
+    del host, layers, dev_table, tier_table
+    torch.cuda.empty_cache()
+    return result
 
 
 def superblock_rounds(acts, replicas, torch, np, synth, MoeRound):
