@@ -47,7 +47,7 @@ def parse():
                    help="skip the kernel-timing pass (no roofline)")
     p.add_argument("--prefill-only", type=int, default=0, metavar="T",
                    help="only the prefill section, at T rows (for profiling it); prints its JSON")
-    p.add_argument("--only", default="", choices=("", "decode", "wide", "deep", "tier"),
+    p.add_argument("--only", default="", choices=("", "decode", "wide", "deep", "tier", "launch"),
                    help="only that extra section (for profiling it); prints its JSON")
     return p.parse_args()
 
@@ -93,7 +93,8 @@ def main():
         run_one = {"decode": lambda: decode_rounds(torch, np, synth, MoeRound),
                    "wide": lambda: wide_rounds(cfg, base, torch, np, synth, MoeRound),
                    "deep": lambda: deep_stack(torch, np, synth, MoeRound),
-                   "tier": lambda: tier_rounds(torch, np, synth, MoeRound)}[args.only]
+                   "tier": lambda: tier_rounds(torch, np, synth, MoeRound),
+                   "launch": lambda: launch_costs(torch, np, synth, MoeRound)}[args.only]
         print(json.dumps({args.only: run_one()}), flush=True)
         return
     reps = [base] + [base.clone() for _ in range(args.replicas - 1)]
@@ -177,7 +178,9 @@ def main():
     per_T = {}
     ctl_buf = torch.empty(CONTROL_BUF_BYTES // 4, device=dev)
     ctl_off = [0]
-    for T in TS_SWEEP:
+    # (a counter pass, --pmc-calibrate, runs only the T = 1, 3, 8 steps: its per-dispatch traffic then
+    # averages the same mix of gate/up launches as the roofline above)
+    for T in (() if args.pmc_calibrate else TS_SWEEP):
         if T not in acts:
             acts[T] = torch.stack([synth.make_activations(cfg, T, seed=0, round_idx=r, device=dev)
                                    for r in range(n_acts)])
@@ -242,7 +245,7 @@ def main():
     del ctl_buf
     # extra verify-row cost between consecutive widths and against T = 1
     per_T["extra_row"] = {}
-    for a_, b_ in list(zip(TS_SWEEP[:-1], TS_SWEEP[1:])) + [(1, 8)]:
+    for a_, b_ in ([] if args.pmc_calibrate else list(zip(TS_SWEEP[:-1], TS_SWEEP[1:])) + [(1, 8)]):
         pa, pb = per_T[str(a_)], per_T[str(b_)]
         per_T["extra_row"][f"{a_}->{b_}"] = {
             "us_per_row": round((pb["round_us_median"] - pa["round_us_median"]) / (b_ - a_), 2),
@@ -253,7 +256,7 @@ def main():
     # Labelled extra: the same widths replayed as captured hipGraphs (one graph per (T, k) and handle;
     # each round names a new input buffer, so each replay first uploads the ingress pointers).
     graph_per_T = None
-    if not args.no_extra and not args.graph:
+    if not args.no_extra and not args.graph and not args.pmc_calibrate:
         ghs = [MoeRound([reps[i]], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(TS_SWEEP), use_graph=True, **shape)
                for i in range(R)]
         graph_per_T = {"mode": "hipGraph replay, one graph per (T, k), ingress upload per round"}
@@ -284,6 +287,7 @@ def main():
     superblock = None if args.no_extra else superblock_rounds(acts, args.replicas, torch, np, synth, MoeRound)
     prefill = None if args.no_extra else prefill_rounds(base, torch, np, synth, MoeRound)
     tier = None if args.no_extra else tier_rounds(torch, np, synth, MoeRound)
+    launch = None if args.no_extra else launch_costs(torch, np, synth, MoeRound)
 
     cpu = None
     if not args.no_cpu:
@@ -318,6 +322,7 @@ def main():
         "superblock_format": superblock,
         "prefill": prefill,
         "expert_tier": tier,
+        "launch_costs": launch,
     }
     print(json.dumps(line), flush=True)
     if args.pmc_calibrate:
@@ -622,6 +627,27 @@ def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager")
         h.close()
     del layers, flush
     torch.cuda.empty_cache()
+    return res
+
+
+def launch_costs(torch, np, synth, MoeRound):
+    """What launching costs on this GPU, for the design's launch budget: chains of N minimal kernels
+    (the byte floor's read kernel over 16 bytes, one block) between two events, and one such kernel
+    alone; medians of 50 timings each."""
+    cfg = synth.config("tiny")
+    layer = synth.make_layer(cfg, seed=0, layer=0, device="cuda")
+    h = MoeRound([layer], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=1, use_graph=False)
+    buf = torch.zeros(4, device="cuda")
+    res = {"kernel": "one block reading 16 bytes", "timing": "torch events around the launches"}
+    for n in (1, 3, 10, 50):
+        def chain():
+            for _ in range(n):
+                h.stream_read(buf)
+        chain()
+        lat = [event_us(torch, chain) for _ in range(50)]
+        med = float(np.median(lat))
+        res[f"chain_{n}"] = {"us_median": round(med, 2), "us_per_launch": round(med / n, 2)}
+    h.close()
     return res
 
 
