@@ -299,6 +299,89 @@ __device__ __forceinline__ void union_block(const Args& a, SS& s, int npairs, bo
   __syncthreads();
 }
 
+// The value of lane (lane ^ stride), stride a power of two below 64 (constant after unrolling).
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int stride) {
+  switch (stride) {
+    case 1: return dpp_u32<kDppXor1>(v);
+    case 2: return dpp_u32<kDppXor2>(v);
+    case 4: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x1F | (4 << 10)));
+    case 8: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x1F | (8 << 10)));
+    case 16: return swap_partner_u32<false>(v);
+    default: return swap_partner_u32<true>(v);
+  }
+}
+__device__ __forceinline__ uint64_t low_bits(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
+
+// The union of a round of at most 64 (row, rank) pairs by one wave (s.sel written; with `skip`,
+// s.res written), the same worklist as union_block: lane i takes pair i as the key expert | row |
+// rank, a bitonic network sorts the 64 keys across the lanes in registers (ascending, so by expert,
+// then row), and runs of equal experts become the unique experts, their offsets and work items
+// through ballots. With the tail skip a run is kept when any of its pairs is not a tail pair.
+template <typename SS>
+__device__ __forceinline__ void union_wave(const Args& a, SS& s, int npairs, bool skip) {
+  const int lane = threadIdx.x & 63;
+  const int k = a.k, rg = a.rg;
+  uint32_t key = 0xFFFFFFFFu;  // past the pairs: sorts last
+  if (lane < npairs) {
+    const int t = lane / k;
+    key = (static_cast<uint32_t>(s.sel[lane]) << 10) | static_cast<uint32_t>(t << 4) | static_cast<uint32_t>(lane - t * k);
+  }
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t other = lane_xor_u32(key, stride);
+      const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);
+      key = keep_min ? min(key, other) : max(key, other);
+    }
+  const bool valid = lane < npairs;
+  const int e = static_cast<int>(key >> 10), t = static_cast<int>((key >> 4) & 63), j = static_cast<int>(key & 15);
+  const uint32_t prev = static_cast<uint32_t>(__shfl_up(static_cast<int>(key), 1, 64));
+  const bool head = valid && (lane == 0 || (prev >> 10) != (key >> 10));
+  const uint64_t heads = __ballot(head);
+  const uint64_t upto = low_bits(lane + 1);
+  const uint64_t above = heads & ~upto;
+  const int next = above ? __builtin_ctzll(above) : npairs;      // end of this lane's run
+  const int first = 63 - __builtin_clzll((heads & upto) | 1ull);  // start of this lane's run
+  bool kept = valid;
+  if (skip) {
+    const bool nt = valid && !tail_pair(a, s, j, e);
+    const uint64_t nts = __ballot(nt);
+    kept = valid && (nts & low_bits(next) & ~low_bits(first)) != 0ull;
+  }
+  const uint64_t keptm = __ballot(kept);
+  const bool khead = kept && head;
+  const uint64_t kheads = __ballot(khead);
+  const int below = static_cast<int>(__popcll(keptm & low_bits(lane)));  // slot among the kept pairs
+  const int u = static_cast<int>(__popcll(kheads & upto)) - 1;
+  const int ngs = khead ? (next - lane + rg - 1) / rg : 0;  // work items of this expert
+  int io = 0, ni = 0;
+#pragma unroll
+  for (int b = 0; b < 7; ++b) {
+    const uint64_t m = __ballot((ngs >> b) & 1);
+    io += static_cast<int>(__popcll(m & low_bits(lane))) << b;
+    ni += static_cast<int>(__popcll(m)) << b;
+  }
+  if (khead) {
+    s.uniq[u] = e;
+    s.offs[u] = below;
+    s.ioffs[u] = io;
+    for (int g = 0; g < ngs; ++g) s.item_u[io + g] = u;
+  }
+  if (valid) {
+    s.slot[t * k + j] = kept ? below : -1;
+    if (kept) s.pairs[below] = t | (j << 8);
+  }
+  if (lane == 0) {
+    const int nu = static_cast<int>(__popcll(kheads)), kept_n = static_cast<int>(__popcll(keptm));
+    s.nu = min(nu, a.Ucap);
+    s.ni = min(ni, a.Icap);
+    s.np = kept_n;
+    s.nskip = static_cast<int>(__popcll(heads)) - nu;
+    s.offs[min(nu, a.Ucap)] = kept_n;
+  }
+}
+
 // The selection of one round by one block (of at least NT threads; the strides use the launched
 // block size): per-row top-k and softmax, the union of
 // the rows' experts, the counting sort of the (row, rank) pairs by expert and the work items (an
@@ -364,10 +447,12 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
     nu = s.nu;
     ni = s.ni;
   } else {
-    for (int e = tid; e < E; e += nt) {
-      s.mask[e] = 0ull;
-      if (skip) s.tmask[e] = 0ull;
-    }
+    const bool small = npairs <= 64;  // the one-wave union (union_wave), else the block's
+    if (!small)
+      for (int e = tid; e < E; e += nt) {
+        s.mask[e] = 0ull;
+        if (skip) s.tmask[e] = 0ull;
+      }
     if constexpr (PRESEL) {
       for (int idx = tid; idx < npairs; idx += nt) {
         s.sel[idx] = min(max(a.tsel[idx], 0), E - 1);
@@ -378,7 +463,14 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
     }
     if (skip && tid < nres) s.res[tid] = resw;
     __syncthreads();
-    union_block<NT>(a, s, npairs, skip, nu, ni);
+    if (small) {
+      if (wave == 0) union_wave(a, s, npairs, skip);
+      __syncthreads();
+      nu = s.nu;
+      ni = s.ni;
+    } else {
+      union_block<NT>(a, s, npairs, skip, nu, ni);
+    }
   }
   if (!publish) return;
 
