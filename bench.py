@@ -459,8 +459,9 @@ def exact_rounds(cfg, layer, acts, torch, np, MoeRound):
 def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
     """Copy-heavy wide verify (T = 16, 32, 64 independent rows, same layer shape): round latency,
     per-kernel time, unique experts and bytes, with the default (the integer-dot GEMV for every work
-    item) and with the int8 matrix-core gate/up tile for items of 3+ rows; the round's useful expert
-    flops (2 T k 3 H I) against the dense bf16 matrix peak."""
+    item) and with the int8 matrix-core tiles (gate/up and down) for items of 3+ rows; the round's
+    useful expert flops (2 T k 3 H I) against the dense bf16 matrix peak, and the useful operations the
+    tiles carried against the dense int8 peak."""
     cfg = synth.config("wide")
     reps = [layer] + [layer.clone() for _ in range(3)]  # 4 x 503 MB: beyond the 256 MB cache
     res = {}
@@ -486,11 +487,11 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
                 h.run(xs[r], cfg.k, out)
                 uniq, offs, _ = h.worklist(0)
                 nus.append(len(uniq))
-                for npr in np.diff(offs):  # items of <= 4 rows; those with >= 3 rows take the tile
+                for npr in np.diff(offs):  # items of <= 4 rows; those with >= 3 rows take the tiles
                     for it in range(0, int(npr), 4):
                         rows = min(4, int(npr) - it)
-                        if mfma > 0 and rows >= mfma:
-                            mfma_ops += 2.0 * 2 * cfg.I * cfg.H * rows
+                        if mfma > 0 and rows >= mfma:  # gate, up and down on the matrix cores
+                            mfma_ops += 2.0 * 3 * cfg.I * cfg.H * rows
             kms, runs = np.zeros(5), 0
             for h in hs:
                 ms, n = h.profile_read()
@@ -511,7 +512,9 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
             useful = 2.0 * T * cfg.k * 3 * cfg.H * cfg.I   # the round's expert multiply-adds x 2
             row[name]["useful_TFLOPs_round"] = round(useful / med / 1e6, 2)
             row[name]["useful_frac_of_bf16_peak"] = round(useful / (med * 1e-6) / BF16_DENSE_PEAK_FLOPS, 5)
-            row[name]["mfma_tile_ops_per_round"] = mfma_ops / 16
+            tile_ops = mfma_ops / 16  # per round (16 rounds counted above)
+            row[name]["mfma_tile_useful_ops_per_round"] = tile_ops
+            row[name]["mfma_tile_frac_of_int8_peak"] = round(tile_ops / (med * 1e-6) / INT8_DENSE_PEAK_OPS, 6)
         res[str(T)] = row
     del reps
     torch.cuda.empty_cache()

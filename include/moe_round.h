@@ -127,9 +127,10 @@ typedef struct moe_round_config {
   int32_t rows_per_item;  /* rows of one expert per GEMV work item; default 2 for rounds
                              under 16 rows, 4 from 16 rows; 1..64                          */
   int32_t mfma_min_rows;  /* rounds of 16+ rows: work items with at least this many rows
-                             use the int8 matrix-core gate/up tile; default -1 = never (the
-                             integer-dot GEMV measured faster at the rows per expert wide
-                             verify rounds produce), 1..64 = from that many rows            */
+                             use the int8 matrix-core tiles of gate/up (H = 2048) and down
+                             (I = 512); default -1 = never (the integer-dot GEMVs measured
+                             faster at the rows per expert wide verify rounds produce),
+                             1..64 = from that many rows                                    */
   int32_t exact;          /* 1: fixed-order combine. The down stage stores each (row, rank)
                              product W_d h and a combine kernel adds them to the residual in
                              rank order: results are bitwise reproducible, and a row's output

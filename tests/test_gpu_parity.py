@@ -142,6 +142,31 @@ def test_gateup_stage(name, T, tiny, verify):
     g.close()
 
 
+@pytest.mark.parametrize("T,mfma_min_rows", [(3, 0), (16, -1), (16, 1), (40, 1), (64, 2)])
+def test_down_stage(verify, T, mfma_min_rows):
+    """The down stage alone, on the GPU's own SwiGLU rows: each output row equals sum_j p_j W_d h_(t,j)
+    with h read back from the gate/up stage (so the check does not depend on gate/up's rounding).
+    Covers the down GEMV and, in wide rounds with the matrix-core tiles on, the down tile (items of at
+    least mfma_min_rows rows)."""
+    cfg, layer, view = verify
+    say(f"case down stage T={T} mfma_min_rows={mfma_min_rows}")
+    wide = synth.config("wide")
+    g = GpuRound([layer], cfg, max_rows=64, mfma_min_rows=mfma_min_rows)
+    X = synth.make_activations(wide if T >= 16 else cfg, T, seed=12, round_idx=T, device=DEV)
+    out, ids, rw, _ = g.run(X)
+    h = g.h.swiglu_rows(T, cfg.k).astype(np.float64)
+    _, _, pairs = g.h.worklist(0)
+    cache = {}
+    ref = np.zeros((T, cfg.H), dtype=np.float64)
+    for p, (t, j) in enumerate(pairs):
+        e = int(ids[0, t, j])
+        if e not in cache:
+            cache[e] = oracle.dequantize(view["down_q"][e], view["down_sm"][e])
+        ref[t] += float(rw[0, t, j]) * (cache[e] @ h[p])
+    assert_close(out, ref, f"down stage T={T} mfma {mfma_min_rows}")
+    g.close()
+
+
 def test_rows_are_independent(verify):
     """A row's output does not depend on the other rows of the round (within fp32 rounding)."""
     cfg, layer, _ = verify

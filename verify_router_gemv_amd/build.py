@@ -31,7 +31,8 @@ FLAGS = [
 # into the accumulators on the vector ALUs: with the results in ordinary VGPRs (not accumulation
 # registers) that costs no register-to-register copies. Its other matrix-core kernel (the fp64
 # router GEMM) only stores its results.
-SOURCE_FLAGS = {"moe_round.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"moe_round.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "moe_gemv_g16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}  # the down tile's results fold on VALU
 
 
 def hipcc() -> str:

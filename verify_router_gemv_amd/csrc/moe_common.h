@@ -46,6 +46,9 @@ constexpr int kRecRowWord = 4;
 // d1*256 + d0). Words [digit d][group g of 8][even/odd]: the even word packs elements 8g+0,2,4,6, the
 // odd word 8g+1,3,5,7, matching the nibble order of a weight code word.
 constexpr int kXqWords = 24;
+// Rounds of at least this many rows are "wide": gate/up stages the input digits in LDS, and both
+// GEMVs may use their matrix-core tiles.
+constexpr int kWideRows = 16;
 constexpr float kXqMax = 8355711.0f;  // 127*65536 + 127*256 + 127
 constexpr int kXStageMax = 8;        // SwiGLU rows the down kernel stages in LDS as digits at a time ...
 constexpr int kXStageBytes = 65536;  // ... within 64 KB of LDS

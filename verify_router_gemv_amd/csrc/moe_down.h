@@ -66,12 +66,109 @@ __device__ __forceinline__ void stage_digits(const float* src, int K, int n, uin
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Matrix-core tile of the down projection (I = 512: 16 blocks of 32 per row), wide rounds.
+//
+// Wave w of the block takes output rows row0 + 16w .. +15 over the whole reduction, so no partial
+// sums meet in LDS: per 32-weight block, v_mfma_i32_16x16x32_i8 multiplies A = the 16 rows' codes as
+// bytes with B = one digit plane of up to 16 staged SwiGLU rows (the chunk's rows; spare columns
+// repeat a staged row and are dropped), three planes per block, folded per block like the GEMV:
+// s * step * (65536 D2 + 256 D1 + D0) + m * sum(h). Lane layouts as in the gate/up tile: lane
+// (r, q) = (l % 16, l / 16) holds row / column r, elements 8q..8q+7 of a block in A and B, and
+// rows 4q..4q+3 of column r in D. The codes arrive as whole 16-byte blocks per lane and are
+// transposed across the lane groups; the rows' (s, m) go through a per-wave table in LDS.
+// ------------------------------------------------------------------------------------------
+constexpr int kDownTileBlocks = 16;                             // I / 32 of the tile
+constexpr int kDownTileSmWords = kDownTileBlocks * 16 * 2;      // per wave: [block][row] (s, m)
+constexpr int kDownTileExtraWords = kWaves * kDownTileSmWords;
+
+template <bool EXACT>
+__device__ __forceinline__ void down_mfma_tile(const Args& a, int layer, const ExpertWork& wk, const ExpertPtrs& W,
+                                               int row0, uint32_t* dig, float2* ss, int xst, float* sm_all,
+                                               float4 h0) {
+  const int H = a.H, I = a.I, T = a.T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int hrow = row0 + wave * 16 + r;                       // this lane's code row
+  const size_t rr = static_cast<size_t>(min(hrow, H - 1));
+  uint4 cd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cd[j] = load_stream_u4(W.dq + rr * (I / 2) + 16 * (4 * j + q));
+  const uint4 smw = load_stream_u4(W.ds + rr * (I / 32) + 4 * q);
+  float* sm_lds = sm_all + wave * kDownTileSmWords;
+  {
+    const uint32_t wv[4] = {smw.x, smw.y, smw.z, smw.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<f32x2*>(sm_lds + ((4 * q + c) * 16 + r) * 2) =
+          f32x2{half_bits_to_float(wv[c]), half_bits_to_float(wv[c] >> 16)};
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) transpose_groups(cd[j]);
+
+  const float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
+  const Ingress in = get_ingress(a);
+  float* __restrict__ xn = layer_output(a, in, layer);
+  for (int s0 = 0; s0 < wk.np; s0 += xst) {
+    const int ns = min(xst, wk.np - s0);
+    if (s0 > 0) __syncthreads();  // the previous chunk has been read by every wave
+    const float* hsrc = a.hbuf + static_cast<size_t>(wk.p0 + s0) * I;
+    stage_digits(hsrc, I, ns, dig, ss, s0 == 0 ? h0 : stage_load(hsrc, I, ns, 0));
+    __syncthreads();  // (also: the (s, m) table written)
+    const int col = min(r, ns - 1);  // B column r: staged row r of the chunk
+    const uint32_t* bsrc = dig + static_cast<size_t>(col) * kDownTileBlocks * kXqWords + 2 * q;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int bs = 0; bs < kDownTileBlocks; ++bs) {
+      uint64_t dg[3];
+#pragma unroll
+      for (int d = 0; d < 3; ++d) dg[d] = *reinterpret_cast<const uint64_t*>(bsrc + bs * kXqWords + d * 8);
+      const float2 sx = ss[col * kDownTileBlocks + bs];
+      const uint4& wq = cd[bs >> 2];
+      const uint32_t ww = (bs & 3) == 0 ? wq.x : (bs & 3) == 1 ? wq.y : (bs & 3) == 2 ? wq.z : wq.w;
+      const long av = static_cast<long>(code_bytes64(ww));
+      const i32x4 z = {0, 0, 0, 0};
+      const i32x4 d0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, static_cast<long>(dg[0]), z, 0, 0, 0);
+      const i32x4 d1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, static_cast<long>(dg[1]), z, 0, 0, 0);
+      const i32x4 d2 = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, static_cast<long>(dg[2]), z, 0, 0, 0);
+      const float* sp = sm_lds + (bs * 16 + 4 * q) * 2;
+      const f32x4 s0v = *reinterpret_cast<const f32x4*>(sp), s1v = *reinterpret_cast<const f32x4*>(sp + 4);
+      acc[0] = fold_block(d0, d1, d2, 0, s0v.x * sx.x, s0v.y, sx.y, acc[0]);
+      acc[1] = fold_block(d0, d1, d2, 1, s0v.z * sx.x, s0v.w, sx.y, acc[1]);
+      acc[2] = fold_block(d0, d1, d2, 2, s1v.x * sx.x, s1v.y, sx.y, acc[2]);
+      acc[3] = fold_block(d0, d1, d2, 3, s1v.z * sx.x, s1v.w, sx.y, acc[3]);
+    }
+    if (r < ns) {  // column r is pair slot s0 + r of the item
+      const int slot = s0 + r;
+      if constexpr (EXACT) {
+        float* y = a.ybuf + static_cast<size_t>(wk.p0 + slot) * H;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int hr = row0 + wave * 16 + 4 * q + i;
+          if (hr < H) y[hr] = acc[i];
+        }
+      } else {
+        const int t = work_row(wk, slot, T);
+        const float wgt = pw[wk.p0 + slot];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int hr = row0 + wave * 16 + 4 * q + i;
+          if (hr < H) atomicAdd(xn + static_cast<size_t>(t) * H + hr, wgt * acc[i]);
+        }
+      }
+    }
+  }
+}
+
 // Down: W_d h for each pair of the work item, the same integer-digit dot product as gate/up: the
 // item's h rows are quantised into LDS (a chunk of a.xstage_i rows at a time), then each lane takes
 // its 32-blocks' digits row by row against its RW weight rows.
 // EXACT: store W_d h of each pair in its slot of ybuf (the combine kernel adds them in rank order)
 // instead of adding the weighted product into the output with an atomic.
-template <int G, int NB, int RW, bool EXACT, int FMT>
+// TILE (G = 16, NB = 1, RW = 4, Q4B32 only; wide rounds with the matrix-core tile enabled): items of at
+// least a.mfma_rows rows take down_mfma_tile. A separate instantiation, so the registers the tile
+// needs do not lower the occupancy of the plain form.
+template <int G, int NB, int RW, bool EXACT, int FMT, bool TILE = false>
 __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   constexpr int RPI = 64 / G;
   constexpr int ROWS_W = RW * RPI;
@@ -86,6 +183,19 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane % G, rs = lane / G;
+  const int xst = a.xstage_i;
+  if constexpr (TILE) {  // 64 rows of H per block, I = 512
+    static_assert(FMT == kFmtQ4B32 && G == 16 && NB == 1 && RW == 4, "the tile's shape");
+    if (a.mfma_rows > 0 && wk.np >= a.mfma_rows) {
+      const ExpertPtrs W = expert_ptrs<FMT>(a, wk.e);
+      const float4 h0 = stage_load(a.hbuf + static_cast<size_t>(wk.p0) * I, I, min(xst, wk.np), 0);
+      float* sm_all = reinterpret_cast<float*>(dlds + static_cast<size_t>(xst) * nblk * (kXqWords + 2));
+      down_mfma_tile<EXACT>(a, layer, wk, W, tile * ROWS_B, dlds,
+                            reinterpret_cast<float2*>(dlds + static_cast<size_t>(xst) * nblk * kXqWords), xst,
+                            sm_all, h0);
+      return;
+    }
+  }
   const float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
   const Ingress in = get_ingress(a);
   float* __restrict__ xn = layer_output(a, in, layer);
@@ -105,7 +215,6 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   // The first chunk's SwiGLU values, loaded before the weights (they return sooner and are needed
   // first: the chunk is quantised into LDS before any weight is used). The scheduling barrier keeps
   // these loads (and the touch) ahead of the weight loads.
-  const int xst = a.xstage_i;
   const float4 h0 = stage_load(a.hbuf + static_cast<size_t>(wk.p0) * I, I, min(xst, wk.np), 0);
   __builtin_amdgcn_sched_barrier(0);
 

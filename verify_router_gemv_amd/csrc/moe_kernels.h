@@ -30,17 +30,20 @@ struct GemvPick {
            : sel == 8 ? gateup_kernel<G, NB, RW, kGuPairs, 8, FMT>
                       : gateup_kernel<G, NB, RW, kGuPairs, 0, FMT>;
   }
-  static KernelFn down(bool exact) {
+  static KernelFn down(bool exact, bool tile) {
+    if constexpr (G == 16 && NB == 1 && RW == 4 && FMT == kFmtQ4B32)
+      if (tile) return exact ? down_kernel<G, NB, RW, true, FMT, true> : down_kernel<G, NB, RW, false, FMT, true>;
     return exact ? down_kernel<G, NB, RW, true, FMT> : down_kernel<G, NB, RW, false, FMT>;
   }
   static constexpr int rows_per_block() { return kWaves * RW * (64 / G); }
 };
 
 // up: the gate/up kernel of form `mode` (kGuOneRow, kGuPairs, kGuStaged) with `sel` keys per lane
-// of a folded selection (0: none); otherwise the down kernel (mode unused), exact mode if sel != 0.
+// of a folded selection (0: none); otherwise the down kernel, exact mode if sel != 0, with the
+// matrix-core tile if mode != 0 (where the shape has one).
 template <int G, int NB, int FMT>
 inline bool pick_form(int mode, bool up, int sel, KernelFn* fn, int* rows) {
-  *fn = up ? GemvPick<G, NB, FMT>::gateup(mode, sel) : GemvPick<G, NB, FMT>::down(sel != 0);
+  *fn = up ? GemvPick<G, NB, FMT>::gateup(mode, sel) : GemvPick<G, NB, FMT>::down(sel != 0, mode != 0);
   *rows = GemvPick<G, NB, FMT>::rows_per_block();
   return true;
 }
@@ -142,9 +145,6 @@ inline KernelFn pick_topk_rows(int E) {
 // Rounds of at least this many rows run the top-k as its own many-block kernel.
 constexpr int kSplitTopkRows = 32;
 
-// Rounds of at least this many rows are "wide": gate/up stages the input digits in LDS and may use
-// the matrix-core tile.
-constexpr int kWideRows = 16;
 // Rounds of at most this many rows fold the selection into the gate/up kernel: every block
 // recomputes it (cheap for a few rows), which saves a launch, its gap and a dependent load.
 constexpr int kFusedMaxRows = 4;

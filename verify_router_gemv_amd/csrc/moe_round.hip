@@ -230,8 +230,11 @@ static bool make_plan(const moe_round* h, int T, int k, RoundPlan* p) {
   int rows_gu = 0, rows_dn = 0;
   const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
   const int fmt = h->cfg.weight_format;
+  // the down tile: wide rounds with the matrix-core tiles enabled, I = 512 (G = 16 x 1 block)
+  const bool down_tile = wide && h->mfma_rows > 0 && !h->cfg.exact && h->Gi == 16 && h->NBi == 1 &&
+                         fmt == MOE_WEIGHT_Q4B32;
   if (!p->lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, p->fused ? fused_select_keys(E) : 0, fmt, &p->gu, &rows_gu) ||
-      !pick_gemv(h->Gi, h->NBi, 0, false, h->cfg.exact, fmt, &p->dn, &rows_dn))
+      !pick_gemv(h->Gi, h->NBi, down_tile ? 1 : 0, false, h->cfg.exact, fmt, &p->dn, &rows_dn))
     return false;
   p->grid_lg = logits_grid(E, H, T);
   const int units_gu = umax * ((I + rows_gu - 1) / rows_gu);
@@ -243,6 +246,7 @@ static bool make_plan(const moe_round* h, int T, int k, RoundPlan* p) {
   if (h->Gh == 64 && h->NBh == 1) gu_words += kMfmaExtraWords;  // matrix-core tile: (s, m) tables, partial sums
   p->shm_gu = wide ? static_cast<int>(sizeof(uint32_t)) * gu_words : 0;
   p->shm_dn = static_cast<int>(sizeof(uint32_t)) * xstage_rows(I) * (I / 32) * (kXqWords + 2);
+  if (down_tile) p->shm_dn += static_cast<int>(sizeof(uint32_t)) * kDownTileExtraWords;  // its (s, m) tables
   return true;
 }
 
