@@ -636,12 +636,22 @@ def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager")
 def launch_costs(torch, np, synth, MoeRound):
     """What launching costs on this GPU, for the design's launch budget: chains of N minimal kernels
     (the byte floor's read kernel over 16 bytes, one block) between two events, and one such kernel
-    alone; medians of 50 timings each."""
+    alone; then chains of 16 one-wave-per-block kernels of B blocks each (B = 1 .. 1024), empty, storing
+    one word per block, or sleeping a fixed time first so that all blocks of a kernel end together:
+    how the time per launch grows with the blocks of the kernel. Medians of 50 timings each."""
     cfg = synth.config("tiny")
     layer = synth.make_layer(cfg, seed=0, layer=0, device="cuda")
     h = MoeRound([layer], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=1, use_graph=False)
     buf = torch.zeros(4, device="cuda")
-    res = {"kernel": "one block reading 16 bytes", "timing": "torch events around the launches"}
+    flags = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    # Half a second of back-to-back launches first, so that the figures do not depend on whether
+    # the GPU was idle (its clocks ramp up under load).
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:
+        h.empty_launches(1024, 64, 4, flags)
+        torch.cuda.synchronize()
+    res = {"kernel": "one block reading 16 bytes", "timing": "torch events around the launches",
+           "warmup": "0.5 s of launches before the first timing"}
     for n in (1, 3, 10, 50):
         def chain():
             for _ in range(n):
@@ -650,6 +660,17 @@ def launch_costs(torch, np, synth, MoeRound):
         lat = [event_us(torch, chain) for _ in range(50)]
         med = float(np.median(lat))
         res[f"chain_{n}"] = {"us_median": round(med, 2), "us_per_launch": round(med / n, 2)}
+    # Chains of 16 one-wave kernels of B blocks: empty; each block storing one word; each block
+    # sleeping ~4 × 2048 clocks first (all blocks of a kernel end together) and then storing.
+    variants = {"empty": (0, None), "store": (0, flags), "sleep_store": (4, flags), "sleep": (4, None)}
+    for name, (su, fl) in variants.items():
+        per_blocks = {}
+        for b in (1, 64, 256, 512, 1024):
+            h.empty_launches(b, 16, su, fl)
+            lat = [event_us(torch, lambda: h.empty_launches(b, 16, su, fl)) for _ in range(50)]
+            per_blocks[str(b)] = round(float(np.median(lat)) / 16, 2)
+        res[f"{name}_kernels_us_per_launch_by_blocks"] = per_blocks
+        res[f"{name}_ns_per_block"] = round((per_blocks["1024"] - per_blocks["1"]) / 1023 * 1e3, 1)
     h.close()
     return res
 

@@ -366,6 +366,21 @@ MOE_ROUND_API moe_status moe_round_floor(moe_round* h);
 MOE_ROUND_API moe_status moe_round_stream_read(moe_round* h, const void* buf, int64_t bytes);
 
 /*
+ * A control measurement of launch costs: `launches` kernels of `blocks` minimal blocks (one wave of
+ * 64 threads each) back to back on the handle's stream (asynchronous). Each wave first sleeps
+ * `sleep_units` times about 2048 shader clocks (0 = not at all), so that the blocks of one kernel
+ * end together; then, when `flags` is not NULL, its first lane stores the block index to
+ * flags[block] (a device buffer of at least `blocks` int32, written, never read). Timed beside the
+ * round it shows what a kernel boundary costs by itself and how that grows with the blocks of the
+ * kernel before it, with and without stores. Passage: "How AlphaInfer makes local decoding fast",
+ * section 7, rule 2 (a same-session control arm).
+ * Errors: MOE_ERR_INVALID_ARG (h NULL, blocks outside 1..65536, launches outside 1..1024,
+ * sleep_units outside 0..64, flags not 4-byte aligned), MOE_ERR_HIP (launch).
+ */
+MOE_ROUND_API moe_status moe_round_empty_launches(moe_round* h, int32_t blocks, int32_t launches,
+                                                  int32_t sleep_units, int32_t* flags);
+
+/*
  * Kernel timing, for measurement ("How AlphaInfer makes local decoding fast", section 7: time
  * uninstrumented, decompose before crediting; the per-kernel times here come from events the runtime
  * stamps with each dispatch's own start and end).  moe_round_profile(h, 1) makes every following run launch its

@@ -28,7 +28,7 @@ def declared():
 def test_header_declares_the_boundary():
     names = declared()
     assert "moe_round_init" in names and "moe_round_run" in names and "moe_round_destroy" in names
-    assert len(names) == 18
+    assert len(names) == 19
     assert {"moe_round_last_stats", "moe_round_floor", "moe_round_stream_read"} <= set(names)
 
 
@@ -221,6 +221,7 @@ def test_new_entry_points_refuse_null_handles(lib):
     assert lib.moe_round_floor(None) == -1
     assert lib.moe_round_layer_input(None, 0, None) == -1
     assert lib.moe_round_stream_read(None, None, 16) == -1
+    assert lib.moe_round_empty_launches(None, 1, 1, 0, None) == -1
 
 
 def test_rejected_layers_keep_the_old_weights_referenced(lib, monkeypatch):

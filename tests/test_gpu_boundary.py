@@ -121,7 +121,8 @@ def test_reductions_without_an_exact_lane_split(H, I):
 
 
 def test_floor_and_stream_read_leave_results_alone(verify):
-    """The measurement calls only read: a round's outputs are the same before and after them."""
+    """The measurement calls leave the round alone: its outputs are the same before and after them;
+    the launch control's store variant writes exactly its blocks' indices."""
     cfg, layer, view = verify
     g = GpuRound([layer], cfg, max_rows=8)
     X = synth.make_activations(cfg, 3, seed=17, round_idx=0, device=DEV)
@@ -130,7 +131,13 @@ def test_floor_and_stream_read_leave_results_alone(verify):
     g.h.floor()
     buf = torch.randn(1 << 20, device=DEV)
     g.h.stream_read(buf)
+    say("case empty launches (plain, storing, sleeping)")
+    flags = torch.full((300,), -1, dtype=torch.int32, device=DEV)
+    g.h.empty_launches(64, 3)
+    g.h.empty_launches(256, 2, 1, flags)
     torch.cuda.synchronize()
+    assert flags[:256].cpu().tolist() == list(range(256))
+    assert (flags[256:] == -1).all().item()
     out2, ids2, _, _ = g.run(X)
     assert np.array_equal(ids1, ids2)
     np.testing.assert_allclose(out1, out2, rtol=1e-5, atol=1e-6)

@@ -87,6 +87,7 @@ def load() -> ctypes.CDLL:
         "moe_round_last_stats": (i32, [vp, P(Stats), P(i32), P(ctypes.c_int64)]),
         "moe_round_floor": (i32, [vp]),
         "moe_round_stream_read": (i32, [vp, vp, ctypes.c_int64]),
+        "moe_round_empty_launches": (i32, [vp, i32, i32, i32, vp]),
         "moe_round_run_noalloc": (i32, [P(Config), P(LayerWeights), vp, i32, i32, vp, vp, vp, vp, P(i32)]),
         "moe_round_bind_experts": (i32, [vp, vp, vp]),
         "moe_round_host_tier_pointer": (i32, [vp, P(vp)]),
@@ -453,6 +454,20 @@ class MoeRound:
                                             buf.numel() * buf.element_size())
         if st != OK:
             self._raise(st, "moe_round_stream_read")
+
+    def empty_launches(self, blocks: int, launches: int = 1, sleep_units: int = 0, flags=None):
+        """Enqueue `launches` kernels of `blocks` one-wave blocks each (a launch-cost control): every
+        wave sleeps `sleep_units` × ~2048 clocks, then stores its block index to `flags` (a device
+        int32 tensor of at least `blocks` elements) when one is given."""
+        fp = None
+        if flags is not None:
+            if (flags.device.type != "cuda" or flags.dtype != torch.int32 or not flags.is_contiguous()
+                    or flags.numel() < blocks):
+                raise ValueError("flags must be a contiguous device int32 tensor of at least `blocks` elements")
+            fp = ctypes.c_void_p(flags.data_ptr())
+        st = self.lib.moe_round_empty_launches(self.h, int(blocks), int(launches), int(sleep_units), fp)
+        if st != OK:
+            self._raise(st, "moe_round_empty_launches")
 
     def last_unique(self):
         arr = (ctypes.c_int32 * self.L)()

@@ -997,6 +997,26 @@ extern "C" moe_status moe_round_stream_read(moe_round* h, const void* buf, int64
   return launch_floor(h, f, static_cast<int>(chunks < (1 << 20) ? chunks : (1 << 20)), 1 << 20);
 }
 
+// One wave per block: an optional fixed sleep (so that all blocks end together), then an optional
+// store of the block index. Bounded, no wait on any other block.
+static __global__ void __launch_bounds__(64) empty_kernel(int sleep_units, int32_t* __restrict__ flags) {
+  for (int i = 0; i < sleep_units; ++i) __builtin_amdgcn_s_sleep(32);
+  if (flags && threadIdx.x == 0) flags[blockIdx.x] = static_cast<int32_t>(blockIdx.x);
+}
+
+extern "C" moe_status moe_round_empty_launches(moe_round* h, int32_t blocks, int32_t launches,
+                                               int32_t sleep_units, int32_t* flags) {
+  if (!h || blocks < 1 || blocks > 65536 || launches < 1 || launches > 1024) return MOE_ERR_INVALID_ARG;
+  if (sleep_units < 0 || sleep_units > 64) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(flags) & 3u) return MOE_ERR_INVALID_ARG;
+  int su = sleep_units;
+  void* params[] = {&su, &flags};
+  for (int i = 0; i < launches; ++i)
+    MOE_HIP(h, hipLaunchKernel(reinterpret_cast<const void*>(empty_kernel), dim3(blocks), dim3(64), params, 0,
+                               h->stream));
+  return MOE_OK;
+}
+
 // ------------------------------------------------------------------------------------------
 // The no-allocation entry point: a decode/verify round whose scratch lives in a fixed device array
 // ------------------------------------------------------------------------------------------
