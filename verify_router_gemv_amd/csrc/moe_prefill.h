@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void pf_topk_kernel(PfArgs a, int layer) 
   const int k = a.k;
   int id;
   float p;
-  topk_row<NPL>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p);
+  topk_row<NPL, kWaves>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p);
   if (lane < k) {
     a.sel[t * k + lane] = id;
     a.selp[t * k + lane] = p;

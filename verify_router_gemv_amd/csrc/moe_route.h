@@ -107,23 +107,47 @@ struct SelectSharedT {
 };
 using SelectShared = SelectSharedT<MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK, kSelectWaves>;
 
-// Top-k of one row on one wave. Each lane sorts its NPL (logit, id) keys once; then each of k
-// rounds takes the largest head over the wave without any round trip through scalar registers: a
-// wave max of the heads' high words (sign, exponent and 20 mantissa bits), then of the low words
-// of the heads holding that high word (the low bits carry the id, so the winner is unique). The
-// lane owning the winner pops its head and lane j keeps the j-th id. The exact fp64 logits of the
+// Top-k of one row on one wave (of NW waves in the block). Each lane sorts its NPL (logit, id) keys
+// once and parks them in LDS, keeping its largest (the head) and the next one in registers. Each of
+// the k rounds then takes the largest head over the wave: a wave max of the heads' high words (sign,
+// exponent and 20 mantissa bits), and only when several lanes hold that high word (a ballot tells)
+// a second one over their low words (the low bits carry the id, so the winner is unique). The
+// winner lane's next key becomes its head and every lane re-reads its next key from LDS, a read
+// whose latency the following round hides. Lane j keeps the j-th id. The exact fp64 logits of the
 // k ids come from their owner lanes once, after the rounds, for the softmax over the k selected.
-// Lane j < k ends with rank j's id and routing weight.
-template <int NPL>
+// With E even the row is read 16 bytes per lane (slot i of lane l holds expert 128 (i / 2) + 2 l +
+// i % 2), else 8 bytes (expert l + 64 i). Lane j < k ends with rank j's id and routing weight.
+template <int NPL, int NW>
 __device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& id_out, float& p_out) {
-  const int lane = threadIdx.x & 63;
+  // Per wave: the lanes' sorted keys by rank (row r holds every lane's r-th largest), then two
+  // rows of zeros, below every real key, for lanes that run out.
+  __shared__ uint64_t lst[NW][NPL + 2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr bool kPairs = NPL % 2 == 0;
+  const bool paired = kPairs && (E & 1) == 0;
   double z[NPL];
   uint64_t key[NPL];
+  if (paired) {
+    const double2* z2 = reinterpret_cast<const double2*>(zrow);
+    const int n2 = E >> 1;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    z[i] = zrow[min(e, E - 1)];  // all loads issued together
-    key[i] = e < E ? logit_key(z[i], e) : 0ull;  // 0 is below every real key
+    for (int i = 0; i < NPL / 2; ++i) {
+      const double2 v = z2[min(lane + 64 * i, n2 - 1)];  // all loads issued together
+      z[2 * i] = v.x;
+      z[2 * i + 1] = v.y;
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = 128 * (i >> 1) + 2 * lane + (i & 1);
+      key[i] = logit_key(z[i], e) & (e < E ? ~0ull : 0ull);  // 0 is below every real key
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      z[i] = zrow[min(e, E - 1)];
+      key[i] = logit_key(z[i], e) & (e < E ? ~0ull : 0ull);
+    }
   }
 #pragma unroll
   for (int pass = 0; pass < NPL; ++pass)
@@ -134,21 +158,36 @@ __device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& 
         key[i] = key[i + 1];
         key[i + 1] = tmp;
       }
+  MOE_LDS uint64_t* mine = (MOE_LDS uint64_t*)&lst[wave][0][lane];  // rank r at mine[64 r]
+#pragma unroll
+  for (int i = 1; i < NPL; ++i) mine[64 * i] = key[i];
+  mine[64 * NPL] = 0ull;
+  mine[64 * (NPL + 1)] = 0ull;
+  uint64_t head = key[0];
+  uint64_t nxt = NPL > 1 ? key[NPL > 1 ? 1 : 0] : 0ull;
+  int c = 1;  // rank of nxt in this lane's list
   int myid = 0;
   for (int j = 0; j < k; ++j) {
-    const uint32_t hi = static_cast<uint32_t>(key[0] >> 32);
-    const uint32_t mhi = wave_max_u32(hi);
-    const uint32_t mlo = wave_max_u32(hi == mhi ? static_cast<uint32_t>(key[0]) : 0u);
-    const int e = key_expert(mlo);
-    if (lane == (e & 63)) {
-#pragma unroll
-      for (int i = 0; i + 1 < NPL; ++i) key[i] = key[i + 1];
-      key[NPL - 1] = 0ull;
+    const uint32_t hh = static_cast<uint32_t>(head >> 32), hl = static_cast<uint32_t>(head);
+    const uint32_t mhi = wave_max_u32(hh);
+    const uint64_t tie = __ballot(hh == mhi);
+    int w;
+    if (__popcll(tie) == 1) {
+      w = __builtin_ctzll(tie);
+    } else {
+      const uint32_t mlo = wave_max_u32(hh == mhi ? hl : 0u);
+      w = __builtin_ctzll(__ballot(hh == mhi && hl == mlo));
     }
+    const int e = key_expert(__builtin_amdgcn_readlane(hl, w));
     if (lane == j) myid = e;
+    const bool pop = lane == w;
+    head = pop ? nxt : head;
+    c += pop ? 1 : 0;  // at most NPL + 1: a lane whose head is 0 never wins again
+    nxt = mine[64 * c];
   }
-  // Lane j < k: the logit of its id, from register slot id / 64 of lane id % 64.
-  const int own = myid & 63, slot = myid >> 6;
+  // Lane j < k: the logit of its id, from the register slot and lane that loaded it.
+  const int own = paired ? (myid & 127) >> 1 : myid & 63;
+  const int slot = paired ? 2 * (myid >> 7) + (myid & 1) : myid >> 6;
   double myz = 0.0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
@@ -163,14 +202,14 @@ __device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& 
 }
 
 // Top-k of row t into the selection state in LDS.
-template <int NPL, typename SS>
+template <int NPL, int NW, typename SS>
 __device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
   const int lane = threadIdx.x & 63;
   const int k = a.k;
   const int slot = t * k + lane;
   int id;
   float p;
-  topk_row<NPL>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p);
+  topk_row<NPL, NW>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p);
   if (lane < k) {
     s.sel[slot] = id;
     s.p[slot] = p;
@@ -409,7 +448,7 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
     // so one wave ranks them (ascending expert id) and writes the worklist directly. With the tail
     // skip an expert is skipped exactly when its one pair is a tail pair.
     if (wave == 0) {
-      select_row<NPL>(a, s, 0);
+      select_row<NPL, NT / 64>(a, s, 0);
       const int j = min(lane, k - 1);
       const int id = s.sel[j];
       bool keep = true;
@@ -459,7 +498,7 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
         s.p[idx] = a.tp[idx];
       }
     } else {
-      for (int t = wave; t < T; t += nw) select_row<NPL>(a, s, t);
+      for (int t = wave; t < T; t += nw) select_row<NPL, NT / 64>(a, s, t);
     }
     if (skip && tid < nres) s.res[tid] = resw;
     __syncthreads();
@@ -542,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Args a, int layer) 
   const int k = a.k;
   int id;
   float p;
-  topk_row<NPL>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p);
+  topk_row<NPL, kWaves>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p);
   if (lane < k) {
     a.tsel[t * k + lane] = id;
     a.tp[t * k + lane] = p;
