@@ -338,33 +338,40 @@ __device__ __forceinline__ void union_block(const Args& a, SS& s, int npairs, bo
   __syncthreads();
 }
 
-// The value of lane (lane ^ stride), stride a power of two below 64 (constant after unrolling).
+// The value of lane (lane ^ stride), stride a power of two below 64 (constant after unrolling), on
+// VALU only: xor 4 and xor 8 are two DPP moves each (lane ^ 3 then the 8-lane mirror lane ^ 7;
+// lane ^ 7 then the 16-lane mirror lane ^ 15), the upper strides the permlane swaps.
 __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int stride) {
+  constexpr int kDppRev4 = 0x1B;  // quad_perm [3,2,1,0]: lane ^ 3
   switch (stride) {
     case 1: return dpp_u32<kDppXor1>(v);
     case 2: return dpp_u32<kDppXor2>(v);
-    case 4: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x1F | (4 << 10)));
-    case 8: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x1F | (8 << 10)));
+    case 4: return dpp_u32<kDppHalfMirror>(dpp_u32<kDppRev4>(v));
+    case 8: return dpp_u32<kDppMirror>(dpp_u32<kDppHalfMirror>(v));
     case 16: return swap_partner_u32<false>(v);
     default: return swap_partner_u32<true>(v);
   }
 }
 __device__ __forceinline__ uint64_t low_bits(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
 
+// floor(n / d) for 0 <= n < 128 and 1 <= d <= 64 through one fp32 reciprocal: n / d is at least
+// 1 / (2 d) away from the next integer, far beyond the reciprocal's error.
+__device__ __forceinline__ int small_div(int n, float rcp_d) {
+  return static_cast<int>((static_cast<float>(n) + 0.5f) * rcp_d);
+}
+
 // The union of a round of at most 64 (row, rank) pairs by one wave (s.sel written; with `skip`,
-// s.res written), the same worklist as union_block: lane i takes pair i as the key expert | row |
-// rank, a bitonic network sorts the 64 keys across the lanes in registers (ascending, so by expert,
-// then row), and runs of equal experts become the unique experts, their offsets and work items
-// through ballots. With the tail skip a run is kept when any of its pairs is not a tail pair.
+// s.res written), the same worklist as union_block: lane i takes pair i = t k + j as the key
+// expert | i, a bitonic network sorts the 64 keys across the lanes in registers (ascending, so by
+// expert, then row, then rank), and runs of equal experts become the unique experts, their
+// offsets and work items through ballots: the kept pairs at run positions 0, rg, 2 rg, ... start
+// the work items. With the tail skip a run is kept when any of its pairs is not a tail pair.
 template <typename SS>
 __device__ __forceinline__ void union_wave(const Args& a, SS& s, int npairs, bool skip) {
   const int lane = threadIdx.x & 63;
   const int k = a.k, rg = a.rg;
   uint32_t key = 0xFFFFFFFFu;  // past the pairs: sorts last
-  if (lane < npairs) {
-    const int t = lane / k;
-    key = (static_cast<uint32_t>(s.sel[lane]) << 10) | static_cast<uint32_t>(t << 4) | static_cast<uint32_t>(lane - t * k);
-  }
+  if (lane < npairs) key = (static_cast<uint32_t>(s.sel[lane]) << 6) | static_cast<uint32_t>(lane);
 #pragma unroll
   for (int size = 2; size <= 64; size <<= 1)
 #pragma unroll
@@ -374,16 +381,17 @@ __device__ __forceinline__ void union_wave(const Args& a, SS& s, int npairs, boo
       key = keep_min ? min(key, other) : max(key, other);
     }
   const bool valid = lane < npairs;
-  const int e = static_cast<int>(key >> 10), t = static_cast<int>((key >> 4) & 63), j = static_cast<int>(key & 15);
-  const uint32_t prev = static_cast<uint32_t>(__shfl_up(static_cast<int>(key), 1, 64));
-  const bool head = valid && (lane == 0 || (prev >> 10) != (key >> 10));
+  const int e = static_cast<int>(key >> 6), pi = static_cast<int>(key & 63);
+  const int t = small_div(pi, __builtin_amdgcn_rcpf(static_cast<float>(k))), j = pi - t * k;
+  constexpr int kDppWaveShr1 = 0x138;  // lane i takes lane i - 1 (lane 0 keeps `old`)
+  const uint32_t prev = __builtin_amdgcn_update_dpp(0xFFFFFFFFu, key, kDppWaveShr1, 0xF, 0xF, false);
+  const bool head = valid && (lane == 0 || (prev >> 6) != (key >> 6));
   const uint64_t heads = __ballot(head);
-  const uint64_t upto = low_bits(lane + 1);
-  const uint64_t above = heads & ~upto;
-  const int next = above ? __builtin_ctzll(above) : npairs;      // end of this lane's run
-  const int first = 63 - __builtin_clzll((heads & upto) | 1ull);  // start of this lane's run
+  const int first = 63 - __builtin_clzll((heads & low_bits(lane + 1)) | 1ull);  // start of this lane's run
   bool kept = valid;
   if (skip) {
+    const uint64_t above = heads & ~low_bits(lane + 1);
+    const int next = above ? __builtin_ctzll(above) : npairs;  // end of this lane's run
     const bool nt = valid && !tail_pair(a, s, j, e);
     const uint64_t nts = __ballot(nt);
     kept = valid && (nts & low_bits(next) & ~low_bits(first)) != 0ull;
@@ -391,30 +399,26 @@ __device__ __forceinline__ void union_wave(const Args& a, SS& s, int npairs, boo
   const uint64_t keptm = __ballot(kept);
   const bool khead = kept && head;
   const uint64_t kheads = __ballot(khead);
-  const int below = static_cast<int>(__popcll(keptm & low_bits(lane)));  // slot among the kept pairs
-  const int u = static_cast<int>(__popcll(kheads & upto)) - 1;
-  const int ngs = khead ? (next - lane + rg - 1) / rg : 0;  // work items of this expert
-  int io = 0, ni = 0;
-#pragma unroll
-  for (int b = 0; b < 7; ++b) {
-    const uint64_t m = __ballot((ngs >> b) & 1);
-    io += static_cast<int>(__popcll(m & low_bits(lane))) << b;
-    ni += static_cast<int>(__popcll(m)) << b;
-  }
+  const int below = mbcnt64(keptm);                      // slot among the kept pairs
+  const int u = mbcnt64(kheads) + (khead ? 1 : 0) - 1;   // this lane's expert among the kept ones
+  const int pos = lane - first;
+  const bool starter = kept && pos == small_div(pos, __builtin_amdgcn_rcpf(static_cast<float>(rg))) * rg;
+  const uint64_t starters = __ballot(starter);
+  const int item = mbcnt64(starters);
   if (khead) {
     s.uniq[u] = e;
     s.offs[u] = below;
-    s.ioffs[u] = io;
-    for (int g = 0; g < ngs; ++g) s.item_u[io + g] = u;
+    s.ioffs[u] = item;
   }
+  if (starter) s.item_u[item] = u;
   if (valid) {
-    s.slot[t * k + j] = kept ? below : -1;
+    s.slot[pi] = kept ? below : -1;
     if (kept) s.pairs[below] = t | (j << 8);
   }
   if (lane == 0) {
     const int nu = static_cast<int>(__popcll(kheads)), kept_n = static_cast<int>(__popcll(keptm));
     s.nu = min(nu, a.Ucap);
-    s.ni = min(ni, a.Icap);
+    s.ni = min(static_cast<int>(__popcll(starters)), a.Icap);
     s.np = kept_n;
     s.nskip = static_cast<int>(__popcll(heads)) - nu;
     s.offs[min(nu, a.Ucap)] = kept_n;
