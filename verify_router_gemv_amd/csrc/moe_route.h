@@ -107,6 +107,34 @@ struct SelectSharedT {
 };
 using SelectShared = SelectSharedT<MOE_ROUND_MAX_ROWS * MOE_ROUND_MAX_TOPK, kSelectWaves>;
 
+// Sorts n keys in registers, largest first: the 5- and 19-comparator networks for 4 and 8 keys
+// (both checked on every 0/1 input), odd-even transposition otherwise.
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&key)[N]) {
+  auto cx = [&](int i, int j) {
+    const uint64_t a = key[i], b = key[j];
+    key[i] = a < b ? b : a;
+    key[j] = a < b ? a : b;
+  };
+  if constexpr (N == 8) {
+    cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+    cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+    cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+    cx(2, 4); cx(3, 5);
+    cx(1, 4); cx(3, 6);
+    cx(1, 2); cx(3, 4); cx(5, 6);
+  } else if constexpr (N == 4) {
+    cx(0, 1); cx(2, 3);
+    cx(0, 2); cx(1, 3);
+    cx(1, 2);
+  } else {
+#pragma unroll
+    for (int pass = 0; pass < N; ++pass)
+#pragma unroll
+      for (int i = pass & 1; i + 1 < N; i += 2) cx(i, i + 1);
+  }
+}
+
 // Top-k of one row on one wave (of NW waves in the block). Each lane sorts its NPL (logit, id) keys
 // once and parks them in LDS, keeping its largest (the head) and the next one in registers. Each of
 // the k rounds then takes the largest head over the wave: a wave max of the heads' high words (sign,
@@ -149,15 +177,7 @@ __device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& 
       key[i] = logit_key(z[i], e) & (e < E ? ~0ull : 0ull);
     }
   }
-#pragma unroll
-  for (int pass = 0; pass < NPL; ++pass)
-#pragma unroll
-    for (int i = pass & 1; i + 1 < NPL; i += 2)
-      if (key[i] < key[i + 1]) {
-        const uint64_t tmp = key[i];
-        key[i] = key[i + 1];
-        key[i + 1] = tmp;
-      }
+  sort_desc<NPL>(key);
   MOE_LDS uint64_t* mine = (MOE_LDS uint64_t*)&lst[wave][0][lane];  // rank r at mine[64 r]
 #pragma unroll
   for (int i = 1; i < NPL; ++i) mine[64 * i] = key[i];
@@ -185,15 +205,13 @@ __device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& 
     c += pop ? 1 : 0;  // at most NPL + 1: a lane whose head is 0 never wins again
     nxt = mine[64 * c];
   }
-  // Lane j < k: the logit of its id, from the register slot and lane that loaded it.
+  // Lane j < k: the logit of its id, from the register slot and lane that loaded it, through the
+  // wave's list rows (free now; LDS operations of one wave complete in order).
   const int own = paired ? (myid & 127) >> 1 : myid & 63;
   const int slot = paired ? 2 * (myid >> 7) + (myid & 1) : myid >> 6;
-  double myz = 0.0;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const double zi = __shfl(z[i], own, 64);
-    if (slot == i) myz = zi;
-  }
+  for (int i = 0; i < NPL; ++i) mine[64 * i] = __builtin_bit_cast(uint64_t, z[i]);
+  const double myz = __builtin_bit_cast(double, ((MOE_LDS uint64_t*)&lst[wave][0][0])[64 * slot + own]);
   const double z0 = __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, myz), 0));
   const double ej = lane < k ? exp(myz - z0) : 0.0;  // rank 0 holds the largest selected logit
   const double sum = wave_sum_f64(ej);
