@@ -146,7 +146,8 @@ __device__ __forceinline__ void sort_desc(uint64_t (&key)[N]) {
 // With E even the row is read 16 bytes per lane (slot i of lane l holds expert 128 (i / 2) + 2 l +
 // i % 2), else 8 bytes (expert l + 64 i). Lane j < k ends with rank j's id and routing weight.
 template <int NPL, int NW>
-__device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& id_out, float& p_out) {
+__device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& id_out, float& p_out,
+                                         bool need_p = true) {
   // Per wave: the lanes' sorted keys by rank (row r holds every lane's r-th largest), then two
   // rows of zeros, below every real key, for lanes that run out.
   __shared__ uint64_t lst[NW][NPL + 2][64];
@@ -205,6 +206,9 @@ __device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& 
     c += pop ? 1 : 0;  // at most NPL + 1: a lane whose head is 0 never wins again
     nxt = mine[64 * c];
   }
+  id_out = myid;
+  p_out = 0.f;
+  if (!need_p) return;  // callers that use only the ids skip the softmax
   // Lane j < k: the logit of its id, from the register slot and lane that loaded it, through the
   // wave's list rows (free now; LDS operations of one wave complete in order).
   const int own = paired ? (myid & 127) >> 1 : myid & 63;
@@ -215,19 +219,18 @@ __device__ __forceinline__ void topk_row(const double* zrow, int E, int k, int& 
   const double z0 = __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, myz), 0));
   const double ej = lane < k ? exp(myz - z0) : 0.0;  // rank 0 holds the largest selected logit
   const double sum = wave_sum_f64(ej);
-  id_out = myid;
   p_out = static_cast<float>(ej / sum);
 }
 
 // Top-k of row t into the selection state in LDS.
 template <int NPL, int NW, typename SS>
-__device__ __forceinline__ void select_row(const Args& a, SS& s, int t) {
+__device__ __forceinline__ void select_row(const Args& a, SS& s, int t, bool need_p) {
   const int lane = threadIdx.x & 63;
   const int k = a.k;
   const int slot = t * k + lane;
   int id;
   float p;
-  topk_row<NPL, NW>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p);
+  topk_row<NPL, NW>(a.logits + static_cast<size_t>(t) * a.E, a.E, k, id, p, need_p);
   if (lane < k) {
     s.sel[slot] = id;
     s.p[slot] = p;
@@ -470,7 +473,7 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
     // so one wave ranks them (ascending expert id) and writes the worklist directly. With the tail
     // skip an expert is skipped exactly when its one pair is a tail pair.
     if (wave == 0) {
-      select_row<NPL, NT / 64>(a, s, 0);
+      select_row<NPL, NT / 64>(a, s, 0, publish);
       const int j = min(lane, k - 1);
       const int id = s.sel[j];
       bool keep = true;
@@ -520,7 +523,7 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
         s.p[idx] = a.tp[idx];
       }
     } else {
-      for (int t = wave; t < T; t += nw) select_row<NPL, NT / 64>(a, s, t);
+      for (int t = wave; t < T; t += nw) select_row<NPL, NT / 64>(a, s, t, publish);
     }
     if (skip && tid < nres) s.res[tid] = resw;
     __syncthreads();
