@@ -8,10 +8,9 @@ namespace moe {
 // Gate/up: integer dot products of the 4-bit codes with the int8 digits of the layer input.
 // Codes unpack into bytes (even / odd elements of each 8-group, two VALU per word); each row
 // routed to the expert then costs 24 v_dot4 per 32-weight block plus the fp32 fold
-// s * step * (65536 A2 + 256 A1 + A0) + m * sum(x).
-template <typename BS>
-__device__ __forceinline__ float block_dot_q8(const uint32_t cw[8], const uint32_t xd[kXqWords], float step,
-                                              float xsum, const BS& sm, float acc) {
+// s * step * (65536 A2 + 256 A1 + A0) + m * sum(x). A0 + 256 A1 is formed as an integer: each
+// plane's sum is at most 32 * 15 * 127 in magnitude, so it stays below 2^24 and converts exactly.
+__device__ __forceinline__ float block_dot(const uint32_t cw[8], const uint32_t xd[kXqWords]) {
   int A[3] = {0, 0, 0};
 #pragma unroll
   for (int dg = 0; dg < 3; ++dg)
@@ -21,9 +20,16 @@ __device__ __forceinline__ float block_dot_q8(const uint32_t cw[8], const uint32
       A[dg] = __builtin_amdgcn_sdot4(static_cast<int>(cw[2 * g + 1]), static_cast<int>(xd[(dg * 4 + g) * 2 + 1]),
                                      A[dg], false);
     }
-  const float dot = fmaf(static_cast<float>(A[2]), 65536.f, fmaf(static_cast<float>(A[1]), 256.f, static_cast<float>(A[0])));
-  const float sc = sm.scale(), mn = sm.minv();
+  return fmaf(static_cast<float>(A[2]), 65536.f, static_cast<float>(A[0] + A[1] * 256));
+}
+// The fold of one block: acc + s * step * dot + m * sum(x), with the block's scale s and minimum m.
+__device__ __forceinline__ float block_fold(float dot, float sc, float mn, float step, float xsum, float acc) {
   return fmaf(sc * step, dot, fmaf(mn, xsum, acc));
+}
+template <typename BS>
+__device__ __forceinline__ float block_dot_q8(const uint32_t cw[8], const uint32_t xd[kXqWords], float step,
+                                              float xsum, const BS& sm, float acc) {
+  return block_fold(block_dot(cw, xd), sm.scale(), sm.minv(), step, xsum, acc);
 }
 
 __device__ __forceinline__ void unpack_bytes(const uint4 c, uint32_t cw[8]) {
