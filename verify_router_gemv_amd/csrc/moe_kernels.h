@@ -146,8 +146,10 @@ inline KernelFn pick_topk_rows(int E) {
 constexpr int kSplitTopkRows = 32;
 
 // Rounds of at most this many rows fold the selection into the gate/up kernel: every block
-// recomputes it (cheap for a few rows), which saves a launch, its gap and a dependent load.
-constexpr int kFusedMaxRows = 4;
+// recomputes it (cheap for a few rows), which saves a launch, its gap and a dependent load. Past 8
+// rows the one-block selection kernel is as fast or faster (the union of more than 64 pairs no
+// longer fits one wave, and each of the grid's blocks would pay for it).
+constexpr int kFusedMaxRows = 8;
 // Gate/up blocks of a round with the selection folded in (each loops over its share of the units).
 constexpr int kFusedBlocks = 768;
 
