@@ -476,28 +476,32 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
       select_row<NPL, NT / 64>(a, s, 0, publish);
       const int j = min(lane, k - 1);
       const int id = s.sel[j];
-      bool keep = true;
+      bool keep = lane < k;
       if (skip) {
         const uint32_t word = static_cast<uint32_t>(__shfl(static_cast<int>(resw), id >> 5, 64));
-        keep = j < a.skip_j || ((word >> (id & 31)) & 1u);
+        keep = keep && (j < a.skip_j || ((word >> (id & 31)) & 1u));
       }
-      const uint64_t kb = __ballot(lane < k && keep);
-      int u = 0;
+      if (lane < k && !keep) s.slot[lane] = -1;
+      // The kept (expert, rank) pairs sorted by expert across lanes 0-15 (a bitonic network of
+      // 16; the ids of one row are distinct): lane u then holds the u-th unique expert.
+      uint32_t key = keep ? (static_cast<uint32_t>(id) << 4) | static_cast<uint32_t>(j) : 0xFFFFFFFFu;
 #pragma unroll
-      for (int m = 0; m < MOE_ROUND_MAX_TOPK; ++m) {
-        const int v = s.sel[min(m, k - 1)];
-        u += (m < k && ((kb >> m) & 1ull) && v < id) ? 1 : 0;
-      }
-      const int nk = __popcll(kb);
-      if (lane < k) {
-        s.slot[lane] = keep ? u : -1;
-        if (keep) {
-          s.uniq[u] = id;
-          s.offs[u] = u;
-          s.ioffs[u] = u;
-          s.item_u[u] = u;
-          s.pairs[u] = j << 8;  // row 0, rank j
+      for (int size = 2; size <= 16; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          const uint32_t other = lane_xor_u32(key, stride);
+          const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);
+          key = keep_min ? min(key, other) : max(key, other);
         }
+      const int nk = static_cast<int>(__popcll(__ballot(keep)));
+      if (lane < nk) {
+        const int u = lane, e = static_cast<int>(key >> 4), jr = static_cast<int>(key & 15);
+        s.slot[jr] = u;
+        s.uniq[u] = e;
+        s.offs[u] = u;
+        s.ioffs[u] = u;
+        s.item_u[u] = u;
+        s.pairs[u] = jr << 8;  // row 0, rank jr
       }
       if (lane == 0) {
         s.nu = min(nk, a.Ucap);
