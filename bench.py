@@ -47,7 +47,7 @@ def parse():
                    help="skip the kernel-timing pass (no roofline)")
     p.add_argument("--prefill-only", type=int, default=0, metavar="T",
                    help="only the prefill section, at T rows (for profiling it); prints its JSON")
-    p.add_argument("--only", default="", choices=("", "decode", "wide", "deep", "tier", "launch", "selection"),
+    p.add_argument("--only", default="", choices=("", "decode", "wide", "deep", "tier", "launch", "choices"),
                    help="only that extra section (for profiling it); prints its JSON")
     return p.parse_args()
 
@@ -95,7 +95,7 @@ def main():
                    "deep": lambda: deep_stack(torch, np, synth, MoeRound),
                    "tier": lambda: tier_rounds(torch, np, synth, MoeRound),
                    "launch": lambda: launch_costs(torch, np, synth, MoeRound),
-                   "selection": lambda: selection_placement(cfg, base, torch, np, MoeRound)}[args.only]
+                   "choices": lambda: launch_choices(cfg, base, torch, np, MoeRound)}[args.only]
         print(json.dumps({args.only: run_one()}), flush=True)
         return
     reps = [base] + [base.clone() for _ in range(args.replicas - 1)]
@@ -289,7 +289,7 @@ def main():
     prefill = None if args.no_extra else prefill_rounds(base, torch, np, synth, MoeRound)
     tier = None if args.no_extra else tier_rounds(torch, np, synth, MoeRound)
     launch = None if args.no_extra else launch_costs(torch, np, synth, MoeRound)
-    placement = None if args.no_extra else selection_placement(cfg, base, torch, np, MoeRound)
+    choices = None if args.no_extra else launch_choices(cfg, base, torch, np, MoeRound)
 
     cpu = None
     if not args.no_cpu:
@@ -325,7 +325,7 @@ def main():
         "prefill": prefill,
         "expert_tier": tier,
         "launch_costs": launch,
-        "selection_placement": placement,
+        "launch_choices": choices,
     }
     print(json.dumps(line), flush=True)
     if args.pmc_calibrate:
@@ -636,31 +636,44 @@ def deep_stack(torch, np, synth, MoeRound, fmt="q4b32", modes=("graph", "eager")
     return res
 
 
-def selection_placement(cfg, base, torch, np, MoeRound, widths=(1, 4, 5, 8, 9, 12), replicas=8):
-    """Where the selection runs: folded into every gate/up block (fused_max_rows = 15) or in its own
-    one-block kernel (-1), per verify width. Rounds of one width over `replicas` copies of the layer
-    (each round reads its weights from HBM), 16 launched back to back between two events; median of
-    12 such chains, per round. The default folds it in up to the widest T where that is faster."""
+def launch_choices(cfg, base, torch, np, MoeRound, replicas=8):
+    """The measurements behind two launch-shape defaults, per verify width:
+    - selection_placement: the selection folded into every gate/up block (fused_max_rows = 15)
+      against its own one-block kernel (-1); the default folds it in up to the widest T where
+      that is faster;
+    - rows_per_item: work items of 1 against 2 rows of an expert; the default takes 1 up to the
+      widest T where that is faster.
+    Rounds of one width over `replicas` copies of the layer (each round reads its weights from
+    HBM), 16 launched back to back between two events; median of 12 such chains, per round."""
     import synth
     reps = [base] + [base.clone() for _ in range(replicas - 1)]
     res = {"timing": "16 rounds back to back between events, median of 12, per round"}
-    for T in widths:
-        xs = [synth.make_activations(cfg, T, seed=0, round_idx=r, device="cuda") for r in range(16)]
-        out = torch.empty((T, cfg.H), device="cuda")
-        row = {}
-        for name, fm in (("fused", 15), ("separate", -1)):
-            hs = [MoeRound([rp], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(widths), use_graph=False,
-                           fused_max_rows=fm) for rp in reps]
 
-            def chain():
-                for i in range(16):
-                    hs[i % replicas].run(xs[i], cfg.k, out)
-            chain()
-            lat = [event_us(torch, chain) / 16 for _ in range(12)]
-            row[name + "_round_us"] = round(float(np.median(lat)), 2)
-            for h in hs:
-                h.close()
-        res[str(T)] = row
+    def compare(widths, variants):
+        table = {}
+        for T in widths:
+            xs = [synth.make_activations(cfg, T, seed=0, round_idx=r, device="cuda") for r in range(16)]
+            out = torch.empty((T, cfg.H), device="cuda")
+            row = {}
+            for name, shape in variants:
+                hs = [MoeRound([rp], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=max(widths), use_graph=False, **shape)
+                      for rp in reps]
+
+                def chain():
+                    for i in range(16):
+                        hs[i % replicas].run(xs[i], cfg.k, out)
+                chain()
+                lat = [event_us(torch, chain) / 16 for _ in range(12)]
+                row[name + "_round_us"] = round(float(np.median(lat)), 2)
+                for h in hs:
+                    h.close()
+            table[str(T)] = row
+        return table
+
+    res["selection_placement"] = compare((1, 4, 5, 8, 9, 12),
+                                         (("fused", {"fused_max_rows": 15}), ("separate", {"fused_max_rows": -1})))
+    res["rows_per_item"] = compare((2, 3, 5, 6, 8),
+                                   (("one_row", {"rows_per_item": 1}), ("two_rows", {"rows_per_item": 2})))
     del reps
     torch.cuda.empty_cache()
     return res

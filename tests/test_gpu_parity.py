@@ -282,6 +282,7 @@ def test_tied_logits_go_to_the_lower_id(verify, k):
 @pytest.mark.parametrize("shape", [
     dict(fused_max_rows=-1, rows_per_item=1),   # separate selection kernel, one row per item
     dict(fused_max_rows=15, rows_per_item=8),   # selection in gate/up up to 15 rows, big items
+    dict(rows_per_item=2),                      # two-row items at every verify width
     dict(prefetch=1),                           # gate/up touches the down rows of its index
 ])
 def test_launch_shape_choices(verify, shape):

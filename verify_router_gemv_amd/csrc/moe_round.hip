@@ -153,10 +153,13 @@ static int xstage_rows(int K) {
 
 // Rows of one expert handled by one work item: verify rounds split an expert shared by many rows
 // over several blocks (each re-reads the expert's tile, mostly from the memory-side cache) so no
-// block carries many rows; wide rounds keep larger items.
+// block carries many rows, down to one row per item up to kOneRowItemsMaxRows rows (the grid still
+// covers the items in about one pass there, and a block's fold work is what bounds it); wide
+// rounds keep larger items.
+constexpr int kOneRowItemsMaxRows = 5;
 static int rows_per_item(const moe_round* h, int T) {
   if (h->rows_per_item > 0) return h->rows_per_item;
-  return T >= kWideRows ? 4 : 2;
+  return T >= kWideRows ? 4 : (T <= kOneRowItemsMaxRows ? 1 : 2);
 }
 
 // Upper bound of the work items of a round: sum over experts of ceil(rows / rg).
