@@ -219,10 +219,11 @@ __device__ __forceinline__ void gateup_mfma_tile(const Args& a, const ExpertWork
   }
 }
 
-constexpr int kGuOneRow = 0, kGuPairs = 1, kGuStaged = 2;
+constexpr int kGuOneRow = 0, kGuPairs = 1, kGuStaged = 2, kGuRowItems = 3;
 
-// MODE: kGuOneRow (T == 1), kGuPairs (verify rounds: rows two at a time from L2), kGuStaged (wide
-// rounds: rows staged in LDS, matrix-core tile for items with many rows).
+// MODE: kGuOneRow (T == 1), kGuRowItems (verify rounds of one-row work items: the one-row unit
+// with the many-row selection), kGuPairs (verify rounds: rows two at a time from L2), kGuStaged
+// (wide rounds: rows staged in LDS, matrix-core tile for items with many rows).
 // SEL > 0 (verify rounds): the block first computes the round's selection itself from the logits
 // (select_block with SEL keys per lane), finds its work item in LDS, and the last block publishes the
 // records and outputs that the down kernel and the caller read; no separate selection launch.
@@ -307,7 +308,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
     }
   };
   const int np = wk.np;
-  if constexpr (MODE == kGuOneRow) {
+  if constexpr (MODE == kGuOneRow || MODE == kGuRowItems) {
     load_row(0, 0);
   } else if constexpr (MODE == kGuPairs) {
     load_row(0, 0);
@@ -409,6 +410,12 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
 
   if constexpr (MODE == kGuOneRow) {
     do_row(0, 0);
+  } else if constexpr (MODE == kGuRowItems) {
+    do_row(0, 0);
+    for (int r = 1; r < np; ++r) {  // items of one row; more only with a wider rows_per_item
+      load_row(0, r);
+      do_row(0, r);
+    }
   } else if constexpr (MODE == kGuPairs) {
     do_row(0, 0);  // the first pair, loaded before the weights (peeled off the loop so that the
     if (np > 1) do_row(SLOTS - 1, 1);  // compiler keeps those loads where they are)

@@ -26,6 +26,10 @@ struct GemvPick {
       return sel == 4   ? gateup_kernel<G, NB, RW, kGuOneRow, 4, FMT>
              : sel == 8 ? gateup_kernel<G, NB, RW, kGuOneRow, 8, FMT>
                         : gateup_kernel<G, NB, RW, kGuOneRow, 0, FMT>;
+    if (mode == kGuRowItems)
+      return sel == 4   ? gateup_kernel<G, NB, RW, kGuRowItems, 4, FMT>
+             : sel == 8 ? gateup_kernel<G, NB, RW, kGuRowItems, 8, FMT>
+                        : gateup_kernel<G, NB, RW, kGuRowItems, 0, FMT>;
     return sel == 4   ? gateup_kernel<G, NB, RW, kGuPairs, 4, FMT>
            : sel == 8 ? gateup_kernel<G, NB, RW, kGuPairs, 8, FMT>
                       : gateup_kernel<G, NB, RW, kGuPairs, 0, FMT>;
@@ -38,7 +42,7 @@ struct GemvPick {
   static constexpr int rows_per_block() { return kWaves * RW * (64 / G); }
 };
 
-// up: the gate/up kernel of form `mode` (kGuOneRow, kGuPairs, kGuStaged) with `sel` keys per lane
+// up: the gate/up kernel of form `mode` (kGuOneRow, kGuRowItems, kGuPairs, kGuStaged) with `sel` keys per lane
 // of a folded selection (0: none); otherwise the down kernel, exact mode if sel != 0, with the
 // matrix-core tile if mode != 0 (where the shape has one).
 template <int G, int NB, int FMT>

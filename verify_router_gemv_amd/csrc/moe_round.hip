@@ -231,7 +231,7 @@ static bool make_plan(const moe_round* h, int T, int k, RoundPlan* p) {
   p->sel = pick_select(E, p->split_topk);
   p->topk = pick_topk_rows(E);
   int rows_gu = 0, rows_dn = 0;
-  const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : kGuPairs);
+  const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : (rows_per_item(h, T) == 1 ? kGuRowItems : kGuPairs));
   const int fmt = h->cfg.weight_format;
   // the down tile: wide rounds with the matrix-core tiles enabled, I = 512 (G = 16 x 1 block)
   const bool down_tile = wide && h->mfma_rows > 0 && !h->cfg.exact && h->Gi == 16 && h->NBi == 1 &&
