@@ -388,7 +388,7 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
       acc[w] = ag;       // gate partials: acc[0 .. RW-1]
       acc[RW + w] = au;  // up partials:   acc[RW .. 2RW-1]
     }
-    float* hrow = a.hbuf + static_cast<size_t>(wk.p0 + p) * I;
+    MOE_GLOBAL float* hrow = (MOE_GLOBAL float*)(a.hbuf + static_cast<size_t>(wk.p0 + p) * I);  // global stores
     if constexpr (G == 64 && RW == 4) {
       float gsum, usum;
       reduce8_wave(acc, gsum, usum);
@@ -444,13 +444,16 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
 }
 
 // Rounds without the residual (and with the atomic combine) start the output rows at zero: the down
-// kernel adds into them. Stores only, spread over the grid.
+// kernel adds into them. Stores only, spread over the grid, issued by every block after its own
+// work (nothing in this kernel reads the output, and the router has read the input by now), as
+// global stores: a flat store would also count against the scalar-load counter, so the next
+// wait for a kernel argument would wait for its write to complete.
 __device__ __forceinline__ void zero_output(const Args& a, int layer) {
   const Ingress in = get_ingress(a);
-  float4* o = reinterpret_cast<float4*>(layer_output(a, in, layer));
+  MOE_GLOBAL f32x4* o = (MOE_GLOBAL f32x4*)(layer_output(a, in, layer));
   const int n4 = a.T * a.H / 4;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x)
-    o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n4; i += gridDim.x * kThreads)  // launched with kThreads
+    o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Blocks with the selection folded in (SEL > 0) compute it once and then take the units (item,
@@ -461,7 +464,6 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
   constexpr int ROWS_B = kWaves * RW * (64 / G);
   extern __shared__ uint32_t xs[];  // staged form: gateup_stage_words(H) (+ matrix-core tile) words
   const int tiles = (a.I + ROWS_B - 1) / ROWS_B;
-  if (!a.residual && !a.exact) zero_output(a, layer);
   if constexpr (SEL > 0) {
     __shared__ SelectSharedT<kFusedPairs, kWaves> ssel;
     // The last block publishes: it is the one most likely to have no (item, tile) unit of its own.
@@ -474,9 +476,9 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
   } else {
     const int u = blockIdx.x / tiles, tile = blockIdx.x - u * tiles;
     const ExpertWork wk = load_work(a, layer, u);
-    if (u >= wk.nu) return;
-    gateup_unit<G, NB, RW, MODE, FMT>(a, layer, wk, tile, xs);
+    if (u < wk.nu) gateup_unit<G, NB, RW, MODE, FMT>(a, layer, wk, tile, xs);
   }
+  if (!a.residual && !a.exact) zero_output(a, layer);
 }
 
 }  // namespace moe

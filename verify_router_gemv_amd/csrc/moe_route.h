@@ -253,8 +253,8 @@ __device__ __forceinline__ bool tail_pair(const Args& a, const SS& s, int j, int
 // `skip`, s.tmask zero and s.res written). Experts the tail skip leaves out get no pairs, slot -1.
 template <int NT, typename SS>
 __device__ __forceinline__ void union_block(const Args& a, SS& s, int npairs, bool skip, int& nu, int& ni) {
-  constexpr int NWMIN = NT / 64;  // fewest waves a caller launches (sizes the per-wave arrays)
-  const int nt = blockDim.x, nw = nt >> 6;
+  constexpr int NWMIN = NT / 64;  // the caller's waves (sizes the per-wave arrays)
+  constexpr int nt = NT, nw = NT / 64;  // the launched block size (not read from the dispatch)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k;
   for (int idx = tid; idx < npairs; idx += nt) {
@@ -451,8 +451,7 @@ __device__ __forceinline__ void union_wave(const Args& a, SS& s, int npairs, boo
   }
 }
 
-// The selection of one round by one block (of at least NT threads; the strides use the launched
-// block size): per-row top-k and softmax, the union of
+// The selection of one round by one block of NT threads: per-row top-k and softmax, the union of
 // the rows' experts, the counting sort of the (row, rank) pairs by expert and the work items (an
 // expert and at most a.rg of its rows). Results stay in `s`; with `publish` the block also writes
 // the per-item records, the unique list, pair table and pair weights, and the caller's ids and
@@ -461,7 +460,7 @@ __device__ __forceinline__ void union_wave(const Args& a, SS& s, int npairs, boo
 // a.tsel / a.tp instead of computed here.
 template <int NPL, int NT, bool ONE_ROW = false, bool PRESEL = false, typename SS>
 __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bool publish) {
-  const int nt = blockDim.x, nw = nt >> 6;
+  constexpr int nt = NT, nw = NT / 64;  // the launched block size (not read from the dispatch)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k, npairs = T * k;
 
