@@ -98,7 +98,28 @@ struct Args {
   int32_t* n_skipped;          // [L] experts the tail skip left out
 };
 
-__device__ __forceinline__ Ingress get_ingress(const Args& a) { return a.ing ? *a.ing : a.in; }
+// Words of device memory that no kernel writes while they are read (changed only between kernels,
+// in stream order), through the constant address space: scalar loads, whose wait is not the
+// vector-memory counter's, so no vector load waits for them (nor they for a vector load).
+template <int N>
+__device__ __forceinline__ void load_const_words(const void* p, uint64_t (&w)[N]) {
+  const __attribute__((address_space(4))) uint64_t* q = (const __attribute__((address_space(4))) uint64_t*)(p);
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = q[i];
+}
+
+// The ingress pointers (graph mode: from the device buffer, by scalar loads).
+__device__ __forceinline__ Ingress get_ingress(const Args& a) {
+  if (!a.ing) return a.in;
+  uint64_t w[4];
+  load_const_words(a.ing, w);
+  Ingress in;
+  in.hidden = reinterpret_cast<const float*>(w[0]);
+  in.out = reinterpret_cast<float*>(w[1]);
+  in.ids = reinterpret_cast<int32_t*>(w[2]);
+  in.route_w = reinterpret_cast<float*>(w[3]);
+  return in;
+}
 // A layer's weight pointers are always kernel arguments (so every weight address is known without a
 // load); graph replays pick up new weights through their nodes' parameters, not a device table.
 __device__ __forceinline__ const moe_layer_weights& get_weights(const Args& a, int) { return a.w; }

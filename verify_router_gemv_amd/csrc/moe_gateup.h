@@ -320,8 +320,8 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
   // before the weight loads, so the wait for the weights covers them; issued in any case (without
   // prefetching they touch a line of the input digits, read anyway).
   const int pf_tiles = (I + ROWS_B - 1) / ROWS_B;
-  const int pf_r0 = static_cast<int>(static_cast<long>(tile) * H / pf_tiles);
-  const int pf_r1 = static_cast<int>(static_cast<long>(tile + 1) * H / pf_tiles);
+  const int pf_r0 = tile * H / pf_tiles;  // tile < I / 16 and H <= 8192: no overflow
+  const int pf_r1 = (tile + 1) * H / pf_tiles;
   const bool pf_on = a.prefetch != 0 && pf_r1 > pf_r0;
   const size_t pf_q = static_cast<size_t>(I) / 2, pf_s = sm_row_words<FMT>(I) * 4;  // bytes per down row
   const size_t pf_d0 = pf_r0;

@@ -47,13 +47,16 @@ __device__ __forceinline__ ExpertPtrs expert_ptrs(const Args& a, int e) {
   e = __builtin_amdgcn_readfirstlane(e);
   ExpertPtrs p;
   if (a.etab) {
-    const moe_expert_ref r = a.etab[e];
-    p.gq = r.gate_q;
-    p.gs = r.gate_sm;
-    p.uq = r.up_q;
-    p.us = r.up_sm;
-    p.dq = r.down_q;
-    p.ds = r.down_sm;
+    // Scalar loads (the table changes only between kernels, in stream order): the weight
+    // addresses then do not wait for vector loads issued before them.
+    uint64_t w[6];
+    load_const_words(a.etab + e, w);
+    p.gq = reinterpret_cast<const uint8_t*>(w[0]);
+    p.gs = reinterpret_cast<const uint32_t*>(w[1]);
+    p.uq = reinterpret_cast<const uint8_t*>(w[2]);
+    p.us = reinterpret_cast<const uint32_t*>(w[3]);
+    p.dq = reinterpret_cast<const uint8_t*>(w[4]);
+    p.ds = reinterpret_cast<const uint32_t*>(w[5]);
     return p;
   }
   const size_t H = a.H, I = a.I, ex = static_cast<size_t>(e);
