@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   const ExpertWork wk = load_work(a, layer, u);
   if (u >= wk.nu) return;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int g = lane % G, rs = lane / G;
   const int xst = a.xstage_i;
   if constexpr (TILE) {  // 64 rows of H per block, I = 512

@@ -240,7 +240,8 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
   constexpr bool STAGE = MODE == kGuStaged;
   const int nblk = H / 32;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a uniform value: row addresses shared by the wave's lanes are then scalar math
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane % G, rs = lane / G;
   const ExpertPtrs W = expert_ptrs<FMT>(a, wk.e);  // issued first: every weight address needs it
   const int row0 = tile * ROWS_B + wave * ROWS_W + rs;
