@@ -140,6 +140,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kDppRor8 = 0x128;       // lane i <-> i ^ 8 within 16 (a rotation by 8)
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -219,6 +220,61 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   v += swap_partner_f64<false>(v);
   v += swap_partner_f64<true>(v);
   return v;
+}
+
+// Both 32-bit halves of two fp64 values through one lane swap (X32: lanes 32 apart, else 16).
+template <bool X32>
+__device__ __forceinline__ void swap_f64(double& a, double& b) {
+  const uint64_t ua = __builtin_bit_cast(uint64_t, a), ub = __builtin_bit_cast(uint64_t, b);
+  uint32_t al = static_cast<uint32_t>(ua), ah = static_cast<uint32_t>(ua >> 32);
+  uint32_t bl = static_cast<uint32_t>(ub), bh = static_cast<uint32_t>(ub >> 32);
+  if constexpr (X32) {
+    permlane32_swap(al, bl);
+    permlane32_swap(ah, bh);
+  } else {
+    permlane16_swap(al, bl);
+    permlane16_swap(ah, bh);
+  }
+  a = __builtin_bit_cast(double, (static_cast<uint64_t>(ah) << 32) | al);
+  b = __builtin_bit_cast(double, (static_cast<uint64_t>(bh) << 32) | bl);
+}
+
+// Wave sums of R rows at once (R = 1, 2, 4 or 8 values per lane). The levels over lane bits 5, 4
+// and 3 first halve the rows each lane carries: lanes with the bit clear keep the lower half of
+// their rows, lanes with it set the upper half, and one lane swap (or DPP rotation) hands each lane
+// its partner's values for the rows it keeps. Once a lane carries a single row, the remaining
+// levels add its partners' copies. Every row goes through the same tree whatever R (partners 32,
+// 16 and 8 lanes apart, then lane i with 7 - i within 8, then 2 and 1 apart; fp addition being
+// commutative, either operand order gives the same bits), so a row's sum does not depend on the
+// rows summed beside it. Lane l returns the sum of row l / (64 / R).
+template <int R>
+__device__ __forceinline__ double wave_sums_f64(const double (&v)[R]) {
+  static_assert(R == 1 || R == 2 || R == 4 || R == 8, "1, 2, 4 or 8 rows");
+  constexpr int R1 = R > 1 ? R / 2 : 1, R2 = R1 > 1 ? R1 / 2 : 1;
+  double s1[R1], s2[R2];
+#pragma unroll
+  for (int i = 0; i < R1; ++i) {
+    double a = v[i], b = v[R > 1 ? i + R1 : i];
+    swap_f64<true>(a, b);  // lanes 0-31: their own a and lane + 32's a; lanes 32-63: the b's
+    s1[i] = a + b;
+  }
+#pragma unroll
+  for (int i = 0; i < R2; ++i) {
+    double a = s1[i], b = s1[R1 > 1 ? i + R2 : i];
+    swap_f64<false>(a, b);  // the same over 16-lane rows: even rows keep a, odd rows b
+    s2[i] = a + b;
+  }
+  double s;
+  if constexpr (R2 > 1) {
+    const bool up = (__lane_id() & 8) != 0;
+    s = (up ? s2[1] : s2[0]) + dpp_f64<kDppRor8>(up ? s2[0] : s2[1]);
+  } else {
+    s = s2[0] + dpp_f64<kDppRor8>(s2[0]);
+  }
+  s += dpp_f64<kDppHalfMirror>(s);
+  s += dpp_f64<kDppXor2>(s);
+  s += dpp_f64<kDppXor1>(s);
+  return s;
 }
 
 // Wave-wide maximum left in every lane, on VALU only (no round trip through scalar registers):

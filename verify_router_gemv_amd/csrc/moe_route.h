@@ -13,7 +13,8 @@ namespace moe {
 //  * Blocks x < E: expert x's logits for rows y * TC .. y * TC + TC - 1. The reduction over H is split
 //    over the block's four waves (thread i takes float4 chunks i, i + 256, ... of the row), every load
 //    of the thread (its router chunks and the TC rows' chunks) is issued before any arithmetic, each
-//    wave sums its part in fp64 and wave 0 adds the four parts in wave order (a fixed order).
+//    wave sums its part of all TC rows at once in fp64 (by a tree that is the same for every row and
+//    every TC) and wave 0 adds the four parts in wave order (a fixed order).
 //  * Blocks x >= E (row chunk 0 only): the layer input as int8 digits per 32-block for the gate/up
 //    kernel, two 32-blocks per wave; with the residual (and the atomic combine) they also seed the
 //    layer's output rows with the input rows. These blocks read no router row, so the router waves
@@ -71,10 +72,9 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
     }
   }
   __shared__ double part[kWaves][TC];
-#pragma unroll
-  for (int r = 0; r < TC; ++r) {
-    acc[r] = wave_sum_f64(acc[r]);
-    if (lane == 0) part[wave][r] = acc[r];
+  {
+    const double sum = wave_sums_f64<TC>(acc);  // row lane / (64 / TC)
+    if ((lane & (64 / TC - 1)) == 0) part[wave][lane / (64 / TC)] = sum;
   }
   __syncthreads();
   if (tid < TC && t0 + tid < T) {
