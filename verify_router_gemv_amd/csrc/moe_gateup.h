@@ -229,6 +229,13 @@ constexpr int kGuOneRow = 0, kGuPairs = 1, kGuStaged = 2, kGuRowItems = 3;
 // records and outputs that the down kernel and the caller read; no separate selection launch.
 // SEL == 0: the work item comes from the records written by select_kernel.
 constexpr int kFusedPairs = 256;  // (row, rank) pairs of a round with the selection fused in
+// Fused blocks of the many-row forms are kFusedGroups groups of kWaves waves: the block's selection
+// runs once for the whole CU (each row on a wave of its own), then each group works on its own
+// units as a four-wave block would.
+constexpr int kFusedGroups = 3;
+constexpr int gateup_groups(int mode, int sel) {
+  return sel > 0 && (mode == kGuRowItems || mode == kGuPairs) ? kFusedGroups : 1;
+}
 
 // One unit of gate/up work: work item `wk`, rows tile * ROWS_B .. of I.
 template <int G, int NB, int RW, int MODE, int FMT>
@@ -241,7 +248,8 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
   const int nblk = H / 32;
 
   // the wave index as a uniform value: row addresses shared by the wave's lanes are then scalar math
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // (in a block of several groups, the thread's index within its group of kWaves waves)
+  const int tid = threadIdx.x & (kThreads - 1), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane % G, rs = lane / G;
   const ExpertPtrs W = expert_ptrs<FMT>(a, wk.e);  // issued first: every weight address needs it
   const int row0 = tile * ROWS_B + wave * ROWS_W + rs;
@@ -449,28 +457,30 @@ __device__ __forceinline__ void gateup_unit(const Args& a, int layer, const Expe
 // work (nothing in this kernel reads the output, and the router has read the input by now), as
 // global stores: a flat store would also count against the scalar-load counter, so the next
 // wait for a kernel argument would wait for its write to complete.
+template <int NT>  // the launched block size
 __device__ __forceinline__ void zero_output(const Args& a, int layer) {
   const Ingress in = get_ingress(a);
   MOE_GLOBAL f32x4* o = (MOE_GLOBAL f32x4*)(layer_output(a, in, layer));
   const int n4 = a.T * a.H / 4;
-  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n4; i += gridDim.x * kThreads)  // launched with kThreads
-    o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n4; i += gridDim.x * NT) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Blocks with the selection folded in (SEL > 0) compute it once and then take the units (item,
 // tile) blockIdx.x, blockIdx.x + gridDim.x, ...: the grid is sized for the chip, not for the
 // largest possible item count, so no block repeats the selection only to find no work.
 template <int G, int NB, int RW, int MODE, int SEL, int FMT>
-__global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
+__global__ __launch_bounds__(kThreads * gateup_groups(MODE, SEL)) void gateup_kernel(Args a, int layer) {
+  constexpr int GR = gateup_groups(MODE, SEL), NT = kThreads * GR;  // launched with NT threads
   constexpr int ROWS_B = kWaves * RW * (64 / G);
   extern __shared__ uint32_t xs[];  // staged form: gateup_stage_words(H) (+ matrix-core tile) words
   const int tiles = (a.I + ROWS_B - 1) / ROWS_B;
   if constexpr (SEL > 0) {
-    __shared__ SelectSharedT<kFusedPairs, kWaves> ssel;
+    __shared__ SelectSharedT<kFusedPairs, NT / 64> ssel;
     // The last block publishes: it is the one most likely to have no (item, tile) unit of its own.
-    select_block<SEL, kThreads, MODE == kGuOneRow>(a, layer, ssel, blockIdx.x == gridDim.x - 1);
+    select_block<SEL, NT, MODE == kGuOneRow>(a, layer, ssel, blockIdx.x == gridDim.x - 1);
     const int units = ssel.ni * tiles;
-    for (int w = blockIdx.x; w < units; w += gridDim.x) {
+    const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kThreads);
+    for (int w = blockIdx.x + grp * gridDim.x; w < units; w += gridDim.x * GR) {  // every CU's first group, then the second ...
       const int u = w / tiles;
       gateup_unit<G, NB, RW, MODE, FMT>(a, layer, work_from_lds(a, ssel, u), w - u * tiles, xs);
     }
@@ -479,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(Args a, int layer) {
     const ExpertWork wk = load_work(a, layer, u);
     if (u < wk.nu) gateup_unit<G, NB, RW, MODE, FMT>(a, layer, wk, tile, xs);
   }
-  if (!a.residual && !a.exact) zero_output(a, layer);
+  if (!a.residual && !a.exact) zero_output<NT>(a, layer);
 }
 
 }  // namespace moe

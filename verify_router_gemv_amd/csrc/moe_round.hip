@@ -216,6 +216,7 @@ struct RoundPlan {
   KernelFn lg = nullptr, sel = nullptr, gu = nullptr, dn = nullptr, topk = nullptr;
   dim3 grid_lg, grid_gu, grid_dn, grid_topk, grid_comb;
   int shm_gu = 0, shm_dn = 0;
+  int thr_gu = kThreads;  // gate/up block size (fused many-row forms: groups of kThreads)
   bool fused = false, split_topk = false, exact = false;
 };
 constexpr int kMaxLaunchesPerLayer = 6;  // logits, top-k, select, gate/up, down, combine
@@ -241,7 +242,9 @@ static bool make_plan(const moe_round* h, int T, int k, RoundPlan* p) {
     return false;
   p->grid_lg = logits_grid(E, H, T);
   const int units_gu = umax * ((I + rows_gu - 1) / rows_gu);
-  p->grid_gu = dim3(p->fused && units_gu > kFusedBlocks ? kFusedBlocks : units_gu);
+  const int groups = gateup_groups(gu_mode, p->fused ? fused_select_keys(E) : 0);
+  p->thr_gu = kThreads * groups;
+  p->grid_gu = dim3(p->fused && units_gu > kFusedBlocks / groups ? kFusedBlocks / groups : units_gu);
   p->grid_dn = dim3(umax * ((H + rows_dn - 1) / rows_dn));
   p->grid_topk = dim3((T + kWaves - 1) / kWaves);
   p->grid_comb = dim3(T, (H + 4 * kThreads - 1) / (4 * kThreads));
@@ -259,7 +262,7 @@ static int layer_launches(const RoundPlan& p, int l, Launch* out) {
   out[n++] = {p.lg, p.grid_lg, kThreads, 0, l, 0};
   if (!p.fused && p.split_topk) out[n++] = {p.topk, p.grid_topk, kThreads, 0, l, 1};
   if (!p.fused) out[n++] = {p.sel, dim3(1), kSelectThreads, 0, l, 1};
-  out[n++] = {p.gu, p.grid_gu, kThreads, p.shm_gu, l, 2};
+  out[n++] = {p.gu, p.grid_gu, p.thr_gu, p.shm_gu, l, 2};
   out[n++] = {p.dn, p.grid_dn, kThreads, p.shm_dn, l, 3};
   if (p.exact) out[n++] = {combine_kernel, p.grid_comb, kThreads, 0, l, 4};
   return n;
