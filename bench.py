@@ -670,9 +670,9 @@ def launch_choices(cfg, base, torch, np, MoeRound, replicas=8):
             table[str(T)] = row
         return table
 
-    res["selection_placement"] = compare((1, 4, 5, 8, 9, 12),
+    res["selection_placement"] = compare((1, 4, 8, 12, 15),
                                          (("fused", {"fused_max_rows": 15}), ("separate", {"fused_max_rows": -1})))
-    res["rows_per_item"] = compare((2, 3, 5, 6, 8),
+    res["rows_per_item"] = compare((3, 6, 8, 10, 12, 15),
                                    (("one_row", {"rows_per_item": 1}), ("two_rows", {"rows_per_item": 2})))
     del reps
     torch.cuda.empty_cache()

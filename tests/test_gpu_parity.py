@@ -289,7 +289,7 @@ def test_launch_shape_choices(verify, shape):
     """Other launch shapes give the same ids and worklists and outputs within tolerance."""
     cfg, layer, view = verify
     g = GpuRound([layer], cfg, max_rows=16, **shape)
-    for T in (1, 3, 8, 15):
+    for T in (1, 3, 8, 12, 15):
         say(f"case launch shape {shape} T={T}")
         X = synth.make_activations(cfg, T, seed=6, round_idx=T, device=DEV)
         check_layer_round(g, [view], X, cfg.k, f"shape {shape} T={T}")

@@ -150,10 +150,10 @@ inline KernelFn pick_topk_rows(int E) {
 constexpr int kSplitTopkRows = 32;
 
 // Rounds of at most this many rows fold the selection into the gate/up kernel: every block
-// recomputes it (cheap for a few rows), which saves a launch, its gap and a dependent load. Past 8
-// rows the one-block selection kernel is as fast or faster (the union of more than 64 pairs no
-// longer fits one wave, and each of the grid's blocks would pay for it).
-constexpr int kFusedMaxRows = 8;
+// recomputes it (one block per CU in the many-row forms, each row on a wave of its own), which
+// saves a launch, its gap and a dependent load. 15 is the most the fused selection state holds
+// (15 rows of 16 ranks); at 15 rows the fold and the one-block selection kernel measure the same.
+constexpr int kFusedMaxRows = 15;
 // Gate/up blocks of a round with the selection folded in (each loops over its share of the units).
 constexpr int kFusedBlocks = 768;
 

@@ -156,7 +156,7 @@ static int xstage_rows(int K) {
 // block carries many rows, down to one row per item up to kOneRowItemsMaxRows rows (the grid still
 // covers the items in about one pass there, and a block's fold work is what bounds it); wide
 // rounds keep larger items.
-constexpr int kOneRowItemsMaxRows = 5;
+constexpr int kOneRowItemsMaxRows = 10;
 static int rows_per_item(const moe_round* h, int T) {
   if (h->rows_per_item > 0) return h->rows_per_item;
   return T >= kWideRows ? 4 : (T <= kOneRowItemsMaxRows ? 1 : 2);
