@@ -240,6 +240,12 @@ static bool make_plan(const moe_round* h, int T, int k, RoundPlan* p) {
   if (!p->lg || !pick_gemv(h->Gh, h->NBh, gu_mode, true, p->fused ? fused_select_keys(E) : 0, fmt, &p->gu, &rows_gu) ||
       !pick_gemv(h->Gi, h->NBi, down_tile ? 1 : 0, false, h->cfg.exact, fmt, &p->dn, &rows_dn))
     return false;
+  // Rounds whose down grid is small (at most kDownHalfMaxBlocks full-height blocks, up to three per
+  // CU) take half-height down blocks: twice the blocks, each with half the rows of H, so more of
+  // the expert tiles' loads are in flight at once.
+  if (!down_tile && umax * ((H + rows_dn - 1) / rows_dn) <= kDownHalfMaxBlocks &&
+      !pick_gemv(h->Gi, h->NBi, 2, false, h->cfg.exact, fmt, &p->dn, &rows_dn))
+    return false;
   p->grid_lg = logits_grid(E, H, T);
   const int units_gu = umax * ((I + rows_gu - 1) / rows_gu);
   const int groups = gateup_groups(gu_mode, p->fused ? fused_select_keys(E) : 0);
