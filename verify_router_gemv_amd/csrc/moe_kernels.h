@@ -156,9 +156,9 @@ constexpr int kSplitTopkRows = 32;
 
 // Rounds of at most this many rows fold the selection into the gate/up kernel: every block
 // recomputes it (one block per CU in the many-row forms, each row on a wave of its own), which
-// saves a launch, its gap and a dependent load. 15 is the most the fused selection state holds
-// (15 rows of 16 ranks); at 15 rows the fold and the one-block selection kernel measure the same.
-constexpr int kFusedMaxRows = 15;
+// saves a launch, its gap and a dependent load. At 15 rows (the most the fused selection state holds,
+// 15 rows of 16 ranks) the one-block selection kernel is as fast or faster.
+constexpr int kFusedMaxRows = 13;
 // Gate/up blocks of a round with the selection folded in (each loops over its share of the units).
 constexpr int kFusedBlocks = 768;
 // Down grids of at most this many full-height blocks use half-height blocks (see make_plan).
