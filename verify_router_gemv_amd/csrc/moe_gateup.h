@@ -466,8 +466,9 @@ __device__ __forceinline__ void zero_output(const Args& a, int layer) {
 }
 
 // Blocks with the selection folded in (SEL > 0) compute it once and then take the units (item,
-// tile) blockIdx.x, blockIdx.x + gridDim.x, ...: the grid is sized for the chip, not for the
-// largest possible item count, so no block repeats the selection only to find no work.
+// tile) blockIdx.x, blockIdx.x + gridDim.x, ... (in blocks of GR four-wave groups, group g starts at
+// blockIdx.x + g * gridDim.x and steps by GR * gridDim.x): the grid is sized for the chip, not for
+// the largest possible item count, so no block repeats the selection only to find no work.
 template <int G, int NB, int RW, int MODE, int SEL, int FMT>
 __global__ __launch_bounds__(kThreads * gateup_groups(MODE, SEL)) void gateup_kernel(Args a, int layer) {
   constexpr int GR = gateup_groups(MODE, SEL), NT = kThreads * GR;  // launched with NT threads
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(kThreads * gateup_groups(MODE, SEL)) void gateup_ke
     select_block<SEL, NT, MODE == kGuOneRow>(a, layer, ssel, blockIdx.x == gridDim.x - 1);
     const int units = ssel.ni * tiles;
     const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kThreads);
-    for (int w = blockIdx.x + grp * gridDim.x; w < units; w += gridDim.x * GR) {  // every CU's first group, then the second ...
+    for (int w = blockIdx.x + grp * gridDim.x; w < units; w += gridDim.x * GR) {
       const int u = w / tiles;
       gateup_unit<G, NB, RW, MODE, FMT>(a, layer, work_from_lds(a, ssel, u), w - u * tiles, xs);
     }

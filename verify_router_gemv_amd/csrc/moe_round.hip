@@ -153,9 +153,9 @@ static int xstage_rows(int K) {
 
 // Rows of one expert handled by one work item: verify rounds split an expert shared by many rows
 // over several blocks (each re-reads the expert's tile, mostly from the memory-side cache) so no
-// block carries many rows, down to one row per item up to kOneRowItemsMaxRows rows (the grid still
-// covers the items in about one pass there, and a block's fold work is what bounds it); wide
-// rounds keep larger items.
+// block carries many rows, down to one row per item up to kOneRowItemsMaxRows rows (timed faster
+// there than two-row items, whose blocks do twice the fold work each; from 12 rows the two-row
+// items are faster); wide rounds keep larger items.
 constexpr int kOneRowItemsMaxRows = 10;
 static int rows_per_item(const moe_round* h, int T) {
   if (h->rows_per_item > 0) return h->rows_per_item;
