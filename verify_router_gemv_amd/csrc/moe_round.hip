@@ -152,7 +152,8 @@ static int xstage_rows(int K) {
 }
 
 // Rows of one expert handled by one work item: verify rounds split an expert shared by many rows
-// over several blocks (each re-reads the expert's tile, mostly from the memory-side cache) so no
+// over several blocks (each re-reads the expert's tile, which the caches serve: the measured
+// gate/up traffic stays at the unique experts' bytes) so no
 // block carries many rows, down to one row per item up to kOneRowItemsMaxRows rows (timed faster
 // there than two-row items, whose blocks do twice the fold work each; from 12 rows the two-row
 // items are faster); wide rounds keep larger items.
