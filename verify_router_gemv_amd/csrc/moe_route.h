@@ -399,13 +399,17 @@ __device__ __forceinline__ void union_wave(const Args& a, SS& s, int npairs, boo
   uint32_t key = 0xFFFFFFFFu;  // past the pairs: sorts last
   if (lane < npairs) key = (static_cast<uint32_t>(s.sel[lane]) << 6) | static_cast<uint32_t>(lane);
 #pragma unroll
-  for (int size = 2; size <= 64; size <<= 1)
+  for (int size = 2; size <= 64; size <<= 1) {
+    // With at most 32 pairs, lanes 32-63 hold only the padding key once the 32-lane halves are
+    // sorted (the lower half ascending), so the last merge would change nothing.
+    if (size == 64 && npairs <= 32) break;
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const uint32_t other = lane_xor_u32(key, stride);
       const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);
       key = keep_min ? min(key, other) : max(key, other);
     }
+  }
   const bool valid = lane < npairs;
   const int e = static_cast<int>(key >> 6), pi = static_cast<int>(key & 63);
   const int t = small_div(pi, __builtin_amdgcn_rcpf(static_cast<float>(k))), j = pi - t * k;
