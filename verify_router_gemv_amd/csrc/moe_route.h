@@ -494,13 +494,15 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
       // 16; the ids of one row are distinct): lane u then holds the u-th unique expert.
       uint32_t key = keep ? (static_cast<uint32_t>(id) << 4) | static_cast<uint32_t>(j) : 0xFFFFFFFFu;
 #pragma unroll
-      for (int size = 2; size <= 16; size <<= 1)
+      for (int size = 2; size <= 16; size <<= 1) {
+        if (size == 16 && k <= 8) break;  // lanes 8-15 hold only the padding key: already in place
 #pragma unroll
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
           const uint32_t other = lane_xor_u32(key, stride);
           const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);
           key = keep_min ? min(key, other) : max(key, other);
         }
+      }
       const int nk = static_cast<int>(__popcll(__ballot(keep)));
       if (lane < nk) {
         const int u = lane, e = static_cast<int>(key >> 4), jr = static_cast<int>(key & 15);
