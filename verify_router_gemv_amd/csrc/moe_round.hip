@@ -158,6 +158,7 @@ static int xstage_rows(int K) {
 // there than two-row items, whose blocks do twice the fold work each; from 12 rows the two-row
 // items are faster); wide rounds keep larger items.
 constexpr int kOneRowItemsMaxRows = 10;
+constexpr int kPairItemMaxRows = 4;  // items the row-pair form takes in wide rounds (see make_plan)
 static int rows_per_item(const moe_round* h, int T) {
   if (h->rows_per_item > 0) return h->rows_per_item;
   return T >= kWideRows ? 4 : (T <= kOneRowItemsMaxRows ? 1 : 2);
@@ -233,7 +234,11 @@ static bool make_plan(const moe_round* h, int T, int k, RoundPlan* p) {
   p->sel = pick_select(E, p->split_topk);
   p->topk = pick_topk_rows(E);
   int rows_gu = 0, rows_dn = 0;
-  const int gu_mode = wide ? kGuStaged : (T == 1 ? kGuOneRow : (rows_per_item(h, T) == 1 ? kGuRowItems : kGuPairs));
+  // Wide rounds take the row-pair form, which loads each pair's input digits from L2, for items of
+  // up to kPairItemMaxRows rows (timed faster than staging the rows in LDS at T = 16, 32 and 64); the
+  // staged form serves larger items and the matrix-core tile.
+  const bool staged = wide && (rows_per_item(h, T) > kPairItemMaxRows || (h->mfma_rows > 0 && !h->cfg.exact));
+  const int gu_mode = staged ? kGuStaged : (T == 1 ? kGuOneRow : (rows_per_item(h, T) == 1 ? kGuRowItems : kGuPairs));
   const int fmt = h->cfg.weight_format;
   // the down tile: wide rounds with the matrix-core tiles enabled, I = 512 (G = 16 x 1 block)
   const bool down_tile = wide && h->mfma_rows > 0 && !h->cfg.exact && h->Gi == 16 && h->NBi == 1 &&
@@ -257,7 +262,7 @@ static bool make_plan(const moe_round* h, int T, int k, RoundPlan* p) {
   p->grid_comb = dim3(T, (H + 4 * kThreads - 1) / (4 * kThreads));
   int gu_words = gateup_stage_words(H);
   if (h->Gh == 64 && h->NBh == 1) gu_words += kMfmaExtraWords;  // matrix-core tile: (s, m) tables, partial sums
-  p->shm_gu = wide ? static_cast<int>(sizeof(uint32_t)) * gu_words : 0;
+  p->shm_gu = staged ? static_cast<int>(sizeof(uint32_t)) * gu_words : 0;
   p->shm_dn = static_cast<int>(sizeof(uint32_t)) * xstage_rows(I) * (I / 32) * (kXqWords + 2);
   if (down_tile) p->shm_dn += static_cast<int>(sizeof(uint32_t)) * kDownTileExtraWords;  // its (s, m) tables
   return true;
