@@ -35,25 +35,33 @@ struct GemvPick {
                       : gateup_kernel<G, NB, RW, kGuPairs, 0, FMT>;
   }
   // down: mode 1 the matrix-core tile (where the shape has one), mode 2 half-height blocks (two
-  // rows per lane group where there are four, for rounds whose full-height grid is small).
+  // rows per lane group where there are four, for rounds whose full-height grid is small), mode 3
+  // double-height blocks (eight rows per lane group there, for one-row items on large grids).
   static KernelFn down(bool exact, int mode) {
     if constexpr (G == 16 && NB == 1 && RW == 4 && FMT == kFmtQ4B32)
       if (mode == 1) return exact ? down_kernel<G, NB, RW, true, FMT, true> : down_kernel<G, NB, RW, false, FMT, true>;
-    if constexpr (RW == 4)
+    if constexpr (RW == 4) {
       if (mode == 2) return exact ? down_kernel<G, NB, 2, true, FMT> : down_kernel<G, NB, 2, false, FMT>;
+      if (mode == 3) return exact ? down_kernel<G, NB, 8, true, FMT> : down_kernel<G, NB, 8, false, FMT>;
+    }
     return exact ? down_kernel<G, NB, RW, true, FMT> : down_kernel<G, NB, RW, false, FMT>;
   }
   static constexpr int rows_per_block() { return kWaves * RW * (64 / G); }
   static constexpr int rows_per_half_block() { return kWaves * (RW == 4 ? 2 : RW) * (64 / G); }
+  static constexpr int rows_per_double_block() { return kWaves * (RW == 4 ? 8 : RW) * (64 / G); }
 };
 
 // up: the gate/up kernel of form `mode` (kGuOneRow, kGuRowItems, kGuPairs, kGuStaged) with `sel` keys per lane
 // of a folded selection (0: none); otherwise the down kernel, exact mode if sel != 0, with the
-// matrix-core tile if mode == 1 (where the shape has one), half-height blocks if mode == 2.
+// matrix-core tile if mode == 1 (where the shape has one), half-height blocks if mode == 2,
+// double-height blocks if mode == 3.
 template <int G, int NB, int FMT>
 inline bool pick_form(int mode, bool up, int sel, KernelFn* fn, int* rows) {
   *fn = up ? GemvPick<G, NB, FMT>::gateup(mode, sel) : GemvPick<G, NB, FMT>::down(sel != 0, mode);
-  *rows = !up && mode == 2 ? GemvPick<G, NB, FMT>::rows_per_half_block() : GemvPick<G, NB, FMT>::rows_per_block();
+  *rows = up          ? GemvPick<G, NB, FMT>::rows_per_block()
+          : mode == 2 ? GemvPick<G, NB, FMT>::rows_per_half_block()
+          : mode == 3 ? GemvPick<G, NB, FMT>::rows_per_double_block()
+                      : GemvPick<G, NB, FMT>::rows_per_block();
   return true;
 }
 
@@ -161,8 +169,10 @@ constexpr int kSplitTopkRows = 32;
 constexpr int kFusedMaxRows = 13;
 // Gate/up blocks of a round with the selection folded in (each loops over its share of the units).
 constexpr int kFusedBlocks = 768;
-// Down grids of at most this many full-height blocks use half-height blocks (see make_plan).
+// Down grids of at most this many full-height blocks use half-height blocks; grids of one-row items
+// past kDownDoubleMinBlocks (more than the CUs hold at once) use double-height blocks (see make_plan).
 constexpr int kDownHalfMaxBlocks = 768;
+constexpr int kDownDoubleMinBlocks = 1280;
 
 
 }  // namespace moe

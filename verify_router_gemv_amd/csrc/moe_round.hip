@@ -248,10 +248,14 @@ static bool make_plan(const moe_round* h, int T, int k, RoundPlan* p) {
     return false;
   // Rounds whose down grid is small (at most kDownHalfMaxBlocks full-height blocks, up to three per
   // CU) take half-height down blocks: twice the blocks, each with half the rows of H, so more of
-  // the expert tiles' loads are in flight at once.
-  if (!down_tile && umax * ((H + rows_dn - 1) / rows_dn) <= kDownHalfMaxBlocks &&
-      !pick_gemv(h->Gi, h->NBi, 2, false, h->cfg.exact, fmt, &p->dn, &rows_dn))
-    return false;
+  // the expert tiles' loads are in flight at once. Rounds of one-row items whose full-height grid
+  // is more than the CUs hold at once (kDownDoubleMinBlocks) take double-height blocks: each
+  // block's record read and SwiGLU staging then serve twice the rows of H.
+  const int blocks_dn = umax * ((H + rows_dn - 1) / rows_dn);
+  const int dn_mode = down_tile ? 1
+                      : blocks_dn <= kDownHalfMaxBlocks ? 2
+                      : (blocks_dn > kDownDoubleMinBlocks && rows_per_item(h, T) == 1) ? 3 : 0;
+  if (dn_mode >= 2 && !pick_gemv(h->Gi, h->NBi, dn_mode, false, h->cfg.exact, fmt, &p->dn, &rows_dn)) return false;
   p->grid_lg = logits_grid(E, H, T);
   const int units_gu = umax * ((I + rows_gu - 1) / rows_gu);
   const int groups = gateup_groups(gu_mode, p->fused ? fused_select_keys(E) : 0);
