@@ -339,6 +339,24 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 #define MOE_GLOBAL __attribute__((address_space(1)))
 #define MOE_LDS __attribute__((address_space(3)))
 
+// Global-address-space views of device pointers the compiler cannot place by itself (those that
+// may come from the ingress buffer): loads, stores and atomics through them are global operations,
+// counted by the vector-memory counter alone. Generic (flat) ones also count against the
+// LDS / scalar-load counter, so every later LDS read or kernel-argument load would wait for them
+// to complete (an atomic's or a store's full round trip).
+template <typename T>
+__device__ __forceinline__ MOE_GLOBAL T* gptr(T* p) {
+  return (MOE_GLOBAL T*)p;
+}
+__device__ __forceinline__ void atomic_add_global(MOE_GLOBAL float* p, float v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A word that no kernel writes while this one runs, by a scalar load (its own counter, so it waits
+// for no vector-memory operation).
+__device__ __forceinline__ float load_const_f32(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)p;
+}
+
 // Streaming (non-temporal) loads through global (not flat) addressing: weights are read once per
 // round; keep them from evicting the small reused data (activations, logits, records).
 // Every load in the kernels below is unconditional with a clamped, in-bounds address: a load under
@@ -418,10 +436,10 @@ __device__ __forceinline__ int key_expert(uint64_t key) { return 511 - static_ca
 // skipped (their lanes still take part in the reductions, on a clamped block). seed: if not null,
 // each element is also copied there (the residual the layer's output rows start from).
 __device__ __forceinline__ void quantize_block_pair(const float* x, uint32_t* xq, float2* xss, int qb, int nq,
-                                                    float* seed) {
+                                                    MOE_GLOBAL float* seed) {
   const int lane = threadIdx.x & 63, e = lane & 31;
   const int b = qb + (lane >> 5);
-  const float v = x[static_cast<size_t>(min(b, nq - 1)) * 32 + e];
+  const float v = gptr(x)[static_cast<size_t>(min(b, nq - 1)) * 32 + e];
   float mx = fabsf(v), sum = v;
   mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
   sum += dpp_f32<kDppXor1>(sum);

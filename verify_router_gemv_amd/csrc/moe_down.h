@@ -108,7 +108,7 @@ __device__ __forceinline__ void down_mfma_tile(const Args& a, int layer, const E
 
   const float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
   const Ingress in = get_ingress(a);
-  float* __restrict__ xn = layer_output(a, in, layer);
+  MOE_GLOBAL float* __restrict__ xn = gptr(layer_output(a, in, layer));
   for (int s0 = 0; s0 < wk.np; s0 += xst) {
     const int ns = min(xst, wk.np - s0);
     if (s0 > 0) __syncthreads();  // the previous chunk has been read by every wave
@@ -149,11 +149,11 @@ __device__ __forceinline__ void down_mfma_tile(const Args& a, int layer, const E
         }
       } else {
         const int t = work_row(wk, slot, T);
-        const float wgt = pw[wk.p0 + slot];
+        const float wgt = load_const_f32(pw + wk.p0 + slot);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int hr = row0 + wave * 16 + 4 * q + i;
-          if (hr < H) atomicAdd(xn + static_cast<size_t>(t) * H + hr, wgt * acc[i]);
+          if (hr < H) atomic_add_global(xn + static_cast<size_t>(t) * H + hr, wgt * acc[i]);
         }
       }
     }
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   }
   const float* pw = a.pair_w + static_cast<size_t>(layer) * a.Pcap;
   const Ingress in = get_ingress(a);
-  float* __restrict__ xn = layer_output(a, in, layer);
+  MOE_GLOBAL float* __restrict__ xn = gptr(layer_output(a, in, layer));
   const int row0 = tile * ROWS_B + wave * ROWS_W + rs;
   const size_t rq = static_cast<size_t>(I) / 2, rsm = sm_row_words<FMT>(I);
 
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
     stage_digits(hsrc, I, ns, dig, ss, s0 == 0 ? h0 : stage_load(hsrc, I, ns, 0));
     __syncthreads();
     for (int c = 0; c < ns; ++c) {
-      const float wgt = pw[wk.p0 + s0 + c];
+      const float wgt = load_const_f32(pw + wk.p0 + s0 + c);  // scalar: waits for no atomic
       uint32_t xd[NB][kXqWords];
       float xstep[NB], xsum[NB];
 #pragma unroll
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
 #pragma unroll
           for (int w = 0; w < RW; ++w) {
             const int hr = row0 + w * RPI;
-            if (hr < H) atomicAdd(xn + static_cast<size_t>(t) * H + hr, wgt * acc[w]);
+            if (hr < H) atomic_add_global(xn + static_cast<size_t>(t) * H + hr, wgt * acc[w]);
           }
         }
       }
@@ -319,7 +319,7 @@ static __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int la
     acc.z = fmaf(w, y.z, acc.z);
     acc.w = fmaf(w, y.w, acc.w);
   }
-  *reinterpret_cast<float4*>(xn + static_cast<size_t>(t) * H + h) = acc;
+  *reinterpret_cast<MOE_GLOBAL f32x4*>(gptr(xn) + static_cast<size_t>(t) * H + h) = f32x4{acc.x, acc.y, acc.z, acc.w};
 }
 
 }  // namespace moe

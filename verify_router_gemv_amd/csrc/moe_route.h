@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Args a, int layer) {
     const int nq = T * (H / 32);  // 32-blocks of the layer input, two per wave
     const int qb = 2 * ((blockIdx.x - E) * kWaves + wave);
     if (qb >= nq) return;
-    float* seed = (a.residual && !a.exact) ? layer_output(a, get_ingress(a), layer) : nullptr;
+    MOE_GLOBAL float* seed = (a.residual && !a.exact) ? gptr(layer_output(a, get_ingress(a), layer)) : nullptr;
     quantize_block_pair(x, a.xq, a.xss, qb, nq, seed);
     return;
   }
@@ -594,8 +594,8 @@ __device__ __forceinline__ void select_block(const Args& a, int layer, SS& s, bo
   for (int i = tid; i < npairs; i += nt) {  // by (row, rank): i = t*k + j
     slot_of[i] = s.slot[i];
     const size_t o = static_cast<size_t>(layer) * npairs + i;  // [L][T][k]
-    if (in.ids) in.ids[o] = s.sel[i];
-    if (in.route_w) in.route_w[o] = s.p[i];
+    if (in.ids) gptr(in.ids)[o] = s.sel[i];
+    if (in.route_w) gptr(in.route_w)[o] = s.p[i];
   }
   if (tid == 0) {
     a.n_unique[layer] = nu;
