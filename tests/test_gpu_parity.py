@@ -219,13 +219,13 @@ def test_ragged_shape_paths():
 
 def test_folded_selection_widths_at_512_experts():
     """E = 512, top-10 (eight keys per lane): the selection folded into gate/up on its many-row
-    forms (one-row items up to 10 rows, two-row items above, the block-wide union past 64 pairs)
-    and the selection kernel just past the fold's last width, each against the oracle."""
+    forms (one-row items up to 10 rows, two-row items above, the block-wide union past 64 pairs,
+    up to the fold's last width) and the selection kernel just past it, each against the oracle."""
     cfg = synth.config("deep").replace(L=1)
     layer = synth.make_layer(cfg, seed=12, layer=0, device=DEV)
     view = oracle_view(layer)
     g = GpuRound([layer], cfg, max_rows=16)
-    for T in (5, 9, 12, 13, 14):
+    for T in (5, 9, 12, 15, 16):
         say(f"case E=512 k=10 T={T}")
         X = synth.make_activations(cfg, T, seed=12, round_idx=T, device=DEV)
         check_layer_round(g, [view], X, cfg.k, f"E=512 T={T}")

@@ -164,9 +164,9 @@ constexpr int kSplitTopkRows = 32;
 
 // Rounds of at most this many rows fold the selection into the gate/up kernel: every block
 // recomputes it (one block per CU in the many-row forms, each row on a wave of its own), which
-// saves a launch, its gap and a dependent load. At 15 rows (the most the fused selection state holds,
-// 15 rows of 16 ranks) the one-block selection kernel is as fast or faster.
-constexpr int kFusedMaxRows = 13;
+// saves a launch, its gap and a dependent load; timed faster than the one-block selection kernel
+// up to 15 rows, the most the fused selection state holds (15 rows of 16 ranks).
+constexpr int kFusedMaxRows = 15;
 // Gate/up blocks of a round with the selection folded in (each loops over its share of the units).
 constexpr int kFusedBlocks = 768;
 // Down grids of at most this many full-height blocks use half-height blocks; grids of one-row items
