@@ -462,7 +462,8 @@ def exact_rounds(cfg, layer, acts, torch, np, MoeRound):
 def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
     """Copy-heavy wide verify (T = 16, 32, 64 independent rows, same layer shape): round latency,
     per-kernel time, unique experts and bytes, with the default (the integer-dot GEMV for every work
-    item) and with the int8 matrix-core tiles (gate/up and down) for items of 3+ rows; the round's
+    item), with work items of 2 and of 4 rows explicitly (the default takes 2 up to 32 rows, 4
+    above) and with the int8 matrix-core tiles (gate/up and down) for 4-row items' 3+ rows; the round's
     useful expert flops (2 T k 3 H I) against the dense bf16 matrix peak, and the useful operations the
     tiles carried against the dense int8 peak."""
     cfg = synth.config("wide")
@@ -472,9 +473,10 @@ def wide_rounds(vcfg, layer, torch, np, synth, MoeRound):
         xs = [synth.make_activations(cfg, T, seed=0, round_idx=r, device="cuda") for r in range(16)]
         out = torch.empty((T, cfg.H), device="cuda")
         row = {}
-        for name, mfma in (("default", 0), ("mfma_tile", 3)):
-            hs = [MoeRound([rp], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=64, use_graph=False, mfma_min_rows=mfma)
-                  for rp in reps]
+        for name, mfma, rpi in (("default", 0, 0), ("two_row_items", 0, 2), ("four_row_items", 0, 4),
+                                ("mfma_tile", 3, 4)):
+            hs = [MoeRound([rp], cfg.H, cfg.I, cfg.E, cfg.k, max_rows=64, use_graph=False, mfma_min_rows=mfma,
+                           rows_per_item=rpi) for rp in reps]
             for r in range(8):
                 hs[r % 4].run(xs[r], cfg.k, out)
             lat = []

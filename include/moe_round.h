@@ -125,7 +125,7 @@ typedef struct moe_round_config {
   int32_t fused_max_rows; /* rounds of up to this many rows fold the selection into the
                              gate/up kernel; default 15, -1 = never, at most 15            */
   int32_t rows_per_item;  /* rows of one expert per GEMV work item; default 1 for rounds of
-                             up to 10 rows, 2 up to 15 rows, 4 from 16 rows; 1..64         */
+                             up to 10 rows, 2 up to 32 rows, 4 from 33 rows; 1..64         */
   int32_t mfma_min_rows;  /* rounds of 16+ rows: work items with at least this many rows
                              use the int8 matrix-core tiles of gate/up (H = 2048) and down
                              (I = 512); default -1 = never (the integer-dot GEMVs measured

@@ -156,12 +156,15 @@ static int xstage_rows(int K) {
 // gate/up traffic stays at the unique experts' bytes) so no
 // block carries many rows, down to one row per item up to kOneRowItemsMaxRows rows (timed faster
 // there than two-row items, whose blocks do twice the fold work each; from 12 rows the two-row
-// items are faster); wide rounds keep larger items.
+// items are faster); wide rounds keep larger items (2 rows up to kWideTwoRowMaxRows rows, then 4:
+// timed faster at T = 32 and slower at T = 64 than the other size, and equal at T = 16).
 constexpr int kOneRowItemsMaxRows = 10;
+constexpr int kWideTwoRowMaxRows = 32;  // wide rounds up to this many rows: 2-row items, then 4
 constexpr int kPairItemMaxRows = 4;  // items the row-pair form takes in wide rounds (see make_plan)
 static int rows_per_item(const moe_round* h, int T) {
   if (h->rows_per_item > 0) return h->rows_per_item;
-  return T >= kWideRows ? 4 : (T <= kOneRowItemsMaxRows ? 1 : 2);
+  if (T >= kWideRows) return T <= kWideTwoRowMaxRows ? 2 : 4;
+  return T <= kOneRowItemsMaxRows ? 1 : 2;
 }
 
 // Upper bound of the work items of a round: sum over experts of ceil(rows / rg).
