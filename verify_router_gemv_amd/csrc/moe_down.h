@@ -218,6 +218,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
   const float4 h0 = stage_load(a.hbuf + static_cast<size_t>(wk.p0) * I, I, min(xst, wk.np), 0);
   __builtin_amdgcn_sched_barrier(0);
 
+  // The scale words are masked where they are used (an idle block slot of a padded split), not
+  // here: a mask here would make the wave wait for them before it stages the first chunk.
   uint4 cd[RW][NB];
   BlockScale<FMT> sd[RW][NB];
 #pragma unroll
@@ -225,20 +227,25 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
     const size_t r = min(row0 + w * RPI, H - 1);  // rows past H: not stored
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int bl = g + nb * G, b = min(bl, nblk - 1);
+      const int b = min(g + nb * G, nblk - 1);
       cd[w][nb] = load_stream_u4(W.dq + r * rq + 16 * b);
       sd[w][nb].load(W.ds + r * rsm, b);
-      sd[w][nb].mask(bl < nblk);
     }
   }
 
   uint32_t* dig = dlds;
   float2* ss = reinterpret_cast<float2*>(dlds + static_cast<size_t>(xst) * nblk * kXqWords);
+  // The first chunk is staged ahead of the loop, from the values loaded before the weights: its
+  // wait then covers those loads alone, and the staging and the barrier overlap the weight loads
+  // (inside the loop the compiler would wait for every load at the loop head).
+  stage_digits(a.hbuf + static_cast<size_t>(wk.p0) * I, I, min(xst, wk.np), dig, ss, h0);
   for (int s0 = 0; s0 < wk.np; s0 += xst) {
     const int ns = min(xst, wk.np - s0);
-    if (s0 > 0) __syncthreads();  // the previous chunk has been read by every wave
-    const float* hsrc = a.hbuf + static_cast<size_t>(wk.p0 + s0) * I;
-    stage_digits(hsrc, I, ns, dig, ss, s0 == 0 ? h0 : stage_load(hsrc, I, ns, 0));
+    if (s0 > 0) {
+      __syncthreads();  // the previous chunk has been read by every wave
+      const float* hsrc = a.hbuf + static_cast<size_t>(wk.p0 + s0) * I;
+      stage_digits(hsrc, I, ns, dig, ss, stage_load(hsrc, I, ns, 0));
+    }
     __syncthreads();
     for (int c = 0; c < ns; ++c) {
       const float wgt = load_const_f32(pw + wk.p0 + s0 + c);  // scalar: waits for no atomic
@@ -270,7 +277,9 @@ __global__ __launch_bounds__(kThreads) void down_kernel(Args a, int layer) {
           opaque(cc);  // unpack here, per row: not hoisted out of the row loop
           uint32_t cw[8];
           unpack_bytes(cc, cw);
-          ay = block_dot_q8(cw, xd[nb], xstep[nb], xsum[nb], sd[w][nb], ay);
+          BlockScale<FMT> sc = sd[w][nb];
+          sc.mask(g + nb * G < nblk);
+          ay = block_dot_q8(cw, xd[nb], xstep[nb], xsum[nb], sc, ay);
         }
         acc[w] = group_sum<G>(ay);
       }
